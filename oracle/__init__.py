@@ -1,0 +1,191 @@
+"""CPU oracle for the activation-sparse FFN -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of ``bench.py`` may import
+this package.  The product path (the HIP library and its binding) never imports it, and the two
+share no code.
+
+The arithmetic lives in ``ffn_oracle.c`` (plain C, double accumulation, one thread); this module
+only compiles it with gcc, marshals numpy arrays and composes per-token calls:
+
+* ``predictor``   -- low-rank activation predictor + strict sigmoid threshold
+  (PowerInfer, unite.ai, section "Adaptive sparse predictor").
+* ``ffn``         -- neuron-aware FFN over a mask (unite.ai, "Neuron-aware operator";
+  citnews, "Dynamic neuron cache": inactive neurons do not change the output).
+* ``router``/``moe`` -- top-k softmax router and the weighted sum of the chosen experts
+  (TurboSparse-Mixtral, nubint.ai review and citnews).
+
+Every function works on one token; batches are independent tokens, each with its own mask.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "ffn_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+F32, F16, I4G32 = 0, 1, 2
+RELU, REGLU, DRELU = 0, 1, 2
+ACT_NAMES = {"relu": RELU, "reglu": REGLU, "drelu": DRELU}
+
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile ffn_oracle.c into liboracle.so with gcc (-O2, no fast-math)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-fno-fast-math", "-std=c99", "-Wall", "-Wextra",
+                               "-shared", "-fPIC", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        build()
+        L = ctypes.CDLL(_LIB)
+        P, L_, I, D = ctypes.c_void_p, ctypes.c_long, ctypes.c_int, ctypes.c_double
+        L.oracle_half_to_double.restype = D
+        L.oracle_half_to_double.argtypes = [ctypes.c_uint16]
+        L.oracle_elem.restype = D
+        L.oracle_elem.argtypes = [I, P, P, L_, L_, L_]
+        L.oracle_predictor.restype = L_
+        L.oracle_predictor.argtypes = [L_, L_, L_, I, P, P, P, P, I, P, D, P, P, P, P]
+        L.oracle_active_list.restype = L_
+        L.oracle_active_list.argtypes = [L_, P, P]
+        L.oracle_ffn.restype = None
+        L.oracle_ffn.argtypes = [L_, L_, I, I, P, P, P, P, P, P, P, P, P, I, P, P, P, P]
+        L.oracle_router.restype = None
+        L.oracle_router.argtypes = [L_, L_, L_, I, P, I, P, P, P, P]
+        _lib = L
+    return _lib
+
+
+def _ptr(a):
+    if a is None:
+        return None
+    assert isinstance(a, np.ndarray) and a.flags["C_CONTIGUOUS"], "oracle wants C-contiguous numpy"
+    return a.ctypes.data
+
+
+def _dtype_code(a) -> int:
+    if a.dtype == np.float32:
+        return F32
+    if a.dtype == np.float16:
+        return F16
+    raise TypeError("unsupported dtype %s" % a.dtype)
+
+
+def half_to_double(bits: int) -> float:
+    return lib().oracle_half_to_double(bits)
+
+
+def decode_matrix(w, scales=None, ncols=None) -> np.ndarray:
+    """Decode a stored weight matrix element by element (f32 / f16 / int4-g32) into float64."""
+    L = lib()
+    if scales is None:
+        code = _dtype_code(w)
+        rows, cols = w.shape
+    else:
+        code = I4G32
+        rows = w.shape[0]
+        cols = ncols if ncols is not None else w.shape[1] * 2
+    out = np.empty((rows, cols), np.float64)
+    for r in range(rows):
+        for c in range(cols):
+            out[r, c] = L.oracle_elem(code, _ptr(w), _ptr(scales), r, c, cols)
+    return out
+
+
+def predictor(p1, p2, c1, c2, x, tau: float):
+    """One token.  Returns dict(z, s, p, active(uint8), idx(int32 ascending), count)."""
+    L = lib()
+    rank, d = p1.shape
+    ffn = p2.shape[0]
+    assert p2.shape == (ffn, rank) and p1.dtype == p2.dtype and x.shape == (d,)
+    z = np.empty(rank, np.float64)
+    s = np.empty(ffn, np.float64)
+    p = np.empty(ffn, np.float64)
+    active = np.empty(ffn, np.uint8)
+    n = L.oracle_predictor(d, ffn, rank, _dtype_code(p1), _ptr(p1), _ptr(p2), _ptr(c1), _ptr(c2),
+                           _dtype_code(x), _ptr(x), float(tau), _ptr(z), _ptr(s), _ptr(p),
+                           _ptr(active))
+    idx = np.empty(ffn, np.int32)
+    m = L.oracle_active_list(ffn, _ptr(active), _ptr(idx))
+    assert m == n
+    return {"z": z, "s": s, "p": p, "active": active, "idx": idx[:n].copy(), "count": int(n)}
+
+
+def ffn(layer: dict, x, mask=None):
+    """One token through the neuron-aware FFN.  ``layer`` holds numpy arrays:
+    act ('relu'|'reglu'|'drelu'), w_up, w_gate, w_down_t ([ffn][d] f32/f16, or uint8 [ffn][d/2]
+    for int4 with s_up/s_gate/s_down_t fp16 [ffn][d/32]), b_up, b_gate, b_down (f32 or None).
+    ``mask`` is a uint8 [ffn] array (None = all neurons).  Returns (y float64[d], h float64[ffn]).
+    """
+    L = lib()
+    act = ACT_NAMES[layer["act"]] if isinstance(layer["act"], str) else int(layer["act"])
+    w_up = layer["w_up"]
+    ffn_n = w_up.shape[0]
+    if layer.get("s_up") is not None:
+        code = I4G32
+        d = w_up.shape[1] * 2
+    else:
+        code = _dtype_code(w_up)
+        d = w_up.shape[1]
+    assert x.shape == (d,)
+    if mask is not None:
+        mask = np.ascontiguousarray(mask, dtype=np.uint8)
+        assert mask.shape == (ffn_n,)
+    h = np.empty(ffn_n, np.float64)
+    y = np.empty(d, np.float64)
+    gate = layer.get("w_gate") if act != RELU else None
+    L.oracle_ffn(d, ffn_n, act, code, _ptr(w_up), _ptr(gate), _ptr(layer["w_down_t"]),
+                 _ptr(layer.get("s_up")), _ptr(layer.get("s_gate") if act != RELU else None),
+                 _ptr(layer.get("s_down_t")), _ptr(layer.get("b_up")),
+                 _ptr(layer.get("b_gate") if act != RELU else None), _ptr(layer.get("b_down")),
+                 _dtype_code(x), _ptr(x), _ptr(mask), _ptr(h), _ptr(y))
+    return y, h
+
+
+def router(R, x, k: int = 2):
+    """Top-k router for one token.  Returns (ids int32[k], w float64[k], logits float64[E])."""
+    L = lib()
+    n_exp, d = R.shape
+    logits = np.empty(n_exp, np.float64)
+    ids = np.empty(k, np.int32)
+    w = np.empty(k, np.float64)
+    L.oracle_router(d, n_exp, k, _dtype_code(R), _ptr(R), _dtype_code(x), _ptr(x),
+                    _ptr(logits), _ptr(ids), _ptr(w))
+    return ids, w, logits
+
+
+def sparse_token(layer: dict, x, mask=None):
+    """Predictor (unless a mask is given) followed by the FFN over the active set, one token.
+    ``layer`` additionally holds p1, p2, c1, c2 and tau.  Returns (y float64[d], pred dict|None)."""
+    pred = None
+    if mask is None:
+        pred = predictor(layer["p1"], layer["p2"], layer.get("c1"), layer.get("c2"), x,
+                         layer["tau"])
+        mask = pred["active"]
+    y, _ = ffn(layer, x, mask)
+    return y, pred
+
+
+def moe_token(experts, R, x, k: int = 2, masks=None):
+    """Mixture of experts, one token: y = sum_t w_t * FFN_{e_t}(x), each chosen expert with its own
+    predictor (or the caller's mask for that expert).  Returns (y, ids, w, preds)."""
+    ids, w, _ = router(R, x, k)
+    y = np.zeros(x.shape[0], np.float64)
+    preds = []
+    for t in range(k):
+        e = int(ids[t])
+        ye, pred = sparse_token(experts[e], x, None if masks is None else masks[t])
+        preds.append(pred)
+        y += w[t] * ye
+    return y, ids, w, preds
