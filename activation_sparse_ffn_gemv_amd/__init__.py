@@ -1,0 +1,248 @@
+"""Python binding of libffn_sparse (the MI355X activation-sparse FFN), argument marshalling only.
+
+The functions below carry the names of the C ABI in ``include/ffn_sparse.h`` and pass plain
+pointers through ctypes; every step of the operator runs in the library's HIP kernels.  PyTorch
+is used for device memory and streams only.  There is no fallback: if the library is not built,
+importing this package raises.
+
+``SparseFFN`` is a thin convenience holder: it keeps the weight tensors and the workspace alive
+and fills the descriptor structs from torch tensors.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # load torch's HIP runtime first so the library binds to the same one
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libffn_sparse.so")
+
+FFN_OK, FFN_ERR_INVALID_ARGUMENT, FFN_ERR_UNSUPPORTED = 0, 1, 2
+FFN_ERR_WORKSPACE_TOO_SMALL, FFN_ERR_HIP, FFN_ERR_INTERNAL = 3, 4, 5
+FFN_ACT_RELU, FFN_ACT_REGLU, FFN_ACT_DRELU = 0, 1, 2
+FFN_F32, FFN_F16, FFN_I4G32 = 0, 1, 2
+FFN_PATH_AUTO, FFN_PATH_SPARSE, FFN_PATH_DENSE = 0, 1, 2
+
+ACT = {"relu": FFN_ACT_RELU, "reglu": FFN_ACT_REGLU, "drelu": FFN_ACT_DRELU}
+DTYPE = {"f32": FFN_F32, "f16": FFN_F16, "i4g32": FFN_I4G32}
+
+# Every symbol the header declares (checked by the tests).
+EXPORTS = [
+    "ffn_workspace_size", "ffn_sparse_plan", "ffn_sparse_forward", "ffn_dense_forward",
+    "ffn_plan_crossover", "ffn_plan_destroy", "ffn_plan_set_timing_events", "ffn_last_error",
+    "ffn_moe_workspace_size",
+    "ffn_moe_plan", "ffn_moe_forward", "ffn_moe_destroy",
+]
+
+
+class FFNError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__("ffn status %d: %s" % (status, msg))
+        self.status = status
+
+
+class ffn_layer_desc(ctypes.Structure):
+    _fields_ = [("d", ctypes.c_int32), ("ffn", ctypes.c_int32), ("rank", ctypes.c_int32),
+                ("act", ctypes.c_int32), ("w_dtype", ctypes.c_int32),
+                ("x_dtype", ctypes.c_int32), ("p_dtype", ctypes.c_int32),
+                ("threshold", ctypes.c_float), ("max_batch", ctypes.c_int32)]
+
+
+class ffn_layer_weights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ["w_up", "w_gate", "w_down_t", "s_up", "s_gate", "s_down_t", "b_up", "b_gate",
+                 "b_down", "p1", "p2", "c1", "c2"]]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded library; raises if it has not been built (no fallback path exists)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError("libffn_sparse.so is not built; run "
+                              "`python activation_sparse_ffn_gemv_amd/build.py`")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I, S = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+        st = ctypes.c_int
+        L.ffn_last_error.restype = ctypes.c_char_p
+        L.ffn_last_error.argtypes = []
+        L.ffn_workspace_size.restype = st
+        L.ffn_workspace_size.argtypes = [ctypes.POINTER(ffn_layer_desc), ctypes.POINTER(S)]
+        L.ffn_sparse_plan.restype = st
+        L.ffn_sparse_plan.argtypes = [ctypes.POINTER(ffn_layer_desc),
+                                      ctypes.POINTER(ffn_layer_weights), P, S, P, I,
+                                      ctypes.POINTER(P)]
+        L.ffn_sparse_forward.restype = st
+        L.ffn_sparse_forward.argtypes = [P, P, I, P, P, P, P, P, I, P]
+        L.ffn_dense_forward.restype = st
+        L.ffn_dense_forward.argtypes = [P, P, I, P, P, P]
+        L.ffn_plan_crossover.restype = st
+        L.ffn_plan_crossover.argtypes = [P, I, ctypes.POINTER(ctypes.c_float)]
+        L.ffn_plan_destroy.restype = st
+        L.ffn_plan_destroy.argtypes = [P]
+        L.ffn_plan_set_timing_events.restype = st
+        L.ffn_plan_set_timing_events.argtypes = [P, P, P]
+        L.ffn_moe_workspace_size.restype = st
+        L.ffn_moe_workspace_size.argtypes = [I, I, P, ctypes.POINTER(S)]
+        L.ffn_moe_plan.restype = st
+        L.ffn_moe_plan.argtypes = [I, I, P, ctypes.POINTER(P), P, S, ctypes.POINTER(P)]
+        L.ffn_moe_forward.restype = st
+        L.ffn_moe_forward.argtypes = [P, P, I, P, P, P, P]
+        L.ffn_moe_destroy.restype = st
+        L.ffn_moe_destroy.argtypes = [P]
+        _lib = L
+    return _lib
+
+
+def _check(status: int):
+    if status != FFN_OK:
+        raise FFNError(status, lib().ffn_last_error().decode())
+
+
+def ffn_last_error() -> str:
+    return lib().ffn_last_error().decode()
+
+
+def ffn_workspace_size(desc: ffn_layer_desc) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().ffn_workspace_size(ctypes.byref(desc), ctypes.byref(n)))
+    return n.value
+
+
+def ffn_sparse_plan(desc, weights, workspace: int, workspace_bytes: int, stream: int = 0,
+                    calibrate: int = 0) -> int:
+    out = ctypes.c_void_p(0)
+    _check(lib().ffn_sparse_plan(ctypes.byref(desc), ctypes.byref(weights), workspace,
+                                 workspace_bytes, stream or None, calibrate, ctypes.byref(out)))
+    return out.value
+
+
+def ffn_sparse_forward(plan: int, x: int, B: int, y: int, mask: int = 0, idx: int = 0,
+                       cnt: int = 0, scores: int = 0, path: int = FFN_PATH_SPARSE,
+                       stream: int = 0):
+    _check(lib().ffn_sparse_forward(plan, x, B, y, mask or None, idx or None, cnt or None,
+                                    scores or None, path, stream or None))
+
+
+def ffn_dense_forward(plan: int, x: int, B: int, y: int, mask: int = 0, stream: int = 0):
+    _check(lib().ffn_dense_forward(plan, x, B, y, mask or None, stream or None))
+
+
+def ffn_plan_crossover(plan: int, B: int) -> float:
+    v = ctypes.c_float(0)
+    _check(lib().ffn_plan_crossover(plan, B, ctypes.byref(v)))
+    return v.value
+
+
+def ffn_plan_destroy(plan: int):
+    _check(lib().ffn_plan_destroy(plan))
+
+
+def ffn_plan_set_timing_events(plan: int, start: int = 0, stop: int = 0):
+    """start / stop: hipEvent_t handles (torch.cuda.Event(enable_timing=True).cuda_event)."""
+    _check(lib().ffn_plan_set_timing_events(plan, start or None, stop or None))
+
+
+def ffn_moe_workspace_size(n_experts: int, top_k: int, expert0: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().ffn_moe_workspace_size(n_experts, top_k, expert0, ctypes.byref(n)))
+    return n.value
+
+
+def ffn_moe_plan(n_experts: int, top_k: int, w_router: int, experts, workspace: int,
+                 workspace_bytes: int) -> int:
+    arr = (ctypes.c_void_p * len(experts))(*experts)
+    out = ctypes.c_void_p(0)
+    _check(lib().ffn_moe_plan(n_experts, top_k, w_router, arr, workspace, workspace_bytes,
+                              ctypes.byref(out)))
+    return out.value
+
+
+def ffn_moe_forward(moe: int, x: int, B: int, y: int, expert_idx: int = 0, expert_w: int = 0,
+                    stream: int = 0):
+    _check(lib().ffn_moe_forward(moe, x, B, y, expert_idx or None, expert_w or None,
+                                 stream or None))
+
+
+def ffn_moe_destroy(moe: int):
+    _check(lib().ffn_moe_destroy(moe))
+
+
+# ---------------------------------------------------------------------------------------------
+def _ptr(t):
+    return 0 if t is None else t.data_ptr()
+
+
+def _stream():
+    return torch.cuda.current_stream().cuda_stream
+
+
+class SparseFFN:
+    """Holds one layer's device tensors, its workspace and its plan.
+
+    ``layer`` maps the names of ``ffn_layer_weights`` to device tensors (missing or None = NULL)
+    and carries ``act``; the storage dtypes are read from the tensors (uint8 up rows = int4).
+    """
+
+    def __init__(self, layer: dict, max_batch: int = 1, threshold: float = 0.5,
+                 workspace: torch.Tensor | None = None, calibrate: bool = False):
+        w_up = layer["w_up"]
+        dev = w_up.device
+        if w_up.dtype == torch.uint8:
+            w_dtype, d = FFN_I4G32, w_up.shape[1] * 2
+        else:
+            w_dtype, d = (FFN_F32 if w_up.dtype == torch.float32 else FFN_F16), w_up.shape[1]
+        p1 = layer.get("p1")
+        rank = 0 if p1 is None else p1.shape[0]
+        x_dtype = FFN_F32 if w_dtype == FFN_F32 else FFN_F16
+        p_dtype = x_dtype if p1 is None else (FFN_F32 if p1.dtype == torch.float32 else FFN_F16)
+        act = layer["act"]
+        self.desc = ffn_layer_desc(d=d, ffn=w_up.shape[0], rank=rank,
+                                   act=ACT[act] if isinstance(act, str) else int(act),
+                                   w_dtype=w_dtype, x_dtype=x_dtype, p_dtype=p_dtype,
+                                   threshold=float(layer.get("tau", threshold)),
+                                   max_batch=max_batch)
+        self.tensors = {k: layer.get(k) for k, _ in ffn_layer_weights._fields_}
+        self.weights = ffn_layer_weights(**{k: (_ptr(v) or None) for k, v in self.tensors.items()})
+        self.ws_bytes = ffn_workspace_size(self.desc)
+        if workspace is None:
+            workspace = torch.empty(self.ws_bytes, dtype=torch.uint8, device=dev)
+        assert workspace.numel() >= self.ws_bytes
+        self.workspace = workspace
+        self.d, self.ffn, self.x_dtype = d, self.desc.ffn, x_dtype
+        self.plan = ffn_sparse_plan(self.desc, self.weights, workspace.data_ptr(),
+                                    workspace.numel(), _stream(), int(calibrate))
+
+    def forward(self, x, y=None, mask=None, idx=None, cnt=None, scores=None,
+                path=FFN_PATH_SPARSE):
+        B = x.shape[0]
+        if y is None:
+            y = torch.empty(B, self.d, dtype=torch.float32, device=x.device)
+        ffn_sparse_forward(self.plan, x.data_ptr(), B, y.data_ptr(), _ptr(mask), _ptr(idx),
+                           _ptr(cnt), _ptr(scores), path, _stream())
+        return y
+
+    def dense(self, x, y=None, mask=None):
+        B = x.shape[0]
+        if y is None:
+            y = torch.empty(B, self.d, dtype=torch.float32, device=x.device)
+        ffn_dense_forward(self.plan, x.data_ptr(), B, y.data_ptr(), _ptr(mask), _stream())
+        return y
+
+    def crossover(self, B: int) -> float:
+        return ffn_plan_crossover(self.plan, B)
+
+    def close(self):
+        if self.plan:
+            ffn_plan_destroy(self.plan)
+            self.plan = 0
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -1,0 +1,300 @@
+// C ABI of libffn_sparse: validation, workspace layout, path choice and launch sequencing.
+// Kernels live in decode.hip (batch-1 decode), batch.hip (several tokens), dense.hip (MFMA
+// GEMMs) and moe.hip (router).  Nothing here allocates device memory or synchronises, except
+// ffn_sparse_plan with calibrate = 1.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <new>
+
+#include "common.h"
+#include "launch.h"
+
+using namespace ffn;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+ffn_status fail(ffn_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+ffn_status fail(ffn_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+ffn_status hip_fail(hipError_t e, const char* what) {
+  return fail(FFN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+int elems_per_chunk(int dt) { return dt == FFN_F32 ? 4 : dt == FFN_F16 ? 8 : 32; }
+
+int cpl_for(int nch) {
+  static const int ok[] = {1, 2, 3, 4, 6, 8, 12, 16};
+  int need = (nch + WAVE - 1) / WAVE;
+  for (int c : ok)
+    if (c >= need) return c;
+  return -1;
+}
+
+constexpr int kTargetChunks = 256;   // one main-kernel workgroup per CU of the MI355X
+
+struct Layout {
+  int nc, n_chunks, cpl_w, cpl_p;
+  size_t off_z, off_ccnt, off_clist, off_part, off_h, off_union, total;
+};
+
+ffn_status check_desc(const ffn_layer_desc* d) {
+  if (!d) return fail(FFN_ERR_INVALID_ARGUMENT, "desc is NULL");
+  if (d->d <= 0 || d->ffn <= 0 || d->rank < 0 || d->max_batch <= 0)
+    return fail(FFN_ERR_INVALID_ARGUMENT, "d, ffn, max_batch must be > 0 and rank >= 0");
+  if (d->act < FFN_ACT_RELU || d->act > FFN_ACT_DRELU)
+    return fail(FFN_ERR_INVALID_ARGUMENT, "act %d is not an ffn_act", d->act);
+  if (d->w_dtype < FFN_F32 || d->w_dtype > FFN_I4G32 || d->x_dtype < FFN_F32 ||
+      d->x_dtype > FFN_F16 || d->p_dtype < FFN_F32 || d->p_dtype > FFN_F16)
+    return fail(FFN_ERR_INVALID_ARGUMENT, "bad dtype (w %d, x %d, p %d)", d->w_dtype,
+                d->x_dtype, d->p_dtype);
+  if (!(d->threshold > 0.0f && d->threshold <= 1.0f))
+    return fail(FFN_ERR_INVALID_ARGUMENT, "threshold must lie in (0, 1]");
+  const int want_x = d->w_dtype == FFN_F32 ? FFN_F32 : FFN_F16;
+  if (d->x_dtype != want_x)
+    return fail(FFN_ERR_UNSUPPORTED, "x_dtype must be %s for this w_dtype",
+                want_x == FFN_F32 ? "FFN_F32" : "FFN_F16");
+  if (d->rank > 0 && d->p_dtype != d->x_dtype)
+    return fail(FFN_ERR_UNSUPPORTED, "p_dtype must equal x_dtype");
+  if (d->d % 8 || (d->w_dtype == FFN_I4G32 && d->d % 32))
+    return fail(FFN_ERR_UNSUPPORTED, "d must be a multiple of 8 (32 for int4)");
+  if (d->d > 8192) return fail(FFN_ERR_UNSUPPORTED, "d > 8192");
+  if (d->ffn % 32) return fail(FFN_ERR_UNSUPPORTED, "ffn must be a multiple of 32");
+  if (d->rank % 8 || d->rank > 4096)
+    return fail(FFN_ERR_UNSUPPORTED, "rank must be a multiple of 8 and <= 4096");
+  if (d->max_batch > 4096) return fail(FFN_ERR_UNSUPPORTED, "max_batch > 4096");
+  return FFN_OK;
+}
+
+Layout layout_for(const ffn_layer_desc* d) {
+  Layout L{};
+  L.nc = (d->ffn + kTargetChunks - 1) / kTargetChunks;
+  L.n_chunks = (d->ffn + L.nc - 1) / L.nc;
+  L.cpl_w = cpl_for(d->d / elems_per_chunk(d->w_dtype));
+  L.cpl_p = d->rank > 0 ? cpl_for(d->d / elems_per_chunk(d->p_dtype)) : 1;
+  const size_t B = (size_t)d->max_batch;
+  size_t off = 0;
+  L.off_z = off;      off = round_up(off + B * (size_t)std::max(d->rank, 1) * 4, 256);
+  L.off_ccnt = off;   off = round_up(off + B * (size_t)L.n_chunks * 4, 256);
+  L.off_clist = off;  off = round_up(off + B * (size_t)d->ffn * 4, 256);
+  L.off_part = off;   off = round_up(off + (size_t)L.n_chunks * d->d * 4, 256);
+  L.off_h = off;      off = round_up(off + 256, 256);
+  L.off_union = off;  off = round_up(off + 256, 256);
+  L.total = off;
+  return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* ffn_last_error(void) { return g_err; }
+
+ffn_status ffn_workspace_size(const ffn_layer_desc* desc, size_t* bytes) {
+  ffn_status st = check_desc(desc);
+  if (st != FFN_OK) return st;
+  if (!bytes) return fail(FFN_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  Layout L = layout_for(desc);
+  if (L.cpl_w < 0 || L.cpl_p < 0) return fail(FFN_ERR_UNSUPPORTED, "d too large");
+  *bytes = L.total;
+  g_err[0] = 0;
+  return FFN_OK;
+}
+
+ffn_status ffn_sparse_plan(const ffn_layer_desc* desc, const ffn_layer_weights* w,
+                           void* workspace, size_t workspace_bytes, void* stream,
+                           int32_t calibrate, ffn_plan** out) {
+  ffn_status st = check_desc(desc);
+  if (st != FFN_OK) return st;
+  if (!w || !out) return fail(FFN_ERR_INVALID_ARGUMENT, "weights / out is NULL");
+  *out = nullptr;
+  const bool i4 = desc->w_dtype == FFN_I4G32;
+  const bool gate = desc->act != FFN_ACT_RELU;
+  if (!w->w_up || !w->w_down_t || (gate && !w->w_gate))
+    return fail(FFN_ERR_INVALID_ARGUMENT, "w_up, w_down_t (and w_gate unless ReLU) required");
+  if (i4 && (!w->s_up || !w->s_down_t || (gate && !w->s_gate)))
+    return fail(FFN_ERR_INVALID_ARGUMENT, "int4 weights need their fp16 scales");
+  if (desc->rank > 0 && (!w->p1 || !w->p2))
+    return fail(FFN_ERR_INVALID_ARGUMENT, "rank > 0 needs p1 and p2");
+  const void* ptrs[] = {w->w_up, gate ? w->w_gate : nullptr, w->w_down_t,
+                        i4 ? w->s_up : nullptr, (i4 && gate) ? w->s_gate : nullptr,
+                        i4 ? w->s_down_t : nullptr, w->b_up, gate ? w->b_gate : nullptr,
+                        w->b_down, w->p1, w->p2, w->c1, w->c2, workspace};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return fail(FFN_ERR_INVALID_ARGUMENT, "pointer not 16-byte aligned");
+  size_t need = 0;
+  if ((st = ffn_workspace_size(desc, &need)) != FFN_OK) return st;
+  if (!workspace) return fail(FFN_ERR_INVALID_ARGUMENT, "workspace is NULL");
+  if (workspace_bytes < need)
+    return fail(FFN_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", workspace_bytes, need);
+
+  ffn_plan* p = new (std::nothrow) ffn_plan();
+  if (!p) return fail(FFN_ERR_INTERNAL, "out of host memory");
+  p->desc = *desc;
+  p->w = *w;
+  if (!gate) { p->w.w_gate = nullptr; p->w.s_gate = nullptr; p->w.b_gate = nullptr; }
+  p->ws = static_cast<char*>(workspace);
+  p->ws_bytes = workspace_bytes;
+  Layout L = layout_for(desc);
+  p->nc = L.nc;
+  p->n_chunks = L.n_chunks;
+  p->cpl_w = L.cpl_w;
+  p->cpl_p = L.cpl_p;
+  p->off_z = L.off_z;
+  p->off_ccnt = L.off_ccnt;
+  p->off_clist = L.off_clist;
+  p->off_part = L.off_part;
+  p->off_h = L.off_h;
+  p->off_union = L.off_union;
+  const double tau = desc->threshold;
+  p->thr = tau >= 1.0 ? INFINITY : (float)log(tau / (1.0 - tau));
+  for (int k = 0; k < 8; ++k) p->crossover_density[k] = 1.0f;
+  p->dense_min_batch = 1 << 30;
+  (void)stream;
+  (void)calibrate;
+  *out = p;
+  g_err[0] = 0;
+  return FFN_OK;
+}
+
+ffn_status ffn_sparse_forward(ffn_plan* p, const void* x, int32_t B, float* y,
+                              const uint8_t* mask, int32_t* idx, int32_t* cnt, float* scores,
+                              int32_t path, void* stream) {
+  if (!p) return fail(FFN_ERR_INVALID_ARGUMENT, "plan is NULL");
+  if (!x || !y) return fail(FFN_ERR_INVALID_ARGUMENT, "x / y is NULL");
+  const ffn_layer_desc& D = p->desc;
+  if (B < 1 || B > D.max_batch)
+    return fail(FFN_ERR_INVALID_ARGUMENT, "B = %d outside [1, %d]", B, D.max_batch);
+  if (!mask && D.rank == 0)
+    return fail(FFN_ERR_INVALID_ARGUMENT, "no predictor (rank 0) and no mask");
+  if (path < FFN_PATH_AUTO || path > FFN_PATH_DENSE)
+    return fail(FFN_ERR_INVALID_ARGUMENT, "path %d is not an ffn_path", path);
+  if (!aligned16(x) || !aligned16(y))
+    return fail(FFN_ERR_INVALID_ARGUMENT, "x / y not 16-byte aligned");
+  if (path == FFN_PATH_DENSE) return fail(FFN_ERR_UNSUPPORTED, "dense path not built yet");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+
+  const size_t xbytes = (size_t)D.d * (D.x_dtype == FFN_F32 ? 4 : 2);
+  float* z = reinterpret_cast<float*>(p->ws + p->off_z);
+  int* ccnt = reinterpret_cast<int*>(p->ws + p->off_ccnt);
+  int* clist = reinterpret_cast<int*>(p->ws + p->off_clist);
+  float* part = reinterpret_cast<float*>(p->ws + p->off_part);
+  const int wk = D.w_dtype == FFN_F32 ? WK_F32 : D.w_dtype == FFN_F16 ? WK_F16 : WK_I4;
+
+  for (int b = 0; b < B; ++b) {
+    const void* xb = static_cast<const char*>(x) + b * xbytes;
+    hipError_t e;
+    if (!mask) {
+      e = launch_pred_z(D.p_dtype == FFN_F16, p->cpl_p, p->w.p1, p->w.c1, xb, z, D.d, D.rank, st);
+      if (e != hipSuccess) return hip_fail(e, "predictor stage 1 launch");
+    }
+    MainArgs a{};
+    a.w_up = p->w.w_up;
+    a.w_gate = p->w.w_gate;
+    a.w_dn = p->w.w_down_t;
+    a.s_up = p->w.s_up;
+    a.s_gate = p->w.s_gate;
+    a.s_dn = p->w.s_down_t;
+    a.b_up = p->w.b_up;
+    a.b_gate = p->w.b_gate;
+    a.p2 = p->w.p2;
+    a.c2 = p->w.c2;
+    a.x = xb;
+    a.z = z;
+    a.mask = mask ? mask + (size_t)b * D.ffn : nullptr;
+    a.scores = (scores && !mask) ? scores + (size_t)b * D.ffn : nullptr;
+    a.chunk_cnt = ccnt;
+    a.chunk_list = clist;
+    a.part = part;
+    a.d = D.d;
+    a.ffn = D.ffn;
+    a.rank = D.rank;
+    a.nc = p->nc;
+    a.act = D.act;
+    a.has_gate = D.act != FFN_ACT_RELU;
+    a.p_f16 = D.p_dtype == FFN_F16;
+    a.thr = p->thr;
+    e = launch_main(wk, p->cpl_w, a, p->n_chunks, st, p->t_start, p->t_stop);
+    if (e != hipSuccess) return hip_fail(e, "main kernel launch");
+    e = launch_reduce(part, p->n_chunks, p->w.b_down, y + (size_t)b * D.d, D.d, st);
+    if (e != hipSuccess) return hip_fail(e, "reduce launch");
+    if (idx || cnt) {
+      e = launch_write_idx(ccnt, clist, p->n_chunks, p->nc, idx ? idx + (size_t)b * D.ffn : nullptr,
+                           cnt ? cnt + b : nullptr, st);
+      if (e != hipSuccess) return hip_fail(e, "index launch");
+    }
+  }
+  g_err[0] = 0;
+  return FFN_OK;
+}
+
+ffn_status ffn_dense_forward(ffn_plan* p, const void* x, int32_t B, float* y,
+                             const uint8_t* mask, void* stream) {
+  (void)p; (void)x; (void)B; (void)y; (void)mask; (void)stream;
+  return fail(FFN_ERR_UNSUPPORTED, "dense path not built yet");
+}
+
+ffn_status ffn_plan_crossover(const ffn_plan* p, int32_t B, float* density) {
+  if (!p || !density) return fail(FFN_ERR_INVALID_ARGUMENT, "plan / density is NULL");
+  if (B < 1) return fail(FFN_ERR_INVALID_ARGUMENT, "B < 1");
+  int k = 0;
+  while (k < 7 && (1 << (k + 1)) <= B) ++k;
+  *density = p->crossover_density[k];
+  return FFN_OK;
+}
+
+ffn_status ffn_plan_set_timing_events(ffn_plan* p, void* start, void* stop) {
+  if (!p) return fail(FFN_ERR_INVALID_ARGUMENT, "plan is NULL");
+  if ((start == nullptr) != (stop == nullptr))
+    return fail(FFN_ERR_INVALID_ARGUMENT, "start and stop must both be set or both be NULL");
+  p->t_start = static_cast<hipEvent_t>(start);
+  p->t_stop = static_cast<hipEvent_t>(stop);
+  return FFN_OK;
+}
+
+ffn_status ffn_plan_destroy(ffn_plan* p) {
+  delete p;
+  return FFN_OK;
+}
+
+ffn_status ffn_moe_workspace_size(int32_t n_experts, int32_t top_k, const ffn_plan* e0,
+                                  size_t* bytes) {
+  (void)n_experts; (void)top_k; (void)e0; (void)bytes;
+  return fail(FFN_ERR_UNSUPPORTED, "mixture of experts not built yet");
+}
+
+ffn_status ffn_moe_plan(int32_t n_experts, int32_t top_k, const void* w_router,
+                        ffn_plan* const* experts, void* workspace, size_t workspace_bytes,
+                        ffn_moe** out) {
+  (void)n_experts; (void)top_k; (void)w_router; (void)experts; (void)workspace;
+  (void)workspace_bytes; (void)out;
+  return fail(FFN_ERR_UNSUPPORTED, "mixture of experts not built yet");
+}
+
+ffn_status ffn_moe_forward(ffn_moe* m, const void* x, int32_t B, float* y, int32_t* expert_idx,
+                           float* expert_w, void* stream) {
+  (void)m; (void)x; (void)B; (void)y; (void)expert_idx; (void)expert_w; (void)stream;
+  return fail(FFN_ERR_UNSUPPORTED, "mixture of experts not built yet");
+}
+
+ffn_status ffn_moe_destroy(ffn_moe* m) {
+  (void)m;
+  return FFN_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,128 @@
+// Internal device helpers and the plan object of libffn_sparse (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/ffn_sparse.h"
+
+namespace ffn {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+
+// Storage kinds of a weight row.  Every row is read in 16-byte chunks: 4 fp32, 8 fp16 or
+// 32 int4 elements (one int4 group of 32 = one chunk, so each chunk has exactly one scale).
+enum { WK_F32 = 0, WK_F16 = 1, WK_I4 = 2 };
+
+template <int WK> struct Kind;
+template <> struct Kind<WK_F32> { static constexpr int EPC = 4;  static constexpr int XW = 1; };
+template <> struct Kind<WK_F16> { static constexpr int EPC = 8;  static constexpr int XW = 1; };
+// int4 chunk: 32 elements; the matching token slice is 32 fp16 = four 16-byte words.
+template <> struct Kind<WK_I4>  { static constexpr int EPC = 32; static constexpr int XW = 4; };
+
+constexpr int WAVE = 64;
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, WAVE);
+  return v;
+}
+
+// Sum over aligned groups of `width` lanes (width a power of two <= 64).
+__device__ __forceinline__ float group_sum(float v, int width) {
+  for (int o = width >> 1; o > 0; o >>= 1) v += __shfl_xor(v, o, WAVE);
+  return v;
+}
+
+__device__ __forceinline__ u32x4 ld16(const void* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+
+__device__ __forceinline__ h2 as_h2(uint32_t v) { return __builtin_bit_cast(h2, v); }
+
+// fp16 x fp16 pairs, fp32 accumulate (v_dot2_f32_f16: the products are exact in fp32).
+__device__ __forceinline__ float dot8_f16(u32x4 w, u32x4 x, float acc) {
+  acc = __builtin_amdgcn_fdot2(as_h2(w.x), as_h2(x.x), acc, false);
+  acc = __builtin_amdgcn_fdot2(as_h2(w.y), as_h2(x.y), acc, false);
+  acc = __builtin_amdgcn_fdot2(as_h2(w.z), as_h2(x.z), acc, false);
+  acc = __builtin_amdgcn_fdot2(as_h2(w.w), as_h2(x.w), acc, false);
+  return acc;
+}
+
+__device__ __forceinline__ float dot4_f32(u32x4 w, u32x4 x, float acc) {
+  f32x4 a = __builtin_bit_cast(f32x4, w), b = __builtin_bit_cast(f32x4, x);
+  acc = __builtin_fmaf(a.x, b.x, acc);
+  acc = __builtin_fmaf(a.y, b.y, acc);
+  acc = __builtin_fmaf(a.z, b.z, acc);
+  acc = __builtin_fmaf(a.w, b.w, acc);
+  return acc;
+}
+
+__device__ __forceinline__ float h_lo(uint32_t v) { return (float)as_h2(v).x; }
+__device__ __forceinline__ float h_hi(uint32_t v) { return (float)as_h2(v).y; }
+
+// int4 group: 16 bytes = 32 signed nibbles, element 2k in the low nibble of byte k.
+// Decoding: flipping the sign bit of each nibble gives n' = q + 8 in [0, 15]; the fp16 with bit
+// pattern 0x6400 | n' equals 1024 + n', so subtracting 1032 gives q exactly.  Even and odd
+// elements are split with masks, so the fp16 pairs hold elements (4m, 4m+2) and (4m+1, 4m+3);
+// the token slice is pre-permuted into the same pair order once (see i4_perm_x).
+__device__ __forceinline__ float dot32_i4(u32x4 w, const u32x4* xp, float scale, float acc) {
+  const h2 bias = {(_Float16)1032.0f, (_Float16)1032.0f};
+  float part = 0.0f;
+  uint32_t words[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    uint32_t t = words[k] ^ 0x88888888u;
+    uint32_t ev = t & 0x0F0F0F0Fu;          // elements 8k+0, +2, +4, +6 (one per byte)
+    uint32_t od = (t >> 4) & 0x0F0F0F0Fu;   // elements 8k+1, +3, +5, +7
+    // byte-interleave with 0x64: pairs (e0,e2) (e4,e6) (o1,o3) (o5,o7)
+    uint32_t p0 = __builtin_amdgcn_perm(0x64646464u, ev, 0x07010700u);
+    uint32_t p1 = __builtin_amdgcn_perm(0x64646464u, ev, 0x07030702u);
+    uint32_t p2 = __builtin_amdgcn_perm(0x64646464u, od, 0x07010700u);
+    uint32_t p3 = __builtin_amdgcn_perm(0x64646464u, od, 0x07030702u);
+    u32x4 xv = xp[k];
+    part = __builtin_amdgcn_fdot2(as_h2(p0) - bias, as_h2(xv.x), part, false);
+    part = __builtin_amdgcn_fdot2(as_h2(p1) - bias, as_h2(xv.y), part, false);
+    part = __builtin_amdgcn_fdot2(as_h2(p2) - bias, as_h2(xv.z), part, false);
+    part = __builtin_amdgcn_fdot2(as_h2(p3) - bias, as_h2(xv.w), part, false);
+  }
+  return __builtin_fmaf(part, scale, acc);
+}
+
+// Reorder a 32-element fp16 token slice (four 16-byte words, natural order) into the pair order
+// dot32_i4 consumes: per 8 elements e0..e7 -> (e0,e2) (e4,e6) (e1,e3) (e5,e7).
+__device__ __forceinline__ void i4_perm_x(u32x4* xs) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    u32x4 v = xs[k];  // halves: v.x = (e0,e1), v.y = (e2,e3), v.z = (e4,e5), v.w = (e6,e7)
+    u32x4 o;
+    o.x = __builtin_amdgcn_perm(v.y, v.x, 0x05040100u);  // (e0, e2)
+    o.y = __builtin_amdgcn_perm(v.w, v.z, 0x05040100u);  // (e4, e6)
+    o.z = __builtin_amdgcn_perm(v.y, v.x, 0x07060302u);  // (e1, e3)
+    o.w = __builtin_amdgcn_perm(v.w, v.z, 0x07060302u);  // (e5, e7)
+    xs[k] = o;
+  }
+}
+
+}  // namespace ffn
+
+// ----------------------------------------------------------------------------------------------
+// Host-side plan.
+struct ffn_plan {
+  ffn_layer_desc desc;
+  ffn_layer_weights w;
+  char* ws;
+  size_t ws_bytes;
+  int nc;            // neurons per chunk (one workgroup of the main kernel per chunk)
+  int n_chunks;
+  int cpl_w;         // 16-byte chunks per lane for a weight row
+  int cpl_p;         // 16-byte chunks per lane for a predictor P1 row
+  float thr;         // logit(threshold): active iff score > thr
+  size_t off_z, off_ccnt, off_clist, off_part, off_h, off_union;
+  float crossover_density[8];   // per batch bucket 1,2,4,...,128
+  int dense_min_batch;          // AUTO takes the dense path from this batch size on
+  hipEvent_t t_start, t_stop;   // instrumentation events attached to the main dispatch
+};

@@ -1,0 +1,179 @@
+/*
+ * ffn_sparse.h -- C ABI of the MI355X (gfx950) activation-sparse FFN library, libffn_sparse.so.
+ *
+ * The operator is the neuron-aware sparse FFN of PowerInfer / PowerInfer-2:
+ *  - "PowerInfer: Fast LLM Serving with a Consumer-grade GPU" (unite.ai): section "Adaptive sparse
+ *    predictor" (a small per-layer model predicts which FFN neurons fire for the current token),
+ *    section "Online stage" (neurons predicted inactive are skipped), section "Neuron-aware
+ *    operator" (the active neurons' row / column vectors are computed directly, with no
+ *    conversion to a dense format), section "Neuron placement and management" (computed neurons
+ *    keep their original positions);
+ *  - nearauto.com PowerInfer article, section "PowerInfer architecture", Fig. 8 (only activated
+ *    neurons are computed, and partial results from disjoint neuron sets are summed);
+ *  - citnews.com.cn PowerInfer-2 article, section "Dynamic neuron cache" (inactive neurons do not
+ *    change the output), section on neuron-cluster computation (prefill with most neurons active
+ *    runs as large dense clusters, decode as small sparse ones) and section on low-cost
+ *    sparsification (dReLU: both gate and up are rectified);
+ *  - nearauto.com section "Experiments", Fig. 13 (INT4-quantised models), Fig. 14 (batch sizes).
+ *
+ * For one token x (d values) and a layer with ffn neurons:
+ *   predictor   z = P1 x + c1              (rank values)
+ *               s = P2 z + c2              (ffn scores)
+ *               A = { i : sigmoid(s_i) > threshold }, ascending
+ *   neurons     u_i = W_up[i] . x + b_up_i,   g_i = W_gate[i] . x + b_gate_i      (i in A)
+ *               h_i = max(u_i,0) (ReLU) | max(g_i,0) u_i (ReGLU) | max(g_i,0) max(u_i,0) (dReLU)
+ *   output      y = b_down + sum_{i in A} h_i W_down_t[i]      (W_down stored transposed)
+ *
+ * Conventions shared by every entry point:
+ *  - Every function returns an ffn_status; none throws, exits or prints.  On any error nothing
+ *    has been enqueued and no output was touched; ffn_last_error() gives a message.
+ *  - Pointers named "device" are HIP device pointers (hipMalloc / torch CUDA tensors); they stay
+ *    owned by the caller and must outlive the plan that references them.  Every device pointer
+ *    must be 16-byte aligned.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).  Forward calls only
+ *    enqueue work on it: they never allocate, never synchronise and never use memset nodes, so a
+ *    caller may capture them in a HIP graph.
+ *  - Shapes: d % 8 == 0 (d % 32 == 0 for int4), d <= 8192, ffn % 32 == 0, rank % 8 == 0,
+ *    rank <= 4096, 1 <= B <= max_batch.  Anything else gives FFN_ERR_UNSUPPORTED or
+ *    FFN_ERR_INVALID_ARGUMENT.
+ *  - A plan is not re-entrant: forward calls on one plan must be ordered (one stream).  Plans used
+ *    one after another on one stream may share one workspace.
+ */
+#ifndef FFN_SPARSE_H
+#define FFN_SPARSE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    FFN_OK = 0,
+    FFN_ERR_INVALID_ARGUMENT = 1,   /* NULL where a pointer is required, bad enum, B out of range */
+    FFN_ERR_UNSUPPORTED = 2,        /* shape / dtype combination the kernels do not cover        */
+    FFN_ERR_WORKSPACE_TOO_SMALL = 3,
+    FFN_ERR_HIP = 4,                /* a HIP runtime call failed (message in ffn_last_error)     */
+    FFN_ERR_INTERNAL = 5
+} ffn_status;
+
+typedef enum { FFN_ACT_RELU = 0, FFN_ACT_REGLU = 1, FFN_ACT_DRELU = 2 } ffn_act;
+
+/* Storage types.  FFN_I4G32: signed two's-complement nibbles, element 2k in the low nibble of
+ * byte k of a row, plus one fp16 scale per 32 consecutive elements of the row; w = scale * q. */
+typedef enum { FFN_F32 = 0, FFN_F16 = 1, FFN_I4G32 = 2 } ffn_dtype;
+
+typedef enum { FFN_PATH_AUTO = 0, FFN_PATH_SPARSE = 1, FFN_PATH_DENSE = 2 } ffn_path;
+
+typedef struct {
+    int32_t d;          /* model width                                                       */
+    int32_t ffn;        /* FFN neurons                                                       */
+    int32_t rank;       /* predictor rank; 0 = no predictor (sparse forward then needs a mask) */
+    int32_t act;        /* ffn_act                                                           */
+    int32_t w_dtype;    /* up / gate / down_t storage: FFN_F32 | FFN_F16 | FFN_I4G32         */
+    int32_t x_dtype;    /* token storage: FFN_F32 | FFN_F16                                  */
+    int32_t p_dtype;    /* predictor storage: FFN_F32 | FFN_F16                              */
+    float threshold;    /* tau in (0, 1]: neuron active iff sigmoid(s) > tau, strictly       */
+    int32_t max_batch;  /* largest B any forward call on this plan will pass                  */
+} ffn_layer_desc;
+
+typedef struct {                       /* all device pointers, caller-owned                   */
+    const void *w_up, *w_gate, *w_down_t; /* [ffn][d] row-major; int4: [ffn][d/2] bytes      */
+    const void *s_up, *s_gate, *s_down_t; /* int4 only: [ffn][d/32] fp16 scales, else NULL   */
+    const float *b_up, *b_gate, *b_down;  /* [ffn], [ffn], [d] fp32; each may be NULL (= 0)  */
+    const void *p1, *p2;                  /* [rank][d], [ffn][rank] in p_dtype               */
+    const float *c1, *c2;                 /* [rank], [ffn] fp32; may be NULL (= 0)           */
+} ffn_layer_weights;                      /* w_gate / s_gate / b_gate are ignored for ReLU     */
+
+typedef struct ffn_plan ffn_plan;          /* opaque host object                              */
+
+/* Bytes of device workspace a plan for `desc` needs (upper bound for any B <= max_batch). */
+ffn_status ffn_workspace_size(const ffn_layer_desc *desc, size_t *bytes);
+
+/*
+ * Validate desc and weights, lay out the caller's device workspace and return a plan.
+ * `workspace` (device, >= ffn_workspace_size bytes) is owned by the caller and must outlive the
+ * plan.  calibrate = 1 times the sparse path against the dense path over a density sweep on
+ * `stream` (the only call that synchronises) and stores the crossover density per batch size
+ * used by FFN_PATH_AUTO; calibrate = 0 keeps the built-in crossover table.
+ */
+ffn_status ffn_sparse_plan(const ffn_layer_desc *desc, const ffn_layer_weights *weights,
+                           void *workspace, size_t workspace_bytes, void *stream,
+                           int32_t calibrate, ffn_plan **out);
+
+/*
+ * y[B][d] (fp32, fully overwritten) = FFN of the B tokens x[B][d] (x_dtype), each over its own
+ * active set (device pointers).
+ *   mask    [B][ffn] uint8 0/1 or NULL.  NULL: the predictor picks each token's set (needs
+ *           rank > 0).  Non-NULL: the caller's set replaces the predictor's (test hook; also
+ *           how a caller runs a precomputed set).
+ *   idx     [B][ffn] int32 or NULL: token b's active neurons in ascending order in
+ *           idx[b*ffn .. b*ffn + cnt[b]); the rest of the row is left unspecified.
+ *   cnt     [B] int32 or NULL: |A_b|.
+ *   scores  [B][ffn] fp32 or NULL: the predictor scores s (only written when mask == NULL).
+ *   path    ffn_path: SPARSE = neuron-aware kernels; DENSE = dense MFMA kernels with the
+ *           per-token active set applied in their epilogue; AUTO = DENSE when B reaches the
+ *           plan's crossover batch, else SPARSE.  Both paths give the same y within rounding.
+ * Errors: FFN_ERR_INVALID_ARGUMENT for NULL x / y, B out of [1, max_batch], mask == NULL with
+ * rank == 0, bad path.
+ */
+ffn_status ffn_sparse_forward(ffn_plan *plan, const void *x, int32_t B, float *y,
+                              const uint8_t *mask, int32_t *idx, int32_t *cnt, float *scores,
+                              int32_t path, void *stream);
+
+/*
+ * Dense FFN (every neuron), y[B][d] fp32, through the MFMA GEMM kernels (the prefill path).
+ * mask [B][ffn] uint8 or NULL: non-NULL zeroes h for inactive (token, neuron) pairs in the
+ * epilogue, which equals the sparse result.
+ */
+ffn_status ffn_dense_forward(ffn_plan *plan, const void *x, int32_t B, float *y,
+                             const uint8_t *mask, void *stream);
+
+/* Crossover density for batch B: the union density above which AUTO takes the dense path. */
+ffn_status ffn_plan_crossover(const ffn_plan *plan, int32_t B, float *density);
+
+ffn_status ffn_plan_destroy(ffn_plan *plan);
+
+/*
+ * Instrumentation for a caller that times the main (gathered-row) kernel on its own.  While
+ * `start` and `stop` (hipEvent_t handles passed as void*, created with timing enabled) are
+ * non-NULL, every forward on this plan launches its main kernel with the two events attached to
+ * the dispatch itself, so hipEventElapsedTime(start, stop) afterwards is that one launch's
+ * execution time.  NULL, NULL turns it off.  Not meant for calls under graph capture.
+ */
+ffn_status ffn_plan_set_timing_events(ffn_plan *plan, void *start, void *stop);
+
+/* Message of the last error on the calling thread ("" if none).  Never NULL. */
+const char *ffn_last_error(void);
+
+/* ---------------------------------------------------------------------------------------------
+ * Mixture of experts (TurboSparse-Mixtral; nubint.ai PowerInfer-2 review and citnews.com.cn):
+ * a router picks top_k experts per token; y = sum_t w_t FFN_{e_t}(x), each expert a sparse FFN
+ * with its own predictor.  Routing stays on the device: the kernels read the chosen expert ids
+ * from device memory, never from the host.
+ *   logits_e = R[e] . x ;  the top_k largest win, ties to the lower expert index;
+ *   w = softmax over the chosen logits.
+ * All expert plans must share d, ffn, rank, act and dtypes; their workspaces may be one buffer.
+ */
+typedef struct ffn_moe ffn_moe;
+
+/* w_router: device [n_experts][d] fp16.  experts: host array of n_experts plans.
+ * workspace: device, >= ffn_moe_workspace_size bytes, caller-owned. */
+ffn_status ffn_moe_workspace_size(int32_t n_experts, int32_t top_k, const ffn_plan *expert0,
+                                  size_t *bytes);
+ffn_status ffn_moe_plan(int32_t n_experts, int32_t top_k, const void *w_router,
+                        ffn_plan *const *experts, void *workspace, size_t workspace_bytes,
+                        ffn_moe **out);
+
+/* B tokens; y[B][d] fp32 overwritten.  expert_idx [B][top_k] int32 and expert_w [B][top_k]
+ * fp32 (device, may be NULL) receive the routing decision. */
+ffn_status ffn_moe_forward(ffn_moe *moe, const void *x, int32_t B, float *y,
+                           int32_t *expert_idx, float *expert_w, void *stream);
+ffn_status ffn_moe_destroy(ffn_moe *moe);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FFN_SPARSE_H */

@@ -1,0 +1,121 @@
+"""The C-ABI library: it loads, exports every symbol include/ffn_sparse.h declares, and its host
+validation rejects bad arguments with the documented status codes (no GPU work is issued)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ffn_sparse.h")
+
+ffn = pytest.importorskip("activation_sparse_ffn_gemv_amd")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(ffn_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_lists_match_binding():
+    assert _declared() == sorted(ffn.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = ffn.lib()
+    for name in _declared():
+        assert hasattr(L, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", ffn.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    syms = {ln.split()[-1] for ln in out.splitlines() if ln.strip()}
+    for name in _declared():
+        assert name in syms, name
+
+
+def test_header_compiles_as_c():
+    r = subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-fsyntax-only", "-x", "c", "-"],
+                       input='#include "%s"\nint main(void){return 0;}\n' % HEADER,
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+
+
+def _desc(**kw):
+    base = dict(d=4096, ffn=11008, rank=256, act=ffn.FFN_ACT_REGLU, w_dtype=ffn.FFN_F16,
+                x_dtype=ffn.FFN_F16, p_dtype=ffn.FFN_F16, threshold=0.5, max_batch=1)
+    base.update(kw)
+    return ffn.ffn_layer_desc(**base)
+
+
+def test_workspace_size_valid_and_monotone_in_batch():
+    a = ffn.ffn_workspace_size(_desc())
+    b = ffn.ffn_workspace_size(_desc(max_batch=32))
+    assert a > 0 and b >= a and a % 256 == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(d=0), ffn.FFN_ERR_INVALID_ARGUMENT),
+    (dict(act=7), ffn.FFN_ERR_INVALID_ARGUMENT),
+    (dict(threshold=0.0), ffn.FFN_ERR_INVALID_ARGUMENT),
+    (dict(threshold=1.5), ffn.FFN_ERR_INVALID_ARGUMENT),
+    (dict(d=4100), ffn.FFN_ERR_UNSUPPORTED),
+    (dict(ffn=11000), ffn.FFN_ERR_UNSUPPORTED),
+    (dict(rank=100), ffn.FFN_ERR_UNSUPPORTED),
+    (dict(x_dtype=ffn.FFN_F32), ffn.FFN_ERR_UNSUPPORTED),
+    (dict(w_dtype=ffn.FFN_I4G32, d=4104), ffn.FFN_ERR_UNSUPPORTED),
+    (dict(d=16384), ffn.FFN_ERR_UNSUPPORTED),
+    (dict(max_batch=0), ffn.FFN_ERR_INVALID_ARGUMENT),
+])
+def test_bad_descriptors_are_rejected(kw, status):
+    with pytest.raises(ffn.FFNError) as e:
+        ffn.ffn_workspace_size(_desc(**kw))
+    assert e.value.status == status
+    assert ffn.ffn_last_error()
+
+
+def test_plan_validation_before_any_gpu_call():
+    d = _desc()
+    w = ffn.ffn_layer_weights()
+    with pytest.raises(ffn.FFNError) as e:          # missing weights
+        ffn.ffn_sparse_plan(d, w, 0x1000, 1 << 30)
+    assert e.value.status == ffn.FFN_ERR_INVALID_ARGUMENT
+    w = ffn.ffn_layer_weights(w_up=0x1000, w_gate=0x2000, w_down_t=0x3000, p1=0x4000,
+                              p2=0x5000)
+    with pytest.raises(ffn.FFNError) as e:          # workspace too small
+        ffn.ffn_sparse_plan(d, w, 0x10000, 16)
+    assert e.value.status == ffn.FFN_ERR_WORKSPACE_TOO_SMALL
+    w.b_up = 0x1004                                 # misaligned pointer
+    with pytest.raises(ffn.FFNError) as e:
+        ffn.ffn_sparse_plan(d, w, 0x10000, 1 << 30)
+    assert e.value.status == ffn.FFN_ERR_INVALID_ARGUMENT
+    w.b_up = None
+    plan = ffn.ffn_sparse_plan(d, w, 0x10000, 1 << 30)   # host-only: nothing is launched
+    try:
+        with pytest.raises(ffn.FFNError) as e:      # B out of range
+            ffn.ffn_sparse_forward(plan, 0x1000, 2, 0x2000)
+        assert e.value.status == ffn.FFN_ERR_INVALID_ARGUMENT
+        with pytest.raises(ffn.FFNError) as e:      # bad path
+            ffn.ffn_sparse_forward(plan, 0x1000, 1, 0x2000, path=9)
+        assert e.value.status == ffn.FFN_ERR_INVALID_ARGUMENT
+        with pytest.raises(ffn.FFNError):           # NULL y
+            ffn.ffn_sparse_forward(plan, 0x1000, 1, 0)
+    finally:
+        ffn.ffn_plan_destroy(plan)
+
+
+def test_no_predictor_requires_mask():
+    d = _desc(rank=0)
+    w = ffn.ffn_layer_weights(w_up=0x1000, w_gate=0x2000, w_down_t=0x3000)
+    plan = ffn.ffn_sparse_plan(d, w, 0x10000, 1 << 30)
+    try:
+        with pytest.raises(ffn.FFNError) as e:
+            ffn.ffn_sparse_forward(plan, 0x1000, 1, 0x2000)
+        assert e.value.status == ffn.FFN_ERR_INVALID_ARGUMENT
+    finally:
+        ffn.ffn_plan_destroy(plan)
+
+
+def test_binding_loads_only_the_in_tree_library():
+    assert os.path.dirname(ffn.LIB_PATH) == os.path.join(ROOT, "activation_sparse_ffn_gemv_amd")
+    assert isinstance(ffn.lib(), ctypes.CDLL)

@@ -1,0 +1,178 @@
+"""GPU parity of the sparse decode path (predictor -> compaction -> gathered rows -> down) against
+the CPU oracle, through the C ABI, on seeded synthetic layers."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from parity import TOL, check_index_list, mask_from_idx, normwise, oracle_layer, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ffn():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import activation_sparse_ffn_gemv_amd as m
+    return m
+
+
+def _run(ffn, L, x, mask=None, tau=None):
+    """Forward through the library; returns y, idx list per token, cnt, scores (numpy)."""
+    dev = x.device
+    B = x.shape[0]
+    F = L["w_up"].shape[0]
+    layer = dict(L)
+    if tau is not None:
+        layer["tau"] = tau
+    m = ffn.SparseFFN(layer, max_batch=B)
+    y = torch.full((B, m.d), float("nan"), dtype=torch.float32, device=dev)
+    idx = torch.full((B, F), -1, dtype=torch.int32, device=dev)
+    cnt = torch.full((B,), -1, dtype=torch.int32, device=dev)
+    scores = torch.zeros((B, F), dtype=torch.float32, device=dev)
+    m.forward(x, y=y, mask=mask, idx=idx, cnt=cnt, scores=scores)
+    torch.cuda.synchronize()
+    cnt_h = cnt.cpu().numpy()
+    idx_h = idx.cpu().numpy()
+    lists = [idx_h[b, :cnt_h[b]] for b in range(B)]
+    m.close()
+    return y.cpu().numpy(), lists, cnt_h, scores.cpu().numpy()
+
+
+def _check_predicted(ffn, cfg, n_tokens, layer_no=0, tau=None):
+    host = synth.make_layer(cfg, layer=layer_no)
+    L = to_device(host)
+    OL = oracle_layer(host)
+    if tau is not None:
+        OL["tau"] = tau
+    x = synth.make_tokens(cfg, n_tokens, layer=layer_no).cuda()
+    y, lists, cnt, scores = _run(ffn, L, x, tau=tau)
+    xh = x.cpu().numpy()
+    worst = 0.0
+    for t in range(n_tokens):
+        pred = oracle.predictor(OL["p1"], OL["p2"], OL["c1"], OL["c2"], xh[t], OL["tau"])
+        check_index_list(lists[t], pred, OL["tau"])
+        assert cnt[t] == len(lists[t])
+        # scores: fp32 sums of the predictor vs the fp64 oracle
+        err_s = normwise(scores[t], pred["s"])
+        assert err_s <= (1e-5 if cfg.p_dtype == "f32" else 2e-3), err_s
+        y_ref, _ = oracle.ffn(OL, xh[t], mask_from_idx(lists[t], cfg.ffn))
+        e = normwise(y[t], y_ref)
+        worst = max(worst, e)
+        assert e <= TOL[cfg.w_dtype], (t, e)
+    return worst, lists
+
+
+SMALL = [
+    dict(d=64, ffn=256, rank=16, act="relu", w_dtype="f32", x_dtype="f32", p_dtype="f32"),
+    dict(d=256, ffn=1056, rank=32, act="reglu", w_dtype="f32", x_dtype="f32", p_dtype="f32",
+         bias_gate=True, bias_down=True),
+    dict(d=136, ffn=608, rank=24, act="drelu", w_dtype="f32", x_dtype="f32", p_dtype="f32",
+         bias_gate=True, bias_up=True),
+    dict(d=512, ffn=2080, rank=64, act="relu", w_dtype="f16", x_dtype="f16", p_dtype="f16",
+         bias_up=True, bias_down=True),
+    dict(d=1024, ffn=4128, rank=128, act="reglu", w_dtype="f16", x_dtype="f16",
+         p_dtype="f16", bias_gate=True),
+    dict(d=520, ffn=1184, rank=40, act="drelu", w_dtype="f16", x_dtype="f16", p_dtype="f16",
+         bias_gate=True, bias_up=True, bias_down=True),
+]
+
+
+@pytest.mark.parametrize("kw", SMALL, ids=lambda k: "%s_%s_d%d_f%d" % (k["act"], k["w_dtype"],
+                                                                       k["d"], k["ffn"]))
+def test_predicted_path_small(ffn, kw):
+    cfg = synth.small_config(density=0.12, **kw)
+    _check_predicted(ffn, cfg, n_tokens=6)
+
+
+def test_opt125m_shape_all_tokens(ffn):
+    cfg = synth.CONFIGS["opt125m_relu_f32"]
+    worst, lists = _check_predicted(ffn, cfg, n_tokens=cfg.tokens)
+    dens = np.mean([len(a) for a in lists]) / cfg.ffn
+    assert 0.07 < dens < 0.13
+
+
+def test_llama2_7b_shape_sampled_tokens(ffn):
+    _check_predicted(ffn, synth.CONFIGS["llama2_7b_reglu_f16"], n_tokens=3)
+
+
+def test_mistral_7b_shape_sampled_tokens(ffn):
+    _check_predicted(ffn, synth.CONFIGS["turbosparse_mistral_7b_drelu_f16"], n_tokens=2)
+
+
+@pytest.mark.parametrize("act", ["relu", "reglu", "drelu"])
+@pytest.mark.parametrize("wd", ["f32", "f16"])
+def test_true_mask_equals_dense_on_gpu(ffn, act, wd):
+    """With the mask set to the true positive set the sparse result equals the dense FFN
+    (inactive neurons contribute exactly zero); with all ones it equals the dense FFN too."""
+    cfg = synth.small_config(d=256, ffn=1024, rank=0, act=act, w_dtype=wd, x_dtype=wd,
+                             p_dtype=wd, density=0.1, bias_up=True, bias_gate=True,
+                             bias_down=True)
+    host = synth.make_layer(cfg)
+    L, OL = to_device(host), oracle_layer(host)
+    x = synth.make_tokens(cfg, 3).cuda()
+    xh = x.cpu().numpy()
+    masks_true, masks_ones = [], []
+    for t in range(3):
+        _, h = oracle.ffn(OL, xh[t], None)
+        masks_true.append((h != 0).astype(np.uint8))
+        masks_ones.append(np.ones(cfg.ffn, np.uint8))
+    for masks in (masks_true, masks_ones):
+        mk = torch.from_numpy(np.stack(masks)).cuda()
+        y, lists, cnt, _ = _run(ffn, L, x, mask=mk)
+        for t in range(3):
+            y_dense, _ = oracle.ffn(OL, xh[t], None)
+            assert normwise(y[t], y_dense) <= TOL[wd]
+            assert np.array_equal(lists[t], np.nonzero(masks[t])[0])
+
+
+def test_empty_and_full_sets(ffn):
+    cfg = synth.small_config(d=128, ffn=512, rank=16, act="relu", density=0.2, bias_down=True)
+    host = synth.make_layer(cfg)
+    L, OL = to_device(host), oracle_layer(host)
+    x = synth.make_tokens(cfg, 2).cuda()
+    # tau = 1: nothing is active -> y = b_down exactly, count 0
+    y, lists, cnt, _ = _run(ffn, L, x, tau=1.0)
+    assert (cnt == 0).all()
+    assert np.array_equal(y, np.tile(OL["b_down"], (2, 1)))
+    # tau tiny: everything is active -> the dense FFN
+    y, lists, cnt, _ = _run(ffn, L, x, tau=1e-30)
+    assert (cnt == cfg.ffn).all()
+    for t in range(2):
+        y_dense, _ = oracle.ffn(OL, x.cpu().numpy()[t], None)
+        assert normwise(y[t], y_dense) <= TOL["f32"]
+    # an all-zero caller mask
+    mk = torch.zeros(2, cfg.ffn, dtype=torch.uint8, device="cuda")
+    y, lists, cnt, _ = _run(ffn, L, x, mask=mk)
+    assert (cnt == 0).all() and np.array_equal(y, np.tile(OL["b_down"], (2, 1)))
+
+
+def test_fig8_split_additive_on_gpu(ffn):
+    """Partial results over disjoint neuron sets add up to the result over their union."""
+    cfg = synth.small_config(d=64, ffn=256, rank=0, act="relu", density=0.3, bias_up=True)
+    host = synth.make_layer(cfg)
+    L = to_device(host)
+    x = synth.make_tokens(cfg, 1).cuda()
+    rng = np.random.default_rng(3)
+    a = (rng.random(cfg.ffn) < 0.3).astype(np.uint8)
+    b = ((rng.random(cfg.ffn) < 0.3) & (a == 0)).astype(np.uint8)
+    ys = []
+    for m in (a, b, a | b):
+        y, _, _, _ = _run(ffn, L, x, mask=torch.from_numpy(m[None]).cuda())
+        ys.append(y[0].astype(np.float64))
+    assert normwise(ys[0] + ys[1], ys[2]) <= 1e-5
+
+
+def test_batch_equals_single_tokens_and_is_deterministic(ffn):
+    cfg = synth.small_config(d=512, ffn=2048, rank=64, act="reglu", w_dtype="f16",
+                             x_dtype="f16", p_dtype="f16", density=0.1, bias_gate=True)
+    L = to_device(synth.make_layer(cfg))
+    x = synth.make_tokens(cfg, 5).cuda()
+    yb, lb, _, _ = _run(ffn, L, x)
+    yb2, _, _, _ = _run(ffn, L, x)
+    assert np.array_equal(yb, yb2)              # no atomics: bit-reproducible
+    for t in range(5):
+        y1, l1, _, _ = _run(ffn, L, x[t:t + 1])
+        assert np.array_equal(y1[0], yb[t]) and np.array_equal(l1[0], lb[t])
