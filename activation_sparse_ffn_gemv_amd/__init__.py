@@ -23,6 +23,8 @@ FFN_ERR_WORKSPACE_TOO_SMALL, FFN_ERR_HIP, FFN_ERR_INTERNAL = 3, 4, 5
 FFN_ACT_RELU, FFN_ACT_REGLU, FFN_ACT_DRELU = 0, 1, 2
 FFN_F32, FFN_F16, FFN_I4G32 = 0, 1, 2
 FFN_PATH_AUTO, FFN_PATH_SPARSE, FFN_PATH_DENSE = 0, 1, 2
+FFN_STAGE_PRED_Z, FFN_STAGE_PRED_S, FFN_STAGE_GATHER, FFN_STAGE_REDUCE = 0, 1, 2, 3
+STAGES = ("pred_z", "pred_s", "gather", "reduce")
 
 ACT = {"relu": FFN_ACT_RELU, "reglu": FFN_ACT_REGLU, "drelu": FFN_ACT_DRELU}
 DTYPE = {"f32": FFN_F32, "f16": FFN_F16, "i4g32": FFN_I4G32}
@@ -85,7 +87,7 @@ def lib():
         L.ffn_plan_destroy.restype = st
         L.ffn_plan_destroy.argtypes = [P]
         L.ffn_plan_set_timing_events.restype = st
-        L.ffn_plan_set_timing_events.argtypes = [P, P, P]
+        L.ffn_plan_set_timing_events.argtypes = [P, I, P, P]
         L.ffn_moe_workspace_size.restype = st
         L.ffn_moe_workspace_size.argtypes = [I, I, P, ctypes.POINTER(S)]
         L.ffn_moe_plan.restype = st
@@ -142,9 +144,9 @@ def ffn_plan_destroy(plan: int):
     _check(lib().ffn_plan_destroy(plan))
 
 
-def ffn_plan_set_timing_events(plan: int, start: int = 0, stop: int = 0):
+def ffn_plan_set_timing_events(plan: int, stage: int, start: int = 0, stop: int = 0):
     """start / stop: hipEvent_t handles (torch.cuda.Event(enable_timing=True).cuda_event)."""
-    _check(lib().ffn_plan_set_timing_events(plan, start or None, stop or None))
+    _check(lib().ffn_plan_set_timing_events(plan, stage, start or None, stop or None))
 
 
 def ffn_moe_workspace_size(n_experts: int, top_k: int, expert0: int) -> int:

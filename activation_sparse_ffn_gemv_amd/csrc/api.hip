@@ -46,11 +46,9 @@ int cpl_for(int nch) {
   return -1;
 }
 
-constexpr int kTargetChunks = 256;   // one main-kernel workgroup per CU of the MI355X
-
 struct Layout {
-  int nc, n_chunks, cpl_w, cpl_p;
-  size_t off_z, off_ccnt, off_clist, off_part, off_h, off_union, total;
+  int cpl_w, cpl_p;
+  size_t off_z, off_bits, off_cnt, off_part, off_union, total;
 };
 
 ffn_status check_desc(const ffn_layer_desc* d) {
@@ -74,26 +72,26 @@ ffn_status check_desc(const ffn_layer_desc* d) {
   if (d->d % 8 || (d->w_dtype == FFN_I4G32 && d->d % 32))
     return fail(FFN_ERR_UNSUPPORTED, "d must be a multiple of 8 (32 for int4)");
   if (d->d > 8192) return fail(FFN_ERR_UNSUPPORTED, "d > 8192");
-  if (d->ffn % 32) return fail(FFN_ERR_UNSUPPORTED, "ffn must be a multiple of 32");
-  if (d->rank % 8 || d->rank > 4096)
-    return fail(FFN_ERR_UNSUPPORTED, "rank must be a multiple of 8 and <= 4096");
+  if (d->ffn % 32 || d->ffn > 32768)
+    return fail(FFN_ERR_UNSUPPORTED, "ffn must be a multiple of 32 and <= 32768");
+  if (d->rank % 8 || (d->rank > 0 && pred_s_cpr(d->p_dtype == FFN_F16, d->rank) < 0))
+    return fail(FFN_ERR_UNSUPPORTED, "rank must be a multiple of 8 and <= 2048 (fp16) / 1024 (fp32)");
   if (d->max_batch > 4096) return fail(FFN_ERR_UNSUPPORTED, "max_batch > 4096");
   return FFN_OK;
 }
 
+// Workspace of one token in flight (tokens of a batch reuse it one after another):
+// z [rank] f32 | bitmap [ffn/32] u32 | |A| i32 | partials [gather workgroups][d] f32
 Layout layout_for(const ffn_layer_desc* d) {
   Layout L{};
-  L.nc = (d->ffn + kTargetChunks - 1) / kTargetChunks;
-  L.n_chunks = (d->ffn + L.nc - 1) / L.nc;
   L.cpl_w = cpl_for(d->d / elems_per_chunk(d->w_dtype));
   L.cpl_p = d->rank > 0 ? cpl_for(d->d / elems_per_chunk(d->p_dtype)) : 1;
-  const size_t B = (size_t)d->max_batch;
   size_t off = 0;
-  L.off_z = off;      off = round_up(off + B * (size_t)std::max(d->rank, 1) * 4, 256);
-  L.off_ccnt = off;   off = round_up(off + B * (size_t)L.n_chunks * 4, 256);
-  L.off_clist = off;  off = round_up(off + B * (size_t)d->ffn * 4, 256);
-  L.off_part = off;   off = round_up(off + (size_t)L.n_chunks * d->d * 4, 256);
-  L.off_h = off;      off = round_up(off + 256, 256);
+  L.off_z = off;      off = round_up(off + (size_t)std::max(d->rank, 1) * 4, 256);
+  L.off_bits = off;   off = round_up(off + (size_t)d->ffn / 32 * 4, 256);
+  L.off_cnt = off;    off = round_up(off + 4, 256);
+  L.off_part = off;
+  off = round_up(off + (size_t)gather_blocks() * reduce_tiles(d->d) * 16 * 4, 256);
   L.off_union = off;  off = round_up(off + 256, 256);
   L.total = off;
   return L;
@@ -151,15 +149,12 @@ ffn_status ffn_sparse_plan(const ffn_layer_desc* desc, const ffn_layer_weights* 
   p->ws = static_cast<char*>(workspace);
   p->ws_bytes = workspace_bytes;
   Layout L = layout_for(desc);
-  p->nc = L.nc;
-  p->n_chunks = L.n_chunks;
   p->cpl_w = L.cpl_w;
   p->cpl_p = L.cpl_p;
   p->off_z = L.off_z;
-  p->off_ccnt = L.off_ccnt;
-  p->off_clist = L.off_clist;
+  p->off_bits = L.off_bits;
+  p->off_cnt = L.off_cnt;
   p->off_part = L.off_part;
-  p->off_h = L.off_h;
   p->off_union = L.off_union;
   const double tau = desc->threshold;
   p->thr = tau >= 1.0 ? INFINITY : (float)log(tau / (1.0 - tau));
@@ -191,53 +186,66 @@ ffn_status ffn_sparse_forward(ffn_plan* p, const void* x, int32_t B, float* y,
 
   const size_t xbytes = (size_t)D.d * (D.x_dtype == FFN_F32 ? 4 : 2);
   float* z = reinterpret_cast<float*>(p->ws + p->off_z);
-  int* ccnt = reinterpret_cast<int*>(p->ws + p->off_ccnt);
-  int* clist = reinterpret_cast<int*>(p->ws + p->off_clist);
+  uint32_t* bits = reinterpret_cast<uint32_t*>(p->ws + p->off_bits);
   float* part = reinterpret_cast<float*>(p->ws + p->off_part);
   const int wk = D.w_dtype == FFN_F32 ? WK_F32 : D.w_dtype == FFN_F16 ? WK_F16 : WK_I4;
+  const int p_f16 = D.p_dtype == FFN_F16;
 
+  int* ws_cnt = reinterpret_cast<int*>(p->ws + p->off_cnt);
   for (int b = 0; b < B; ++b) {
     const void* xb = static_cast<const char*>(x) + b * xbytes;
     hipError_t e;
-    if (!mask) {
-      e = launch_pred_z(D.p_dtype == FFN_F16, p->cpl_p, p->w.p1, p->w.c1, xb, z, D.d, D.rank, st);
+    if (mask) {
+      e = launch_mask_bits(mask + (size_t)b * D.ffn, bits, D.ffn / 32, st);
+      if (e != hipSuccess) return hip_fail(e, "mask launch");
+    } else {
+      e = launch_pred_z(p_f16, p->cpl_p, p->w.p1, p->w.c1, xb, z, D.d, D.rank, st,
+                        p->ev[FFN_STAGE_PRED_Z][0], p->ev[FFN_STAGE_PRED_Z][1]);
       if (e != hipSuccess) return hip_fail(e, "predictor stage 1 launch");
+      PredArgs pa{};
+      pa.p2 = p->w.p2;
+      pa.c2 = p->w.c2;
+      pa.z = z;
+      pa.scores = scores ? scores + (size_t)b * D.ffn : nullptr;
+      pa.bitmap = bits;
+      pa.ffn = D.ffn;
+      pa.rank = D.rank;
+      pa.thr = p->thr;
+      e = launch_pred_s(p_f16, pa, st, p->ev[FFN_STAGE_PRED_S][0], p->ev[FFN_STAGE_PRED_S][1]);
+      if (e != hipSuccess) return hip_fail(e, "predictor stage 2 launch");
     }
-    MainArgs a{};
-    a.w_up = p->w.w_up;
-    a.w_gate = p->w.w_gate;
-    a.w_dn = p->w.w_down_t;
-    a.s_up = p->w.s_up;
-    a.s_gate = p->w.s_gate;
-    a.s_dn = p->w.s_down_t;
-    a.b_up = p->w.b_up;
-    a.b_gate = p->w.b_gate;
-    a.p2 = p->w.p2;
-    a.c2 = p->w.c2;
-    a.x = xb;
-    a.z = z;
-    a.mask = mask ? mask + (size_t)b * D.ffn : nullptr;
-    a.scores = (scores && !mask) ? scores + (size_t)b * D.ffn : nullptr;
-    a.chunk_cnt = ccnt;
-    a.chunk_list = clist;
-    a.part = part;
-    a.d = D.d;
-    a.ffn = D.ffn;
-    a.rank = D.rank;
-    a.nc = p->nc;
-    a.act = D.act;
-    a.has_gate = D.act != FFN_ACT_RELU;
-    a.p_f16 = D.p_dtype == FFN_F16;
-    a.thr = p->thr;
-    e = launch_main(wk, p->cpl_w, a, p->n_chunks, st, p->t_start, p->t_stop);
-    if (e != hipSuccess) return hip_fail(e, "main kernel launch");
-    e = launch_reduce(part, p->n_chunks, p->w.b_down, y + (size_t)b * D.d, D.d, st);
+    GatherArgs ga{};
+    ga.w_up = p->w.w_up;
+    ga.w_gate = p->w.w_gate;
+    ga.w_dn = p->w.w_down_t;
+    ga.s_up = p->w.s_up;
+    ga.s_gate = p->w.s_gate;
+    ga.s_dn = p->w.s_down_t;
+    ga.b_up = p->w.b_up;
+    ga.b_gate = p->w.b_gate;
+    ga.x = xb;
+    ga.bitmap = bits;
+    ga.part = part;
+    ga.cnt = ws_cnt;
+    ga.d = D.d;
+    ga.ffn = D.ffn;
+    ga.act = D.act;
+    ga.has_gate = D.act != FFN_ACT_RELU;
+    e = launch_gather(wk, ga, st, p->ev[FFN_STAGE_GATHER][0], p->ev[FFN_STAGE_GATHER][1]);
+    if (e != hipSuccess) return hip_fail(e, "gather launch");
+    ReduceArgs ra{};
+    ra.part = part;
+    ra.cnt = ws_cnt;
+    ra.bitmap = bits;
+    ra.b_down = p->w.b_down;
+    ra.y = y + (size_t)b * D.d;
+    ra.idx_out = idx ? idx + (size_t)b * D.ffn : nullptr;
+    ra.cnt_out = cnt ? cnt + b : nullptr;
+    ra.d = D.d;
+    ra.ffn = D.ffn;
+    ra.n_part = gather_blocks();
+    e = launch_reduce(ra, st, p->ev[FFN_STAGE_REDUCE][0], p->ev[FFN_STAGE_REDUCE][1]);
     if (e != hipSuccess) return hip_fail(e, "reduce launch");
-    if (idx || cnt) {
-      e = launch_write_idx(ccnt, clist, p->n_chunks, p->nc, idx ? idx + (size_t)b * D.ffn : nullptr,
-                           cnt ? cnt + b : nullptr, st);
-      if (e != hipSuccess) return hip_fail(e, "index launch");
-    }
   }
   g_err[0] = 0;
   return FFN_OK;
@@ -258,12 +266,14 @@ ffn_status ffn_plan_crossover(const ffn_plan* p, int32_t B, float* density) {
   return FFN_OK;
 }
 
-ffn_status ffn_plan_set_timing_events(ffn_plan* p, void* start, void* stop) {
+ffn_status ffn_plan_set_timing_events(ffn_plan* p, int32_t stage, void* start, void* stop) {
   if (!p) return fail(FFN_ERR_INVALID_ARGUMENT, "plan is NULL");
+  if (stage < FFN_STAGE_PRED_Z || stage > FFN_STAGE_REDUCE)
+    return fail(FFN_ERR_INVALID_ARGUMENT, "stage %d is not an ffn_stage", stage);
   if ((start == nullptr) != (stop == nullptr))
     return fail(FFN_ERR_INVALID_ARGUMENT, "start and stop must both be set or both be NULL");
-  p->t_start = static_cast<hipEvent_t>(start);
-  p->t_stop = static_cast<hipEvent_t>(stop);
+  p->ev[stage][0] = static_cast<hipEvent_t>(start);
+  p->ev[stage][1] = static_cast<hipEvent_t>(stop);
   return FFN_OK;
 }
 

@@ -25,17 +25,69 @@ template <> struct Kind<WK_I4>  { static constexpr int EPC = 32; static constexp
 
 constexpr int WAVE = 64;
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, WAVE);
+// Optional timeline trace (builds with -DFFN_TRACE only): thread 0 of every workgroup stores the
+// 100 MHz real-time counter at a few points of a kernel into trace[(kernel * 4096 + block) * 8 +
+// point].  The buffer is set with ffn_trace_set_buffer (declared in the trace build only).
+#ifdef FFN_TRACE
+extern __device__ unsigned long long* g_trace;
+#define FFN_TS(K, PH)                                                                          \
+  do {                                                                                         \
+    if (threadIdx.x == 0 && g_trace)                                                           \
+      g_trace[((K) * 4096 + blockIdx.x) * 8 + (PH)] = __builtin_amdgcn_s_memrealtime();        \
+  } while (0)
+#define FFN_TV(K, PH, V)                                                                       \
+  do {                                                                                         \
+    if (threadIdx.x == 0 && g_trace) g_trace[((K) * 4096 + blockIdx.x) * 8 + (PH)] = (V);      \
+  } while (0)
+#define FFN_TRACE_SYNC() __syncthreads()
+#else
+#define FFN_TS(K, PH) ((void)0)
+#define FFN_TV(K, PH, V) ((void)0)
+#define FFN_TRACE_SYNC() ((void)0)
+#endif
+
+// DPP lane exchange (gfx9 data-parallel primitives): lanes of rows outside ROW_MASK read 0.
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
+                                                               ROW_MASK, 0xf, false));
+}
+
+// Sum over aligned groups of 16 lanes; every lane of the group gets the sum.
+// quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror, row_mirror.
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp<0xb1>(v);
+  v += dpp<0x4e>(v);
+  v += dpp<0x141>(v);
+  v += dpp<0x140>(v);
   return v;
 }
 
-// Sum over aligned groups of `width` lanes (width a power of two <= 64).
-__device__ __forceinline__ float group_sum(float v, int width) {
-  for (int o = width >> 1; o > 0; o >>= 1) v += __shfl_xor(v, o, WAVE);
+// Sum over the 64 lanes of a wave, returned to every lane (row sums, then row_bcast15 into rows
+// 1 and 3, row_bcast31 into rows 2 and 3: lane 63 holds the total).
+__device__ __forceinline__ float wave_sum(float v) {
+  v = row16_sum(v);
+  v += dpp<0x142, 0xa>(v);
+  v += dpp<0x143, 0xc>(v);
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+
+// Sum over aligned groups of `width` lanes (a power of two, 4 <= width <= 64).  The sum is valid
+// in the last lane of each group (lane % width == width - 1); for width <= 16 in every lane.
+__device__ __forceinline__ float group_sum_last(float v, int width) {
+  v += dpp<0xb1>(v);
+  v += dpp<0x4e>(v);
+  if (width >= 8) v += dpp<0x141>(v);
+  if (width >= 16) v += dpp<0x140>(v);
+  if (width >= 32) v += dpp<0x142, 0xa>(v);
+  if (width >= 64) v += dpp<0x143, 0xc>(v);
   return v;
 }
+
+// Scheduling fence: the compiler may not move instructions across it.  Placed between the
+// instructions that issue a batch of loads and the first use of their results, so that the
+// whole batch is in flight before the wave waits (instead of load / wait / use one by one).
+__device__ __forceinline__ void issue_fence() { __builtin_amdgcn_sched_barrier(0); }
 
 __device__ __forceinline__ u32x4 ld16(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
@@ -116,13 +168,11 @@ struct ffn_plan {
   ffn_layer_weights w;
   char* ws;
   size_t ws_bytes;
-  int nc;            // neurons per chunk (one workgroup of the main kernel per chunk)
-  int n_chunks;
   int cpl_w;         // 16-byte chunks per lane for a weight row
   int cpl_p;         // 16-byte chunks per lane for a predictor P1 row
   float thr;         // logit(threshold): active iff score > thr
-  size_t off_z, off_ccnt, off_clist, off_part, off_h, off_union;
+  size_t off_z, off_bits, off_cnt, off_part, off_union;
   float crossover_density[8];   // per batch bucket 1,2,4,...,128
   int dense_min_batch;          // AUTO takes the dense path from this batch size on
-  hipEvent_t t_start, t_stop;   // instrumentation events attached to the main dispatch
+  hipEvent_t ev[4][2];          // instrumentation events attached to each stage's dispatch
 };

@@ -1,16 +1,20 @@
 // Batch-1 decode path of the activation-sparse FFN on gfx950.
 //
-// Per token and layer, three launches on the caller's stream:
-//   k_pred_z     z = P1 x + c1                                   (predictor stage 1)
-//   k_main       per neuron chunk: s = P2 z + c2, threshold, ballot compaction of the chunk's
-//                active neurons, gathered up/gate rows -> activation -> h, and the transposed
-//                down rows scaled by h, reduced across the workgroup's waves in LDS into one
-//                fp32 partial of y per chunk
-//   k_reduce     y = b_down + sum over chunks of the partials, in a fixed order
-// Nothing is accumulated with global atomics, so y is bit-reproducible run to run.
+// Per token and layer, four launches on the caller's stream; each spreads its bytes evenly over
+// all the CUs (a CU can only keep so many requests in flight, so an uneven split leaves the
+// busiest CU setting the time):
+//   k_pred_z   z = P1 x + c1                            (predictor stage 1; one wave per P1 row)
+//   k_pred_s   s = P2 z + c2, active iff s > logit(tau); one word of the active bitmap per 32
+//              neurons, built with a wave ballot                       (predictor stage 2)
+//   k_gather   256 workgroups split the active neurons evenly by rank; each reads the up, gate
+//              and transposed-down rows of its neurons in one trip (every thread the same column
+//              chunks of every row), forms u, g, h from workgroup-wide sums and adds one
+//              contiguous-row axpy per neuron into its partial of y
+//   k_reduce   y = b_down + sum of the partials, in a fixed order
+// No global atomics anywhere, so y is bit-reproducible run to run.
 //
 // The method (PowerInfer, unite.ai: "Adaptive sparse predictor", "Neuron-aware operator";
-// nearauto.com Fig. 8; citnews.com.cn "Dynamic neuron cache") computes only the predicted
+// nearauto.com Fig. 8; citnews.com.cn "Dynamic neuron cache") reads only the predicted
 // neurons' rows of up / gate and of the transposed down projection.
 #include <hip/hip_ext.h>
 
@@ -19,8 +23,15 @@
 
 namespace ffn {
 
+#ifdef FFN_TRACE
+__device__ unsigned long long* g_trace;
+extern "C" hipError_t ffn_trace_set_buffer(void* p) {
+  return hipMemcpyToSymbol(HIP_SYMBOL(g_trace), &p, sizeof(p));
+}
+#endif
+
 // ---------------------------------------------------------------------------------------------
-// Token slice held in registers: lane `l` owns 16-byte chunks l, l+64, l+128, ... of a row.
+// Token slice held in registers: lane `l` owns 16-byte row chunks l, l+64, l+128, ...
 template <int WK, int CPL>
 struct XRegs {
   u32x4 v[CPL][Kind<WK>::XW];
@@ -30,21 +41,18 @@ template <int WK, int CPL>
 __device__ __forceinline__ void load_x(XRegs<WK, CPL>& xr, const void* x, int nch, int lane) {
 #pragma unroll
   for (int k = 0; k < CPL; ++k) {
-    int c = lane + k * WAVE;
+    const int c = lane + k * WAVE;
+    const int cc = min(c, nch - 1);           // clamped: loads are never predicated
 #pragma unroll
     for (int q = 0; q < Kind<WK>::XW; ++q) {
-      if (c < nch) {
-        // fp32 / fp16 tokens: 16 bytes per chunk.  int4 rows: 32 fp16 token values per chunk.
-        xr.v[k][q] = ld16(static_cast<const char*>(x) + (size_t)c * 16 * Kind<WK>::XW + q * 16);
-      } else {
-        xr.v[k][q] = u32x4{0u, 0u, 0u, 0u};
-      }
+      // fp32 / fp16 rows: 16 token bytes per chunk.  int4 rows: 32 fp16 token values per chunk.
+      const u32x4 v = ld16(static_cast<const char*>(x) + (size_t)cc * 16 * Kind<WK>::XW + q * 16);
+      xr.v[k][q] = c < nch ? v : u32x4{0u, 0u, 0u, 0u};
     }
     if constexpr (WK == WK_I4) i4_perm_x(xr.v[k]);
   }
 }
 
-// Dot product of one weight row with the register-resident token (partial per lane).
 template <int WK, int CPL>
 __device__ __forceinline__ float row_dot(const u32x4 (&w)[CPL], const float (&sc)[CPL],
                                          const XRegs<WK, CPL>& xr) {
@@ -61,285 +69,463 @@ __device__ __forceinline__ float row_dot(const u32x4 (&w)[CPL], const float (&sc
 template <int WK, int CPL>
 __device__ __forceinline__ void load_row(u32x4 (&w)[CPL], float (&sc)[CPL], const void* base,
                                          const void* scales, size_t row, int nch, int lane) {
+  // Chunks past the row end (ragged d) re-read the last chunk and meet a zero token slice.
   const char* rp = static_cast<const char*>(base) + row * (size_t)nch * 16;
 #pragma unroll
   for (int k = 0; k < CPL; ++k) {
-    int c = lane + k * WAVE;
-    w[k] = c < nch ? ld16(rp + (size_t)c * 16) : u32x4{0u, 0u, 0u, 0u};
+    const int cc = min(lane + k * WAVE, nch - 1);
+    w[k] = ld16(rp + (size_t)cc * 16);
     if constexpr (WK == WK_I4) {
       const _Float16* sp = static_cast<const _Float16*>(scales) + row * (size_t)nch;
-      sc[k] = c < nch ? (float)sp[c] : 0.0f;
+      sc[k] = (float)sp[cc];
     } else {
       sc[k] = 0.0f;
     }
   }
 }
 
-// acc[k][e] += h * w (row chunk k, element e); int4 elements are decoded exactly (scale * q).
-template <int WK, int CPL>
-__device__ __forceinline__ void axpy_row(float (&acc)[CPL][Kind<WK>::EPC], float h,
-                                         const u32x4 (&w)[CPL], const float (&sc)[CPL]) {
-#pragma unroll
-  for (int k = 0; k < CPL; ++k) {
-    if constexpr (WK == WK_F32) {
-      f32x4 a = __builtin_bit_cast(f32x4, w[k]);
-      acc[k][0] = __builtin_fmaf(h, a.x, acc[k][0]);
-      acc[k][1] = __builtin_fmaf(h, a.y, acc[k][1]);
-      acc[k][2] = __builtin_fmaf(h, a.z, acc[k][2]);
-      acc[k][3] = __builtin_fmaf(h, a.w, acc[k][3]);
-    } else if constexpr (WK == WK_F16) {
-      uint32_t ww[4] = {w[k].x, w[k].y, w[k].z, w[k].w};
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        acc[k][2 * q] = __builtin_fmaf(h, h_lo(ww[q]), acc[k][2 * q]);
-        acc[k][2 * q + 1] = __builtin_fmaf(h, h_hi(ww[q]), acc[k][2 * q + 1]);
-      }
-    } else {
-      float hs = h * sc[k];
-      uint32_t ww[4] = {w[k].x, w[k].y, w[k].z, w[k].w};
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-#pragma unroll
-        for (int b = 0; b < 8; ++b) {
-          int nib = (ww[q] >> (4 * b)) & 0xF;
-          int qv = nib >= 8 ? nib - 16 : nib;
-          acc[k][8 * q + b] = __builtin_fmaf(hs, (float)qv, acc[k][8 * q + b]);
-        }
-      }
-    }
-  }
-}
-
 // ---------------------------------------------------------------------------------------------
-// Predictor stage 1: one wave per row of P1.  z[k] = c1[k] + P1[k] . x
+// Predictor stage 1: one 64-thread workgroup per row of P1.  z[k] = c1[k] + P1[k] . x
 template <int PK, int CPL>
-__global__ __launch_bounds__(256) void k_pred_z(const void* __restrict__ p1,
-                                                const float* __restrict__ c1,
-                                                const void* __restrict__ x,
-                                                float* __restrict__ z, int d, int rank) {
-  const int lane = threadIdx.x & (WAVE - 1);
-  const int row = blockIdx.x * (blockDim.x / WAVE) + (threadIdx.x / WAVE);
-  if (row >= rank) return;
+__global__ __launch_bounds__(64) void k_pred_z(const void* __restrict__ p1,
+                                               const float* __restrict__ c1,
+                                               const void* __restrict__ x,
+                                               float* __restrict__ z, int d, int rank) {
+  FFN_TS(0, 0);
+  const int lane = threadIdx.x;
+  const int row = blockIdx.x;
   const int nch = d / Kind<PK>::EPC;
   XRegs<PK, CPL> xr;
   load_x<PK, CPL>(xr, x, nch, lane);
   u32x4 w[CPL];
   float sc[CPL];
   load_row<PK, CPL>(w, sc, p1, nullptr, row, nch, lane);
-  float acc = wave_sum(row_dot<PK, CPL>(w, sc, xr));
+  issue_fence();
+  const float acc = wave_sum(row_dot<PK, CPL>(w, sc, xr));
+  FFN_TS(0, 1);
   if (lane == 0) z[row] = acc + (c1 ? c1[row] : 0.0f);
+  FFN_TS(0, 2);
 }
 
 // ---------------------------------------------------------------------------------------------
-// Main kernel.  Workgroup = one chunk of `nc` consecutive neurons; MW waves.
-// Waves per workgroup: 8, or 4 when the token, three rows and the accumulators of a wave need
-// more than the 256 registers a lane gets at two waves per SIMD.
-constexpr int waves_for(int cpl) { return cpl >= 12 ? 4 : 8; }
-int main_waves(int cpl) { return waves_for(cpl); }
+// Predictor stage 2 + threshold + bitmap.  Workgroup of 256 threads = 32 neurons = one word of
+// the active bitmap.  A P2 row (rank values) is split over L lanes (L = next power of two >= its
+// 16-byte chunk count, 4..64; CPR chunks per lane beyond 64 chunks); all passes' loads are issued
+// before any is used.
+constexpr int PS_THREADS = 256;
+constexpr int PS_MAXP = 8;
 
-template <int WK, int CPL, int MAIN_WAVES>
-__global__ __launch_bounds__(MAIN_WAVES * WAVE) void k_main(MainArgs a) {
-  extern __shared__ float smem[];
-  // LDS layout: acc[d] | z[rank] | score[nc] | h[nc] | list[nc] | count
-  float* s_acc = smem;
-  float* s_z = s_acc + a.d;
-  float* s_score = s_z + a.rank;
-  float* s_h = s_score + a.nc;
-  int* s_list = reinterpret_cast<int*>(s_h + a.nc);
-  int* s_m = s_list + a.nc;
-
+template <int PK, int CPR>
+__global__ __launch_bounds__(PS_THREADS) void k_pred_s(PredArgs a) {
+  constexpr int PE = Kind<PK>::EPC;           // predictor elements per 16-byte chunk
+  __shared__ float s_score[32];
   const int tid = threadIdx.x;
-  const int lane = tid & (WAVE - 1);
-  const int wave = tid / WAVE;
-  const int chunk = blockIdx.x;
-  const int i0 = chunk * a.nc;
-  const int n = min(a.nc, a.ffn - i0);
-  const int nch = a.d / Kind<WK>::EPC;
-
-  // Token in registers (every wave needs all of it).
-  XRegs<WK, CPL> xr;
-  load_x<WK, CPL>(xr, a.x, nch, lane);
-
-  for (int j = tid; j < a.d; j += blockDim.x) s_acc[j] = 0.0f;
-
-  if (a.mask == nullptr) {
-    // ---- predictor stage 2 over this chunk's neurons
-    for (int k = tid; k < a.rank; k += blockDim.x) s_z[k] = a.z[k];
-    __syncthreads();
-    const int pe = a.p_f16 ? 8 : 4;                 // P2 elements per 16-byte chunk
-    const int pch = a.rank / pe;                    // 16-byte chunks per P2 row
-    int L = 64;                                     // lanes per row: next pow2 >= pch, <= 64
-    while (L > 1 && (L >> 1) >= pch) L >>= 1;
-    const int rpw = WAVE / L;                       // rows per wave per pass
-    const int g = lane / L, gl = lane % L;
-    for (int base = wave * rpw; base < n; base += MAIN_WAVES * rpw) {
-      const int r = base + g;
-      float acc = 0.0f;
-      if (r < n) {
-        const char* rp = static_cast<const char*>(a.p2) + (size_t)(i0 + r) * a.rank * (a.p_f16 ? 2 : 4);
-        for (int c = gl; c < pch; c += L) {
-          u32x4 w = ld16(rp + (size_t)c * 16);
-          const float* zp = s_z + c * pe;
-          if (a.p_f16) {
-            uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+  const int pch = a.rank / PE;
+  int L = 64;
+  while (L > 4 && (L >> 1) >= pch) L >>= 1;
+  const int R = PS_THREADS / L;               // rows per pass
+  const int P = (32 + R - 1) / R;             // passes (<= 8)
+  const int g = tid / L, gl = tid % L;
+  const int i0 = blockIdx.x * 32;
+  FFN_TS(1, 0);
+  const float c2v = (tid < 32 && a.c2) ? a.c2[i0 + tid] : 0.0f;
+  f32x4 zr[CPR][PE / 4];                      // this lane's z slice, fixed across rows
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              acc = __builtin_fmaf(h_lo(ww[q]), zp[2 * q], acc);
-              acc = __builtin_fmaf(h_hi(ww[q]), zp[2 * q + 1], acc);
+  for (int k = 0; k < CPR; ++k) {
+    const int c = gl + k * L;
+    const int cc = min(c, pch - 1);
+#pragma unroll
+    for (int q = 0; q < PE / 4; ++q) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(a.z + cc * PE + 4 * q);
+      zr[k][q] = c < pch ? v : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+  u32x4 w[PS_MAXP][CPR];
+#pragma unroll
+  for (int p = 0; p < PS_MAXP; ++p) {
+    const int r = min(p * R + g, 31);
+#pragma unroll
+    for (int k = 0; k < CPR; ++k) {
+      const int cc = min(gl + k * L, pch - 1);
+      if (p < P) w[p][k] = ld16(static_cast<const char*>(a.p2) + ((size_t)(i0 + r) * pch + cc) * 16);
+    }
+  }
+  issue_fence();
+#pragma unroll
+  for (int p = 0; p < PS_MAXP; ++p) {
+    if (p >= P) break;
+    float acc = 0.0f;
+#pragma unroll
+    for (int k = 0; k < CPR; ++k) {
+      if (gl + k * L >= pch) continue;        // lane past the row end (small ranks)
+      const float* zf = reinterpret_cast<const float*>(&zr[k][0]);
+      if constexpr (PK == WK_F16) {
+        const uint32_t ww[4] = {w[p][k].x, w[p][k].y, w[p][k].z, w[p][k].w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          acc = __builtin_fmaf(h_lo(ww[q]), zf[2 * q], acc);
+          acc = __builtin_fmaf(h_hi(ww[q]), zf[2 * q + 1], acc);
+        }
+      } else {
+        const f32x4 wf = __builtin_bit_cast(f32x4, w[p][k]);
+        acc = __builtin_fmaf(wf.x, zf[0], acc);
+        acc = __builtin_fmaf(wf.y, zf[1], acc);
+        acc = __builtin_fmaf(wf.z, zf[2], acc);
+        acc = __builtin_fmaf(wf.w, zf[3], acc);
+      }
+    }
+    acc = group_sum_last(acc, L);
+    const int r = p * R + g;
+    if (gl == L - 1 && r < 32) s_score[r] = acc;
+  }
+  __syncthreads();
+  if (tid < WAVE) {
+    bool on = false;
+    if (tid < 32) {
+      const float sc = s_score[tid] + c2v;
+      on = sc > a.thr;
+      if (a.scores) a.scores[i0 + tid] = sc;
+    }
+    const unsigned long long bal = __ballot(on);
+    if (tid == 0) a.bitmap[blockIdx.x] = (uint32_t)bal;
+  }
+  FFN_TS(1, 5);
+}
+
+// Caller-supplied mask -> bitmap: one wave builds two 32-bit words.
+__global__ __launch_bounds__(256) void k_mask_bits(const unsigned char* __restrict__ mask,
+                                                   uint32_t* __restrict__ bitmap, int words) {
+  const int w = blockIdx.x * 4 + threadIdx.x / WAVE;
+  const int lane = threadIdx.x & (WAVE - 1);
+  const int word = w * 2 + (lane >> 5);
+  const bool on = word < words && mask[(size_t)word * 32 + (lane & 31)] != 0;
+  const unsigned long long bal = __ballot(on);
+  if (lane == 0 && word < words) bitmap[word] = (uint32_t)bal;
+  if (lane == 32 && word < words) bitmap[word] = (uint32_t)(bal >> 32);
+}
+
+// ---------------------------------------------------------------------------------------------
+// Balanced gather.  GA_BLOCKS workgroups of 512 threads split the active neurons evenly by
+// rank: workgroup g owns ranks [g*|A|/G, (g+1)*|A|/G).
+//   1. the bitmap (two words per thread) is prefix-summed over the workgroup; the threads whose
+//      words hold the workgroup's ranks write those neurons to an LDS list;
+//   2. rounds of up to RN neurons: thread t owns the 16-byte column chunks t, t + 512, ... of
+//      every row; it requests its chunks of the up, gate and transposed-down rows of all the
+//      round's neurons at once, forms partial dot products with its slice of the token; the
+//      partials are summed over the workgroup (DPP wave sums, then the waves in order) into
+//      u, g and h; each thread adds h * (its down chunks) to its own accumulator: one
+//      contiguous-row axpy per active neuron;
+//   3. the accumulators are the workgroup's partial of y (written only when it owns a rank).
+// Every workgroup and every thread does the same work, so the load is even over the CUs.
+constexpr int GA_THREADS = 512;
+constexpr int GA_NW = GA_THREADS / WAVE;
+constexpr int GA_BLOCKS = 256;
+constexpr int RD_TW = 16;             // columns per reduce tile (64 bytes of every partial)
+constexpr int GA_MAXW = 2;            // bitmap words per thread: ffn <= 32768
+constexpr int GA_LIST = 64;           // ranks resolved per batch
+
+template <int WK, int CPT> struct Round { static constexpr int RN = WK == WK_I4 ? 8 : 16 / CPT; };
+
+template <int WK, int CPT>
+__global__ __launch_bounds__(GA_THREADS) void k_gather(GatherArgs a) {
+  constexpr int NT = GA_THREADS;
+  constexpr int RN = Round<WK, CPT>::RN;
+  constexpr int EPC = Kind<WK>::EPC;
+  __shared__ int s_wsum[GA_NW];
+  __shared__ int s_list[GA_LIST];
+  __shared__ float s_red[GA_NW][2 * RN];
+  __shared__ float s_h[RN];
+  const int tid = threadIdx.x;
+  const int lane = tid & (WAVE - 1), wave = tid / WAVE;
+  const int nch = a.d / EPC;
+  FFN_TS(1, 0);
+
+  // this thread's chunks of the token (chunk tid + k*NT)
+  u32x4 xr[CPT][Kind<WK>::XW];
+#pragma unroll
+  for (int k = 0; k < CPT; ++k) {
+    const int c = tid + k * NT;
+    const int cc = min(c, nch - 1);
+#pragma unroll
+    for (int q = 0; q < Kind<WK>::XW; ++q) {
+      const u32x4 v = ld16(static_cast<const char*>(a.x) + (size_t)cc * 16 * Kind<WK>::XW + q * 16);
+      xr[k][q] = c < nch ? v : u32x4{0u, 0u, 0u, 0u};
+    }
+    if constexpr (WK == WK_I4) i4_perm_x(xr[k]);
+  }
+
+  // 1. word prefix of the bitmap: thread t owns words 2t, 2t+1 (consecutive)
+  const int words = a.ffn / 32;
+  uint32_t b[GA_MAXW];
+  int local = 0;
+#pragma unroll
+  for (int k = 0; k < GA_MAXW; ++k) {
+    const int w = tid * GA_MAXW + k;
+    b[k] = w < words ? a.bitmap[w] : 0u;
+    local += __popc(b[k]);
+  }
+  int v = local;
+#pragma unroll
+  for (int o = 1; o < WAVE; o <<= 1) {
+    const int u = __shfl_up(v, o, WAVE);
+    if (lane >= o) v += u;
+  }
+  if (lane == WAVE - 1) s_wsum[wave] = v;
+  __syncthreads();
+  int base = 0, total = 0;
+#pragma unroll
+  for (int k = 0; k < GA_NW; ++k) {
+    base += k < wave ? s_wsum[k] : 0;
+    total += s_wsum[k];
+  }
+  const int run0 = base + v - local;           // rank of this thread's first active neuron
+  if (blockIdx.x == 0 && tid == 0) *a.cnt = total;
+  const int r0 = (int)(((long long)total * blockIdx.x) / gridDim.x);
+  const int r1 = (int)(((long long)total * (blockIdx.x + 1)) / gridDim.x);
+  FFN_TS(1, 1);
+
+  float acc[CPT][EPC];
+#pragma unroll
+  for (int k = 0; k < CPT; ++k)
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) acc[k][e] = 0.0f;
+
+  for (int l0 = r0; l0 < r1; l0 += GA_LIST) {
+    const int nl = min(GA_LIST, r1 - l0);
+    // owners of ranks [l0, l0 + nl): every thread whose words hold some of them writes those
+    // (no search: a thread knows the ranks of its own active neurons)
+    if (run0 < l0 + nl && run0 + local > l0) {
+      int pos = run0;
+#pragma unroll
+      for (int k = 0; k < GA_MAXW; ++k) {
+        uint32_t bb = b[k];
+        const int nbase = (tid * GA_MAXW + k) * 32;
+        while (bb) {
+          if (pos >= l0 && pos < l0 + nl) s_list[pos - l0] = nbase + __builtin_ctz(bb);
+          bb &= bb - 1;
+          ++pos;
+        }
+      }
+    }
+    __syncthreads();
+    FFN_TS(1, 2);
+    for (int t0 = 0; t0 < nl; t0 += RN) {
+      u32x4 wu[RN][CPT], wg[RN][CPT], wd[RN][CPT];
+      float su[RN][CPT], sg[RN][CPT], sd[RN][CPT];
+#pragma unroll
+      for (int r = 0; r < RN; ++r) {
+        const bool live_r = t0 + r < nl;                     // uniform across the workgroup
+        const size_t nr = (size_t)s_list[min(t0 + r, nl - 1)];
+#pragma unroll
+        for (int k = 0; k < CPT; ++k) {
+          const int cc = min(tid + k * NT, nch - 1);
+          const size_t off = (nr * nch + cc) * 16;
+          wu[r][k] = wg[r][k] = wd[r][k] = u32x4{0u, 0u, 0u, 0u};
+          su[r][k] = sg[r][k] = sd[r][k] = 0.0f;
+          if (live_r) {
+            wu[r][k] = ld16(static_cast<const char*>(a.w_up) + off);
+            if (a.has_gate) wg[r][k] = ld16(static_cast<const char*>(a.w_gate) + off);
+            wd[r][k] = ld16(static_cast<const char*>(a.w_dn) + off);
+            if constexpr (WK == WK_I4) {
+              su[r][k] = (float)static_cast<const _Float16*>(a.s_up)[nr * nch + cc];
+              if (a.has_gate) sg[r][k] = (float)static_cast<const _Float16*>(a.s_gate)[nr * nch + cc];
+              sd[r][k] = (float)static_cast<const _Float16*>(a.s_dn)[nr * nch + cc];
             }
-          } else {
-            f32x4 wf = __builtin_bit_cast(f32x4, w);
-            acc = __builtin_fmaf(wf.x, zp[0], acc);
-            acc = __builtin_fmaf(wf.y, zp[1], acc);
-            acc = __builtin_fmaf(wf.z, zp[2], acc);
-            acc = __builtin_fmaf(wf.w, zp[3], acc);
           }
         }
       }
-      acc = group_sum(acc, L);
-      if (r < n && gl == 0) {
-        float s = acc + (a.c2 ? a.c2[i0 + r] : 0.0f);
-        s_score[r] = s;
-        if (a.scores) a.scores[i0 + r] = s;
+      issue_fence();
+#pragma unroll
+      for (int r = 0; r < RN; ++r) {
+        float pu = 0.0f, pg = 0.0f;
+#pragma unroll
+        for (int k = 0; k < CPT; ++k) {
+          if constexpr (WK == WK_F32) {
+            pu = dot4_f32(wu[r][k], xr[k][0], pu);
+            if (a.has_gate) pg = dot4_f32(wg[r][k], xr[k][0], pg);
+          } else if constexpr (WK == WK_F16) {
+            pu = dot8_f16(wu[r][k], xr[k][0], pu);
+            if (a.has_gate) pg = dot8_f16(wg[r][k], xr[k][0], pg);
+          } else {
+            pu = dot32_i4(wu[r][k], xr[k], su[r][k], pu);
+            if (a.has_gate) pg = dot32_i4(wg[r][k], xr[k], sg[r][k], pg);
+          }
+        }
+        if (t0 + r < nl) {                                   // uniform across the workgroup
+          pu = wave_sum(pu);
+          if (a.has_gate) pg = wave_sum(pg);
+          if (lane == 0) {
+            s_red[wave][2 * r] = pu;
+            s_red[wave][2 * r + 1] = pg;
+          }
+        }
       }
-    }
-    __syncthreads();
-    // ---- compaction: ascending local list of neurons with score > thr (wave 0, ballots)
-    if (wave == 0) {
-      int m = 0;
-      for (int b = 0; b < n; b += WAVE) {
-        const int r = b + lane;
-        const bool on = r < n && s_score[r] > a.thr;
-        const unsigned long long bal = __ballot(on);
-        const int pos = m + __popcll(bal & ((1ull << lane) - 1ull));
-        if (on) s_list[pos] = i0 + r;
-        m += __popcll(bal);
+      __syncthreads();
+      if (tid < RN) {
+        float u = 0.0f, g = 0.0f, h = 0.0f;
+        if (t0 + tid < nl) {
+#pragma unroll
+          for (int w = 0; w < GA_NW; ++w) {
+            u += s_red[w][2 * tid];
+            g += s_red[w][2 * tid + 1];
+          }
+          const int nr = s_list[t0 + tid];
+          u += a.b_up ? a.b_up[nr] : 0.0f;
+          if (a.act == FFN_ACT_RELU) {
+            h = fmaxf(u, 0.0f);
+          } else {
+            g = fmaxf(g + (a.b_gate ? a.b_gate[nr] : 0.0f), 0.0f);
+            h = a.act == FFN_ACT_REGLU ? g * u : g * fmaxf(u, 0.0f);
+          }
+        }
+        s_h[tid] = h;                                        // 0 for slots past the list
       }
-      if (lane == 0) *s_m = m;
-    }
-  } else {
-    // ---- caller's mask replaces the predictor
-    if (wave == 0) {
-      int m = 0;
-      for (int b = 0; b < n; b += WAVE) {
-        const int r = b + lane;
-        const bool on = r < n && a.mask[i0 + r] != 0;
-        const unsigned long long bal = __ballot(on);
-        const int pos = m + __popcll(bal & ((1ull << lane) - 1ull));
-        if (on) s_list[pos] = i0 + r;
-        m += __popcll(bal);
+      __syncthreads();
+      FFN_TS(1, 3);
+#pragma unroll
+      for (int r = 0; r < RN; ++r) {
+        const float h = s_h[r];
+#pragma unroll
+        for (int k = 0; k < CPT; ++k) {
+          if constexpr (WK == WK_F32) {
+            const f32x4 q = __builtin_bit_cast(f32x4, wd[r][k]);
+            acc[k][0] = __builtin_fmaf(h, q.x, acc[k][0]);
+            acc[k][1] = __builtin_fmaf(h, q.y, acc[k][1]);
+            acc[k][2] = __builtin_fmaf(h, q.z, acc[k][2]);
+            acc[k][3] = __builtin_fmaf(h, q.w, acc[k][3]);
+          } else if constexpr (WK == WK_F16) {
+            const uint32_t ww[4] = {wd[r][k].x, wd[r][k].y, wd[r][k].z, wd[r][k].w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              acc[k][2 * q] = __builtin_fmaf(h, h_lo(ww[q]), acc[k][2 * q]);
+              acc[k][2 * q + 1] = __builtin_fmaf(h, h_hi(ww[q]), acc[k][2 * q + 1]);
+            }
+          } else {
+            const float hs = h * sd[r][k];
+            const uint32_t ww[4] = {wd[r][k].x, wd[r][k].y, wd[r][k].z, wd[r][k].w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+              for (int bb = 0; bb < 8; ++bb)
+                acc[k][8 * q + bb] = __builtin_fmaf(hs, (float)((int)(ww[q] << (28 - 4 * bb)) >> 28),
+                                                    acc[k][8 * q + bb]);
+          }
+        }
       }
-      if (lane == 0) *s_m = m;
+      __syncthreads();                                       // s_red / s_h reused
     }
   }
-  __syncthreads();
-  const int m = *s_m;
-  if (tid == 0) a.chunk_cnt[chunk] = m;
-  for (int k = tid; k < m; k += blockDim.x) a.chunk_list[i0 + k] = s_list[k];
-
-  // ---- gathered rows: wave w takes active neurons w, w + MW, ...  Up, gate and down rows of a
-  // neuron are all requested before any of them is used.
-  float acc[CPL][Kind<WK>::EPC];
+  if (r1 > r0) {
+    // partial of y, tile-major: part[col / RD_TW][workgroup][col % RD_TW], so that the reduce
+    // reads one contiguous block per tile
 #pragma unroll
-  for (int k = 0; k < CPL; ++k)
+    for (int k = 0; k < CPT; ++k) {
+      const int c = tid + k * NT;
+      if (c < nch) {
 #pragma unroll
-    for (int e = 0; e < Kind<WK>::EPC; ++e) acc[k][e] = 0.0f;
-
-  for (int t = wave; t < m; t += MAIN_WAVES) {
-    const size_t i = (size_t)s_list[t];
-    u32x4 wu[CPL], wg[CPL], wd[CPL];
-    float su[CPL], sg[CPL], sd[CPL];
-    load_row<WK, CPL>(wu, su, a.w_up, a.s_up, i, nch, lane);
-    if (a.has_gate) load_row<WK, CPL>(wg, sg, a.w_gate, a.s_gate, i, nch, lane);
-    load_row<WK, CPL>(wd, sd, a.w_dn, a.s_dn, i, nch, lane);
-    float u = wave_sum(row_dot<WK, CPL>(wu, su, xr)) + (a.b_up ? a.b_up[i] : 0.0f);
-    float h;
-    if (a.act == FFN_ACT_RELU) {
-      h = fmaxf(u, 0.0f);
-    } else {
-      float gv = wave_sum(row_dot<WK, CPL>(wg, sg, xr)) + (a.b_gate ? a.b_gate[i] : 0.0f);
-      float gr = fmaxf(gv, 0.0f);
-      h = a.act == FFN_ACT_REGLU ? gr * u : gr * fmaxf(u, 0.0f);
-    }
-    axpy_row<WK, CPL>(acc, h, wd, sd);
-  }
-
-  // ---- cross-wave reduction in LDS, fixed wave order, then one partial row per chunk
-  const int active_waves = min(m, MAIN_WAVES);
-  for (int w = 0; w < active_waves; ++w) {
-    __syncthreads();
-    if (wave == w) {
-#pragma unroll
-      for (int k = 0; k < CPL; ++k) {
-        const int c = lane + k * WAVE;
-        if (c < nch) {
-#pragma unroll
-          for (int e = 0; e < Kind<WK>::EPC; ++e) s_acc[c * Kind<WK>::EPC + e] += acc[k][e];
+        for (int e = 0; e < EPC; e += 4) {
+          const int col = c * EPC + e;
+          float* dst = a.part + ((size_t)(col / RD_TW) * GA_BLOCKS + blockIdx.x) * RD_TW +
+                       col % RD_TW;
+          // streaming store: the partial is read once, by the next kernel
+          __builtin_nontemporal_store(f32x4{acc[k][e], acc[k][e + 1], acc[k][e + 2], acc[k][e + 3]},
+                                      reinterpret_cast<f32x4*>(dst));
         }
       }
     }
   }
-  __syncthreads();
-  float* prow = a.part + (size_t)chunk * a.d;
-  for (int j = tid * 4; j < a.d; j += blockDim.x * 4)
-    *reinterpret_cast<f32x4*>(prow + j) = *reinterpret_cast<const f32x4*>(s_acc + j);
+  FFN_TRACE_SYNC();
+  FFN_TS(1, 5);
+  FFN_TV(1, 6, r1 - r0);
 }
 
 // ---------------------------------------------------------------------------------------------
-// y[j] = b_down[j] + sum_c part[c][j].  Block = 64 columns x 16 chunk groups.
-__global__ __launch_bounds__(256) void k_reduce(const float* __restrict__ part, int n_chunks,
-                                                const float* __restrict__ b_down,
-                                                float* __restrict__ y, int d) {
-  __shared__ f32x4 s[16][16];
-  const int q = threadIdx.x & 15;        // float4 column within the tile
-  const int cg = threadIdx.x >> 4;       // chunk group
-  const int j = (blockIdx.x * 16 + q) * 4;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  if (j < d) {
-    for (int c = cg; c < n_chunks; c += 16)
-      acc += *reinterpret_cast<const f32x4*>(part + (size_t)c * d + j);
-  }
-  s[cg][q] = acc;
-  __syncthreads();
-  if (cg == 0 && j < d) {
-    f32x4 t = s[0][q];
+// y = b_down + sum of the gather partials, in workgroup order.  Workgroup j owns the RD_TW
+// columns of tile j; the partials are stored tile-major, so it reads one contiguous block of
+// GA_BLOCKS * RD_TW floats (every thread four 16-byte pieces at once).  Partials of gather
+// workgroups that owned no rank were not written and are skipped (their ranges follow from |A|).
+// Workgroup 0 also writes the ascending index list and the count when the caller asks for them.
+constexpr int RD_THREADS = 256;
+constexpr int RD_Q = RD_TW / 4;                        // float4 columns per tile
+constexpr int RD_G = RD_THREADS / RD_Q;                // partial groups
+constexpr int RD_UNROLL = GA_BLOCKS / RD_G;
+static_assert(GA_BLOCKS % RD_G == 0, "whole partial groups");
+
+__device__ void write_index_list(const uint32_t* __restrict__ bitmap, int words,
+                                 int* __restrict__ idx_out, int* __restrict__ cnt_out) {
+  __shared__ int s_ws[RD_THREADS / WAVE];
+  const int tid = threadIdx.x, lane = tid & (WAVE - 1), wave = tid / WAVE;
+  int before = 0;
+  for (int w0 = 0; w0 < words; w0 += RD_THREADS) {
+    const int w = w0 + tid;
+    const uint32_t b = w < words ? bitmap[w] : 0u;
+    const int c = __popc(b);
+    int v = c;
 #pragma unroll
-    for (int k = 1; k < 16; ++k) t += s[k][q];
-    if (b_down) t += *reinterpret_cast<const f32x4*>(b_down + j);
-    *reinterpret_cast<f32x4*>(y + j) = t;
+    for (int o = 1; o < WAVE; o <<= 1) {
+      const int u = __shfl_up(v, o, WAVE);
+      if (lane >= o) v += u;
+    }
+    __syncthreads();
+    if (lane == WAVE - 1) s_ws[wave] = v;
+    __syncthreads();
+    int base = before, tot = 0;
+    for (int k = 0; k < RD_THREADS / WAVE; ++k) {
+      base += k < wave ? s_ws[k] : 0;
+      tot += s_ws[k];
+    }
+    if (idx_out) {
+      int pos = base + v - c;
+      uint32_t bb = b;
+      while (bb) {
+        idx_out[pos++] = w * 32 + __builtin_ctz(bb);
+        bb &= bb - 1;
+      }
+    }
+    before += tot;
   }
+  if (tid == 0 && cnt_out) *cnt_out = before;
 }
 
-// Global ascending index list from the per-chunk lists (test hook; not on the timed path).
-__global__ __launch_bounds__(256) void k_write_idx(const int* __restrict__ ccnt,
-                                                   const int* __restrict__ clist, int n_chunks,
-                                                   int nc, int* __restrict__ idx,
-                                                   int* __restrict__ cnt) {
-  __shared__ int s_off;
-  const int chunk = blockIdx.x;
-  if (threadIdx.x == 0) {
-    int off = 0;
-    for (int c = 0; c < chunk; ++c) off += ccnt[c];
-    s_off = off;
-    if (chunk == n_chunks - 1 && cnt) *cnt = off + ccnt[chunk];
+__global__ __launch_bounds__(RD_THREADS) void k_reduce(ReduceArgs a) {
+  __shared__ f32x4 s[RD_G][RD_Q];
+  const int q = threadIdx.x % RD_Q;          // float4 column within the tile
+  const int g = threadIdx.x / RD_Q;          // partials g, g + RD_G, ...
+  const int tile = blockIdx.x;
+  FFN_TS(2, 0);
+  const int total = *a.cnt;
+  const float* blk = a.part + (size_t)tile * GA_BLOCKS * RD_TW;
+  f32x4 v[RD_UNROLL];
+  bool on[RD_UNROLL];
+#pragma unroll
+  for (int u = 0; u < RD_UNROLL; ++u) {
+    const int c = g + u * RD_G;
+    // partial c exists iff gather workgroup c owned at least one rank
+    on[u] = ((long long)total * (c + 1)) / GA_BLOCKS > ((long long)total * c) / GA_BLOCKS;
+    v[u] = *reinterpret_cast<const f32x4*>(blk + (size_t)c * RD_TW + q * 4);
   }
+  issue_fence();
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int u = 0; u < RD_UNROLL; ++u)
+    if (on[u]) acc += v[u];
+  s[g][q] = acc;
   __syncthreads();
-  const int m = ccnt[chunk];
-  if (idx)
-    for (int k = threadIdx.x; k < m; k += blockDim.x) idx[s_off + k] = clist[chunk * nc + k];
+  const int j = tile * RD_TW + threadIdx.x * 4;
+  if (threadIdx.x < RD_Q && j < a.d) {
+    f32x4 t = s[0][threadIdx.x];
+#pragma unroll 8
+    for (int k = 1; k < RD_G; ++k) t += s[k][threadIdx.x];
+    if (a.b_down) t += *reinterpret_cast<const f32x4*>(a.b_down + j);
+    *reinterpret_cast<f32x4*>(a.y + j) = t;
+  }
+  if (blockIdx.x == 0 && (a.idx_out || a.cnt_out))
+    write_index_list(a.bitmap, a.ffn / 32, a.idx_out, a.cnt_out);
+  FFN_TS(2, 5);
 }
 
 // ---------------------------------------------------------------------------------------------
 // Host launchers.
-template <int PK, int CPL>
-static hipError_t launch_pred_z_t(const void* p1, const float* c1, const void* x, float* z,
-                                  int d, int rank, hipStream_t st) {
-  const int wpb = 4;
-  dim3 grid((rank + wpb - 1) / wpb);
-  hipLaunchKernelGGL((k_pred_z<PK, CPL>), grid, dim3(wpb * WAVE), 0, st, p1, c1, x, z, d, rank);
-  return hipGetLastError();
-}
-
 #define CPL_SWITCH(cpl, F)                                                                    \
   switch (cpl) {                                                                              \
     case 1: return F(1); case 2: return F(2); case 3: return F(3); case 4: return F(4);       \
@@ -347,71 +533,114 @@ static hipError_t launch_pred_z_t(const void* p1, const float* c1, const void* x
     default: return hipErrorInvalidValue;                                                     \
   }
 
+template <int PK, int CPL>
+static hipError_t launch_pred_z_t(const void* p1, const float* c1, const void* x, float* z,
+                                  int d, int rank, hipStream_t st, hipEvent_t ev0,
+                                  hipEvent_t ev1) {
+  if (ev0 && ev1)
+    hipExtLaunchKernelGGL((k_pred_z<PK, CPL>), dim3(rank), dim3(WAVE), 0, st, ev0, ev1, 0, p1,
+                          c1, x, z, d, rank);
+  else
+    hipLaunchKernelGGL((k_pred_z<PK, CPL>), dim3(rank), dim3(WAVE), 0, st, p1, c1, x, z, d,
+                       rank);
+  return hipGetLastError();
+}
+
 hipError_t launch_pred_z(int p_f16, int cpl, const void* p1, const float* c1, const void* x,
-                         float* z, int d, int rank, hipStream_t st) {
+                         float* z, int d, int rank, hipStream_t st, hipEvent_t ev0,
+                         hipEvent_t ev1) {
   if (p_f16) {
-#define F16Z(c) launch_pred_z_t<WK_F16, c>(p1, c1, x, z, d, rank, st)
+#define F16Z(c) launch_pred_z_t<WK_F16, c>(p1, c1, x, z, d, rank, st, ev0, ev1)
     CPL_SWITCH(cpl, F16Z)
 #undef F16Z
   } else {
-#define F32Z(c) launch_pred_z_t<WK_F32, c>(p1, c1, x, z, d, rank, st)
+#define F32Z(c) launch_pred_z_t<WK_F32, c>(p1, c1, x, z, d, rank, st, ev0, ev1)
     CPL_SWITCH(cpl, F32Z)
 #undef F32Z
   }
 }
 
-size_t main_lds_bytes(int d, int rank, int nc) {
-  return (size_t)(d + rank + 3 * nc + 1) * 4;
+int pred_s_cpr(int p_f16, int rank) {
+  const int pch = rank / (p_f16 ? 8 : 4);
+  if (pch <= 64) return 1;
+  if (pch <= 128) return 2;
+  if (pch <= 256) return 4;
+  return -1;
 }
 
-template <int WK, int CPL>
-static hipError_t launch_main_t(const MainArgs& a, int n_chunks, hipStream_t st,
-                                hipEvent_t ev0, hipEvent_t ev1) {
-  constexpr int MW = waves_for(CPL);
-  size_t lds = main_lds_bytes(a.d, a.rank, a.nc);
-  if (ev0 && ev1) {
-    // events attached to the dispatch: their elapsed time is this launch's execution time
-    hipExtLaunchKernelGGL((k_main<WK, CPL, MW>), dim3(n_chunks), dim3(MW * WAVE), lds, st, ev0,
+template <int PK, int CPR>
+static hipError_t launch_pred_s_t(const PredArgs& a, hipStream_t st, hipEvent_t ev0,
+                                  hipEvent_t ev1) {
+  if (ev0 && ev1)
+    hipExtLaunchKernelGGL((k_pred_s<PK, CPR>), dim3(a.ffn / 32), dim3(PS_THREADS), 0, st, ev0,
                           ev1, 0, a);
-  } else {
-    hipLaunchKernelGGL((k_main<WK, CPL, MW>), dim3(n_chunks), dim3(MW * WAVE), lds, st, a);
-  }
+  else
+    hipLaunchKernelGGL((k_pred_s<PK, CPR>), dim3(a.ffn / 32), dim3(PS_THREADS), 0, st, a);
   return hipGetLastError();
 }
 
-hipError_t launch_main(int wk, int cpl, const MainArgs& a, int n_chunks, hipStream_t st,
-                       hipEvent_t ev0, hipEvent_t ev1) {
+hipError_t launch_pred_s(int p_f16, const PredArgs& a, hipStream_t st, hipEvent_t ev0,
+                         hipEvent_t ev1) {
+  const int cpr = pred_s_cpr(p_f16, a.rank);
+  if (p_f16) {
+    if (cpr == 1) return launch_pred_s_t<WK_F16, 1>(a, st, ev0, ev1);
+    if (cpr == 2) return launch_pred_s_t<WK_F16, 2>(a, st, ev0, ev1);
+    if (cpr == 4) return launch_pred_s_t<WK_F16, 4>(a, st, ev0, ev1);
+  } else {
+    if (cpr == 1) return launch_pred_s_t<WK_F32, 1>(a, st, ev0, ev1);
+    if (cpr == 2) return launch_pred_s_t<WK_F32, 2>(a, st, ev0, ev1);
+    if (cpr == 4) return launch_pred_s_t<WK_F32, 4>(a, st, ev0, ev1);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_mask_bits(const unsigned char* mask, uint32_t* bitmap, int words,
+                            hipStream_t st) {
+  hipLaunchKernelGGL(k_mask_bits, dim3((words + 7) / 8), dim3(256), 0, st, mask, bitmap, words);
+  return hipGetLastError();
+}
+
+// 16-byte chunks of a weight row per thread of the gather kernel
+int gather_cpt(int wk, int d) {
+  const int nch = d / (wk == WK_F32 ? 4 : wk == WK_F16 ? 8 : 32);
+  return (nch + GA_THREADS - 1) / GA_THREADS;
+}
+int gather_blocks() { return GA_BLOCKS; }
+
+template <int WK, int CPT>
+static hipError_t launch_gather_t(const GatherArgs& a, hipStream_t st, hipEvent_t ev0,
+                                  hipEvent_t ev1) {
+  if (ev0 && ev1)
+    hipExtLaunchKernelGGL((k_gather<WK, CPT>), dim3(GA_BLOCKS), dim3(GA_THREADS), 0, st, ev0, ev1,
+                          0, a);
+  else
+    hipLaunchKernelGGL((k_gather<WK, CPT>), dim3(GA_BLOCKS), dim3(GA_THREADS), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather(int wk, const GatherArgs& a, hipStream_t st, hipEvent_t ev0,
+                         hipEvent_t ev1) {
+  const int cpt = gather_cpt(wk, a.d);
   if (wk == WK_F32) {
-#define M32(c) launch_main_t<WK_F32, c>(a, n_chunks, st, ev0, ev1)
-    CPL_SWITCH(cpl, M32)
-#undef M32
+    if (cpt == 1) return launch_gather_t<WK_F32, 1>(a, st, ev0, ev1);
+    if (cpt == 2) return launch_gather_t<WK_F32, 2>(a, st, ev0, ev1);
   } else if (wk == WK_F16) {
-#define M16(c) launch_main_t<WK_F16, c>(a, n_chunks, st, ev0, ev1)
-    CPL_SWITCH(cpl, M16)
-#undef M16
+    if (cpt == 1) return launch_gather_t<WK_F16, 1>(a, st, ev0, ev1);
+    if (cpt == 2) return launch_gather_t<WK_F16, 2>(a, st, ev0, ev1);
   } else {
-    // int4 rows: 32 elements per chunk, so d <= 8192 needs at most 4 chunks per lane
-    switch (cpl) {
-      case 1: return launch_main_t<WK_I4, 1>(a, n_chunks, st, ev0, ev1);
-      case 2: return launch_main_t<WK_I4, 2>(a, n_chunks, st, ev0, ev1);
-      case 3: return launch_main_t<WK_I4, 3>(a, n_chunks, st, ev0, ev1);
-      case 4: return launch_main_t<WK_I4, 4>(a, n_chunks, st, ev0, ev1);
-      default: return hipErrorInvalidValue;
-    }
+    if (cpt == 1) return launch_gather_t<WK_I4, 1>(a, st, ev0, ev1);
   }
+  return hipErrorInvalidValue;
 }
 
-hipError_t launch_reduce(const float* part, int n_chunks, const float* b_down, float* y, int d,
-                         hipStream_t st) {
-  dim3 grid((d / 4 + 15) / 16);
-  hipLaunchKernelGGL(k_reduce, grid, dim3(256), 0, st, part, n_chunks, b_down, y, d);
-  return hipGetLastError();
-}
+int reduce_tiles(int d) { return (d + RD_TW - 1) / RD_TW; }
 
-hipError_t launch_write_idx(const int* ccnt, const int* clist, int n_chunks, int nc, int* idx,
-                            int* cnt, hipStream_t st) {
-  hipLaunchKernelGGL(k_write_idx, dim3(n_chunks), dim3(256), 0, st, ccnt, clist, n_chunks, nc,
-                     idx, cnt);
+hipError_t launch_reduce(const ReduceArgs& a, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
+  const dim3 grid(reduce_tiles(a.d)), block(RD_THREADS);
+  if (ev0 && ev1)
+    hipExtLaunchKernelGGL(k_reduce, grid, block, 0, st, ev0, ev1, 0, a);
+  else
+    hipLaunchKernelGGL(k_reduce, grid, block, 0, st, a);
   return hipGetLastError();
 }
 

@@ -35,16 +35,20 @@ def row_bytes(cfg) -> float:
     return {"f32": 4 * cfg.d, "f16": 2 * cfg.d, "i4g32": cfg.d // 2 + (cfg.d // 32) * 2}[cfg.w_dtype]
 
 
-def per_unit_bytes(cfg):
-    """Algorithmic bytes: (predictor bytes of the main kernel, predictor stage-1 bytes,
-    bytes per active neuron).  x, y, index lists and partials are overhead, not counted."""
+def stage_bytes(cfg):
+    """Algorithmic bytes of each kernel as (fixed bytes per launch, bytes per active neuron):
+    the weights the method must read.  x, y, z, the bitmap and the (index, h) list are overhead
+    and not counted."""
     pb = 4 if cfg.p_dtype == "f32" else 2
     rows = 2 if cfg.act == "relu" else 3
     nbias = (1 if cfg.bias_up else 0) + (1 if (cfg.act != "relu" and cfg.bias_gate) else 0)
-    main_fixed = cfg.ffn * cfg.rank * pb + 4 * cfg.ffn          # P2 + c2
-    stage1 = cfg.rank * cfg.d * pb                               # P1 (no c1)
-    per_active = rows * row_bytes(cfg) + 4 * nbias
-    return main_fixed, stage1, per_active
+    return {
+        "pred_z": (cfg.rank * cfg.d * pb, 0),                      # P1 (c1 absent)
+        "pred_s": (cfg.ffn * cfg.rank * pb + 4 * cfg.ffn, 0),      # P2 + c2
+        # the active neurons' up (+ gate) and transposed-down rows and their biases
+        "gather": (0, rows * row_bytes(cfg) + 4 * nbias),
+        "reduce": (0, 0),                                          # partials only (overhead)
+    }
 
 
 def main():
@@ -53,8 +57,8 @@ def main():
     ap.add_argument("--steps", type=int, default=None, help="timed decode tokens (default: all)")
     ap.add_argument("--warmup", type=int, default=16, help="untimed tokens replayed first")
     ap.add_argument("--config", default="llama2_7b_reglu_f16")
-    ap.add_argument("--kernel-sample", type=int, default=64,
-                    help="tokens whose main-kernel launches are timed with dispatch events")
+    ap.add_argument("--kernel-sample", type=int, default=32,
+                    help="tokens whose kernel launches are timed with dispatch events")
     ap.add_argument("--cpu-tokens", type=int, default=1,
                     help="tokens (x all layers) the CPU oracle baseline runs; 0 = skip")
     args = ap.parse_args()
@@ -147,38 +151,45 @@ def main():
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1)
     tok_s = K / (ms / 1e3)
-    main_fixed, stage1, per_active = per_unit_bytes(cfg)
-    touched = L * K * (main_fixed + stage1) + per_active * cnt_h.sum()
+    SB = stage_bytes(cfg)
+    touched = sum(f * L * K + a * cnt_h.sum() for f, a in SB.values())
     eff_gbps = touched / (ms / 1e3) / 1e9
     log("timed %d tokens: %.3f ms/token, %.1f tok/s, %.1f GB/s effective over touched bytes" % (
         K, ms / K, tok_s, eff_gbps))
 
-    # ---- dominant kernel: events attached to each main-kernel dispatch (plain launches)
+    # ---- per-kernel durations: HIP events attached to each kernel's own dispatch (plain
+    # launches of the same tokens); the dominant kernel gives the roofline
     S = min(args.kernel_sample, K)
-    n_ev = S * L
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(n_ev)]
-    with torch.cuda.stream(stream):
-        for a, b in evs:            # materialise the events
-            a.record(stream)
-            b.record(stream)
-    torch.cuda.synchronize()
-    i = 0
-    with torch.cuda.stream(stream):
-        for t in range(S):
-            for l in range(L):
-                a, b = evs[i]
-                ffn.ffn_plan_set_timing_events(plans[l], a.cuda_event, b.cuda_event)
-                ffn.ffn_sparse_forward(plans[l], xp[l][t], 1, yp[l][t], stream=sp)
-                i += 1
-    torch.cuda.synchronize()
-    for p in plans:
-        ffn.ffn_plan_set_timing_events(p, 0, 0)
-    dur_ms = np.array([a.elapsed_time(b) for a, b in evs])
-    main_bytes = main_fixed * n_ev + per_active * cnt_h[:, :S].sum()
-    achieved = main_bytes / (dur_ms.sum() / 1e3) / 1e9
-    log("main kernel: %.2f us average over %d launches, %.1f GB/s algorithmic" % (
-        dur_ms.mean() * 1e3, n_ev, achieved))
+    stages = {}
+    for si, sname in enumerate(ffn.STAGES):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(S * L)]
+        with torch.cuda.stream(stream):
+            for a, b in evs:            # materialise the events
+                a.record(stream)
+                b.record(stream)
+        torch.cuda.synchronize()
+        i = 0
+        with torch.cuda.stream(stream):
+            for t in range(S):
+                for l in range(L):
+                    a, b = evs[i]
+                    ffn.ffn_plan_set_timing_events(plans[l], si, a.cuda_event, b.cuda_event)
+                    ffn.ffn_sparse_forward(plans[l], xp[l][t], 1, yp[l][t], stream=sp)
+                    i += 1
+        torch.cuda.synchronize()
+        for p in plans:
+            ffn.ffn_plan_set_timing_events(p, si, 0, 0)
+        dur_ms = np.array([a.elapsed_time(b) for a, b in evs])
+        fixed, per_a = SB[sname]
+        nbytes = fixed * S * L + per_a * cnt_h[:, :S].sum()
+        stages[sname] = {"avg_us": round(float(dur_ms.mean()) * 1e3, 3),
+                         "bytes_per_launch": int(nbytes / (S * L)),
+                         "gbps": round(nbytes / (dur_ms.sum() / 1e3) / 1e9, 1)}
+        log("kernel %-7s %8.2f us avg over %d launches, %7.1f GB/s algorithmic" % (
+            sname, dur_ms.mean() * 1e3, S * L, stages[sname]["gbps"]))
+    dom = max(stages, key=lambda k: stages[k]["avg_us"])
+    achieved = stages[dom]["gbps"]
 
     # ---- CPU oracle baseline on a bounded sample (first tokens x all layers), one thread, plus a
     # parity spot check of the GPU outputs of the timed run on the same sample
@@ -247,11 +258,12 @@ def main():
                    "target_density": cfg.density, "measured_density": round(density, 5)},
         "effective_gbps": round(eff_gbps, 1),
         "touched_bytes_per_token": int(touched / K),
-        "roofline": {"bound": "hbm", "kernel": "k_main (predictor stage 2 + gathered rows)",
-                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+        "roofline": {"bound": "hbm", "kernel": "k_" + dom,
+                     "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
-                     "avg_us": round(float(dur_ms.mean()) * 1e3, 3),
-                     "bytes_per_launch": int(main_bytes / n_ev)},
+                     "avg_us": stages[dom]["avg_us"],
+                     "bytes_per_launch": stages[dom]["bytes_per_launch"]},
+        "kernels": stages,
         "cpu_baseline": cpu,
         "parity_sample": parity,
     }

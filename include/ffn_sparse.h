@@ -33,8 +33,8 @@
  *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).  Forward calls only
  *    enqueue work on it: they never allocate, never synchronise and never use memset nodes, so a
  *    caller may capture them in a HIP graph.
- *  - Shapes: d % 8 == 0 (d % 32 == 0 for int4), d <= 8192, ffn % 32 == 0, rank % 8 == 0,
- *    rank <= 4096, 1 <= B <= max_batch.  Anything else gives FFN_ERR_UNSUPPORTED or
+ *  - Shapes: d % 8 == 0 (d % 32 == 0 for int4), d <= 8192, ffn % 32 == 0, ffn <= 32768,
+ *    rank % 8 == 0, rank <= 2048 (fp16 predictor) / 1024 (fp32 predictor), 1 <= B <= max_batch.  Anything else gives FFN_ERR_UNSUPPORTED or
  *    FFN_ERR_INVALID_ARGUMENT.
  *  - A plan is not re-entrant: forward calls on one plan must be ordered (one stream).  Plans used
  *    one after another on one stream may share one workspace.
@@ -136,13 +136,24 @@ ffn_status ffn_plan_crossover(const ffn_plan *plan, int32_t B, float *density);
 ffn_status ffn_plan_destroy(ffn_plan *plan);
 
 /*
- * Instrumentation for a caller that times the main (gathered-row) kernel on its own.  While
- * `start` and `stop` (hipEvent_t handles passed as void*, created with timing enabled) are
- * non-NULL, every forward on this plan launches its main kernel with the two events attached to
- * the dispatch itself, so hipEventElapsedTime(start, stop) afterwards is that one launch's
- * execution time.  NULL, NULL turns it off.  Not meant for calls under graph capture.
+ * Instrumentation, for a caller that times one kernel of the decode path on its own.  A forward
+ * runs four kernels per token: FFN_STAGE_PRED_Z (predictor stage 1), FFN_STAGE_PRED_S
+ * (predictor stage 2, threshold and active bitmap), FFN_STAGE_GATHER (the active neurons' up,
+ * gate and transposed-down rows: activation and one row axpy per neuron into partials of y) and
+ * FFN_STAGE_REDUCE (sum of the partials).  While `start` and `stop`
+ * (hipEvent_t handles passed as void*, created with timing enabled) are set for a stage, every
+ * forward on this plan launches that stage's kernel with the two events attached to the dispatch
+ * itself, so hipEventElapsedTime(start, stop) afterwards is that one launch's execution time.
+ * NULL, NULL turns it off.  Not meant for calls under graph capture.
  */
-ffn_status ffn_plan_set_timing_events(ffn_plan *plan, void *start, void *stop);
+typedef enum {
+    FFN_STAGE_PRED_Z = 0,
+    FFN_STAGE_PRED_S = 1,
+    FFN_STAGE_GATHER = 2,
+    FFN_STAGE_REDUCE = 3
+} ffn_stage;
+
+ffn_status ffn_plan_set_timing_events(ffn_plan *plan, int32_t stage, void *start, void *stop);
 
 /* Message of the last error on the calling thread ("" if none).  Never NULL. */
 const char *ffn_last_error(void);

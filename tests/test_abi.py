@@ -65,6 +65,8 @@ def test_workspace_size_valid_and_monotone_in_batch():
     (dict(x_dtype=ffn.FFN_F32), ffn.FFN_ERR_UNSUPPORTED),
     (dict(w_dtype=ffn.FFN_I4G32, d=4104), ffn.FFN_ERR_UNSUPPORTED),
     (dict(d=16384), ffn.FFN_ERR_UNSUPPORTED),
+    (dict(ffn=32800), ffn.FFN_ERR_UNSUPPORTED),
+    (dict(rank=4096), ffn.FFN_ERR_UNSUPPORTED),
     (dict(max_batch=0), ffn.FFN_ERR_INVALID_ARGUMENT),
 ])
 def test_bad_descriptors_are_rejected(kw, status):

@@ -176,3 +176,57 @@ def test_batch_equals_single_tokens_and_is_deterministic(ffn):
     for t in range(5):
         y1, l1, _, _ = _run(ffn, L, x[t:t + 1])
         assert np.array_equal(y1[0], yb[t]) and np.array_equal(l1[0], lb[t])
+
+
+def test_stage_timing_events(ffn):
+    """The instrumentation hook attaches events to each kernel's dispatch; the result of the
+    forward is unchanged by it."""
+    cfg = synth.small_config(d=512, ffn=2048, rank=64, act="relu", w_dtype="f16",
+                             x_dtype="f16", p_dtype="f16", density=0.1, bias_up=True)
+    L = to_device(synth.make_layer(cfg))
+    x = synth.make_tokens(cfg, 1).cuda()
+    m = ffn.SparseFFN(L)
+    y0 = m.forward(x).clone()
+    for stage in range(4):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        b.record()
+        ffn.ffn_plan_set_timing_events(m.plan, stage, a.cuda_event, b.cuda_event)
+        y1 = m.forward(x)
+        torch.cuda.synchronize()
+        ffn.ffn_plan_set_timing_events(m.plan, stage, 0, 0)
+        assert a.elapsed_time(b) > 0
+        assert torch.equal(y0, y1)
+    with pytest.raises(ffn.FFNError):
+        ffn.ffn_plan_set_timing_events(m.plan, 4, 0, 0)
+    m.close()
+
+
+def test_index_and_count_outputs_are_independent(ffn):
+    """idx without cnt, cnt without idx, and neither: each combination gives the same y and
+    the requested outputs only (regression: the count-only call once wrote through the absent
+    index pointer)."""
+    cfg = synth.small_config(d=256, ffn=1024, rank=32, act="relu", w_dtype="f16",
+                             x_dtype="f16", p_dtype="f16", density=0.15, bias_up=True)
+    L = to_device(synth.make_layer(cfg))
+    x = synth.make_tokens(cfg, 2).cuda()
+    m = ffn.SparseFFN(L, max_batch=2)
+    idx = torch.full((2, cfg.ffn), -1, dtype=torch.int32, device="cuda")
+    cnt = torch.full((2,), -1, dtype=torch.int32, device="cuda")
+    y_both = m.forward(x, idx=idx, cnt=cnt).clone()
+    torch.cuda.synchronize()
+    ref_idx, ref_cnt = idx.clone(), cnt.clone()
+    cnt2 = torch.full((2,), -1, dtype=torch.int32, device="cuda")
+    y_cnt = m.forward(x, cnt=cnt2).clone()
+    idx2 = torch.full((2, cfg.ffn), -1, dtype=torch.int32, device="cuda")
+    y_idx = m.forward(x, idx=idx2).clone()
+    y_none = m.forward(x).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(cnt2, ref_cnt)
+    for b in range(2):
+        n = int(ref_cnt[b])
+        assert torch.equal(idx2[b, :n], ref_idx[b, :n])
+    for yy in (y_cnt, y_idx, y_none):
+        assert torch.equal(yy, y_both)
+    m.close()
