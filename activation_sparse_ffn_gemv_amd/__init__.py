@@ -248,3 +248,44 @@ class SparseFFN:
             self.close()
         except Exception:
             pass
+
+
+class MoEFFN:
+    """A mixture of sparse-FFN experts with an on-device top-k router.
+
+    ``experts`` is a list of layer dicts (as for ``SparseFFN``); ``router`` is the [E][d] router
+    matrix in the experts' activation dtype.  The expert plans share one workspace (they are
+    only used for their weights and shapes); the mixture has its own.
+    """
+
+    def __init__(self, experts, router: torch.Tensor, top_k: int = 2, max_batch: int = 1):
+        self.experts = [SparseFFN(e, max_batch=max_batch) for e in experts]
+        self.router = router
+        self.top_k = top_k
+        self.d = self.experts[0].d
+        plans = [e.plan for e in self.experts]
+        n = ffn_moe_workspace_size(len(plans), top_k, plans[0])
+        self.workspace = torch.empty(n, dtype=torch.uint8, device=router.device)
+        self.moe = ffn_moe_plan(len(plans), top_k, router.data_ptr(), plans,
+                                self.workspace.data_ptr(), n)
+
+    def forward(self, x, y=None, expert_idx=None, expert_w=None):
+        B = x.shape[0]
+        if y is None:
+            y = torch.empty(B, self.d, dtype=torch.float32, device=x.device)
+        ffn_moe_forward(self.moe, x.data_ptr(), B, y.data_ptr(), _ptr(expert_idx), _ptr(expert_w),
+                        _stream())
+        return y
+
+    def close(self):
+        if self.moe:
+            ffn_moe_destroy(self.moe)
+            self.moe = 0
+        for e in self.experts:
+            e.close()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

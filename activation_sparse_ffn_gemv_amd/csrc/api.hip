@@ -76,6 +76,9 @@ ffn_status check_desc(const ffn_layer_desc* d) {
     return fail(FFN_ERR_UNSUPPORTED, "ffn must be a multiple of 32 and <= 32768");
   if (d->rank % 8 || (d->rank > 0 && pred_s_cpr(d->p_dtype == FFN_F16, d->rank) < 0))
     return fail(FFN_ERR_UNSUPPORTED, "rank must be a multiple of 8 and <= 2048 (fp16) / 1024 (fp32)");
+  const int wk = d->w_dtype == FFN_F32 ? WK_F32 : d->w_dtype == FFN_F16 ? WK_F16 : WK_I4;
+  if (gather_cpt(wk, d->d) > (wk == WK_I4 ? 1 : 2))
+    return fail(FFN_ERR_UNSUPPORTED, "d > %d for this w_dtype", wk == WK_F32 ? 4096 : 8192);
   if (d->max_batch > 4096) return fail(FFN_ERR_UNSUPPORTED, "max_batch > 4096");
   return FFN_OK;
 }
@@ -95,6 +98,117 @@ Layout layout_for(const ffn_layer_desc* d) {
   L.off_union = off;  off = round_up(off + 256, 256);
   L.total = off;
   return L;
+}
+
+
+// Workspace of a mixture: the expert pipeline's scratch (the layout of one expert), then the
+// per-slot expert records [max_batch][top_k].
+struct MoeLayout {
+  size_t off_slots, total;
+};
+
+MoeLayout moe_layout(const ffn_plan* e0, int top_k) {
+  MoeLayout L{};
+  L.off_slots = layout_for(&e0->desc).total;
+  L.total = round_up(L.off_slots + (size_t)e0->desc.max_batch * top_k * sizeof(ExpertW), 256);
+  return L;
+}
+
+}  // namespace
+
+struct ffn_moe {
+  int n_experts, top_k;
+  const void* router;
+  const ffn_plan* e0;             // shapes and threshold (every expert shares them)
+  char* ws;
+  MoeLayout L;
+  ExpertTable tab;                // every expert's weight pointers, passed to the router
+};
+
+namespace {
+
+// Scratch of the token in flight inside a workspace laid out by layout_for.
+struct TokenBufs {
+  float* z;
+  uint32_t* bits;
+  int* cnt;
+  float* part;
+};
+
+TokenBufs token_bufs(char* ws, const ffn_plan* p) {
+  return TokenBufs{reinterpret_cast<float*>(ws + p->off_z),
+                   reinterpret_cast<uint32_t*>(ws + p->off_bits),
+                   reinterpret_cast<int*>(ws + p->off_cnt),
+                   reinterpret_cast<float*>(ws + p->off_part)};
+}
+
+// The launches of one token: active set (predictor or caller mask) -> balanced gather -> reduce.
+// slot != nullptr: the expert is chosen on the device and the kernels take its weights from the
+// slot record (p then only supplies shapes and the threshold); accumulate adds the weighted
+// result to y.
+ffn_status enqueue_token(const ffn_plan* p, const TokenBufs& wb, const void* xb,
+                         const uint8_t* maskb, float* yb, int* idxb, int* cntb, float* scoresb,
+                         const ExpertW* slot, int accumulate, hipStream_t st) {
+  const ffn_layer_desc& D = p->desc;
+  const int wk = D.w_dtype == FFN_F32 ? WK_F32 : D.w_dtype == FFN_F16 ? WK_F16 : WK_I4;
+  hipError_t e;
+  if (maskb) {
+    e = launch_mask_bits(maskb, wb.bits, D.ffn / 32, st);
+    if (e != hipSuccess) return hip_fail(e, "mask launch");
+  } else {
+    e = launch_pred_z(D.p_dtype == FFN_F16, p->cpl_p, p->w.p1, p->w.c1, xb, wb.z, D.d, D.rank,
+                      slot, st, p->ev[FFN_STAGE_PRED_Z][0], p->ev[FFN_STAGE_PRED_Z][1]);
+    if (e != hipSuccess) return hip_fail(e, "predictor stage 1 launch");
+    PredArgs pa{};
+    pa.p2 = p->w.p2;
+    pa.c2 = p->w.c2;
+    pa.z = wb.z;
+    pa.scores = scoresb;
+    pa.bitmap = wb.bits;
+    pa.ffn = D.ffn;
+    pa.rank = D.rank;
+    pa.thr = p->thr;
+    pa.slot = slot;
+    e = launch_pred_s(D.p_dtype == FFN_F16, pa, st, p->ev[FFN_STAGE_PRED_S][0],
+                      p->ev[FFN_STAGE_PRED_S][1]);
+    if (e != hipSuccess) return hip_fail(e, "predictor stage 2 launch");
+  }
+  GatherArgs ga{};
+  ga.w_up = p->w.w_up;
+  ga.w_gate = p->w.w_gate;
+  ga.w_dn = p->w.w_down_t;
+  ga.s_up = p->w.s_up;
+  ga.s_gate = p->w.s_gate;
+  ga.s_dn = p->w.s_down_t;
+  ga.b_up = p->w.b_up;
+  ga.b_gate = p->w.b_gate;
+  ga.x = xb;
+  ga.bitmap = wb.bits;
+  ga.part = wb.part;
+  ga.cnt = wb.cnt;
+  ga.d = D.d;
+  ga.ffn = D.ffn;
+  ga.act = D.act;
+  ga.has_gate = D.act != FFN_ACT_RELU;
+  ga.slot = slot;
+  e = launch_gather(wk, ga, st, p->ev[FFN_STAGE_GATHER][0], p->ev[FFN_STAGE_GATHER][1]);
+  if (e != hipSuccess) return hip_fail(e, "gather launch");
+  ReduceArgs ra{};
+  ra.part = wb.part;
+  ra.cnt = wb.cnt;
+  ra.bitmap = wb.bits;
+  ra.b_down = p->w.b_down;
+  ra.y = yb;
+  ra.idx_out = idxb;
+  ra.cnt_out = cntb;
+  ra.d = D.d;
+  ra.ffn = D.ffn;
+  ra.n_part = gather_blocks();
+  ra.slot = slot;
+  ra.accumulate = accumulate;
+  e = launch_reduce(ra, st, p->ev[FFN_STAGE_REDUCE][0], p->ev[FFN_STAGE_REDUCE][1]);
+  if (e != hipSuccess) return hip_fail(e, "reduce launch");
+  return FFN_OK;
 }
 
 }  // namespace
@@ -183,69 +297,14 @@ ffn_status ffn_sparse_forward(ffn_plan* p, const void* x, int32_t B, float* y,
     return fail(FFN_ERR_INVALID_ARGUMENT, "x / y not 16-byte aligned");
   if (path == FFN_PATH_DENSE) return fail(FFN_ERR_UNSUPPORTED, "dense path not built yet");
   hipStream_t st = static_cast<hipStream_t>(stream);
-
   const size_t xbytes = (size_t)D.d * (D.x_dtype == FFN_F32 ? 4 : 2);
-  float* z = reinterpret_cast<float*>(p->ws + p->off_z);
-  uint32_t* bits = reinterpret_cast<uint32_t*>(p->ws + p->off_bits);
-  float* part = reinterpret_cast<float*>(p->ws + p->off_part);
-  const int wk = D.w_dtype == FFN_F32 ? WK_F32 : D.w_dtype == FFN_F16 ? WK_F16 : WK_I4;
-  const int p_f16 = D.p_dtype == FFN_F16;
-
-  int* ws_cnt = reinterpret_cast<int*>(p->ws + p->off_cnt);
+  const TokenBufs wb = token_bufs(p->ws, p);
   for (int b = 0; b < B; ++b) {
-    const void* xb = static_cast<const char*>(x) + b * xbytes;
-    hipError_t e;
-    if (mask) {
-      e = launch_mask_bits(mask + (size_t)b * D.ffn, bits, D.ffn / 32, st);
-      if (e != hipSuccess) return hip_fail(e, "mask launch");
-    } else {
-      e = launch_pred_z(p_f16, p->cpl_p, p->w.p1, p->w.c1, xb, z, D.d, D.rank, st,
-                        p->ev[FFN_STAGE_PRED_Z][0], p->ev[FFN_STAGE_PRED_Z][1]);
-      if (e != hipSuccess) return hip_fail(e, "predictor stage 1 launch");
-      PredArgs pa{};
-      pa.p2 = p->w.p2;
-      pa.c2 = p->w.c2;
-      pa.z = z;
-      pa.scores = scores ? scores + (size_t)b * D.ffn : nullptr;
-      pa.bitmap = bits;
-      pa.ffn = D.ffn;
-      pa.rank = D.rank;
-      pa.thr = p->thr;
-      e = launch_pred_s(p_f16, pa, st, p->ev[FFN_STAGE_PRED_S][0], p->ev[FFN_STAGE_PRED_S][1]);
-      if (e != hipSuccess) return hip_fail(e, "predictor stage 2 launch");
-    }
-    GatherArgs ga{};
-    ga.w_up = p->w.w_up;
-    ga.w_gate = p->w.w_gate;
-    ga.w_dn = p->w.w_down_t;
-    ga.s_up = p->w.s_up;
-    ga.s_gate = p->w.s_gate;
-    ga.s_dn = p->w.s_down_t;
-    ga.b_up = p->w.b_up;
-    ga.b_gate = p->w.b_gate;
-    ga.x = xb;
-    ga.bitmap = bits;
-    ga.part = part;
-    ga.cnt = ws_cnt;
-    ga.d = D.d;
-    ga.ffn = D.ffn;
-    ga.act = D.act;
-    ga.has_gate = D.act != FFN_ACT_RELU;
-    e = launch_gather(wk, ga, st, p->ev[FFN_STAGE_GATHER][0], p->ev[FFN_STAGE_GATHER][1]);
-    if (e != hipSuccess) return hip_fail(e, "gather launch");
-    ReduceArgs ra{};
-    ra.part = part;
-    ra.cnt = ws_cnt;
-    ra.bitmap = bits;
-    ra.b_down = p->w.b_down;
-    ra.y = y + (size_t)b * D.d;
-    ra.idx_out = idx ? idx + (size_t)b * D.ffn : nullptr;
-    ra.cnt_out = cnt ? cnt + b : nullptr;
-    ra.d = D.d;
-    ra.ffn = D.ffn;
-    ra.n_part = gather_blocks();
-    e = launch_reduce(ra, st, p->ev[FFN_STAGE_REDUCE][0], p->ev[FFN_STAGE_REDUCE][1]);
-    if (e != hipSuccess) return hip_fail(e, "reduce launch");
+    ffn_status s = enqueue_token(p, wb, static_cast<const char*>(x) + b * xbytes,
+                                 mask ? mask + (size_t)b * D.ffn : nullptr, y + (size_t)b * D.d,
+                                 idx ? idx + (size_t)b * D.ffn : nullptr, cnt ? cnt + b : nullptr,
+                                 scores ? scores + (size_t)b * D.ffn : nullptr, nullptr, 0, st);
+    if (s != FFN_OK) return s;
   }
   g_err[0] = 0;
   return FFN_OK;
@@ -284,26 +343,113 @@ ffn_status ffn_plan_destroy(ffn_plan* p) {
 
 ffn_status ffn_moe_workspace_size(int32_t n_experts, int32_t top_k, const ffn_plan* e0,
                                   size_t* bytes) {
-  (void)n_experts; (void)top_k; (void)e0; (void)bytes;
-  return fail(FFN_ERR_UNSUPPORTED, "mixture of experts not built yet");
+  if (!e0 || !bytes) return fail(FFN_ERR_INVALID_ARGUMENT, "expert0 / bytes is NULL");
+  if (n_experts < 1 || n_experts > MOE_MAX_E)
+    return fail(FFN_ERR_UNSUPPORTED, "n_experts must lie in [1, %d]", MOE_MAX_E);
+  if (top_k < 1 || top_k > MOE_MAX_K || top_k > n_experts)
+    return fail(FFN_ERR_UNSUPPORTED, "top_k must lie in [1, min(n_experts, %d)]", MOE_MAX_K);
+  *bytes = moe_layout(e0, top_k).total;
+  g_err[0] = 0;
+  return FFN_OK;
 }
 
 ffn_status ffn_moe_plan(int32_t n_experts, int32_t top_k, const void* w_router,
                         ffn_plan* const* experts, void* workspace, size_t workspace_bytes,
                         ffn_moe** out) {
-  (void)n_experts; (void)top_k; (void)w_router; (void)experts; (void)workspace;
-  (void)workspace_bytes; (void)out;
-  return fail(FFN_ERR_UNSUPPORTED, "mixture of experts not built yet");
+  if (!out) return fail(FFN_ERR_INVALID_ARGUMENT, "out is NULL");
+  *out = nullptr;
+  if (!experts || !w_router || !workspace)
+    return fail(FFN_ERR_INVALID_ARGUMENT, "experts / w_router / workspace is NULL");
+  for (int e = 0; e < n_experts && e < MOE_MAX_E; ++e)
+    if (!experts[e]) return fail(FFN_ERR_INVALID_ARGUMENT, "expert plan %d is NULL", e);
+  size_t need = 0;
+  ffn_status st = ffn_moe_workspace_size(n_experts, top_k, experts[0], &need);
+  if (st != FFN_OK) return st;
+  const ffn_layer_desc& D = experts[0]->desc;
+  if (D.rank == 0) return fail(FFN_ERR_INVALID_ARGUMENT, "experts need a predictor (rank > 0)");
+  for (int e = 1; e < n_experts; ++e) {
+    const ffn_layer_desc& E = experts[e]->desc;
+    if (E.d != D.d || E.ffn != D.ffn || E.rank != D.rank || E.act != D.act ||
+        E.w_dtype != D.w_dtype || E.x_dtype != D.x_dtype || E.p_dtype != D.p_dtype ||
+        E.threshold != D.threshold || E.max_batch != D.max_batch)
+      return fail(FFN_ERR_INVALID_ARGUMENT, "expert %d differs from expert 0 in its descriptor", e);
+  }
+  if (!aligned16(w_router) || !aligned16(workspace))
+    return fail(FFN_ERR_INVALID_ARGUMENT, "pointer not 16-byte aligned");
+  if (workspace_bytes < need)
+    return fail(FFN_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", workspace_bytes, need);
+  ffn_moe* m = new (std::nothrow) ffn_moe();
+  if (!m) return fail(FFN_ERR_INTERNAL, "out of host memory");
+  m->n_experts = n_experts;
+  m->top_k = top_k;
+  m->router = w_router;
+  m->e0 = experts[0];
+  m->ws = static_cast<char*>(workspace);
+  m->L = moe_layout(experts[0], top_k);
+  for (int e = 0; e < n_experts; ++e) {
+    const ffn_layer_weights& w = experts[e]->w;
+    ExpertW& r = m->tab.e[e];
+    r.p1 = w.p1;
+    r.p2 = w.p2;
+    r.c1 = w.c1;
+    r.c2 = w.c2;
+    r.w_up = w.w_up;
+    r.w_gate = w.w_gate;
+    r.w_dn = w.w_down_t;
+    r.s_up = w.s_up;
+    r.s_gate = w.s_gate;
+    r.s_dn = w.s_down_t;
+    r.b_up = w.b_up;
+    r.b_gate = w.b_gate;
+    r.b_down = w.b_down;
+    r.wgt = 0.0f;
+    r.expert = e;
+  }
+  *out = m;
+  g_err[0] = 0;
+  return FFN_OK;
 }
 
 ffn_status ffn_moe_forward(ffn_moe* m, const void* x, int32_t B, float* y, int32_t* expert_idx,
                            float* expert_w, void* stream) {
-  (void)m; (void)x; (void)B; (void)y; (void)expert_idx; (void)expert_w; (void)stream;
-  return fail(FFN_ERR_UNSUPPORTED, "mixture of experts not built yet");
+  if (!m) return fail(FFN_ERR_INVALID_ARGUMENT, "moe is NULL");
+  if (!x || !y) return fail(FFN_ERR_INVALID_ARGUMENT, "x / y is NULL");
+  const ffn_plan* p = m->e0;
+  const ffn_layer_desc& D = p->desc;
+  if (B < 1 || B > D.max_batch)
+    return fail(FFN_ERR_INVALID_ARGUMENT, "B = %d outside [1, %d]", B, D.max_batch);
+  if (!aligned16(x) || !aligned16(y))
+    return fail(FFN_ERR_INVALID_ARGUMENT, "x / y not 16-byte aligned");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  ExpertW* slots = reinterpret_cast<ExpertW*>(m->ws + m->L.off_slots);
+  RouterArgs ra{};
+  ra.R = m->router;
+  ra.x = x;
+  ra.ids_out = expert_idx;
+  ra.w_out = expert_w;
+  ra.slots = slots;
+  ra.d = D.d;
+  ra.E = m->n_experts;
+  ra.K = m->top_k;
+  ra.x_f16 = D.x_dtype == FFN_F16;
+  ra.tab = m->tab;
+  hipError_t e = launch_router(ra, B, st);
+  if (e != hipSuccess) return hip_fail(e, "router launch");
+  const size_t xbytes = (size_t)D.d * (D.x_dtype == FFN_F32 ? 4 : 2);
+  const TokenBufs wb = token_bufs(m->ws, p);
+  for (int b = 0; b < B; ++b)
+    for (int k = 0; k < m->top_k; ++k) {
+      ffn_status s = enqueue_token(p, wb, static_cast<const char*>(x) + b * xbytes, nullptr,
+                                   y + (size_t)b * D.d, nullptr, nullptr, nullptr,
+                                   slots + (size_t)b * m->top_k + k, k > 0, st);
+      if (s != FFN_OK) return s;
+    }
+  g_err[0] = 0;
+  return FFN_OK;
 }
 
 ffn_status ffn_moe_destroy(ffn_moe* m) {
-  (void)m;
+  delete m;
   return FFN_OK;
 }
 

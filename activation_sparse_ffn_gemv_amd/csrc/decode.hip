@@ -90,8 +90,13 @@ template <int PK, int CPL>
 __global__ __launch_bounds__(64) void k_pred_z(const void* __restrict__ p1,
                                                const float* __restrict__ c1,
                                                const void* __restrict__ x,
-                                               float* __restrict__ z, int d, int rank) {
+                                               float* __restrict__ z, int d, int rank,
+                                               const ExpertW* __restrict__ slot) {
   FFN_TS(0, 0);
+  if (slot) {
+    p1 = slot->p1;
+    c1 = slot->c1;
+  }
   const int lane = threadIdx.x;
   const int row = blockIdx.x;
   const int nch = d / Kind<PK>::EPC;
@@ -128,6 +133,10 @@ __global__ __launch_bounds__(PS_THREADS) void k_pred_s(PredArgs a) {
   const int g = tid / L, gl = tid % L;
   const int i0 = blockIdx.x * 32;
   FFN_TS(1, 0);
+  if (a.slot) {
+    a.p2 = a.slot->p2;
+    a.c2 = a.slot->c2;
+  }
   const float c2v = (tid < 32 && a.c2) ? a.c2[i0 + tid] : 0.0f;
   f32x4 zr[CPR][PE / 4];                      // this lane's z slice, fixed across rows
 #pragma unroll
@@ -239,6 +248,17 @@ __global__ __launch_bounds__(GA_THREADS) void k_gather(GatherArgs a) {
   const int lane = tid & (WAVE - 1), wave = tid / WAVE;
   const int nch = a.d / EPC;
   FFN_TS(1, 0);
+  if (a.slot) {
+    const ExpertW& e = *a.slot;
+    a.w_up = e.w_up;
+    a.w_gate = e.w_gate;
+    a.w_dn = e.w_dn;
+    a.s_up = e.s_up;
+    a.s_gate = e.s_gate;
+    a.s_dn = e.s_dn;
+    a.b_up = e.b_up;
+    a.b_gate = e.b_gate;
+  }
 
   // this thread's chunks of the token (chunk tid + k*NT)
   u32x4 xr[CPT][Kind<WK>::XW];
@@ -513,10 +533,17 @@ __global__ __launch_bounds__(RD_THREADS) void k_reduce(ReduceArgs a) {
   __syncthreads();
   const int j = tile * RD_TW + threadIdx.x * 4;
   if (threadIdx.x < RD_Q && j < a.d) {
+    const float* b_down = a.slot ? a.slot->b_down : a.b_down;
     f32x4 t = s[0][threadIdx.x];
 #pragma unroll 8
     for (int k = 1; k < RD_G; ++k) t += s[k][threadIdx.x];
-    if (a.b_down) t += *reinterpret_cast<const f32x4*>(a.b_down + j);
+    if (b_down) t += *reinterpret_cast<const f32x4*>(b_down + j);
+    if (a.slot) {
+      // expert slot of a mixture: weighted, summed over the slots in slot order
+      const float wgt = a.slot->wgt;
+      t *= wgt;
+      if (a.accumulate) t += *reinterpret_cast<const f32x4*>(a.y + j);
+    }
     *reinterpret_cast<f32x4*>(a.y + j) = t;
   }
   if (blockIdx.x == 0 && (a.idx_out || a.cnt_out))
@@ -535,26 +562,26 @@ __global__ __launch_bounds__(RD_THREADS) void k_reduce(ReduceArgs a) {
 
 template <int PK, int CPL>
 static hipError_t launch_pred_z_t(const void* p1, const float* c1, const void* x, float* z,
-                                  int d, int rank, hipStream_t st, hipEvent_t ev0,
-                                  hipEvent_t ev1) {
+                                  int d, int rank, const ExpertW* slot, hipStream_t st,
+                                  hipEvent_t ev0, hipEvent_t ev1) {
   if (ev0 && ev1)
     hipExtLaunchKernelGGL((k_pred_z<PK, CPL>), dim3(rank), dim3(WAVE), 0, st, ev0, ev1, 0, p1,
-                          c1, x, z, d, rank);
+                          c1, x, z, d, rank, slot);
   else
     hipLaunchKernelGGL((k_pred_z<PK, CPL>), dim3(rank), dim3(WAVE), 0, st, p1, c1, x, z, d,
-                       rank);
+                       rank, slot);
   return hipGetLastError();
 }
 
 hipError_t launch_pred_z(int p_f16, int cpl, const void* p1, const float* c1, const void* x,
-                         float* z, int d, int rank, hipStream_t st, hipEvent_t ev0,
-                         hipEvent_t ev1) {
+                         float* z, int d, int rank, const ExpertW* slot, hipStream_t st,
+                         hipEvent_t ev0, hipEvent_t ev1) {
   if (p_f16) {
-#define F16Z(c) launch_pred_z_t<WK_F16, c>(p1, c1, x, z, d, rank, st, ev0, ev1)
+#define F16Z(c) launch_pred_z_t<WK_F16, c>(p1, c1, x, z, d, rank, slot, st, ev0, ev1)
     CPL_SWITCH(cpl, F16Z)
 #undef F16Z
   } else {
-#define F32Z(c) launch_pred_z_t<WK_F32, c>(p1, c1, x, z, d, rank, st, ev0, ev1)
+#define F32Z(c) launch_pred_z_t<WK_F32, c>(p1, c1, x, z, d, rank, slot, st, ev0, ev1)
     CPL_SWITCH(cpl, F32Z)
 #undef F32Z
   }

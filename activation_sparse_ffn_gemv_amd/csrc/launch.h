@@ -7,6 +7,35 @@
 
 namespace ffn {
 
+// One expert's weights as the kernels read them when the expert is chosen on the device (a
+// mixture of experts): the router copies the chosen experts' records into per-slot records in
+// the workspace, and a kernel given such a record takes its weight pointers from it instead of
+// from its arguments.  wgt is the slot's routing weight.
+struct ExpertW {
+  const void *p1, *p2;
+  const float *c1, *c2;
+  const void *w_up, *w_gate, *w_dn, *s_up, *s_gate, *s_dn;
+  const float *b_up, *b_gate, *b_down;
+  float wgt;
+  int expert;
+};
+constexpr int MOE_MAX_E = 16;
+constexpr int MOE_MAX_K = 4;
+struct ExpertTable {
+  ExpertW e[MOE_MAX_E];
+};
+
+// Router of a mixture of experts (B tokens, one workgroup each).
+struct RouterArgs {
+  const void* R;              // [E][d] x dtype
+  const void* x;              // [B][d]
+  int* ids_out;               // [B][K] or nullptr
+  float* w_out;               // [B][K] or nullptr
+  ExpertW* slots;             // [B][K] out
+  int d, E, K, x_f16;
+  ExpertTable tab;
+};
+
 // Predictor stage 2 (one token).
 struct PredArgs {
   const void* p2;             // [ffn][rank] p_dtype
@@ -16,6 +45,7 @@ struct PredArgs {
   uint32_t* bitmap;           // [ffn/32] out
   int ffn, rank;
   float thr;                  // logit(threshold)
+  const ExpertW* slot;        // device-chosen expert (p2, c2 from it), or nullptr
 };
 
 // Balanced gather of the active rows (one token).
@@ -33,6 +63,7 @@ struct GatherArgs {
   float* part;                // [GA_BLOCKS][d] out: partial of y per workgroup
   int* cnt;                   // [1] out: |A|
   int d, ffn, act, has_gate;
+  const ExpertW* slot;        // device-chosen expert (rows, scales, biases from it), or nullptr
 };
 
 // Sum of the gather partials (one token).
@@ -45,11 +76,13 @@ struct ReduceArgs {
   int* idx_out;               // [ffn] ascending active list, or nullptr
   int* cnt_out;               // [1], or nullptr
   int d, ffn, n_part;
+  const ExpertW* slot;        // device-chosen expert: b_down and the routing weight, or nullptr
+  int accumulate;             // y += wgt * result (later expert slots) instead of y = ...
 };
 
 hipError_t launch_pred_z(int p_f16, int cpl, const void* p1, const float* c1, const void* x,
-                         float* z, int d, int rank, hipStream_t st, hipEvent_t ev0 = nullptr,
-                         hipEvent_t ev1 = nullptr);
+                         float* z, int d, int rank, const ExpertW* slot, hipStream_t st,
+                         hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
 int pred_s_cpr(int p_f16, int rank);
 hipError_t launch_pred_s(int p_f16, const PredArgs& a, hipStream_t st, hipEvent_t ev0 = nullptr,
                          hipEvent_t ev1 = nullptr);
@@ -62,5 +95,6 @@ hipError_t launch_gather(int wk, const GatherArgs& a, hipStream_t st, hipEvent_t
                          hipEvent_t ev1 = nullptr);
 hipError_t launch_reduce(const ReduceArgs& a, hipStream_t st, hipEvent_t ev0 = nullptr,
                          hipEvent_t ev1 = nullptr);
+hipError_t launch_router(const RouterArgs& a, int B, hipStream_t st);
 
 }  // namespace ffn

@@ -159,26 +159,33 @@ ffn_status ffn_plan_set_timing_events(ffn_plan *plan, int32_t stage, void *start
 const char *ffn_last_error(void);
 
 /* ---------------------------------------------------------------------------------------------
- * Mixture of experts (TurboSparse-Mixtral; nubint.ai PowerInfer-2 review and citnews.com.cn):
- * a router picks top_k experts per token; y = sum_t w_t FFN_{e_t}(x), each expert a sparse FFN
- * with its own predictor.  Routing stays on the device: the kernels read the chosen expert ids
- * from device memory, never from the host.
- *   logits_e = R[e] . x ;  the top_k largest win, ties to the lower expert index;
- *   w = softmax over the chosen logits.
- * All expert plans must share d, ffn, rank, act and dtypes; their workspaces may be one buffer.
+ * Mixture of experts (TurboSparse-Mixtral; nubint.ai PowerInfer-2 review, section on the models
+ * it runs; citnews.com.cn PowerInfer-2 article): a router picks top_k experts per token and
+ *   logits_e = R[e] . x ;  the top_k largest win, ties going to the lower expert index;
+ *   w = softmax over the chosen logits;   y = sum_t w_t FFN_{e_t}(x),
+ * each expert a sparse FFN (predictor, active set, rows) of its own.  Routing stays on the
+ * device: the router kernel copies the chosen experts' weight pointers into per-slot records in
+ * the mixture's workspace and the expert kernels read them there; the host never sees the
+ * choice.  The weighted expert results are summed in slot order (no atomics).
+ * Limits: 1 <= n_experts <= 16, 1 <= top_k <= min(n_experts, 4); every expert plan has the same
+ * descriptor (shapes, dtypes, threshold, max_batch) and a predictor (rank > 0).
  */
 typedef struct ffn_moe ffn_moe;
 
-/* w_router: device [n_experts][d] fp16.  experts: host array of n_experts plans.
- * workspace: device, >= ffn_moe_workspace_size bytes, caller-owned. */
+/* Bytes of device workspace the mixture needs (expert0 gives the shapes). */
 ffn_status ffn_moe_workspace_size(int32_t n_experts, int32_t top_k, const ffn_plan *expert0,
                                   size_t *bytes);
+
+/* w_router: device [n_experts][d] in the experts' x_dtype (fp16 for fp16 / int4 experts).
+ * experts: host array of n_experts plans, which must outlive the mixture (only their weights and
+ * shapes are used; their own workspaces are not touched).  workspace: device, >=
+ * ffn_moe_workspace_size bytes, caller-owned, not shared with a plan used concurrently. */
 ffn_status ffn_moe_plan(int32_t n_experts, int32_t top_k, const void *w_router,
                         ffn_plan *const *experts, void *workspace, size_t workspace_bytes,
                         ffn_moe **out);
 
-/* B tokens; y[B][d] fp32 overwritten.  expert_idx [B][top_k] int32 and expert_w [B][top_k]
- * fp32 (device, may be NULL) receive the routing decision. */
+/* B tokens x[B][d]; y[B][d] fp32 overwritten.  expert_idx [B][top_k] int32 and expert_w
+ * [B][top_k] fp32 (device, each may be NULL) receive the routing decision, best expert first. */
 ffn_status ffn_moe_forward(ffn_moe *moe, const void *x, int32_t B, float *y,
                            int32_t *expert_idx, float *expert_w, void *stream);
 ffn_status ffn_moe_destroy(ffn_moe *moe);

@@ -68,6 +68,8 @@ def test_workspace_size_valid_and_monotone_in_batch():
     (dict(ffn=32800), ffn.FFN_ERR_UNSUPPORTED),
     (dict(rank=4096), ffn.FFN_ERR_UNSUPPORTED),
     (dict(max_batch=0), ffn.FFN_ERR_INVALID_ARGUMENT),
+    (dict(d=8192, w_dtype=ffn.FFN_F32, x_dtype=ffn.FFN_F32, p_dtype=ffn.FFN_F32, rank=64),
+     ffn.FFN_ERR_UNSUPPORTED),
 ])
 def test_bad_descriptors_are_rejected(kw, status):
     with pytest.raises(ffn.FFNError) as e:
@@ -121,3 +123,40 @@ def test_no_predictor_requires_mask():
 def test_binding_loads_only_the_in_tree_library():
     assert os.path.dirname(ffn.LIB_PATH) == os.path.join(ROOT, "activation_sparse_ffn_gemv_amd")
     assert isinstance(ffn.lib(), ctypes.CDLL)
+
+
+def _fake_plan(**kw):
+    d = _desc(**kw)
+    w = ffn.ffn_layer_weights(w_up=0x1000, w_gate=0x2000, w_down_t=0x3000, p1=0x4000,
+                              p2=0x5000)
+    return ffn.ffn_sparse_plan(d, w, 0x10000, 1 << 30)
+
+
+def test_moe_validation_before_any_gpu_call():
+    e = [_fake_plan() for _ in range(3)]
+    odd = _fake_plan(rank=128)
+    try:
+        n = ffn.ffn_moe_workspace_size(3, 2, e[0])
+        assert n >= ffn.ffn_workspace_size(_desc()) and n % 256 == 0
+        for E, K in [(0, 1), (17, 2), (3, 0), (3, 4), (8, 5)]:
+            with pytest.raises(ffn.FFNError) as ex:
+                ffn.ffn_moe_workspace_size(E, K, e[0])
+            assert ex.value.status == ffn.FFN_ERR_UNSUPPORTED
+        with pytest.raises(ffn.FFNError) as ex:           # descriptors differ
+            ffn.ffn_moe_plan(2, 1, 0x8000, [e[0], odd], 0x20000, n)
+        assert ex.value.status == ffn.FFN_ERR_INVALID_ARGUMENT
+        with pytest.raises(ffn.FFNError) as ex:           # workspace too small
+            ffn.ffn_moe_plan(3, 2, 0x8000, e, 0x20000, 64)
+        assert ex.value.status == ffn.FFN_ERR_WORKSPACE_TOO_SMALL
+        m = ffn.ffn_moe_plan(3, 2, 0x8000, e, 0x20000, n)
+        try:
+            with pytest.raises(ffn.FFNError) as ex:       # B out of range
+                ffn.ffn_moe_forward(m, 0x1000, 2, 0x2000)
+            assert ex.value.status == ffn.FFN_ERR_INVALID_ARGUMENT
+            with pytest.raises(ffn.FFNError):             # NULL y
+                ffn.ffn_moe_forward(m, 0x1000, 1, 0)
+        finally:
+            ffn.ffn_moe_destroy(m)
+    finally:
+        for p in e + [odd]:
+            ffn.ffn_plan_destroy(p)

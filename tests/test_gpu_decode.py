@@ -42,7 +42,7 @@ def _run(ffn, L, x, mask=None, tau=None):
 
 
 def _check_predicted(ffn, cfg, n_tokens, layer_no=0, tau=None):
-    host = synth.make_layer(cfg, layer=layer_no)
+    host = synth.make_layer(cfg, layer=layer_no, device="cuda")
     L = to_device(host)
     OL = oracle_layer(host)
     if tau is not None:
@@ -77,6 +77,12 @@ SMALL = [
          p_dtype="f16", bias_gate=True),
     dict(d=520, ffn=1184, rank=40, act="drelu", w_dtype="f16", x_dtype="f16", p_dtype="f16",
          bias_gate=True, bias_up=True, bias_down=True),
+    dict(d=256, ffn=1024, rank=32, act="drelu", w_dtype="i4g32", x_dtype="f16", p_dtype="f16",
+         bias_gate=True, bias_up=True, bias_down=True),
+    dict(d=288, ffn=1056, rank=24, act="relu", w_dtype="i4g32", x_dtype="f16", p_dtype="f16",
+         bias_up=True),
+    dict(d=544, ffn=2080, rank=48, act="reglu", w_dtype="i4g32", x_dtype="f16", p_dtype="f16",
+         bias_gate=True),
 ]
 
 
@@ -102,13 +108,38 @@ def test_mistral_7b_shape_sampled_tokens(ffn):
     _check_predicted(ffn, synth.CONFIGS["turbosparse_mistral_7b_drelu_f16"], n_tokens=2)
 
 
+@pytest.mark.parametrize("expert", [0, 7])
+def test_mixtral_int4_expert_shape_sampled_tokens(ffn, expert):
+    """One int4 group-32 dReLU expert of the mixture workload (d=4096, ffn=14336), the least and
+    the most dense expert."""
+    cfg = synth.CONFIGS["turbosparse_mixtral_47b_moe_int4"]
+    host = synth.make_layer(cfg, layer=0, expert=expert, device="cuda")
+    L, OL = to_device(host), oracle_layer(host)
+    x = synth.make_tokens(cfg, 2, layer=0).cuda()
+    y, lists, cnt, _ = _run(ffn, L, x)
+    xh = x.cpu().numpy()
+    for t in range(2):
+        pred = oracle.predictor(OL["p1"], OL["p2"], OL["c1"], OL["c2"], xh[t], OL["tau"])
+        check_index_list(lists[t], pred, OL["tau"])
+        y_ref, _ = oracle.ffn(OL, xh[t], mask_from_idx(lists[t], cfg.ffn))
+        assert normwise(y[t], y_ref) <= TOL["i4g32"]
+    dens = np.mean(cnt) / cfg.ffn
+    assert abs(dens - cfg.expert_density[expert]) < 0.03
+
+
+def test_falcon_40b_shape_sampled_token(ffn):
+    """The widest layer (d=8192, ffn=32768, rank 1024): two column chunks per gather thread."""
+    _check_predicted(ffn, synth.CONFIGS["falcon_40b_relu_f16"], n_tokens=1)
+
+
 @pytest.mark.parametrize("act", ["relu", "reglu", "drelu"])
-@pytest.mark.parametrize("wd", ["f32", "f16"])
+@pytest.mark.parametrize("wd", ["f32", "f16", "i4g32"])
 def test_true_mask_equals_dense_on_gpu(ffn, act, wd):
     """With the mask set to the true positive set the sparse result equals the dense FFN
     (inactive neurons contribute exactly zero); with all ones it equals the dense FFN too."""
-    cfg = synth.small_config(d=256, ffn=1024, rank=0, act=act, w_dtype=wd, x_dtype=wd,
-                             p_dtype=wd, density=0.1, bias_up=True, bias_gate=True,
+    xd = "f32" if wd == "f32" else "f16"
+    cfg = synth.small_config(d=256, ffn=1024, rank=0, act=act, w_dtype=wd, x_dtype=xd,
+                             p_dtype=xd, density=0.1, bias_up=True, bias_gate=True,
                              bias_down=True)
     host = synth.make_layer(cfg)
     L, OL = to_device(host), oracle_layer(host)
