@@ -51,6 +51,29 @@ def stage_bytes(cfg):
     }
 
 
+def profiled_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` on `workload` from a committed rocprofv3 summary under
+    profiles/ (FETCH_SIZE + WRITE_SIZE, scaled against a copy of known size), or None when there
+    is none or the kernel source has changed since the counters were taken."""
+    import glob
+    import hashlib
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
+        for line in open(path):
+            f = line.split()
+            if not f or f[0] != "traffic":
+                continue
+            kv = dict(t.split("=", 1) for t in f[1:] if "=" in t)
+            if kv.get("kernel") != kernel or kv.get("workload") != workload:
+                continue
+            src = os.path.join(ROOT, kv["source"])
+            if not os.path.exists(src):
+                return None
+            if hashlib.sha256(open(src, "rb").read()).hexdigest() != kv.get("sha256"):
+                return None
+            return int(kv["bytes_per_launch"])
+    return None
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -59,8 +82,11 @@ def main():
     ap.add_argument("--config", default="llama2_7b_reglu_f16")
     ap.add_argument("--kernel-sample", type=int, default=32,
                     help="tokens whose kernel launches are timed with dispatch events")
-    ap.add_argument("--cpu-tokens", type=int, default=1,
+    ap.add_argument("--cpu-tokens", type=int, default=3,
                     help="tokens (x all layers) the CPU oracle baseline runs; 0 = skip")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="first run a plain device copy of this many MiB five times (a known "
+                         "size against which a profiler's HBM byte counters are scaled)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (the operator "
@@ -84,6 +110,16 @@ def main():
     torch.cuda.set_device(dev)
     log("config %s: d=%d ffn=%d rank=%d act=%s w=%s layers=%d tokens=%d" % (
         cfg.name, cfg.d, cfg.ffn, cfg.rank, cfg.act, cfg.w_dtype, L, K))
+
+    if args.copy_mib:
+        n = args.copy_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copy calibration: 5 x %d MiB device-to-device" % args.copy_mib)
+        del src, dst
 
     t0 = time.time()
     layers, plans = [], []
@@ -260,7 +296,8 @@ def main():
         "touched_bytes_per_token": int(touched / K),
         "roofline": {"bound": "hbm", "kernel": "k_" + dom,
                      "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": profiled_traffic("k_" + dom, cfg.name),
                      "avg_us": stages[dom]["avg_us"],
                      "bytes_per_launch": stages[dom]["bytes_per_launch"]},
         "kernels": stages,
