@@ -48,8 +48,11 @@ int cpl_for(int nch) {
 
 struct Layout {
   int cpl_w, cpl_p;
-  size_t off_z, off_bits, off_cnt, off_part, off_union, total;
+  size_t off_z, off_bits, off_cnt, off_part, off_union, off_batch, total;
 };
+
+// The batched kernels (MFMA) cover fp16 layers; other storage types run B > 1 token by token.
+bool batched(const ffn_layer_desc* d) { return d->w_dtype == FFN_F16; }
 
 ffn_status check_desc(const ffn_layer_desc* d) {
   if (!d) return fail(FFN_ERR_INVALID_ARGUMENT, "desc is NULL");
@@ -96,8 +99,58 @@ Layout layout_for(const ffn_layer_desc* d) {
   L.off_part = off;
   off = round_up(off + (size_t)gather_blocks() * reduce_tiles(d->d) * 16 * 4, 256);
   L.off_union = off;  off = round_up(off + 256, 256);
+  L.off_batch = 0;
+  if (batched(d)) {
+    // batched region: zpart | zhl | bits | ubits | ucnt | uidx | H | ypart
+    const BatchShape s = batch_shape(d->d, d->ffn, d->rank);
+    L.off_batch = off;
+    off = round_up(off + s.zpart_bytes, 256);
+    off = round_up(off + s.zhl_bytes, 256);
+    off = round_up(off + s.bits_bytes, 256);
+    off = round_up(off + s.ubits_bytes, 256);
+    off = round_up(off + 4, 256);
+    off = round_up(off + s.uidx_bytes, 256);
+    off = round_up(off + s.H_bytes, 256);
+    off = round_up(off + s.ypart_bytes, 256);
+  }
   L.total = off;
   return L;
+}
+
+// The batched region's buffers, in the order layout_for reserves them.
+BatchArgs batch_bufs(char* ws, const ffn_plan* p) {
+  const ffn_layer_desc& D = p->desc;
+  const BatchShape s = batch_shape(D.d, D.ffn, D.rank);
+  BatchArgs a{};
+  size_t off = p->off_batch;
+  a.zpart = reinterpret_cast<float*>(ws + off);        off = round_up(off + s.zpart_bytes, 256);
+  a.zhl = reinterpret_cast<_Float16*>(ws + off);       off = round_up(off + s.zhl_bytes, 256);
+  a.bits = reinterpret_cast<uint32_t*>(ws + off);      off = round_up(off + s.bits_bytes, 256);
+  a.ubits = reinterpret_cast<uint32_t*>(ws + off);     off = round_up(off + s.ubits_bytes, 256);
+  a.ucnt = reinterpret_cast<int*>(ws + off);           off = round_up(off + 4, 256);
+  a.uidx = reinterpret_cast<int*>(ws + off);           off = round_up(off + s.uidx_bytes, 256);
+  a.H = reinterpret_cast<_Float16*>(ws + off);         off = round_up(off + s.H_bytes, 256);
+  a.ypart = reinterpret_cast<float*>(ws + off);
+  a.ks = s.ks;
+  a.spw = s.spw;
+  a.S = s.S;
+  a.p1 = p->w.p1;
+  a.p2 = p->w.p2;
+  a.c1 = p->w.c1;
+  a.c2 = p->w.c2;
+  a.w_up = p->w.w_up;
+  a.w_gate = p->w.w_gate;
+  a.w_dn = p->w.w_down_t;
+  a.b_up = p->w.b_up;
+  a.b_gate = p->w.b_gate;
+  a.b_down = p->w.b_down;
+  a.d = D.d;
+  a.ffn = D.ffn;
+  a.r = D.rank;
+  a.act = D.act;
+  a.has_gate = D.act != FFN_ACT_RELU;
+  a.thr = p->thr;
+  return a;
 }
 
 
@@ -270,6 +323,7 @@ ffn_status ffn_sparse_plan(const ffn_layer_desc* desc, const ffn_layer_weights* 
   p->off_cnt = L.off_cnt;
   p->off_part = L.off_part;
   p->off_union = L.off_union;
+  p->off_batch = L.off_batch;
   const double tau = desc->threshold;
   p->thr = tau >= 1.0 ? INFINITY : (float)log(tau / (1.0 - tau));
   for (int k = 0; k < 8; ++k) p->crossover_density[k] = 1.0f;
@@ -298,6 +352,23 @@ ffn_status ffn_sparse_forward(ffn_plan* p, const void* x, int32_t B, float* y,
   if (path == FFN_PATH_DENSE) return fail(FFN_ERR_UNSUPPORTED, "dense path not built yet");
   hipStream_t st = static_cast<hipStream_t>(stream);
   const size_t xbytes = (size_t)D.d * (D.x_dtype == FFN_F32 ? 4 : 2);
+  if (B > 1 && batched(&D)) {
+    // passes of up to BATCH_TILE tokens, each reading the union of its tokens' rows once
+    for (int b0 = 0; b0 < B; b0 += BATCH_TILE) {
+      BatchArgs a = batch_bufs(p->ws, p);
+      a.B = std::min(BATCH_TILE, B - b0);
+      a.x = static_cast<const char*>(x) + b0 * xbytes;
+      a.mask = mask ? mask + (size_t)b0 * D.ffn : nullptr;
+      a.y = y + (size_t)b0 * D.d;
+      a.scores = scores ? scores + (size_t)b0 * D.ffn : nullptr;
+      a.idx_out = idx ? idx + (size_t)b0 * D.ffn : nullptr;
+      a.cnt_out = cnt ? cnt + b0 : nullptr;
+      hipError_t e = launch_batch(a, mask == nullptr, st);
+      if (e != hipSuccess) return hip_fail(e, "batched launch");
+    }
+    g_err[0] = 0;
+    return FFN_OK;
+  }
   const TokenBufs wb = token_bufs(p->ws, p);
   for (int b = 0; b < B; ++b) {
     ffn_status s = enqueue_token(p, wb, static_cast<const char*>(x) + b * xbytes,

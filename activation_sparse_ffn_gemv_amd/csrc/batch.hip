@@ -1,0 +1,453 @@
+// Batched path of the activation-sparse FFN on gfx950 (fp16 layers, 2..32 tokens per pass).
+//
+// Every token keeps its own active set; the rows read are those of the union U of the tokens'
+// sets, each read once per pass (nearauto.com, experiments, Fig. 14: batches; the pages' method
+// per token is the neuron-aware operator of PowerInfer, unite.ai "神经元感知运算符").  With up to
+// 32 tokens the per-row work is a skinny matrix product, so the contractions run on the MFMA
+// units (32x32 tiles, M = the pass's tokens, zero-padded):
+//   k_bz     Z = X P1^T, split over K            (predictor stage 1; partial sums per K slice)
+//   k_bzr    z = sum of the K slices + c1, split into fp16 hi + lo parts (z = hi + lo to ~2^-22)
+//   k_bs     S = Z P2^T + c2 (hi and lo MFMAs); per-token bitmap words by ballot; union words
+//   k_bug    for 32 union neurons (by rank) per workgroup: U = X W_up^T, G = X W_gate^T;
+//            h = act(u, g), zero where the token's own set excludes the neuron; H in fp16
+//   k_bdown  Y_s = H[:, seg s] W_down_t[U_s]: split over union segments and 256-column tiles
+//   k_bred   y = b_down + sum_s Y_s in segment order; per-token index lists and counts
+// The fp16 rounding of h (relative 2^-11 per term) is the only precision given up against the
+// batch-1 path.  No global atomics: the result is reproducible.
+//
+// MFMA lane layout (v_mfma_f32_32x32x16_f16 / 32x32x8_f16): lane l supplies row (l % 32) of A
+// and column (l % 32) of B, each with the K elements 8*(l/32) .. +7 (x16) or 4*(l/32) .. +3
+// (x8); accumulator element i of lane l is D[8*(i/4) + 4*(l/32) + i%4][l % 32].
+#include <algorithm>
+
+#include "common.h"
+#include "launch.h"
+
+namespace ffn {
+
+constexpr int MB = BATCH_TILE;     // tokens per pass
+constexpr int BT = 256;            // threads per workgroup: 4 waves
+constexpr int GRP = 8;             // 16-k steps whose loads are issued together
+constexpr int DN_CH = 512;         // union ranks staged in LDS at a time by k_bdown
+constexpr int DN_COLS = 256;       // columns of y per k_bdown workgroup
+constexpr int GRPD = 4;            // 8-rank steps whose loads k_bdown issues together
+
+typedef _Float16 h8v __attribute__((ext_vector_type(8)));
+typedef _Float16 h4v __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ f32x16 mma16(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(h8v, a),
+                                                __builtin_bit_cast(h8v, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mma8(u32x2 a, u32x2 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x8f16(__builtin_bit_cast(h4v, a),
+                                              __builtin_bit_cast(h4v, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ int acc_row(int i, int lane) {
+  return 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+}
+
+// Sum of the four waves' 32x32 accumulators in wave order; the result is valid in wave 0.
+__device__ __forceinline__ f32x16 wg_sum4(f32x16 acc, float* red /* [3][16][64] */) {
+  const int lane = threadIdx.x & (WAVE - 1), wave = threadIdx.x / WAVE;
+  __syncthreads();                      // red may still be read by a previous call
+  if (wave > 0) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) red[((wave - 1) * 16 + i) * WAVE + lane] = acc[i];
+  }
+  __syncthreads();
+  if (wave == 0) {
+#pragma unroll
+    for (int w = 0; w < 3; ++w)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[i] += red[(w * 16 + i) * WAVE + lane];
+  }
+  return acc;
+}
+
+// Union ranks [r0, r1) of segment s: segments are cut at multiples of 8 ranks (one x8 step).
+__device__ __forceinline__ void seg_range(int total, int s, int S, int& r0, int& r1) {
+  const long long units = (total + 7) / 8;
+  r0 = (int)(8 * (units * s / S));
+  r1 = (int)(8 * (units * (s + 1) / S));
+}
+
+// ---------------------------------------------------------------------------------------------
+// Predictor stage 1: workgroup (tile of 32 P1 rows, K slice); wave w of slice k takes 16-k
+// steps [(4k + w) * spw, ... + spw).
+__global__ __launch_bounds__(BT) void k_bz(BatchArgs a) {
+  __shared__ float red[3 * 16 * WAVE];
+  const int lane = threadIdx.x & (WAVE - 1), wave = threadIdx.x / WAVE;
+  const int n0 = blockIdx.x * 32, row = lane & 31, g = lane >> 5;
+  const int nchk = a.d / 8, nsteps = (nchk + 1) / 2;
+  const int s0 = (blockIdx.y * 4 + wave) * a.spw, s1 = min(nsteps, s0 + a.spw);
+  const bool pok = n0 + row < a.r, xok = row < a.B;
+  const char* pr = static_cast<const char*>(a.p1) + (size_t)min(n0 + row, a.r - 1) * a.d * 2;
+  const char* xr = static_cast<const char*>(a.x) + (size_t)min(row, a.B - 1) * a.d * 2;
+  f32x16 acc = {};
+  for (int s = s0; s < s1; s += GRP) {
+    u32x4 av[GRP], bv[GRP];
+#pragma unroll
+    for (int j = 0; j < GRP; ++j) {
+      const int c = 2 * (s + j) + g;
+      const int cc = min(c, nchk - 1);
+      const bool ok = s + j < s1 && c < nchk;
+      const u32x4 bl = ld16(pr + (size_t)cc * 16);
+      const u32x4 al = ld16(xr + (size_t)cc * 16);
+      bv[j] = (ok && pok) ? bl : u32x4{0u, 0u, 0u, 0u};
+      av[j] = (ok && xok) ? al : u32x4{0u, 0u, 0u, 0u};
+    }
+    issue_fence();
+#pragma unroll
+    for (int j = 0; j < GRP; ++j) acc = mma16(av[j], bv[j], acc);
+  }
+  acc = wg_sum4(acc, red);
+  if (wave == 0 && n0 + row < a.r) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      a.zpart[((size_t)blockIdx.y * MB + acc_row(i, lane)) * a.r + n0 + row] = acc[i];
+  }
+}
+
+// z = sum over the K slices (in order) + c1, stored as fp16 hi and lo planes.
+__global__ __launch_bounds__(256) void k_bzr(BatchArgs a) {
+  const int e = blockIdx.x * 256 + threadIdx.x;       // m * r + k
+  if (e >= MB * a.r) return;
+  const int k = e % a.r;
+  float z = 0.0f;
+  for (int q = 0; q < a.ks; ++q) z += a.zpart[(size_t)q * MB * a.r + e];
+  if (a.c1) z += a.c1[k];
+  const _Float16 hi = (_Float16)z;
+  const _Float16 lo = (_Float16)(z - (float)hi);
+  a.zhl[e] = hi;
+  a.zhl[(size_t)MB * a.r + e] = lo;
+}
+
+// Predictor stage 2 for 32 neurons (one bitmap word per token): S = Z P2^T + c2.
+__global__ __launch_bounds__(BT) void k_bs(BatchArgs a) {
+  __shared__ float red[3 * 16 * WAVE];
+  const int lane = threadIdx.x & (WAVE - 1), wave = threadIdx.x / WAVE;
+  const int n0 = blockIdx.x * 32, row = lane & 31, g = lane >> 5;
+  const int rch = a.r / 8, nsteps = (rch + 1) / 2;
+  const char* pr = static_cast<const char*>(a.p2) + (size_t)(n0 + row) * a.r * 2;
+  const char* zh = reinterpret_cast<const char*>(a.zhl + (size_t)row * a.r);
+  const char* zl = reinterpret_cast<const char*>(a.zhl + (size_t)(MB + row) * a.r);
+  f32x16 acc = {};
+  for (int s0 = wave; s0 < nsteps; s0 += 4 * GRP) {
+    u32x4 ah[GRP], al[GRP], bv[GRP];
+#pragma unroll
+    for (int j = 0; j < GRP; ++j) {
+      const int c = 2 * (s0 + 4 * j) + g;
+      const int cc = min(c, rch - 1);
+      const bool ok = s0 + 4 * j < nsteps && c < rch;
+      const u32x4 bl = ld16(pr + (size_t)cc * 16);
+      ah[j] = ld16(zh + (size_t)cc * 16);
+      al[j] = ld16(zl + (size_t)cc * 16);
+      bv[j] = ok ? bl : u32x4{0u, 0u, 0u, 0u};
+    }
+    issue_fence();
+#pragma unroll
+    for (int j = 0; j < GRP; ++j) {
+      acc = mma16(ah[j], bv[j], acc);
+      acc = mma16(al[j], bv[j], acc);
+    }
+  }
+  acc = wg_sum4(acc, red);
+  if (wave == 0) {
+    const int W = a.ffn / 32;
+    const float c2v = a.c2 ? a.c2[n0 + row] : 0.0f;
+    uint32_t uw = 0u;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int m = acc_row(i, lane);
+      const float sc = acc[i] + c2v;
+      const bool on = sc > a.thr && m < a.B;
+      if (a.scores && m < a.B) a.scores[(size_t)m * a.ffn + n0 + row] = sc;
+      const unsigned long long bal = __ballot(on);
+      const int m0 = 8 * (i >> 2) + (i & 3);          // lanes 0..31: token m0; 32..63: m0 + 4
+      if (lane == 0) a.bits[(size_t)m0 * W + blockIdx.x] = (uint32_t)bal;
+      if (lane == 32) a.bits[(size_t)(m0 + 4) * W + blockIdx.x] = (uint32_t)(bal >> 32);
+      uw |= (uint32_t)bal | (uint32_t)(bal >> 32);
+    }
+    if (lane == 0) a.ubits[blockIdx.x] = uw;
+  }
+}
+
+// Caller masks -> per-token bitmap words and the union words (one thread per word).
+__global__ __launch_bounds__(256) void k_bmask(BatchArgs a) {
+  const int w = blockIdx.x * 256 + threadIdx.x;
+  const int W = a.ffn / 32;
+  if (w >= W) return;
+  uint32_t uw = 0u;
+  for (int m = 0; m < MB; ++m) {
+    uint32_t bw = 0u;
+    if (m < a.B) {
+      if (a.mask) {
+        const u32x4* mp = reinterpret_cast<const u32x4*>(a.mask + (size_t)m * a.ffn + w * 32);
+        const u32x4 q0 = mp[0], q1 = mp[1];
+        const uint32_t v[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+#pragma unroll
+          for (int t = 0; t < 4; ++t)
+            if ((v[k] >> (8 * t)) & 0xffu) bw |= 1u << (4 * k + t);
+      } else {
+        bw = 0xffffffffu;                               // dense: every neuron
+      }
+    }
+    a.bits[(size_t)m * W + w] = bw;
+    uw |= bw;
+  }
+  a.ubits[w] = uw;
+}
+
+// Rows of 32 union neurons (ranks [32 b, 32 b + 32)): u, g on the MFMA units, then h.
+__global__ __launch_bounds__(BT) void k_bug(BatchArgs a) {
+  __shared__ int s_wsum[BT / WAVE];
+  __shared__ int s_nid[32];
+  __shared__ float red[3 * 16 * WAVE];
+  const int tid = threadIdx.x, lane = tid & (WAVE - 1), wave = tid / WAVE;
+  const int W = a.ffn / 32;
+  constexpr int WPT = 4;                                // bitmap words per thread (ffn <= 32768)
+  // 1. union ranks: prefix of popcounts over the words (thread t owns words 4t .. 4t+3)
+  uint32_t bw[WPT];
+  int local = 0;
+#pragma unroll
+  for (int k = 0; k < WPT; ++k) {
+    const int w = tid * WPT + k;
+    bw[k] = w < W ? a.ubits[w] : 0u;
+    local += __popc(bw[k]);
+  }
+  int v = local;
+#pragma unroll
+  for (int o = 1; o < WAVE; o <<= 1) {
+    const int u = __shfl_up(v, o, WAVE);
+    if (lane >= o) v += u;
+  }
+  if (lane == WAVE - 1) s_wsum[wave] = v;
+  if (tid < 32) s_nid[tid] = -1;
+  __syncthreads();
+  int base = 0, total = 0;
+#pragma unroll
+  for (int k = 0; k < BT / WAVE; ++k) {
+    base += k < wave ? s_wsum[k] : 0;
+    total += s_wsum[k];
+  }
+  if (blockIdx.x == 0 && tid == 0) *a.ucnt = total;
+  const int t0 = blockIdx.x * 32;
+  if (t0 >= total) return;                              // uniform over the workgroup
+  const int run0 = base + v - local;
+  if (run0 < t0 + 32 && run0 + local > t0) {
+    int pos = run0;
+#pragma unroll
+    for (int k = 0; k < WPT; ++k) {
+      uint32_t bb = bw[k];
+      const int nb = (tid * WPT + k) * 32;
+      while (bb) {
+        if (pos >= t0 && pos < t0 + 32) {
+          const int nid = nb + __builtin_ctz(bb);
+          s_nid[pos - t0] = nid;
+          a.uidx[pos] = nid;
+        }
+        bb &= bb - 1;
+        ++pos;
+      }
+    }
+  }
+  __syncthreads();
+
+  // 2. U = X W_up^T and G = X W_gate^T for the 32 neurons, K split over the waves
+  const int row = lane & 31, g = lane >> 5;
+  const int nid = s_nid[row];
+  const size_t rowoff = (size_t)max(nid, 0) * a.d * 2;
+  const char* up = static_cast<const char*>(a.w_up) + rowoff;
+  const char* gp = static_cast<const char*>(a.has_gate ? a.w_gate : a.w_up) + rowoff;
+  const char* xr = static_cast<const char*>(a.x) + (size_t)min(row, a.B - 1) * a.d * 2;
+  const bool xok = row < a.B;
+  const int nchk = a.d / 8, nsteps = (nchk + 1) / 2;
+  f32x16 au = {}, ag = {};
+  for (int s0 = wave; s0 < nsteps; s0 += 4 * GRP) {
+    u32x4 xv[GRP], uv[GRP], gv[GRP];
+#pragma unroll
+    for (int j = 0; j < GRP; ++j) {
+      const int c = 2 * (s0 + 4 * j) + g;
+      const int cc = min(c, nchk - 1);
+      const bool ok = s0 + 4 * j < nsteps && c < nchk;
+      const u32x4 xl = ld16(xr + (size_t)cc * 16);
+      uv[j] = ld16(up + (size_t)cc * 16);
+      gv[j] = a.has_gate ? ld16(gp + (size_t)cc * 16) : u32x4{0u, 0u, 0u, 0u};
+      xv[j] = (ok && xok) ? xl : u32x4{0u, 0u, 0u, 0u};
+    }
+    issue_fence();
+#pragma unroll
+    for (int j = 0; j < GRP; ++j) {
+      au = mma16(xv[j], uv[j], au);
+      if (a.has_gate) ag = mma16(xv[j], gv[j], ag);
+    }
+  }
+  au = wg_sum4(au, red);
+  if (a.has_gate) ag = wg_sum4(ag, red);
+
+  // 3. h per (token, neuron), masked by the token's own set; H column = union rank
+  if (wave == 0) {
+    const float bu = (nid >= 0 && a.b_up) ? a.b_up[nid] : 0.0f;
+    const float bg = (nid >= 0 && a.b_gate) ? a.b_gate[nid] : 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int m = acc_row(i, lane);
+      const float u = au[i] + bu;
+      float h;
+      if (a.act == FFN_ACT_RELU) {
+        h = fmaxf(u, 0.0f);
+      } else {
+        const float gg = fmaxf(ag[i] + bg, 0.0f);
+        h = a.act == FFN_ACT_REGLU ? gg * u : gg * fmaxf(u, 0.0f);
+      }
+      bool on = false;
+      if (nid >= 0 && m < a.B) on = (a.bits[(size_t)m * W + (nid >> 5)] >> (nid & 31)) & 1u;
+      a.H[(size_t)m * a.ffn + t0 + row] = (_Float16)(on ? h : 0.0f);
+    }
+  }
+}
+
+// Y_s[:, c0 .. c0+256) = H[:, U_s] W_down_t[U_s, c0 .. c0+256); K (union ranks) split over the
+// waves, each rank's down row read as 16-byte column chunks.  Lane (p, g) loads columns
+// c0 + 8p .. c0 + 8p + 7 of four rows; element b of those chunks feeds MFMA block b, whose
+// output column p is y column c0 + 8p + b.
+__global__ __launch_bounds__(BT) void k_bdown(BatchArgs a) {
+  __shared__ int s_nid[DN_CH];
+  __shared__ float s_y[MB * DN_COLS];
+  const int tid = threadIdx.x, lane = tid & (WAVE - 1), wave = tid / WAVE;
+  const int total = *a.ucnt;
+  int r0, r1;
+  seg_range(total, blockIdx.y, a.S, r0, r1);
+  if (r0 >= r1) return;                                 // uniform: segment is empty
+  const int c0 = blockIdx.x * DN_COLS, p = lane & 31, g = lane >> 5;
+  const int col = min(c0 + 8 * p, a.d - 8);
+  const char* dn = static_cast<const char*>(a.w_dn) + (size_t)col * 2;
+  const char* hr = reinterpret_cast<const char*>(a.H + (size_t)p * a.ffn);
+  f32x16 acc[8];
+#pragma unroll
+  for (int b = 0; b < 8; ++b) acc[b] = f32x16{};
+  for (int q0 = r0; q0 < r1; q0 += DN_CH) {
+    const int nq = min(DN_CH, r1 - q0);                 // a multiple of 8
+    __syncthreads();
+    for (int t = tid; t < nq; t += BT) s_nid[t] = q0 + t < total ? a.uidx[q0 + t] : 0;
+    __syncthreads();
+    const int nst = nq / 8;
+    for (int s0 = wave; s0 < nst; s0 += 4 * GRPD) {
+      u32x2 av[GRPD];
+      u32x4 bv[GRPD][4];
+#pragma unroll
+      for (int j = 0; j < GRPD; ++j) {
+        const int s = s0 + 4 * j;
+        const bool ok = s < nst;
+        const int kb = 8 * min(s, nst - 1) + 4 * g;     // rank offset within the chunk
+        const u32x2 hl = *reinterpret_cast<const u32x2*>(hr + (size_t)(q0 + kb) * 2);
+        av[j] = ok ? hl : u32x2{0u, 0u};
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+          bv[j][jj] = ld16(dn + (size_t)s_nid[kb + jj] * a.d * 2);
+      }
+      issue_fence();
+#pragma unroll
+      for (int j = 0; j < GRPD; ++j) {
+        const uint32_t w0[4] = {bv[j][0].x, bv[j][0].y, bv[j][0].z, bv[j][0].w};
+        const uint32_t w1[4] = {bv[j][1].x, bv[j][1].y, bv[j][1].z, bv[j][1].w};
+        const uint32_t w2[4] = {bv[j][2].x, bv[j][2].y, bv[j][2].z, bv[j][2].w};
+        const uint32_t w3[4] = {bv[j][3].x, bv[j][3].y, bv[j][3].z, bv[j][3].w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          // column 8p + 2q (low halves) and 8p + 2q + 1 (high halves) of the four rows
+          const u32x2 blo = {__builtin_amdgcn_perm(w1[q], w0[q], 0x05040100u),
+                             __builtin_amdgcn_perm(w3[q], w2[q], 0x05040100u)};
+          const u32x2 bhi = {__builtin_amdgcn_perm(w1[q], w0[q], 0x07060302u),
+                             __builtin_amdgcn_perm(w3[q], w2[q], 0x07060302u)};
+          acc[2 * q] = mma8(av[j], blo, acc[2 * q]);
+          acc[2 * q + 1] = mma8(av[j], bhi, acc[2 * q + 1]);
+        }
+      }
+    }
+  }
+  // sum the waves' tiles in wave order through LDS, then write this segment's partial
+  for (int w = 0; w < 4; ++w) {
+    if (wave == w) {
+#pragma unroll
+      for (int b = 0; b < 8; ++b)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float& dst = s_y[acc_row(i, lane) * DN_COLS + 8 * p + b];
+          dst = w == 0 ? acc[b][i] : dst + acc[b][i];
+        }
+    }
+    __syncthreads();
+  }
+  for (int e = tid; e < MB * DN_COLS / 4; e += BT) {
+    const int m = e / (DN_COLS / 4), c4 = e % (DN_COLS / 4);
+    const int cc = c0 + 4 * c4;
+    if (m < a.B && cc < a.d)
+      *reinterpret_cast<f32x4*>(a.ypart + ((size_t)blockIdx.y * MB + m) * a.d + cc) =
+          *reinterpret_cast<const f32x4*>(&s_y[m * DN_COLS + 4 * c4]);
+  }
+}
+
+// y = b_down + sum of the non-empty segments' partials (in segment order); workgroup (0, m)
+// also writes token m's ascending index list and count.
+__global__ __launch_bounds__(256) void k_bred(BatchArgs a) {
+  const int m = blockIdx.y;
+  const int col = (blockIdx.x * 256 + threadIdx.x) * 4;
+  const int total = *a.ucnt;
+  if (col < a.d) {
+    f32x4 t = {0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < a.S; ++s) {
+      int r0, r1;
+      seg_range(total, s, a.S, r0, r1);
+      if (r0 < r1) t += *reinterpret_cast<const f32x4*>(a.ypart + ((size_t)s * MB + m) * a.d + col);
+    }
+    if (a.b_down) t += *reinterpret_cast<const f32x4*>(a.b_down + col);
+    *reinterpret_cast<f32x4*>(a.y + (size_t)m * a.d + col) = t;
+  }
+  if (blockIdx.x == 0 && (a.idx_out || a.cnt_out))
+    write_index_list<256>(a.bits + (size_t)m * (a.ffn / 32), a.ffn / 32,
+                          a.idx_out ? a.idx_out + (size_t)m * a.ffn : nullptr,
+                          a.cnt_out ? a.cnt_out + m : nullptr);
+}
+
+// ---------------------------------------------------------------------------------------------
+// Host side.
+BatchShape batch_shape(int d, int ffn, int r) {
+  BatchShape s{};
+  const int tiles = (r + 31) / 32;
+  const int nsteps = (d / 8 + 1) / 2;
+  s.ks = r > 0 ? std::max(1, std::min({32, 256 / std::max(tiles, 1), nsteps / 4})) : 1;
+  s.spw = (nsteps + s.ks * 4 - 1) / (s.ks * 4);
+  const int ctiles = (d + DN_COLS - 1) / DN_COLS;
+  s.S = std::max(1, std::min(64, 256 / ctiles));
+  s.zpart_bytes = (size_t)s.ks * MB * std::max(r, 1) * 4;
+  s.zhl_bytes = (size_t)2 * MB * std::max(r, 1) * 2;
+  s.bits_bytes = (size_t)MB * (ffn / 32) * 4;
+  s.ubits_bytes = (size_t)(ffn / 32) * 4;
+  s.uidx_bytes = (size_t)ffn * 4;
+  s.H_bytes = (size_t)MB * ffn * 2;
+  s.ypart_bytes = (size_t)s.S * MB * d * 4;
+  return s;
+}
+
+hipError_t launch_batch(const BatchArgs& a, int use_predictor, hipStream_t st) {
+  const int W = a.ffn / 32;
+  if (use_predictor) {
+    hipLaunchKernelGGL(k_bz, dim3((a.r + 31) / 32, a.ks), dim3(BT), 0, st, a);
+    hipLaunchKernelGGL(k_bzr, dim3((MB * a.r + 255) / 256), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(k_bs, dim3(W), dim3(BT), 0, st, a);
+  } else {
+    hipLaunchKernelGGL(k_bmask, dim3((W + 255) / 256), dim3(256), 0, st, a);
+  }
+  hipLaunchKernelGGL(k_bug, dim3(W), dim3(BT), 0, st, a);
+  hipLaunchKernelGGL(k_bdown, dim3((a.d + DN_COLS - 1) / DN_COLS, a.S), dim3(BT), 0, st, a);
+  hipLaunchKernelGGL(k_bred, dim3((a.d + 1023) / 1024, a.B), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace ffn

@@ -159,6 +159,45 @@ __device__ __forceinline__ void i4_perm_x(u32x4* xs) {
   }
 }
 
+// Ascending list of the set bits of bitmap[0 .. words) (neuron w*32 + b for bit b of word w) and
+// its length, written by one workgroup of NT threads.  idx_out / cnt_out may each be nullptr.
+template <int NT>
+__device__ void write_index_list(const uint32_t* __restrict__ bitmap, int words,
+                                 int* __restrict__ idx_out, int* __restrict__ cnt_out) {
+  __shared__ int s_ws[NT / WAVE];
+  const int tid = threadIdx.x, lane = tid & (WAVE - 1), wave = tid / WAVE;
+  int before = 0;
+  for (int w0 = 0; w0 < words; w0 += NT) {
+    const int w = w0 + tid;
+    const uint32_t b = w < words ? bitmap[w] : 0u;
+    const int c = __popc(b);
+    int v = c;
+#pragma unroll
+    for (int o = 1; o < WAVE; o <<= 1) {
+      const int u = __shfl_up(v, o, WAVE);
+      if (lane >= o) v += u;
+    }
+    __syncthreads();
+    if (lane == WAVE - 1) s_ws[wave] = v;
+    __syncthreads();
+    int base = before, tot = 0;
+    for (int k = 0; k < NT / WAVE; ++k) {
+      base += k < wave ? s_ws[k] : 0;
+      tot += s_ws[k];
+    }
+    if (idx_out) {
+      int pos = base + v - c;
+      uint32_t bb = b;
+      while (bb) {
+        idx_out[pos++] = w * 32 + __builtin_ctz(bb);
+        bb &= bb - 1;
+      }
+    }
+    before += tot;
+  }
+  if (tid == 0 && cnt_out) *cnt_out = before;
+}
+
 }  // namespace ffn
 
 // ----------------------------------------------------------------------------------------------
@@ -172,6 +211,7 @@ struct ffn_plan {
   int cpl_p;         // 16-byte chunks per lane for a predictor P1 row
   float thr;         // logit(threshold): active iff score > thr
   size_t off_z, off_bits, off_cnt, off_part, off_union;
+  size_t off_batch;  // batched-path region (fp16 layers with max_batch > 1), else 0
   float crossover_density[8];   // per batch bucket 1,2,4,...,128
   int dense_min_batch;          // AUTO takes the dense path from this batch size on
   hipEvent_t ev[4][2];          // instrumentation events attached to each stage's dispatch

@@ -471,42 +471,6 @@ constexpr int RD_G = RD_THREADS / RD_Q;                // partial groups
 constexpr int RD_UNROLL = GA_BLOCKS / RD_G;
 static_assert(GA_BLOCKS % RD_G == 0, "whole partial groups");
 
-__device__ void write_index_list(const uint32_t* __restrict__ bitmap, int words,
-                                 int* __restrict__ idx_out, int* __restrict__ cnt_out) {
-  __shared__ int s_ws[RD_THREADS / WAVE];
-  const int tid = threadIdx.x, lane = tid & (WAVE - 1), wave = tid / WAVE;
-  int before = 0;
-  for (int w0 = 0; w0 < words; w0 += RD_THREADS) {
-    const int w = w0 + tid;
-    const uint32_t b = w < words ? bitmap[w] : 0u;
-    const int c = __popc(b);
-    int v = c;
-#pragma unroll
-    for (int o = 1; o < WAVE; o <<= 1) {
-      const int u = __shfl_up(v, o, WAVE);
-      if (lane >= o) v += u;
-    }
-    __syncthreads();
-    if (lane == WAVE - 1) s_ws[wave] = v;
-    __syncthreads();
-    int base = before, tot = 0;
-    for (int k = 0; k < RD_THREADS / WAVE; ++k) {
-      base += k < wave ? s_ws[k] : 0;
-      tot += s_ws[k];
-    }
-    if (idx_out) {
-      int pos = base + v - c;
-      uint32_t bb = b;
-      while (bb) {
-        idx_out[pos++] = w * 32 + __builtin_ctz(bb);
-        bb &= bb - 1;
-      }
-    }
-    before += tot;
-  }
-  if (tid == 0 && cnt_out) *cnt_out = before;
-}
-
 __global__ __launch_bounds__(RD_THREADS) void k_reduce(ReduceArgs a) {
   __shared__ f32x4 s[RD_G][RD_Q];
   const int q = threadIdx.x % RD_Q;          // float4 column within the tile
@@ -547,7 +511,7 @@ __global__ __launch_bounds__(RD_THREADS) void k_reduce(ReduceArgs a) {
     *reinterpret_cast<f32x4*>(a.y + j) = t;
   }
   if (blockIdx.x == 0 && (a.idx_out || a.cnt_out))
-    write_index_list(a.bitmap, a.ffn / 32, a.idx_out, a.cnt_out);
+    write_index_list<RD_THREADS>(a.bitmap, a.ffn / 32, a.idx_out, a.cnt_out);
   FFN_TS(2, 5);
 }
 

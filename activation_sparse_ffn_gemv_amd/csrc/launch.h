@@ -97,4 +97,39 @@ hipError_t launch_reduce(const ReduceArgs& a, hipStream_t st, hipEvent_t ev0 = n
                          hipEvent_t ev1 = nullptr);
 hipError_t launch_router(const RouterArgs& a, int B, hipStream_t st);
 
+// Batched path (fp16 layers): up to BATCH_TILE tokens per pass share one read of the union of
+// their active neurons' rows.
+constexpr int BATCH_TILE = 32;
+
+struct BatchArgs {
+  const void* x;              // [B][d] fp16, this pass's tokens
+  const uint8_t* mask;        // [B][ffn] caller sets (k_bmask; nullptr there = every neuron)
+  const void *p1, *p2;
+  const float *c1, *c2;
+  const void *w_up, *w_gate, *w_dn;
+  const float *b_up, *b_gate, *b_down;
+  float* zpart;               // [ks][BATCH_TILE][r] partial sums of predictor stage 1
+  _Float16* zhl;              // [2][BATCH_TILE][r] z as fp16 hi + lo
+  uint32_t* bits;             // [BATCH_TILE][ffn/32] per-token active bitmaps
+  uint32_t* ubits;            // [ffn/32] union bitmap
+  int* ucnt;                  // [1] |U|
+  int* uidx;                  // [ffn] union neurons by rank
+  _Float16* H;                // [BATCH_TILE][ffn] h per token, column = union rank
+  float* ypart;               // [S][BATCH_TILE][d] per-segment partials of y
+  float* y;                   // [B][d]
+  float* scores;              // [B][ffn] or nullptr
+  int* idx_out;               // [B][ffn] or nullptr
+  int* cnt_out;               // [B] or nullptr
+  int B, d, ffn, r, act, has_gate;
+  int ks, spw, S;
+  float thr;
+};
+
+struct BatchShape {
+  int ks, spw, S;
+  size_t zpart_bytes, zhl_bytes, bits_bytes, ubits_bytes, uidx_bytes, H_bytes, ypart_bytes;
+};
+BatchShape batch_shape(int d, int ffn, int r);
+hipError_t launch_batch(const BatchArgs& a, int use_predictor, hipStream_t st);
+
 }  // namespace ffn

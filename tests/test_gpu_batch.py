@@ -1,0 +1,122 @@
+"""GPU parity of the batched path (fp16 layers, several tokens per call: the union of the tokens'
+active sets is read once per pass of up to 32 tokens, each token keeps its own set) against the
+CPU oracle, through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from parity import TOL, check_index_list, mask_from_idx, normwise, oracle_layer, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ffn():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import activation_sparse_ffn_gemv_amd as m
+    return m
+
+
+def _run(ffn, L, x, mask=None):
+    B = x.shape[0]
+    F = L["w_up"].shape[0]
+    m = ffn.SparseFFN(L, max_batch=B)
+    y = torch.full((B, m.d), float("nan"), dtype=torch.float32, device="cuda")
+    idx = torch.full((B, F), -1, dtype=torch.int32, device="cuda")
+    cnt = torch.full((B,), -1, dtype=torch.int32, device="cuda")
+    scores = torch.zeros((B, F), dtype=torch.float32, device="cuda")
+    m.forward(x, y=y, mask=mask, idx=idx, cnt=cnt, scores=scores)
+    torch.cuda.synchronize()
+    cnt_h, idx_h = cnt.cpu().numpy(), idx.cpu().numpy()
+    lists = [idx_h[b, :cnt_h[b]] for b in range(B)]
+    m.close()
+    return y.cpu().numpy(), lists, cnt_h, scores.cpu().numpy()
+
+
+def _check(ffn, cfg, B, tokens=None, layer_dev="cuda"):
+    host = synth.make_layer(cfg, device=layer_dev)
+    L, OL = to_device(host), oracle_layer(host)
+    x = synth.make_tokens(cfg, B).cuda()
+    y, lists, cnt, scores = _run(ffn, L, x)
+    xh = x.cpu().numpy()
+    union = set()
+    for t in (range(B) if tokens is None else tokens):
+        pred = oracle.predictor(OL["p1"], OL["p2"], OL["c1"], OL["c2"], xh[t], OL["tau"])
+        check_index_list(lists[t], pred, OL["tau"])
+        assert cnt[t] == len(lists[t])
+        assert normwise(scores[t], pred["s"]) <= 2e-3
+        y_ref, _ = oracle.ffn(OL, xh[t], mask_from_idx(lists[t], cfg.ffn))
+        e = normwise(y[t], y_ref)
+        assert e <= TOL["f16"], (t, e)
+    for t in range(B):
+        union |= set(lists[t].tolist())
+    return y, lists, len(union)
+
+
+BATCH_SHAPES = [
+    dict(d=512, ffn=2048, rank=64, act="relu", bias_up=True, bias_down=True),
+    dict(d=1024, ffn=4128, rank=128, act="reglu", bias_gate=True),
+    dict(d=520, ffn=1184, rank=40, act="drelu", bias_gate=True, bias_up=True, bias_down=True),
+    dict(d=136, ffn=1056, rank=24, act="reglu", bias_gate=True),
+]
+
+
+@pytest.mark.parametrize("B", [2, 7, 32, 33, 45])
+@pytest.mark.parametrize("kw", BATCH_SHAPES, ids=lambda k: "%s_d%d_f%d" % (k["act"], k["d"],
+                                                                          k["ffn"]))
+def test_batched_predicted_path(ffn, kw, B):
+    cfg = synth.small_config(w_dtype="f16", x_dtype="f16", p_dtype="f16", density=0.1, **kw)
+    _check(ffn, cfg, B)
+
+
+def test_batched_caller_masks(ffn):
+    """Per-token caller masks: each token's result is the oracle over its own mask; the lists
+    returned are exactly the masks."""
+    cfg = synth.small_config(d=256, ffn=1024, rank=0, act="drelu", w_dtype="f16", x_dtype="f16",
+                             p_dtype="f16", density=0.1, bias_gate=True, bias_up=True,
+                             bias_down=True)
+    host = synth.make_layer(cfg)
+    L, OL = to_device(host), oracle_layer(host)
+    B = 9
+    x = synth.make_tokens(cfg, B).cuda()
+    rng = np.random.default_rng(11)
+    masks = (rng.random((B, cfg.ffn)) < rng.uniform(0.0, 0.4, size=(B, 1))).astype(np.uint8)
+    masks[3] = 0                                   # one token with an empty set
+    masks[5] = 1                                   # one with every neuron
+    y, lists, cnt, _ = _run(ffn, L, x, mask=torch.from_numpy(masks).cuda())
+    xh = x.cpu().numpy()
+    for t in range(B):
+        assert np.array_equal(lists[t], np.nonzero(masks[t])[0])
+        y_ref, _ = oracle.ffn(OL, xh[t], masks[t])
+        assert normwise(y[t], y_ref) <= TOL["f16"]
+    assert np.array_equal(y[3], np.asarray(OL["b_down"], np.float32))
+
+
+def test_batched_deterministic_and_close_to_single(ffn):
+    cfg = synth.small_config(d=512, ffn=2048, rank=64, act="reglu", w_dtype="f16",
+                             x_dtype="f16", p_dtype="f16", density=0.1, bias_gate=True)
+    L = to_device(synth.make_layer(cfg))
+    x = synth.make_tokens(cfg, 12).cuda()
+    yb, lb, _, _ = _run(ffn, L, x)
+    yb2, _, _, _ = _run(ffn, L, x)
+    assert np.array_equal(yb, yb2)
+    for t in (0, 5, 11):
+        y1, l1, _, _ = _run(ffn, L, x[t:t + 1])
+        assert np.array_equal(l1[0], lb[t])
+        assert normwise(yb[t], y1[0].astype(np.float64)) <= 1e-3
+
+
+def test_llama2_7b_shape_batch8(ffn):
+    _, lists, nu = _check(ffn, synth.CONFIGS["llama2_7b_reglu_f16"], 8, tokens=[0, 7])
+    assert nu > max(len(a) for a in lists)
+
+
+@pytest.mark.parametrize("B", [8, 32])
+def test_falcon_40b_shape_batched(ffn, B):
+    """The 8192 x 32768 ReLU layer at batch 8 and 32 (the union grows with the batch)."""
+    cfg = synth.CONFIGS["falcon_40b_relu_f16"]
+    _, lists, nu = _check(ffn, cfg, B, tokens=[0, B // 2, B - 1])
+    assert nu / cfg.ffn > 0.3

@@ -196,9 +196,12 @@ def test_fig8_split_additive_on_gpu(ffn):
     assert normwise(ys[0] + ys[1], ys[2]) <= 1e-5
 
 
-def test_batch_equals_single_tokens_and_is_deterministic(ffn):
-    cfg = synth.small_config(d=512, ffn=2048, rank=64, act="reglu", w_dtype="f16",
-                             x_dtype="f16", p_dtype="f16", density=0.1, bias_gate=True)
+@pytest.mark.parametrize("wd", ["f32", "i4g32"])
+def test_batch_equals_single_tokens_and_is_deterministic(ffn, wd):
+    """fp32 and int4 layers run a batch token by token: bit-identical to single-token calls."""
+    xd = "f32" if wd == "f32" else "f16"
+    cfg = synth.small_config(d=512, ffn=2048, rank=64, act="reglu", w_dtype=wd, x_dtype=xd,
+                             p_dtype=xd, density=0.1, bias_gate=True)
     L = to_device(synth.make_layer(cfg))
     x = synth.make_tokens(cfg, 5).cuda()
     yb, lb, _, _ = _run(ffn, L, x)

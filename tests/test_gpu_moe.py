@@ -28,12 +28,14 @@ def ffn():
 
 
 def _expert_sets(ffn, L, x):
-    """Active lists of every token under one expert, from the single-expert forward."""
-    m = ffn.SparseFFN(L, max_batch=x.shape[0])
+    """Active lists of every token under one expert, from the single-expert forward (token by
+    token, the kernels the mixture runs)."""
+    m = ffn.SparseFFN(L, max_batch=1)
     F = L["w_up"].shape[0]
     idx = torch.zeros(x.shape[0], F, dtype=torch.int32, device="cuda")
     cnt = torch.zeros(x.shape[0], dtype=torch.int32, device="cuda")
-    m.forward(x, idx=idx, cnt=cnt)
+    for t in range(x.shape[0]):
+        m.forward(x[t:t + 1], idx=idx[t:t + 1], cnt=cnt[t:t + 1])
     torch.cuda.synchronize()
     out = [idx[b, :int(cnt[b])].cpu().numpy() for b in range(x.shape[0])]
     m.close()
@@ -110,8 +112,8 @@ def test_identical_experts_reduce_to_one_ffn(ffn):
     x = synth.make_tokens(cfg, 3).cuda()
     moe = ffn.MoEFFN([L] * 4, R, top_k=2, max_batch=3)
     y_moe = moe.forward(x).clone()
-    single = ffn.SparseFFN(L, max_batch=3)
-    y_one = single.forward(x).clone()
+    single = ffn.SparseFFN(L, max_batch=1)             # token by token, as the mixture runs
+    y_one = torch.cat([single.forward(x[t:t + 1]).clone() for t in range(3)])
     torch.cuda.synchronize()
     for t in range(3):
         assert normwise(y_moe[t].cpu().numpy(), y_one[t].cpu().numpy().astype(np.float64)) <= 1e-5
