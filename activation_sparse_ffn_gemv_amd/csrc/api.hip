@@ -201,11 +201,12 @@ TokenBufs token_bufs(char* ws, const ffn_plan* p) {
 // result to y.
 ffn_status enqueue_token(const ffn_plan* p, const TokenBufs& wb, const void* xb,
                          const uint8_t* maskb, float* yb, int* idxb, int* cntb, float* scoresb,
-                         const ExpertW* slot, int accumulate, hipStream_t st) {
+                         const ExpertW* slot, int accumulate, hipStream_t st,
+                         bool all_neurons = false) {
   const ffn_layer_desc& D = p->desc;
   const int wk = D.w_dtype == FFN_F32 ? WK_F32 : D.w_dtype == FFN_F16 ? WK_F16 : WK_I4;
   hipError_t e;
-  if (maskb) {
+  if (maskb || all_neurons) {
     e = launch_mask_bits(maskb, wb.bits, D.ffn / 32, st);
     if (e != hipSuccess) return hip_fail(e, "mask launch");
   } else {
@@ -326,8 +327,10 @@ ffn_status ffn_sparse_plan(const ffn_layer_desc* desc, const ffn_layer_weights* 
   p->off_batch = L.off_batch;
   const double tau = desc->threshold;
   p->thr = tau >= 1.0 ? INFINITY : (float)log(tau / (1.0 - tau));
+  // built-in table: the batched kernels read the union of the tokens' rows, which never costs
+  // more than every row, so the union is kept (crossover 1) until calibration says otherwise
   for (int k = 0; k < 8; ++k) p->crossover_density[k] = 1.0f;
-  p->dense_min_batch = 1 << 30;
+  p->dense_min_batch = 2;
   (void)stream;
   (void)calibrate;
   *out = p;
@@ -349,11 +352,24 @@ ffn_status ffn_sparse_forward(ffn_plan* p, const void* x, int32_t B, float* y,
     return fail(FFN_ERR_INVALID_ARGUMENT, "path %d is not an ffn_path", path);
   if (!aligned16(x) || !aligned16(y))
     return fail(FFN_ERR_INVALID_ARGUMENT, "x / y not 16-byte aligned");
-  if (path == FFN_PATH_DENSE) return fail(FFN_ERR_UNSUPPORTED, "dense path not built yet");
   hipStream_t st = static_cast<hipStream_t>(stream);
   const size_t xbytes = (size_t)D.d * (D.x_dtype == FFN_F32 ? 4 : 2);
-  if (B > 1 && batched(&D)) {
-    // passes of up to BATCH_TILE tokens, each reading the union of its tokens' rows once
+  // Path: fp32 / int4 layers always run the per-token kernels (they have no MFMA path; the
+  // dense request gives the same result over the same sets).  fp16: SPARSE runs the batch-1
+  // kernels for one token and the batched kernels for more; DENSE and AUTO run the batched
+  // kernels with the device-side path choice (DENSE: always every row; AUTO: every row when the
+  // union exceeds the plan's crossover density for this batch size).
+  if (batched(&D) && (B > 1 || path == FFN_PATH_DENSE)) {
+    int choose = 0, dense_above = 0;
+    if (path == FFN_PATH_DENSE) {
+      choose = 1;
+      dense_above = -1;
+    } else if (path == FFN_PATH_AUTO && B >= p->dense_min_batch) {
+      float rho = 1.0f;
+      ffn_plan_crossover(p, std::min(B, BATCH_TILE), &rho);
+      choose = rho < 1.0f;
+      dense_above = (int)(rho * D.ffn);
+    }
     for (int b0 = 0; b0 < B; b0 += BATCH_TILE) {
       BatchArgs a = batch_bufs(p->ws, p);
       a.B = std::min(BATCH_TILE, B - b0);
@@ -363,7 +379,8 @@ ffn_status ffn_sparse_forward(ffn_plan* p, const void* x, int32_t B, float* y,
       a.scores = scores ? scores + (size_t)b0 * D.ffn : nullptr;
       a.idx_out = idx ? idx + (size_t)b0 * D.ffn : nullptr;
       a.cnt_out = cnt ? cnt + b0 : nullptr;
-      hipError_t e = launch_batch(a, mask == nullptr, st);
+      a.dense_above = dense_above;
+      hipError_t e = launch_batch(a, mask == nullptr, choose, st);
       if (e != hipSuccess) return hip_fail(e, "batched launch");
     }
     g_err[0] = 0;
@@ -383,8 +400,38 @@ ffn_status ffn_sparse_forward(ffn_plan* p, const void* x, int32_t B, float* y,
 
 ffn_status ffn_dense_forward(ffn_plan* p, const void* x, int32_t B, float* y,
                              const uint8_t* mask, void* stream) {
-  (void)p; (void)x; (void)B; (void)y; (void)mask; (void)stream;
-  return fail(FFN_ERR_UNSUPPORTED, "dense path not built yet");
+  if (!p) return fail(FFN_ERR_INVALID_ARGUMENT, "plan is NULL");
+  if (!x || !y) return fail(FFN_ERR_INVALID_ARGUMENT, "x / y is NULL");
+  const ffn_layer_desc& D = p->desc;
+  if (B < 1 || B > D.max_batch)
+    return fail(FFN_ERR_INVALID_ARGUMENT, "B = %d outside [1, %d]", B, D.max_batch);
+  if (!aligned16(x) || !aligned16(y) || !aligned16(mask))
+    return fail(FFN_ERR_INVALID_ARGUMENT, "x / y / mask not 16-byte aligned");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const size_t xbytes = (size_t)D.d * (D.x_dtype == FFN_F32 ? 4 : 2);
+  if (batched(&D)) {
+    for (int b0 = 0; b0 < B; b0 += BATCH_TILE) {
+      BatchArgs a = batch_bufs(p->ws, p);
+      a.B = std::min(BATCH_TILE, B - b0);
+      a.x = static_cast<const char*>(x) + b0 * xbytes;
+      a.mask = mask ? mask + (size_t)b0 * D.ffn : nullptr;
+      a.y = y + (size_t)b0 * D.d;
+      a.dense_above = -1;                  // every neuron's rows
+      hipError_t e = launch_batch(a, 0, 1, st);
+      if (e != hipSuccess) return hip_fail(e, "dense launch");
+    }
+  } else {
+    // fp32 / int4: the per-token kernels over every neuron (or the caller's sets)
+    const TokenBufs wb = token_bufs(p->ws, p);
+    for (int b = 0; b < B; ++b) {
+      ffn_status s = enqueue_token(p, wb, static_cast<const char*>(x) + b * xbytes,
+                                   mask ? mask + (size_t)b * D.ffn : nullptr, y + (size_t)b * D.d,
+                                   nullptr, nullptr, nullptr, nullptr, 0, st, true);
+      if (s != FFN_OK) return s;
+    }
+  }
+  g_err[0] = 0;
+  return FFN_OK;
 }
 
 ffn_status ffn_plan_crossover(const ffn_plan* p, int32_t B, float* density) {

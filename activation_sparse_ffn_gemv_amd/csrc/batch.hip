@@ -203,6 +203,21 @@ __global__ __launch_bounds__(256) void k_bmask(BatchArgs a) {
   a.ubits[w] = uw;
 }
 
+// Path choice on the device (nearauto.com / citnews.com.cn: prefill, where most neurons fire,
+// runs dense; decode runs sparse): when the union holds more than dense_above neurons, the pass
+// reads every neuron's rows; each token's h is still zeroed outside its own set, so the result
+// is the same either way.
+__global__ __launch_bounds__(1024) void k_bpath(BatchArgs a) {
+  __shared__ int s_total;
+  const int W = a.ffn / 32;
+  const int w = threadIdx.x;                            // W <= 1024
+  if (w == 0) s_total = 0;
+  __syncthreads();
+  if (w < W) atomicAdd(&s_total, __popc(a.ubits[w]));   // LDS atomic
+  __syncthreads();
+  if (s_total > a.dense_above && w < W) a.ubits[w] = 0xffffffffu;
+}
+
 // Rows of 32 union neurons (ranks [32 b, 32 b + 32)): u, g on the MFMA units, then h.
 __global__ __launch_bounds__(BT) void k_bug(BatchArgs a) {
   __shared__ int s_wsum[BT / WAVE];
@@ -435,7 +450,8 @@ BatchShape batch_shape(int d, int ffn, int r) {
   return s;
 }
 
-hipError_t launch_batch(const BatchArgs& a, int use_predictor, hipStream_t st) {
+hipError_t launch_batch(const BatchArgs& a, int use_predictor, int choose_path,
+                        hipStream_t st) {
   const int W = a.ffn / 32;
   if (use_predictor) {
     hipLaunchKernelGGL(k_bz, dim3((a.r + 31) / 32, a.ks), dim3(BT), 0, st, a);
@@ -444,6 +460,7 @@ hipError_t launch_batch(const BatchArgs& a, int use_predictor, hipStream_t st) {
   } else {
     hipLaunchKernelGGL(k_bmask, dim3((W + 255) / 256), dim3(256), 0, st, a);
   }
+  if (choose_path) hipLaunchKernelGGL(k_bpath, dim3(1), dim3(1024), 0, st, a);
   hipLaunchKernelGGL(k_bug, dim3(W), dim3(BT), 0, st, a);
   hipLaunchKernelGGL(k_bdown, dim3((a.d + DN_COLS - 1) / DN_COLS, a.S), dim3(BT), 0, st, a);
   hipLaunchKernelGGL(k_bred, dim3((a.d + 1023) / 1024, a.B), dim3(256), 0, st, a);

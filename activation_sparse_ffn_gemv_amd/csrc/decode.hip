@@ -201,13 +201,14 @@ __global__ __launch_bounds__(PS_THREADS) void k_pred_s(PredArgs a) {
   FFN_TS(1, 5);
 }
 
-// Caller-supplied mask -> bitmap: one wave builds two 32-bit words.
+// Caller-supplied mask -> bitmap: one wave builds two 32-bit words.  mask == nullptr sets every
+// bit (the dense FFN over all neurons).
 __global__ __launch_bounds__(256) void k_mask_bits(const unsigned char* __restrict__ mask,
                                                    uint32_t* __restrict__ bitmap, int words) {
   const int w = blockIdx.x * 4 + threadIdx.x / WAVE;
   const int lane = threadIdx.x & (WAVE - 1);
   const int word = w * 2 + (lane >> 5);
-  const bool on = word < words && mask[(size_t)word * 32 + (lane & 31)] != 0;
+  const bool on = word < words && (!mask || mask[(size_t)word * 32 + (lane & 31)] != 0);
   const unsigned long long bal = __ballot(on);
   if (lane == 0 && word < words) bitmap[word] = (uint32_t)bal;
   if (lane == 32 && word < words) bitmap[word] = (uint32_t)(bal >> 32);

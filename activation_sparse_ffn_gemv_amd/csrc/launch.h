@@ -123,6 +123,7 @@ struct BatchArgs {
   int B, d, ffn, r, act, has_gate;
   int ks, spw, S;
   float thr;
+  int dense_above;            // path choice: union larger than this -> every neuron's row
 };
 
 struct BatchShape {
@@ -130,6 +131,8 @@ struct BatchShape {
   size_t zpart_bytes, zhl_bytes, bits_bytes, ubits_bytes, uidx_bytes, H_bytes, ypart_bytes;
 };
 BatchShape batch_shape(int d, int ffn, int r);
-hipError_t launch_batch(const BatchArgs& a, int use_predictor, hipStream_t st);
+// use_predictor: predictor kernels (else caller masks); choose_path: run k_bpath, which widens
+// the union to every neuron when it holds more than dense_above neurons (-1: always).
+hipError_t launch_batch(const BatchArgs& a, int use_predictor, int choose_path, hipStream_t st);
 
 }  // namespace ffn

@@ -104,6 +104,13 @@ def test_plan_validation_before_any_gpu_call():
         assert e.value.status == ffn.FFN_ERR_INVALID_ARGUMENT
         with pytest.raises(ffn.FFNError):           # NULL y
             ffn.ffn_sparse_forward(plan, 0x1000, 1, 0)
+        with pytest.raises(ffn.FFNError) as e:      # dense: B out of range, misaligned mask
+            ffn.ffn_dense_forward(plan, 0x1000, 2, 0x2000)
+        assert e.value.status == ffn.FFN_ERR_INVALID_ARGUMENT
+        with pytest.raises(ffn.FFNError) as e:
+            ffn.ffn_dense_forward(plan, 0x1000, 1, 0x2000, mask=0x3001)
+        assert e.value.status == ffn.FFN_ERR_INVALID_ARGUMENT
+        assert ffn.ffn_plan_crossover(plan, 1) <= 1.0
     finally:
         ffn.ffn_plan_destroy(plan)
 

@@ -120,3 +120,77 @@ def test_falcon_40b_shape_batched(ffn, B):
     cfg = synth.CONFIGS["falcon_40b_relu_f16"]
     _, lists, nu = _check(ffn, cfg, B, tokens=[0, B // 2, B - 1])
     assert nu / cfg.ffn > 0.3
+
+
+# ---- dense fallback and path choice --------------------------------------------------------
+@pytest.mark.parametrize("B", [1, 3, 40])
+@pytest.mark.parametrize("wd,act", [("f16", "relu"), ("f16", "reglu"), ("f16", "drelu"),
+                                    ("f32", "reglu"), ("i4g32", "drelu")])
+def test_dense_forward_is_the_dense_ffn(ffn, wd, act, B):
+    xd = "f32" if wd == "f32" else "f16"
+    cfg = synth.small_config(d=256, ffn=1056, rank=32, act=act, w_dtype=wd, x_dtype=xd,
+                             p_dtype=xd, density=0.1, bias_up=True, bias_gate=True,
+                             bias_down=True)
+    host = synth.make_layer(cfg)
+    L, OL = to_device(host), oracle_layer(host)
+    x = synth.make_tokens(cfg, B).cuda()
+    m = ffn.SparseFFN(L, max_batch=B)
+    y = m.dense(x)
+    rng = np.random.default_rng(5)
+    masks = (rng.random((B, cfg.ffn)) < 0.3).astype(np.uint8)
+    ym = m.dense(x, mask=torch.from_numpy(masks).cuda())
+    torch.cuda.synchronize()
+    xh, yh, ymh = x.cpu().numpy(), y.cpu().numpy(), ym.cpu().numpy()
+    for t in range(B):
+        y_ref, _ = oracle.ffn(OL, xh[t], None)
+        assert normwise(yh[t], y_ref) <= TOL[wd], (t, normwise(yh[t], y_ref))
+        y_ref, _ = oracle.ffn(OL, xh[t], masks[t])
+        assert normwise(ymh[t], y_ref) <= TOL[wd]
+    m.close()
+
+
+@pytest.mark.parametrize("B", [1, 6, 32])
+def test_dense_and_auto_paths_equal_sparse(ffn, B):
+    """path=DENSE reads every neuron's rows but keeps each token's predicted set (h = 0 outside
+    it), so DENSE, AUTO and SPARSE agree within rounding and report the same index lists."""
+    cfg = synth.small_config(d=512, ffn=2048, rank=64, act="drelu", w_dtype="f16",
+                             x_dtype="f16", p_dtype="f16", density=0.1, bias_gate=True,
+                             bias_up=True)
+    host = synth.make_layer(cfg)
+    L, OL = to_device(host), oracle_layer(host)
+    x = synth.make_tokens(cfg, B).cuda()
+    m = ffn.SparseFFN(L, max_batch=B)
+    out = {}
+    for path in (ffn.FFN_PATH_SPARSE, ffn.FFN_PATH_DENSE, ffn.FFN_PATH_AUTO):
+        idx = torch.full((B, cfg.ffn), -1, dtype=torch.int32, device="cuda")
+        cnt = torch.zeros(B, dtype=torch.int32, device="cuda")
+        y = m.forward(x, idx=idx, cnt=cnt, path=path)
+        torch.cuda.synchronize()
+        out[path] = (y.cpu().numpy(), idx.cpu().numpy(), cnt.cpu().numpy())
+    xh = x.cpu().numpy()
+    ys, idxs, cnts = out[ffn.FFN_PATH_SPARSE]
+    for path in (ffn.FFN_PATH_DENSE, ffn.FFN_PATH_AUTO):
+        yp, idxp, cntp = out[path]
+        for t in range(B):
+            lt = idxp[t, :cntp[t]]
+            pred = oracle.predictor(OL["p1"], OL["p2"], OL["c1"], OL["c2"], xh[t], OL["tau"])
+            check_index_list(lt, pred, OL["tau"])
+            y_ref, _ = oracle.ffn(OL, xh[t], mask_from_idx(lt, cfg.ffn))
+            assert normwise(yp[t], y_ref) <= TOL["f16"]
+    m.close()
+
+
+def test_falcon_40b_shape_prefill_dense(ffn):
+    """Prefill-style dense pass of the 8192 x 32768 layer over 64 tokens (two passes)."""
+    cfg = synth.CONFIGS["falcon_40b_relu_f16"]
+    host = synth.make_layer(cfg, device="cuda")
+    L, OL = to_device(host), oracle_layer(host)
+    x = synth.make_tokens(cfg, 64).cuda()
+    m = ffn.SparseFFN(L, max_batch=64)
+    y = m.dense(x)
+    torch.cuda.synchronize()
+    xh, yh = x.cpu().numpy(), y.cpu().numpy()
+    for t in (0, 63):
+        y_ref, _ = oracle.ffn(OL, xh[t], None)
+        assert normwise(yh[t], y_ref) <= TOL["f16"]
+    m.close()
