@@ -24,7 +24,11 @@ FFN_ACT_RELU, FFN_ACT_REGLU, FFN_ACT_DRELU = 0, 1, 2
 FFN_F32, FFN_F16, FFN_I4G32 = 0, 1, 2
 FFN_PATH_AUTO, FFN_PATH_SPARSE, FFN_PATH_DENSE = 0, 1, 2
 FFN_STAGE_PRED_Z, FFN_STAGE_PRED_S, FFN_STAGE_GATHER, FFN_STAGE_REDUCE = 0, 1, 2, 3
-STAGES = ("pred_z", "pred_s", "gather", "reduce")
+FFN_STAGE_BATCH_UPGATE, FFN_STAGE_BATCH_DOWN = 4, 5
+FFN_STAGE_DENSE_UP, FFN_STAGE_DENSE_DOWN, FFN_STAGE_DENSE_REDUCE = 6, 7, 8
+STAGES = ("pred_z", "pred_s", "gather", "reduce")          # the batch-1 decode kernels
+BATCH_STAGES = ("batch_upgate", "batch_down")
+DENSE_STAGES = ("dense_up", "dense_down", "dense_reduce")
 
 ACT = {"relu": FFN_ACT_RELU, "reglu": FFN_ACT_REGLU, "drelu": FFN_ACT_DRELU}
 DTYPE = {"f32": FFN_F32, "f16": FFN_F16, "i4g32": FFN_I4G32}
@@ -32,7 +36,7 @@ DTYPE = {"f32": FFN_F32, "f16": FFN_F16, "i4g32": FFN_I4G32}
 # Every symbol the header declares (checked by the tests).
 EXPORTS = [
     "ffn_workspace_size", "ffn_sparse_plan", "ffn_sparse_forward", "ffn_dense_forward",
-    "ffn_plan_crossover", "ffn_plan_destroy", "ffn_plan_set_timing_events", "ffn_last_error",
+    "ffn_plan_crossover", "ffn_plan_set_crossover", "ffn_plan_destroy", "ffn_plan_set_timing_events", "ffn_last_error",
     "ffn_moe_workspace_size",
     "ffn_moe_plan", "ffn_moe_forward", "ffn_moe_destroy",
 ]
@@ -84,6 +88,8 @@ def lib():
         L.ffn_dense_forward.argtypes = [P, P, I, P, P, P]
         L.ffn_plan_crossover.restype = st
         L.ffn_plan_crossover.argtypes = [P, I, ctypes.POINTER(ctypes.c_float)]
+        L.ffn_plan_set_crossover.restype = st
+        L.ffn_plan_set_crossover.argtypes = [P, I, ctypes.c_float]
         L.ffn_plan_destroy.restype = st
         L.ffn_plan_destroy.argtypes = [P]
         L.ffn_plan_set_timing_events.restype = st
@@ -138,6 +144,10 @@ def ffn_plan_crossover(plan: int, B: int) -> float:
     v = ctypes.c_float(0)
     _check(lib().ffn_plan_crossover(plan, B, ctypes.byref(v)))
     return v.value
+
+
+def ffn_plan_set_crossover(plan: int, B: int, density: float):
+    _check(lib().ffn_plan_set_crossover(plan, B, density))
 
 
 def ffn_plan_destroy(plan: int):

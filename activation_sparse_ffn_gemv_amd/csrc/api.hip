@@ -48,8 +48,17 @@ int cpl_for(int nch) {
 
 struct Layout {
   int cpl_w, cpl_p;
-  size_t off_z, off_bits, off_cnt, off_part, off_union, off_batch, total;
+  size_t off_z, off_bits, off_cnt, off_part, off_union, off_batch, off_dense, dense_rows, total;
 };
+
+// Dense-GEMM region (fp16 layers that may see DENSE_MIN_M tokens or more): dbits [max_batch]
+// [ffn/32] | flag | H [max_batch][ffn] fp16 | partials [rows][d] fp32.
+size_t dense_rows_for(const ffn_layer_desc* d) {
+  size_t rows = 0;
+  for (int M = DENSE_MIN_M; M <= d->max_batch; ++M)
+    rows = std::max(rows, (size_t)dense_ks(M, d->d, d->ffn) * M);
+  return rows;
+}
 
 // The batched kernels (MFMA) cover fp16 layers; other storage types run B > 1 token by token.
 bool batched(const ffn_layer_desc* d) { return d->w_dtype == FFN_F16; }
@@ -113,8 +122,61 @@ Layout layout_for(const ffn_layer_desc* d) {
     off = round_up(off + s.H_bytes, 256);
     off = round_up(off + s.ypart_bytes, 256);
   }
+  L.off_dense = 0;
+  L.dense_rows = 0;
+  if (batched(d) && d->max_batch >= DENSE_MIN_M) {
+    L.off_dense = off;
+    L.dense_rows = dense_rows_for(d);
+    off = round_up(off + (size_t)d->max_batch * (d->ffn / 32) * 4, 256);
+    off = round_up(off + 4, 256);
+    off = round_up(off + (size_t)d->max_batch * d->ffn * 2, 256);
+    off = round_up(off + L.dense_rows * d->d * 4, 256);
+  }
   L.total = off;
   return L;
+}
+
+struct DenseBufs {
+  uint32_t* bits;
+  int* flag;
+  _Float16* H;
+  float* ypart;
+};
+
+DenseBufs dense_bufs(char* ws, const ffn_plan* p) {
+  const ffn_layer_desc& D = p->desc;
+  size_t off = p->off_dense;
+  DenseBufs b{};
+  b.bits = reinterpret_cast<uint32_t*>(ws + off);
+  off = round_up(off + (size_t)D.max_batch * (D.ffn / 32) * 4, 256);
+  b.flag = reinterpret_cast<int*>(ws + off);
+  off = round_up(off + 4, 256);
+  b.H = reinterpret_cast<_Float16*>(ws + off);
+  off = round_up(off + (size_t)D.max_batch * D.ffn * 2, 256);
+  b.ypart = reinterpret_cast<float*>(ws + off);
+  return b;
+}
+
+DenseArgs dense_args(const ffn_plan* p, const DenseBufs& db, const void* x, int M, float* y) {
+  const ffn_layer_desc& D = p->desc;
+  DenseArgs a{};
+  a.x = x;
+  a.w_up = p->w.w_up;
+  a.w_gate = p->w.w_gate;
+  a.w_dn = p->w.w_down_t;
+  a.b_up = p->w.b_up;
+  a.b_gate = p->w.b_gate;
+  a.b_down = p->w.b_down;
+  a.H = db.H;
+  a.ypart = db.ypart;
+  a.y = y;
+  a.M = M;
+  a.d = D.d;
+  a.ffn = D.ffn;
+  a.act = D.act;
+  a.has_gate = D.act != FFN_ACT_RELU;
+  a.ks = dense_ks(M, D.d, D.ffn);
+  return a;
 }
 
 // The batched region's buffers, in the order layout_for reserves them.
@@ -325,11 +387,13 @@ ffn_status ffn_sparse_plan(const ffn_layer_desc* desc, const ffn_layer_weights* 
   p->off_part = L.off_part;
   p->off_union = L.off_union;
   p->off_batch = L.off_batch;
+  p->off_dense = L.off_dense;
+  p->dense_ypart_rows = L.dense_rows;
   const double tau = desc->threshold;
   p->thr = tau >= 1.0 ? INFINITY : (float)log(tau / (1.0 - tau));
   // built-in table: the batched kernels read the union of the tokens' rows, which never costs
   // more than every row, so the union is kept (crossover 1) until calibration says otherwise
-  for (int k = 0; k < 8; ++k) p->crossover_density[k] = 1.0f;
+  for (int k = 0; k < 13; ++k) p->crossover_density[k] = 1.0f;
   p->dense_min_batch = 2;
   (void)stream;
   (void)calibrate;
@@ -337,6 +401,78 @@ ffn_status ffn_sparse_plan(const ffn_layer_desc* desc, const ffn_layer_weights* 
   g_err[0] = 0;
   return FFN_OK;
 }
+
+}  // extern "C"
+
+namespace {
+
+// fp16 call with a dense region and B >= DENSE_MIN_M: every token's set goes to the region's
+// bitmaps first (predictor or caller masks, 32 tokens per pass), then the rows run as dense
+// GEMMs (DENSE), as sparse passes (SPARSE), or as whichever the device picks from the union
+// density of the whole call (AUTO: both are enqueued, each gated on the device flag).
+ffn_status run_large(ffn_plan* p, const void* x, int32_t B, float* y, const uint8_t* mask,
+                     int32_t* idx, int32_t* cnt, float* scores, int32_t path, hipStream_t st,
+                     bool dense_only) {
+  const ffn_layer_desc& D = p->desc;
+  const int W = D.ffn / 32;
+  const size_t xbytes = (size_t)D.d * 2;
+  const DenseBufs db = dense_bufs(p->ws, p);
+  const bool sets = !dense_only || mask;         // dense FFN without a mask needs no sets
+  hipError_t e;
+  if (sets) {
+    for (int b0 = 0; b0 < B; b0 += BATCH_TILE) {
+      BatchArgs a = batch_bufs(p->ws, p);
+      a.B = std::min(BATCH_TILE, B - b0);
+      a.x = static_cast<const char*>(x) + b0 * xbytes;
+      a.mask = mask ? mask + (size_t)b0 * D.ffn : nullptr;
+      a.bits = db.bits + (size_t)b0 * W;
+      a.scores = scores ? scores + (size_t)b0 * D.ffn : nullptr;
+      if ((e = launch_batch_sets(a, mask == nullptr, st)) != hipSuccess)
+        return hip_fail(e, "active-set launch");
+    }
+  }
+  const int* flag = nullptr;
+  if (path == FFN_PATH_AUTO) {
+    float rho = 1.0f;
+    ffn_plan_crossover(p, B, &rho);
+    const int dense_above = rho >= 1.0f ? D.ffn : (int)(rho * D.ffn);
+    if ((e = launch_dense_choice(db.bits, B, D.ffn, dense_above, db.flag, st)) != hipSuccess)
+      return hip_fail(e, "path choice launch");
+    flag = db.flag;
+  }
+  if (path != FFN_PATH_SPARSE) {
+    DenseArgs da = dense_args(p, db, x, B, y);
+    da.bits = sets ? db.bits : nullptr;
+    da.idx_out = idx;
+    da.cnt_out = cnt;
+    da.run_if = flag;
+    da.run_want = 1;
+    if ((e = launch_dense(da, st, p->ev + FFN_STAGE_DENSE_UP)) != hipSuccess)
+      return hip_fail(e, "dense launch");
+  }
+  if (path != FFN_PATH_DENSE) {
+    for (int b0 = 0; b0 < B; b0 += BATCH_TILE) {
+      BatchArgs a = batch_bufs(p->ws, p);
+      a.B = std::min(BATCH_TILE, B - b0);
+      a.x = static_cast<const char*>(x) + b0 * xbytes;
+      a.bits = db.bits + (size_t)b0 * W;
+      a.y = y + (size_t)b0 * D.d;
+      a.idx_out = idx ? idx + (size_t)b0 * D.ffn : nullptr;
+      a.cnt_out = cnt ? cnt + b0 : nullptr;
+      a.run_if = flag;
+      a.run_want = 0;
+      if ((e = launch_batch_union(a, st)) != hipSuccess ||
+          (e = launch_batch_rows(a, 0, st, p->ev + FFN_STAGE_BATCH_UPGATE)) != hipSuccess)
+        return hip_fail(e, "batched launch");
+    }
+  }
+  g_err[0] = 0;
+  return FFN_OK;
+}
+
+}  // namespace
+
+extern "C" {
 
 ffn_status ffn_sparse_forward(ffn_plan* p, const void* x, int32_t B, float* y,
                               const uint8_t* mask, int32_t* idx, int32_t* cnt, float* scores,
@@ -350,15 +486,19 @@ ffn_status ffn_sparse_forward(ffn_plan* p, const void* x, int32_t B, float* y,
     return fail(FFN_ERR_INVALID_ARGUMENT, "no predictor (rank 0) and no mask");
   if (path < FFN_PATH_AUTO || path > FFN_PATH_DENSE)
     return fail(FFN_ERR_INVALID_ARGUMENT, "path %d is not an ffn_path", path);
-  if (!aligned16(x) || !aligned16(y))
-    return fail(FFN_ERR_INVALID_ARGUMENT, "x / y not 16-byte aligned");
+  if (!aligned16(x) || !aligned16(y) || !aligned16(mask))
+    return fail(FFN_ERR_INVALID_ARGUMENT, "x / y / mask not 16-byte aligned");
   hipStream_t st = static_cast<hipStream_t>(stream);
   const size_t xbytes = (size_t)D.d * (D.x_dtype == FFN_F32 ? 4 : 2);
-  // Path: fp32 / int4 layers always run the per-token kernels (they have no MFMA path; the
-  // dense request gives the same result over the same sets).  fp16: SPARSE runs the batch-1
-  // kernels for one token and the batched kernels for more; DENSE and AUTO run the batched
-  // kernels with the device-side path choice (DENSE: always every row; AUTO: every row when the
-  // union exceeds the plan's crossover density for this batch size).
+  // Paths.  fp32 / int4 layers always run the per-token kernels (they have no MFMA path; a
+  // dense request gives the same result over the same sets).  fp16:
+  //  - B >= DENSE_MIN_M (and a dense region): sets first, then dense GEMMs / sparse passes /
+  //    the device's choice between them (run_large);
+  //  - otherwise SPARSE runs the batch-1 kernels for one token and the batched kernels for
+  //    more; DENSE and AUTO run the batched kernels, widening the pass's union to every neuron
+  //    (DENSE: always; AUTO: when it exceeds the crossover density).
+  if (batched(&D) && p->off_dense && B >= DENSE_MIN_M && path != FFN_PATH_SPARSE)
+    return run_large(p, x, B, y, mask, idx, cnt, scores, path, st, false);
   if (batched(&D) && (B > 1 || path == FFN_PATH_DENSE)) {
     int choose = 0, dense_above = 0;
     if (path == FFN_PATH_DENSE) {
@@ -380,7 +520,7 @@ ffn_status ffn_sparse_forward(ffn_plan* p, const void* x, int32_t B, float* y,
       a.idx_out = idx ? idx + (size_t)b0 * D.ffn : nullptr;
       a.cnt_out = cnt ? cnt + b0 : nullptr;
       a.dense_above = dense_above;
-      hipError_t e = launch_batch(a, mask == nullptr, choose, st);
+      hipError_t e = launch_batch(a, mask == nullptr, choose, st, p->ev + FFN_STAGE_BATCH_UPGATE);
       if (e != hipSuccess) return hip_fail(e, "batched launch");
     }
     g_err[0] = 0;
@@ -409,6 +549,8 @@ ffn_status ffn_dense_forward(ffn_plan* p, const void* x, int32_t B, float* y,
     return fail(FFN_ERR_INVALID_ARGUMENT, "x / y / mask not 16-byte aligned");
   hipStream_t st = static_cast<hipStream_t>(stream);
   const size_t xbytes = (size_t)D.d * (D.x_dtype == FFN_F32 ? 4 : 2);
+  if (batched(&D) && p->off_dense && B >= DENSE_MIN_M)
+    return run_large(p, x, B, y, mask, nullptr, nullptr, nullptr, FFN_PATH_DENSE, st, true);
   if (batched(&D)) {
     for (int b0 = 0; b0 < B; b0 += BATCH_TILE) {
       BatchArgs a = batch_bufs(p->ws, p);
@@ -417,7 +559,7 @@ ffn_status ffn_dense_forward(ffn_plan* p, const void* x, int32_t B, float* y,
       a.mask = mask ? mask + (size_t)b0 * D.ffn : nullptr;
       a.y = y + (size_t)b0 * D.d;
       a.dense_above = -1;                  // every neuron's rows
-      hipError_t e = launch_batch(a, 0, 1, st);
+      hipError_t e = launch_batch(a, 0, 1, st, p->ev + FFN_STAGE_BATCH_UPGATE);
       if (e != hipSuccess) return hip_fail(e, "dense launch");
     }
   } else {
@@ -438,14 +580,25 @@ ffn_status ffn_plan_crossover(const ffn_plan* p, int32_t B, float* density) {
   if (!p || !density) return fail(FFN_ERR_INVALID_ARGUMENT, "plan / density is NULL");
   if (B < 1) return fail(FFN_ERR_INVALID_ARGUMENT, "B < 1");
   int k = 0;
-  while (k < 7 && (1 << (k + 1)) <= B) ++k;
+  while (k < 12 && (1 << (k + 1)) <= B) ++k;
   *density = p->crossover_density[k];
+  return FFN_OK;
+}
+
+ffn_status ffn_plan_set_crossover(ffn_plan* p, int32_t B, float density) {
+  if (!p) return fail(FFN_ERR_INVALID_ARGUMENT, "plan is NULL");
+  if (B < 1) return fail(FFN_ERR_INVALID_ARGUMENT, "B < 1");
+  if (!(density >= 0.0f && density <= 1.0f))
+    return fail(FFN_ERR_INVALID_ARGUMENT, "density must lie in [0, 1]");
+  int k = 0;
+  while (k < 12 && (1 << (k + 1)) <= B) ++k;
+  p->crossover_density[k] = density;
   return FFN_OK;
 }
 
 ffn_status ffn_plan_set_timing_events(ffn_plan* p, int32_t stage, void* start, void* stop) {
   if (!p) return fail(FFN_ERR_INVALID_ARGUMENT, "plan is NULL");
-  if (stage < FFN_STAGE_PRED_Z || stage > FFN_STAGE_REDUCE)
+  if (stage < FFN_STAGE_PRED_Z || stage > FFN_STAGE_DENSE_REDUCE)
     return fail(FFN_ERR_INVALID_ARGUMENT, "stage %d is not an ffn_stage", stage);
   if ((start == nullptr) != (stop == nullptr))
     return fail(FFN_ERR_INVALID_ARGUMENT, "start and stop must both be set or both be NULL");

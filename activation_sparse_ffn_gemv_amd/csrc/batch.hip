@@ -18,6 +18,8 @@
 // MFMA lane layout (v_mfma_f32_32x32x16_f16 / 32x32x8_f16): lane l supplies row (l % 32) of A
 // and column (l % 32) of B, each with the K elements 8*(l/32) .. +7 (x16) or 4*(l/32) .. +3
 // (x8); accumulator element i of lane l is D[8*(i/4) + 4*(l/32) + i%4][l % 32].
+#include <hip/hip_ext.h>
+
 #include <algorithm>
 
 #include "common.h"
@@ -167,8 +169,9 @@ __global__ __launch_bounds__(BT) void k_bs(BatchArgs a) {
       if (a.scores && m < a.B) a.scores[(size_t)m * a.ffn + n0 + row] = sc;
       const unsigned long long bal = __ballot(on);
       const int m0 = 8 * (i >> 2) + (i & 3);          // lanes 0..31: token m0; 32..63: m0 + 4
-      if (lane == 0) a.bits[(size_t)m0 * W + blockIdx.x] = (uint32_t)bal;
-      if (lane == 32) a.bits[(size_t)(m0 + 4) * W + blockIdx.x] = (uint32_t)(bal >> 32);
+      // rows of tokens past B are never read (and may lie past the caller's bitmap rows)
+      if (lane == 0 && m0 < a.B) a.bits[(size_t)m0 * W + blockIdx.x] = (uint32_t)bal;
+      if (lane == 32 && m0 + 4 < a.B) a.bits[(size_t)(m0 + 4) * W + blockIdx.x] = (uint32_t)(bal >> 32);
       uw |= (uint32_t)bal | (uint32_t)(bal >> 32);
     }
     if (lane == 0) a.ubits[blockIdx.x] = uw;
@@ -181,9 +184,9 @@ __global__ __launch_bounds__(256) void k_bmask(BatchArgs a) {
   const int W = a.ffn / 32;
   if (w >= W) return;
   uint32_t uw = 0u;
-  for (int m = 0; m < MB; ++m) {
+  for (int m = 0; m < a.B; ++m) {
     uint32_t bw = 0u;
-    if (m < a.B) {
+    {
       if (a.mask) {
         const u32x4* mp = reinterpret_cast<const u32x4*>(a.mask + (size_t)m * a.ffn + w * 32);
         const u32x4 q0 = mp[0], q1 = mp[1];
@@ -209,6 +212,7 @@ __global__ __launch_bounds__(256) void k_bmask(BatchArgs a) {
 // is the same either way.
 __global__ __launch_bounds__(1024) void k_bpath(BatchArgs a) {
   __shared__ int s_total;
+  if (a.run_if && *a.run_if != a.run_want) return;
   const int W = a.ffn / 32;
   const int w = threadIdx.x;                            // W <= 1024
   if (w == 0) s_total = 0;
@@ -218,11 +222,38 @@ __global__ __launch_bounds__(1024) void k_bpath(BatchArgs a) {
   if (s_total > a.dense_above && w < W) a.ubits[w] = 0xffffffffu;
 }
 
+// Union words of the pass's tokens from their bitmap words (bits written by an earlier step).
+__global__ __launch_bounds__(256) void k_bunion(BatchArgs a) {
+  if (a.run_if && *a.run_if != a.run_want) return;
+  const int w = blockIdx.x * 256 + threadIdx.x, W = a.ffn / 32;
+  if (w >= W) return;
+  uint32_t uw = 0u;
+  for (int m = 0; m < a.B; ++m) uw |= a.bits[(size_t)m * W + w];
+  a.ubits[w] = uw;
+}
+
+// Dense-or-sparse for a whole call: union of B tokens' sets against dense_above.
+__global__ __launch_bounds__(1024) void k_dchoice(const uint32_t* __restrict__ bits, int B,
+                                                  int W, int dense_above, int* __restrict__ flag) {
+  __shared__ int s_total;
+  const int w = threadIdx.x;                            // W <= 1024
+  if (w == 0) s_total = 0;
+  __syncthreads();
+  if (w < W) {
+    uint32_t uw = 0u;
+    for (int m = 0; m < B; ++m) uw |= bits[(size_t)m * W + w];
+    atomicAdd(&s_total, __popc(uw));                    // LDS atomic
+  }
+  __syncthreads();
+  if (w == 0) *flag = s_total > dense_above ? 1 : 0;
+}
+
 // Rows of 32 union neurons (ranks [32 b, 32 b + 32)): u, g on the MFMA units, then h.
 __global__ __launch_bounds__(BT) void k_bug(BatchArgs a) {
   __shared__ int s_wsum[BT / WAVE];
   __shared__ int s_nid[32];
   __shared__ float red[3 * 16 * WAVE];
+  if (a.run_if && *a.run_if != a.run_want) return;
   const int tid = threadIdx.x, lane = tid & (WAVE - 1), wave = tid / WAVE;
   const int W = a.ffn / 32;
   constexpr int WPT = 4;                                // bitmap words per thread (ffn <= 32768)
@@ -335,6 +366,7 @@ __global__ __launch_bounds__(BT) void k_bdown(BatchArgs a) {
   __shared__ int s_nid[DN_CH];
   __shared__ float s_y[MB * DN_COLS];
   const int tid = threadIdx.x, lane = tid & (WAVE - 1), wave = tid / WAVE;
+  if (a.run_if && *a.run_if != a.run_want) return;
   const int total = *a.ucnt;
   int r0, r1;
   seg_range(total, blockIdx.y, a.S, r0, r1);
@@ -411,6 +443,7 @@ __global__ __launch_bounds__(BT) void k_bdown(BatchArgs a) {
 // y = b_down + sum of the non-empty segments' partials (in segment order); workgroup (0, m)
 // also writes token m's ascending index list and count.
 __global__ __launch_bounds__(256) void k_bred(BatchArgs a) {
+  if (a.run_if && *a.run_if != a.run_want) return;
   const int m = blockIdx.y;
   const int col = (blockIdx.x * 256 + threadIdx.x) * 4;
   const int total = *a.ucnt;
@@ -450,8 +483,7 @@ BatchShape batch_shape(int d, int ffn, int r) {
   return s;
 }
 
-hipError_t launch_batch(const BatchArgs& a, int use_predictor, int choose_path,
-                        hipStream_t st) {
+hipError_t launch_batch_sets(const BatchArgs& a, int use_predictor, hipStream_t st) {
   const int W = a.ffn / 32;
   if (use_predictor) {
     hipLaunchKernelGGL(k_bz, dim3((a.r + 31) / 32, a.ks), dim3(BT), 0, st, a);
@@ -460,10 +492,41 @@ hipError_t launch_batch(const BatchArgs& a, int use_predictor, int choose_path,
   } else {
     hipLaunchKernelGGL(k_bmask, dim3((W + 255) / 256), dim3(256), 0, st, a);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_batch_union(const BatchArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(k_bunion, dim3((a.ffn / 32 + 255) / 256), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_batch_rows(const BatchArgs& a, int choose_path, hipStream_t st,
+                             hipEvent_t (*ev)[2]) {
+  const int W = a.ffn / 32;
   if (choose_path) hipLaunchKernelGGL(k_bpath, dim3(1), dim3(1024), 0, st, a);
-  hipLaunchKernelGGL(k_bug, dim3(W), dim3(BT), 0, st, a);
-  hipLaunchKernelGGL(k_bdown, dim3((a.d + DN_COLS - 1) / DN_COLS, a.S), dim3(BT), 0, st, a);
+  if (ev && ev[0][0])
+    hipExtLaunchKernelGGL(k_bug, dim3(W), dim3(BT), 0, st, ev[0][0], ev[0][1], 0, a);
+  else
+    hipLaunchKernelGGL(k_bug, dim3(W), dim3(BT), 0, st, a);
+  const dim3 gd((a.d + DN_COLS - 1) / DN_COLS, a.S);
+  if (ev && ev[1][0])
+    hipExtLaunchKernelGGL(k_bdown, gd, dim3(BT), 0, st, ev[1][0], ev[1][1], 0, a);
+  else
+    hipLaunchKernelGGL(k_bdown, gd, dim3(BT), 0, st, a);
   hipLaunchKernelGGL(k_bred, dim3((a.d + 1023) / 1024, a.B), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_batch(const BatchArgs& a, int use_predictor, int choose_path, hipStream_t st,
+                        hipEvent_t (*ev)[2]) {
+  hipError_t e = launch_batch_sets(a, use_predictor, st);
+  if (e != hipSuccess) return e;
+  return launch_batch_rows(a, choose_path, st, ev);
+}
+
+hipError_t launch_dense_choice(const uint32_t* bits, int B, int ffn, int dense_above, int* flag,
+                               hipStream_t st) {
+  hipLaunchKernelGGL(k_dchoice, dim3(1), dim3(1024), 0, st, bits, B, ffn / 32, dense_above, flag);
   return hipGetLastError();
 }
 

@@ -212,7 +212,9 @@ struct ffn_plan {
   float thr;         // logit(threshold): active iff score > thr
   size_t off_z, off_bits, off_cnt, off_part, off_union;
   size_t off_batch;  // batched-path region (fp16 layers with max_batch > 1), else 0
-  float crossover_density[8];   // per batch bucket 1,2,4,...,128
+  size_t off_dense;  // dense-GEMM region (fp16 layers with max_batch >= 64), else 0
+  size_t dense_ypart_rows;      // rows of the dense partial buffer (max over M of ks * M)
+  float crossover_density[13];  // per batch bucket 1, 2, 4, ..., 4096
   int dense_min_batch;          // AUTO takes the dense path from this batch size on
-  hipEvent_t ev[4][2];          // instrumentation events attached to each stage's dispatch
+  hipEvent_t ev[9][2];          // instrumentation events attached to each stage's dispatch
 };

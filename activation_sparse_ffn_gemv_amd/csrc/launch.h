@@ -124,6 +124,8 @@ struct BatchArgs {
   int ks, spw, S;
   float thr;
   int dense_above;            // path choice: union larger than this -> every neuron's row
+  const int* run_if;          // device flag: the row kernels run only if *run_if == run_want
+  int run_want;               //   (nullptr: always)
 };
 
 struct BatchShape {
@@ -133,6 +135,40 @@ struct BatchShape {
 BatchShape batch_shape(int d, int ffn, int r);
 // use_predictor: predictor kernels (else caller masks); choose_path: run k_bpath, which widens
 // the union to every neuron when it holds more than dense_above neurons (-1: always).
-hipError_t launch_batch(const BatchArgs& a, int use_predictor, int choose_path, hipStream_t st);
+// ev: (start, stop) pairs for k_bug and k_bdown (entries may be null), or nullptr.
+hipError_t launch_batch(const BatchArgs& a, int use_predictor, int choose_path, hipStream_t st,
+                        hipEvent_t (*ev)[2] = nullptr);
+// The pieces: the pass's active sets (bits, scores, union) ...
+hipError_t launch_batch_sets(const BatchArgs& a, int use_predictor, hipStream_t st);
+// ... the union recomputed from bits (when bits were written by an earlier step) ...
+hipError_t launch_batch_union(const BatchArgs& a, hipStream_t st);
+// ... and the rows (optional k_bpath, k_bug, k_bdown, k_bred).
+hipError_t launch_batch_rows(const BatchArgs& a, int choose_path, hipStream_t st,
+                             hipEvent_t (*ev)[2] = nullptr);
+// Device-side choice for a call of B tokens whose sets are in bits[B][ffn/32]: flag = 1 when the
+// union of all their sets holds more than dense_above neurons.
+hipError_t launch_dense_choice(const uint32_t* bits, int B, int ffn, int dense_above, int* flag,
+                               hipStream_t st);
+
+// Dense path (fp16 layers, many tokens): two MFMA GEMMs and a fixed-order reduce.
+constexpr int DENSE_MIN_M = 64;   // token count from which the dense GEMMs replace the batched kernels
+
+struct DenseArgs {
+  const void* x;              // [M][d] fp16
+  const uint32_t* bits;       // [M][ffn/32] per-token sets, or nullptr (every neuron)
+  const void *w_up, *w_gate, *w_dn;
+  const float *b_up, *b_gate, *b_down;
+  _Float16* H;                // [M][ffn]
+  float* ypart;               // [ks][M][d]
+  float* y;                   // [M][d]
+  int* idx_out;               // [M][ffn] or nullptr (from bits)
+  int* cnt_out;               // [M] or nullptr
+  int M, d, ffn, act, has_gate, ks;
+  const int* run_if;          // device flag: run only if *run_if == run_want (nullptr: always)
+  int run_want;
+};
+int dense_ks(int M, int d, int ffn);
+// ev: three (start, stop) pairs for k_dup, k_ddown, k_dred (entries may be null), or nullptr
+hipError_t launch_dense(const DenseArgs& a, hipStream_t st, hipEvent_t (*ev)[2]);
 
 }  // namespace ffn

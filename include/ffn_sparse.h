@@ -112,9 +112,14 @@ ffn_status ffn_sparse_plan(const ffn_layer_desc *desc, const ffn_layer_weights *
  *           idx[b*ffn .. b*ffn + cnt[b]); the rest of the row is left unspecified.
  *   cnt     [B] int32 or NULL: |A_b|.
  *   scores  [B][ffn] fp32 or NULL: the predictor scores s (only written when mask == NULL).
- *   path    ffn_path: SPARSE = neuron-aware kernels; DENSE = dense MFMA kernels with the
- *           per-token active set applied in their epilogue; AUTO = DENSE when B reaches the
- *           plan's crossover batch, else SPARSE.  Both paths give the same y within rounding.
+ *   path    ffn_path.  SPARSE: only the rows of active neurons are read (one token: the batch-1
+ *           kernels; several fp16 tokens: passes of up to 32 tokens over the union of their
+ *           sets, on the matrix cores).  DENSE: every neuron's rows are read (fp16: the
+ *           batched kernels for fewer than 64 tokens, two MFMA GEMMs from 64 on), each token's
+ *           h still zeroed outside its own set.  AUTO: the device compares the union density
+ *           of the call's sets with the plan's crossover density for B and takes DENSE above
+ *           it, SPARSE below.  All paths give the same y within rounding.  fp32 and int4
+ *           layers have no matrix-core path: every path runs their per-token kernels.
  * Errors: FFN_ERR_INVALID_ARGUMENT for NULL x / y, B out of [1, max_batch], mask == NULL with
  * rank == 0, bad path.
  */
@@ -130,27 +135,39 @@ ffn_status ffn_sparse_forward(ffn_plan *plan, const void *x, int32_t B, float *y
 ffn_status ffn_dense_forward(ffn_plan *plan, const void *x, int32_t B, float *y,
                              const uint8_t *mask, void *stream);
 
-/* Crossover density for batch B: the union density above which AUTO takes the dense path. */
+/* Crossover density for batch B: the union density above which AUTO takes the dense path
+ * (batch buckets 1, 2-3, 4-7, ..., 4096).  The built-in value is 1 (never dense); calibration
+ * measures it, and a caller may set it. */
 ffn_status ffn_plan_crossover(const ffn_plan *plan, int32_t B, float *density);
+ffn_status ffn_plan_set_crossover(ffn_plan *plan, int32_t B, float density);
 
 ffn_status ffn_plan_destroy(ffn_plan *plan);
 
 /*
- * Instrumentation, for a caller that times one kernel of the decode path on its own.  A forward
- * runs four kernels per token: FFN_STAGE_PRED_Z (predictor stage 1), FFN_STAGE_PRED_S
- * (predictor stage 2, threshold and active bitmap), FFN_STAGE_GATHER (the active neurons' up,
- * gate and transposed-down rows: activation and one row axpy per neuron into partials of y) and
- * FFN_STAGE_REDUCE (sum of the partials).  While `start` and `stop`
- * (hipEvent_t handles passed as void*, created with timing enabled) are set for a stage, every
- * forward on this plan launches that stage's kernel with the two events attached to the dispatch
- * itself, so hipEventElapsedTime(start, stop) afterwards is that one launch's execution time.
- * NULL, NULL turns it off.  Not meant for calls under graph capture.
+ * Instrumentation, for a caller that times one kernel of a path on its own.  Stages:
+ *   batch-1 decode (four kernels per token): FFN_STAGE_PRED_Z (predictor stage 1),
+ *     FFN_STAGE_PRED_S (predictor stage 2, threshold and active bitmap), FFN_STAGE_GATHER (the
+ *     active neurons' up, gate and transposed-down rows: activation and one row axpy per
+ *     neuron into partials of y), FFN_STAGE_REDUCE (sum of the partials);
+ *   batched passes (fp16, several tokens): FFN_STAGE_BATCH_UPGATE (union rows of up / gate and
+ *     h on the matrix cores), FFN_STAGE_BATCH_DOWN (h times the union's transposed-down rows);
+ *   dense GEMMs (fp16, 64 tokens or more): FFN_STAGE_DENSE_UP (X W_up^T [, X W_gate^T] and h),
+ *     FFN_STAGE_DENSE_DOWN (H W_down_t), FFN_STAGE_DENSE_REDUCE (sum of its K slices).
+ * While `start` and `stop` (hipEvent_t handles passed as void*, created with timing enabled)
+ * are set for a stage, every launch of that stage's kernel on this plan carries the two events
+ * on the dispatch itself, so hipEventElapsedTime(start, stop) afterwards is the last such
+ * launch's execution time.  NULL, NULL turns it off.  Not meant for calls under graph capture.
  */
 typedef enum {
     FFN_STAGE_PRED_Z = 0,
     FFN_STAGE_PRED_S = 1,
     FFN_STAGE_GATHER = 2,
-    FFN_STAGE_REDUCE = 3
+    FFN_STAGE_REDUCE = 3,
+    FFN_STAGE_BATCH_UPGATE = 4,
+    FFN_STAGE_BATCH_DOWN = 5,
+    FFN_STAGE_DENSE_UP = 6,
+    FFN_STAGE_DENSE_DOWN = 7,
+    FFN_STAGE_DENSE_REDUCE = 8
 } ffn_stage;
 
 ffn_status ffn_plan_set_timing_events(ffn_plan *plan, int32_t stage, void *start, void *stop);

@@ -123,12 +123,17 @@ def test_falcon_40b_shape_batched(ffn, B):
 
 
 # ---- dense fallback and path choice --------------------------------------------------------
-@pytest.mark.parametrize("B", [1, 3, 40])
-@pytest.mark.parametrize("wd,act", [("f16", "relu"), ("f16", "reglu"), ("f16", "drelu"),
-                                    ("f32", "reglu"), ("i4g32", "drelu")])
-def test_dense_forward_is_the_dense_ffn(ffn, wd, act, B):
+@pytest.mark.parametrize("B", [1, 3, 40, 64, 130])
+@pytest.mark.parametrize("wd,act,d", [("f16", "relu", 256), ("f16", "reglu", 264),
+                                      ("f16", "drelu", 520), ("f32", "reglu", 256),
+                                      ("i4g32", "drelu", 256)])
+def test_dense_forward_is_the_dense_ffn(ffn, wd, act, d, B):
+    """fp16 with 64 tokens or more runs the two MFMA GEMMs (ragged token, K and column tiles
+    here), fewer tokens the batched kernels over every neuron."""
+    if wd != "f16" and B > 40:
+        pytest.skip("fp32 / int4 dense runs token by token: covered by the smaller batches")
     xd = "f32" if wd == "f32" else "f16"
-    cfg = synth.small_config(d=256, ffn=1056, rank=32, act=act, w_dtype=wd, x_dtype=xd,
+    cfg = synth.small_config(d=d, ffn=1056, rank=32, act=act, w_dtype=wd, x_dtype=xd,
                              p_dtype=xd, density=0.1, bias_up=True, bias_gate=True,
                              bias_down=True)
     host = synth.make_layer(cfg)
@@ -141,7 +146,7 @@ def test_dense_forward_is_the_dense_ffn(ffn, wd, act, B):
     ym = m.dense(x, mask=torch.from_numpy(masks).cuda())
     torch.cuda.synchronize()
     xh, yh, ymh = x.cpu().numpy(), y.cpu().numpy(), ym.cpu().numpy()
-    for t in range(B):
+    for t in (range(B) if B <= 40 else [0, 1, 63, B - 1]):
         y_ref, _ = oracle.ffn(OL, xh[t], None)
         assert normwise(yh[t], y_ref) <= TOL[wd], (t, normwise(yh[t], y_ref))
         y_ref, _ = oracle.ffn(OL, xh[t], masks[t])
@@ -149,7 +154,7 @@ def test_dense_forward_is_the_dense_ffn(ffn, wd, act, B):
     m.close()
 
 
-@pytest.mark.parametrize("B", [1, 6, 32])
+@pytest.mark.parametrize("B", [1, 6, 32, 70])
 def test_dense_and_auto_paths_equal_sparse(ffn, B):
     """path=DENSE reads every neuron's rows but keeps each token's predicted set (h = 0 outside
     it), so DENSE, AUTO and SPARSE agree within rounding and report the same index lists."""
@@ -181,7 +186,7 @@ def test_dense_and_auto_paths_equal_sparse(ffn, B):
 
 
 def test_falcon_40b_shape_prefill_dense(ffn):
-    """Prefill-style dense pass of the 8192 x 32768 layer over 64 tokens (two passes)."""
+    """Prefill-style dense GEMMs of the 8192 x 32768 layer over 64 tokens."""
     cfg = synth.CONFIGS["falcon_40b_relu_f16"]
     host = synth.make_layer(cfg, device="cuda")
     L, OL = to_device(host), oracle_layer(host)
@@ -193,4 +198,26 @@ def test_falcon_40b_shape_prefill_dense(ffn):
     for t in (0, 63):
         y_ref, _ = oracle.ffn(OL, xh[t], None)
         assert normwise(yh[t], y_ref) <= TOL["f16"]
+    m.close()
+
+
+@pytest.mark.parametrize("B", [8, 96])
+def test_auto_follows_the_device_choice(ffn, B):
+    """AUTO with the crossover forced to 0 takes the dense rows (bit-identical to DENSE); with
+    the crossover at 1 it keeps the sparse rows (bit-identical to SPARSE)."""
+    cfg = synth.small_config(d=256, ffn=1024, rank=32, act="reglu", w_dtype="f16",
+                             x_dtype="f16", p_dtype="f16", density=0.1, bias_gate=True)
+    L = to_device(synth.make_layer(cfg))
+    x = synth.make_tokens(cfg, B).cuda()
+    m = ffn.SparseFFN(L, max_batch=B)
+    y_sp = m.forward(x, path=ffn.FFN_PATH_SPARSE).clone()
+    y_de = m.forward(x, path=ffn.FFN_PATH_DENSE).clone()
+    ffn.ffn_plan_set_crossover(m.plan, B, 0.0)
+    y_a0 = m.forward(x, path=ffn.FFN_PATH_AUTO).clone()
+    ffn.ffn_plan_set_crossover(m.plan, B, 1.0)
+    y_a1 = m.forward(x, path=ffn.FFN_PATH_AUTO).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(y_a0, y_de)
+    assert torch.equal(y_a1, y_sp)
+    assert normwise(y_de.cpu().numpy(), y_sp.cpu().numpy().astype(np.float64)) <= 1e-3
     m.close()

@@ -233,7 +233,7 @@ def test_stage_timing_events(ffn):
         assert a.elapsed_time(b) > 0
         assert torch.equal(y0, y1)
     with pytest.raises(ffn.FFNError):
-        ffn.ffn_plan_set_timing_events(m.plan, 4, 0, 0)
+        ffn.ffn_plan_set_timing_events(m.plan, 9, 0, 0)
     m.close()
 
 
