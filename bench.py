@@ -1,14 +1,17 @@
 #!/usr/bin/env python3
-"""Decode benchmark of the activation-sparse FFN on one MI355X.
+"""Benchmark of the activation-sparse FFN on one MI355X.
 
-A step is one decode token (batch 1) through every layer of the workload: per layer the
-predictor picks the token's active neurons and only their rows are read (PowerInfer, unite.ai,
-"Adaptive sparse predictor" / "Neuron-aware operator").  Layers run one after another on one
-stream, as in a real decode.  Inputs are seeded synthetic tensors already resident in HBM; the
-timed region replays HIP graphs of the library's launches.
+Default: decode of the Llama-2-7B-shaped ReGLU layer stack (d=4096, ffn=11008, predictor rank
+256, fp16 weights, 32 layers, 512 tokens, batch 1).  A step is one decode token through every
+layer: per layer the predictor picks the token's active neurons and only their rows are read
+(PowerInfer, unite.ai, "自适应稀疏预测器" / "神经元感知运算符").  Layers run one after another on one
+stream, as in a real decode.  Other workloads: --config (the OPT-125m, Mistral-7B dReLU,
+Mixtral-47B int4 mixture and Falcon-40B shaped ones), --batch N (decode steps of N tokens whose
+active sets are united), --prefill N (N tokens per layer through the dense MFMA path).
 
-Printed (one JSON line on stdout): decode tokens/s, the effective HBM bandwidth over the bytes
-the method touches, the roofline of the dominant kernel (the gathered-row main kernel, timed with
+Inputs are seeded synthetic tensors already resident in HBM; the timed region replays HIP graphs
+of the library's launches.  Printed (one JSON line on stdout): tokens/s, the effective HBM
+bandwidth over the bytes the method touches, the roofline of the dominant kernel (timed with
 HIP events attached to its own dispatches), and the CPU oracle timed on the host as a baseline.
 Progress goes to stderr.
 """
@@ -16,7 +19,6 @@ from __future__ import annotations
 
 import argparse
 import json
-import math
 import os
 import sys
 import time
@@ -24,7 +26,9 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-HBM_PEAK_GBPS = 8000.0   # MI355X HBM3E, published
+HBM_PEAK_GBPS = 8000.0         # MI355X HBM3E, published
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 matrix, published
+CPU_BUDGET_S = 25.0            # CPU oracle sample: stop adding layers past this much CPU time
 
 
 def log(msg):
@@ -35,20 +39,19 @@ def row_bytes(cfg) -> float:
     return {"f32": 4 * cfg.d, "f16": 2 * cfg.d, "i4g32": cfg.d // 2 + (cfg.d // 32) * 2}[cfg.w_dtype]
 
 
-def stage_bytes(cfg):
-    """Algorithmic bytes of each kernel as (fixed bytes per launch, bytes per active neuron):
-    the weights the method must read.  x, y, z, the bitmap and the (index, h) list are overhead
-    and not counted."""
+def n_rows(cfg) -> int:
+    return 2 if cfg.act == "relu" else 3
+
+
+def n_bias(cfg) -> int:
+    return (1 if cfg.bias_up else 0) + (1 if (cfg.act != "relu" and cfg.bias_gate) else 0)
+
+
+def pred_bytes(cfg):
+    """Predictor bytes per token-layer (per step-layer in a batch): stage 1 (P1), stage 2 (P2 and
+    c2)."""
     pb = 4 if cfg.p_dtype == "f32" else 2
-    rows = 2 if cfg.act == "relu" else 3
-    nbias = (1 if cfg.bias_up else 0) + (1 if (cfg.act != "relu" and cfg.bias_gate) else 0)
-    return {
-        "pred_z": (cfg.rank * cfg.d * pb, 0),                      # P1 (c1 absent)
-        "pred_s": (cfg.ffn * cfg.rank * pb + 4 * cfg.ffn, 0),      # P2 + c2
-        # the active neurons' up (+ gate) and transposed-down rows and their biases
-        "gather": (0, rows * row_bytes(cfg) + 4 * nbias),
-        "reduce": (0, 0),                                          # partials only (overhead)
-    }
+    return cfg.rank * cfg.d * pb, cfg.ffn * cfg.rank * pb + 4 * cfg.ffn
 
 
 def profiled_traffic(kernel: str, workload: str):
@@ -77,13 +80,18 @@ def profiled_traffic(kernel: str, workload: str):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=None, help="timed decode tokens (default: all)")
-    ap.add_argument("--warmup", type=int, default=16, help="untimed tokens replayed first")
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default: the workload's token count / batch)")
+    ap.add_argument("--warmup", type=int, default=16, help="untimed steps replayed first")
     ap.add_argument("--config", default="llama2_7b_reglu_f16")
+    ap.add_argument("--batch", type=int, default=1, help="tokens per decode step (union path)")
+    ap.add_argument("--prefill", type=int, default=0,
+                    help="tokens per layer through the dense MFMA path instead of decode")
+    ap.add_argument("--layers", type=int, default=0, help="override the layer count (0: all)")
     ap.add_argument("--kernel-sample", type=int, default=32,
-                    help="tokens whose kernel launches are timed with dispatch events")
+                    help="steps whose kernel launches are timed with dispatch events")
     ap.add_argument("--cpu-tokens", type=int, default=3,
-                    help="tokens (x all layers) the CPU oracle baseline runs; 0 = skip")
+                    help="tokens the CPU oracle baseline runs per layer; 0 = skip")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="first run a plain device copy of this many MiB five times (a known "
                          "size against which a profiler's HBM byte counters are scaled)")
@@ -101,15 +109,19 @@ def main():
     import synth
 
     cfg = synth.CONFIGS[args.config]
-    if cfg.n_experts > 1:
-        raise SystemExit("the mixture-of-experts workload has its own bench mode (not built yet)")
-    L, T = cfg.layers, cfg.tokens
-    K = args.steps if args.steps else T
+    L = args.layers or cfg.layers
+    moe = cfg.n_experts > 1
+    prefill = args.prefill > 0
+    Bt = args.prefill if prefill else args.batch      # tokens per layer call
+    if moe and (Bt != 1 or prefill):
+        raise SystemExit("the mixture workload is measured at batch-1 decode")
+    K = args.steps if args.steps else (4 if prefill else max(1, cfg.tokens // Bt))
     W = min(args.warmup, K)
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
-    log("config %s: d=%d ffn=%d rank=%d act=%s w=%s layers=%d tokens=%d" % (
-        cfg.name, cfg.d, cfg.ffn, cfg.rank, cfg.act, cfg.w_dtype, L, K))
+    mode = "prefill" if prefill else "decode"
+    log("config %s (%s, %d token(s) per call): d=%d ffn=%d rank=%d act=%s w=%s layers=%d "
+        "steps=%d" % (cfg.name, mode, Bt, cfg.d, cfg.ffn, cfg.rank, cfg.act, cfg.w_dtype, L, K))
 
     if args.copy_mib:
         n = args.copy_mib << 20
@@ -121,56 +133,124 @@ def main():
         log("copy calibration: 5 x %d MiB device-to-device" % args.copy_mib)
         del src, dst
 
+    # ---- inputs, resident in HBM
     t0 = time.time()
-    layers, plans = [], []
-    for l in range(L):
-        layers.append(synth.make_layer(cfg, layer=l, device=dev))
-    x = torch.stack([synth.make_tokens(cfg, K, layer=l, device=dev) for l in range(L)])  # [L][K][d]
-    y = torch.empty(L, K, cfg.d, dtype=torch.float32, device=dev)
+    E = cfg.n_experts
+    layers = [[synth.make_layer(cfg, layer=l, expert=e, device=dev) for e in range(E)]
+              for l in range(L)]
+    routers = [synth.make_router(cfg, layer=l, device=dev) for l in range(L)] if moe else None
+    x = torch.stack([synth.make_tokens(cfg, K * Bt, layer=l, device=dev) for l in range(L)])
+    y = torch.empty(L, K * Bt, cfg.d, dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
     log("inputs generated on the GPU in %.1f s" % (time.time() - t0))
 
     stream = torch.cuda.Stream(device=dev)
     sp = stream.cuda_stream
-    probe = ffn.SparseFFN(layers[0], max_batch=1)
-    ws = torch.empty(probe.ws_bytes, dtype=torch.uint8, device=dev)   # one workspace, shared
-    probe.close()
-    mods = [ffn.SparseFFN(layers[l], max_batch=1, workspace=ws) for l in range(L)]
-    plans = [m.plan for m in mods]
-    xb = x.element_size() * cfg.d
-    xp = [[x[l].data_ptr() + t * xb for t in range(K)] for l in range(L)]
-    yp = [[y[l].data_ptr() + t * cfg.d * 4 for t in range(K)] for l in range(L)]
-
-    def token(t):
-        for l in range(L):
-            ffn.ffn_sparse_forward(plans[l], xp[l][t], 1, yp[l][t], path=ffn.FFN_PATH_SPARSE,
-                                   stream=sp)
-
-    # ---- active-set sizes of every timed (token, layer): a separate, untimed counting pass
-    cnt = torch.zeros(L, K, dtype=torch.int32, device=dev)
     with torch.cuda.stream(stream):
+        probe = ffn.SparseFFN(layers[0][0], max_batch=Bt)
+        ws = torch.empty(probe.ws_bytes, dtype=torch.uint8, device=dev)   # one, shared
+        probe.close()
+        mods = [[ffn.SparseFFN(layers[l][e], max_batch=Bt, workspace=ws) for e in range(E)]
+                for l in range(L)]
+        moes = None
+        if moe:
+            n = ffn.ffn_moe_workspace_size(E, cfg.top_k, mods[0][0].plan)
+            mws = torch.empty(n, dtype=torch.uint8, device=dev)
+            moes = [ffn.ffn_moe_plan(E, cfg.top_k, routers[l].data_ptr(),
+                                     [m.plan for m in mods[l]], mws.data_ptr(), n)
+                    for l in range(L)]
+    plans = [m.plan for row in mods for m in row]
+    xb = x.element_size() * cfg.d
+    xp = [[x[l].data_ptr() + t * Bt * xb for t in range(K)] for l in range(L)]
+    yp = [[y[l].data_ptr() + t * Bt * cfg.d * 4 for t in range(K)] for l in range(L)]
+
+    def call(l, t, **kw):
+        if prefill:
+            ffn.ffn_dense_forward(mods[l][0].plan, xp[l][t], Bt, yp[l][t], stream=sp)
+        elif moe:
+            ffn.ffn_moe_forward(moes[l], xp[l][t], 1, yp[l][t], stream=sp, **kw)
+        else:
+            ffn.ffn_sparse_forward(mods[l][0].plan, xp[l][t], Bt, yp[l][t],
+                                   path=ffn.FFN_PATH_SPARSE, stream=sp, **kw)
+
+    def step(t):
+        for l in range(L):
+            call(l, t)
+
+    # ---- bytes the method touches per (layer, step): an untimed counting pass
+    pz, ps = pred_bytes(cfg)
+    rowb = n_rows(cfg) * row_bytes(cfg) + 4 * n_bias(cfg)
+    router_b = cfg.n_experts * cfg.d * 2 if moe else 0
+    if prefill:
+        touched = np.full((L, K), float(cfg.ffn * rowb))      # every row once per call
+        density = 1.0
+    elif moe:
+        ids = torch.zeros(L, K, cfg.top_k, dtype=torch.int32, device=dev)
+        with torch.cuda.stream(stream):
+            for t in range(K):
+                for l in range(L):
+                    call(l, t, expert_idx=ids[l, t].data_ptr())
+        torch.cuda.synchronize()
+        ids_h = ids.cpu().numpy()
+        cnt = torch.zeros(L, K, cfg.top_k, dtype=torch.int32, device=dev)
+        with torch.cuda.stream(stream):
+            for t in range(K):
+                for l in range(L):
+                    for j in range(cfg.top_k):
+                        ffn.ffn_sparse_forward(mods[l][ids_h[l, t, j]].plan, xp[l][t], 1,
+                                               yp[l][t], cnt=cnt[l, t].data_ptr() + 4 * j,
+                                               stream=sp)
+        torch.cuda.synchronize()
+        cnt_h = cnt.cpu().numpy().astype(np.float64)
+        touched = router_b + cfg.top_k * (pz + ps) + cnt_h.sum(axis=2) * rowb
+        density = float(cnt_h.mean() / cfg.ffn)
+        log("measured density %.4f over the chosen experts" % density)
+    elif Bt == 1:
+        cnt = torch.zeros(L, K, dtype=torch.int32, device=dev)
+        with torch.cuda.stream(stream):
+            for t in range(K):
+                for l in range(L):
+                    call(l, t, cnt=cnt[l].data_ptr() + 4 * t)
+        torch.cuda.synchronize()
+        cnt_h = cnt.cpu().numpy().astype(np.float64)
+        touched = pz + ps + cnt_h * rowb
+        density = float(cnt_h.mean() / cfg.ffn)
+        log("measured density %.4f (mean |A| = %.1f of %d)" % (density, cnt_h.mean(), cfg.ffn))
+    else:
+        F = cfg.ffn
+        union = np.zeros((L, K))
+        idx = torch.zeros(Bt, F, dtype=torch.int32, device=dev)
+        cnt = torch.zeros(Bt, dtype=torch.int32, device=dev)
+        ar = torch.arange(F, device=dev)
+        per_tok = []
         for t in range(K):
             for l in range(L):
-                ffn.ffn_sparse_forward(plans[l], xp[l][t], 1, yp[l][t],
-                                       cnt=cnt[l].data_ptr() + 4 * t, stream=sp)
+                with torch.cuda.stream(stream):
+                    call(l, t, idx=idx.data_ptr(), cnt=cnt.data_ptr())
+                stream.synchronize()
+                valid = ar[None, :] < cnt[:, None].long()
+                m = torch.zeros(Bt, F, dtype=torch.bool, device=dev)
+                m.scatter_(1, torch.where(valid, idx.long(), 0), valid)
+                union[l, t] = float(m.any(dim=0).sum())
+                per_tok.append(float(cnt.float().mean()))
+        touched = pz + ps + union * rowb
+        density = float(np.mean(per_tok) / F)
+        log("measured per-token density %.4f, union density %.4f" % (
+            density, union.mean() / F))
     torch.cuda.synchronize()
-    cnt_h = cnt.cpu().numpy().astype(np.int64)
-    density = float(cnt_h.mean() / cfg.ffn)
-    log("measured density %.4f (mean |A| = %.1f of %d)" % (density, cnt_h.mean(), cfg.ffn))
 
-    # ---- HIP graphs of whole tokens (all layers), G tokens per graph
-    G = max(1, 256 // L)
+    # ---- HIP graphs of whole steps (all layers)
+    G = 1 if prefill else max(1, min(K, 256 // L))
     graphs = []
     with torch.cuda.stream(stream):
         for g0 in range(0, K, G):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g, stream=stream):
                 for t in range(g0, min(K, g0 + G)):
-                    token(t)
+                    step(t)
             graphs.append(g)
     torch.cuda.synchronize()
-    log("captured %d graphs of %d tokens" % (len(graphs), G))
-
+    log("captured %d graph(s) of %d step(s)" % (len(graphs), G))
     with torch.cuda.stream(stream):
         for g in graphs[:max(1, (W + G - 1) // G)]:
             g.replay()
@@ -186,98 +266,190 @@ def main():
         e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1)
-    tok_s = K / (ms / 1e3)
-    SB = stage_bytes(cfg)
-    touched = sum(f * L * K + a * cnt_h.sum() for f, a in SB.values())
-    eff_gbps = touched / (ms / 1e3) / 1e9
-    log("timed %d tokens: %.3f ms/token, %.1f tok/s, %.1f GB/s effective over touched bytes" % (
-        K, ms / K, tok_s, eff_gbps))
+    tok_s = K * Bt / (ms / 1e3)
+    eff_gbps = touched.sum() / (ms / 1e3) / 1e9
+    log("timed %d step(s): %.3f ms/step, %.1f tokens/s, %.1f GB/s effective over touched bytes"
+        % (K, ms / K, tok_s, eff_gbps))
 
-    # ---- per-kernel durations: HIP events attached to each kernel's own dispatch (plain
-    # launches of the same tokens); the dominant kernel gives the roofline
+    # ---- per-kernel durations: plain launches of the sampled steps with HIP events attached to
+    # the dispatches of one stage's kernel (on the stream they run on)
     S = min(args.kernel_sample, K)
+    passes = 1 if (prefill or Bt == 1) else (Bt + 31) // 32
+    if prefill:
+        kinds = [("dense_up", ffn.FFN_STAGE_DENSE_UP,
+                  2.0 * Bt * cfg.d * cfg.ffn * (1 if cfg.act == "relu" else 2)),
+                 ("dense_down", ffn.FFN_STAGE_DENSE_DOWN, 2.0 * Bt * cfg.d * cfg.ffn)]
+    elif Bt > 1:
+        kinds = [("batch_upgate", ffn.FFN_STAGE_BATCH_UPGATE, None),
+                 ("batch_down", ffn.FFN_STAGE_BATCH_DOWN, None)]
+    else:
+        kinds = [(n, i, None) for i, n in enumerate(ffn.STAGES)]
     stages = {}
-    for si, sname in enumerate(ffn.STAGES):
+    for sname, sid, flops in kinds:
+        n_launch = S * L
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(S * L)]
+               for _ in range(n_launch)]
         with torch.cuda.stream(stream):
-            for a, b in evs:            # materialise the events
+            for a, b in evs:              # materialise the events
                 a.record(stream)
                 b.record(stream)
         torch.cuda.synchronize()
-        i = 0
         with torch.cuda.stream(stream):
-            for t in range(S):
-                for l in range(L):
-                    a, b = evs[i]
-                    ffn.ffn_plan_set_timing_events(plans[l], si, a.cuda_event, b.cuda_event)
-                    ffn.ffn_sparse_forward(plans[l], xp[l][t], 1, yp[l][t], stream=sp)
-                    i += 1
+            for i in range(n_launch):
+                l, t = i % L, i // L
+                a, b = evs[i]
+                for m in mods[l]:
+                    ffn.ffn_plan_set_timing_events(m.plan, sid, a.cuda_event, b.cuda_event)
+                call(l, t)
         torch.cuda.synchronize()
-        for p in plans:
-            ffn.ffn_plan_set_timing_events(p, si, 0, 0)
-        dur_ms = np.array([a.elapsed_time(b) for a, b in evs])
-        fixed, per_a = SB[sname]
-        nbytes = fixed * S * L + per_a * cnt_h[:, :S].sum()
-        stages[sname] = {"avg_us": round(float(dur_ms.mean()) * 1e3, 3),
-                         "bytes_per_launch": int(nbytes / (S * L)),
-                         "gbps": round(nbytes / (dur_ms.sum() / 1e3) / 1e9, 1)}
-        log("kernel %-7s %8.2f us avg over %d launches, %7.1f GB/s algorithmic" % (
-            sname, dur_ms.mean() * 1e3, S * L, stages[sname]["gbps"]))
+        for q in plans:
+            ffn.ffn_plan_set_timing_events(q, sid, 0, 0)
+        dur = np.array([a.elapsed_time(b) for a, b in evs])      # ms, last launch of each call
+        rec = {"avg_us": round(float(dur.mean()) * 1e3, 3)}
+        if flops is not None:
+            rec["tflops"] = round(flops / (dur.mean() / 1e3) / 1e12, 1)
+            rec["flops_per_launch"] = flops
+        else:
+            per_call = touched[:, :S].sum() / (L * S)
+            k = cfg.top_k if moe else 1
+            if sname == "pred_z":
+                nb = pz
+            elif sname == "pred_s":
+                nb = ps
+            elif sname == "gather":
+                nb = (per_call - router_b - k * (pz + ps)) / k       # one expert slot's rows
+            elif sname == "reduce":
+                nb = 0.0
+            else:
+                rows_u = (per_call - pz - ps) / rowb / passes         # union rows per pass
+                nb = rows_u * (n_rows(cfg) - 1 if sname == "batch_upgate" else 1) * row_bytes(cfg)
+            rec["bytes_per_launch"] = int(nb)
+            rec["gbps"] = round(nb / (dur.mean() / 1e3) / 1e9, 1)
+        stages[sname] = rec
+        log("kernel %-13s %9.2f us avg over %d launches  %s" % (
+            sname, dur.mean() * 1e3, len(dur),
+            ("%.1f TFLOP/s" % rec["tflops"]) if "tflops" in rec else
+            ("%.1f GB/s algorithmic" % rec["gbps"])))
     dom = max(stages, key=lambda k: stages[k]["avg_us"])
-    achieved = stages[dom]["gbps"]
+    knames = {"pred_z": "k_pred_z", "pred_s": "k_pred_s", "gather": "k_gather",
+              "reduce": "k_reduce", "batch_upgate": "k_bug", "batch_down": "k_bdown",
+              "dense_up": "k_dup", "dense_down": "k_ddown"}
+    if prefill:
+        roof = {"bound": "mfma", "kernel": knames[dom], "achieved": stages[dom]["tflops"],
+                "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(stages[dom]["tflops"] / MFMA_F16_PEAK_TFLOPS, 4),
+                "traffic": profiled_traffic(knames[dom], cfg.name + ":prefill%d" % Bt),
+                "avg_us": stages[dom]["avg_us"],
+                "flops_per_launch": stages[dom]["flops_per_launch"]}
+    else:
+        wl = cfg.name if Bt == 1 else cfg.name + ":batch%d" % Bt
+        roof = {"bound": "hbm", "kernel": knames[dom], "achieved": stages[dom]["gbps"],
+                "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(stages[dom]["gbps"] / HBM_PEAK_GBPS, 4),
+                "traffic": profiled_traffic(knames[dom], wl),
+                "avg_us": stages[dom]["avg_us"],
+                "bytes_per_launch": stages[dom]["bytes_per_launch"]}
 
-    # ---- CPU oracle baseline on a bounded sample (first tokens x all layers), one thread, plus a
-    # parity spot check of the GPU outputs of the timed run on the same sample
+    # ---- CPU oracle baseline on a bounded sample (the first tokens, layer after layer until the
+    # CPU budget is spent; single thread), and a parity spot check of the GPU on layer 0
     cpu, parity = None, None
-    nt = min(args.cpu_tokens, K)
+    nt = min(args.cpu_tokens, K * Bt)
     if nt > 0:
         import oracle
         oracle.build()
-        idx = torch.zeros(L, nt, cfg.ffn, dtype=torch.int32, device=dev)
-        cn = torch.zeros(L, nt, dtype=torch.int32, device=dev)
-        ychk = torch.empty(L, nt, cfg.d, dtype=torch.float32, device=dev)
-        with torch.cuda.stream(stream):
-            for t in range(nt):
-                for l in range(L):
-                    ffn.ffn_sparse_forward(plans[l], xp[l][t], 1, ychk[l, t].data_ptr(),
-                                           idx=idx[l, t].data_ptr(), cnt=cn[l, t].data_ptr(),
-                                           stream=sp)
-        torch.cuda.synchronize()
-        same = bool(torch.equal(ychk, y[:, :nt]))
-        t_cpu, worst, flips = 0.0, 0.0, 0
         keys = ["w_up", "w_gate", "w_down_t", "s_up", "s_gate", "s_down_t", "b_up", "b_gate",
                 "b_down", "p1", "p2", "c1", "c2"]
-        for l in range(L):
-            OL = {k: (None if layers[l].get(k) is None else
-                      np.ascontiguousarray(layers[l][k].cpu().numpy())) for k in keys}
+
+        def host(layer):
+            OL = {k: (None if layer.get(k) is None else
+                      np.ascontiguousarray(layer[k].cpu().numpy())) for k in keys}
             OL["act"], OL["tau"] = cfg.act, cfg.tau
+            return OL
+
+        t_cpu, L_cpu = 0.0, 0
+        for l in range(L):
             xh = x[l, :nt].cpu().numpy()
+            if moe:
+                OLs = [host(e) for e in layers[l]]
+                Rh = routers[l].cpu().numpy()
+            else:
+                OL = host(layers[l][0])
             for t in range(nt):
                 c0 = time.perf_counter()
-                yref, pred = oracle.sparse_token(OL, xh[t])
+                if prefill:
+                    oracle.ffn(OL, xh[t], None)
+                elif moe:
+                    oracle.moe_token(OLs, Rh, xh[t], cfg.top_k)
+                else:
+                    oracle.sparse_token(OL, xh[t])
                 t_cpu += time.perf_counter() - c0
-                got = idx[l, t, :int(cn[l, t])].cpu().numpy()
-                if not np.array_equal(got, pred["idx"]):
-                    flips += 1
-                    band = np.abs(pred["p"] - cfg.tau) <= 1e-4
-                    assert np.array_equal(got[~band[got]], pred["idx"][~band[pred["idx"]]])
-                    mask = np.zeros(cfg.ffn, np.uint8)
-                    mask[got] = 1
-                    yref, _ = oracle.ffn(OL, xh[t], mask)
-                yg = y[l, t].cpu().numpy().astype(np.float64)
-                worst = max(worst, float(np.max(np.abs(yg - yref)) / np.max(np.abs(yref))))
-            del OL
-        cpu = {"value": round(nt / t_cpu, 4), "unit": "tokens/s", "cores": 1, "kind": "oracle",
-               "sample": "first %d token(s) x %d layers, predictor + FFN, single-threaded C, "
-                         "fp64 accumulation (%.1f s)" % (nt, L, t_cpu)}
-        parity = {"tokens": nt, "layers": L, "max_normwise_err": worst,
-                  "band_flips": flips, "timed_outputs_reproduced": same}
-        log("oracle: %.2f s for %d token(s); GPU parity max normwise error %.2e" % (
-            t_cpu, nt, worst))
+            L_cpu = l + 1
+            if t_cpu > CPU_BUDGET_S:
+                break
+        rate = nt * L_cpu / t_cpu / L          # tokens through all L layers per second
+        what = ("dense FFN" if prefill else
+                "router + the chosen experts' predictor and sparse FFN" if moe else
+                "predictor + sparse FFN")
+        cpu = {"value": round(rate, 5), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+               "sample": "first %d token(s) x %d of %d layers, %s, single-threaded C with fp64 "
+                         "accumulation (%.1f s of CPU), scaled to all layers" % (
+                             nt, L_cpu, L, what, t_cpu)}
 
+        # parity spot check: layer 0, the sampled tokens, against the oracle on the GPU's sets
+        OLs = [host(e) for e in layers[0]]
+        xh = x[0, :nt].cpu().numpy()
+        worst = 0.0
+        torch.cuda.synchronize()
+
+        def gpu_set(plan, t_ptr):
+            ie = torch.zeros(1, cfg.ffn, dtype=torch.int32, device=dev)
+            ce = torch.zeros(1, dtype=torch.int32, device=dev)
+            yy = torch.zeros(1, cfg.d, dtype=torch.float32, device=dev)
+            ffn.ffn_sparse_forward(plan, t_ptr, 1, yy.data_ptr(), idx=ie.data_ptr(),
+                                   cnt=ce.data_ptr(), stream=sp)
+            torch.cuda.synchronize()
+            mk = np.zeros(cfg.ffn, np.uint8)
+            mk[ie[0, :int(ce[0])].cpu().numpy()] = 1
+            return mk
+
+        for t in range(nt):
+            t_ptr = x[0].data_ptr() + t * xb
+            yg = y[0, t].cpu().numpy().astype(np.float64)          # from the timed run
+            if prefill:
+                yref, _ = oracle.ffn(OLs[0], xh[t], None)
+            elif moe:
+                idsc = torch.zeros(1, cfg.top_k, dtype=torch.int32, device=dev)
+                wc = torch.zeros(1, cfg.top_k, dtype=torch.float32, device=dev)
+                yy = torch.zeros(1, cfg.d, dtype=torch.float32, device=dev)
+                ffn.ffn_moe_forward(moes[0], t_ptr, 1, yy.data_ptr(), idsc.data_ptr(),
+                                    wc.data_ptr(), stream=sp)
+                torch.cuda.synchronize()
+                yref = np.zeros(cfg.d)
+                for j in range(cfg.top_k):
+                    e = int(idsc[0, j])
+                    ye, _ = oracle.ffn(OLs[e], xh[t], gpu_set(mods[0][e].plan, t_ptr))
+                    yref += float(wc[0, j]) * ye
+            elif Bt == 1:
+                yref, _ = oracle.ffn(OLs[0], xh[t], gpu_set(mods[0][0].plan, t_ptr))
+            else:
+                idx = torch.zeros(Bt, cfg.ffn, dtype=torch.int32, device=dev)
+                cn = torch.zeros(Bt, dtype=torch.int32, device=dev)
+                yb = torch.zeros(Bt, cfg.d, dtype=torch.float32, device=dev)
+                ffn.ffn_sparse_forward(mods[0][0].plan, x[0].data_ptr(), Bt, yb.data_ptr(),
+                                       idx=idx.data_ptr(), cnt=cn.data_ptr(), stream=sp)
+                torch.cuda.synchronize()
+                mk = np.zeros(cfg.ffn, np.uint8)
+                mk[idx[t, :int(cn[t])].cpu().numpy()] = 1
+                yref, _ = oracle.ffn(OLs[0], xh[t], mk)
+            worst = max(worst, float(np.max(np.abs(yg - yref)) / np.max(np.abs(yref))))
+        parity = {"tokens": nt, "layer": 0, "max_normwise_err": worst}
+        log("oracle: %.2f s for %d token(s) x %d layer(s); GPU parity max normwise error %.2e"
+            % (t_cpu, nt, L_cpu, worst))
+
+    dtype = {"f32": "f32", "f16": "f16xf16->f32", "i4g32": "i4g32xf16->f32"}[cfg.w_dtype]
     result = {
-        "metric": "sparse-FFN decode tokens/s at 1 GPU; effective HBM GB/s of touched weights",
+        "metric": ("sparse-FFN decode tokens/s at 1 GPU; effective HBM GB/s of touched weights"
+                   if not prefill else "dense-FFN prefill tokens/s at 1 GPU (MFMA fallback)"),
         "value": round(tok_s, 2),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -287,19 +459,15 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {"f32": "f32", "f16": "f16xf16->f32", "i4g32": "i4g32xf16->f32"}[cfg.w_dtype],
+        "dtype": dtype,
         "data": "synthetic (seeded; power-law hot set)",
-        "config": {"workload": cfg.name, "d": cfg.d, "ffn": cfg.ffn, "rank": cfg.rank,
-                   "act": cfg.act, "layers": L, "tokens": K, "batch": 1,
+        "config": {"workload": cfg.name, "mode": mode, "tokens_per_call": Bt, "d": cfg.d,
+                   "ffn": cfg.ffn, "rank": cfg.rank, "act": cfg.act, "layers": L,
+                   "experts": cfg.n_experts, "top_k": cfg.top_k if moe else None,
                    "target_density": cfg.density, "measured_density": round(density, 5)},
         "effective_gbps": round(eff_gbps, 1),
-        "touched_bytes_per_token": int(touched / K),
-        "roofline": {"bound": "hbm", "kernel": "k_" + dom,
-                     "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": profiled_traffic("k_" + dom, cfg.name),
-                     "avg_us": stages[dom]["avg_us"],
-                     "bytes_per_launch": stages[dom]["bytes_per_launch"]},
+        "touched_bytes_per_step": int(touched.sum() / K),
+        "roofline": roof,
         "kernels": stages,
         "cpu_baseline": cpu,
         "parity_sample": parity,
