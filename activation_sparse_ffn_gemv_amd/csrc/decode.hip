@@ -219,13 +219,16 @@ __global__ __launch_bounds__(256) void k_mask_bits(const unsigned char* __restri
 // rank: workgroup g owns ranks [g*|A|/G, (g+1)*|A|/G).
 //   1. the bitmap (two words per thread) is prefix-summed over the workgroup; the threads whose
 //      words hold the workgroup's ranks write those neurons to an LDS list;
-//   2. rounds of up to RN neurons: thread t owns the 16-byte column chunks t, t + 512, ... of
-//      every row; it requests its chunks of the up, gate and transposed-down rows of all the
-//      round's neurons at once, forms partial dot products with its slice of the token; the
-//      partials are summed over the workgroup (DPP wave sums, then the waves in order) into
-//      u, g and h; each thread adds h * (its down chunks) to its own accumulator: one
-//      contiguous-row axpy per active neuron;
-//   3. the accumulators are the workgroup's partial of y (written only when it owns a rank).
+//   2. the threads form SLOTS groups of TPR = 512 / SLOTS (SLOTS > 1 when a row has fewer
+//      16-byte chunks than the workgroup has threads); thread (slot, c) owns the column chunks
+//      c, c + TPR, ... of every row.  Rounds of up to SLOTS * RN neurons, neuron q of a round on
+//      slot q % SLOTS: every thread requests its chunks of the up, gate and transposed-down rows
+//      of its slot's neurons at once (the neurons' biases with them), forms partial dot products
+//      with its slice of the token; the partials are summed over the slot (DPP wave sums, then
+//      the slot's waves in order) into u, g and h; each thread adds h * (its down chunks) to its
+//      own accumulator: one contiguous-row axpy per active neuron;
+//   3. the slots' accumulators are summed through LDS (fixed order) and form the workgroup's
+//      partial of y (written only when it owns a rank).
 // Every workgroup and every thread does the same work, so the load is even over the CUs.
 constexpr int GA_THREADS = 512;
 constexpr int GA_NW = GA_THREADS / WAVE;
@@ -234,19 +237,28 @@ constexpr int RD_TW = 16;             // columns per reduce tile (64 bytes of ev
 constexpr int GA_MAXW = 2;            // bitmap words per thread: ffn <= 32768
 constexpr int GA_LIST = 64;           // ranks resolved per batch
 
-template <int WK, int CPT> struct Round { static constexpr int RN = WK == WK_I4 ? 8 : 16 / CPT; };
+// Neurons per slot and round: as many as the registers hold, and every round fits the rank batch.
+template <int WK, int CPT, int SLOTS> struct Round {
+  static constexpr int BASE = WK == WK_I4 ? 8 : 16 / CPT;
+  static constexpr int RN = BASE * SLOTS <= GA_LIST ? BASE : GA_LIST / SLOTS;
+};
 
-template <int WK, int CPT>
+template <int WK, int CPT, int SLOTS>
 __global__ __launch_bounds__(GA_THREADS) void k_gather(GatherArgs a) {
   constexpr int NT = GA_THREADS;
-  constexpr int RN = Round<WK, CPT>::RN;
+  constexpr int TPR = NT / SLOTS;                 // threads per row
+  constexpr int WPS = TPR / WAVE;                 // waves per slot
+  constexpr int RN = Round<WK, CPT, SLOTS>::RN;   // neurons per slot and round
+  constexpr int RQ = RN * SLOTS;                  // neurons per round
   constexpr int EPC = Kind<WK>::EPC;
+  static_assert(RQ <= GA_LIST && GA_LIST % RQ == 0, "rounds tile the rank batch");
   __shared__ int s_wsum[GA_NW];
   __shared__ int s_list[GA_LIST];
   __shared__ float s_red[GA_NW][2 * RN];
-  __shared__ float s_h[RN];
+  __shared__ float s_h[RQ];
   const int tid = threadIdx.x;
   const int lane = tid & (WAVE - 1), wave = tid / WAVE;
+  const int slot = tid / TPR, ct = tid % TPR;
   const int nch = a.d / EPC;
   FFN_TS(1, 0);
   if (a.slot) {
@@ -261,11 +273,11 @@ __global__ __launch_bounds__(GA_THREADS) void k_gather(GatherArgs a) {
     a.b_gate = e.b_gate;
   }
 
-  // this thread's chunks of the token (chunk tid + k*NT)
+  // this thread's chunks of the token (chunk ct + k*TPR)
   u32x4 xr[CPT][Kind<WK>::XW];
 #pragma unroll
   for (int k = 0; k < CPT; ++k) {
-    const int c = tid + k * NT;
+    const int c = ct + k * TPR;
     const int cc = min(c, nch - 1);
 #pragma unroll
     for (int q = 0; q < Kind<WK>::XW; ++q) {
@@ -330,16 +342,24 @@ __global__ __launch_bounds__(GA_THREADS) void k_gather(GatherArgs a) {
     }
     __syncthreads();
     FFN_TS(1, 2);
-    for (int t0 = 0; t0 < nl; t0 += RN) {
+    for (int t0 = 0; t0 < nl; t0 += RQ) {
       u32x4 wu[RN][CPT], wg[RN][CPT], wd[RN][CPT];
       float su[RN][CPT], sg[RN][CPT], sd[RN][CPT];
+      // the biases of the round's neurons travel with the rows (thread q < RQ: neuron q)
+      float bu = 0.0f, bgt = 0.0f;
+      if (tid < RQ && t0 + tid < nl) {
+        const int nq = s_list[t0 + tid];
+        if (a.b_up) bu = a.b_up[nq];
+        if (a.b_gate) bgt = a.b_gate[nq];
+      }
 #pragma unroll
       for (int r = 0; r < RN; ++r) {
-        const bool live_r = t0 + r < nl;                     // uniform across the workgroup
-        const size_t nr = (size_t)s_list[min(t0 + r, nl - 1)];
+        const int q = r * SLOTS + slot;                      // this slot's r-th neuron
+        const bool live_r = t0 + q < nl;                     // uniform across the slot's waves
+        const size_t nr = (size_t)s_list[min(t0 + q, nl - 1)];
 #pragma unroll
         for (int k = 0; k < CPT; ++k) {
-          const int cc = min(tid + k * NT, nch - 1);
+          const int cc = min(ct + k * TPR, nch - 1);
           const size_t off = (nr * nch + cc) * 16;
           wu[r][k] = wg[r][k] = wd[r][k] = u32x4{0u, 0u, 0u, 0u};
           su[r][k] = sg[r][k] = sd[r][k] = 0.0f;
@@ -372,7 +392,7 @@ __global__ __launch_bounds__(GA_THREADS) void k_gather(GatherArgs a) {
             if (a.has_gate) pg = dot32_i4(wg[r][k], xr[k], sg[r][k], pg);
           }
         }
-        if (t0 + r < nl) {                                   // uniform across the workgroup
+        if (t0 + r * SLOTS + slot < nl) {                    // uniform across the wave
           pu = wave_sum(pu);
           if (a.has_gate) pg = wave_sum(pg);
           if (lane == 0) {
@@ -382,30 +402,30 @@ __global__ __launch_bounds__(GA_THREADS) void k_gather(GatherArgs a) {
         }
       }
       __syncthreads();
-      if (tid < RN) {
+      if (tid < RQ) {
+        const int q = tid, qs = q % SLOTS, qr = q / SLOTS;
         float u = 0.0f, g = 0.0f, h = 0.0f;
-        if (t0 + tid < nl) {
+        if (t0 + q < nl) {
 #pragma unroll
-          for (int w = 0; w < GA_NW; ++w) {
-            u += s_red[w][2 * tid];
-            g += s_red[w][2 * tid + 1];
+          for (int w = 0; w < WPS; ++w) {
+            u += s_red[qs * WPS + w][2 * qr];
+            g += s_red[qs * WPS + w][2 * qr + 1];
           }
-          const int nr = s_list[t0 + tid];
-          u += a.b_up ? a.b_up[nr] : 0.0f;
+          u += bu;
           if (a.act == FFN_ACT_RELU) {
             h = fmaxf(u, 0.0f);
           } else {
-            g = fmaxf(g + (a.b_gate ? a.b_gate[nr] : 0.0f), 0.0f);
+            g = fmaxf(g + bgt, 0.0f);
             h = a.act == FFN_ACT_REGLU ? g * u : g * fmaxf(u, 0.0f);
           }
         }
-        s_h[tid] = h;                                        // 0 for slots past the list
+        s_h[q] = h;                                          // 0 for slots past the list
       }
       __syncthreads();
       FFN_TS(1, 3);
 #pragma unroll
       for (int r = 0; r < RN; ++r) {
-        const float h = s_h[r];
+        const float h = s_h[r * SLOTS + slot];
 #pragma unroll
         for (int k = 0; k < CPT; ++k) {
           if constexpr (WK == WK_F32) {
@@ -437,20 +457,45 @@ __global__ __launch_bounds__(GA_THREADS) void k_gather(GatherArgs a) {
     }
   }
   if (r1 > r0) {
+    if constexpr (SLOTS > 1) {
+      // sum the slots' accumulators: halve the live slots through LDS until slot 0 holds all
+      extern __shared__ __align__(16) float s_acc[];         // (SLOTS/2) * TPR * CPT * EPC
+#pragma unroll
+      for (int half = SLOTS / 2; half >= 1; half /= 2) {
+        if (slot >= half && slot < 2 * half) {
+#pragma unroll
+          for (int k = 0; k < CPT; ++k)
+#pragma unroll
+            for (int e = 0; e < EPC; ++e)
+              s_acc[(((slot - half) * CPT + k) * EPC + e) * TPR + ct] = acc[k][e];
+        }
+        __syncthreads();
+        if (slot < half) {
+#pragma unroll
+          for (int k = 0; k < CPT; ++k)
+#pragma unroll
+            for (int e = 0; e < EPC; ++e)
+              acc[k][e] += s_acc[((slot * CPT + k) * EPC + e) * TPR + ct];
+        }
+        __syncthreads();
+      }
+    }
     // partial of y, tile-major: part[col / RD_TW][workgroup][col % RD_TW], so that the reduce
     // reads one contiguous block per tile
+    if (slot == 0) {
 #pragma unroll
-    for (int k = 0; k < CPT; ++k) {
-      const int c = tid + k * NT;
-      if (c < nch) {
+      for (int k = 0; k < CPT; ++k) {
+        const int c = ct + k * TPR;
+        if (c < nch) {
 #pragma unroll
-        for (int e = 0; e < EPC; e += 4) {
-          const int col = c * EPC + e;
-          float* dst = a.part + ((size_t)(col / RD_TW) * GA_BLOCKS + blockIdx.x) * RD_TW +
-                       col % RD_TW;
-          // streaming store: the partial is read once, by the next kernel
-          __builtin_nontemporal_store(f32x4{acc[k][e], acc[k][e + 1], acc[k][e + 2], acc[k][e + 3]},
-                                      reinterpret_cast<f32x4*>(dst));
+          for (int e = 0; e < EPC; e += 4) {
+            const int col = c * EPC + e;
+            float* dst = a.part + ((size_t)(col / RD_TW) * GA_BLOCKS + blockIdx.x) * RD_TW +
+                         col % RD_TW;
+            // streaming store: the partial is read once, by the next kernel
+            __builtin_nontemporal_store(f32x4{acc[k][e], acc[k][e + 1], acc[k][e + 2], acc[k][e + 3]},
+                                        reinterpret_cast<f32x4*>(dst));
+          }
         }
       }
     }
@@ -592,36 +637,53 @@ hipError_t launch_mask_bits(const unsigned char* mask, uint32_t* bitmap, int wor
   return hipGetLastError();
 }
 
+// Threads per row of the gather kernel: the smallest multiple of 64 lanes, a power-of-two
+// fraction of the workgroup, that covers the row's 16-byte chunks once or twice.
+static int gather_slots(int nch) {
+  int slots = 1;
+  while (slots < 8 && GA_THREADS / (slots * 2) >= nch) slots *= 2;
+  return slots;
+}
+
 // 16-byte chunks of a weight row per thread of the gather kernel
 int gather_cpt(int wk, int d) {
   const int nch = d / (wk == WK_F32 ? 4 : wk == WK_F16 ? 8 : 32);
-  return (nch + GA_THREADS - 1) / GA_THREADS;
+  const int tpr = GA_THREADS / gather_slots(nch);
+  return (nch + tpr - 1) / tpr;
 }
 int gather_blocks() { return GA_BLOCKS; }
 
-template <int WK, int CPT>
+template <int WK, int CPT, int SLOTS>
 static hipError_t launch_gather_t(const GatherArgs& a, hipStream_t st, hipEvent_t ev0,
                                   hipEvent_t ev1) {
+  // LDS for the slots' accumulator sum (dynamic: only multi-slot variants use it)
+  const size_t lds = SLOTS > 1 ? (size_t)(SLOTS / 2) * (GA_THREADS / SLOTS) * CPT *
+                                     Kind<WK>::EPC * sizeof(float) : 0;
   if (ev0 && ev1)
-    hipExtLaunchKernelGGL((k_gather<WK, CPT>), dim3(GA_BLOCKS), dim3(GA_THREADS), 0, st, ev0, ev1,
-                          0, a);
+    hipExtLaunchKernelGGL((k_gather<WK, CPT, SLOTS>), dim3(GA_BLOCKS), dim3(GA_THREADS), lds, st,
+                          ev0, ev1, 0, a);
   else
-    hipLaunchKernelGGL((k_gather<WK, CPT>), dim3(GA_BLOCKS), dim3(GA_THREADS), 0, st, a);
+    hipLaunchKernelGGL((k_gather<WK, CPT, SLOTS>), dim3(GA_BLOCKS), dim3(GA_THREADS), lds, st, a);
   return hipGetLastError();
 }
 
 hipError_t launch_gather(int wk, const GatherArgs& a, hipStream_t st, hipEvent_t ev0,
                          hipEvent_t ev1) {
+  const int nch = a.d / (wk == WK_F32 ? 4 : wk == WK_F16 ? 8 : 32);
+  const int slots = gather_slots(nch);
   const int cpt = gather_cpt(wk, a.d);
+#define GA_CASE(W, C, S) \
+  if (cpt == C && slots == S) return launch_gather_t<W, C, S>(a, st, ev0, ev1);
   if (wk == WK_F32) {
-    if (cpt == 1) return launch_gather_t<WK_F32, 1>(a, st, ev0, ev1);
-    if (cpt == 2) return launch_gather_t<WK_F32, 2>(a, st, ev0, ev1);
+    GA_CASE(WK_F32, 1, 1) GA_CASE(WK_F32, 2, 1) GA_CASE(WK_F32, 1, 2) GA_CASE(WK_F32, 1, 4)
+    GA_CASE(WK_F32, 1, 8)
   } else if (wk == WK_F16) {
-    if (cpt == 1) return launch_gather_t<WK_F16, 1>(a, st, ev0, ev1);
-    if (cpt == 2) return launch_gather_t<WK_F16, 2>(a, st, ev0, ev1);
+    GA_CASE(WK_F16, 1, 1) GA_CASE(WK_F16, 2, 1) GA_CASE(WK_F16, 1, 2) GA_CASE(WK_F16, 1, 4)
+    GA_CASE(WK_F16, 1, 8)
   } else {
-    if (cpt == 1) return launch_gather_t<WK_I4, 1>(a, st, ev0, ev1);
+    GA_CASE(WK_I4, 1, 1) GA_CASE(WK_I4, 1, 2) GA_CASE(WK_I4, 1, 4) GA_CASE(WK_I4, 1, 8)
   }
+#undef GA_CASE
   return hipErrorInvalidValue;
 }
 
