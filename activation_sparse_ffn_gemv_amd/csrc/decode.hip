@@ -378,21 +378,21 @@ __global__ __launch_bounds__(GA_THREADS) void k_gather(GatherArgs a) {
       issue_fence();
 #pragma unroll
       for (int r = 0; r < RN; ++r) {
-        float pu = 0.0f, pg = 0.0f;
-#pragma unroll
-        for (int k = 0; k < CPT; ++k) {
-          if constexpr (WK == WK_F32) {
-            pu = dot4_f32(wu[r][k], xr[k][0], pu);
-            if (a.has_gate) pg = dot4_f32(wg[r][k], xr[k][0], pg);
-          } else if constexpr (WK == WK_F16) {
-            pu = dot8_f16(wu[r][k], xr[k][0], pu);
-            if (a.has_gate) pg = dot8_f16(wg[r][k], xr[k][0], pg);
-          } else {
-            pu = dot32_i4(wu[r][k], xr[k], su[r][k], pu);
-            if (a.has_gate) pg = dot32_i4(wg[r][k], xr[k], sg[r][k], pg);
-          }
-        }
         if (t0 + r * SLOTS + slot < nl) {                    // uniform across the wave
+          float pu = 0.0f, pg = 0.0f;
+#pragma unroll
+          for (int k = 0; k < CPT; ++k) {
+            if constexpr (WK == WK_F32) {
+              pu = dot4_f32(wu[r][k], xr[k][0], pu);
+              if (a.has_gate) pg = dot4_f32(wg[r][k], xr[k][0], pg);
+            } else if constexpr (WK == WK_F16) {
+              pu = dot8_f16(wu[r][k], xr[k][0], pu);
+              if (a.has_gate) pg = dot8_f16(wg[r][k], xr[k][0], pg);
+            } else {
+              pu = dot32_i4(wu[r][k], xr[k], su[r][k], pu);
+              if (a.has_gate) pg = dot32_i4(wg[r][k], xr[k], sg[r][k], pg);
+            }
+          }
           pu = wave_sum(pu);
           if (a.has_gate) pg = wave_sum(pg);
           if (lane == 0) {
@@ -425,6 +425,7 @@ __global__ __launch_bounds__(GA_THREADS) void k_gather(GatherArgs a) {
       FFN_TS(1, 3);
 #pragma unroll
       for (int r = 0; r < RN; ++r) {
+        if (t0 + r * SLOTS + slot >= nl) break;              // uniform; later slots are dead too
         const float h = s_h[r * SLOTS + slot];
 #pragma unroll
         for (int k = 0; k < CPT; ++k) {

@@ -59,8 +59,10 @@ __device__ __forceinline__ int xcd_tile(int total) {
 
 }  // namespace
 
+template <bool GATE>
 __global__ __launch_bounds__(DT) void k_dup(DenseArgs a) {
-  __shared__ u32x4 s_b[2][2][DU_N * DU_LD];          // [buffer][up, gate][row * DU_LD + chunk]
+  constexpr int NMAT = GATE ? 2 : 1;
+  __shared__ u32x4 s_b[2][NMAT][DU_N * DU_LD];       // [buffer][up, gate][row * DU_LD + chunk]
   if (a.run_if && *a.run_if != a.run_want) return;
   const int nb_m = (a.M + DU_M - 1) / DU_M, nb_n = (a.ffn + DU_N - 1) / DU_N;
   const int tile = xcd_tile(nb_m * nb_n);
@@ -69,7 +71,6 @@ __global__ __launch_bounds__(DT) void k_dup(DenseArgs a) {
   const int tid = threadIdx.x, lane = tid & (WAVE - 1), wave = tid / WAVE;
   const int r32 = lane & 31, g = lane >> 5;
   const int nchk = a.d / 8;
-  const int nmat = a.has_gate ? 2 : 1;
 
   // token row of this lane (A operand), clamped; rows past M read zeros
   const int am = m0 + wave * 32 + r32;
@@ -77,7 +78,7 @@ __global__ __launch_bounds__(DT) void k_dup(DenseArgs a) {
   const char* arow = static_cast<const char*>(a.x) + (size_t)min(am, a.M - 1) * a.d * 2;
   // weight tile loads: 128 rows x 4 chunks per matrix, two per thread
   const char* wsrc[2] = {static_cast<const char*>(a.w_up),
-                         static_cast<const char*>(a.has_gate ? a.w_gate : a.w_up)};
+                         static_cast<const char*>(GATE ? a.w_gate : a.w_up)};
   int lrow[2], lch[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
@@ -85,18 +86,15 @@ __global__ __launch_bounds__(DT) void k_dup(DenseArgs a) {
     lch[i] = tid % DU_KC;
   }
 
-  auto load_w = [&](int k0c, u32x4 (&v)[2][2]) {
+  auto load_w = [&](int k0c, u32x4 (&v)[NMAT][2]) {
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+    for (int mt = 0; mt < NMAT; ++mt)
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        v[mt][i] = u32x4{0u, 0u, 0u, 0u};
-        if (mt < nmat) {                               // uniform: no gate rows for ReLU
-          const int c = k0c + lch[i];
-          const size_t row = (size_t)min(n0 + lrow[i], a.ffn - 1);
-          const u32x4 t = ld16(wsrc[mt] + (row * nchk + min(c, nchk - 1)) * 16);
-          v[mt][i] = c < nchk ? t : u32x4{0u, 0u, 0u, 0u};
-        }
+        const int c = k0c + lch[i];
+        const size_t row = (size_t)min(n0 + lrow[i], a.ffn - 1);
+        const u32x4 t = ld16(wsrc[mt] + (row * nchk + min(c, nchk - 1)) * 16);
+        v[mt][i] = c < nchk ? t : u32x4{0u, 0u, 0u, 0u};
       }
   };
   auto load_a = [&](int k0c, u32x4 (&v)[2]) {
@@ -107,19 +105,21 @@ __global__ __launch_bounds__(DT) void k_dup(DenseArgs a) {
       v[kk] = (aok && c < nchk) ? t : u32x4{0u, 0u, 0u, 0u};
     }
   };
-  auto store_w = [&](int buf, const u32x4 (&v)[2][2]) {
+  auto store_w = [&](int buf, const u32x4 (&v)[NMAT][2]) {
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+    for (int mt = 0; mt < NMAT; ++mt)
 #pragma unroll
       for (int i = 0; i < 2; ++i) s_b[buf][mt][lrow[i] * DU_LD + lch[i]] = v[mt][i];
   };
 
-  f32x16 au[4], ag[4];
+  f32x16 au[4], ag[GATE ? 4 : 1];
 #pragma unroll
-  for (int t = 0; t < 4; ++t) au[t] = ag[t] = f32x16{};
+  for (int t = 0; t < 4; ++t) au[t] = f32x16{};
+#pragma unroll
+  for (int t = 0; t < (GATE ? 4 : 1); ++t) ag[t] = f32x16{};
 
   const int nstage = (nchk + DU_KC - 1) / DU_KC;
-  u32x4 wv[2][2], av[2];
+  u32x4 wv[NMAT][2], av[2];
   load_w(0, wv);
   load_a(0, av);
   store_w(0, wv);
@@ -138,7 +138,7 @@ __global__ __launch_bounds__(DT) void k_dup(DenseArgs a) {
       for (int t = 0; t < 4; ++t) {
         const int idx = (t * 32 + r32) * DU_LD + 2 * kk + g;
         au[t] = mma16(av[kk], s_b[buf][0][idx], au[t]);
-        if (a.has_gate) ag[t] = mma16(av[kk], s_b[buf][1][idx], ag[t]);
+        if constexpr (GATE) ag[t] = mma16(av[kk], s_b[buf][NMAT - 1][idx], ag[t]);
       }
     if (more) {
       store_w(buf ^ 1, wv);
@@ -161,7 +161,7 @@ __global__ __launch_bounds__(DT) void k_dup(DenseArgs a) {
       const int m = m0 + wave * 32 + acc_row(i, lane);
       const float u = au[t][i] + bu;
       float h;
-      if (a.act == FFN_ACT_RELU) {
+      if constexpr (!GATE) {
         h = fmaxf(u, 0.0f);
       } else {
         const float gg = fmaxf(ag[t][i] + bg, 0.0f);
@@ -332,10 +332,17 @@ hipError_t launch_dense(const DenseArgs& a, hipStream_t st, hipEvent_t (*ev)[2])
   const int t_dn = ((a.M + DD_M - 1) / DD_M) * ((a.d + DD_N - 1) / DD_N) * a.ks;
   const dim3 g_up(8 * ((t_up + 7) / 8)), g_dn(8 * ((t_dn + 7) / 8));
   const dim3 g_red((unsigned)(((size_t)a.M * a.d / 4 + 255) / 256));
-  if (ev && ev[0][0])
-    hipExtLaunchKernelGGL(k_dup, g_up, dim3(DT), 0, st, ev[0][0], ev[0][1], 0, a);
-  else
-    hipLaunchKernelGGL(k_dup, g_up, dim3(DT), 0, st, a);
+  if (a.has_gate) {
+    if (ev && ev[0][0])
+      hipExtLaunchKernelGGL(k_dup<true>, g_up, dim3(DT), 0, st, ev[0][0], ev[0][1], 0, a);
+    else
+      hipLaunchKernelGGL(k_dup<true>, g_up, dim3(DT), 0, st, a);
+  } else {
+    if (ev && ev[0][0])
+      hipExtLaunchKernelGGL(k_dup<false>, g_up, dim3(DT), 0, st, ev[0][0], ev[0][1], 0, a);
+    else
+      hipLaunchKernelGGL(k_dup<false>, g_up, dim3(DT), 0, st, a);
+  }
   if (ev && ev[1][0])
     hipExtLaunchKernelGGL(k_ddown, g_dn, dim3(DT), 0, st, ev[1][0], ev[1][1], 0, a);
   else
