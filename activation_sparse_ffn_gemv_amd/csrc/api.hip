@@ -8,7 +8,9 @@
 #include <string.h>
 
 #include <algorithm>
+#include <functional>
 #include <new>
+#include <vector>
 
 #include "common.h"
 #include "launch.h"
@@ -231,6 +233,8 @@ MoeLayout moe_layout(const ffn_plan* e0, int top_k) {
 
 }  // namespace
 
+ffn_status calibrate_crossover(ffn_plan* p, hipStream_t st);
+
 struct ffn_moe {
   int n_experts, top_k;
   const void* router;
@@ -327,6 +331,103 @@ ffn_status enqueue_token(const ffn_plan* p, const TokenBufs& wb, const void* xb,
   return FFN_OK;
 }
 
+// Measured crossover (ffn_sparse_plan with calibrate = 1).  For each batch bucket B = 2, 4, 8,
+// ... up to max_batch, the plan's own kernels are timed on its own weights: the dense path
+// (every neuron's rows) and the sparse path over caller sets in which every token has the same
+// random set of density rho, for rho on a grid.  The crossover is the density at which the
+// sparse time reaches the dense time (linear between grid points; 1 when the sparse path is
+// never slower).  Synchronous; the scratch buffers are allocated and freed here.
+ffn_status time_call(hipStream_t st, hipEvent_t e0, hipEvent_t e1, float* ms,
+                     const std::function<ffn_status()>& f) {
+  float best = 1e30f;
+  for (int rep = 0; rep < 4; ++rep) {
+    hipError_t e = hipEventRecord(e0, st);
+    if (e != hipSuccess) return hip_fail(e, "calibration event");
+    ffn_status s = f();
+    if (s != FFN_OK) return s;
+    if ((e = hipEventRecord(e1, st)) != hipSuccess || (e = hipEventSynchronize(e1)) != hipSuccess)
+      return hip_fail(e, "calibration event");
+    float t = 0.0f;
+    if ((e = hipEventElapsedTime(&t, e0, e1)) != hipSuccess) return hip_fail(e, "calibration");
+    if (rep > 0) best = std::min(best, t);        // the first call warms up
+  }
+  *ms = best;
+  return FFN_OK;
+}
+
+}  // namespace
+
+ffn_status calibrate_crossover(ffn_plan* p, hipStream_t st) {
+  const ffn_layer_desc& D = p->desc;
+  const int Bmax = D.max_batch;
+  void *x = nullptr, *y = nullptr, *mask = nullptr;
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  ffn_status res = FFN_OK;
+  std::vector<unsigned char> hm((size_t)Bmax * D.ffn);
+  static const float grid[] = {0.0625f, 0.125f, 0.25f, 0.5f, 0.75f, 1.0f};
+  constexpr int NG = sizeof(grid) / sizeof(grid[0]);
+  hipError_t e;
+  if ((e = hipMalloc(&x, (size_t)Bmax * D.d * 2)) != hipSuccess ||
+      (e = hipMalloc(&y, (size_t)Bmax * D.d * 4)) != hipSuccess ||
+      (e = hipMalloc(&mask, hm.size())) != hipSuccess ||
+      (e = hipMemsetAsync(x, 0, (size_t)Bmax * D.d * 2, st)) != hipSuccess ||
+      (e = hipEventCreate(&e0)) != hipSuccess || (e = hipEventCreate(&e1)) != hipSuccess) {
+    res = hip_fail(e, "calibration setup");
+  }
+  for (int k = 1; res == FFN_OK && k < 13 && (1 << k) <= Bmax; ++k) {
+    const int B = 1 << k;
+    float t_dense = 0.0f, t_sp[NG];
+    res = time_call(st, e0, e1, &t_dense, [&] {
+      return ffn_dense_forward(p, x, B, static_cast<float*>(y), nullptr, st);
+    });
+    for (int gi = 0; res == FFN_OK && gi < NG; ++gi) {
+      // the same random set for every token: union density = grid[gi]
+      uint64_t h = 0x9e3779b97f4a7c15ull * (gi + 1);
+      for (int i = 0; i < D.ffn; ++i) {
+        h ^= h >> 33;
+        h *= 0xff51afd7ed558ccdull;
+        h ^= h >> 29;
+        hm[i] = (double)(h >> 11) * (1.0 / 9007199254740992.0) < grid[gi] ? 1 : 0;
+      }
+      for (int b = 1; b < B; ++b) memcpy(&hm[(size_t)b * D.ffn], &hm[0], D.ffn);
+      if ((e = hipMemcpy(mask, hm.data(), (size_t)B * D.ffn, hipMemcpyHostToDevice)) !=
+          hipSuccess) {
+        res = hip_fail(e, "calibration mask upload");
+        break;
+      }
+      res = time_call(st, e0, e1, &t_sp[gi], [&] {
+        return ffn_sparse_forward(p, x, B, static_cast<float*>(y),
+                                  static_cast<const uint8_t*>(mask), nullptr, nullptr, nullptr,
+                                  FFN_PATH_SPARSE, st);
+      });
+    }
+    if (res != FFN_OK) break;
+    float rho = 1.0f;
+    for (int gi = 0; gi < NG; ++gi) {
+      if (t_sp[gi] >= t_dense) {
+        if (gi == 0) {
+          rho = 0.0f;
+        } else {
+          const float f = (t_dense - t_sp[gi - 1]) / std::max(t_sp[gi] - t_sp[gi - 1], 1e-6f);
+          rho = grid[gi - 1] + f * (grid[gi] - grid[gi - 1]);
+        }
+        break;
+      }
+    }
+    p->crossover_density[k] = rho;
+    // buckets above the largest measured batch inherit its value
+    for (int kk = k + 1; kk < 13; ++kk) p->crossover_density[kk] = rho;
+  }
+  if (e0) hipEventDestroy(e0);
+  if (e1) hipEventDestroy(e1);
+  if (x) hipFree(x);
+  if (y) hipFree(y);
+  if (mask) hipFree(mask);
+  return res;
+}
+
+namespace {
+
 }  // namespace
 
 extern "C" {
@@ -395,8 +496,13 @@ ffn_status ffn_sparse_plan(const ffn_layer_desc* desc, const ffn_layer_weights* 
   // more than every row, so the union is kept (crossover 1) until calibration says otherwise
   for (int k = 0; k < 13; ++k) p->crossover_density[k] = 1.0f;
   p->dense_min_batch = 2;
-  (void)stream;
-  (void)calibrate;
+  if (calibrate && batched(desc) && desc->max_batch >= 2) {
+    st = calibrate_crossover(p, static_cast<hipStream_t>(stream));
+    if (st != FFN_OK) {
+      delete p;
+      return st;
+    }
+  }
   *out = p;
   g_err[0] = 0;
   return FFN_OK;

@@ -92,6 +92,9 @@ def main():
                     help="steps whose kernel launches are timed with dispatch events")
     ap.add_argument("--cpu-tokens", type=int, default=3,
                     help="tokens the CPU oracle baseline runs per layer; 0 = skip")
+    ap.add_argument("--calibrate", type=int, default=0,
+                    help="also calibrate layer 0's plan for batches up to this size and report "
+                         "its measured crossover densities (fp16 layers)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="first run a plain device copy of this many MiB five times (a known "
                          "size against which a profiler's HBM byte counters are scaled)")
@@ -446,6 +449,16 @@ def main():
         log("oracle: %.2f s for %d token(s) x %d layer(s); GPU parity max normwise error %.2e"
             % (t_cpu, nt, L_cpu, worst))
 
+    crossover = None
+    if args.calibrate and cfg.w_dtype == "f16":
+        t_cal = time.time()
+        with torch.cuda.stream(stream):
+            cal = ffn.SparseFFN(layers[0][0], max_batch=args.calibrate, calibrate=True)
+        crossover = {str(1 << k): round(cal.crossover(1 << k), 4)
+                     for k in range(13) if (1 << k) <= args.calibrate}
+        cal.close()
+        log("calibrated crossover densities (%.1f s): %s" % (time.time() - t_cal, crossover))
+
     dtype = {"f32": "f32", "f16": "f16xf16->f32", "i4g32": "i4g32xf16->f32"}[cfg.w_dtype]
     result = {
         "metric": ("sparse-FFN decode tokens/s at 1 GPU; effective HBM GB/s of touched weights"
@@ -472,6 +485,8 @@ def main():
         "cpu_baseline": cpu,
         "parity_sample": parity,
     }
+    if crossover is not None:
+        result["crossover_density"] = crossover
     print(json.dumps(result), flush=True)
 
 

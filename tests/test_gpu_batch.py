@@ -221,3 +221,30 @@ def test_auto_follows_the_device_choice(ffn, B):
     assert torch.equal(y_a1, y_sp)
     assert normwise(y_de.cpu().numpy(), y_sp.cpu().numpy().astype(np.float64)) <= 1e-3
     m.close()
+
+
+def test_calibrated_crossover(ffn):
+    """calibrate=1 times the plan's own dense and sparse kernels and stores a crossover density
+    per batch bucket; AUTO then follows it and still gives the oracle's result."""
+    cfg = synth.small_config(d=512, ffn=2048, rank=64, act="relu", w_dtype="f16", x_dtype="f16",
+                             p_dtype="f16", density=0.1, bias_up=True)
+    host = synth.make_layer(cfg)
+    L, OL = to_device(host), oracle_layer(host)
+    m = ffn.SparseFFN(L, max_batch=128, calibrate=True)
+    rho = {B: m.crossover(B) for B in (1, 2, 8, 32, 64, 128)}
+    assert rho[1] == 1.0                          # batch 1 is never calibrated: sparse
+    assert all(0.0 <= v <= 1.0 for v in rho.values()), rho
+    B = 100
+    x = synth.make_tokens(cfg, B).cuda()
+    idx = torch.full((B, cfg.ffn), -1, dtype=torch.int32, device="cuda")
+    cnt = torch.zeros(B, dtype=torch.int32, device="cuda")
+    y = m.forward(x, idx=idx, cnt=cnt, path=ffn.FFN_PATH_AUTO)
+    torch.cuda.synchronize()
+    xh, yh, ih, ch = x.cpu().numpy(), y.cpu().numpy(), idx.cpu().numpy(), cnt.cpu().numpy()
+    for t in (0, 50, 99):
+        lt = ih[t, :ch[t]]
+        pred = oracle.predictor(OL["p1"], OL["p2"], OL["c1"], OL["c2"], xh[t], OL["tau"])
+        check_index_list(lt, pred, OL["tau"])
+        y_ref, _ = oracle.ffn(OL, xh[t], mask_from_idx(lt, cfg.ffn))
+        assert normwise(yh[t], y_ref) <= TOL["f16"]
+    m.close()
