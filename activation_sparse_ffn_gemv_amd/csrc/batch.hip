@@ -249,10 +249,20 @@ __global__ __launch_bounds__(1024) void k_dchoice(const uint32_t* __restrict__ b
 }
 
 // Rows of 32 union neurons (ranks [32 b, 32 b + 32)): u, g on the MFMA units, then h.
+// The rows stream through LDS in stages of UG_KC 16-byte chunks (a wave's load instruction
+// covers two rows' 512 contiguous bytes), double-buffered; the waves split each stage's K
+// between them for the MFMAs, and their 32x32 sums are added in wave order at the end.
+constexpr int UG_KC = 32;                 // chunks per row per stage (256 k)
+constexpr int UG_LD = UG_KC + 1;          // padded LDS row
+
+template <bool GATE>
 __global__ __launch_bounds__(BT) void k_bug(BatchArgs a) {
+  constexpr int NMAT = GATE ? 2 : 1;
+  constexpr int LPT = 32 * UG_KC / BT;    // chunk loads per thread and matrix per stage
   __shared__ int s_wsum[BT / WAVE];
   __shared__ int s_nid[32];
   __shared__ float red[3 * 16 * WAVE];
+  __shared__ u32x4 s_w[2][NMAT][32 * UG_LD];
   if (a.run_if && *a.run_if != a.run_want) return;
   const int tid = threadIdx.x, lane = tid & (WAVE - 1), wave = tid / WAVE;
   const int W = a.ffn / 32;
@@ -304,37 +314,82 @@ __global__ __launch_bounds__(BT) void k_bug(BatchArgs a) {
   }
   __syncthreads();
 
-  // 2. U = X W_up^T and G = X W_gate^T for the 32 neurons, K split over the waves
+  // 2. U = X W_up^T and G = X W_gate^T for the 32 neurons
   const int row = lane & 31, g = lane >> 5;
   const int nid = s_nid[row];
-  const size_t rowoff = (size_t)max(nid, 0) * a.d * 2;
-  const char* up = static_cast<const char*>(a.w_up) + rowoff;
-  const char* gp = static_cast<const char*>(a.has_gate ? a.w_gate : a.w_up) + rowoff;
+  const int nchk = a.d / 8;
+  const int nstage = (nchk + UG_KC - 1) / UG_KC;
+  // cooperative row loads: element e = tid + BT * i -> (row e / UG_KC, chunk e % UG_KC)
+  const char* wsrc[2] = {static_cast<const char*>(a.w_up),
+                         static_cast<const char*>(GATE ? a.w_gate : a.w_up)};
+  size_t lrow_off[LPT];
+  int lch[LPT];
+#pragma unroll
+  for (int i = 0; i < LPT; ++i) {
+    const int e = tid + BT * i;
+    lrow_off[i] = (size_t)max(s_nid[e / UG_KC], 0) * nchk * 16;
+    lch[i] = e % UG_KC;
+  }
+  auto load_w = [&](int st, u32x4 (&r)[NMAT][LPT]) {
+#pragma unroll
+    for (int mt = 0; mt < NMAT; ++mt)
+#pragma unroll
+      for (int i = 0; i < LPT; ++i) {
+        const int c = st * UG_KC + lch[i];
+        const u32x4 t = ld16(wsrc[mt] + lrow_off[i] + (size_t)min(c, nchk - 1) * 16);
+        r[mt][i] = c < nchk ? t : u32x4{0u, 0u, 0u, 0u};
+      }
+  };
+  auto store_w = [&](int buf, const u32x4 (&r)[NMAT][LPT]) {
+#pragma unroll
+    for (int mt = 0; mt < NMAT; ++mt)
+#pragma unroll
+      for (int i = 0; i < LPT; ++i) {
+        const int e = tid + BT * i;
+        s_w[buf][mt][(e / UG_KC) * UG_LD + e % UG_KC] = r[mt][i];
+      }
+  };
+  // token operand straight from global: wave w takes the stage's 16-k steps 4w .. 4w+3
+  constexpr int SPW = UG_KC / 2 / 4;                    // steps per wave and stage
   const char* xr = static_cast<const char*>(a.x) + (size_t)min(row, a.B - 1) * a.d * 2;
   const bool xok = row < a.B;
-  const int nchk = a.d / 8, nsteps = (nchk + 1) / 2;
+  auto load_x = [&](int st, u32x4 (&xv)[SPW]) {
+#pragma unroll
+    for (int j = 0; j < SPW; ++j) {
+      const int c = st * UG_KC + 2 * (wave * SPW + j) + g;
+      const u32x4 t = ld16(xr + (size_t)min(c, nchk - 1) * 16);
+      xv[j] = (xok && c < nchk) ? t : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+
   f32x16 au = {}, ag = {};
-  for (int s0 = wave; s0 < nsteps; s0 += 4 * GRP) {
-    u32x4 xv[GRP], uv[GRP], gv[GRP];
-#pragma unroll
-    for (int j = 0; j < GRP; ++j) {
-      const int c = 2 * (s0 + 4 * j) + g;
-      const int cc = min(c, nchk - 1);
-      const bool ok = s0 + 4 * j < nsteps && c < nchk;
-      const u32x4 xl = ld16(xr + (size_t)cc * 16);
-      uv[j] = ld16(up + (size_t)cc * 16);
-      gv[j] = a.has_gate ? ld16(gp + (size_t)cc * 16) : u32x4{0u, 0u, 0u, 0u};
-      xv[j] = (ok && xok) ? xl : u32x4{0u, 0u, 0u, 0u};
+  u32x4 wr[NMAT][LPT], xv[SPW], xn[SPW];
+  load_w(0, wr);
+  load_x(0, xv);
+  store_w(0, wr);
+  __syncthreads();
+  for (int st = 0; st < nstage; ++st) {
+    const int buf = st & 1;
+    const bool more = st + 1 < nstage;
+    if (more) {
+      load_w(st + 1, wr);
+      load_x(st + 1, xn);
     }
-    issue_fence();
 #pragma unroll
-    for (int j = 0; j < GRP; ++j) {
-      au = mma16(xv[j], uv[j], au);
-      if (a.has_gate) ag = mma16(xv[j], gv[j], ag);
+    for (int j = 0; j < SPW; ++j) {
+      const int idx = row * UG_LD + 2 * (wave * SPW + j) + g;
+      au = mma16(xv[j], s_w[buf][0][idx], au);
+      if constexpr (GATE) ag = mma16(xv[j], s_w[buf][NMAT - 1][idx], ag);
     }
+    if (more) {
+      store_w(buf ^ 1, wr);
+#pragma unroll
+      for (int j = 0; j < SPW; ++j) xv[j] = xn[j];
+    }
+    __syncthreads();
   }
   au = wg_sum4(au, red);
-  if (a.has_gate) ag = wg_sum4(ag, red);
+  if constexpr (GATE) ag = wg_sum4(ag, red);
 
   // 3. h per (token, neuron), masked by the token's own set; H column = union rank
   if (wave == 0) {
@@ -345,7 +400,7 @@ __global__ __launch_bounds__(BT) void k_bug(BatchArgs a) {
       const int m = acc_row(i, lane);
       const float u = au[i] + bu;
       float h;
-      if (a.act == FFN_ACT_RELU) {
+      if constexpr (!GATE) {
         h = fmaxf(u, 0.0f);
       } else {
         const float gg = fmaxf(ag[i] + bg, 0.0f);
@@ -504,10 +559,17 @@ hipError_t launch_batch_rows(const BatchArgs& a, int choose_path, hipStream_t st
                              hipEvent_t (*ev)[2]) {
   const int W = a.ffn / 32;
   if (choose_path) hipLaunchKernelGGL(k_bpath, dim3(1), dim3(1024), 0, st, a);
-  if (ev && ev[0][0])
-    hipExtLaunchKernelGGL(k_bug, dim3(W), dim3(BT), 0, st, ev[0][0], ev[0][1], 0, a);
-  else
-    hipLaunchKernelGGL(k_bug, dim3(W), dim3(BT), 0, st, a);
+  if (a.has_gate) {
+    if (ev && ev[0][0])
+      hipExtLaunchKernelGGL(k_bug<true>, dim3(W), dim3(BT), 0, st, ev[0][0], ev[0][1], 0, a);
+    else
+      hipLaunchKernelGGL(k_bug<true>, dim3(W), dim3(BT), 0, st, a);
+  } else {
+    if (ev && ev[0][0])
+      hipExtLaunchKernelGGL(k_bug<false>, dim3(W), dim3(BT), 0, st, ev[0][0], ev[0][1], 0, a);
+    else
+      hipLaunchKernelGGL(k_bug<false>, dim3(W), dim3(BT), 0, st, a);
+  }
   const dim3 gd((a.d + DN_COLS - 1) / DN_COLS, a.S);
   if (ev && ev[1][0])
     hipExtLaunchKernelGGL(k_bdown, gd, dim3(BT), 0, st, ev[1][0], ev[1][1], 0, a);
