@@ -323,7 +323,8 @@ __global__ __launch_bounds__(256) void k_dlists(DenseArgs a) {
 // ---------------------------------------------------------------------------------------------
 int dense_ks(int M, int d, int ffn) {
   const int tiles = ((M + DD_M - 1) / DD_M) * ((d + DD_N - 1) / DD_N);
-  const int ks = std::max(1, std::min({8, (256 + tiles - 1) / tiles, ffn / DD_K}));
+  // two workgroups per CU (the kernel's occupancy): split ffn until the grid reaches 512
+  const int ks = std::max(1, std::min({8, (512 + tiles - 1) / tiles, ffn / DD_K}));
   return ks;
 }
 
