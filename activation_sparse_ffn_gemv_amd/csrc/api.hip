@@ -218,15 +218,16 @@ BatchArgs batch_bufs(char* ws, const ffn_plan* p) {
 }
 
 
-// Workspace of a mixture: the expert pipeline's scratch (the layout of one expert), then the
-// per-slot expert records [max_batch][top_k].
+// Workspace of a mixture: one decode scratch (z, bitmap, |A|, partials: the front of an
+// expert's layout) per expert slot, then the per-slot expert records [max_batch][top_k].
 struct MoeLayout {
-  size_t off_slots, total;
+  size_t slot_stride, off_slots, total;
 };
 
 MoeLayout moe_layout(const ffn_plan* e0, int top_k) {
   MoeLayout L{};
-  L.off_slots = layout_for(&e0->desc).total;
+  L.slot_stride = round_up(layout_for(&e0->desc).off_union, 256);
+  L.off_slots = L.slot_stride * top_k;
   L.total = round_up(L.off_slots + (size_t)e0->desc.max_batch * top_k * sizeof(ExpertW), 256);
   return L;
 }
@@ -262,22 +263,25 @@ TokenBufs token_bufs(char* ws, const ffn_plan* p) {
 }
 
 // The launches of one token: active set (predictor or caller mask) -> balanced gather -> reduce.
-// slot != nullptr: the expert is chosen on the device and the kernels take its weights from the
-// slot record (p then only supplies shapes and the threshold); accumulate adds the weighted
-// result to y.
+// slot != nullptr: the experts are chosen on the device; the kernels take their weights from
+// the nslot consecutive slot records (p then only supplies shapes and the threshold) and run
+// the slots side by side, slot k's scratch at slot_stride bytes past slot k-1's; the reduce
+// writes the routing-weighted sum of the slots.
 ffn_status enqueue_token(const ffn_plan* p, const TokenBufs& wb, const void* xb,
                          const uint8_t* maskb, float* yb, int* idxb, int* cntb, float* scoresb,
-                         const ExpertW* slot, int accumulate, hipStream_t st,
+                         const ExpertW* slot, int nslot, size_t slot_stride, hipStream_t st,
                          bool all_neurons = false) {
   const ffn_layer_desc& D = p->desc;
   const int wk = D.w_dtype == FFN_F32 ? WK_F32 : D.w_dtype == FFN_F16 ? WK_F16 : WK_I4;
+  const int es = (int)(slot_stride / 4);      // the same stride in 4-byte elements
   hipError_t e;
   if (maskb || all_neurons) {
     e = launch_mask_bits(maskb, wb.bits, D.ffn / 32, st);
     if (e != hipSuccess) return hip_fail(e, "mask launch");
   } else {
     e = launch_pred_z(D.p_dtype == FFN_F16, p->cpl_p, p->w.p1, p->w.c1, xb, wb.z, D.d, D.rank,
-                      slot, st, p->ev[FFN_STAGE_PRED_Z][0], p->ev[FFN_STAGE_PRED_Z][1]);
+                      slot, nslot, es, st, p->ev[FFN_STAGE_PRED_Z][0],
+                      p->ev[FFN_STAGE_PRED_Z][1]);
     if (e != hipSuccess) return hip_fail(e, "predictor stage 1 launch");
     PredArgs pa{};
     pa.p2 = p->w.p2;
@@ -289,6 +293,9 @@ ffn_status enqueue_token(const ffn_plan* p, const TokenBufs& wb, const void* xb,
     pa.rank = D.rank;
     pa.thr = p->thr;
     pa.slot = slot;
+    pa.nslot = nslot;
+    pa.zstride = es;
+    pa.bstride = es;
     e = launch_pred_s(D.p_dtype == FFN_F16, pa, st, p->ev[FFN_STAGE_PRED_S][0],
                       p->ev[FFN_STAGE_PRED_S][1]);
     if (e != hipSuccess) return hip_fail(e, "predictor stage 2 launch");
@@ -311,6 +318,10 @@ ffn_status enqueue_token(const ffn_plan* p, const TokenBufs& wb, const void* xb,
   ga.act = D.act;
   ga.has_gate = D.act != FFN_ACT_RELU;
   ga.slot = slot;
+  ga.nslot = nslot;
+  ga.bstride = es;
+  ga.cstride = es;
+  ga.pstride = (size_t)es;
   e = launch_gather(wk, ga, st, p->ev[FFN_STAGE_GATHER][0], p->ev[FFN_STAGE_GATHER][1]);
   if (e != hipSuccess) return hip_fail(e, "gather launch");
   ReduceArgs ra{};
@@ -325,7 +336,9 @@ ffn_status enqueue_token(const ffn_plan* p, const TokenBufs& wb, const void* xb,
   ra.ffn = D.ffn;
   ra.n_part = gather_blocks();
   ra.slot = slot;
-  ra.accumulate = accumulate;
+  ra.nslot = nslot;
+  ra.cstride = es;
+  ra.pstride = (size_t)es;
   e = launch_reduce(ra, st, p->ev[FFN_STAGE_REDUCE][0], p->ev[FFN_STAGE_REDUCE][1]);
   if (e != hipSuccess) return hip_fail(e, "reduce launch");
   return FFN_OK;
@@ -637,7 +650,7 @@ ffn_status ffn_sparse_forward(ffn_plan* p, const void* x, int32_t B, float* y,
     ffn_status s = enqueue_token(p, wb, static_cast<const char*>(x) + b * xbytes,
                                  mask ? mask + (size_t)b * D.ffn : nullptr, y + (size_t)b * D.d,
                                  idx ? idx + (size_t)b * D.ffn : nullptr, cnt ? cnt + b : nullptr,
-                                 scores ? scores + (size_t)b * D.ffn : nullptr, nullptr, 0, st);
+                                 scores ? scores + (size_t)b * D.ffn : nullptr, nullptr, 1, 0, st);
     if (s != FFN_OK) return s;
   }
   g_err[0] = 0;
@@ -674,7 +687,7 @@ ffn_status ffn_dense_forward(ffn_plan* p, const void* x, int32_t B, float* y,
     for (int b = 0; b < B; ++b) {
       ffn_status s = enqueue_token(p, wb, static_cast<const char*>(x) + b * xbytes,
                                    mask ? mask + (size_t)b * D.ffn : nullptr, y + (size_t)b * D.d,
-                                   nullptr, nullptr, nullptr, nullptr, 0, st, true);
+                                   nullptr, nullptr, nullptr, nullptr, 1, 0, st, true);
       if (s != FFN_OK) return s;
     }
   }
@@ -814,13 +827,13 @@ ffn_status ffn_moe_forward(ffn_moe* m, const void* x, int32_t B, float* y, int32
   if (e != hipSuccess) return hip_fail(e, "router launch");
   const size_t xbytes = (size_t)D.d * (D.x_dtype == FFN_F32 ? 4 : 2);
   const TokenBufs wb = token_bufs(m->ws, p);
-  for (int b = 0; b < B; ++b)
-    for (int k = 0; k < m->top_k; ++k) {
-      ffn_status s = enqueue_token(p, wb, static_cast<const char*>(x) + b * xbytes, nullptr,
-                                   y + (size_t)b * D.d, nullptr, nullptr, nullptr,
-                                   slots + (size_t)b * m->top_k + k, k > 0, st);
-      if (s != FFN_OK) return s;
-    }
+  for (int b = 0; b < B; ++b) {
+    // the token's top_k experts run side by side, one launch per stage
+    ffn_status s = enqueue_token(p, wb, static_cast<const char*>(x) + b * xbytes, nullptr,
+                                 y + (size_t)b * D.d, nullptr, nullptr, nullptr,
+                                 slots + (size_t)b * m->top_k, m->top_k, m->L.slot_stride, st);
+    if (s != FFN_OK) return s;
+  }
   g_err[0] = 0;
   return FFN_OK;
 }

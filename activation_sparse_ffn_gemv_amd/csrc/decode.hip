@@ -91,9 +91,11 @@ __global__ __launch_bounds__(64) void k_pred_z(const void* __restrict__ p1,
                                                const float* __restrict__ c1,
                                                const void* __restrict__ x,
                                                float* __restrict__ z, int d, int rank,
-                                               const ExpertW* __restrict__ slot) {
+                                               const ExpertW* __restrict__ slot, int zstride) {
   FFN_TS(0, 0);
   if (slot) {
+    slot += blockIdx.y;                         // expert slots side by side
+    z += (size_t)blockIdx.y * zstride;
     p1 = slot->p1;
     c1 = slot->c1;
   }
@@ -134,6 +136,9 @@ __global__ __launch_bounds__(PS_THREADS) void k_pred_s(PredArgs a) {
   const int i0 = blockIdx.x * 32;
   FFN_TS(1, 0);
   if (a.slot) {
+    a.slot += blockIdx.y;                       // expert slots side by side
+    a.z += (size_t)blockIdx.y * a.zstride;
+    a.bitmap += (size_t)blockIdx.y * a.bstride;
     a.p2 = a.slot->p2;
     a.c2 = a.slot->c2;
   }
@@ -262,6 +267,10 @@ __global__ __launch_bounds__(GA_THREADS) void k_gather(GatherArgs a) {
   const int nch = a.d / EPC;
   FFN_TS(1, 0);
   if (a.slot) {
+    a.slot += blockIdx.y;                       // expert slots side by side
+    a.bitmap += (size_t)blockIdx.y * a.bstride;
+    a.cnt += (size_t)blockIdx.y * a.cstride;
+    a.part += (size_t)blockIdx.y * a.pstride;
     const ExpertW& e = *a.slot;
     a.w_up = e.w_up;
     a.w_gate = e.w_gate;
@@ -523,40 +532,42 @@ __global__ __launch_bounds__(RD_THREADS) void k_reduce(ReduceArgs a) {
   const int q = threadIdx.x % RD_Q;          // float4 column within the tile
   const int g = threadIdx.x / RD_Q;          // partials g, g + RD_G, ...
   const int tile = blockIdx.x;
-  FFN_TS(2, 0);
-  const int total = *a.cnt;
-  const float* blk = a.part + (size_t)tile * GA_BLOCKS * RD_TW;
-  f32x4 v[RD_UNROLL];
-  bool on[RD_UNROLL];
-#pragma unroll
-  for (int u = 0; u < RD_UNROLL; ++u) {
-    const int c = g + u * RD_G;
-    // partial c exists iff gather workgroup c owned at least one rank
-    on[u] = ((long long)total * (c + 1)) / GA_BLOCKS > ((long long)total * c) / GA_BLOCKS;
-    v[u] = *reinterpret_cast<const f32x4*>(blk + (size_t)c * RD_TW + q * 4);
-  }
-  issue_fence();
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int u = 0; u < RD_UNROLL; ++u)
-    if (on[u]) acc += v[u];
-  s[g][q] = acc;
-  __syncthreads();
   const int j = tile * RD_TW + threadIdx.x * 4;
-  if (threadIdx.x < RD_Q && j < a.d) {
-    const float* b_down = a.slot ? a.slot->b_down : a.b_down;
-    f32x4 t = s[0][threadIdx.x];
-#pragma unroll 8
-    for (int k = 1; k < RD_G; ++k) t += s[k][threadIdx.x];
-    if (b_down) t += *reinterpret_cast<const f32x4*>(b_down + j);
-    if (a.slot) {
-      // expert slot of a mixture: weighted, summed over the slots in slot order
-      const float wgt = a.slot->wgt;
-      t *= wgt;
-      if (a.accumulate) t += *reinterpret_cast<const f32x4*>(a.y + j);
+  FFN_TS(2, 0);
+  const int nslot = a.slot ? a.nslot : 1;
+  f32x4 out = {0.f, 0.f, 0.f, 0.f};
+  for (int k = 0; k < nslot; ++k) {
+    const int total = a.cnt[(size_t)k * a.cstride];
+    const float* blk = a.part + (size_t)k * a.pstride + (size_t)tile * GA_BLOCKS * RD_TW;
+    f32x4 v[RD_UNROLL];
+    bool on[RD_UNROLL];
+#pragma unroll
+    for (int u = 0; u < RD_UNROLL; ++u) {
+      const int c = g + u * RD_G;
+      // partial c exists iff gather workgroup c owned at least one rank
+      on[u] = ((long long)total * (c + 1)) / GA_BLOCKS > ((long long)total * c) / GA_BLOCKS;
+      v[u] = *reinterpret_cast<const f32x4*>(blk + (size_t)c * RD_TW + q * 4);
     }
-    *reinterpret_cast<f32x4*>(a.y + j) = t;
+    issue_fence();
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < RD_UNROLL; ++u)
+      if (on[u]) acc += v[u];
+    __syncthreads();                         // s reused across slots
+    s[g][q] = acc;
+    __syncthreads();
+    if (threadIdx.x < RD_Q && j < a.d) {
+      const float* b_down = a.slot ? a.slot[k].b_down : a.b_down;
+      f32x4 t = s[0][threadIdx.x];
+#pragma unroll 8
+      for (int kk = 1; kk < RD_G; ++kk) t += s[kk][threadIdx.x];
+      if (b_down) t += *reinterpret_cast<const f32x4*>(b_down + j);
+      // expert slots of a mixture: weighted, summed in slot order
+      if (a.slot) out += a.slot[k].wgt * t;
+      else out = t;
+    }
   }
+  if (threadIdx.x < RD_Q && j < a.d) *reinterpret_cast<f32x4*>(a.y + j) = out;
   if (blockIdx.x == 0 && (a.idx_out || a.cnt_out))
     write_index_list<RD_THREADS>(a.bitmap, a.ffn / 32, a.idx_out, a.cnt_out);
   FFN_TS(2, 5);
@@ -573,26 +584,27 @@ __global__ __launch_bounds__(RD_THREADS) void k_reduce(ReduceArgs a) {
 
 template <int PK, int CPL>
 static hipError_t launch_pred_z_t(const void* p1, const float* c1, const void* x, float* z,
-                                  int d, int rank, const ExpertW* slot, hipStream_t st,
-                                  hipEvent_t ev0, hipEvent_t ev1) {
+                                  int d, int rank, const ExpertW* slot, int nslot, int zstride,
+                                  hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
+  const dim3 grid(rank, slot ? nslot : 1);
   if (ev0 && ev1)
-    hipExtLaunchKernelGGL((k_pred_z<PK, CPL>), dim3(rank), dim3(WAVE), 0, st, ev0, ev1, 0, p1,
-                          c1, x, z, d, rank, slot);
+    hipExtLaunchKernelGGL((k_pred_z<PK, CPL>), grid, dim3(WAVE), 0, st, ev0, ev1, 0, p1, c1, x,
+                          z, d, rank, slot, zstride);
   else
-    hipLaunchKernelGGL((k_pred_z<PK, CPL>), dim3(rank), dim3(WAVE), 0, st, p1, c1, x, z, d,
-                       rank, slot);
+    hipLaunchKernelGGL((k_pred_z<PK, CPL>), grid, dim3(WAVE), 0, st, p1, c1, x, z, d, rank, slot,
+                       zstride);
   return hipGetLastError();
 }
 
 hipError_t launch_pred_z(int p_f16, int cpl, const void* p1, const float* c1, const void* x,
-                         float* z, int d, int rank, const ExpertW* slot, hipStream_t st,
-                         hipEvent_t ev0, hipEvent_t ev1) {
+                         float* z, int d, int rank, const ExpertW* slot, int nslot, int zstride,
+                         hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
   if (p_f16) {
-#define F16Z(c) launch_pred_z_t<WK_F16, c>(p1, c1, x, z, d, rank, slot, st, ev0, ev1)
+#define F16Z(c) launch_pred_z_t<WK_F16, c>(p1, c1, x, z, d, rank, slot, nslot, zstride, st, ev0, ev1)
     CPL_SWITCH(cpl, F16Z)
 #undef F16Z
   } else {
-#define F32Z(c) launch_pred_z_t<WK_F32, c>(p1, c1, x, z, d, rank, slot, st, ev0, ev1)
+#define F32Z(c) launch_pred_z_t<WK_F32, c>(p1, c1, x, z, d, rank, slot, nslot, zstride, st, ev0, ev1)
     CPL_SWITCH(cpl, F32Z)
 #undef F32Z
   }
@@ -610,10 +622,11 @@ template <int PK, int CPR>
 static hipError_t launch_pred_s_t(const PredArgs& a, hipStream_t st, hipEvent_t ev0,
                                   hipEvent_t ev1) {
   if (ev0 && ev1)
-    hipExtLaunchKernelGGL((k_pred_s<PK, CPR>), dim3(a.ffn / 32), dim3(PS_THREADS), 0, st, ev0,
-                          ev1, 0, a);
+    hipExtLaunchKernelGGL((k_pred_s<PK, CPR>), dim3(a.ffn / 32, a.slot ? a.nslot : 1),
+                          dim3(PS_THREADS), 0, st, ev0, ev1, 0, a);
   else
-    hipLaunchKernelGGL((k_pred_s<PK, CPR>), dim3(a.ffn / 32), dim3(PS_THREADS), 0, st, a);
+    hipLaunchKernelGGL((k_pred_s<PK, CPR>), dim3(a.ffn / 32, a.slot ? a.nslot : 1),
+                       dim3(PS_THREADS), 0, st, a);
   return hipGetLastError();
 }
 
@@ -661,10 +674,11 @@ static hipError_t launch_gather_t(const GatherArgs& a, hipStream_t st, hipEvent_
   const size_t lds = SLOTS > 1 ? (size_t)(SLOTS / 2) * (GA_THREADS / SLOTS) * CPT *
                                      Kind<WK>::EPC * sizeof(float) : 0;
   if (ev0 && ev1)
-    hipExtLaunchKernelGGL((k_gather<WK, CPT, SLOTS>), dim3(GA_BLOCKS), dim3(GA_THREADS), lds, st,
-                          ev0, ev1, 0, a);
+    hipExtLaunchKernelGGL((k_gather<WK, CPT, SLOTS>), dim3(GA_BLOCKS, a.slot ? a.nslot : 1),
+                          dim3(GA_THREADS), lds, st, ev0, ev1, 0, a);
   else
-    hipLaunchKernelGGL((k_gather<WK, CPT, SLOTS>), dim3(GA_BLOCKS), dim3(GA_THREADS), lds, st, a);
+    hipLaunchKernelGGL((k_gather<WK, CPT, SLOTS>), dim3(GA_BLOCKS, a.slot ? a.nslot : 1),
+                       dim3(GA_THREADS), lds, st, a);
   return hipGetLastError();
 }
 

@@ -46,6 +46,8 @@ struct PredArgs {
   int ffn, rank;
   float thr;                  // logit(threshold)
   const ExpertW* slot;        // device-chosen expert (p2, c2 from it), or nullptr
+  int nslot;                  // expert slots run side by side (grid.y); slot k uses slot + k,
+  int zstride, bstride;       //   z + k*zstride, bitmap + k*bstride (elements)
 };
 
 // Balanced gather of the active rows (one token).
@@ -64,6 +66,9 @@ struct GatherArgs {
   int* cnt;                   // [1] out: |A|
   int d, ffn, act, has_gate;
   const ExpertW* slot;        // device-chosen expert (rows, scales, biases from it), or nullptr
+  int nslot;                  // expert slots side by side (grid.y): slot + k, bitmap + k*bstride,
+  int bstride, cstride;       //   cnt + k*cstride, part + k*pstride (elements)
+  size_t pstride;
 };
 
 // Sum of the gather partials (one token).
@@ -76,13 +81,15 @@ struct ReduceArgs {
   int* idx_out;               // [ffn] ascending active list, or nullptr
   int* cnt_out;               // [1], or nullptr
   int d, ffn, n_part;
-  const ExpertW* slot;        // device-chosen expert: b_down and the routing weight, or nullptr
-  int accumulate;             // y += wgt * result (later expert slots) instead of y = ...
+  const ExpertW* slot;        // device-chosen experts: b_down and the routing weights, or nullptr
+  int nslot;                  // y = sum over the nslot slots (in order) of wgt_k * result_k;
+  int cstride;                //   slot k's partials at part + k*pstride, its |A| at cnt + k*cstride
+  size_t pstride;
 };
 
 hipError_t launch_pred_z(int p_f16, int cpl, const void* p1, const float* c1, const void* x,
-                         float* z, int d, int rank, const ExpertW* slot, hipStream_t st,
-                         hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
+                         float* z, int d, int rank, const ExpertW* slot, int nslot, int zstride,
+                         hipStream_t st, hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
 int pred_s_cpr(int p_f16, int rank);
 hipError_t launch_pred_s(int p_f16, const PredArgs& a, hipStream_t st, hipEvent_t ev0 = nullptr,
                          hipEvent_t ev1 = nullptr);

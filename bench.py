@@ -316,11 +316,11 @@ def main():
             per_call = touched[:, :S].sum() / (L * S)
             k = cfg.top_k if moe else 1
             if sname == "pred_z":
-                nb = pz
+                nb = pz * k                                          # the slots run side by side
             elif sname == "pred_s":
-                nb = ps
+                nb = ps * k
             elif sname == "gather":
-                nb = (per_call - router_b - k * (pz + ps)) / k       # one expert slot's rows
+                nb = per_call - router_b - k * (pz + ps)             # all expert slots' rows
             elif sname == "reduce":
                 nb = 0.0
             else:

@@ -144,7 +144,8 @@ def test_moe_validation_before_any_gpu_call():
     odd = _fake_plan(rank=128)
     try:
         n = ffn.ffn_moe_workspace_size(3, 2, e[0])
-        assert n >= ffn.ffn_workspace_size(_desc()) and n % 256 == 0
+        assert n > 0 and n % 256 == 0
+        assert ffn.ffn_moe_workspace_size(3, 1, e[0]) < n      # one decode scratch per slot
         for E, K in [(0, 1), (17, 2), (3, 0), (3, 4), (8, 5)]:
             with pytest.raises(ffn.FFNError) as ex:
                 ffn.ffn_moe_workspace_size(E, K, e[0])
