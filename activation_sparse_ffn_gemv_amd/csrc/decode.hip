@@ -466,28 +466,34 @@ __global__ __launch_bounds__(GA_THREADS) void k_gather(GatherArgs a) {
       __syncthreads();                                       // s_red / s_h reused
     }
   }
+  FFN_TS(1, 4);
   if (r1 > r0) {
     if constexpr (SLOTS > 1) {
-      // sum the slots' accumulators: halve the live slots through LDS until slot 0 holds all
-      extern __shared__ __align__(16) float s_acc[];         // (SLOTS/2) * TPR * CPT * EPC
+      // sum the slots' accumulators: slots 1.. park theirs in LDS (16-byte vectors, consecutive
+      // threads at consecutive addresses), slot 0 adds them in slot order
+      extern __shared__ __align__(16) f32x4 s_acc[];         // [SLOTS-1][CPT][EPC/4][TPR]
+      if (slot > 0) {
 #pragma unroll
-      for (int half = SLOTS / 2; half >= 1; half /= 2) {
-        if (slot >= half && slot < 2 * half) {
+        for (int k = 0; k < CPT; ++k)
+#pragma unroll
+          for (int e = 0; e < EPC; e += 4)
+            s_acc[(((slot - 1) * CPT + k) * (EPC / 4) + e / 4) * TPR + ct] =
+                f32x4{acc[k][e], acc[k][e + 1], acc[k][e + 2], acc[k][e + 3]};
+      }
+      __syncthreads();
+      if (slot == 0) {
+#pragma unroll
+        for (int o = 1; o < SLOTS; ++o)
 #pragma unroll
           for (int k = 0; k < CPT; ++k)
 #pragma unroll
-            for (int e = 0; e < EPC; ++e)
-              s_acc[(((slot - half) * CPT + k) * EPC + e) * TPR + ct] = acc[k][e];
-        }
-        __syncthreads();
-        if (slot < half) {
-#pragma unroll
-          for (int k = 0; k < CPT; ++k)
-#pragma unroll
-            for (int e = 0; e < EPC; ++e)
-              acc[k][e] += s_acc[((slot * CPT + k) * EPC + e) * TPR + ct];
-        }
-        __syncthreads();
+            for (int e = 0; e < EPC; e += 4) {
+              const f32x4 t = s_acc[(((o - 1) * CPT + k) * (EPC / 4) + e / 4) * TPR + ct];
+              acc[k][e] += t.x;
+              acc[k][e + 1] += t.y;
+              acc[k][e + 2] += t.z;
+              acc[k][e + 3] += t.w;
+            }
       }
     }
     // partial of y, tile-major: part[col / RD_TW][workgroup][col % RD_TW], so that the reduce
@@ -671,7 +677,7 @@ template <int WK, int CPT, int SLOTS>
 static hipError_t launch_gather_t(const GatherArgs& a, hipStream_t st, hipEvent_t ev0,
                                   hipEvent_t ev1) {
   // LDS for the slots' accumulator sum (dynamic: only multi-slot variants use it)
-  const size_t lds = SLOTS > 1 ? (size_t)(SLOTS / 2) * (GA_THREADS / SLOTS) * CPT *
+  const size_t lds = SLOTS > 1 ? (size_t)(SLOTS - 1) * (GA_THREADS / SLOTS) * CPT *
                                      Kind<WK>::EPC * sizeof(float) : 0;
   if (ev0 && ev1)
     hipExtLaunchKernelGGL((k_gather<WK, CPT, SLOTS>), dim3(GA_BLOCKS, a.slot ? a.nslot : 1),
