@@ -41,10 +41,6 @@ __device__ __forceinline__ int acc_row(int i, int lane) {
 }
 
 constexpr int DT = 256;            // threads per workgroup: 4 waves
-constexpr int DU_M = 128;          // k_dup: tokens per tile (32 per wave)
-constexpr int DU_N = 128;          // k_dup: neurons per tile (4 MFMA blocks)
-constexpr int DU_KC = 4;           // k_dup: 16-byte chunks (8 k) per row per stage: K = 32
-constexpr int DU_LD = DU_KC + 1;   // padded LDS row (chunks)
 constexpr int DD_M = 128;          // k_ddown: tokens per tile
 constexpr int DD_N = 256;          // k_ddown: columns per tile (8 MFMA blocks of 32 x 8)
 constexpr int DD_K = 32;           // k_ddown: ffn rows per stage
@@ -59,119 +55,150 @@ __device__ __forceinline__ int xcd_tile(int total) {
 
 }  // namespace
 
+// k_dup: 256 tokens x 256 neurons (ReLU) or 256 x 128 neurons with their gate rows per
+// workgroup of 8 waves; both operands staged through LDS per K stage of 32, double-buffered, with
+// the global loads of the next stage in flight during the current one's MFMAs.  Wave w owns
+// tokens 64 (w / 2) .. +63 and half of the tile's neurons (w % 2).
+constexpr int UP_T = 512;                  // threads
+constexpr int UP_M = 256;                  // tokens per tile
+constexpr int UP_KC = 4;                   // 16-byte chunks per row per stage (K = 32)
+constexpr int UP_LD = UP_KC + 1;           // padded LDS row
+
 template <bool GATE>
-__global__ __launch_bounds__(DT) void k_dup(DenseArgs a) {
+__global__ __launch_bounds__(UP_T) void k_dup(DenseArgs a) {
   constexpr int NMAT = GATE ? 2 : 1;
-  __shared__ u32x4 s_b[2][NMAT][DU_N * DU_LD];       // [buffer][up, gate][row * DU_LD + chunk]
+  constexpr int UP_N = GATE ? 128 : 256;   // neurons per tile
+  constexpr int BROWS = UP_N * NMAT;       // weight rows per stage (up rows, then gate rows)
+  constexpr int NSUB = UP_N / 2 / 32;      // 32-neuron MFMA blocks per wave
+  constexpr int LA = UP_M * UP_KC / UP_T;  // A chunk loads per thread and stage (2)
+  constexpr int LB = BROWS * UP_KC / UP_T; // B chunk loads per thread and stage (2)
+  __shared__ u32x4 sA[2][UP_M * UP_LD];
+  __shared__ u32x4 sB[2][BROWS * UP_LD];
   if (a.run_if && *a.run_if != a.run_want) return;
-  const int nb_m = (a.M + DU_M - 1) / DU_M, nb_n = (a.ffn + DU_N - 1) / DU_N;
+  const int nb_m = (a.M + UP_M - 1) / UP_M, nb_n = (a.ffn + UP_N - 1) / UP_N;
   const int tile = xcd_tile(nb_m * nb_n);
   if (tile >= nb_m * nb_n) return;
-  const int m0 = (tile % nb_m) * DU_M, n0 = (tile / nb_m) * DU_N;
+  const int m0 = (tile % nb_m) * UP_M, n0 = (tile / nb_m) * UP_N;
   const int tid = threadIdx.x, lane = tid & (WAVE - 1), wave = tid / WAVE;
   const int r32 = lane & 31, g = lane >> 5;
+  const int wm = wave >> 1, wn = wave & 1;
   const int nchk = a.d / 8;
 
-  // token row of this lane (A operand), clamped; rows past M read zeros
-  const int am = m0 + wave * 32 + r32;
-  const bool aok = am < a.M;
-  const char* arow = static_cast<const char*>(a.x) + (size_t)min(am, a.M - 1) * a.d * 2;
-  // weight tile loads: 128 rows x 4 chunks per matrix, two per thread
-  const char* wsrc[2] = {static_cast<const char*>(a.w_up),
-                         static_cast<const char*>(GATE ? a.w_gate : a.w_up)};
-  int lrow[2], lch[2];
+  // cooperative loads: element e = tid + UP_T * i -> (row e / UP_KC, chunk e % UP_KC)
+  const char* xsrc = static_cast<const char*>(a.x);
+  size_t aoff[LA], boff[LB];
+  bool aok[LA];
+  int ach[LA], bch[LB];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    lrow[i] = tid / DU_KC + i * (DT / DU_KC);
-    lch[i] = tid % DU_KC;
+  for (int i = 0; i < LA; ++i) {
+    const int e = tid + UP_T * i, row = e / UP_KC;
+    aok[i] = m0 + row < a.M;
+    aoff[i] = (size_t)min(m0 + row, a.M - 1) * nchk * 16;
+    ach[i] = e % UP_KC;
   }
-
-  auto load_w = [&](int k0c, u32x4 (&v)[NMAT][2]) {
+  const char* bsrc[LB];
 #pragma unroll
-    for (int mt = 0; mt < NMAT; ++mt)
+  for (int i = 0; i < LB; ++i) {
+    const int e = tid + UP_T * i, row = e / UP_KC;
+    const int mat = row / UP_N, n = min(n0 + row % UP_N, a.ffn - 1);
+    bsrc[i] = static_cast<const char*>(mat == 0 ? a.w_up : a.w_gate);
+    boff[i] = (size_t)n * nchk * 16;
+    bch[i] = e % UP_KC;
+  }
+  auto load = [&](int st, u32x4 (&ra)[LA], u32x4 (&rb)[LB]) {
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int c = k0c + lch[i];
-        const size_t row = (size_t)min(n0 + lrow[i], a.ffn - 1);
-        const u32x4 t = ld16(wsrc[mt] + (row * nchk + min(c, nchk - 1)) * 16);
-        v[mt][i] = c < nchk ? t : u32x4{0u, 0u, 0u, 0u};
-      }
-  };
-  auto load_a = [&](int k0c, u32x4 (&v)[2]) {
+    for (int i = 0; i < LA; ++i) {
+      const int c = st * UP_KC + ach[i];
+      const u32x4 t = ld16(xsrc + aoff[i] + (size_t)min(c, nchk - 1) * 16);
+      ra[i] = (aok[i] && c < nchk) ? t : u32x4{0u, 0u, 0u, 0u};
+    }
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const int c = k0c + 2 * kk + g;
-      const u32x4 t = ld16(arow + (size_t)min(c, nchk - 1) * 16);
-      v[kk] = (aok && c < nchk) ? t : u32x4{0u, 0u, 0u, 0u};
+    for (int i = 0; i < LB; ++i) {
+      const int c = st * UP_KC + bch[i];
+      const u32x4 t = ld16(bsrc[i] + boff[i] + (size_t)min(c, nchk - 1) * 16);
+      rb[i] = c < nchk ? t : u32x4{0u, 0u, 0u, 0u};
     }
   };
-  auto store_w = [&](int buf, const u32x4 (&v)[NMAT][2]) {
+  auto store = [&](int buf, const u32x4 (&ra)[LA], const u32x4 (&rb)[LB]) {
 #pragma unroll
-    for (int mt = 0; mt < NMAT; ++mt)
+    for (int i = 0; i < LA; ++i) {
+      const int e = tid + UP_T * i;
+      sA[buf][(e / UP_KC) * UP_LD + e % UP_KC] = ra[i];
+    }
 #pragma unroll
-      for (int i = 0; i < 2; ++i) s_b[buf][mt][lrow[i] * DU_LD + lch[i]] = v[mt][i];
+    for (int i = 0; i < LB; ++i) {
+      const int e = tid + UP_T * i;
+      sB[buf][(e / UP_KC) * UP_LD + e % UP_KC] = rb[i];
+    }
   };
 
-  f32x16 au[4], ag[GATE ? 4 : 1];
+  f32x16 acc[2][NSUB][NMAT];
 #pragma unroll
-  for (int t = 0; t < 4; ++t) au[t] = f32x16{};
+  for (int ms = 0; ms < 2; ++ms)
 #pragma unroll
-  for (int t = 0; t < (GATE ? 4 : 1); ++t) ag[t] = f32x16{};
+    for (int ns = 0; ns < NSUB; ++ns)
+#pragma unroll
+      for (int mt = 0; mt < NMAT; ++mt) acc[ms][ns][mt] = f32x16{};
 
-  const int nstage = (nchk + DU_KC - 1) / DU_KC;
-  u32x4 wv[NMAT][2], av[2];
-  load_w(0, wv);
-  load_a(0, av);
-  store_w(0, wv);
+  // loads run two stages ahead (two register sets), LDS holds the current and the next stage
+  const int nstage = (nchk + UP_KC - 1) / UP_KC;
+  u32x4 ra1[LA], rb1[LB], ra2[LA], rb2[LB];             // stages s+1 and s+2 in flight
+  load(0, ra1, rb1);
+  store(0, ra1, rb1);
+  if (nstage > 1) load(1, ra1, rb1);
   __syncthreads();
   for (int s = 0; s < nstage; ++s) {
     const int buf = s & 1;
-    u32x4 an[2];
-    const bool more = s + 1 < nstage;
-    if (more) {
-      load_w((s + 1) * DU_KC, wv);
-      load_a((s + 1) * DU_KC, an);
-    }
+    if (s + 2 < nstage) load(s + 2, ra2, rb2);
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
+    for (int kk = 0; kk < 2; ++kk) {
+      u32x4 af[2];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int idx = (t * 32 + r32) * DU_LD + 2 * kk + g;
-        au[t] = mma16(av[kk], s_b[buf][0][idx], au[t]);
-        if constexpr (GATE) ag[t] = mma16(av[kk], s_b[buf][NMAT - 1][idx], ag[t]);
-      }
-    if (more) {
-      store_w(buf ^ 1, wv);
-      av[0] = an[0];
-      av[1] = an[1];
+      for (int ms = 0; ms < 2; ++ms)
+        af[ms] = sA[buf][(wm * 64 + ms * 32 + r32) * UP_LD + 2 * kk + g];
+#pragma unroll
+      for (int ns = 0; ns < NSUB; ++ns)
+#pragma unroll
+        for (int mt = 0; mt < NMAT; ++mt) {
+          const u32x4 bf = sB[buf][(mt * UP_N + wn * (UP_N / 2) + ns * 32 + r32) * UP_LD + 2 * kk + g];
+#pragma unroll
+          for (int ms = 0; ms < 2; ++ms) acc[ms][ns][mt] = mma16(af[ms], bf, acc[ms][ns][mt]);
+        }
     }
+    if (s + 1 < nstage) store(buf ^ 1, ra1, rb1);
+#pragma unroll
+    for (int i = 0; i < LA; ++i) ra1[i] = ra2[i];
+#pragma unroll
+    for (int i = 0; i < LB; ++i) rb1[i] = rb2[i];
     __syncthreads();
   }
 
   // epilogue: h per (token, neuron), masked by the token's set, to H (fp16)
   const int W = a.ffn / 32;
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const int n = n0 + t * 32 + r32;
+  for (int ns = 0; ns < NSUB; ++ns) {
+    const int n = n0 + wn * (UP_N / 2) + ns * 32 + r32;
     const int nc = min(n, a.ffn - 1);
     const float bu = a.b_up ? a.b_up[nc] : 0.0f;
-    const float bg = a.b_gate ? a.b_gate[nc] : 0.0f;
+    const float bg = (GATE && a.b_gate) ? a.b_gate[nc] : 0.0f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int m = m0 + wave * 32 + acc_row(i, lane);
-      const float u = au[t][i] + bu;
-      float h;
-      if constexpr (!GATE) {
-        h = fmaxf(u, 0.0f);
-      } else {
-        const float gg = fmaxf(ag[t][i] + bg, 0.0f);
-        h = a.act == FFN_ACT_REGLU ? gg * u : gg * fmaxf(u, 0.0f);
+    for (int ms = 0; ms < 2; ++ms)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int m = m0 + wm * 64 + ms * 32 + acc_row(i, lane);
+        const float u = acc[ms][ns][0][i] + bu;
+        float h;
+        if constexpr (!GATE) {
+          h = fmaxf(u, 0.0f);
+        } else {
+          const float gg = fmaxf(acc[ms][ns][NMAT - 1][i] + bg, 0.0f);
+          h = a.act == FFN_ACT_REGLU ? gg * u : gg * fmaxf(u, 0.0f);
+        }
+        if (m < a.M && n < a.ffn) {
+          if (a.bits && !((a.bits[(size_t)m * W + (n >> 5)] >> (n & 31)) & 1u)) h = 0.0f;
+          a.H[(size_t)m * a.ffn + n] = (_Float16)h;
+        }
       }
-      if (m < a.M && n < a.ffn) {
-        if (a.bits && !((a.bits[(size_t)m * W + (n >> 5)] >> (n & 31)) & 1u)) h = 0.0f;
-        a.H[(size_t)m * a.ffn + n] = (_Float16)h;
-      }
-    }
   }
 }
 
@@ -228,18 +255,22 @@ __global__ __launch_bounds__(DT) void k_ddown(DenseArgs a) {
   for (int b = 0; b < 8; ++b) acc[b] = f32x16{};
 
   if (st0 < st1) {
-    u32x4 wv[4], av[2];
-    load_w(st0 * DD_K, wv);
+    // loads two stages ahead: (wn1, an1) hold stage s+1, (wn2, an2) receive stage s+2; LDS holds
+    // the current and the next stage
+    u32x4 wn1[4], wn2[4], av[2], an1[2], an2[2];
+    load_w(st0 * DD_K, wn1);
     load_a(st0 * DD_K, av);
-    store_w(0, wv);
+    store_w(0, wn1);
+    if (st0 + 1 < st1) {
+      load_w((st0 + 1) * DD_K, wn1);
+      load_a((st0 + 1) * DD_K, an1);
+    }
     __syncthreads();
     for (int s = st0; s < st1; ++s) {
       const int buf = (s - st0) & 1;
-      const bool more = s + 1 < st1;
-      u32x4 an[2];
-      if (more) {
-        load_w((s + 1) * DD_K, wv);
-        load_a((s + 1) * DD_K, an);
+      if (s + 2 < st1) {
+        load_w((s + 2) * DD_K, wn2);
+        load_a((s + 2) * DD_K, an2);
       }
 #pragma unroll
       for (int ss = 0; ss < 2; ++ss) {
@@ -269,11 +300,13 @@ __global__ __launch_bounds__(DT) void k_ddown(DenseArgs a) {
           acc[2 * q + 1] = mma16(av[ss], hi, acc[2 * q + 1]);
         }
       }
-      if (more) {
-        store_w(buf ^ 1, wv);
-        av[0] = an[0];
-        av[1] = an[1];
-      }
+      if (s + 1 < st1) store_w(buf ^ 1, wn1);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) wn1[i] = wn2[i];
+      av[0] = an1[0];
+      av[1] = an1[1];
+      an1[0] = an2[0];
+      an1[1] = an2[1];
       __syncthreads();
     }
   }
@@ -329,20 +362,21 @@ int dense_ks(int M, int d, int ffn) {
 }
 
 hipError_t launch_dense(const DenseArgs& a, hipStream_t st, hipEvent_t (*ev)[2]) {
-  const int t_up = ((a.M + DU_M - 1) / DU_M) * ((a.ffn + DU_N - 1) / DU_N);
+  const int up_n = a.has_gate ? 128 : 256;
+  const int t_up = ((a.M + UP_M - 1) / UP_M) * ((a.ffn + up_n - 1) / up_n);
   const int t_dn = ((a.M + DD_M - 1) / DD_M) * ((a.d + DD_N - 1) / DD_N) * a.ks;
   const dim3 g_up(8 * ((t_up + 7) / 8)), g_dn(8 * ((t_dn + 7) / 8));
   const dim3 g_red((unsigned)(((size_t)a.M * a.d / 4 + 255) / 256));
   if (a.has_gate) {
     if (ev && ev[0][0])
-      hipExtLaunchKernelGGL(k_dup<true>, g_up, dim3(DT), 0, st, ev[0][0], ev[0][1], 0, a);
+      hipExtLaunchKernelGGL(k_dup<true>, g_up, dim3(UP_T), 0, st, ev[0][0], ev[0][1], 0, a);
     else
-      hipLaunchKernelGGL(k_dup<true>, g_up, dim3(DT), 0, st, a);
+      hipLaunchKernelGGL(k_dup<true>, g_up, dim3(UP_T), 0, st, a);
   } else {
     if (ev && ev[0][0])
-      hipExtLaunchKernelGGL(k_dup<false>, g_up, dim3(DT), 0, st, ev[0][0], ev[0][1], 0, a);
+      hipExtLaunchKernelGGL(k_dup<false>, g_up, dim3(UP_T), 0, st, ev[0][0], ev[0][1], 0, a);
     else
-      hipLaunchKernelGGL(k_dup<false>, g_up, dim3(DT), 0, st, a);
+      hipLaunchKernelGGL(k_dup<false>, g_up, dim3(UP_T), 0, st, a);
   }
   if (ev && ev[1][0])
     hipExtLaunchKernelGGL(k_ddown, g_dn, dim3(DT), 0, st, ev[1][0], ev[1][1], 0, a);
