@@ -50,7 +50,7 @@ int cpl_for(int nch) {
 
 struct Layout {
   int cpl_w, cpl_p;
-  size_t off_z, off_bits, off_cnt, off_part, off_union, off_batch, off_dense, dense_rows, total;
+  size_t off_z, off_bits, off_cnt, off_part, scratch_end, off_batch, off_dense, dense_rows, total;
 };
 
 // Dense-GEMM region (fp16 layers that may see DENSE_MIN_M tokens or more): dbits [max_batch]
@@ -109,7 +109,7 @@ Layout layout_for(const ffn_layer_desc* d) {
   L.off_cnt = off;    off = round_up(off + 4, 256);
   L.off_part = off;
   off = round_up(off + (size_t)gather_blocks() * reduce_tiles(d->d) * 16 * 4, 256);
-  L.off_union = off;  off = round_up(off + 256, 256);
+  L.scratch_end = off;              // end of one token's decode scratch
   L.off_batch = 0;
   if (batched(d)) {
     // batched region: zpart | zhl | bits | ubits | ucnt | uidx | H | ypart
@@ -226,7 +226,7 @@ struct MoeLayout {
 
 MoeLayout moe_layout(const ffn_plan* e0, int top_k) {
   MoeLayout L{};
-  L.slot_stride = round_up(layout_for(&e0->desc).off_union, 256);
+  L.slot_stride = round_up(layout_for(&e0->desc).scratch_end, 256);
   L.off_slots = L.slot_stride * top_k;
   L.total = round_up(L.off_slots + (size_t)e0->desc.max_batch * top_k * sizeof(ExpertW), 256);
   return L;
@@ -499,7 +499,6 @@ ffn_status ffn_sparse_plan(const ffn_layer_desc* desc, const ffn_layer_weights* 
   p->off_bits = L.off_bits;
   p->off_cnt = L.off_cnt;
   p->off_part = L.off_part;
-  p->off_union = L.off_union;
   p->off_batch = L.off_batch;
   p->off_dense = L.off_dense;
   p->dense_ypart_rows = L.dense_rows;

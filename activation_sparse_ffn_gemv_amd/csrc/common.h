@@ -210,7 +210,7 @@ struct ffn_plan {
   int cpl_w;         // 16-byte chunks per lane for a weight row
   int cpl_p;         // 16-byte chunks per lane for a predictor P1 row
   float thr;         // logit(threshold): active iff score > thr
-  size_t off_z, off_bits, off_cnt, off_part, off_union;
+  size_t off_z, off_bits, off_cnt, off_part;
   size_t off_batch;  // batched-path region (fp16 layers with max_batch > 1), else 0
   size_t off_dense;  // dense-GEMM region (fp16 layers with max_batch >= 64), else 0
   size_t dense_ypart_rows;      // rows of the dense partial buffer (max over M of ks * M)

@@ -111,6 +111,13 @@ def test_plan_validation_before_any_gpu_call():
             ffn.ffn_dense_forward(plan, 0x1000, 1, 0x2000, mask=0x3001)
         assert e.value.status == ffn.FFN_ERR_INVALID_ARGUMENT
         assert ffn.ffn_plan_crossover(plan, 1) <= 1.0
+        ffn.ffn_plan_set_crossover(plan, 8, 0.25)           # bucket 8..15
+        assert ffn.ffn_plan_crossover(plan, 8) == 0.25
+        assert ffn.ffn_plan_crossover(plan, 15) == 0.25
+        assert ffn.ffn_plan_crossover(plan, 16) == 1.0
+        with pytest.raises(ffn.FFNError) as e:
+            ffn.ffn_plan_set_crossover(plan, 8, 1.5)
+        assert e.value.status == ffn.FFN_ERR_INVALID_ARGUMENT
     finally:
         ffn.ffn_plan_destroy(plan)
 

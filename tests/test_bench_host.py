@@ -1,0 +1,64 @@
+"""Host-side logic of bench.py (no GPU): the single-GPU contract, the byte accounting helpers and
+the lookup of profiled traffic."""
+import hashlib
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+import synth  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+
+
+def test_row_bytes_and_predictor_bytes():
+    c2 = synth.CONFIGS["llama2_7b_reglu_f16"]
+    assert bench.row_bytes(c2) == 2 * 4096
+    assert bench.n_rows(c2) == 3 and bench.n_bias(c2) == 1
+    pz, ps = bench.pred_bytes(c2)
+    assert pz == 256 * 4096 * 2 and ps == 11008 * 256 * 2 + 4 * 11008
+    c4 = synth.CONFIGS["turbosparse_mixtral_47b_moe_int4"]
+    assert bench.row_bytes(c4) == 4096 // 2 + (4096 // 32) * 2       # packed nibbles + fp16 scales
+    assert bench.n_bias(c4) == 2
+    c1 = synth.CONFIGS["opt125m_relu_f32"]
+    assert bench.row_bytes(c1) == 4 * 768 and bench.n_rows(c1) == 2
+
+
+def test_profiled_traffic_follows_the_source_hash(tmp_path, monkeypatch):
+    src = tmp_path / "k.hip"
+    src.write_text("kernel source v1\n")
+    h = hashlib.sha256(src.read_bytes()).hexdigest()
+    prof = tmp_path / "profiles"
+    prof.mkdir()
+    (prof / "k_x_w.md").write_text(
+        "# summary\n\n    traffic kernel=k_x workload=w bytes_per_launch=1234 source=k.hip "
+        "sha256=%s\n" % h)
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    assert bench.profiled_traffic("k_x", "w") == 1234
+    assert bench.profiled_traffic("k_x", "other") is None
+    assert bench.profiled_traffic("k_y", "w") is None
+    src.write_text("kernel source v2\n")                 # kernel changed since the counters
+    assert bench.profiled_traffic("k_x", "w") is None
+
+
+def test_committed_profiles_name_existing_sources():
+    pdir = os.path.join(ROOT, "profiles")
+    n = 0
+    for f in os.listdir(pdir):
+        for line in open(os.path.join(pdir, f)):
+            t = line.split()
+            if t and t[0] == "traffic":
+                kv = dict(x.split("=", 1) for x in t[1:])
+                assert os.path.exists(os.path.join(ROOT, kv["source"])), kv["source"]
+                assert int(kv["bytes_per_launch"]) > 0
+                n += 1
+    assert n >= 1
