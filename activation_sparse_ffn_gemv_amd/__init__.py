@@ -36,7 +36,8 @@ DTYPE = {"f32": FFN_F32, "f16": FFN_F16, "i4g32": FFN_I4G32}
 # Every symbol the header declares (checked by the tests).
 EXPORTS = [
     "ffn_workspace_size", "ffn_sparse_plan", "ffn_sparse_forward", "ffn_dense_forward",
-    "ffn_plan_crossover", "ffn_plan_set_crossover", "ffn_plan_destroy", "ffn_plan_set_timing_events", "ffn_last_error",
+    "ffn_plan_crossover", "ffn_plan_set_crossover", "ffn_plan_set_decode_variant",
+    "ffn_plan_destroy", "ffn_plan_set_timing_events", "ffn_last_error",
     "ffn_moe_workspace_size",
     "ffn_moe_plan", "ffn_moe_forward", "ffn_moe_destroy",
 ]
@@ -90,6 +91,8 @@ def lib():
         L.ffn_plan_crossover.argtypes = [P, I, ctypes.POINTER(ctypes.c_float)]
         L.ffn_plan_set_crossover.restype = st
         L.ffn_plan_set_crossover.argtypes = [P, I, ctypes.c_float]
+        L.ffn_plan_set_decode_variant.restype = st
+        L.ffn_plan_set_decode_variant.argtypes = [P, I]
         L.ffn_plan_destroy.restype = st
         L.ffn_plan_destroy.argtypes = [P]
         L.ffn_plan_set_timing_events.restype = st
@@ -148,6 +151,10 @@ def ffn_plan_crossover(plan: int, B: int) -> float:
 
 def ffn_plan_set_crossover(plan: int, B: int, density: float):
     _check(lib().ffn_plan_set_crossover(plan, B, density))
+
+
+def ffn_plan_set_decode_variant(plan: int, variant: int):
+    _check(lib().ffn_plan_set_decode_variant(plan, variant))
 
 
 def ffn_plan_destroy(plan: int):

@@ -108,7 +108,8 @@ Layout layout_for(const ffn_layer_desc* d) {
   L.off_bits = off;   off = round_up(off + (size_t)d->ffn / 32 * 4, 256);
   L.off_cnt = off;    off = round_up(off + 4, 256);
   L.off_part = off;
-  off = round_up(off + (size_t)gather_blocks() * reduce_tiles(d->d) * 16 * 4, 256);
+  off = round_up(off + (size_t)std::max(gather_blocks(), fused_blocks(d->ffn)) *
+                           reduce_tiles(d->d) * 16 * 4, 256);
   L.scratch_end = off;              // end of one token's decode scratch
   L.off_batch = 0;
   if (batched(d)) {
@@ -275,6 +276,8 @@ ffn_status enqueue_token(const ffn_plan* p, const TokenBufs& wb, const void* xb,
   const int wk = D.w_dtype == FFN_F32 ? WK_F32 : D.w_dtype == FFN_F16 ? WK_F16 : WK_I4;
   const int es = (int)(slot_stride / 4);      // the same stride in 4-byte elements
   hipError_t e;
+  const bool fused = !maskb && !all_neurons && !slot && p->decode_variant == 1 &&
+                     fused_supported(wk, D.d);
   if (maskb || all_neurons) {
     e = launch_mask_bits(maskb, wb.bits, D.ffn / 32, st);
     if (e != hipSuccess) return hip_fail(e, "mask launch");
@@ -296,9 +299,27 @@ ffn_status enqueue_token(const ffn_plan* p, const TokenBufs& wb, const void* xb,
     pa.nslot = nslot;
     pa.zstride = es;
     pa.bstride = es;
-    e = launch_pred_s(D.p_dtype == FFN_F16, pa, st, p->ev[FFN_STAGE_PRED_S][0],
-                      p->ev[FFN_STAGE_PRED_S][1]);
-    if (e != hipSuccess) return hip_fail(e, "predictor stage 2 launch");
+    if (!fused) {
+      e = launch_pred_s(D.p_dtype == FFN_F16, pa, st, p->ev[FFN_STAGE_PRED_S][0],
+                        p->ev[FFN_STAGE_PRED_S][1]);
+      if (e != hipSuccess) return hip_fail(e, "predictor stage 2 launch");
+    } else {
+      FusedArgs fa{};
+      fa.pa = pa;
+      fa.ga.w_up = p->w.w_up;
+      fa.ga.w_gate = p->w.w_gate;
+      fa.ga.w_dn = p->w.w_down_t;
+      fa.ga.b_up = p->w.b_up;
+      fa.ga.b_gate = p->w.b_gate;
+      fa.ga.x = xb;
+      fa.ga.part = wb.part;
+      fa.ga.d = D.d;
+      fa.ga.ffn = D.ffn;
+      fa.ga.act = D.act;
+      fa.ga.has_gate = D.act != FFN_ACT_RELU;
+      e = launch_fused(wk, fa, st, p->ev[FFN_STAGE_GATHER][0], p->ev[FFN_STAGE_GATHER][1]);
+      if (e != hipSuccess) return hip_fail(e, "fused predictor + gather launch");
+    }
   }
   GatherArgs ga{};
   ga.w_up = p->w.w_up;
@@ -322,8 +343,10 @@ ffn_status enqueue_token(const ffn_plan* p, const TokenBufs& wb, const void* xb,
   ga.bstride = es;
   ga.cstride = es;
   ga.pstride = (size_t)es;
-  e = launch_gather(wk, ga, st, p->ev[FFN_STAGE_GATHER][0], p->ev[FFN_STAGE_GATHER][1]);
-  if (e != hipSuccess) return hip_fail(e, "gather launch");
+  if (!fused) {
+    e = launch_gather(wk, ga, st, p->ev[FFN_STAGE_GATHER][0], p->ev[FFN_STAGE_GATHER][1]);
+    if (e != hipSuccess) return hip_fail(e, "gather launch");
+  }
   ReduceArgs ra{};
   ra.part = wb.part;
   ra.cnt = wb.cnt;
@@ -334,7 +357,8 @@ ffn_status enqueue_token(const ffn_plan* p, const TokenBufs& wb, const void* xb,
   ra.cnt_out = cntb;
   ra.d = D.d;
   ra.ffn = D.ffn;
-  ra.n_part = gather_blocks();
+  ra.n_part = fused ? fused_blocks(D.ffn) : gather_blocks();
+  ra.fused = fused;
   ra.slot = slot;
   ra.nslot = nslot;
   ra.cstride = es;
@@ -508,6 +532,7 @@ ffn_status ffn_sparse_plan(const ffn_layer_desc* desc, const ffn_layer_weights* 
   // more than every row, so the union is kept (crossover 1) until calibration says otherwise
   for (int k = 0; k < 13; ++k) p->crossover_density[k] = 1.0f;
   p->dense_min_batch = 2;
+  p->decode_variant = 0;
   if (calibrate && batched(desc) && desc->max_batch >= 2) {
     st = calibrate_crossover(p, static_cast<hipStream_t>(stream));
     if (st != FFN_OK) {
@@ -711,6 +736,19 @@ ffn_status ffn_plan_set_crossover(ffn_plan* p, int32_t B, float density) {
   int k = 0;
   while (k < 12 && (1 << (k + 1)) <= B) ++k;
   p->crossover_density[k] = density;
+  return FFN_OK;
+}
+
+ffn_status ffn_plan_set_decode_variant(ffn_plan* p, int32_t variant) {
+  if (!p) return fail(FFN_ERR_INVALID_ARGUMENT, "plan is NULL");
+  if (variant < 0 || variant > 1)
+    return fail(FFN_ERR_INVALID_ARGUMENT, "variant %d is not 0 or 1", variant);
+  const ffn_layer_desc& D = p->desc;
+  const int wk = D.w_dtype == FFN_F32 ? WK_F32 : D.w_dtype == FFN_F16 ? WK_F16 : WK_I4;
+  if (variant == 1 && (!fused_supported(wk, D.d) || D.rank == 0))
+    return fail(FFN_ERR_UNSUPPORTED, "the fused decode variant needs fp32 / fp16 rows of "
+                "%d..%d chunks and a predictor", 256, 1024);
+  p->decode_variant = variant;
   return FFN_OK;
 }
 

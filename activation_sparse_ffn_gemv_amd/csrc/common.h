@@ -217,4 +217,5 @@ struct ffn_plan {
   float crossover_density[13];  // per batch bucket 1, 2, 4, ..., 4096
   int dense_min_batch;          // AUTO takes the dense path from this batch size on
   hipEvent_t ev[9][2];          // instrumentation events attached to each stage's dispatch
+  int decode_variant;           // batch-1 decode: 0 rank-balanced gather, 1 fused predictor + gather
 };

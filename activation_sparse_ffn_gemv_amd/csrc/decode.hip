@@ -522,6 +522,250 @@ __global__ __launch_bounds__(GA_THREADS) void k_gather(GatherArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------------
+// Fused predictor stage 2 + gather (batch-1 decode variant).  A workgroup of 512 threads owns 64
+// consecutive neurons (two bitmap words; the last may own 32):
+//   1. s = P2 z + c2 for its rows (as k_pred_s: a P2 row split over L lanes, all passes' loads
+//      in flight together with the token's), threshold, a 64-lane ballot -> the two bitmap words
+//      and the ascending local list of its active neurons;
+//   2. rounds of up to RN of those neurons exactly as in k_gather (thread t owns column chunks
+//      t, t + 512, ...; workgroup sums through DPP and LDS; one row axpy per neuron);
+//   3. its partial of y (written only when one of its neurons fired).
+// No rank balancing: the workgroups' loads differ with the token's set, but the predictor's
+// second stage and the gather share one launch and no scan is needed.
+constexpr int FU_THREADS = 512;
+constexpr int FU_NW = FU_THREADS / WAVE;
+constexpr int FU_ROWS = 64;
+
+template <int WK, int CPT, int CPR>
+__global__ __launch_bounds__(FU_THREADS) void k_fused(FusedArgs f) {
+  constexpr int NT = FU_THREADS;
+  constexpr int RN = 16 / CPT;
+  constexpr int EPC = Kind<WK>::EPC;
+  constexpr int PK = WK == WK_F32 ? WK_F32 : WK_F16;    // predictor storage = token storage
+  constexpr int PE = Kind<PK>::EPC;
+  __shared__ float s_score[FU_ROWS];
+  __shared__ int s_list[FU_ROWS];
+  __shared__ int s_m;
+  __shared__ float s_red[FU_NW][2 * RN];
+  __shared__ float s_h[RN];
+  const PredArgs& p = f.pa;
+  const GatherArgs& a = f.ga;
+  const int tid = threadIdx.x;
+  const int lane = tid & (WAVE - 1), wave = tid / WAVE;
+  const int i0 = blockIdx.x * FU_ROWS;
+  const int n = min(FU_ROWS, p.ffn - i0);               // 64, or 32 for the last workgroup
+  const int nch = a.d / EPC;
+  FFN_TS(1, 0);
+
+  // this thread's chunks of the token (chunk tid + k*NT)
+  u32x4 xr[CPT];
+#pragma unroll
+  for (int k = 0; k < CPT; ++k) {
+    const int c = tid + k * NT;
+    const u32x4 v = ld16(static_cast<const char*>(a.x) + (size_t)min(c, nch - 1) * 16);
+    xr[k] = c < nch ? v : u32x4{0u, 0u, 0u, 0u};
+  }
+
+  // 1. scores of the workgroup's rows
+  const int pch = p.rank / PE;
+  int L = 64;
+  while (L > 4 && (L >> 1) >= pch) L >>= 1;
+  const int R = NT / L;                                 // rows per pass
+  const int P = (n + R - 1) / R;                        // passes (<= PS_MAXP)
+  const int g = tid / L, gl = tid % L;
+  const float c2v = (tid < n && p.c2) ? p.c2[i0 + tid] : 0.0f;
+  f32x4 zr[CPR][PE / 4];
+#pragma unroll
+  for (int k = 0; k < CPR; ++k) {
+    const int c = gl + k * L;
+    const int cc = min(c, pch - 1);
+#pragma unroll
+    for (int q = 0; q < PE / 4; ++q) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(p.z + cc * PE + 4 * q);
+      zr[k][q] = c < pch ? v : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+  u32x4 w[PS_MAXP][CPR];
+#pragma unroll
+  for (int pp = 0; pp < PS_MAXP; ++pp) {
+    const int r = min(pp * R + g, n - 1);
+#pragma unroll
+    for (int k = 0; k < CPR; ++k) {
+      const int cc = min(gl + k * L, pch - 1);
+      if (pp < P) w[pp][k] = ld16(static_cast<const char*>(p.p2) + ((size_t)(i0 + r) * pch + cc) * 16);
+    }
+  }
+  issue_fence();
+#pragma unroll
+  for (int pp = 0; pp < PS_MAXP; ++pp) {
+    if (pp < P) {                                       // uniform
+    float acc = 0.0f;
+#pragma unroll
+    for (int k = 0; k < CPR; ++k) {
+      if (gl + k * L >= pch) continue;                 // lane past the row end (small ranks)
+      const float* zf = reinterpret_cast<const float*>(&zr[k][0]);
+      if constexpr (PK == WK_F16) {
+        const uint32_t ww[4] = {w[pp][k].x, w[pp][k].y, w[pp][k].z, w[pp][k].w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          acc = __builtin_fmaf(h_lo(ww[q]), zf[2 * q], acc);
+          acc = __builtin_fmaf(h_hi(ww[q]), zf[2 * q + 1], acc);
+        }
+      } else {
+        const f32x4 wf = __builtin_bit_cast(f32x4, w[pp][k]);
+        acc = __builtin_fmaf(wf.x, zf[0], acc);
+        acc = __builtin_fmaf(wf.y, zf[1], acc);
+        acc = __builtin_fmaf(wf.z, zf[2], acc);
+        acc = __builtin_fmaf(wf.w, zf[3], acc);
+      }
+    }
+    acc = group_sum_last(acc, L);
+    const int r = pp * R + g;
+    if (gl == L - 1 && r < n) s_score[r] = acc;
+    }
+  }
+  __syncthreads();
+  FFN_TS(1, 1);
+  if (wave == 0) {
+    bool on = false;
+    if (lane < n) {
+      const float sc = s_score[lane] + c2v;
+      on = sc > p.thr;
+      if (p.scores) p.scores[i0 + lane] = sc;
+    }
+    const unsigned long long bal = __ballot(on);
+    if (on) s_list[__popcll(bal & ((1ull << lane) - 1ull))] = i0 + lane;
+    if (lane == 0) {
+      p.bitmap[blockIdx.x * 2] = (uint32_t)bal;
+      if (n > 32) p.bitmap[blockIdx.x * 2 + 1] = (uint32_t)(bal >> 32);
+      s_m = __popcll(bal);
+    }
+  }
+  __syncthreads();
+  FFN_TS(1, 2);
+  const int m = s_m;
+
+  float acc[CPT][EPC];
+#pragma unroll
+  for (int k = 0; k < CPT; ++k)
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) acc[k][e] = 0.0f;
+
+  for (int t0 = 0; t0 < m; t0 += RN) {
+    u32x4 wu[RN][CPT], wg[RN][CPT], wd[RN][CPT];
+    float bu = 0.0f, bgt = 0.0f;
+    if (tid < RN && t0 + tid < m) {
+      const int nq = s_list[t0 + tid];
+      if (a.b_up) bu = a.b_up[nq];
+      if (a.b_gate) bgt = a.b_gate[nq];
+    }
+#pragma unroll
+    for (int r = 0; r < RN; ++r) {
+      const bool live_r = t0 + r < m;                   // uniform across the workgroup
+      const size_t nr = (size_t)s_list[min(t0 + r, m - 1)];
+#pragma unroll
+      for (int k = 0; k < CPT; ++k) {
+        const size_t off = (nr * nch + min(tid + k * NT, nch - 1)) * 16;
+        wu[r][k] = wg[r][k] = wd[r][k] = u32x4{0u, 0u, 0u, 0u};
+        if (live_r) {
+          wu[r][k] = ld16(static_cast<const char*>(a.w_up) + off);
+          if (a.has_gate) wg[r][k] = ld16(static_cast<const char*>(a.w_gate) + off);
+          wd[r][k] = ld16(static_cast<const char*>(a.w_dn) + off);
+        }
+      }
+    }
+    issue_fence();
+#pragma unroll
+    for (int r = 0; r < RN; ++r) {
+      if (t0 + r < m) {                                  // uniform across the workgroup
+        float pu = 0.0f, pg = 0.0f;
+#pragma unroll
+        for (int k = 0; k < CPT; ++k) {
+          if constexpr (WK == WK_F32) {
+            pu = dot4_f32(wu[r][k], xr[k], pu);
+            if (a.has_gate) pg = dot4_f32(wg[r][k], xr[k], pg);
+          } else {
+            pu = dot8_f16(wu[r][k], xr[k], pu);
+            if (a.has_gate) pg = dot8_f16(wg[r][k], xr[k], pg);
+          }
+        }
+        pu = wave_sum(pu);
+        if (a.has_gate) pg = wave_sum(pg);
+        if (lane == 0) {
+          s_red[wave][2 * r] = pu;
+          s_red[wave][2 * r + 1] = pg;
+        }
+      }
+    }
+    __syncthreads();
+    if (tid < RN) {
+      float u = 0.0f, gg = 0.0f, h = 0.0f;
+      if (t0 + tid < m) {
+#pragma unroll
+        for (int ww = 0; ww < FU_NW; ++ww) {
+          u += s_red[ww][2 * tid];
+          gg += s_red[ww][2 * tid + 1];
+        }
+        u += bu;
+        if (a.act == FFN_ACT_RELU) {
+          h = fmaxf(u, 0.0f);
+        } else {
+          gg = fmaxf(gg + bgt, 0.0f);
+          h = a.act == FFN_ACT_REGLU ? gg * u : gg * fmaxf(u, 0.0f);
+        }
+      }
+      s_h[tid] = h;
+    }
+    __syncthreads();
+    FFN_TS(1, 3);
+#pragma unroll
+    for (int r = 0; r < RN; ++r) {
+      if (t0 + r < m) {                                  // uniform
+      const float h = s_h[r];
+#pragma unroll
+      for (int k = 0; k < CPT; ++k) {
+        if constexpr (WK == WK_F32) {
+          const f32x4 q = __builtin_bit_cast(f32x4, wd[r][k]);
+          acc[k][0] = __builtin_fmaf(h, q.x, acc[k][0]);
+          acc[k][1] = __builtin_fmaf(h, q.y, acc[k][1]);
+          acc[k][2] = __builtin_fmaf(h, q.z, acc[k][2]);
+          acc[k][3] = __builtin_fmaf(h, q.w, acc[k][3]);
+        } else {
+          const uint32_t ww[4] = {wd[r][k].x, wd[r][k].y, wd[r][k].z, wd[r][k].w};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            acc[k][2 * q] = __builtin_fmaf(h, h_lo(ww[q]), acc[k][2 * q]);
+            acc[k][2 * q + 1] = __builtin_fmaf(h, h_hi(ww[q]), acc[k][2 * q + 1]);
+          }
+        }
+      }
+      }
+    }
+    __syncthreads();                                     // s_red / s_h reused
+  }
+  FFN_TS(1, 4);
+  if (m > 0) {
+    const int nparts = gridDim.x;
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) {
+      const int c = tid + k * NT;
+      if (c < nch) {
+#pragma unroll
+        for (int e = 0; e < EPC; e += 4) {
+          const int col = c * EPC + e;
+          float* dst = a.part + ((size_t)(col / RD_TW) * nparts + blockIdx.x) * RD_TW + col % RD_TW;
+          __builtin_nontemporal_store(f32x4{acc[k][e], acc[k][e + 1], acc[k][e + 2], acc[k][e + 3]},
+                                      reinterpret_cast<f32x4*>(dst));
+        }
+      }
+    }
+  }
+  FFN_TRACE_SYNC();
+  FFN_TS(1, 5);
+  FFN_TV(1, 6, m);
+}
+
+// ---------------------------------------------------------------------------------------------
 // y = b_down + sum of the gather partials, in workgroup order.  Workgroup j owns the RD_TW
 // columns of tile j; the partials are stored tile-major, so it reads one contiguous block of
 // GA_BLOCKS * RD_TW floats (every thread four 16-byte pieces at once).  Partials of gather
@@ -530,8 +774,7 @@ __global__ __launch_bounds__(GA_THREADS) void k_gather(GatherArgs a) {
 constexpr int RD_THREADS = 256;
 constexpr int RD_Q = RD_TW / 4;                        // float4 columns per tile
 constexpr int RD_G = RD_THREADS / RD_Q;                // partial groups
-constexpr int RD_UNROLL = GA_BLOCKS / RD_G;
-static_assert(GA_BLOCKS % RD_G == 0, "whole partial groups");
+constexpr int RD_UNROLL = 4;                           // partials per thread in flight
 
 __global__ __launch_bounds__(RD_THREADS) void k_reduce(ReduceArgs a) {
   __shared__ f32x4 s[RD_G][RD_Q];
@@ -544,21 +787,27 @@ __global__ __launch_bounds__(RD_THREADS) void k_reduce(ReduceArgs a) {
   f32x4 out = {0.f, 0.f, 0.f, 0.f};
   for (int k = 0; k < nslot; ++k) {
     const int total = a.cnt[(size_t)k * a.cstride];
-    const float* blk = a.part + (size_t)k * a.pstride + (size_t)tile * GA_BLOCKS * RD_TW;
-    f32x4 v[RD_UNROLL];
-    bool on[RD_UNROLL];
-#pragma unroll
-    for (int u = 0; u < RD_UNROLL; ++u) {
-      const int c = g + u * RD_G;
-      // partial c exists iff gather workgroup c owned at least one rank
-      on[u] = ((long long)total * (c + 1)) / GA_BLOCKS > ((long long)total * c) / GA_BLOCKS;
-      v[u] = *reinterpret_cast<const f32x4*>(blk + (size_t)c * RD_TW + q * 4);
-    }
-    issue_fence();
+    const float* blk = a.part + (size_t)k * a.pstride + (size_t)tile * a.n_part * RD_TW;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int c0 = 0; c0 < a.n_part; c0 += RD_G * RD_UNROLL) {
+      f32x4 v[RD_UNROLL];
+      bool on[RD_UNROLL];
 #pragma unroll
-    for (int u = 0; u < RD_UNROLL; ++u)
-      if (on[u]) acc += v[u];
+      for (int u = 0; u < RD_UNROLL; ++u) {
+        const int c = c0 + g + u * RD_G;
+        // partial c exists iff its workgroup had an active neuron
+        if (a.fused)
+          on[u] = c < a.n_part && (a.bitmap[2 * c] | (2 * c + 1 < a.ffn / 32 ? a.bitmap[2 * c + 1] : 0u));
+        else
+          on[u] = c < a.n_part &&
+                  ((long long)total * (c + 1)) / a.n_part > ((long long)total * c) / a.n_part;
+        v[u] = *reinterpret_cast<const f32x4*>(blk + (size_t)min(c, a.n_part - 1) * RD_TW + q * 4);
+      }
+      issue_fence();
+#pragma unroll
+      for (int u = 0; u < RD_UNROLL; ++u)
+        if (on[u]) acc += v[u];
+    }
     __syncthreads();                         // s reused across slots
     s[g][q] = acc;
     __syncthreads();
@@ -709,6 +958,45 @@ hipError_t launch_gather(int wk, const GatherArgs& a, hipStream_t st, hipEvent_t
 }
 
 int reduce_tiles(int d) { return (d + RD_TW - 1) / RD_TW; }
+
+int fused_blocks(int ffn) { return (ffn + FU_ROWS - 1) / FU_ROWS; }
+
+// fp32 / fp16 rows of at least 512 chunks per 512 threads (one or two chunks per thread)
+bool fused_supported(int wk, int d) {
+  if (wk == WK_I4) return false;
+  const int nch = d / (wk == WK_F32 ? 4 : 8);
+  return nch >= FU_THREADS / 2 && nch <= 2 * FU_THREADS;
+}
+
+template <int WK, int CPT, int CPR>
+static hipError_t launch_fused_t(const FusedArgs& a, hipStream_t st, hipEvent_t ev0,
+                                 hipEvent_t ev1) {
+  const dim3 grid(fused_blocks(a.pa.ffn));
+  if (ev0 && ev1)
+    hipExtLaunchKernelGGL((k_fused<WK, CPT, CPR>), grid, dim3(FU_THREADS), 0, st, ev0, ev1, 0, a);
+  else
+    hipLaunchKernelGGL((k_fused<WK, CPT, CPR>), grid, dim3(FU_THREADS), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_fused(int wk, const FusedArgs& a, hipStream_t st, hipEvent_t ev0,
+                        hipEvent_t ev1) {
+  if (!fused_supported(wk, a.ga.d)) return hipErrorInvalidValue;
+  const int nch = a.ga.d / (wk == WK_F32 ? 4 : 8);
+  const int cpt = (nch + FU_THREADS - 1) / FU_THREADS;
+  const int cpr = pred_s_cpr(wk == WK_F16, a.pa.rank);
+#define FU_CASE(W, C, R) \
+  if (cpt == C && cpr == R) return launch_fused_t<W, C, R>(a, st, ev0, ev1);
+  if (wk == WK_F32) {
+    FU_CASE(WK_F32, 1, 1) FU_CASE(WK_F32, 1, 2) FU_CASE(WK_F32, 1, 4)
+    FU_CASE(WK_F32, 2, 1) FU_CASE(WK_F32, 2, 2) FU_CASE(WK_F32, 2, 4)
+  } else {
+    FU_CASE(WK_F16, 1, 1) FU_CASE(WK_F16, 1, 2) FU_CASE(WK_F16, 1, 4)
+    FU_CASE(WK_F16, 2, 1) FU_CASE(WK_F16, 2, 2) FU_CASE(WK_F16, 2, 4)
+  }
+#undef FU_CASE
+  return hipErrorInvalidValue;
+}
 
 hipError_t launch_reduce(const ReduceArgs& a, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
   const dim3 grid(reduce_tiles(a.d)), block(RD_THREADS);

@@ -81,11 +81,25 @@ struct ReduceArgs {
   int* idx_out;               // [ffn] ascending active list, or nullptr
   int* cnt_out;               // [1], or nullptr
   int d, ffn, n_part;
+  int fused;                  // partials from the fused kernel: partial c exists iff bitmap words
+                              //   2c, 2c+1 are not both zero (else: from |A| and the rank split)
   const ExpertW* slot;        // device-chosen experts: b_down and the routing weights, or nullptr
   int nslot;                  // y = sum over the nslot slots (in order) of wgt_k * result_k;
   int cstride;                //   slot k's partials at part + k*pstride, its |A| at cnt + k*cstride
   size_t pstride;
 };
+
+// Fused predictor stage 2 + gather (the alternative batch-1 decode variant): a workgroup
+// scores its own 64 neurons and gathers the active ones among them (no rank balancing, one
+// launch fewer).  Partials: one per workgroup, tile-major like the balanced gather's.
+struct FusedArgs {
+  PredArgs pa;                // p2, c2, z, scores, bitmap, ffn, rank, thr
+  GatherArgs ga;              // rows, scales, biases, x, part, d, act, has_gate
+};
+int fused_blocks(int ffn);
+bool fused_supported(int wk, int d);
+hipError_t launch_fused(int wk, const FusedArgs& a, hipStream_t st, hipEvent_t ev0 = nullptr,
+                        hipEvent_t ev1 = nullptr);
 
 hipError_t launch_pred_z(int p_f16, int cpl, const void* p1, const float* c1, const void* x,
                          float* z, int d, int rank, const ExpertW* slot, int nslot, int zstride,

@@ -92,6 +92,9 @@ def main():
                     help="steps whose kernel launches are timed with dispatch events")
     ap.add_argument("--cpu-tokens", type=int, default=3,
                     help="tokens the CPU oracle baseline runs per layer; 0 = skip")
+    ap.add_argument("--decode-variant", type=int, default=None,
+                    help="batch-1 decode variant for every plan (0 balanced, 1 fused); "
+                         "default: the library's")
     ap.add_argument("--calibrate", type=int, default=0,
                     help="also calibrate layer 0's plan for batches up to this size and report "
                          "its measured crossover densities (fp16 layers)")
@@ -163,6 +166,9 @@ def main():
                                      [m.plan for m in mods[l]], mws.data_ptr(), n)
                     for l in range(L)]
     plans = [m.plan for row in mods for m in row]
+    if args.decode_variant is not None:
+        for q in plans:
+            ffn.ffn_plan_set_decode_variant(q, args.decode_variant)
     xb = x.element_size() * cfg.d
     xp = [[x[l].data_ptr() + t * Bt * xb for t in range(K)] for l in range(L)]
     yp = [[y[l].data_ptr() + t * Bt * cfg.d * 4 for t in range(K)] for l in range(L)]
@@ -475,6 +481,7 @@ def main():
         "dtype": dtype,
         "data": "synthetic (seeded; power-law hot set)",
         "config": {"workload": cfg.name, "mode": mode, "tokens_per_call": Bt, "d": cfg.d,
+                   "decode_variant": args.decode_variant,
                    "ffn": cfg.ffn, "rank": cfg.rank, "act": cfg.act, "layers": L,
                    "experts": cfg.n_experts, "top_k": cfg.top_k if moe else None,
                    "target_density": cfg.density, "measured_density": round(density, 5)},

@@ -141,6 +141,15 @@ ffn_status ffn_dense_forward(ffn_plan *plan, const void *x, int32_t B, float *y,
 ffn_status ffn_plan_crossover(const ffn_plan *plan, int32_t B, float *density);
 ffn_status ffn_plan_set_crossover(ffn_plan *plan, int32_t B, float density);
 
+/*
+ * Batch-1 decode variant (a tuning knob; results agree within rounding).  0: the predictor's
+ * second stage and a rank-balanced gather are separate launches (the default); 1: one fused
+ * launch in which every workgroup scores 64 neurons and gathers its own active ones (one launch
+ * and one scan fewer, no balancing).  1 needs fp32 / fp16 rows of 256..1024 16-byte chunks and
+ * a predictor (FFN_ERR_UNSUPPORTED otherwise); calls with a caller mask use variant 0.
+ */
+ffn_status ffn_plan_set_decode_variant(ffn_plan *plan, int32_t variant);
+
 ffn_status ffn_plan_destroy(ffn_plan *plan);
 
 /*

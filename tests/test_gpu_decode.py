@@ -264,3 +264,70 @@ def test_index_and_count_outputs_are_independent(ffn):
     for yy in (y_cnt, y_idx, y_none):
         assert torch.equal(yy, y_both)
     m.close()
+
+
+@pytest.mark.parametrize("cfgname,tokens", [("llama2_7b_reglu_f16", 3),
+                                            ("turbosparse_mistral_7b_drelu_f16", 2),
+                                            ("falcon_40b_relu_f16", 1)])
+def test_fused_decode_variant(ffn, cfgname, tokens):
+    """The fused predictor + gather variant against the oracle (and the balanced variant)."""
+    cfg = synth.CONFIGS[cfgname]
+    host = synth.make_layer(cfg, device="cuda")
+    L, OL = to_device(host), oracle_layer(host)
+    x = synth.make_tokens(cfg, tokens).cuda()
+    m = ffn.SparseFFN(L, max_batch=1)
+    outs = []
+    for variant in (0, 1):
+        ffn.ffn_plan_set_decode_variant(m.plan, variant)
+        y = torch.zeros(tokens, cfg.d, device="cuda")
+        idx = torch.full((tokens, cfg.ffn), -1, dtype=torch.int32, device="cuda")
+        cnt = torch.zeros(tokens, dtype=torch.int32, device="cuda")
+        for t in range(tokens):
+            m.forward(x[t:t + 1], y=y[t:t + 1], idx=idx[t:t + 1], cnt=cnt[t:t + 1])
+        torch.cuda.synchronize()
+        outs.append((y.cpu().numpy(), idx.cpu().numpy(), cnt.cpu().numpy()))
+    xh = x.cpu().numpy()
+    (y0, i0, c0), (y1, i1, c1) = outs
+    for t in range(tokens):
+        lt = i1[t, :c1[t]]
+        pred = oracle.predictor(OL["p1"], OL["p2"], OL["c1"], OL["c2"], xh[t], OL["tau"])
+        check_index_list(lt, pred, OL["tau"])
+        assert np.array_equal(lt, i0[t, :c0[t]])          # same predictor arithmetic
+        y_ref, _ = oracle.ffn(OL, xh[t], mask_from_idx(lt, cfg.ffn))
+        assert normwise(y1[t], y_ref) <= TOL[cfg.w_dtype]
+        assert normwise(y1[t], y0[t].astype(np.float64)) <= 1e-5
+    with pytest.raises(ffn.FFNError):
+        ffn.ffn_plan_set_decode_variant(m.plan, 2)
+    m.close()
+
+
+def test_fused_variant_small_and_edge_sets(ffn):
+    """Fused variant with a ragged ffn (last workgroup owns 32 neurons), tau = 1 (nothing
+    fires: y = b_down) and a tiny tau (everything fires: the dense FFN)."""
+    cfg = synth.small_config(d=2048, ffn=1056, rank=32, act="drelu", w_dtype="f16",
+                             x_dtype="f16", p_dtype="f16", density=0.15, bias_gate=True,
+                             bias_up=True, bias_down=True)
+    host = synth.make_layer(cfg)
+    L, OL = to_device(host), oracle_layer(host)
+    x = synth.make_tokens(cfg, 2).cuda()
+    xh = x.cpu().numpy()
+    for tau in (0.5, 1.0, 1e-30):
+        layer = dict(L)
+        layer["tau"] = tau
+        m = ffn.SparseFFN(layer, max_batch=1)
+        ffn.ffn_plan_set_decode_variant(m.plan, 1)
+        for t in range(2):
+            idx = torch.full((1, cfg.ffn), -1, dtype=torch.int32, device="cuda")
+            cnt = torch.zeros(1, dtype=torch.int32, device="cuda")
+            y = m.forward(x[t:t + 1], idx=idx, cnt=cnt)
+            torch.cuda.synchronize()
+            lt = idx[0, :int(cnt[0])].cpu().numpy()
+            if tau == 1.0:
+                assert lt.size == 0
+                assert np.array_equal(y[0].cpu().numpy(), np.asarray(OL["b_down"], np.float32))
+            else:
+                if tau < 1e-10:
+                    assert lt.size == cfg.ffn
+                y_ref, _ = oracle.ffn(OL, xh[t], mask_from_idx(lt, cfg.ffn))
+                assert normwise(y[0].cpu().numpy(), y_ref) <= TOL["f16"]
+        m.close()
