@@ -25,16 +25,20 @@
  *   output      y = b_down + sum_{i in A} h_i W_down_t[i]      (W_down stored transposed)
  *
  * Conventions shared by every entry point:
- *  - Every function returns an ffn_status; none throws, exits or prints.  On any error nothing
- *    has been enqueued and no output was touched; ffn_last_error() gives a message.
+ *  - Every function returns an ffn_status; none throws, exits or prints.  Arguments are checked
+ *    before anything is enqueued: on FFN_ERR_INVALID_ARGUMENT / FFN_ERR_UNSUPPORTED /
+ *    FFN_ERR_WORKSPACE_TOO_SMALL nothing was enqueued and no output was touched.  FFN_ERR_HIP
+ *    from a forward (a launch the runtime refused) can leave the kernels enqueued before it in
+ *    place; the outputs are then unspecified.  ffn_last_error() gives a message.
  *  - Pointers named "device" are HIP device pointers (hipMalloc / torch CUDA tensors); they stay
  *    owned by the caller and must outlive the plan that references them.  Every device pointer
  *    must be 16-byte aligned.
  *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).  Forward calls only
  *    enqueue work on it: they never allocate, never synchronise and never use memset nodes, so a
  *    caller may capture them in a HIP graph.
- *  - Shapes: d % 8 == 0 (d % 32 == 0 for int4), d <= 8192, ffn % 32 == 0, ffn <= 32768,
- *    rank % 8 == 0, rank <= 2048 (fp16 predictor) / 1024 (fp32 predictor), 1 <= B <= max_batch.  Anything else gives FFN_ERR_UNSUPPORTED or
+ *  - Shapes: d % 8 == 0 (d % 32 == 0 for int4), d <= 8192 (fp32 rows: d <= 4096),
+ *    ffn % 32 == 0, ffn <= 32768, rank % 8 == 0, rank <= 2048 (fp16 predictor) / 1024 (fp32
+ *    predictor), 1 <= B <= max_batch <= 4096.  Anything else gives FFN_ERR_UNSUPPORTED or
  *    FFN_ERR_INVALID_ARGUMENT.
  *  - A plan is not re-entrant: forward calls on one plan must be ordered (one stream).  Plans used
  *    one after another on one stream may share one workspace.
@@ -94,9 +98,11 @@ ffn_status ffn_workspace_size(const ffn_layer_desc *desc, size_t *bytes);
 /*
  * Validate desc and weights, lay out the caller's device workspace and return a plan.
  * `workspace` (device, >= ffn_workspace_size bytes) is owned by the caller and must outlive the
- * plan.  calibrate = 1 times the sparse path against the dense path over a density sweep on
- * `stream` (the only call that synchronises) and stores the crossover density per batch size
- * used by FFN_PATH_AUTO; calibrate = 0 keeps the built-in crossover table.
+ * plan.  calibrate = 1 (fp16 layers with max_batch >= 2) times the plan's dense path against
+ * its sparse path over a density sweep for B = 2, 4, ..., max_batch on `stream` and stores the
+ * crossover density per batch bucket used by FFN_PATH_AUTO; it is the only call that
+ * synchronises, and it allocates (and frees) its own scratch inputs.  calibrate = 0 keeps the
+ * built-in crossover table (1: never dense).
  */
 ffn_status ffn_sparse_plan(const ffn_layer_desc *desc, const ffn_layer_weights *weights,
                            void *workspace, size_t workspace_bytes, void *stream,
