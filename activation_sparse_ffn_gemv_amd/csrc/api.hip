@@ -357,7 +357,7 @@ ffn_status enqueue_token(const ffn_plan* p, const TokenBufs& wb, const void* xb,
   ra.cnt_out = cntb;
   ra.d = D.d;
   ra.ffn = D.ffn;
-  ra.n_part = fused ? fused_blocks(D.ffn) : gather_blocks();
+  ra.n_part = fused ? fused_blocks(D.ffn) : gather_blocks(slot ? nslot : 1);
   ra.fused = fused;
   ra.slot = slot;
   ra.nslot = nslot;

@@ -122,7 +122,8 @@ __global__ __launch_bounds__(64) void k_pred_z(const void* __restrict__ p1,
 constexpr int PS_THREADS = 256;
 constexpr int PS_MAXP = 8;
 
-template <int PK, int CPR>
+// MAXP: the passes the rank needs (1, 2, 4 or 8), so that no registers sit idle.
+template <int PK, int CPR, int MAXP>
 __global__ __launch_bounds__(PS_THREADS) void k_pred_s(PredArgs a) {
   constexpr int PE = Kind<PK>::EPC;           // predictor elements per 16-byte chunk
   __shared__ float s_score[32];
@@ -154,9 +155,9 @@ __global__ __launch_bounds__(PS_THREADS) void k_pred_s(PredArgs a) {
       zr[k][q] = c < pch ? v : f32x4{0.f, 0.f, 0.f, 0.f};
     }
   }
-  u32x4 w[PS_MAXP][CPR];
+  u32x4 w[MAXP][CPR];
 #pragma unroll
-  for (int p = 0; p < PS_MAXP; ++p) {
+  for (int p = 0; p < MAXP; ++p) {
     const int r = min(p * R + g, 31);
 #pragma unroll
     for (int k = 0; k < CPR; ++k) {
@@ -166,8 +167,8 @@ __global__ __launch_bounds__(PS_THREADS) void k_pred_s(PredArgs a) {
   }
   issue_fence();
 #pragma unroll
-  for (int p = 0; p < PS_MAXP; ++p) {
-    if (p >= P) break;
+  for (int p = 0; p < MAXP; ++p) {
+    if (p < P) {                              // uniform
     float acc = 0.0f;
 #pragma unroll
     for (int k = 0; k < CPR; ++k) {
@@ -191,6 +192,7 @@ __global__ __launch_bounds__(PS_THREADS) void k_pred_s(PredArgs a) {
     acc = group_sum_last(acc, L);
     const int r = p * R + g;
     if (gl == L - 1 && r < 32) s_score[r] = acc;
+    }
   }
   __syncthreads();
   if (tid < WAVE) {
@@ -506,7 +508,7 @@ __global__ __launch_bounds__(GA_THREADS) void k_gather(GatherArgs a) {
 #pragma unroll
           for (int e = 0; e < EPC; e += 4) {
             const int col = c * EPC + e;
-            float* dst = a.part + ((size_t)(col / RD_TW) * GA_BLOCKS + blockIdx.x) * RD_TW +
+            float* dst = a.part + ((size_t)(col / RD_TW) * gridDim.x + blockIdx.x) * RD_TW +
                          col % RD_TW;
             // streaming store: the partial is read once, by the next kernel
             __builtin_nontemporal_store(f32x4{acc[k][e], acc[k][e + 1], acc[k][e + 2], acc[k][e + 3]},
@@ -873,30 +875,35 @@ int pred_s_cpr(int p_f16, int rank) {
   return -1;
 }
 
-template <int PK, int CPR>
+template <int PK, int CPR, int MAXP>
 static hipError_t launch_pred_s_t(const PredArgs& a, hipStream_t st, hipEvent_t ev0,
                                   hipEvent_t ev1) {
+  const dim3 grid(a.ffn / 32, a.slot ? a.nslot : 1);
   if (ev0 && ev1)
-    hipExtLaunchKernelGGL((k_pred_s<PK, CPR>), dim3(a.ffn / 32, a.slot ? a.nslot : 1),
-                          dim3(PS_THREADS), 0, st, ev0, ev1, 0, a);
+    hipExtLaunchKernelGGL((k_pred_s<PK, CPR, MAXP>), grid, dim3(PS_THREADS), 0, st, ev0, ev1, 0,
+                          a);
   else
-    hipLaunchKernelGGL((k_pred_s<PK, CPR>), dim3(a.ffn / 32, a.slot ? a.nslot : 1),
-                       dim3(PS_THREADS), 0, st, a);
+    hipLaunchKernelGGL((k_pred_s<PK, CPR, MAXP>), grid, dim3(PS_THREADS), 0, st, a);
   return hipGetLastError();
 }
 
 hipError_t launch_pred_s(int p_f16, const PredArgs& a, hipStream_t st, hipEvent_t ev0,
                          hipEvent_t ev1) {
   const int cpr = pred_s_cpr(p_f16, a.rank);
+  const int pch = a.rank / (p_f16 ? 8 : 4);
+  int L = 64;
+  while (L > 4 && (L >> 1) >= pch) L >>= 1;
+  const int passes = (32 * L + PS_THREADS - 1) / PS_THREADS;     // 1, 2, 4 or 8
+#define PS_CASE(K, C, P) \
+  if (cpr == C && passes == P) return launch_pred_s_t<K, C, P>(a, st, ev0, ev1);
   if (p_f16) {
-    if (cpr == 1) return launch_pred_s_t<WK_F16, 1>(a, st, ev0, ev1);
-    if (cpr == 2) return launch_pred_s_t<WK_F16, 2>(a, st, ev0, ev1);
-    if (cpr == 4) return launch_pred_s_t<WK_F16, 4>(a, st, ev0, ev1);
+    PS_CASE(WK_F16, 1, 1) PS_CASE(WK_F16, 1, 2) PS_CASE(WK_F16, 1, 4) PS_CASE(WK_F16, 1, 8)
+    PS_CASE(WK_F16, 2, 8) PS_CASE(WK_F16, 4, 8)
   } else {
-    if (cpr == 1) return launch_pred_s_t<WK_F32, 1>(a, st, ev0, ev1);
-    if (cpr == 2) return launch_pred_s_t<WK_F32, 2>(a, st, ev0, ev1);
-    if (cpr == 4) return launch_pred_s_t<WK_F32, 4>(a, st, ev0, ev1);
+    PS_CASE(WK_F32, 1, 1) PS_CASE(WK_F32, 1, 2) PS_CASE(WK_F32, 1, 4) PS_CASE(WK_F32, 1, 8)
+    PS_CASE(WK_F32, 2, 8) PS_CASE(WK_F32, 4, 8)
   }
+#undef PS_CASE
   return hipErrorInvalidValue;
 }
 
@@ -920,7 +927,9 @@ int gather_cpt(int wk, int d) {
   const int tpr = GA_THREADS / gather_slots(nch);
   return (nch + tpr - 1) / tpr;
 }
-int gather_blocks() { return GA_BLOCKS; }
+// Workgroups per gather launch and slot: expert slots running side by side share the GPU's
+// one wave of resident workgroups.
+int gather_blocks(int nslot) { return GA_BLOCKS / (nslot < 1 ? 1 : nslot); }
 
 template <int WK, int CPT, int SLOTS>
 static hipError_t launch_gather_t(const GatherArgs& a, hipStream_t st, hipEvent_t ev0,
@@ -929,10 +938,12 @@ static hipError_t launch_gather_t(const GatherArgs& a, hipStream_t st, hipEvent_
   const size_t lds = SLOTS > 1 ? (size_t)(SLOTS - 1) * (GA_THREADS / SLOTS) * CPT *
                                      Kind<WK>::EPC * sizeof(float) : 0;
   if (ev0 && ev1)
-    hipExtLaunchKernelGGL((k_gather<WK, CPT, SLOTS>), dim3(GA_BLOCKS, a.slot ? a.nslot : 1),
+    hipExtLaunchKernelGGL((k_gather<WK, CPT, SLOTS>),
+                          dim3(gather_blocks(a.slot ? a.nslot : 1), a.slot ? a.nslot : 1),
                           dim3(GA_THREADS), lds, st, ev0, ev1, 0, a);
   else
-    hipLaunchKernelGGL((k_gather<WK, CPT, SLOTS>), dim3(GA_BLOCKS, a.slot ? a.nslot : 1),
+    hipLaunchKernelGGL((k_gather<WK, CPT, SLOTS>),
+                       dim3(gather_blocks(a.slot ? a.nslot : 1), a.slot ? a.nslot : 1),
                        dim3(GA_THREADS), lds, st, a);
   return hipGetLastError();
 }

@@ -110,7 +110,7 @@ hipError_t launch_pred_s(int p_f16, const PredArgs& a, hipStream_t st, hipEvent_
 hipError_t launch_mask_bits(const unsigned char* mask, uint32_t* bitmap, int words,
                             hipStream_t st);
 int gather_cpt(int wk, int d);
-int gather_blocks();
+int gather_blocks(int nslot = 1);
 int reduce_tiles(int d);
 hipError_t launch_gather(int wk, const GatherArgs& a, hipStream_t st, hipEvent_t ev0 = nullptr,
                          hipEvent_t ev1 = nullptr);
