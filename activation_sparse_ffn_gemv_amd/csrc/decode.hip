@@ -324,8 +324,9 @@ __global__ __launch_bounds__(GA_THREADS) void k_gather(GatherArgs a) {
   }
   const int run0 = base + v - local;           // rank of this thread's first active neuron
   if (blockIdx.x == 0 && tid == 0) *a.cnt = total;
-  const int r0 = (int)(((long long)total * blockIdx.x) / gridDim.x);
-  const int r1 = (int)(((long long)total * (blockIdx.x + 1)) / gridDim.x);
+  // 32-bit exact: |A| <= 32768 and at most 256 workgroups
+  const int r0 = (int)(((uint32_t)total * blockIdx.x) / gridDim.x);
+  const int r1 = (int)(((uint32_t)total * (blockIdx.x + 1)) / gridDim.x);
   FFN_TS(1, 1);
 
   float acc[CPT][EPC];
@@ -778,53 +779,67 @@ constexpr int RD_Q = RD_TW / 4;                        // float4 columns per til
 constexpr int RD_G = RD_THREADS / RD_Q;                // partial groups
 constexpr int RD_UNROLL = 4;                           // partials per thread in flight
 
+// MODE 0: one token, balanced gather (GA_BLOCKS partials, existence from |A| and the rank
+// split); MODE 1: one token, fused variant (existence from the bitmap words); MODE 2: expert
+// slots side by side (slot-major (slot, partial) items, routing-weighted).
+template <int MODE>
 __global__ __launch_bounds__(RD_THREADS) void k_reduce(ReduceArgs a) {
   __shared__ f32x4 s[RD_G][RD_Q];
   const int q = threadIdx.x % RD_Q;          // float4 column within the tile
-  const int g = threadIdx.x / RD_Q;          // partials g, g + RD_G, ...
+  const int g = threadIdx.x / RD_Q;          // items g, g + RD_G, ...
   const int tile = blockIdx.x;
   const int j = tile * RD_TW + threadIdx.x * 4;
   FFN_TS(2, 0);
-  const int nslot = a.slot ? a.nslot : 1;
-  f32x4 out = {0.f, 0.f, 0.f, 0.f};
-  for (int k = 0; k < nslot; ++k) {
-    const int total = a.cnt[(size_t)k * a.cstride];
-    const float* blk = a.part + (size_t)k * a.pstride + (size_t)tile * a.n_part * RD_TW;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int c0 = 0; c0 < a.n_part; c0 += RD_G * RD_UNROLL) {
-      f32x4 v[RD_UNROLL];
-      bool on[RD_UNROLL];
+  const int nslot = MODE == 2 ? a.nslot : 1;
+  const uint32_t np = MODE == 0 ? (uint32_t)GA_BLOCKS : (uint32_t)a.n_part;
+  const uint32_t items = (uint32_t)nslot * np;
+  const uint32_t total0 = MODE == 0 ? (uint32_t)a.cnt[0] : 0u;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (uint32_t i0 = 0; i0 < items; i0 += RD_G * RD_UNROLL) {
+    f32x4 v[RD_UNROLL];
+    float wt[RD_UNROLL];
 #pragma unroll
-      for (int u = 0; u < RD_UNROLL; ++u) {
-        const int c = c0 + g + u * RD_G;
-        // partial c exists iff its workgroup had an active neuron
-        if (a.fused)
-          on[u] = c < a.n_part && (a.bitmap[2 * c] | (2 * c + 1 < a.ffn / 32 ? a.bitmap[2 * c + 1] : 0u));
-        else
-          on[u] = c < a.n_part &&
-                  ((long long)total * (c + 1)) / a.n_part > ((long long)total * c) / a.n_part;
-        v[u] = *reinterpret_cast<const f32x4*>(blk + (size_t)min(c, a.n_part - 1) * RD_TW + q * 4);
+    for (int u = 0; u < RD_UNROLL; ++u) {
+      const uint32_t it = min(i0 + g + u * RD_G, items - 1);
+      const uint32_t k = MODE == 2 ? it / np : 0u;
+      const uint32_t c = it - k * np;
+      bool on;
+      if (MODE == 1) {
+        on = (a.bitmap[2 * c] | (2 * c + 1 < (uint32_t)a.ffn / 32 ? a.bitmap[2 * c + 1] : 0u)) != 0u;
+      } else {
+        // partial c exists iff gather workgroup c owned at least one rank (32-bit exact:
+        // |A| <= 32768 and c < 512)
+        const uint32_t total = MODE == 0 ? total0 : (uint32_t)a.cnt[(size_t)k * a.cstride];
+        on = (total * (c + 1)) / np > (total * c) / np;
       }
-      issue_fence();
-#pragma unroll
-      for (int u = 0; u < RD_UNROLL; ++u)
-        if (on[u]) acc += v[u];
+      on = on && i0 + g + u * RD_G < items;
+      wt[u] = on ? (MODE == 2 ? a.slot[k].wgt : 1.0f) : 0.0f;
+      v[u] = *reinterpret_cast<const f32x4*>(a.part + (size_t)k * a.pstride +
+                                             ((size_t)tile * np + c) * RD_TW + q * 4);
     }
-    __syncthreads();                         // s reused across slots
-    s[g][q] = acc;
-    __syncthreads();
-    if (threadIdx.x < RD_Q && j < a.d) {
-      const float* b_down = a.slot ? a.slot[k].b_down : a.b_down;
-      f32x4 t = s[0][threadIdx.x];
-#pragma unroll 8
-      for (int kk = 1; kk < RD_G; ++kk) t += s[kk][threadIdx.x];
-      if (b_down) t += *reinterpret_cast<const f32x4*>(b_down + j);
-      // expert slots of a mixture: weighted, summed in slot order
-      if (a.slot) out += a.slot[k].wgt * t;
-      else out = t;
+    issue_fence();
+#pragma unroll
+    for (int u = 0; u < RD_UNROLL; ++u) {
+      // partials that were not written hold stale bytes: skipped, never multiplied by 0
+      if (wt[u] != 0.0f) acc += MODE == 2 ? wt[u] * v[u] : v[u];
     }
   }
-  if (threadIdx.x < RD_Q && j < a.d) *reinterpret_cast<f32x4*>(a.y + j) = out;
+  s[g][q] = acc;
+  __syncthreads();
+  if (threadIdx.x < RD_Q && j < a.d) {
+    f32x4 t = s[0][threadIdx.x];
+#pragma unroll 8
+    for (int kk = 1; kk < RD_G; ++kk) t += s[kk][threadIdx.x];
+    // b_down (of each expert slot, routing-weighted)
+    for (int k = 0; k < nslot; ++k) {
+      const float* b_down = MODE == 2 ? a.slot[k].b_down : a.b_down;
+      if (b_down) {
+        const f32x4 b = *reinterpret_cast<const f32x4*>(b_down + j);
+        t += MODE == 2 ? a.slot[k].wgt * b : b;
+      }
+    }
+    *reinterpret_cast<f32x4*>(a.y + j) = t;
+  }
   if (blockIdx.x == 0 && (a.idx_out || a.cnt_out))
     write_index_list<RD_THREADS>(a.bitmap, a.ffn / 32, a.idx_out, a.cnt_out);
   FFN_TS(2, 5);
@@ -1011,10 +1026,12 @@ hipError_t launch_fused(int wk, const FusedArgs& a, hipStream_t st, hipEvent_t e
 
 hipError_t launch_reduce(const ReduceArgs& a, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
   const dim3 grid(reduce_tiles(a.d)), block(RD_THREADS);
+  auto kern = a.slot ? k_reduce<2> : a.fused ? k_reduce<1> : k_reduce<0>;
+  if (!a.slot && !a.fused && a.n_part != GA_BLOCKS) return hipErrorInvalidValue;
   if (ev0 && ev1)
-    hipExtLaunchKernelGGL(k_reduce, grid, block, 0, st, ev0, ev1, 0, a);
+    hipExtLaunchKernelGGL(kern, grid, block, 0, st, ev0, ev1, 0, a);
   else
-    hipLaunchKernelGGL(k_reduce, grid, block, 0, st, a);
+    hipLaunchKernelGGL(kern, grid, block, 0, st, a);
   return hipGetLastError();
 }
 
