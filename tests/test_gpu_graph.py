@@ -1,0 +1,86 @@
+"""The forward calls only enqueue work (no allocation, no synchronisation, no memset nodes), so a
+caller can capture them in a HIP graph: every path is captured once and replayed several times,
+with eager work and synchronisations in between, and every replay must equal the eager result
+bit for bit."""
+import pytest
+import torch
+
+import synth
+from parity import to_device
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ffn():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import activation_sparse_ffn_gemv_amd as m
+    return m
+
+
+def _replays_match(run, out, n=3):
+    """run() enqueues on the current stream and writes `out`; compare graph replays to eager."""
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        run()
+    torch.cuda.synchronize()
+    ref = out.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            run()
+    torch.cuda.synchronize()
+    for rep in range(n):
+        out.fill_(float("nan"))
+        junk = torch.randn(1 << 20, device="cuda").sum()     # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), "replay %d differs" % rep
+        del junk
+
+
+@pytest.mark.parametrize("wd,B,path", [("f16", 1, "sparse"), ("f16", 5, "sparse"),
+                                       ("f16", 70, "auto"), ("f16", 70, "dense"),
+                                       ("i4g32", 1, "sparse"), ("f32", 2, "sparse")])
+def test_forward_in_a_graph(ffn, wd, B, path):
+    xd = "f32" if wd == "f32" else "f16"
+    cfg = synth.small_config(d=512, ffn=2048, rank=64, act="reglu", w_dtype=wd, x_dtype=xd,
+                             p_dtype=xd, density=0.1, bias_gate=True, bias_down=True)
+    L = to_device(synth.make_layer(cfg))
+    x = synth.make_tokens(cfg, B).cuda()
+    m = ffn.SparseFFN(L, max_batch=B)
+    if path == "auto":
+        ffn.ffn_plan_set_crossover(m.plan, B, 0.3)        # let the device choose the dense rows
+    y = torch.zeros(B, cfg.d, device="cuda")
+    idx = torch.zeros(B, cfg.ffn, dtype=torch.int32, device="cuda")
+    cnt = torch.zeros(B, dtype=torch.int32, device="cuda")
+    p = {"sparse": ffn.FFN_PATH_SPARSE, "auto": ffn.FFN_PATH_AUTO,
+         "dense": ffn.FFN_PATH_DENSE}[path]
+    _replays_match(lambda: m.forward(x, y=y, idx=idx, cnt=cnt, path=p), y)
+    m.close()
+
+
+def test_mixture_in_a_graph(ffn):
+    cfg = synth.small_config(d=256, ffn=1024, rank=32, act="drelu", w_dtype="i4g32",
+                             x_dtype="f16", p_dtype="f16", density=0.1, bias_gate=True,
+                             bias_up=True)
+    experts = [to_device(synth.make_layer(cfg, expert=e)) for e in range(4)]
+    R = synth.make_router(synth.with_(cfg, n_experts=4), device="cuda")
+    x = synth.make_tokens(cfg, 3).cuda()
+    moe = ffn.MoEFFN(experts, R, top_k=2, max_batch=3)
+    y = torch.zeros(3, cfg.d, device="cuda")
+    _replays_match(lambda: moe.forward(x, y=y), y)
+    moe.close()
+
+
+def test_dense_forward_in_a_graph(ffn):
+    cfg = synth.small_config(d=256, ffn=1024, rank=32, act="relu", w_dtype="f16",
+                             x_dtype="f16", p_dtype="f16", density=0.1, bias_up=True)
+    L = to_device(synth.make_layer(cfg))
+    x = synth.make_tokens(cfg, 96).cuda()
+    m = ffn.SparseFFN(L, max_batch=96)
+    y = torch.zeros(96, cfg.d, device="cuda")
+    _replays_match(lambda: m.dense(x, y=y), y)
+    m.close()
