@@ -261,8 +261,11 @@ __global__ __launch_bounds__(BT) void k_bug(BatchArgs a) {
   constexpr int LPT = 32 * UG_KC / BT;    // chunk loads per thread and matrix per stage
   __shared__ int s_wsum[BT / WAVE];
   __shared__ int s_nid[32];
-  __shared__ float red[3 * 16 * WAVE];
+  // the row stages; after the last stage the same bytes hold the waves' sums (keeping the LDS
+  // per workgroup small enough for four resident workgroups per CU)
   __shared__ u32x4 s_w[2][NMAT][32 * UG_LD];
+  static_assert(sizeof(s_w) >= 3 * 16 * WAVE * sizeof(float), "sums fit in the stage buffers");
+  float* red = reinterpret_cast<float*>(&s_w[0][0][0]);
   if (a.run_if && *a.run_if != a.run_want) return;
   const int tid = threadIdx.x, lane = tid & (WAVE - 1), wave = tid / WAVE;
   const int W = a.ffn / 32;
@@ -362,18 +365,22 @@ __global__ __launch_bounds__(BT) void k_bug(BatchArgs a) {
     }
   };
 
+  // loads two stages ahead: (wr1, xn1) hold stage st+1, (wr2, xn2) receive stage st+2
   f32x16 au = {}, ag = {};
-  u32x4 wr[NMAT][LPT], xv[SPW], xn[SPW];
-  load_w(0, wr);
+  u32x4 wr1[NMAT][LPT], wr2[NMAT][LPT], xv[SPW], xn1[SPW], xn2[SPW];
+  load_w(0, wr1);
   load_x(0, xv);
-  store_w(0, wr);
+  store_w(0, wr1);
+  if (nstage > 1) {
+    load_w(1, wr1);
+    load_x(1, xn1);
+  }
   __syncthreads();
   for (int st = 0; st < nstage; ++st) {
     const int buf = st & 1;
-    const bool more = st + 1 < nstage;
-    if (more) {
-      load_w(st + 1, wr);
-      load_x(st + 1, xn);
+    if (st + 2 < nstage) {
+      load_w(st + 2, wr2);
+      load_x(st + 2, xn2);
     }
 #pragma unroll
     for (int j = 0; j < SPW; ++j) {
@@ -381,10 +388,15 @@ __global__ __launch_bounds__(BT) void k_bug(BatchArgs a) {
       au = mma16(xv[j], s_w[buf][0][idx], au);
       if constexpr (GATE) ag = mma16(xv[j], s_w[buf][NMAT - 1][idx], ag);
     }
-    if (more) {
-      store_w(buf ^ 1, wr);
+    if (st + 1 < nstage) store_w(buf ^ 1, wr1);
 #pragma unroll
-      for (int j = 0; j < SPW; ++j) xv[j] = xn[j];
+    for (int mt = 0; mt < NMAT; ++mt)
+#pragma unroll
+      for (int i = 0; i < LPT; ++i) wr1[mt][i] = wr2[mt][i];
+#pragma unroll
+    for (int j = 0; j < SPW; ++j) {
+      xv[j] = xn1[j];
+      xn1[j] = xn2[j];
     }
     __syncthreads();
   }
