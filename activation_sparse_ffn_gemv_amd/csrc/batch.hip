@@ -248,22 +248,25 @@ __global__ __launch_bounds__(1024) void k_dchoice(const uint32_t* __restrict__ b
   if (w == 0) *flag = s_total > dense_above ? 1 : 0;
 }
 
-// Rows of 32 union neurons (ranks [32 b, 32 b + 32)): u, g on the MFMA units, then h.
+// Rows of NN union neurons (ranks [NN b, NN b + NN)): u, g on the MFMA units, then h.
 // The rows stream through LDS in stages of UG_KC 16-byte chunks (a wave's load instruction
 // covers two rows' 512 contiguous bytes), double-buffered; the waves split each stage's K
 // between them for the MFMAs, and their 32x32 sums are added in wave order at the end.
 constexpr int UG_KC = 32;                 // chunks per row per stage (256 k)
 constexpr int UG_LD = UG_KC + 1;          // padded LDS row
+constexpr int UG_WIDE_B = 16;             // ReLU batches above this take 64 neurons per workgroup
 
-template <bool GATE>
+// NN = 32 or 64 neurons per workgroup (64: each token slice read from L2 serves twice the rows).
+template <bool GATE, int NN>
 __global__ __launch_bounds__(BT) void k_bug(BatchArgs a) {
   constexpr int NMAT = GATE ? 2 : 1;
-  constexpr int LPT = 32 * UG_KC / BT;    // chunk loads per thread and matrix per stage
+  constexpr int NTL = NN / 32;            // 32-neuron MFMA tiles
+  constexpr int LPT = NN * UG_KC / BT;    // chunk loads per thread and matrix per stage
   __shared__ int s_wsum[BT / WAVE];
-  __shared__ int s_nid[32];
+  __shared__ int s_nid[NN];
   // the row stages; after the last stage the same bytes hold the waves' sums (keeping the LDS
   // per workgroup small enough for four resident workgroups per CU)
-  __shared__ u32x4 s_w[2][NMAT][32 * UG_LD];
+  __shared__ u32x4 s_w[2][NMAT][NN * UG_LD];
   static_assert(sizeof(s_w) >= 3 * 16 * WAVE * sizeof(float), "sums fit in the stage buffers");
   float* red = reinterpret_cast<float*>(&s_w[0][0][0]);
   if (a.run_if && *a.run_if != a.run_want) return;
@@ -286,7 +289,7 @@ __global__ __launch_bounds__(BT) void k_bug(BatchArgs a) {
     if (lane >= o) v += u;
   }
   if (lane == WAVE - 1) s_wsum[wave] = v;
-  if (tid < 32) s_nid[tid] = -1;
+  if (tid < NN) s_nid[tid] = -1;
   __syncthreads();
   int base = 0, total = 0;
 #pragma unroll
@@ -295,17 +298,17 @@ __global__ __launch_bounds__(BT) void k_bug(BatchArgs a) {
     total += s_wsum[k];
   }
   if (blockIdx.x == 0 && tid == 0) *a.ucnt = total;
-  const int t0 = blockIdx.x * 32;
+  const int t0 = blockIdx.x * NN;
   if (t0 >= total) return;                              // uniform over the workgroup
   const int run0 = base + v - local;
-  if (run0 < t0 + 32 && run0 + local > t0) {
+  if (run0 < t0 + NN && run0 + local > t0) {
     int pos = run0;
 #pragma unroll
     for (int k = 0; k < WPT; ++k) {
       uint32_t bb = bw[k];
       const int nb = (tid * WPT + k) * 32;
       while (bb) {
-        if (pos >= t0 && pos < t0 + 32) {
+        if (pos >= t0 && pos < t0 + NN) {
           const int nid = nb + __builtin_ctz(bb);
           s_nid[pos - t0] = nid;
           a.uidx[pos] = nid;
@@ -317,9 +320,8 @@ __global__ __launch_bounds__(BT) void k_bug(BatchArgs a) {
   }
   __syncthreads();
 
-  // 2. U = X W_up^T and G = X W_gate^T for the 32 neurons
+  // 2. U = X W_up^T and G = X W_gate^T for the NN neurons
   const int row = lane & 31, g = lane >> 5;
-  const int nid = s_nid[row];
   const int nchk = a.d / 8;
   const int nstage = (nchk + UG_KC - 1) / UG_KC;
   // cooperative row loads: element e = tid + BT * i -> (row e / UG_KC, chunk e % UG_KC)
@@ -366,7 +368,9 @@ __global__ __launch_bounds__(BT) void k_bug(BatchArgs a) {
   };
 
   // loads two stages ahead: (wr1, xn1) hold stage st+1, (wr2, xn2) receive stage st+2
-  f32x16 au = {}, ag = {};
+  f32x16 au[NTL], ag[NTL];
+#pragma unroll
+  for (int t = 0; t < NTL; ++t) au[t] = ag[t] = f32x16{};
   u32x4 wr1[NMAT][LPT], wr2[NMAT][LPT], xv[SPW], xn1[SPW], xn2[SPW];
   load_w(0, wr1);
   load_x(0, xv);
@@ -383,11 +387,13 @@ __global__ __launch_bounds__(BT) void k_bug(BatchArgs a) {
       load_x(st + 2, xn2);
     }
 #pragma unroll
-    for (int j = 0; j < SPW; ++j) {
-      const int idx = row * UG_LD + 2 * (wave * SPW + j) + g;
-      au = mma16(xv[j], s_w[buf][0][idx], au);
-      if constexpr (GATE) ag = mma16(xv[j], s_w[buf][NMAT - 1][idx], ag);
-    }
+    for (int j = 0; j < SPW; ++j)
+#pragma unroll
+      for (int t = 0; t < NTL; ++t) {
+        const int idx = (t * 32 + row) * UG_LD + 2 * (wave * SPW + j) + g;
+        au[t] = mma16(xv[j], s_w[buf][0][idx], au[t]);
+        if constexpr (GATE) ag[t] = mma16(xv[j], s_w[buf][NMAT - 1][idx], ag[t]);
+      }
     if (st + 1 < nstage) store_w(buf ^ 1, wr1);
 #pragma unroll
     for (int mt = 0; mt < NMAT; ++mt)
@@ -400,27 +406,34 @@ __global__ __launch_bounds__(BT) void k_bug(BatchArgs a) {
     }
     __syncthreads();
   }
-  au = wg_sum4(au, red);
-  if constexpr (GATE) ag = wg_sum4(ag, red);
+#pragma unroll
+  for (int t = 0; t < NTL; ++t) {
+    au[t] = wg_sum4(au[t], red);
+    if constexpr (GATE) ag[t] = wg_sum4(ag[t], red);
+  }
 
   // 3. h per (token, neuron), masked by the token's own set; H column = union rank
   if (wave == 0) {
-    const float bu = (nid >= 0 && a.b_up) ? a.b_up[nid] : 0.0f;
-    const float bg = (nid >= 0 && a.b_gate) ? a.b_gate[nid] : 0.0f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int m = acc_row(i, lane);
-      const float u = au[i] + bu;
-      float h;
-      if constexpr (!GATE) {
-        h = fmaxf(u, 0.0f);
-      } else {
-        const float gg = fmaxf(ag[i] + bg, 0.0f);
-        h = a.act == FFN_ACT_REGLU ? gg * u : gg * fmaxf(u, 0.0f);
+    for (int t = 0; t < NTL; ++t) {
+      const int nid = s_nid[t * 32 + row];
+      const float bu = (nid >= 0 && a.b_up) ? a.b_up[nid] : 0.0f;
+      const float bg = (nid >= 0 && a.b_gate) ? a.b_gate[nid] : 0.0f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int m = acc_row(i, lane);
+        const float u = au[t][i] + bu;
+        float h;
+        if constexpr (!GATE) {
+          h = fmaxf(u, 0.0f);
+        } else {
+          const float gg = fmaxf(ag[t][i] + bg, 0.0f);
+          h = a.act == FFN_ACT_REGLU ? gg * u : gg * fmaxf(u, 0.0f);
+        }
+        bool on = false;
+        if (nid >= 0 && m < a.B) on = (a.bits[(size_t)m * W + (nid >> 5)] >> (nid & 31)) & 1u;
+        if (t0 + t * 32 + row < a.ffn) a.H[(size_t)m * a.ffn + t0 + t * 32 + row] = (_Float16)(on ? h : 0.0f);
       }
-      bool on = false;
-      if (nid >= 0 && m < a.B) on = (a.bits[(size_t)m * W + (nid >> 5)] >> (nid & 31)) & 1u;
-      a.H[(size_t)m * a.ffn + t0 + row] = (_Float16)(on ? h : 0.0f);
     }
   }
 }
@@ -571,16 +584,25 @@ hipError_t launch_batch_rows(const BatchArgs& a, int choose_path, hipStream_t st
                              hipEvent_t (*ev)[2]) {
   const int W = a.ffn / 32;
   if (choose_path) hipLaunchKernelGGL(k_bpath, dim3(1), dim3(1024), 0, st, a);
+  // ReLU layers at larger batches take 64 union neurons per workgroup: each token slice then
+  // serves twice the rows (at small batches the union is too small to fill the chip that way,
+  // and the gate's second tile would not fit the LDS of several resident workgroups)
   if (a.has_gate) {
     if (ev && ev[0][0])
-      hipExtLaunchKernelGGL(k_bug<true>, dim3(W), dim3(BT), 0, st, ev[0][0], ev[0][1], 0, a);
+      hipExtLaunchKernelGGL((k_bug<true, 32>), dim3(W), dim3(BT), 0, st, ev[0][0], ev[0][1], 0, a);
     else
-      hipLaunchKernelGGL(k_bug<true>, dim3(W), dim3(BT), 0, st, a);
+      hipLaunchKernelGGL((k_bug<true, 32>), dim3(W), dim3(BT), 0, st, a);
+  } else if (a.B > UG_WIDE_B) {
+    const dim3 g2((W + 1) / 2);
+    if (ev && ev[0][0])
+      hipExtLaunchKernelGGL((k_bug<false, 64>), g2, dim3(BT), 0, st, ev[0][0], ev[0][1], 0, a);
+    else
+      hipLaunchKernelGGL((k_bug<false, 64>), g2, dim3(BT), 0, st, a);
   } else {
     if (ev && ev[0][0])
-      hipExtLaunchKernelGGL(k_bug<false>, dim3(W), dim3(BT), 0, st, ev[0][0], ev[0][1], 0, a);
+      hipExtLaunchKernelGGL((k_bug<false, 32>), dim3(W), dim3(BT), 0, st, ev[0][0], ev[0][1], 0, a);
     else
-      hipLaunchKernelGGL(k_bug<false>, dim3(W), dim3(BT), 0, st, a);
+      hipLaunchKernelGGL((k_bug<false, 32>), dim3(W), dim3(BT), 0, st, a);
   }
   const dim3 gd((a.d + DN_COLS - 1) / DN_COLS, a.S);
   if (ev && ev[1][0])

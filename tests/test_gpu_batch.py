@@ -61,6 +61,7 @@ BATCH_SHAPES = [
     dict(d=1024, ffn=4128, rank=128, act="reglu", bias_gate=True),
     dict(d=520, ffn=1184, rank=40, act="drelu", bias_gate=True, bias_up=True, bias_down=True),
     dict(d=136, ffn=1056, rank=24, act="reglu", bias_gate=True),
+    dict(d=264, ffn=1056, rank=24, act="relu", bias_up=True),      # odd number of 32-row tiles
 ]
 
 
