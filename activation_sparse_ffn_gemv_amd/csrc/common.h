@@ -27,7 +27,8 @@ constexpr int WAVE = 64;
 
 // Optional timeline trace (builds with -DFFN_TRACE only): thread 0 of every workgroup stores the
 // 100 MHz real-time counter at a few points of a kernel into trace[(kernel * 4096 + block) * 8 +
-// point].  The buffer is set with ffn_trace_set_buffer (declared in the trace build only).
+// point] (kernel 0 predictor stage 1, 3 stage 2, 1 gather, 2 reduce).  The buffer is set with
+// ffn_trace_set_buffer (declared in the trace build only).
 #ifdef FFN_TRACE
 extern __device__ unsigned long long* g_trace;
 #define FFN_TS(K, PH)                                                                          \

@@ -135,7 +135,7 @@ __global__ __launch_bounds__(PS_THREADS) void k_pred_s(PredArgs a) {
   const int P = (32 + R - 1) / R;             // passes (<= 8)
   const int g = tid / L, gl = tid % L;
   const int i0 = blockIdx.x * 32;
-  FFN_TS(1, 0);
+  FFN_TS(3, 0);
   if (a.slot) {
     a.slot += blockIdx.y;                       // expert slots side by side
     a.z += (size_t)blockIdx.y * a.zstride;
@@ -205,7 +205,7 @@ __global__ __launch_bounds__(PS_THREADS) void k_pred_s(PredArgs a) {
     const unsigned long long bal = __ballot(on);
     if (tid == 0) a.bitmap[blockIdx.x] = (uint32_t)bal;
   }
-  FFN_TS(1, 5);
+  FFN_TS(3, 5);
 }
 
 // Caller-supplied mask -> bitmap: one wave builds two 32-bit words.  mask == nullptr sets every
@@ -323,7 +323,6 @@ __global__ __launch_bounds__(GA_THREADS) void k_gather(GatherArgs a) {
     total += s_wsum[k];
   }
   const int run0 = base + v - local;           // rank of this thread's first active neuron
-  if (blockIdx.x == 0 && tid == 0) *a.cnt = total;
   // 32-bit exact: |A| <= 32768 and at most 256 workgroups
   const int r0 = (int)(((uint32_t)total * blockIdx.x) / gridDim.x);
   const int r1 = (int)(((uint32_t)total * (blockIdx.x + 1)) / gridDim.x);
@@ -519,6 +518,8 @@ __global__ __launch_bounds__(GA_THREADS) void k_gather(GatherArgs a) {
       }
     }
   }
+  // stored last: a store ahead of a barrier would hold this workgroup at the barrier
+  if (blockIdx.x == 0 && tid == 0) *a.cnt = total;
   FFN_TRACE_SYNC();
   FFN_TS(1, 5);
   FFN_TV(1, 6, r1 - r0);
@@ -784,13 +785,25 @@ constexpr int RD_UNROLL = 4;                           // partials per thread in
 // slots side by side (slot-major (slot, partial) items, routing-weighted).
 template <int MODE>
 __global__ __launch_bounds__(RD_THREADS) void k_reduce(ReduceArgs a) {
-  __shared__ f32x4 s[RD_G][RD_Q];
+  __shared__ f32x4 s[RD_THREADS / WAVE][RD_Q];
   const int q = threadIdx.x % RD_Q;          // float4 column within the tile
   const int g = threadIdx.x / RD_Q;          // items g, g + RD_G, ...
+  const int lane = threadIdx.x & (WAVE - 1), wave = threadIdx.x / WAVE;
   const int tile = blockIdx.x;
-  const int j = tile * RD_TW + threadIdx.x * 4;
+  const int j = tile * RD_TW + q * 4;
   FFN_TS(2, 0);
   const int nslot = MODE == 2 ? a.nslot : 1;
+  // b_down (of each expert slot, routing-weighted), fetched with the partials
+  f32x4 bias = {0.f, 0.f, 0.f, 0.f};
+  if (threadIdx.x < RD_Q && j < a.d) {
+    for (int k = 0; k < nslot; ++k) {
+      const float* b_down = MODE == 2 ? a.slot[k].b_down : a.b_down;
+      if (b_down) {
+        const f32x4 b = *reinterpret_cast<const f32x4*>(b_down + j);
+        bias += MODE == 2 ? a.slot[k].wgt * b : b;
+      }
+    }
+  }
   const uint32_t np = MODE == 0 ? (uint32_t)GA_BLOCKS : (uint32_t)a.n_part;
   const uint32_t items = (uint32_t)nslot * np;
   const uint32_t total0 = MODE == 0 ? (uint32_t)a.cnt[0] : 0u;
@@ -824,21 +837,22 @@ __global__ __launch_bounds__(RD_THREADS) void k_reduce(ReduceArgs a) {
       if (wt[u] != 0.0f) acc += MODE == 2 ? wt[u] * v[u] : v[u];
     }
   }
-  s[g][q] = acc;
+  // fixed-order tree over the groups: within each wave by lane exchange (lane = 4 g' + q), then
+  // the waves' sums through LDS
+#pragma unroll
+  for (int o = RD_Q; o < WAVE; o <<= 1) {
+    acc.x += __shfl_xor(acc.x, o, WAVE);
+    acc.y += __shfl_xor(acc.y, o, WAVE);
+    acc.z += __shfl_xor(acc.z, o, WAVE);
+    acc.w += __shfl_xor(acc.w, o, WAVE);
+  }
+  if (lane < RD_Q) s[wave][lane] = acc;
   __syncthreads();
   if (threadIdx.x < RD_Q && j < a.d) {
-    f32x4 t = s[0][threadIdx.x];
-#pragma unroll 8
-    for (int kk = 1; kk < RD_G; ++kk) t += s[kk][threadIdx.x];
-    // b_down (of each expert slot, routing-weighted)
-    for (int k = 0; k < nslot; ++k) {
-      const float* b_down = MODE == 2 ? a.slot[k].b_down : a.b_down;
-      if (b_down) {
-        const f32x4 b = *reinterpret_cast<const f32x4*>(b_down + j);
-        t += MODE == 2 ? a.slot[k].wgt * b : b;
-      }
-    }
-    *reinterpret_cast<f32x4*>(a.y + j) = t;
+    f32x4 t = s[0][q];
+#pragma unroll
+    for (int w = 1; w < RD_THREADS / WAVE; ++w) t += s[w][q];
+    *reinterpret_cast<f32x4*>(a.y + j) = t + bias;
   }
   if (blockIdx.x == 0 && (a.idx_out || a.cnt_out))
     write_index_list<RD_THREADS>(a.bitmap, a.ffn / 32, a.idx_out, a.cnt_out);
