@@ -70,10 +70,11 @@ __device__ __forceinline__ f32x16 wg_sum4(f32x16 acc, float* red /* [3][16][64] 
 }
 
 // Union ranks [r0, r1) of segment s: segments are cut at multiples of 8 ranks (one x8 step).
+// 32-bit exact: total <= 32768 (so units <= 4096) and s + 1 <= S <= 64.
 __device__ __forceinline__ void seg_range(int total, int s, int S, int& r0, int& r1) {
-  const long long units = (total + 7) / 8;
-  r0 = (int)(8 * (units * s / S));
-  r1 = (int)(8 * (units * (s + 1) / S));
+  const uint32_t units = ((uint32_t)total + 7u) / 8u;
+  r0 = (int)(8u * (units * (uint32_t)s / (uint32_t)S));
+  r1 = (int)(8u * (units * (uint32_t)(s + 1) / (uint32_t)S));
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -119,7 +120,16 @@ __global__ __launch_bounds__(256) void k_bzr(BatchArgs a) {
   if (e >= MB * a.r) return;
   const int k = e % a.r;
   float z = 0.0f;
-  for (int q = 0; q < a.ks; ++q) z += a.zpart[(size_t)q * MB * a.r + e];
+  // split-K slices in order, eight loads in flight at a time
+  for (int q0 = 0; q0 < a.ks; q0 += 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      v[u] = q0 + u < a.ks ? a.zpart[(size_t)(q0 + u) * MB * a.r + e] : 0.0f;
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (q0 + u < a.ks) z += v[u];
+  }
   if (a.c1) z += a.c1[k];
   const _Float16 hi = (_Float16)z;
   const _Float16 lo = (_Float16)(z - (float)hi);
@@ -529,12 +539,23 @@ __global__ __launch_bounds__(256) void k_bred(BatchArgs a) {
   const int total = *a.ucnt;
   if (col < a.d) {
     f32x4 t = {0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < a.S; ++s) {
-      int r0, r1;
-      seg_range(total, s, a.S, r0, r1);
-      if (r0 < r1) t += *reinterpret_cast<const f32x4*>(a.ypart + ((size_t)s * MB + m) * a.d + col);
+    const f32x4 bd = a.b_down ? *reinterpret_cast<const f32x4*>(a.b_down + col) : t;
+    // segments in order, eight loads in flight at a time; empty segments were not written
+    for (int s0 = 0; s0 < a.S; s0 += 8) {
+      f32x4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int s = min(s0 + u, a.S - 1);
+        v[u] = *reinterpret_cast<const f32x4*>(a.ypart + ((size_t)s * MB + m) * a.d + col);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        int r0, r1;
+        seg_range(total, s0 + u, a.S, r0, r1);
+        if (s0 + u < a.S && r0 < r1) t += v[u];
+      }
     }
-    if (a.b_down) t += *reinterpret_cast<const f32x4*>(a.b_down + col);
+    if (a.b_down) t += bd;
     *reinterpret_cast<f32x4*>(a.y + (size_t)m * a.d + col) = t;
   }
   if (blockIdx.x == 0 && (a.idx_out || a.cnt_out))

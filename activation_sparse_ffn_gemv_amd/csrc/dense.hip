@@ -339,9 +339,19 @@ __global__ __launch_bounds__(256) void k_dred(DenseArgs a) {
   const size_t e = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4;     // m * d + col
   if (e >= (size_t)a.M * a.d) return;
   const int col = (int)(e % a.d);
+  const f32x4 bd = a.b_down ? *reinterpret_cast<const f32x4*>(a.b_down + col) : f32x4{0.f, 0.f, 0.f, 0.f};
   f32x4 t = *reinterpret_cast<const f32x4*>(a.ypart + e);
-  for (int k = 1; k < a.ks; ++k) t += *reinterpret_cast<const f32x4*>(a.ypart + (size_t)k * a.M * a.d + e);
-  if (a.b_down) t += *reinterpret_cast<const f32x4*>(a.b_down + col);
+  // K slices in order, eight loads in flight at a time
+  for (int k0 = 1; k0 < a.ks; k0 += 8) {
+    f32x4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      v[u] = *reinterpret_cast<const f32x4*>(a.ypart + (size_t)min(k0 + u, a.ks - 1) * a.M * a.d + e);
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (k0 + u < a.ks) t += v[u];
+  }
+  if (a.b_down) t += bd;
   *reinterpret_cast<f32x4*>(a.y + e) = t;
 }
 
