@@ -3,7 +3,7 @@
 // top-K experts by the logits l_e = R[e] . x, ties going to the lower expert index, and weighs
 // them by the softmax over the chosen logits.
 //
-// One workgroup per token.  The routing decision never leaves the device: the workgroup copies
+// One workgroup of eight waves per token.  The routing decision never leaves the device: the workgroup copies
 // the chosen experts' weight records (from the table passed by value in the kernel arguments)
 // into per-slot records in the workspace, and the expert kernels that follow take their weight
 // pointers from those records.
@@ -12,8 +12,10 @@
 
 namespace ffn {
 
-constexpr int RT_THREADS = 256;
+constexpr int RT_THREADS = 512;
 constexpr int RT_NW = RT_THREADS / WAVE;
+constexpr int RT_EPW = (MOE_MAX_E + RT_NW - 1) / RT_NW;   // experts per wave
+constexpr int RT_CPL = 8;                                  // chunks per lane in flight
 
 template <int XK>
 __global__ __launch_bounds__(RT_THREADS) void k_router(RouterArgs a) {
@@ -27,18 +29,38 @@ __global__ __launch_bounds__(RT_THREADS) void k_router(RouterArgs a) {
   const char* xb = static_cast<const char*>(a.x) + (size_t)b * nch * 16;
   const char* R = static_cast<const char*>(a.R);
 
-  // logits: wave w takes experts w, w + RT_NW, ...; lanes split the row in 16-byte chunks
-  for (int e = wave; e < a.E; e += RT_NW) {
-    float acc = 0.0f;
-#pragma unroll 4
-    for (int c = lane; c < nch; c += WAVE) {
-      const u32x4 w = ld16(R + ((size_t)e * nch + c) * 16);
-      const u32x4 xv = ld16(xb + (size_t)c * 16);
-      if constexpr (XK == WK_F16) acc = dot8_f16(w, xv, acc);
-      else acc = dot4_f32(w, xv, acc);
+  // logits: wave w takes experts w and w + RT_NW; lanes split the rows in 16-byte chunks, and a
+  // lane's chunks of the token and of both rows are requested together (one round trip at
+  // d = 4096 fp16)
+  float acc[RT_EPW] = {};
+  for (int c0 = 0; c0 < nch; c0 += RT_CPL * WAVE) {
+    u32x4 xv[RT_CPL], w[RT_EPW][RT_CPL];
+#pragma unroll
+    for (int k = 0; k < RT_CPL; ++k) {
+      const int c = min(c0 + lane + k * WAVE, nch - 1);
+      xv[k] = ld16(xb + (size_t)c * 16);
+#pragma unroll
+      for (int j = 0; j < RT_EPW; ++j) {
+        const int e = min(wave + j * RT_NW, a.E - 1);
+        w[j][k] = ld16(R + ((size_t)e * nch + c) * 16);
+      }
     }
-    acc = wave_sum(acc);
-    if (lane == 0) s_logit[e] = acc;
+    issue_fence();
+#pragma unroll
+    for (int k = 0; k < RT_CPL; ++k) {
+      if (c0 + lane + k * WAVE < nch) {
+#pragma unroll
+        for (int j = 0; j < RT_EPW; ++j) {
+          if constexpr (XK == WK_F16) acc[j] = dot8_f16(w[j][k], xv[k], acc[j]);
+          else acc[j] = dot4_f32(w[j][k], xv[k], acc[j]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < RT_EPW; ++j) {
+    const float l = wave_sum(acc[j]);
+    if (lane == 0 && wave + j * RT_NW < a.E) s_logit[wave + j * RT_NW] = l;
   }
   __syncthreads();
 
