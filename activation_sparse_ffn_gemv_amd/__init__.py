@@ -37,7 +37,7 @@ DTYPE = {"f32": FFN_F32, "f16": FFN_F16, "i4g32": FFN_I4G32}
 EXPORTS = [
     "ffn_workspace_size", "ffn_sparse_plan", "ffn_sparse_forward", "ffn_dense_forward",
     "ffn_plan_crossover", "ffn_plan_set_crossover", "ffn_plan_set_decode_variant",
-    "ffn_plan_destroy", "ffn_plan_set_timing_events", "ffn_last_error",
+    "ffn_plan_set_hot_head", "ffn_plan_destroy", "ffn_plan_set_timing_events", "ffn_last_error",
     "ffn_moe_workspace_size",
     "ffn_moe_plan", "ffn_moe_forward", "ffn_moe_destroy",
 ]
@@ -93,6 +93,8 @@ def lib():
         L.ffn_plan_set_crossover.argtypes = [P, I, ctypes.c_float]
         L.ffn_plan_set_decode_variant.restype = st
         L.ffn_plan_set_decode_variant.argtypes = [P, I]
+        L.ffn_plan_set_hot_head.restype = st
+        L.ffn_plan_set_hot_head.argtypes = [P, I]
         L.ffn_plan_destroy.restype = st
         L.ffn_plan_destroy.argtypes = [P]
         L.ffn_plan_set_timing_events.restype = st
@@ -157,6 +159,10 @@ def ffn_plan_set_decode_variant(plan: int, variant: int):
     _check(lib().ffn_plan_set_decode_variant(plan, variant))
 
 
+def ffn_plan_set_hot_head(plan: int, n_hot: int):
+    _check(lib().ffn_plan_set_hot_head(plan, n_hot))
+
+
 def ffn_plan_destroy(plan: int):
     _check(lib().ffn_plan_destroy(plan))
 
@@ -205,6 +211,7 @@ class SparseFFN:
 
     ``layer`` maps the names of ``ffn_layer_weights`` to device tensors (missing or None = NULL)
     and carries ``act``; the storage dtypes are read from the tensors (uint8 up rows = int4).
+    An optional ``n_hot`` sets the always-active head (``ffn_plan_set_hot_head``).
     """
 
     def __init__(self, layer: dict, max_batch: int = 1, threshold: float = 0.5,
@@ -235,6 +242,12 @@ class SparseFFN:
         self.d, self.ffn, self.x_dtype = d, self.desc.ffn, x_dtype
         self.plan = ffn_sparse_plan(self.desc, self.weights, workspace.data_ptr(),
                                     workspace.numel(), _stream(), int(calibrate))
+        if layer.get("n_hot"):
+            self.set_hot_head(int(layer["n_hot"]))
+
+    def set_hot_head(self, n_hot: int):
+        """Neurons [0, n_hot) always active (the layer's neurons ordered hottest first)."""
+        ffn_plan_set_hot_head(self.plan, n_hot)
 
     def forward(self, x, y=None, mask=None, idx=None, cnt=None, scores=None,
                 path=FFN_PATH_SPARSE):

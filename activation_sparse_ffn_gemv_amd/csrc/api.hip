@@ -209,6 +209,7 @@ BatchArgs batch_bufs(char* ws, const ffn_plan* p) {
   a.b_up = p->w.b_up;
   a.b_gate = p->w.b_gate;
   a.b_down = p->w.b_down;
+  a.head_words = p->head_words;
   a.d = D.d;
   a.ffn = D.ffn;
   a.r = D.rank;
@@ -299,6 +300,7 @@ ffn_status enqueue_token(const ffn_plan* p, const TokenBufs& wb, const void* xb,
     pa.nslot = nslot;
     pa.zstride = es;
     pa.bstride = es;
+    pa.head_words = slot ? 0 : p->head_words;
     if (!fused) {
       e = launch_pred_s(D.p_dtype == FFN_F16, pa, st, p->ev[FFN_STAGE_PRED_S][0],
                         p->ev[FFN_STAGE_PRED_S][1]);
@@ -533,6 +535,7 @@ ffn_status ffn_sparse_plan(const ffn_layer_desc* desc, const ffn_layer_weights* 
   for (int k = 0; k < 13; ++k) p->crossover_density[k] = 1.0f;
   p->dense_min_batch = 2;
   p->decode_variant = 0;
+  p->head_words = 0;
   if (calibrate && batched(desc) && desc->max_batch >= 2) {
     st = calibrate_crossover(p, static_cast<hipStream_t>(stream));
     if (st != FFN_OK) {
@@ -749,6 +752,15 @@ ffn_status ffn_plan_set_decode_variant(ffn_plan* p, int32_t variant) {
     return fail(FFN_ERR_UNSUPPORTED, "the fused decode variant needs fp32 / fp16 rows of "
                 "%d..%d chunks and a predictor", 256, 1024);
   p->decode_variant = variant;
+  return FFN_OK;
+}
+
+ffn_status ffn_plan_set_hot_head(ffn_plan* p, int32_t n_hot) {
+  if (!p) return fail(FFN_ERR_INVALID_ARGUMENT, "plan is NULL");
+  if (n_hot < 0 || n_hot > p->desc.ffn || n_hot % 32 != 0)
+    return fail(FFN_ERR_INVALID_ARGUMENT, "n_hot %d must be a multiple of 32 in [0, %d]", n_hot,
+                p->desc.ffn);
+  p->head_words = n_hot / 32;
   return FFN_OK;
 }
 

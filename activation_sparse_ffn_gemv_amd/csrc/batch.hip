@@ -141,6 +141,12 @@ __global__ __launch_bounds__(256) void k_bzr(BatchArgs a) {
 __global__ __launch_bounds__(BT) void k_bs(BatchArgs a) {
   __shared__ float red[3 * 16 * WAVE];
   const int lane = threadIdx.x & (WAVE - 1), wave = threadIdx.x / WAVE;
+  if ((int)blockIdx.x < a.head_words) {        // hot head: every token's word set, no score
+    const int W = a.ffn / 32;
+    if ((int)threadIdx.x < min(a.B, MB)) a.bits[(size_t)threadIdx.x * W + blockIdx.x] = ~0u;
+    if (threadIdx.x == 0) a.ubits[blockIdx.x] = ~0u;
+    return;
+  }
   const int n0 = blockIdx.x * 32, row = lane & 31, g = lane >> 5;
   const int rch = a.r / 8, nsteps = (rch + 1) / 2;
   const char* pr = static_cast<const char*>(a.p2) + (size_t)(n0 + row) * a.r * 2;

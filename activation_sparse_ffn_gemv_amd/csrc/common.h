@@ -219,4 +219,5 @@ struct ffn_plan {
   int dense_min_batch;          // AUTO takes the dense path from this batch size on
   hipEvent_t ev[9][2];          // instrumentation events attached to each stage's dispatch
   int decode_variant;           // batch-1 decode: 0 rank-balanced gather, 1 fused predictor + gather
+  int head_words;               // hot head: neurons [0, 32 head_words) always active
 };

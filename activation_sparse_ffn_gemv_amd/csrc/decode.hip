@@ -143,6 +143,10 @@ __global__ __launch_bounds__(PS_THREADS) void k_pred_s(PredArgs a) {
     a.p2 = a.slot->p2;
     a.c2 = a.slot->c2;
   }
+  if ((int)blockIdx.x < a.head_words) {         // hot head: always active, no score computed
+    if (tid == 0) a.bitmap[blockIdx.x] = ~0u;
+    return;
+  }
   const float c2v = (tid < 32 && a.c2) ? a.c2[i0 + tid] : 0.0f;
   f32x4 zr[CPR][PE / 4];                      // this lane's z slice, fixed across rows
 #pragma unroll
@@ -558,6 +562,7 @@ __global__ __launch_bounds__(FU_THREADS) void k_fused(FusedArgs f) {
   const int lane = tid & (WAVE - 1), wave = tid / WAVE;
   const int i0 = blockIdx.x * FU_ROWS;
   const int n = min(FU_ROWS, p.ffn - i0);               // 64, or 32 for the last workgroup
+  const int nh = min(max(32 * p.head_words - i0, 0), n); // hot-head rows: on, no score
   const int nch = a.d / EPC;
   FFN_TS(1, 0);
 
@@ -577,7 +582,7 @@ __global__ __launch_bounds__(FU_THREADS) void k_fused(FusedArgs f) {
   const int R = NT / L;                                 // rows per pass
   const int P = (n + R - 1) / R;                        // passes (<= PS_MAXP)
   const int g = tid / L, gl = tid % L;
-  const float c2v = (tid < n && p.c2) ? p.c2[i0 + tid] : 0.0f;
+  const float c2v = (tid >= nh && tid < n && p.c2) ? p.c2[i0 + tid] : 0.0f;
   f32x4 zr[CPR][PE / 4];
 #pragma unroll
   for (int k = 0; k < CPR; ++k) {
@@ -596,13 +601,14 @@ __global__ __launch_bounds__(FU_THREADS) void k_fused(FusedArgs f) {
 #pragma unroll
     for (int k = 0; k < CPR; ++k) {
       const int cc = min(gl + k * L, pch - 1);
-      if (pp < P) w[pp][k] = ld16(static_cast<const char*>(p.p2) + ((size_t)(i0 + r) * pch + cc) * 16);
+      if (pp < P && nh < n)
+        w[pp][k] = ld16(static_cast<const char*>(p.p2) + ((size_t)(i0 + r) * pch + cc) * 16);
     }
   }
   issue_fence();
 #pragma unroll
   for (int pp = 0; pp < PS_MAXP; ++pp) {
-    if (pp < P) {                                       // uniform
+    if (pp < P && nh < n) {                             // uniform
     float acc = 0.0f;
 #pragma unroll
     for (int k = 0; k < CPR; ++k) {
@@ -632,7 +638,9 @@ __global__ __launch_bounds__(FU_THREADS) void k_fused(FusedArgs f) {
   FFN_TS(1, 1);
   if (wave == 0) {
     bool on = false;
-    if (lane < n) {
+    if (lane < nh) {
+      on = true;
+    } else if (lane < n) {
       const float sc = s_score[lane] + c2v;
       on = sc > p.thr;
       if (p.scores) p.scores[i0 + lane] = sc;

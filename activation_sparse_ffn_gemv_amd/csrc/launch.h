@@ -48,6 +48,8 @@ struct PredArgs {
   const ExpertW* slot;        // device-chosen expert (p2, c2 from it), or nullptr
   int nslot;                  // expert slots run side by side (grid.y); slot k uses slot + k,
   int zstride, bstride;       //   z + k*zstride, bitmap + k*bstride (elements)
+  int head_words;             // hot head: bitmap words [0, head_words) always set, their P2 rows
+                              //   and c2 entries never read
 };
 
 // Balanced gather of the active rows (one token).
@@ -147,6 +149,7 @@ struct BatchArgs {
   int dense_above;            // path choice: union larger than this -> every neuron's row
   const int* run_if;          // device flag: the row kernels run only if *run_if == run_want
   int run_want;               //   (nullptr: always)
+  int head_words;             // hot head (as PredArgs)
 };
 
 struct BatchShape {

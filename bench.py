@@ -47,11 +47,12 @@ def n_bias(cfg) -> int:
     return (1 if cfg.bias_up else 0) + (1 if (cfg.act != "relu" and cfg.bias_gate) else 0)
 
 
-def pred_bytes(cfg):
+def pred_bytes(cfg, n_hot=0):
     """Predictor bytes per token-layer (per step-layer in a batch): stage 1 (P1), stage 2 (P2 and
-    c2)."""
+    c2 of the predicted neurons: all but an always-active head of n_hot)."""
     pb = 4 if cfg.p_dtype == "f32" else 2
-    return cfg.rank * cfg.d * pb, cfg.ffn * cfg.rank * pb + 4 * cfg.ffn
+    nf = cfg.ffn - n_hot
+    return cfg.rank * cfg.d * pb, nf * cfg.rank * pb + 4 * nf
 
 
 def profiled_traffic(kernel: str, workload: str):
@@ -95,6 +96,10 @@ def main():
     ap.add_argument("--decode-variant", type=int, default=None,
                     help="batch-1 decode variant for every plan (0 balanced, 1 fused); "
                          "default: the library's")
+    ap.add_argument("--hot-head", action="store_true",
+                    help="order each layer's neurons hottest first (the generator's firing "
+                         "probabilities stand in for a profile) and keep the capped head always "
+                         "active; only the rest is predicted")
     ap.add_argument("--calibrate", type=int, default=0,
                     help="also calibrate layer 0's plan for batches up to this size and report "
                          "its measured crossover densities (fp16 layers)")
@@ -121,6 +126,8 @@ def main():
     Bt = args.prefill if prefill else args.batch      # tokens per layer call
     if moe and (Bt != 1 or prefill):
         raise SystemExit("the mixture workload is measured at batch-1 decode")
+    if args.hot_head and (moe or prefill):
+        raise SystemExit("--hot-head applies to the single-layer decode workloads")
     K = args.steps if args.steps else (4 if prefill else max(1, cfg.tokens // Bt))
     W = min(args.warmup, K)
     dev = torch.device("cuda", 0)
@@ -144,6 +151,13 @@ def main():
     E = cfg.n_experts
     layers = [[synth.make_layer(cfg, layer=l, expert=e, device=dev) for e in range(E)]
               for l in range(L)]
+    n_hot = 0
+    if args.hot_head:
+        layers = [[synth.hot_first(le) for le in row] for row in layers]
+        n_hot = synth.hot_head_size(layers[0][0])
+        for row in layers:
+            for le in row:
+                le["n_hot"] = n_hot
     routers = [synth.make_router(cfg, layer=l, device=dev) for l in range(L)] if moe else None
     x = torch.stack([synth.make_tokens(cfg, K * Bt, layer=l, device=dev) for l in range(L)])
     y = torch.empty(L, K * Bt, cfg.d, dtype=torch.float32, device=dev)
@@ -187,7 +201,7 @@ def main():
             call(l, t)
 
     # ---- bytes the method touches per (layer, step): an untimed counting pass
-    pz, ps = pred_bytes(cfg)
+    pz, ps = pred_bytes(cfg, n_hot)
     rowb = n_rows(cfg) * row_bytes(cfg) + 4 * n_bias(cfg)
     router_b = cfg.n_experts * cfg.d * 2 if moe else 0
     if prefill:
@@ -351,7 +365,7 @@ def main():
                 "avg_us": stages[dom]["avg_us"],
                 "flops_per_launch": stages[dom]["flops_per_launch"]}
     else:
-        wl = cfg.name if Bt == 1 else cfg.name + ":batch%d" % Bt
+        wl = (cfg.name if Bt == 1 else cfg.name + ":batch%d" % Bt) + (":hot" if n_hot else "")
         roof = {"bound": "hbm", "kernel": knames[dom], "achieved": stages[dom]["gbps"],
                 "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(stages[dom]["gbps"] / HBM_PEAK_GBPS, 4),
@@ -390,7 +404,7 @@ def main():
                 elif moe:
                     oracle.moe_token(OLs, Rh, xh[t], cfg.top_k)
                 else:
-                    oracle.sparse_token(OL, xh[t])
+                    oracle.sparse_token(OL, xh[t], n_hot=n_hot)
                 t_cpu += time.perf_counter() - c0
             L_cpu = l + 1
             if t_cpu > CPU_BUDGET_S:
@@ -481,7 +495,7 @@ def main():
         "dtype": dtype,
         "data": "synthetic (seeded; power-law hot set)",
         "config": {"workload": cfg.name, "mode": mode, "tokens_per_call": Bt, "d": cfg.d,
-                   "decode_variant": args.decode_variant,
+                   "decode_variant": args.decode_variant, "hot_head": n_hot or None,
                    "ffn": cfg.ffn, "rank": cfg.rank, "act": cfg.act, "layers": L,
                    "experts": cfg.n_experts, "top_k": cfg.top_k if moe else None,
                    "target_density": cfg.density, "measured_density": round(density, 5)},

@@ -156,6 +156,21 @@ ffn_status ffn_plan_set_crossover(ffn_plan *plan, int32_t B, float density);
  */
 ffn_status ffn_plan_set_decode_variant(ffn_plan *plan, int32_t variant);
 
+/*
+ * Hot head (unite.ai PowerInfer, sections "Offline stage" and "Neuron placement and management":
+ * an offline profile separates the few neurons that fire for almost every input from the rest,
+ * and neurons are placed by that profile).  The caller orders the layer's neurons by profiled
+ * firing frequency, hottest first (every per-neuron array permuted alike: rows of W_up, W_gate,
+ * W_down_t and their int4 scales, b_up, b_gate, rows of P2, c2), and passes the head length
+ * n_hot.  From then on, whenever the predictor picks the sets (mask == NULL), neurons
+ * [0, n_hot) are always active and only [n_hot, ffn) are predicted: the head's P2 rows and c2
+ * entries are never read and its scores are not written (their slots in `scores` keep what they
+ * held).  The head's rows are contiguous, so the gather reads them as one dense block.  Calls
+ * with a caller mask are unaffected.  n_hot must be a multiple of 32 in [0, ffn]
+ * (FFN_ERR_INVALID_ARGUMENT otherwise); 0 (the default) turns the head off.
+ */
+ffn_status ffn_plan_set_hot_head(ffn_plan *plan, int32_t n_hot);
+
 ffn_status ffn_plan_destroy(ffn_plan *plan);
 
 /*

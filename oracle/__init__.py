@@ -9,6 +9,8 @@ only compiles it with gcc, marshals numpy arrays and composes per-token calls:
 
 * ``predictor``   -- low-rank activation predictor + strict sigmoid threshold
   (PowerInfer, unite.ai, section "Adaptive sparse predictor").
+* ``predictor_hot`` -- the same with an always-active hot head of profiled neurons placed first
+  (unite.ai, sections "Offline stage" and "Neuron placement and management").
 * ``ffn``         -- neuron-aware FFN over a mask (unite.ai, "Neuron-aware operator";
   citnews, "Dynamic neuron cache": inactive neurons do not change the output).
 * ``router``/``moe`` -- top-k softmax router and the weighted sum of the chosen experts
@@ -122,6 +124,30 @@ def predictor(p1, p2, c1, c2, x, tau: float):
     return {"z": z, "s": s, "p": p, "active": active, "idx": idx[:n].copy(), "count": int(n)}
 
 
+def predictor_hot(p1, p2, c1, c2, x, tau: float, n_hot: int):
+    """One token with an always-active hot head (unite.ai PowerInfer, "Offline stage" and "Neuron
+    placement and management": profiled hot neurons are told apart from the rest and placed
+    first).  Neurons [0, n_hot) are active whatever the predictor says; neurons [n_hot, ffn) are
+    decided by ``predictor`` on rows n_hot.. of P2 and c2.  The head's scores are NaN (never
+    computed).  Returns the same dict as ``predictor``."""
+    ffn_n = p2.shape[0]
+    assert 0 <= n_hot <= ffn_n
+    active = np.zeros(ffn_n, np.uint8)
+    active[:n_hot] = 1
+    s = np.full(ffn_n, np.nan)
+    p = np.full(ffn_n, np.nan)
+    z = None
+    if n_hot < ffn_n:
+        tail = predictor(p1, np.ascontiguousarray(p2[n_hot:]), c1,
+                         None if c2 is None else np.ascontiguousarray(c2[n_hot:]), x, tau)
+        active[n_hot:] = tail["active"]
+        s[n_hot:] = tail["s"]
+        p[n_hot:] = tail["p"]
+        z = tail["z"]
+    idx = np.flatnonzero(active).astype(np.int32)
+    return {"z": z, "s": s, "p": p, "active": active, "idx": idx, "count": int(idx.size)}
+
+
 def ffn(layer: dict, x, mask=None):
     """One token through the neuron-aware FFN.  ``layer`` holds numpy arrays:
     act ('relu'|'reglu'|'drelu'), w_up, w_gate, w_down_t ([ffn][d] f32/f16, or uint8 [ffn][d/2]
@@ -165,13 +191,18 @@ def router(R, x, k: int = 2):
     return ids, w, logits
 
 
-def sparse_token(layer: dict, x, mask=None):
+def sparse_token(layer: dict, x, mask=None, n_hot: int = 0):
     """Predictor (unless a mask is given) followed by the FFN over the active set, one token.
-    ``layer`` additionally holds p1, p2, c1, c2 and tau.  Returns (y float64[d], pred dict|None)."""
+    ``layer`` additionally holds p1, p2, c1, c2 and tau; n_hot > 0 takes ``predictor_hot``.
+    Returns (y float64[d], pred dict|None)."""
     pred = None
     if mask is None:
-        pred = predictor(layer["p1"], layer["p2"], layer.get("c1"), layer.get("c2"), x,
-                         layer["tau"])
+        if n_hot:
+            pred = predictor_hot(layer["p1"], layer["p2"], layer.get("c1"), layer.get("c2"), x,
+                                 layer["tau"], n_hot)
+        else:
+            pred = predictor(layer["p1"], layer["p2"], layer.get("c1"), layer.get("c2"), x,
+                             layer["tau"])
         mask = pred["active"]
     y, _ = ffn(layer, x, mask)
     return y, pred

@@ -215,6 +215,39 @@ def make_layer(cfg: LayerConfig, layer: int = 0, expert: int = 0, device="cpu") 
     return out
 
 
+# Per-neuron arrays of a layer dict (rows for matrices, entries for vectors).
+NEURON_KEYS = ("w_up", "s_up", "w_gate", "s_gate", "w_down_t", "s_down_t", "b_up", "b_gate",
+               "p2", "c2", "probs")
+
+
+def hot_first(layer: dict) -> dict:
+    """The same layer with its neurons ordered by firing probability, hottest first (stable
+    order among equals): the offline profile and placement step, with the generator's own
+    probabilities standing in for a profiler.  Every per-neuron array is permuted alike, so the
+    dense FFN and each neuron's predictor score are unchanged; ``order[j]`` is the original
+    index of neuron j."""
+    order = np.argsort(-np.asarray(layer["probs"]), kind="stable")
+    out = dict(layer)
+    for k in NEURON_KEYS:
+        v = layer.get(k)
+        if v is None:
+            continue
+        if isinstance(v, torch.Tensor):
+            out[k] = v[torch.from_numpy(order).to(v.device)].contiguous()
+        else:
+            out[k] = np.ascontiguousarray(np.asarray(v)[order])
+    out["order"] = order
+    return out
+
+
+def hot_head_size(layer: dict) -> int:
+    """Neurons whose firing probability sits at the generator's cap (the always-firing head),
+    rounded down to a multiple of 32."""
+    cap = layer["cfg"].cap
+    n = int(np.count_nonzero(np.asarray(layer["probs"]) >= cap * (1.0 - 1e-12)))
+    return n - n % 32
+
+
 def make_tokens(cfg: LayerConfig, n: int, layer: int = 0, device="cpu", offset: int = 0,
                 salt: int = 0) -> torch.Tensor:
     """n tokens x ~ N(0, 1) [n][d] in the activation dtype, for one layer."""

@@ -118,6 +118,12 @@ def test_plan_validation_before_any_gpu_call():
         with pytest.raises(ffn.FFNError) as e:
             ffn.ffn_plan_set_crossover(plan, 8, 1.5)
         assert e.value.status == ffn.FFN_ERR_INVALID_ARGUMENT
+        for bad in (-32, 16, d.ffn + 32):                  # hot head: multiple of 32 in [0, ffn]
+            with pytest.raises(ffn.FFNError) as e:
+                ffn.ffn_plan_set_hot_head(plan, bad)
+            assert e.value.status == ffn.FFN_ERR_INVALID_ARGUMENT
+        ffn.ffn_plan_set_hot_head(plan, d.ffn)
+        ffn.ffn_plan_set_hot_head(plan, 0)
     finally:
         ffn.ffn_plan_destroy(plan)
 
