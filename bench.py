@@ -100,6 +100,13 @@ def main():
                     help="order each layer's neurons hottest first (the generator's firing "
                          "probabilities stand in for a profile) and keep the capped head always "
                          "active; only the rest is predicted")
+    ap.add_argument("--spectrum-alpha", type=float, default=0.0,
+                    help="shape the predictor's source matrix to singular values ~ k^-alpha")
+    ap.add_argument("--fit-recall", type=float, default=0.0,
+                    help="replace each layer's predictor by a least-squares fit whose rank is the "
+                         "smallest (step 32) with this expected recall")
+    ap.add_argument("--fit-margin", type=float, default=0.0,
+                    help="recall margin of the fitted predictors (residual standard deviations)")
     ap.add_argument("--calibrate", type=int, default=0,
                     help="also calibrate layer 0's plan for batches up to this size and report "
                          "its measured crossover densities (fp16 layers)")
@@ -120,6 +127,8 @@ def main():
     import synth
 
     cfg = synth.CONFIGS[args.config]
+    if args.spectrum_alpha > 0:
+        cfg = synth.with_(cfg, spectrum_alpha=args.spectrum_alpha)
     L = args.layers or cfg.layers
     moe = cfg.n_experts > 1
     prefill = args.prefill > 0
@@ -151,6 +160,25 @@ def main():
     E = cfg.n_experts
     layers = [[synth.make_layer(cfg, layer=l, expert=e, device=dev) for e in range(E)]
               for l in range(L)]
+    fitq = None
+    if args.fit_recall > 0:
+        if moe or prefill:
+            raise SystemExit("--fit-recall applies to the single-layer decode workloads")
+        from synth import fit
+        t1 = time.time()
+        fitq = []
+        for row in layers:
+            V = fit.spectrum(row[0])[0]
+            r, q = fit.choose_rank(row[0], args.fit_recall, margin=args.fit_margin, step=32,
+                                   basis=V)
+            row[0] = fit.fit_predictor(row[0], r, margin=args.fit_margin, basis=V)
+            fitq.append((r,) + tuple(q))
+            del V
+        fitq = np.array(fitq)
+        log("fitted predictors in %.1f s: rank per layer %s; expected recall %.3f precision %.3f"
+            % (time.time() - t1, fitq[:, 0].astype(int).tolist(), fitq[:, 1].mean(),
+               fitq[:, 2].mean()))
+    ranks = np.array([row[0]["p1"].shape[0] for row in layers], np.float64)[:, None]
     n_hot = 0
     if args.hot_head:
         layers = [[synth.hot_first(le) for le in row] for row in layers]
@@ -202,6 +230,7 @@ def main():
 
     # ---- bytes the method touches per (layer, step): an untimed counting pass
     pz, ps = pred_bytes(cfg, n_hot)
+    pz, ps = pz * ranks / cfg.rank, ps * ranks / cfg.rank       # [L][1]: each layer's own rank
     rowb = n_rows(cfg) * row_bytes(cfg) + 4 * n_bias(cfg)
     router_b = cfg.n_experts * cfg.d * 2 if moe else 0
     if prefill:
@@ -261,6 +290,44 @@ def main():
         log("measured per-token density %.4f, union density %.4f" % (
             density, union.mean() / F))
     torch.cuda.synchronize()
+
+    # ---- predictor quality on a few tokens of every layer: the kernels' sets against the true
+    # sets (h != 0, from the source pre-activations computed here in float64 for measurement)
+    quality = None
+    if not prefill and not moe and Bt == 1:
+        from synth import fit as sfit
+        ns = min(K, 8)
+        qi = torch.zeros(ns, cfg.ffn, dtype=torch.int32, device=dev)
+        qc = torch.zeros(ns, dtype=torch.int32, device=dev)
+        ar = torch.arange(cfg.ffn, device=dev)
+        tp = npred = ntrue = 0
+        for l in range(L):
+            with torch.cuda.stream(stream):
+                for t in range(ns):
+                    call(l, t, idx=qi[t].data_ptr(), cnt=qc[t].data_ptr())
+            torch.cuda.synchronize()
+            valid = ar[None, :] < qc[:, None].long()
+            pm = torch.zeros(ns, cfg.ffn, dtype=torch.bool, device=dev)
+            pm.scatter_(1, torch.where(valid, qi.long(), 0), valid)
+            xs = x[l, :ns].double()
+            w_src, b_src = sfit.source(layers[l][0])
+            tm = (xs @ w_src.T + b_src) > 0
+            if cfg.act == "drelu":
+                w_u, b_u = sfit.source(dict(layers[l][0], act="relu"))
+                tm &= (xs @ w_u.T + b_u) > 0
+            del w_src
+            tp += int((pm & tm).sum())
+            npred += int(pm.sum())
+            ntrue += int(tm.sum())
+        quality = {"tokens": ns, "measured_recall": round(tp / max(ntrue, 1), 4),
+                   "measured_precision": round(tp / max(npred, 1), 4),
+                   "rank_per_layer": ranks[:, 0].astype(int).tolist()}
+        if fitq is not None:
+            quality.update(expected_recall=round(float(fitq[:, 1].mean()), 4),
+                           expected_precision=round(float(fitq[:, 2].mean()), 4),
+                           fit_target_recall=args.fit_recall, fit_margin=args.fit_margin)
+        log("predictor on %d token(s) x %d layers: recall %.3f, precision %.3f" % (
+            ns, L, quality["measured_recall"], quality["measured_precision"]))
 
     # ---- HIP graphs of whole steps (all layers)
     G = 1 if prefill else max(1, min(K, 256 // L))
@@ -335,16 +402,17 @@ def main():
         else:
             per_call = touched[:, :S].sum() / (L * S)
             k = cfg.top_k if moe else 1
+            pzm, psm = float(pz.mean()), float(ps.mean())
             if sname == "pred_z":
-                nb = pz * k                                          # the slots run side by side
+                nb = pzm * k                                         # the slots run side by side
             elif sname == "pred_s":
-                nb = ps * k
+                nb = psm * k
             elif sname == "gather":
-                nb = per_call - router_b - k * (pz + ps)             # all expert slots' rows
+                nb = per_call - router_b - k * (pzm + psm)           # all expert slots' rows
             elif sname == "reduce":
                 nb = 0.0
             else:
-                rows_u = (per_call - pz - ps) / rowb / passes         # union rows per pass
+                rows_u = (per_call - pzm - psm) / rowb / passes       # union rows per pass
                 nb = rows_u * (n_rows(cfg) - 1 if sname == "batch_upgate" else 1) * row_bytes(cfg)
             rec["bytes_per_launch"] = int(nb)
             rec["gbps"] = round(nb / (dur.mean() / 1e3) / 1e9, 1)
@@ -365,7 +433,8 @@ def main():
                 "avg_us": stages[dom]["avg_us"],
                 "flops_per_launch": stages[dom]["flops_per_launch"]}
     else:
-        wl = (cfg.name if Bt == 1 else cfg.name + ":batch%d" % Bt) + (":hot" if n_hot else "")
+        wl = ((cfg.name if Bt == 1 else cfg.name + ":batch%d" % Bt) + (":hot" if n_hot else "")
+              + (":fit" if fitq is not None or cfg.spectrum_alpha else ""))
         roof = {"bound": "hbm", "kernel": knames[dom], "achieved": stages[dom]["gbps"],
                 "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(stages[dom]["gbps"] / HBM_PEAK_GBPS, 4),
@@ -496,9 +565,11 @@ def main():
         "data": "synthetic (seeded; power-law hot set)",
         "config": {"workload": cfg.name, "mode": mode, "tokens_per_call": Bt, "d": cfg.d,
                    "decode_variant": args.decode_variant, "hot_head": n_hot or None,
+                   "spectrum_alpha": cfg.spectrum_alpha or None,
                    "ffn": cfg.ffn, "rank": cfg.rank, "act": cfg.act, "layers": L,
                    "experts": cfg.n_experts, "top_k": cfg.top_k if moe else None,
                    "target_density": cfg.density, "measured_density": round(density, 5)},
+        "predictor": quality,
         "effective_gbps": round(eff_gbps, 1),
         "touched_bytes_per_step": int(touched.sum() / K),
         "roofline": roof,

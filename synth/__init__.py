@@ -10,7 +10,8 @@ PowerInfer, unite.ai, introduction and "Architecture and methodology": a few hot
 almost every input, most cold neurons only for some inputs; nearauto.com Fig. 8: the hot neurons
 are scattered through the matrix):
 
-* weights ~ N(0, 0.02^2), rounded once to the storage dtype (fp32, fp16 round-to-nearest-even,
+* weights ~ N(0, 0.02^2) (optionally, for the predictor's source matrix, shaped to a power-law
+  singular spectrum with the same row norms: ``spectrum_alpha``), rounded once to the storage dtype (fp32, fp16 round-to-nearest-even,
   or int4 with one fp16 scale per 32 consecutive elements of a row:
   s = fp16(max|w| / 7), q = clamp(rint(w / s), -8, 7), q = 0 where s = 0; for int4 the bias
   calibration and the predictor use the weights before quantisation);
@@ -60,6 +61,7 @@ class LayerConfig:
     tau: float = 0.5
     zipf_s: float = 1.1
     cap: float = 0.99
+    spectrum_alpha: float = 0.0  # > 0: the predictor's source matrix gets singular values ~ k^-alpha
     batches: tuple = (1,)
     seed: int = 1000
     expert_density: tuple = field(default=())
@@ -152,9 +154,17 @@ def quantize_i4g32(w: torch.Tensor):
     return packed.contiguous(), s16.contiguous()
 
 
-def _weight(cfg, rows, cols, device, seed):
+def _weight(cfg, rows, cols, device, seed, shaped=False):
     w = torch.randn(rows, cols, generator=_gen(device, seed), device=device,
                     dtype=torch.float32) * 0.02
+    if shaped and cfg.spectrum_alpha > 0:
+        # a trained-looking spectrum: w = A diag(sv) Q^T with a seeded orthonormal Q and
+        # sv_k ~ (k+1)^-alpha, scaled so that rows keep E|w_row|^2 = 0.02^2 cols
+        q, _ = torch.linalg.qr(torch.randn(cols, cols, generator=_gen(device, seed + 17),
+                                           device=device, dtype=torch.float64))
+        sv = torch.arange(1, cols + 1, device=device, dtype=torch.float64) ** (-cfg.spectrum_alpha)
+        sv = sv * (0.02 * np.sqrt(cols) / sv.square().sum().sqrt())
+        w = ((w.double() / 0.02) @ (sv[:, None] * q.T)).float()
     if cfg.w_dtype == I4G32:
         packed, scales = quantize_i4g32(w)
         return packed, scales, w          # norms taken before quantisation
@@ -169,11 +179,13 @@ def make_layer(cfg: LayerConfig, layer: int = 0, expert: int = 0, device="cpu") 
     probs = zipf_probs(F, density, cfg.zipf_s, cfg.cap, _seed(cfg, layer, expert, 0))
     out = {"cfg": cfg, "act": cfg.act, "probs": probs, "tau": cfg.tau, "layer": layer,
            "expert": expert}
-    w_up, s_up, f_up = _weight(cfg, F, d, device, _seed(cfg, layer, expert, 1))
+    w_up, s_up, f_up = _weight(cfg, F, d, device, _seed(cfg, layer, expert, 1),
+                               shaped=cfg.act == "relu")
     out["w_up"], out["s_up"] = w_up, s_up
     f_gate = None
     if cfg.act != "relu":
-        w_gate, s_gate, f_gate = _weight(cfg, F, d, device, _seed(cfg, layer, expert, 2))
+        w_gate, s_gate, f_gate = _weight(cfg, F, d, device, _seed(cfg, layer, expert, 2),
+                                         shaped=True)
         out["w_gate"], out["s_gate"] = w_gate, s_gate
     else:
         out["w_gate"], out["s_gate"] = None, None
