@@ -15,6 +15,8 @@ only compiles it with gcc, marshals numpy arrays and composes per-token calls:
   citnews, "Dynamic neuron cache": inactive neurons do not change the output).
 * ``router``/``moe`` -- top-k softmax router and the weighted sum of the chosen experts
   (TurboSparse-Mixtral, nubint.ai review and citnews).
+* ``NeuronCache`` -- the LRU neuron cache of host-resident FFN rows (citnews, "Dynamic neuron
+  cache": an LRU pool of neurons, segmented by weight type).
 
 Every function works on one token; batches are independent tokens, each with its own mask.
 """
@@ -220,3 +222,62 @@ def moe_token(experts, R, x, k: int = 2, masks=None):
         preds.append(pred)
         y += w[t] * ye
     return y, ids, w, preds
+
+
+PINNED = 0xFFFFFFFF
+
+
+class NeuronCache:
+    """LRU cache of FFN neurons in device memory, one token at a time (citnews.com.cn PowerInfer-2
+    article, section "Dynamic neuron cache": an in-memory pool of neurons managed by LRU, the
+    cache segmented by weight type -- here the predictor segment is always resident and only the
+    FFN rows of neurons are cached).
+
+    ``capacity`` slots; slots [0, n_pinned) hold neurons [0, n_pinned) for good (the hot head).
+    ``step(active)`` takes one token's active neurons in ascending order and returns, per rank,
+    the slot the neuron is read from (-1: read from host memory) and the slot it is admitted to
+    (-1: none):
+      * the token's stamp is the previous one plus 1 (the first token has stamp 1);
+      * a resident neuron is a hit; its slot's last use becomes the stamp (pinned slots keep
+        theirs);
+      * the misses, in rank order, take the free or least recently used slots -- the slots not
+        used by this token and not pinned, in ascending (last use, slot) order (free slots have
+        last use 0); a miss beyond those slots is read from host memory and not admitted;
+      * an admitted neuron evicts the slot's previous neuron, and the slot's last use becomes the
+        stamp.
+    """
+
+    def __init__(self, ffn: int, capacity: int, n_pinned: int = 0):
+        assert 0 <= n_pinned <= capacity and n_pinned <= ffn
+        self.slot_of = np.full(ffn, -1, np.int64)
+        self.neuron_of = np.full(capacity, -1, np.int64)
+        self.last_use = np.zeros(capacity, np.int64)
+        self.slot_of[:n_pinned] = np.arange(n_pinned)
+        self.neuron_of[:n_pinned] = np.arange(n_pinned)
+        self.last_use[:n_pinned] = PINNED
+        self.stamp = 0
+
+    def step(self, active):
+        self.stamp += 1
+        active = [int(n) for n in active]
+        src = [int(self.slot_of[n]) for n in active]
+        for s in src:
+            if s >= 0 and self.last_use[s] != PINNED:
+                self.last_use[s] = self.stamp
+        free = sorted((int(self.last_use[s]), s) for s in range(len(self.last_use))
+                      if self.last_use[s] < self.stamp)
+        victim = [-1] * len(active)
+        k = 0
+        for j, n in enumerate(active):
+            if src[j] >= 0 or k >= len(free):
+                continue
+            v = free[k][1]
+            k += 1
+            old = int(self.neuron_of[v])
+            if old >= 0:
+                self.slot_of[old] = -1
+            self.neuron_of[v] = n
+            self.slot_of[n] = v
+            self.last_use[v] = self.stamp
+            victim[j] = v
+        return src, victim
