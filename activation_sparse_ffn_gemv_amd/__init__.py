@@ -37,7 +37,8 @@ DTYPE = {"f32": FFN_F32, "f16": FFN_F16, "i4g32": FFN_I4G32}
 EXPORTS = [
     "ffn_workspace_size", "ffn_sparse_plan", "ffn_sparse_forward", "ffn_dense_forward",
     "ffn_plan_crossover", "ffn_plan_set_crossover", "ffn_plan_set_decode_variant",
-    "ffn_plan_set_hot_head", "ffn_plan_destroy", "ffn_plan_set_timing_events", "ffn_last_error",
+    "ffn_plan_set_hot_head", "ffn_offload_workspace_size", "ffn_offload_plan",
+    "ffn_offload_tables", "ffn_plan_destroy", "ffn_plan_set_timing_events", "ffn_last_error",
     "ffn_moe_workspace_size",
     "ffn_moe_plan", "ffn_moe_forward", "ffn_moe_destroy",
 ]
@@ -95,6 +96,15 @@ def lib():
         L.ffn_plan_set_decode_variant.argtypes = [P, I]
         L.ffn_plan_set_hot_head.restype = st
         L.ffn_plan_set_hot_head.argtypes = [P, I]
+        L.ffn_offload_workspace_size.restype = st
+        L.ffn_offload_workspace_size.argtypes = [ctypes.POINTER(ffn_layer_desc), I,
+                                                 ctypes.POINTER(S)]
+        L.ffn_offload_plan.restype = st
+        L.ffn_offload_plan.argtypes = [ctypes.POINTER(ffn_layer_desc),
+                                       ctypes.POINTER(ffn_layer_weights), I, I, P, S, P,
+                                       ctypes.POINTER(P)]
+        L.ffn_offload_tables.restype = st
+        L.ffn_offload_tables.argtypes = [P] + [ctypes.POINTER(P)] * 4
         L.ffn_plan_destroy.restype = st
         L.ffn_plan_destroy.argtypes = [P]
         L.ffn_plan_set_timing_events.restype = st
@@ -161,6 +171,27 @@ def ffn_plan_set_decode_variant(plan: int, variant: int):
 
 def ffn_plan_set_hot_head(plan: int, n_hot: int):
     _check(lib().ffn_plan_set_hot_head(plan, n_hot))
+
+
+def ffn_offload_workspace_size(desc: ffn_layer_desc, capacity: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().ffn_offload_workspace_size(ctypes.byref(desc), capacity, ctypes.byref(n)))
+    return n.value
+
+
+def ffn_offload_plan(desc, weights, capacity: int, n_pinned: int, workspace: int,
+                     workspace_bytes: int, stream: int = 0) -> int:
+    out = ctypes.c_void_p(0)
+    _check(lib().ffn_offload_plan(ctypes.byref(desc), ctypes.byref(weights), capacity, n_pinned,
+                                  workspace, workspace_bytes, stream or None, ctypes.byref(out)))
+    return out.value
+
+
+def ffn_offload_tables(plan: int):
+    """Device addresses of (slot_of, neuron_of, last_use, stats) inside the plan's workspace."""
+    ptrs = [ctypes.c_void_p(0) for _ in range(4)]
+    _check(lib().ffn_offload_tables(plan, *[ctypes.byref(q) for q in ptrs]))
+    return tuple(q.value for q in ptrs)
 
 
 def ffn_plan_destroy(plan: int):
@@ -278,6 +309,48 @@ class SparseFFN:
             self.close()
         except Exception:
             pass
+
+
+class OffloadFFN(SparseFFN):
+    """A layer whose up / gate / down rows stay in pinned host memory behind a pool of
+    ``capacity`` neuron slots in device memory (``ffn_offload_plan``).  ``layer`` holds the rows
+    as pinned CPU tensors (``pin_memory=True``) and the predictor and biases as device tensors;
+    neurons [0, n_pinned) are kept in the pool for good.  One token per call."""
+
+    def __init__(self, layer: dict, capacity: int, n_pinned: int = 0, threshold: float = 0.5,
+                 device=None):
+        w_up = layer["w_up"]
+        assert w_up.dtype == torch.float16 and w_up.is_pinned(), "rows: pinned fp16 CPU tensors"
+        dev = device or layer["p1"].device
+        p1 = layer["p1"]
+        act = layer["act"]
+        self.desc = ffn_layer_desc(d=w_up.shape[1], ffn=w_up.shape[0], rank=p1.shape[0],
+                                   act=ACT[act] if isinstance(act, str) else int(act),
+                                   w_dtype=FFN_F16, x_dtype=FFN_F16,
+                                   p_dtype=FFN_F32 if p1.dtype == torch.float32 else FFN_F16,
+                                   threshold=float(layer.get("tau", threshold)), max_batch=1)
+        self.tensors = {k: layer.get(k) for k, _ in ffn_layer_weights._fields_}
+        self.weights = ffn_layer_weights(**{k: (_ptr(v) or None) for k, v in self.tensors.items()})
+        self.ws_bytes = ffn_offload_workspace_size(self.desc, capacity)
+        self.workspace = torch.empty(self.ws_bytes, dtype=torch.uint8, device=dev)
+        self.d, self.ffn, self.x_dtype = self.desc.d, self.desc.ffn, FFN_F16
+        self.capacity = capacity
+        self.plan = ffn_offload_plan(self.desc, self.weights, capacity, n_pinned,
+                                     self.workspace.data_ptr(), self.ws_bytes, _stream())
+        if layer.get("n_hot"):
+            self.set_hot_head(int(layer["n_hot"]))
+
+    def tables(self):
+        """(slot_of [ffn], neuron_of [capacity], last_use [capacity] (as int64), stats [4]) --
+        copies of the pool's device tables."""
+        base = self.workspace.data_ptr()
+        so, no, lu, st = ffn_offload_tables(self.plan)
+
+        def view(addr, n):
+            return self.workspace[addr - base: addr - base + 4 * n].view(torch.int32)
+        last = view(lu, self.capacity).clone().to(torch.int64) & 0xFFFFFFFF
+        return (view(so, self.ffn).clone(), view(no, self.capacity).clone(), last,
+                view(st, 4).clone())
 
 
 class MoEFFN:

@@ -264,6 +264,44 @@ TokenBufs token_bufs(char* ws, const ffn_plan* p) {
                    reinterpret_cast<float*>(ws + p->off_part)};
 }
 
+// The neuron-cache region: c_up | c_gate | c_dn [cap][d] fp16 | slot_of [ffn] | neuron_of [cap] |
+// last_use [cap] | stamp | rank_nid, rank_src, rank_vic [ffn] | stats [4].
+size_t cache_region_bytes(const ffn_layer_desc& D, int cap) {
+  const size_t rows = round_up((size_t)cap * D.d * 2, 256);
+  return 3 * rows + round_up((size_t)D.ffn * 4, 256) + 2 * round_up((size_t)cap * 4, 256) + 256 +
+         3 * round_up((size_t)D.ffn * 4, 256) + 256;
+}
+
+struct CacheBufs {
+  char* c_up;
+  char* c_gate;
+  char* c_dn;
+  CacheArgs a;
+};
+
+CacheBufs cache_bufs(const ffn_plan* p) {
+  const ffn_layer_desc& D = p->desc;
+  const int cap = p->cache_cap;
+  const size_t rows = round_up((size_t)cap * D.d * 2, 256);
+  char* b = p->ws + p->off_cache;
+  CacheBufs c{};
+  c.c_up = b;
+  c.c_gate = b + rows;
+  c.c_dn = b + 2 * rows;
+  size_t off = 3 * rows;
+  c.a.ffn = D.ffn;
+  c.a.cap = cap;
+  c.a.slot_of = reinterpret_cast<int*>(b + off);         off += round_up((size_t)D.ffn * 4, 256);
+  c.a.neuron_of = reinterpret_cast<int*>(b + off);       off += round_up((size_t)cap * 4, 256);
+  c.a.last_use = reinterpret_cast<uint32_t*>(b + off);   off += round_up((size_t)cap * 4, 256);
+  c.a.stamp = reinterpret_cast<uint32_t*>(b + off);      off += 256;
+  c.a.rank_nid = reinterpret_cast<int*>(b + off);        off += round_up((size_t)D.ffn * 4, 256);
+  c.a.rank_src = reinterpret_cast<int*>(b + off);        off += round_up((size_t)D.ffn * 4, 256);
+  c.a.rank_vic = reinterpret_cast<int*>(b + off);        off += round_up((size_t)D.ffn * 4, 256);
+  c.a.stats = reinterpret_cast<int*>(b + off);
+  return c;
+}
+
 // The launches of one token: active set (predictor or caller mask) -> balanced gather -> reduce.
 // slot != nullptr: the experts are chosen on the device; the kernels take their weights from
 // the nslot consecutive slot records (p then only supplies shapes and the threshold) and run
@@ -278,7 +316,7 @@ ffn_status enqueue_token(const ffn_plan* p, const TokenBufs& wb, const void* xb,
   const int es = (int)(slot_stride / 4);      // the same stride in 4-byte elements
   hipError_t e;
   const bool fused = !maskb && !all_neurons && !slot && p->decode_variant == 1 &&
-                     fused_supported(wk, D.d);
+                     fused_supported(wk, D.d) && p->cache_cap == 0;
   if (maskb || all_neurons) {
     e = launch_mask_bits(maskb, wb.bits, D.ffn / 32, st);
     if (e != hipSuccess) return hip_fail(e, "mask launch");
@@ -345,7 +383,22 @@ ffn_status enqueue_token(const ffn_plan* p, const TokenBufs& wb, const void* xb,
   ga.bstride = es;
   ga.cstride = es;
   ga.pstride = (size_t)es;
-  if (!fused) {
+  if (p->cache_cap > 0 && !slot) {
+    // host-resident rows: the cache plan ranks the set and picks each row's source, then the
+    // gather reads hits from the cache and misses from host memory (admitting them)
+    CacheBufs cb = cache_bufs(p);
+    cb.a.bitmap = wb.bits;
+    cb.a.cnt = wb.cnt;
+    if ((e = launch_cache_plan(cb.a, st)) != hipSuccess) return hip_fail(e, "cache plan launch");
+    ga.rank_nid = cb.a.rank_nid;
+    ga.rank_src = cb.a.rank_src;
+    ga.rank_vic = cb.a.rank_vic;
+    ga.c_up = cb.c_up;
+    ga.c_gate = cb.c_gate;
+    ga.c_dn = cb.c_dn;
+    e = launch_gather_cached(ga, st, p->ev[FFN_STAGE_GATHER][0], p->ev[FFN_STAGE_GATHER][1]);
+    if (e != hipSuccess) return hip_fail(e, "cached gather launch");
+  } else if (!fused) {
     e = launch_gather(wk, ga, st, p->ev[FFN_STAGE_GATHER][0], p->ev[FFN_STAGE_GATHER][1]);
     if (e != hipSuccess) return hip_fail(e, "gather launch");
   }
@@ -536,6 +589,8 @@ ffn_status ffn_sparse_plan(const ffn_layer_desc* desc, const ffn_layer_weights* 
   p->dense_min_batch = 2;
   p->decode_variant = 0;
   p->head_words = 0;
+  p->cache_cap = 0;
+  p->off_cache = 0;
   if (calibrate && batched(desc) && desc->max_batch >= 2) {
     st = calibrate_crossover(p, static_cast<hipStream_t>(stream));
     if (st != FFN_OK) {
@@ -545,6 +600,98 @@ ffn_status ffn_sparse_plan(const ffn_layer_desc* desc, const ffn_layer_weights* 
   }
   *out = p;
   g_err[0] = 0;
+  return FFN_OK;
+}
+
+ffn_status ffn_offload_workspace_size(const ffn_layer_desc* desc, int32_t capacity,
+                                      size_t* bytes) {
+  if (!desc || !bytes) return fail(FFN_ERR_INVALID_ARGUMENT, "desc / bytes is NULL");
+  ffn_layer_desc d1 = *desc;
+  d1.max_batch = 1;
+  size_t main_bytes = 0;
+  ffn_status st = ffn_workspace_size(&d1, &main_bytes);
+  if (st != FFN_OK) return st;
+  if (desc->w_dtype != FFN_F16 || desc->x_dtype != FFN_F16 || desc->rank == 0)
+    return fail(FFN_ERR_UNSUPPORTED, "the neuron cache holds fp16 rows of a layer with a predictor");
+  if (capacity < 32 || capacity > CACHE_MAX_SLOTS || capacity % 32 || capacity > desc->ffn)
+    return fail(FFN_ERR_INVALID_ARGUMENT, "capacity %d: a multiple of 32 in [32, min(ffn, %d)]",
+                capacity, CACHE_MAX_SLOTS);
+  *bytes = round_up(main_bytes, 256) + cache_region_bytes(d1, capacity);
+  g_err[0] = 0;
+  return FFN_OK;
+}
+
+// A host pointer the kernels may read: pinned (hipHostMalloc) host memory, mapped for the GPU.
+static const void* mapped_host(const void* h) {
+  hipPointerAttribute_t at{};
+  if (hipPointerGetAttributes(&at, h) != hipSuccess) {
+    (void)hipGetLastError();                      // unregistered memory: clear the error
+    return nullptr;
+  }
+  if (at.type != hipMemoryTypeHost) return nullptr;
+  return at.devicePointer ? at.devicePointer : h;
+}
+
+ffn_status ffn_offload_plan(const ffn_layer_desc* desc, const ffn_layer_weights* w,
+                            int32_t capacity, int32_t n_pinned, void* workspace,
+                            size_t workspace_bytes, void* stream, ffn_plan** out) {
+  if (!desc || !w || !out) return fail(FFN_ERR_INVALID_ARGUMENT, "desc / weights / out is NULL");
+  *out = nullptr;
+  size_t need = 0;
+  ffn_status st = ffn_offload_workspace_size(desc, capacity, &need);
+  if (st != FFN_OK) return st;
+  if (n_pinned < 0 || n_pinned > capacity)
+    return fail(FFN_ERR_INVALID_ARGUMENT, "n_pinned %d not in [0, capacity]", n_pinned);
+  if (!workspace) return fail(FFN_ERR_INVALID_ARGUMENT, "workspace is NULL");
+  if (workspace_bytes < need)
+    return fail(FFN_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", workspace_bytes, need);
+  const bool gate = desc->act != FFN_ACT_RELU;
+  if (!w->w_up || !w->w_down_t || (gate && !w->w_gate))
+    return fail(FFN_ERR_INVALID_ARGUMENT, "w_up, w_down_t (and w_gate unless ReLU) required");
+  ffn_layer_weights wd = *w;
+  wd.w_up = mapped_host(w->w_up);
+  wd.w_gate = gate ? mapped_host(w->w_gate) : nullptr;
+  wd.w_down_t = mapped_host(w->w_down_t);
+  if (!wd.w_up || !wd.w_down_t || (gate && !wd.w_gate))
+    return fail(FFN_ERR_INVALID_ARGUMENT, "w_up / w_gate / w_down_t must be pinned host memory "
+                "(hipHostMalloc) for a neuron-cache plan");
+  ffn_layer_desc d1 = *desc;
+  d1.max_batch = 1;
+  ffn_plan* p = nullptr;
+  if ((st = ffn_sparse_plan(&d1, &wd, workspace, workspace_bytes, stream, 0, &p)) != FFN_OK)
+    return st;
+  size_t main_bytes = 0;
+  ffn_workspace_size(&d1, &main_bytes);
+  p->cache_cap = capacity;
+  p->off_cache = round_up(main_bytes, 256);
+  // tables, and the pinned head's rows copied into slots [0, n_pinned)
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  CacheBufs cb = cache_bufs(p);
+  hipError_t e = launch_cache_init(cb.a, n_pinned, s);
+  const size_t hb = (size_t)n_pinned * d1.d * 2;
+  if (e == hipSuccess && hb) e = hipMemcpyAsync(cb.c_up, wd.w_up, hb, hipMemcpyDefault, s);
+  if (e == hipSuccess && hb && gate) e = hipMemcpyAsync(cb.c_gate, wd.w_gate, hb, hipMemcpyDefault, s);
+  if (e == hipSuccess && hb) e = hipMemcpyAsync(cb.c_dn, wd.w_down_t, hb, hipMemcpyDefault, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) {
+    delete p;
+    return hip_fail(e, "neuron cache initialisation");
+  }
+  *out = p;
+  g_err[0] = 0;
+  return FFN_OK;
+}
+
+ffn_status ffn_offload_tables(const ffn_plan* p, const int32_t** slot_of,
+                              const int32_t** neuron_of, const uint32_t** last_use,
+                              const int32_t** stats) {
+  if (!p) return fail(FFN_ERR_INVALID_ARGUMENT, "plan is NULL");
+  if (p->cache_cap == 0) return fail(FFN_ERR_INVALID_ARGUMENT, "not a neuron-cache plan");
+  const CacheBufs cb = cache_bufs(p);
+  if (slot_of) *slot_of = cb.a.slot_of;
+  if (neuron_of) *neuron_of = cb.a.neuron_of;
+  if (last_use) *last_use = cb.a.last_use;
+  if (stats) *stats = cb.a.stats;
   return FFN_OK;
 }
 
@@ -748,6 +895,8 @@ ffn_status ffn_plan_set_decode_variant(ffn_plan* p, int32_t variant) {
     return fail(FFN_ERR_INVALID_ARGUMENT, "variant %d is not 0 or 1", variant);
   const ffn_layer_desc& D = p->desc;
   const int wk = D.w_dtype == FFN_F32 ? WK_F32 : D.w_dtype == FFN_F16 ? WK_F16 : WK_I4;
+  if (variant == 1 && p->cache_cap > 0)
+    return fail(FFN_ERR_UNSUPPORTED, "the fused decode variant does not read a neuron cache");
   if (variant == 1 && (!fused_supported(wk, D.d) || D.rank == 0))
     return fail(FFN_ERR_UNSUPPORTED, "the fused decode variant needs fp32 / fp16 rows of "
                 "%d..%d chunks and a predictor", 256, 1024);
@@ -806,6 +955,9 @@ ffn_status ffn_moe_plan(int32_t n_experts, int32_t top_k, const void* w_router,
   if (st != FFN_OK) return st;
   const ffn_layer_desc& D = experts[0]->desc;
   if (D.rank == 0) return fail(FFN_ERR_INVALID_ARGUMENT, "experts need a predictor (rank > 0)");
+  for (int e = 0; e < n_experts && e < MOE_MAX_E; ++e)
+    if (experts[e]->cache_cap > 0)
+      return fail(FFN_ERR_UNSUPPORTED, "expert %d is a neuron-cache plan", e);
   for (int e = 1; e < n_experts; ++e) {
     const ffn_layer_desc& E = experts[e]->desc;
     if (E.d != D.d || E.ffn != D.ffn || E.rank != D.rank || E.act != D.act ||

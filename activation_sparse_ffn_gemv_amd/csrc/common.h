@@ -220,4 +220,6 @@ struct ffn_plan {
   hipEvent_t ev[9][2];          // instrumentation events attached to each stage's dispatch
   int decode_variant;           // batch-1 decode: 0 rank-balanced gather, 1 fused predictor + gather
   int head_words;               // hot head: neurons [0, 32 head_words) always active
+  int cache_cap;                // neuron cache slots (host-resident rows), 0: rows resident
+  size_t off_cache;             // the cache region of the workspace
 };

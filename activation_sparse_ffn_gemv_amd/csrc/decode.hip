@@ -254,7 +254,10 @@ template <int WK, int CPT, int SLOTS> struct Round {
   static constexpr int RN = BASE * SLOTS <= GA_LIST ? BASE : GA_LIST / SLOTS;
 };
 
-template <int WK, int CPT, int SLOTS>
+// CACHED: the neuron-cache variant (fp16 rows): the ranks' neurons and row sources come from
+// the cache plan instead of the bitmap, and rows read from host memory are also written to
+// their cache slot.
+template <int WK, int CPT, int SLOTS, bool CACHED = false>
 __global__ __launch_bounds__(GA_THREADS) void k_gather(GatherArgs a) {
   constexpr int NT = GA_THREADS;
   constexpr int TPR = NT / SLOTS;                 // threads per row
@@ -263,8 +266,11 @@ __global__ __launch_bounds__(GA_THREADS) void k_gather(GatherArgs a) {
   constexpr int RQ = RN * SLOTS;                  // neurons per round
   constexpr int EPC = Kind<WK>::EPC;
   static_assert(RQ <= GA_LIST && GA_LIST % RQ == 0, "rounds tile the rank batch");
+  static_assert(!CACHED || WK == WK_F16, "the neuron cache holds fp16 rows");
   __shared__ int s_wsum[GA_NW];
   __shared__ int s_list[GA_LIST];
+  __shared__ int s_src[CACHED ? GA_LIST : 1];
+  __shared__ int s_vic[CACHED ? GA_LIST : 1];
   __shared__ float s_red[GA_NW][2 * RN];
   __shared__ float s_h[RQ];
   const int tid = threadIdx.x;
@@ -305,7 +311,10 @@ __global__ __launch_bounds__(GA_THREADS) void k_gather(GatherArgs a) {
   // 1. word prefix of the bitmap: thread t owns words 2t, 2t+1 (consecutive)
   const int words = a.ffn / 32;
   uint32_t b[GA_MAXW];
-  int local = 0;
+  int local = 0, total = 0, run0 = 0;
+  if constexpr (CACHED) {
+    total = *a.cnt;                              // written by the cache plan
+  } else {
 #pragma unroll
   for (int k = 0; k < GA_MAXW; ++k) {
     const int w = tid * GA_MAXW + k;
@@ -320,13 +329,14 @@ __global__ __launch_bounds__(GA_THREADS) void k_gather(GatherArgs a) {
   }
   if (lane == WAVE - 1) s_wsum[wave] = v;
   __syncthreads();
-  int base = 0, total = 0;
+  int base = 0;
 #pragma unroll
   for (int k = 0; k < GA_NW; ++k) {
     base += k < wave ? s_wsum[k] : 0;
     total += s_wsum[k];
   }
-  const int run0 = base + v - local;           // rank of this thread's first active neuron
+  run0 = base + v - local;                       // rank of this thread's first active neuron
+  }
   // 32-bit exact: |A| <= 32768 and at most 256 workgroups
   const int r0 = (int)(((uint32_t)total * blockIdx.x) / gridDim.x);
   const int r1 = (int)(((uint32_t)total * (blockIdx.x + 1)) / gridDim.x);
@@ -342,7 +352,13 @@ __global__ __launch_bounds__(GA_THREADS) void k_gather(GatherArgs a) {
     const int nl = min(GA_LIST, r1 - l0);
     // owners of ranks [l0, l0 + nl): every thread whose words hold some of them writes those
     // (no search: a thread knows the ranks of its own active neurons)
-    if (run0 < l0 + nl && run0 + local > l0) {
+    if constexpr (CACHED) {
+      if (tid < nl) {
+        s_list[tid] = a.rank_nid[l0 + tid];
+        s_src[tid] = a.rank_src[l0 + tid];
+        s_vic[tid] = a.rank_vic[l0 + tid];
+      }
+    } else if (run0 < l0 + nl && run0 + local > l0) {
       int pos = run0;
 #pragma unroll
       for (int k = 0; k < GA_MAXW; ++k) {
@@ -372,16 +388,30 @@ __global__ __launch_bounds__(GA_THREADS) void k_gather(GatherArgs a) {
         const int q = r * SLOTS + slot;                      // this slot's r-th neuron
         const bool live_r = t0 + q < nl;                     // uniform across the slot's waves
         const size_t nr = (size_t)s_list[min(t0 + q, nl - 1)];
+        // row bases: the neuron's rows, or (cache) its slot's rows when it is resident
+        size_t row = nr;
+        const char* pu = static_cast<const char*>(a.w_up);
+        const char* pg = static_cast<const char*>(a.w_gate);
+        const char* pd = static_cast<const char*>(a.w_dn);
+        if constexpr (CACHED) {
+          const int sr = s_src[min(t0 + q, nl - 1)];
+          if (sr >= 0) {
+            row = (size_t)sr;
+            pu = static_cast<const char*>(a.c_up);
+            pg = static_cast<const char*>(a.c_gate);
+            pd = static_cast<const char*>(a.c_dn);
+          }
+        }
 #pragma unroll
         for (int k = 0; k < CPT; ++k) {
           const int cc = min(ct + k * TPR, nch - 1);
-          const size_t off = (nr * nch + cc) * 16;
+          const size_t off = (row * nch + cc) * 16;
           wu[r][k] = wg[r][k] = wd[r][k] = u32x4{0u, 0u, 0u, 0u};
           su[r][k] = sg[r][k] = sd[r][k] = 0.0f;
           if (live_r) {
-            wu[r][k] = ld16(static_cast<const char*>(a.w_up) + off);
-            if (a.has_gate) wg[r][k] = ld16(static_cast<const char*>(a.w_gate) + off);
-            wd[r][k] = ld16(static_cast<const char*>(a.w_dn) + off);
+            wu[r][k] = ld16(pu + off);
+            if (a.has_gate) wg[r][k] = ld16(pg + off);
+            wd[r][k] = ld16(pd + off);
             if constexpr (WK == WK_I4) {
               su[r][k] = (float)static_cast<const _Float16*>(a.s_up)[nr * nch + cc];
               if (a.has_gate) sg[r][k] = (float)static_cast<const _Float16*>(a.s_gate)[nr * nch + cc];
@@ -413,6 +443,21 @@ __global__ __launch_bounds__(GA_THREADS) void k_gather(GatherArgs a) {
           if (lane == 0) {
             s_red[wave][2 * r] = pu;
             s_red[wave][2 * r + 1] = pg;
+          }
+          if constexpr (CACHED) {
+            // a row read from host memory goes to its cache slot as well
+            const int vs = s_vic[t0 + r * SLOTS + slot];
+            if (vs >= 0) {
+#pragma unroll
+              for (int k = 0; k < CPT; ++k) {
+                if (ct + k * TPR < nch) {
+                  const size_t off = ((size_t)vs * nch + ct + k * TPR) * 16;
+                  *reinterpret_cast<u32x4*>(static_cast<char*>(a.c_up) + off) = wu[r][k];
+                  if (a.has_gate) *reinterpret_cast<u32x4*>(static_cast<char*>(a.c_gate) + off) = wg[r][k];
+                  *reinterpret_cast<u32x4*>(static_cast<char*>(a.c_dn) + off) = wd[r][k];
+                }
+              }
+            }
           }
         }
       }
@@ -523,7 +568,7 @@ __global__ __launch_bounds__(GA_THREADS) void k_gather(GatherArgs a) {
     }
   }
   // stored last: a store ahead of a barrier would hold this workgroup at the barrier
-  if (blockIdx.x == 0 && tid == 0) *a.cnt = total;
+  if (!CACHED && blockIdx.x == 0 && tid == 0) *a.cnt = total;
   FFN_TRACE_SYNC();
   FFN_TS(1, 5);
   FFN_TV(1, 6, r1 - r0);
@@ -968,18 +1013,18 @@ int gather_cpt(int wk, int d) {
 // one wave of resident workgroups.
 int gather_blocks(int nslot) { return GA_BLOCKS / (nslot < 1 ? 1 : nslot); }
 
-template <int WK, int CPT, int SLOTS>
+template <int WK, int CPT, int SLOTS, bool CACHED = false>
 static hipError_t launch_gather_t(const GatherArgs& a, hipStream_t st, hipEvent_t ev0,
                                   hipEvent_t ev1) {
   // LDS for the slots' accumulator sum (dynamic: only multi-slot variants use it)
   const size_t lds = SLOTS > 1 ? (size_t)(SLOTS - 1) * (GA_THREADS / SLOTS) * CPT *
                                      Kind<WK>::EPC * sizeof(float) : 0;
   if (ev0 && ev1)
-    hipExtLaunchKernelGGL((k_gather<WK, CPT, SLOTS>),
+    hipExtLaunchKernelGGL((k_gather<WK, CPT, SLOTS, CACHED>),
                           dim3(gather_blocks(a.slot ? a.nslot : 1), a.slot ? a.nslot : 1),
                           dim3(GA_THREADS), lds, st, ev0, ev1, 0, a);
   else
-    hipLaunchKernelGGL((k_gather<WK, CPT, SLOTS>),
+    hipLaunchKernelGGL((k_gather<WK, CPT, SLOTS, CACHED>),
                        dim3(gather_blocks(a.slot ? a.nslot : 1), a.slot ? a.nslot : 1),
                        dim3(GA_THREADS), lds, st, a);
   return hipGetLastError();
@@ -1002,6 +1047,18 @@ hipError_t launch_gather(int wk, const GatherArgs& a, hipStream_t st, hipEvent_t
     GA_CASE(WK_I4, 1, 1) GA_CASE(WK_I4, 1, 2) GA_CASE(WK_I4, 1, 4) GA_CASE(WK_I4, 1, 8)
   }
 #undef GA_CASE
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_gather_cached(const GatherArgs& a, hipStream_t st, hipEvent_t ev0,
+                                hipEvent_t ev1) {
+  const int nch = a.d / 8;
+  const int slots = gather_slots(nch);
+  const int cpt = gather_cpt(WK_F16, a.d);
+#define GC_CASE(C, S) \
+  if (cpt == C && slots == S) return launch_gather_t<WK_F16, C, S, true>(a, st, ev0, ev1);
+  GC_CASE(1, 1) GC_CASE(2, 1) GC_CASE(1, 2) GC_CASE(1, 4) GC_CASE(1, 8)
+#undef GC_CASE
   return hipErrorInvalidValue;
 }
 

@@ -71,6 +71,31 @@ struct GatherArgs {
   int nslot;                  // expert slots side by side (grid.y): slot + k, bitmap + k*bstride,
   int bstride, cstride;       //   cnt + k*cstride, part + k*pstride (elements)
   size_t pstride;
+  // neuron cache (host-resident rows): per rank the neuron, the cache slot its rows are read
+  // from (-1: from w_up / w_gate / w_dn, which then point to host memory) and the slot they are
+  // written to on the way (-1: none); |A| is read from cnt
+  const int* rank_nid;
+  const int* rank_src;
+  const int* rank_vic;
+  void* c_up;                 // cache rows [capacity][d]
+  void* c_gate;
+  void* c_dn;
+};
+
+// Neuron cache of host-resident rows (one token): tables and per-rank outputs.
+constexpr int CACHE_MAX_SLOTS = 8192;
+struct CacheArgs {
+  const uint32_t* bitmap;     // [ffn/32] the token's active set
+  int ffn, cap;               // neurons, cache slots
+  int* slot_of;               // [ffn] slot holding the neuron, or -1
+  int* neuron_of;             // [cap] neuron in the slot, or -1
+  uint32_t* last_use;         // [cap] stamp of the last token that used the slot (pinned: ~0)
+  uint32_t* stamp;            // [1] stamp of the last token
+  int* cnt;                   // [1] out: |A|
+  int* rank_nid;              // [ffn] out per rank: neuron, source slot (-1: host), admission slot
+  int* rank_src;
+  int* rank_vic;
+  int* stats;                 // [4] out: hits, misses, admitted, |A|
 };
 
 // Sum of the gather partials (one token).
@@ -116,6 +141,10 @@ int gather_blocks(int nslot = 1);
 int reduce_tiles(int d);
 hipError_t launch_gather(int wk, const GatherArgs& a, hipStream_t st, hipEvent_t ev0 = nullptr,
                          hipEvent_t ev1 = nullptr);
+hipError_t launch_gather_cached(const GatherArgs& a, hipStream_t st, hipEvent_t ev0,
+                                hipEvent_t ev1);
+hipError_t launch_cache_plan(const CacheArgs& a, hipStream_t st);
+hipError_t launch_cache_init(const CacheArgs& a, int n_pinned, hipStream_t st);
 hipError_t launch_reduce(const ReduceArgs& a, hipStream_t st, hipEvent_t ev0 = nullptr,
                          hipEvent_t ev1 = nullptr);
 hipError_t launch_router(const RouterArgs& a, int B, hipStream_t st);

@@ -171,6 +171,46 @@ ffn_status ffn_plan_set_decode_variant(ffn_plan *plan, int32_t variant);
  */
 ffn_status ffn_plan_set_hot_head(ffn_plan *plan, int32_t n_hot);
 
+/*
+ * Neuron cache for layers whose FFN rows live in host memory (citnews.com.cn PowerInfer-2
+ * article, section "Dynamic neuron cache": an in-memory pool of neurons under LRU replacement,
+ * segmented by weight type; neuron-cluster pipelining: neurons waiting for I/O overlap neurons
+ * being computed).  Here the pool is `capacity` slots of HBM holding the up / gate / down rows
+ * of recently used neurons; the predictor (p1, p2, c1, c2) and the biases stay device-resident
+ * (the always-resident segment), and w_up / w_gate / w_down_t are pinned host memory
+ * (hipHostMalloc; anything else gives FFN_ERR_INVALID_ARGUMENT), read over PCIe.
+ *
+ * Per token, after the active set is known: every active neuron found in the pool is read from
+ * its slot, whose last use becomes the token's stamp (a counter starting at 1); the misses, in
+ * ascending neuron order, are read from host memory and admitted to the free or least recently
+ * used slots not used by this token (ascending (last use, slot)), evicting those slots' neurons;
+ * misses beyond them are read without admission.  Neurons [0, n_pinned) are copied into slots
+ * [0, n_pinned) at plan time and never evicted (pair with ffn_plan_set_hot_head).  y is
+ * bit-identical to a plan over the same rows held in device memory.
+ *
+ * fp16 rows and tokens and a predictor are required (FFN_ERR_UNSUPPORTED otherwise); capacity is
+ * a multiple of 32 in [32, min(ffn, 8192)] (FFN_ERR_INVALID_ARGUMENT otherwise); the plan takes
+ * one token per call (max_batch is treated as 1), runs ffn_sparse_forward / ffn_dense_forward
+ * like any plan (variant 0) and is freed with ffn_plan_destroy; it cannot be a mixture expert.
+ * The plan call initialises the pool on `stream` and synchronises it.  The pool's state lives
+ * in the workspace: successive calls share it, so calls must stay ordered; a stamp wraps after
+ * 2^32 - 1 tokens, which this library does not handle.
+ */
+ffn_status ffn_offload_workspace_size(const ffn_layer_desc *desc, int32_t capacity,
+                                      size_t *bytes);
+ffn_status ffn_offload_plan(const ffn_layer_desc *desc, const ffn_layer_weights *weights,
+                            int32_t capacity, int32_t n_pinned, void *workspace,
+                            size_t workspace_bytes, void *stream, ffn_plan **out);
+
+/* Device pointers (inside the plan's workspace, read-only for the caller) to the pool's tables:
+ * slot_of [ffn] (slot of each neuron, or -1), neuron_of [capacity] (or -1), last_use [capacity]
+ * (stamp of the last token that used the slot; pinned slots 0xFFFFFFFF) and stats [4] of the
+ * last call (hits, misses, admitted misses, |A|).  Any output pointer may be NULL.
+ * FFN_ERR_INVALID_ARGUMENT for a plan without a pool. */
+ffn_status ffn_offload_tables(const ffn_plan *plan, const int32_t **slot_of,
+                              const int32_t **neuron_of, const uint32_t **last_use,
+                              const int32_t **stats);
+
 ffn_status ffn_plan_destroy(ffn_plan *plan);
 
 /*

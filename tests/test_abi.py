@@ -181,3 +181,29 @@ def test_moe_validation_before_any_gpu_call():
     finally:
         for p in e + [odd]:
             ffn.ffn_plan_destroy(p)
+
+
+def test_offload_validation_before_any_gpu_call():
+    d = _desc()
+    d.w_dtype, d.x_dtype, d.p_dtype = ffn.FFN_F16, ffn.FFN_F16, ffn.FFN_F16
+    assert ffn.ffn_offload_workspace_size(d, 64) > ffn.ffn_workspace_size(d) // 2
+    for cap in (0, 16, 48, d.ffn + 32, 8192 + 32):              # multiple of 32 in [32, min]
+        with pytest.raises(ffn.FFNError) as e:
+            ffn.ffn_offload_workspace_size(d, cap)
+        assert e.value.status == ffn.FFN_ERR_INVALID_ARGUMENT
+    f32 = _desc()
+    f32.w_dtype = ffn.FFN_F32
+    with pytest.raises(ffn.FFNError) as e:                     # fp16 rows only
+        ffn.ffn_offload_workspace_size(f32, 64)
+    assert e.value.status == ffn.FFN_ERR_UNSUPPORTED
+    w = ffn.ffn_layer_weights(w_up=0x1000, w_gate=0x2000, w_down_t=0x3000, p1=0x4000,
+                              p2=0x5000)
+    with pytest.raises(ffn.FFNError) as e:                     # rows not pinned host memory
+        ffn.ffn_offload_plan(d, w, 64, 0, 0x10000, 1 << 30)
+    assert e.value.status == ffn.FFN_ERR_INVALID_ARGUMENT
+    with pytest.raises(ffn.FFNError) as e:                     # n_pinned beyond the pool
+        ffn.ffn_offload_plan(d, w, 64, 96, 0x10000, 1 << 30)
+    assert e.value.status == ffn.FFN_ERR_INVALID_ARGUMENT
+    with pytest.raises(ffn.FFNError) as e:                     # not a pool plan
+        ffn.ffn_offload_tables(0)
+    assert e.value.status == ffn.FFN_ERR_INVALID_ARGUMENT
