@@ -341,8 +341,9 @@ class OffloadFFN(SparseFFN):
             self.set_hot_head(int(layer["n_hot"]))
 
     def tables(self):
-        """(slot_of [ffn], neuron_of [capacity], last_use [capacity] (as int64), stats [4]) --
-        copies of the pool's device tables."""
+        """(slot_of [ffn], neuron_of [capacity], last_use [capacity] (as int64), stats [8]) --
+        copies of the pool's device tables (stats: the last call's hits, misses, admissions, |A|,
+        then their running totals)."""
         base = self.workspace.data_ptr()
         so, no, lu, st = ffn_offload_tables(self.plan)
 
@@ -350,7 +351,7 @@ class OffloadFFN(SparseFFN):
             return self.workspace[addr - base: addr - base + 4 * n].view(torch.int32)
         last = view(lu, self.capacity).clone().to(torch.int64) & 0xFFFFFFFF
         return (view(so, self.ffn).clone(), view(no, self.capacity).clone(), last,
-                view(st, 4).clone())
+                view(st, 8).clone())
 
 
 class MoEFFN:

@@ -95,7 +95,7 @@ struct CacheArgs {
   int* rank_nid;              // [ffn] out per rank: neuron, source slot (-1: host), admission slot
   int* rank_src;
   int* rank_vic;
-  int* stats;                 // [4] out: hits, misses, admitted, |A|
+  int* stats;                 // [8] out: hits, misses, admitted, |A|; then their running totals
 };
 
 // Sum of the gather partials (one token).

@@ -147,10 +147,12 @@ __global__ __launch_bounds__(CP_THREADS) void k_cache_plan(CacheArgs a) {
   if (tid == 0) {
     *a.stamp = stamp;
     *a.cnt = total;
-    a.stats[0] = hits;
-    a.stats[1] = misses;
-    a.stats[2] = min(misses, avail);
-    a.stats[3] = total;
+    const int st[4] = {hits, misses, min(misses, avail), total};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      a.stats[i] = st[i];
+      a.stats[4 + i] = (int)((uint32_t)a.stats[4 + i] + (uint32_t)st[i]);   // running totals
+    }
   }
 }
 
@@ -162,7 +164,7 @@ __global__ __launch_bounds__(256) void k_cache_init(CacheArgs a, int n_pinned) {
     a.neuron_of[i] = i < n_pinned ? i : -1;
     a.last_use[i] = i < n_pinned ? CP_PINNED : 0u;
   }
-  if (i < 4) a.stats[i] = 0;
+  if (i < 8) a.stats[i] = 0;
   if (i == 0) *a.stamp = 0u;
 }
 

@@ -107,6 +107,12 @@ def main():
                          "smallest (step 32) with this expected recall")
     ap.add_argument("--fit-margin", type=float, default=0.0,
                     help="recall margin of the fitted predictors (residual standard deviations)")
+    ap.add_argument("--offload", type=int, default=0,
+                    help="keep each layer's up/gate/down rows in pinned host memory behind a "
+                         "neuron cache of this many slots per layer (fp16 decode workloads)")
+    ap.add_argument("--pin", type=int, default=0,
+                    help="with --offload: neurons [0, N) stay in the cache for good (use with "
+                         "--hot-head and N = the head)")
     ap.add_argument("--calibrate", type=int, default=0,
                     help="also calibrate layer 0's plan for batches up to this size and report "
                          "its measured crossover densities (fp16 layers)")
@@ -137,6 +143,8 @@ def main():
         raise SystemExit("the mixture workload is measured at batch-1 decode")
     if args.hot_head and (moe or prefill):
         raise SystemExit("--hot-head applies to the single-layer decode workloads")
+    if args.offload and (moe or prefill or Bt != 1 or cfg.w_dtype != "f16"):
+        raise SystemExit("--offload applies to the fp16 single-layer workloads at batch 1")
     K = args.steps if args.steps else (4 if prefill else max(1, cfg.tokens // Bt))
     W = min(args.warmup, K)
     dev = torch.device("cuda", 0)
@@ -195,11 +203,24 @@ def main():
     stream = torch.cuda.Stream(device=dev)
     sp = stream.cuda_stream
     with torch.cuda.stream(stream):
-        probe = ffn.SparseFFN(layers[0][0], max_batch=Bt)
-        ws = torch.empty(probe.ws_bytes, dtype=torch.uint8, device=dev)   # one, shared
-        probe.close()
-        mods = [[ffn.SparseFFN(layers[l][e], max_batch=Bt, workspace=ws) for e in range(E)]
-                for l in range(L)]
+        if args.offload:
+            # rows to pinned host memory; each layer's cache (and its state) in its own workspace
+            t1 = time.time()
+            for row in layers:
+                for k in ("w_up", "w_gate", "w_down_t"):
+                    if row[0].get(k) is not None:
+                        row[0][k] = row[0][k].cpu().pin_memory()
+            torch.cuda.empty_cache()
+            mods = [[ffn.OffloadFFN(layers[l][0], args.offload, n_pinned=args.pin)]
+                    for l in range(L)]
+            log("rows of %d layers in pinned host memory (%.1f s); %d-slot cache per layer, %d "
+                "pinned" % (L, time.time() - t1, args.offload, args.pin))
+        else:
+            probe = ffn.SparseFFN(layers[0][0], max_batch=Bt)
+            ws = torch.empty(probe.ws_bytes, dtype=torch.uint8, device=dev)   # one, shared
+            probe.close()
+            mods = [[ffn.SparseFFN(layers[l][e], max_batch=Bt, workspace=ws) for e in range(E)]
+                    for l in range(L)]
         moes = None
         if moe:
             n = ffn.ffn_moe_workspace_size(E, cfg.top_k, mods[0][0].plan)
@@ -311,10 +332,10 @@ def main():
             pm.scatter_(1, torch.where(valid, qi.long(), 0), valid)
             xs = x[l, :ns].double()
             w_src, b_src = sfit.source(layers[l][0])
-            tm = (xs @ w_src.T + b_src) > 0
+            tm = (xs @ w_src.to(dev).T + b_src.to(dev)) > 0
             if cfg.act == "drelu":
                 w_u, b_u = sfit.source(dict(layers[l][0], act="relu"))
-                tm &= (xs @ w_u.T + b_u) > 0
+                tm &= (xs @ w_u.to(dev).T + b_u.to(dev)) > 0
             del w_src
             tp += int((pm & tm).sum())
             npred += int(pm.sum())
@@ -349,6 +370,7 @@ def main():
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    tot0 = [m[0].tables()[3][4:].double() for m in mods] if args.offload else None
     with torch.cuda.stream(stream):
         e0.record(stream)
         for g in graphs:
@@ -356,6 +378,19 @@ def main():
         e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1)
+    offload = None
+    if args.offload:
+        # cache counters over the timed steps (running totals, modulo 2^32)
+        dt = sum((m[0].tables()[3][4:].double() - t0v) % 2.0 ** 32 for m, t0v in zip(mods, tot0))
+        hits, misses, adm, act = [float(v) for v in dt]
+        pcie = misses * (n_rows(cfg) * row_bytes(cfg))
+        offload = {"capacity": args.offload, "pinned": args.pin,
+                   "hit_rate": round(hits / max(act, 1.0), 4),
+                   "admitted_per_token_layer": round(adm / (K * L), 2),
+                   "pcie_bytes_per_token": int(pcie / K),
+                   "pcie_gbps": round(pcie / (ms / 1e3) / 1e9, 2)}
+        log("cache: hit rate %.4f, %.1f MB per token over PCIe (%.1f GB/s)" % (
+            offload["hit_rate"], pcie / K / 1e6, offload["pcie_gbps"]))
     tok_s = K * Bt / (ms / 1e3)
     eff_gbps = touched.sum() / (ms / 1e3) / 1e9
     log("timed %d step(s): %.3f ms/step, %.1f tokens/s, %.1f GB/s effective over touched bytes"
@@ -434,7 +469,8 @@ def main():
                 "flops_per_launch": stages[dom]["flops_per_launch"]}
     else:
         wl = ((cfg.name if Bt == 1 else cfg.name + ":batch%d" % Bt) + (":hot" if n_hot else "")
-              + (":fit" if fitq is not None or cfg.spectrum_alpha else ""))
+              + (":fit" if fitq is not None or cfg.spectrum_alpha else "")
+              + (":offload" if args.offload else ""))
         roof = {"bound": "hbm", "kernel": knames[dom], "achieved": stages[dom]["gbps"],
                 "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(stages[dom]["gbps"] / HBM_PEAK_GBPS, 4),
@@ -570,6 +606,7 @@ def main():
                    "experts": cfg.n_experts, "top_k": cfg.top_k if moe else None,
                    "target_density": cfg.density, "measured_density": round(density, 5)},
         "predictor": quality,
+        "offload": offload,
         "effective_gbps": round(eff_gbps, 1),
         "touched_bytes_per_step": int(touched.sum() / K),
         "roofline": roof,

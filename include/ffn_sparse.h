@@ -204,8 +204,9 @@ ffn_status ffn_offload_plan(const ffn_layer_desc *desc, const ffn_layer_weights 
 
 /* Device pointers (inside the plan's workspace, read-only for the caller) to the pool's tables:
  * slot_of [ffn] (slot of each neuron, or -1), neuron_of [capacity] (or -1), last_use [capacity]
- * (stamp of the last token that used the slot; pinned slots 0xFFFFFFFF) and stats [4] of the
- * last call (hits, misses, admitted misses, |A|).  Any output pointer may be NULL.
+ * (stamp of the last token that used the slot; pinned slots 0xFFFFFFFF) and stats [8]: the
+ * last call's hits, misses, admitted misses and |A|, then the same four summed over every call
+ * since the plan was made (modulo 2^32).  Any output pointer may be NULL.
  * FFN_ERR_INVALID_ARGUMENT for a plan without a pool. */
 ffn_status ffn_offload_tables(const ffn_plan *plan, const int32_t **slot_of,
                               const int32_t **neuron_of, const uint32_t **last_use,

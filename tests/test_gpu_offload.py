@@ -43,6 +43,7 @@ def _run_pair(ffn, cfg, capacity, n_tokens, n_pinned=0, hot=False, layer_no=0):
     x = synth.make_tokens(cfg, n_tokens, layer=layer_no, salt=7).cuda()
     F = cfg.ffn
     out = []
+    tot = [0, 0, 0, 0]
     for t in range(n_tokens):
         ys = []
         lists = []
@@ -63,7 +64,9 @@ def _run_pair(ffn, cfg, capacity, n_tokens, n_pinned=0, hot=False, layer_no=0):
         assert np.array_equal(last_use.cpu().numpy(), model.last_use), t
         hits = sum(s >= 0 for s in src)
         adm = sum(v >= 0 for v in victim)
-        assert stats.cpu().tolist() == [hits, len(src) - hits, adm, len(src)], t
+        assert stats.cpu().tolist()[:4] == [hits, len(src) - hits, adm, len(src)], t
+        tot = [tot[0] + hits, tot[1] + len(src) - hits, tot[2] + adm, tot[3] + len(src)]
+        assert stats.cpu().tolist()[4:] == tot, t
         out.append((x[t].cpu().numpy(), lists[1], ys[1][0].cpu().numpy(), hits, adm))
     res.close()
     off.close()
