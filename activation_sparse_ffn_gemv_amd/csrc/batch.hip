@@ -7,7 +7,8 @@
 // units (32x32 tiles, M = the pass's tokens, zero-padded):
 //   k_bz     Z = X P1^T, split over K            (predictor stage 1; partial sums per K slice)
 //   k_bzr    z = sum of the K slices + c1, split into fp16 hi + lo parts (z = hi + lo to ~2^-22)
-//   k_bs     S = Z P2^T + c2 (hi and lo MFMAs); per-token bitmap words by ballot; union words
+//   k_bs     S = Z P2^T + c2 (hi and lo MFMAs) for 128 neurons per workgroup, Z streamed through
+//            LDS; per-token bitmap words by ballot; union words
 //   k_bug    for 32 union neurons (by rank) per workgroup: U = X W_up^T, G = X W_gate^T;
 //            h = act(u, g), zero where the token's own set excludes the neuron; H in fp16
 //   k_bdown  Y_s = H[:, seg s] W_down_t[U_s]: split over union segments and 256-column tiles
@@ -137,44 +138,90 @@ __global__ __launch_bounds__(256) void k_bzr(BatchArgs a) {
   a.zhl[(size_t)MB * a.r + e] = lo;
 }
 
-// Predictor stage 2 for 32 neurons (one bitmap word per token): S = Z P2^T + c2.
+// Predictor stage 2 for 128 neurons (four bitmap words per token) per workgroup:
+// S = Z P2^T + c2.  Wave w owns the 32 neurons of word 4 b + w over the whole rank, so its
+// sums need no reduction; Z (hi and lo rows of the pass's tokens) streams through LDS in chunks
+// of BS_KC ranks that the four waves share, and the next chunk's Z and P2 loads are in flight
+// while the current chunk's MFMAs run.
+constexpr int BS_KC = 256;                 // ranks per chunk
+constexpr int BS_PC = BS_KC / 8;           // 16-byte pieces of a row per chunk (32)
+constexpr int BS_LD = BS_PC + 1;           // padded LDS row
+constexpr int BS_ZL = 2 * MB * BS_PC / BT; // Z pieces per thread and chunk (8)
+
 __global__ __launch_bounds__(BT) void k_bs(BatchArgs a) {
-  __shared__ float red[3 * 16 * WAVE];
-  const int lane = threadIdx.x & (WAVE - 1), wave = threadIdx.x / WAVE;
-  if ((int)blockIdx.x < a.head_words) {        // hot head: every token's word set, no score
-    const int W = a.ffn / 32;
-    if ((int)threadIdx.x < min(a.B, MB)) a.bits[(size_t)threadIdx.x * W + blockIdx.x] = ~0u;
-    if (threadIdx.x == 0) a.ubits[blockIdx.x] = ~0u;
-    return;
+  __shared__ u32x4 s_z[2][2][MB * BS_LD];  // [buffer][hi, lo][token row][piece]
+  const int tid = threadIdx.x, lane = tid & (WAVE - 1), wave = tid / WAVE;
+  const int W = a.ffn / 32;
+  const int word = blockIdx.x * 4 + wave;
+  const bool head = word < a.head_words;   // hot head: every token's word set, no score
+  const bool live = word < W && !head;     // uniform per wave
+  if (word < W && head) {
+    if (lane < min(a.B, MB)) a.bits[(size_t)lane * W + word] = ~0u;
+    if (lane == 0) a.ubits[word] = ~0u;
   }
-  const int n0 = blockIdx.x * 32, row = lane & 31, g = lane >> 5;
-  const int rch = a.r / 8, nsteps = (rch + 1) / 2;
-  const char* pr = static_cast<const char*>(a.p2) + (size_t)(n0 + row) * a.r * 2;
-  const char* zh = reinterpret_cast<const char*>(a.zhl + (size_t)row * a.r);
-  const char* zl = reinterpret_cast<const char*>(a.zhl + (size_t)(MB + row) * a.r);
+  const int n0 = word * 32, row = lane & 31, g = lane >> 5;
+  const int rch = a.r / 8;
+  const int nchunk = (rch + BS_PC - 1) / BS_PC;
+  const char* pr = static_cast<const char*>(a.p2) + (size_t)min(n0 + row, a.ffn - 1) * a.r * 2;
+  const char* zb = reinterpret_cast<const char*>(a.zhl);
+
+  auto load_z = [&](int c, u32x4 (&z)[BS_ZL]) {
+#pragma unroll
+    for (int i = 0; i < BS_ZL; ++i) {
+      const int e = tid + BT * i;          // (hl, token row, piece)
+      const int hl = e / (MB * BS_PC), zr = (e / BS_PC) % MB, zc = e % BS_PC;
+      const int pc = c * BS_PC + zc;
+      const u32x4 v = ld16(zb + (((size_t)hl * MB + zr) * a.r) * 2 + (size_t)min(pc, rch - 1) * 16);
+      z[i] = pc < rch ? v : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  auto store_z = [&](int buf, const u32x4 (&z)[BS_ZL]) {
+#pragma unroll
+    for (int i = 0; i < BS_ZL; ++i) {
+      const int e = tid + BT * i;
+      const int hl = e / (MB * BS_PC), zr = (e / BS_PC) % MB, zc = e % BS_PC;
+      s_z[buf][hl][zr * BS_LD + zc] = z[i];
+    }
+  };
+  // P2 row pieces of this lane for chunk c: step s reads piece c * BS_PC + 2 s + g
+  auto load_p = [&](int c, u32x4 (&b)[BS_PC / 2]) {
+#pragma unroll
+    for (int s = 0; s < BS_PC / 2; ++s) {
+      const int pc = c * BS_PC + 2 * s + g;
+      const u32x4 v = ld16(pr + (size_t)min(pc, rch - 1) * 16);
+      b[s] = (live && pc < rch) ? v : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+
   f32x16 acc = {};
-  for (int s0 = wave; s0 < nsteps; s0 += 4 * GRP) {
-    u32x4 ah[GRP], al[GRP], bv[GRP];
-#pragma unroll
-    for (int j = 0; j < GRP; ++j) {
-      const int c = 2 * (s0 + 4 * j) + g;
-      const int cc = min(c, rch - 1);
-      const bool ok = s0 + 4 * j < nsteps && c < rch;
-      const u32x4 bl = ld16(pr + (size_t)cc * 16);
-      ah[j] = ld16(zh + (size_t)cc * 16);
-      al[j] = ld16(zl + (size_t)cc * 16);
-      bv[j] = ok ? bl : u32x4{0u, 0u, 0u, 0u};
+  u32x4 zn[BS_ZL], bc[BS_PC / 2], bn[BS_PC / 2];
+  load_z(0, zn);
+  load_p(0, bc);
+  store_z(0, zn);
+  __syncthreads();
+  for (int c = 0; c < nchunk; ++c) {
+    const int buf = c & 1;
+    if (c + 1 < nchunk) {
+      load_z(c + 1, zn);
+      load_p(c + 1, bn);
     }
-    issue_fence();
+    if (live) {
 #pragma unroll
-    for (int j = 0; j < GRP; ++j) {
-      acc = mma16(ah[j], bv[j], acc);
-      acc = mma16(al[j], bv[j], acc);
+      for (int s = 0; s < BS_PC / 2; ++s) {
+        const u32x4 ah = s_z[buf][0][row * BS_LD + 2 * s + g];
+        const u32x4 al = s_z[buf][1][row * BS_LD + 2 * s + g];
+        acc = mma16(ah, bc[s], acc);
+        acc = mma16(al, bc[s], acc);
+      }
     }
+    if (c + 1 < nchunk) {
+      store_z(buf ^ 1, zn);
+#pragma unroll
+      for (int s = 0; s < BS_PC / 2; ++s) bc[s] = bn[s];
+    }
+    __syncthreads();
   }
-  acc = wg_sum4(acc, red);
-  if (wave == 0) {
-    const int W = a.ffn / 32;
+  if (live) {
     const float c2v = a.c2 ? a.c2[n0 + row] : 0.0f;
     uint32_t uw = 0u;
 #pragma unroll
@@ -186,11 +233,11 @@ __global__ __launch_bounds__(BT) void k_bs(BatchArgs a) {
       const unsigned long long bal = __ballot(on);
       const int m0 = 8 * (i >> 2) + (i & 3);          // lanes 0..31: token m0; 32..63: m0 + 4
       // rows of tokens past B are never read (and may lie past the caller's bitmap rows)
-      if (lane == 0 && m0 < a.B) a.bits[(size_t)m0 * W + blockIdx.x] = (uint32_t)bal;
-      if (lane == 32 && m0 + 4 < a.B) a.bits[(size_t)(m0 + 4) * W + blockIdx.x] = (uint32_t)(bal >> 32);
+      if (lane == 0 && m0 < a.B) a.bits[(size_t)m0 * W + word] = (uint32_t)bal;
+      if (lane == 32 && m0 + 4 < a.B) a.bits[(size_t)(m0 + 4) * W + word] = (uint32_t)(bal >> 32);
       uw |= (uint32_t)bal | (uint32_t)(bal >> 32);
     }
-    if (lane == 0) a.ubits[blockIdx.x] = uw;
+    if (lane == 0) a.ubits[word] = uw;
   }
 }
 
@@ -595,7 +642,7 @@ hipError_t launch_batch_sets(const BatchArgs& a, int use_predictor, hipStream_t 
   if (use_predictor) {
     hipLaunchKernelGGL(k_bz, dim3((a.r + 31) / 32, a.ks), dim3(BT), 0, st, a);
     hipLaunchKernelGGL(k_bzr, dim3((MB * a.r + 255) / 256), dim3(256), 0, st, a);
-    hipLaunchKernelGGL(k_bs, dim3(W), dim3(BT), 0, st, a);
+    hipLaunchKernelGGL(k_bs, dim3((W + 3) / 4), dim3(BT), 0, st, a);
   } else {
     hipLaunchKernelGGL(k_bmask, dim3((W + 255) / 256), dim3(256), 0, st, a);
   }

@@ -62,6 +62,7 @@ BATCH_SHAPES = [
     dict(d=520, ffn=1184, rank=40, act="drelu", bias_gate=True, bias_up=True, bias_down=True),
     dict(d=136, ffn=1056, rank=24, act="reglu", bias_gate=True),
     dict(d=264, ffn=1056, rank=24, act="relu", bias_up=True),      # odd number of 32-row tiles
+    dict(d=1024, ffn=1120, rank=520, act="drelu", bias_gate=True, bias_up=True),  # ragged rank chunks
 ]
 
 
