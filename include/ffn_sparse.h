@@ -190,8 +190,11 @@ ffn_status ffn_plan_set_hot_head(ffn_plan *plan, int32_t n_hot);
  *
  * fp16 rows and tokens and a predictor are required (FFN_ERR_UNSUPPORTED otherwise); capacity is
  * a multiple of 32 in [32, min(ffn, 8192)] (FFN_ERR_INVALID_ARGUMENT otherwise); the plan takes
- * one token per call (max_batch is treated as 1), runs ffn_sparse_forward / ffn_dense_forward
- * like any plan (variant 0) and is freed with ffn_plan_destroy; it cannot be a mixture expert.
+ * one token per call (max_batch is treated as 1) and is freed with ffn_plan_destroy; it cannot
+ * be a mixture expert, and runs decode variant 0 only.  ffn_sparse_forward with path SPARSE or
+ * AUTO (predicted sets or a caller mask) goes through the pool; path DENSE and ffn_dense_forward
+ * read every row once straight from host memory and leave the pool as it was (a dense call
+ * would only churn it).
  * The plan call initialises the pool on `stream` and synchronises it.  The pool's state lives
  * in the workspace: successive calls share it, so calls must stay ordered; a stamp wraps after
  * 2^32 - 1 tokens, which this library does not handle.

@@ -139,3 +139,35 @@ def test_offload_graph_replay_matches_eager(ffn):
         assert torch.equal(a, b)
     eager.close()
     graph.close()
+
+
+def test_offload_dense_and_caller_mask(ffn):
+    """A caller mask goes through the pool like a predicted set; the dense FFN reads every row
+    straight from host memory and leaves the pool as it was.  Both bit-identical to the
+    resident layer, the pool following the model."""
+    cfg = synth.small_config(d=1024, ffn=2048, rank=64, act="drelu", w_dtype="f16",
+                             x_dtype="f16", p_dtype="f16", density=0.1, bias_gate=True,
+                             bias_up=True, bias_down=True)
+    L = to_device(synth.make_layer(cfg, device="cuda"))
+    res = ffn.SparseFFN(L, max_batch=1)
+    off = ffn.OffloadFFN(_host_rows(L), 256)
+    model = oracle.NeuronCache(cfg.ffn, 256)
+    x = synth.make_tokens(cfg, 3, salt=11).cuda()
+    rng = np.random.default_rng(4)
+    for t in range(3):
+        y0 = res.dense(x[t:t + 1]).clone()
+        y1 = off.dense(x[t:t + 1]).clone()
+        torch.cuda.synchronize()
+        assert torch.equal(y0, y1)
+        mask = (rng.random(cfg.ffn) < 0.2).astype(np.uint8)
+        mt = torch.from_numpy(mask).cuda().view(1, -1)
+        y0 = res.forward(x[t:t + 1], mask=mt).clone()
+        y1 = off.forward(x[t:t + 1], mask=mt).clone()
+        torch.cuda.synchronize()
+        assert torch.equal(y0, y1)
+        model.step(np.flatnonzero(mask))
+        slot_of, neuron_of, last_use, stats = off.tables()
+        assert np.array_equal(neuron_of.cpu().numpy(), model.neuron_of)
+        assert np.array_equal(last_use.cpu().numpy(), model.last_use)
+    res.close()
+    off.close()
