@@ -56,12 +56,12 @@ __device__ __forceinline__ int xcd_tile(int total) {
 }  // namespace
 
 // k_dup: 256 tokens x 256 neurons (ReLU) or 256 x 128 neurons with their gate rows per
-// workgroup of 8 waves; both operands staged through LDS per K stage of 32, double-buffered, with
+// workgroup of 8 waves; both operands staged through LDS per K stage of 64, double-buffered, with
 // the global loads of the next stage in flight during the current one's MFMAs.  Wave w owns
 // tokens 64 (w / 2) .. +63 and half of the tile's neurons (w % 2).
 constexpr int UP_T = 512;                  // threads
 constexpr int UP_M = 256;                  // tokens per tile
-constexpr int UP_KC = 4;                   // 16-byte chunks per row per stage (K = 32)
+constexpr int UP_KC = 8;                   // 16-byte chunks per row per stage (K = 64)
 constexpr int UP_LD = UP_KC + 1;           // padded LDS row
 
 template <bool GATE>
@@ -70,8 +70,8 @@ __global__ __launch_bounds__(UP_T) void k_dup(DenseArgs a) {
   constexpr int UP_N = GATE ? 128 : 256;   // neurons per tile
   constexpr int BROWS = UP_N * NMAT;       // weight rows per stage (up rows, then gate rows)
   constexpr int NSUB = UP_N / 2 / 32;      // 32-neuron MFMA blocks per wave
-  constexpr int LA = UP_M * UP_KC / UP_T;  // A chunk loads per thread and stage (2)
-  constexpr int LB = BROWS * UP_KC / UP_T; // B chunk loads per thread and stage (2)
+  constexpr int LA = UP_M * UP_KC / UP_T;  // A chunk loads per thread and stage (4)
+  constexpr int LB = BROWS * UP_KC / UP_T; // B chunk loads per thread and stage (4)
   __shared__ u32x4 sA[2][UP_M * UP_LD];
   __shared__ u32x4 sB[2][BROWS * UP_LD];
   if (a.run_if && *a.run_if != a.run_want) return;
@@ -151,7 +151,7 @@ __global__ __launch_bounds__(UP_T) void k_dup(DenseArgs a) {
     const int buf = s & 1;
     if (s + 2 < nstage) load(s + 2, ra2, rb2);
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
+    for (int kk = 0; kk < UP_KC / 2; ++kk) {
       u32x4 af[2];
 #pragma unroll
       for (int ms = 0; ms < 2; ++ms)
