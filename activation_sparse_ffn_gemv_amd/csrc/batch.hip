@@ -139,23 +139,27 @@ __global__ __launch_bounds__(256) void k_bzr(BatchArgs a) {
 }
 
 // Predictor stage 2 for 128 neurons (four bitmap words per token) per workgroup:
-// S = Z P2^T + c2.  Wave w owns the 32 neurons of word 4 b + w over the whole rank, so its
-// sums need no reduction; Z (hi and lo rows of the pass's tokens) streams through LDS in chunks
-// of BS_KC ranks that the four waves share, and the next chunk's Z and P2 loads are in flight
-// while the current chunk's MFMAs run.
+// S = Z P2^T + c2.  Eight waves: waves w and w + 4 own the 32 neurons of word 4 b + w, each
+// taking half of every chunk's rank steps (their two sums are added once, at the end); Z (hi and
+// lo rows of the pass's tokens) streams through LDS in chunks of BS_KC ranks that all eight
+// waves share, and the next chunk's Z and P2 loads are in flight while the current chunk's MFMAs
+// run.
+constexpr int BS_T = 512;                  // threads: 8 waves
 constexpr int BS_KC = 256;                 // ranks per chunk
 constexpr int BS_PC = BS_KC / 8;           // 16-byte pieces of a row per chunk (32)
+constexpr int BS_SW = BS_PC / 4;           // MFMA steps per wave and chunk (8: half the chunk)
 constexpr int BS_LD = BS_PC + 1;           // padded LDS row
-constexpr int BS_ZL = 2 * MB * BS_PC / BT; // Z pieces per thread and chunk (8)
+constexpr int BS_ZL = 2 * MB * BS_PC / BS_T; // Z pieces per thread and chunk (4)
 
-__global__ __launch_bounds__(BT) void k_bs(BatchArgs a) {
+__global__ __launch_bounds__(BS_T) void k_bs(BatchArgs a) {
   __shared__ u32x4 s_z[2][2][MB * BS_LD];  // [buffer][hi, lo][token row][piece]
   const int tid = threadIdx.x, lane = tid & (WAVE - 1), wave = tid / WAVE;
   const int W = a.ffn / 32;
-  const int word = blockIdx.x * 4 + wave;
+  const int tw = wave & 3, kh = wave >> 2; // word of the workgroup, half of each chunk
+  const int word = blockIdx.x * 4 + tw;
   const bool head = word < a.head_words;   // hot head: every token's word set, no score
   const bool live = word < W && !head;     // uniform per wave
-  if (word < W && head) {
+  if (kh == 0 && word < W && head) {
     if (lane < min(a.B, MB)) a.bits[(size_t)lane * W + word] = ~0u;
     if (lane == 0) a.ubits[word] = ~0u;
   }
@@ -168,7 +172,7 @@ __global__ __launch_bounds__(BT) void k_bs(BatchArgs a) {
   auto load_z = [&](int c, u32x4 (&z)[BS_ZL]) {
 #pragma unroll
     for (int i = 0; i < BS_ZL; ++i) {
-      const int e = tid + BT * i;          // (hl, token row, piece)
+      const int e = tid + BS_T * i;        // (hl, token row, piece)
       const int hl = e / (MB * BS_PC), zr = (e / BS_PC) % MB, zc = e % BS_PC;
       const int pc = c * BS_PC + zc;
       const u32x4 v = ld16(zb + (((size_t)hl * MB + zr) * a.r) * 2 + (size_t)min(pc, rch - 1) * 16);
@@ -178,23 +182,24 @@ __global__ __launch_bounds__(BT) void k_bs(BatchArgs a) {
   auto store_z = [&](int buf, const u32x4 (&z)[BS_ZL]) {
 #pragma unroll
     for (int i = 0; i < BS_ZL; ++i) {
-      const int e = tid + BT * i;
+      const int e = tid + BS_T * i;
       const int hl = e / (MB * BS_PC), zr = (e / BS_PC) % MB, zc = e % BS_PC;
       s_z[buf][hl][zr * BS_LD + zc] = z[i];
     }
   };
-  // P2 row pieces of this lane for chunk c: step s reads piece c * BS_PC + 2 s + g
-  auto load_p = [&](int c, u32x4 (&b)[BS_PC / 2]) {
+  // P2 row pieces of this lane for chunk c: step s (of this wave's half) reads piece
+  // c * BS_PC + 2 (kh BS_SW + s) + g
+  auto load_p = [&](int c, u32x4 (&b)[BS_SW]) {
 #pragma unroll
-    for (int s = 0; s < BS_PC / 2; ++s) {
-      const int pc = c * BS_PC + 2 * s + g;
+    for (int s = 0; s < BS_SW; ++s) {
+      const int pc = c * BS_PC + 2 * (kh * BS_SW + s) + g;
       const u32x4 v = ld16(pr + (size_t)min(pc, rch - 1) * 16);
       b[s] = (live && pc < rch) ? v : u32x4{0u, 0u, 0u, 0u};
     }
   };
 
   f32x16 acc = {};
-  u32x4 zn[BS_ZL], bc[BS_PC / 2], bn[BS_PC / 2];
+  u32x4 zn[BS_ZL], bc[BS_SW], bn[BS_SW];
   load_z(0, zn);
   load_p(0, bc);
   store_z(0, zn);
@@ -207,9 +212,10 @@ __global__ __launch_bounds__(BT) void k_bs(BatchArgs a) {
     }
     if (live) {
 #pragma unroll
-      for (int s = 0; s < BS_PC / 2; ++s) {
-        const u32x4 ah = s_z[buf][0][row * BS_LD + 2 * s + g];
-        const u32x4 al = s_z[buf][1][row * BS_LD + 2 * s + g];
+      for (int s = 0; s < BS_SW; ++s) {
+        const int pcs = 2 * (kh * BS_SW + s) + g;
+        const u32x4 ah = s_z[buf][0][row * BS_LD + pcs];
+        const u32x4 al = s_z[buf][1][row * BS_LD + pcs];
         acc = mma16(ah, bc[s], acc);
         acc = mma16(al, bc[s], acc);
       }
@@ -217,11 +223,21 @@ __global__ __launch_bounds__(BT) void k_bs(BatchArgs a) {
     if (c + 1 < nchunk) {
       store_z(buf ^ 1, zn);
 #pragma unroll
-      for (int s = 0; s < BS_PC / 2; ++s) bc[s] = bn[s];
+      for (int s = 0; s < BS_SW; ++s) bc[s] = bn[s];
     }
     __syncthreads();
   }
-  if (live) {
+  // the second half's sums join the first's (the Z buffers are free now)
+  float* red = reinterpret_cast<float*>(&s_z[0][0][0]);   // [4 words][16][64]
+  static_assert(sizeof(s_z) >= 4 * 16 * WAVE * sizeof(float), "sums fit in the Z buffers");
+  if (kh == 1) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) red[(tw * 16 + i) * WAVE + lane] = acc[i];
+  }
+  __syncthreads();
+  if (kh == 0 && live) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] += red[(tw * 16 + i) * WAVE + lane];
     const float c2v = a.c2 ? a.c2[n0 + row] : 0.0f;
     uint32_t uw = 0u;
 #pragma unroll
@@ -642,7 +658,7 @@ hipError_t launch_batch_sets(const BatchArgs& a, int use_predictor, hipStream_t 
   if (use_predictor) {
     hipLaunchKernelGGL(k_bz, dim3((a.r + 31) / 32, a.ks), dim3(BT), 0, st, a);
     hipLaunchKernelGGL(k_bzr, dim3((MB * a.r + 255) / 256), dim3(256), 0, st, a);
-    hipLaunchKernelGGL(k_bs, dim3((W + 3) / 4), dim3(BT), 0, st, a);
+    hipLaunchKernelGGL(k_bs, dim3((W + 3) / 4), dim3(BS_T), 0, st, a);
   } else {
     hipLaunchKernelGGL(k_bmask, dim3((W + 255) / 256), dim3(256), 0, st, a);
   }
