@@ -30,7 +30,7 @@ namespace ffn {
 
 constexpr int MB = BATCH_TILE;     // tokens per pass
 constexpr int BT = 256;            // threads per workgroup: 4 waves
-constexpr int GRP = 8;             // 16-k steps whose loads are issued together
+constexpr int BZ_GRP = 16;         // predictor stage 1: 16-k steps whose loads are issued together
 constexpr int DN_CH = 512;         // union ranks staged in LDS at a time by k_bdown
 constexpr int DN_COLS = 256;       // columns of y per k_bdown workgroup
 constexpr int GRPD = 4;            // 8-rank steps whose loads k_bdown issues together
@@ -91,21 +91,24 @@ __global__ __launch_bounds__(BT) void k_bz(BatchArgs a) {
   const char* pr = static_cast<const char*>(a.p1) + (size_t)min(n0 + row, a.r - 1) * a.d * 2;
   const char* xr = static_cast<const char*>(a.x) + (size_t)min(row, a.B - 1) * a.d * 2;
   f32x16 acc = {};
-  for (int s = s0; s < s1; s += GRP) {
-    u32x4 av[GRP], bv[GRP];
+  for (int s = s0; s < s1; s += BZ_GRP) {
+    u32x4 av[BZ_GRP], bv[BZ_GRP];
 #pragma unroll
-    for (int j = 0; j < GRP; ++j) {
-      const int c = 2 * (s + j) + g;
-      const int cc = min(c, nchk - 1);
-      const bool ok = s + j < s1 && c < nchk;
-      const u32x4 bl = ld16(pr + (size_t)cc * 16);
-      const u32x4 al = ld16(xr + (size_t)cc * 16);
-      bv[j] = (ok && pok) ? bl : u32x4{0u, 0u, 0u, 0u};
-      av[j] = (ok && xok) ? al : u32x4{0u, 0u, 0u, 0u};
+    for (int j = 0; j < BZ_GRP; ++j) {
+      av[j] = bv[j] = u32x4{0u, 0u, 0u, 0u};
+      if (s + j < s1) {                                   // uniform across the wave
+        const int c = 2 * (s + j) + g;
+        const int cc = min(c, nchk - 1);
+        const u32x4 bl = ld16(pr + (size_t)cc * 16);
+        const u32x4 al = ld16(xr + (size_t)cc * 16);
+        bv[j] = (c < nchk && pok) ? bl : u32x4{0u, 0u, 0u, 0u};
+        av[j] = (c < nchk && xok) ? al : u32x4{0u, 0u, 0u, 0u};
+      }
     }
     issue_fence();
 #pragma unroll
-    for (int j = 0; j < GRP; ++j) acc = mma16(av[j], bv[j], acc);
+    for (int j = 0; j < BZ_GRP; ++j)
+      if (s + j < s1) acc = mma16(av[j], bv[j], acc);
   }
   acc = wg_sum4(acc, red);
   if (wave == 0 && n0 + row < a.r) {
