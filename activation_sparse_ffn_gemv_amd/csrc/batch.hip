@@ -143,19 +143,22 @@ __global__ __launch_bounds__(256) void k_bzr(BatchArgs a) {
 
 // Predictor stage 2 for 128 neurons (four bitmap words per token) per workgroup:
 // S = Z P2^T + c2.  Eight waves: waves w and w + 4 own the 32 neurons of word 4 b + w, each
-// taking half of every chunk's rank steps (their two sums are added once, at the end); Z (hi and
-// lo rows of the pass's tokens) streams through LDS in chunks of BS_KC ranks that all eight
-// waves share, and the next chunk's Z and P2 loads are in flight while the current chunk's MFMAs
-// run.
+// taking half of every chunk's rank steps (their two sums are added once, at the end).  Both
+// operands stream through LDS in chunks of BS_KC ranks, loaded with whole contiguous row pieces
+// (a wave's load instruction covers four P2 rows' 256 bytes), the next two chunks in flight
+// while the current chunk's MFMAs run.
 constexpr int BS_T = 512;                  // threads: 8 waves
-constexpr int BS_KC = 256;                 // ranks per chunk
-constexpr int BS_PC = BS_KC / 8;           // 16-byte pieces of a row per chunk (32)
-constexpr int BS_SW = BS_PC / 4;           // MFMA steps per wave and chunk (8: half the chunk)
+constexpr int BS_N = 128;                  // neurons per workgroup
+constexpr int BS_KC = 128;                 // ranks per chunk
+constexpr int BS_PC = BS_KC / 8;           // 16-byte pieces of a row per chunk (16)
+constexpr int BS_SW = BS_PC / 4;           // MFMA steps per wave and chunk (4: half the chunk)
 constexpr int BS_LD = BS_PC + 1;           // padded LDS row
-constexpr int BS_ZL = 2 * MB * BS_PC / BS_T; // Z pieces per thread and chunk (4)
+constexpr int BS_ZL = 2 * MB * BS_PC / BS_T;   // Z pieces per thread and chunk (2)
+constexpr int BS_PL = BS_N * BS_PC / BS_T;     // P2 pieces per thread and chunk (4)
 
 __global__ __launch_bounds__(BS_T) void k_bs(BatchArgs a) {
   __shared__ u32x4 s_z[2][2][MB * BS_LD];  // [buffer][hi, lo][token row][piece]
+  __shared__ u32x4 s_p[2][BS_N * BS_LD];   // [buffer][neuron][piece]
   const int tid = threadIdx.x, lane = tid & (WAVE - 1), wave = tid / WAVE;
   const int W = a.ffn / 32;
   const int tw = wave & 3, kh = wave >> 2; // word of the workgroup, half of each chunk
@@ -166,13 +169,14 @@ __global__ __launch_bounds__(BS_T) void k_bs(BatchArgs a) {
     if (lane < min(a.B, MB)) a.bits[(size_t)lane * W + word] = ~0u;
     if (lane == 0) a.ubits[word] = ~0u;
   }
-  const int n0 = word * 32, row = lane & 31, g = lane >> 5;
+  const int nb = blockIdx.x * BS_N;        // first neuron of the workgroup
+  const int row = lane & 31, g = lane >> 5;
   const int rch = a.r / 8;
   const int nchunk = (rch + BS_PC - 1) / BS_PC;
-  const char* pr = static_cast<const char*>(a.p2) + (size_t)min(n0 + row, a.ffn - 1) * a.r * 2;
   const char* zb = reinterpret_cast<const char*>(a.zhl);
+  const char* pb = static_cast<const char*>(a.p2);
 
-  auto load_z = [&](int c, u32x4 (&z)[BS_ZL]) {
+  auto load = [&](int c, u32x4 (&z)[BS_ZL], u32x4 (&p)[BS_PL]) {
 #pragma unroll
     for (int i = 0; i < BS_ZL; ++i) {
       const int e = tid + BS_T * i;        // (hl, token row, piece)
@@ -181,64 +185,67 @@ __global__ __launch_bounds__(BS_T) void k_bs(BatchArgs a) {
       const u32x4 v = ld16(zb + (((size_t)hl * MB + zr) * a.r) * 2 + (size_t)min(pc, rch - 1) * 16);
       z[i] = pc < rch ? v : u32x4{0u, 0u, 0u, 0u};
     }
+#pragma unroll
+    for (int i = 0; i < BS_PL; ++i) {
+      const int e = tid + BS_T * i;        // (neuron, piece)
+      const int n = nb + e / BS_PC, pc = c * BS_PC + e % BS_PC;
+      const u32x4 v = ld16(pb + ((size_t)min(n, a.ffn - 1) * rch + min(pc, rch - 1)) * 16);
+      p[i] = (n < a.ffn && pc < rch) ? v : u32x4{0u, 0u, 0u, 0u};
+    }
   };
-  auto store_z = [&](int buf, const u32x4 (&z)[BS_ZL]) {
+  auto store = [&](int buf, const u32x4 (&z)[BS_ZL], const u32x4 (&p)[BS_PL]) {
 #pragma unroll
     for (int i = 0; i < BS_ZL; ++i) {
       const int e = tid + BS_T * i;
       const int hl = e / (MB * BS_PC), zr = (e / BS_PC) % MB, zc = e % BS_PC;
       s_z[buf][hl][zr * BS_LD + zc] = z[i];
     }
-  };
-  // P2 row pieces of this lane for chunk c: step s (of this wave's half) reads piece
-  // c * BS_PC + 2 (kh BS_SW + s) + g
-  auto load_p = [&](int c, u32x4 (&b)[BS_SW]) {
 #pragma unroll
-    for (int s = 0; s < BS_SW; ++s) {
-      const int pc = c * BS_PC + 2 * (kh * BS_SW + s) + g;
-      const u32x4 v = ld16(pr + (size_t)min(pc, rch - 1) * 16);
-      b[s] = (live && pc < rch) ? v : u32x4{0u, 0u, 0u, 0u};
+    for (int i = 0; i < BS_PL; ++i) {
+      const int e = tid + BS_T * i;
+      s_p[buf][(e / BS_PC) * BS_LD + e % BS_PC] = p[i];
     }
   };
 
+  // loads run two chunks ahead: (z1, p1) hold chunk c+1, (z2, p2) receive chunk c+2; LDS holds
+  // the current chunk and the next one
   f32x16 acc = {};
-  u32x4 zn[BS_ZL], bc[BS_SW], bn[BS_SW];
-  load_z(0, zn);
-  load_p(0, bc);
-  store_z(0, zn);
+  u32x4 z1[BS_ZL], z2[BS_ZL], q1[BS_PL], q2[BS_PL];
+  load(0, z1, q1);
+  store(0, z1, q1);
+  if (nchunk > 1) load(1, z1, q1);
   __syncthreads();
   for (int c = 0; c < nchunk; ++c) {
     const int buf = c & 1;
-    if (c + 1 < nchunk) {
-      load_z(c + 1, zn);
-      load_p(c + 1, bn);
-    }
+    if (c + 2 < nchunk) load(c + 2, z2, q2);
     if (live) {
 #pragma unroll
       for (int s = 0; s < BS_SW; ++s) {
         const int pcs = 2 * (kh * BS_SW + s) + g;
         const u32x4 ah = s_z[buf][0][row * BS_LD + pcs];
         const u32x4 al = s_z[buf][1][row * BS_LD + pcs];
-        acc = mma16(ah, bc[s], acc);
-        acc = mma16(al, bc[s], acc);
+        const u32x4 bv = s_p[buf][(tw * 32 + row) * BS_LD + pcs];
+        acc = mma16(ah, bv, acc);
+        acc = mma16(al, bv, acc);
       }
     }
-    if (c + 1 < nchunk) {
-      store_z(buf ^ 1, zn);
+    if (c + 1 < nchunk) store(buf ^ 1, z1, q1);
 #pragma unroll
-      for (int s = 0; s < BS_SW; ++s) bc[s] = bn[s];
-    }
+    for (int i = 0; i < BS_ZL; ++i) z1[i] = z2[i];
+#pragma unroll
+    for (int i = 0; i < BS_PL; ++i) q1[i] = q2[i];
     __syncthreads();
   }
   // the second half's sums join the first's (the Z buffers are free now)
-  float* red = reinterpret_cast<float*>(&s_z[0][0][0]);   // [4 words][16][64]
-  static_assert(sizeof(s_z) >= 4 * 16 * WAVE * sizeof(float), "sums fit in the Z buffers");
+  float* red = reinterpret_cast<float*>(&s_p[0][0]);      // [4 words][16][64]
+  static_assert(sizeof(s_p) >= 4 * 16 * WAVE * sizeof(float), "sums fit in the P2 buffers");
   if (kh == 1) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) red[(tw * 16 + i) * WAVE + lane] = acc[i];
   }
   __syncthreads();
   if (kh == 0 && live) {
+    const int n0 = word * 32;
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[i] += red[(tw * 16 + i) * WAVE + lane];
     const float c2v = a.c2 ? a.c2[n0 + row] : 0.0f;
