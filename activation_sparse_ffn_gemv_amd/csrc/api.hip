@@ -223,14 +223,17 @@ BatchArgs batch_bufs(char* ws, const ffn_plan* p) {
 // Workspace of a mixture: one decode scratch (z, bitmap, |A|, partials: the front of an
 // expert's layout) per expert slot, then the per-slot expert records [max_batch][top_k].
 struct MoeLayout {
-  size_t slot_stride, off_slots, total;
+  size_t slot_stride, off_slots, off_zall, total;
 };
 
-MoeLayout moe_layout(const ffn_plan* e0, int top_k) {
+// slots' decode scratch | slot records [max_batch][top_k] | stage-1 results [max_batch][E][rank]
+MoeLayout moe_layout(const ffn_plan* e0, int n_experts, int top_k) {
   MoeLayout L{};
-  L.slot_stride = round_up(layout_for(&e0->desc).scratch_end, 256);
+  const ffn_layer_desc& D = e0->desc;
+  L.slot_stride = round_up(layout_for(&D).scratch_end, 256);
   L.off_slots = L.slot_stride * top_k;
-  L.total = round_up(L.off_slots + (size_t)e0->desc.max_batch * top_k * sizeof(ExpertW), 256);
+  L.off_zall = round_up(L.off_slots + (size_t)D.max_batch * top_k * sizeof(ExpertW), 256);
+  L.total = round_up(L.off_zall + (size_t)D.max_batch * n_experts * D.rank * 4, 256);
   return L;
 }
 
@@ -310,7 +313,7 @@ CacheBufs cache_bufs(const ffn_plan* p) {
 ffn_status enqueue_token(const ffn_plan* p, const TokenBufs& wb, const void* xb,
                          const uint8_t* maskb, float* yb, int* idxb, int* cntb, float* scoresb,
                          const ExpertW* slot, int nslot, size_t slot_stride, hipStream_t st,
-                         bool all_neurons = false) {
+                         bool all_neurons = false, const float* zall = nullptr) {
   const ffn_layer_desc& D = p->desc;
   const int wk = D.w_dtype == FFN_F32 ? WK_F32 : D.w_dtype == FFN_F16 ? WK_F16 : WK_I4;
   const int es = (int)(slot_stride / 4);      // the same stride in 4-byte elements
@@ -321,10 +324,12 @@ ffn_status enqueue_token(const ffn_plan* p, const TokenBufs& wb, const void* xb,
     e = launch_mask_bits(maskb, wb.bits, D.ffn / 32, st);
     if (e != hipSuccess) return hip_fail(e, "mask launch");
   } else {
-    e = launch_pred_z(D.p_dtype == FFN_F16, p->cpl_p, p->w.p1, p->w.c1, xb, wb.z, D.d, D.rank,
-                      slot, nslot, es, st, p->ev[FFN_STAGE_PRED_Z][0],
-                      p->ev[FFN_STAGE_PRED_Z][1]);
-    if (e != hipSuccess) return hip_fail(e, "predictor stage 1 launch");
+    if (!zall) {                                 // (a mixture ran stage 1 with its router)
+      e = launch_pred_z(D.p_dtype == FFN_F16, p->cpl_p, p->w.p1, p->w.c1, xb, wb.z, D.d, D.rank,
+                        slot, nslot, es, st, p->ev[FFN_STAGE_PRED_Z][0],
+                        p->ev[FFN_STAGE_PRED_Z][1]);
+      if (e != hipSuccess) return hip_fail(e, "predictor stage 1 launch");
+    }
     PredArgs pa{};
     pa.p2 = p->w.p2;
     pa.c2 = p->w.c2;
@@ -339,6 +344,7 @@ ffn_status enqueue_token(const ffn_plan* p, const TokenBufs& wb, const void* xb,
     pa.zstride = es;
     pa.bstride = es;
     pa.head_words = slot ? 0 : p->head_words;
+    pa.zall = zall;
     if (!fused) {
       e = launch_pred_s(D.p_dtype == FFN_F16, pa, st, p->ev[FFN_STAGE_PRED_S][0],
                         p->ev[FFN_STAGE_PRED_S][1]);
@@ -936,7 +942,7 @@ ffn_status ffn_moe_workspace_size(int32_t n_experts, int32_t top_k, const ffn_pl
     return fail(FFN_ERR_UNSUPPORTED, "n_experts must lie in [1, %d]", MOE_MAX_E);
   if (top_k < 1 || top_k > MOE_MAX_K || top_k > n_experts)
     return fail(FFN_ERR_UNSUPPORTED, "top_k must lie in [1, min(n_experts, %d)]", MOE_MAX_K);
-  *bytes = moe_layout(e0, top_k).total;
+  *bytes = moe_layout(e0, n_experts, top_k).total;
   g_err[0] = 0;
   return FFN_OK;
 }
@@ -976,7 +982,7 @@ ffn_status ffn_moe_plan(int32_t n_experts, int32_t top_k, const void* w_router,
   m->router = w_router;
   m->e0 = experts[0];
   m->ws = static_cast<char*>(workspace);
-  m->L = moe_layout(experts[0], top_k);
+  m->L = moe_layout(experts[0], n_experts, top_k);
   for (int e = 0; e < n_experts; ++e) {
     const ffn_layer_weights& w = experts[e]->w;
     ExpertW& r = m->tab.e[e];
@@ -1024,7 +1030,13 @@ ffn_status ffn_moe_forward(ffn_moe* m, const void* x, int32_t B, float* y, int32
   ra.K = m->top_k;
   ra.x_f16 = D.x_dtype == FFN_F16;
   ra.tab = m->tab;
-  hipError_t e = launch_router(ra, B, st);
+  float* zall = reinterpret_cast<float*>(m->ws + m->L.off_zall);
+  ra.zall = zall;
+  ra.rank = D.rank;
+  ra.cpl = p->cpl_p;
+  ra.B = B;
+  // timed as the plan's stage-1 stage (it is the mixture's stage 1, with the router)
+  hipError_t e = launch_route_z(ra, st, p->ev[FFN_STAGE_PRED_Z][0], p->ev[FFN_STAGE_PRED_Z][1]);
   if (e != hipSuccess) return hip_fail(e, "router launch");
   const size_t xbytes = (size_t)D.d * (D.x_dtype == FFN_F32 ? 4 : 2);
   const TokenBufs wb = token_bufs(m->ws, p);
@@ -1032,7 +1044,8 @@ ffn_status ffn_moe_forward(ffn_moe* m, const void* x, int32_t B, float* y, int32
     // the token's top_k experts run side by side, one launch per stage
     ffn_status s = enqueue_token(p, wb, static_cast<const char*>(x) + b * xbytes, nullptr,
                                  y + (size_t)b * D.d, nullptr, nullptr, nullptr,
-                                 slots + (size_t)b * m->top_k, m->top_k, m->L.slot_stride, st);
+                                 slots + (size_t)b * m->top_k, m->top_k, m->L.slot_stride, st,
+                                 false, zall + (size_t)b * m->n_experts * D.rank);
     if (s != FFN_OK) return s;
   }
   g_err[0] = 0;

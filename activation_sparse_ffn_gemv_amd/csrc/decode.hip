@@ -31,60 +31,6 @@ extern "C" hipError_t ffn_trace_set_buffer(void* p) {
 #endif
 
 // ---------------------------------------------------------------------------------------------
-// Token slice held in registers: lane `l` owns 16-byte row chunks l, l+64, l+128, ...
-template <int WK, int CPL>
-struct XRegs {
-  u32x4 v[CPL][Kind<WK>::XW];
-};
-
-template <int WK, int CPL>
-__device__ __forceinline__ void load_x(XRegs<WK, CPL>& xr, const void* x, int nch, int lane) {
-#pragma unroll
-  for (int k = 0; k < CPL; ++k) {
-    const int c = lane + k * WAVE;
-    const int cc = min(c, nch - 1);           // clamped: loads are never predicated
-#pragma unroll
-    for (int q = 0; q < Kind<WK>::XW; ++q) {
-      // fp32 / fp16 rows: 16 token bytes per chunk.  int4 rows: 32 fp16 token values per chunk.
-      const u32x4 v = ld16(static_cast<const char*>(x) + (size_t)cc * 16 * Kind<WK>::XW + q * 16);
-      xr.v[k][q] = c < nch ? v : u32x4{0u, 0u, 0u, 0u};
-    }
-    if constexpr (WK == WK_I4) i4_perm_x(xr.v[k]);
-  }
-}
-
-template <int WK, int CPL>
-__device__ __forceinline__ float row_dot(const u32x4 (&w)[CPL], const float (&sc)[CPL],
-                                         const XRegs<WK, CPL>& xr) {
-  float acc = 0.0f;
-#pragma unroll
-  for (int k = 0; k < CPL; ++k) {
-    if constexpr (WK == WK_F32) acc = dot4_f32(w[k], xr.v[k][0], acc);
-    else if constexpr (WK == WK_F16) acc = dot8_f16(w[k], xr.v[k][0], acc);
-    else acc = dot32_i4(w[k], xr.v[k], sc[k], acc);
-  }
-  return acc;
-}
-
-template <int WK, int CPL>
-__device__ __forceinline__ void load_row(u32x4 (&w)[CPL], float (&sc)[CPL], const void* base,
-                                         const void* scales, size_t row, int nch, int lane) {
-  // Chunks past the row end (ragged d) re-read the last chunk and meet a zero token slice.
-  const char* rp = static_cast<const char*>(base) + row * (size_t)nch * 16;
-#pragma unroll
-  for (int k = 0; k < CPL; ++k) {
-    const int cc = min(lane + k * WAVE, nch - 1);
-    w[k] = ld16(rp + (size_t)cc * 16);
-    if constexpr (WK == WK_I4) {
-      const _Float16* sp = static_cast<const _Float16*>(scales) + row * (size_t)nch;
-      sc[k] = (float)sp[cc];
-    } else {
-      sc[k] = 0.0f;
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------------------------
 // Predictor stage 1: one 64-thread workgroup per row of P1.  z[k] = c1[k] + P1[k] . x
 template <int PK, int CPL>
 __global__ __launch_bounds__(64) void k_pred_z(const void* __restrict__ p1,
@@ -138,7 +84,7 @@ __global__ __launch_bounds__(PS_THREADS) void k_pred_s(PredArgs a) {
   FFN_TS(3, 0);
   if (a.slot) {
     a.slot += blockIdx.y;                       // expert slots side by side
-    a.z += (size_t)blockIdx.y * a.zstride;
+    a.z = a.zall ? a.zall + (size_t)a.slot->expert * a.rank : a.z + (size_t)blockIdx.y * a.zstride;
     a.bitmap += (size_t)blockIdx.y * a.bstride;
     a.p2 = a.slot->p2;
     a.c2 = a.slot->c2;

@@ -34,6 +34,10 @@ struct RouterArgs {
   ExpertW* slots;             // [B][K] out
   int d, E, K, x_f16;
   ExpertTable tab;
+  // predictor stage 1 of every expert, computed in the router's launch (the chosen experts are
+  // not known yet): zall[(b * E + e) * rank + k] = c1_e[k] + P1_e[k] . x_b
+  float* zall;
+  int rank, cpl, B;
 };
 
 // Predictor stage 2 (one token).
@@ -50,6 +54,8 @@ struct PredArgs {
   int zstride, bstride;       //   z + k*zstride, bitmap + k*bstride (elements)
   int head_words;             // hot head: bitmap words [0, head_words) always set, their P2 rows
                               //   and c2 entries never read
+  const float* zall;          // expert slots: the token's stage-1 results of every expert
+                              //   ([E][rank]); slot k reads the row of its expert
 };
 
 // Balanced gather of the active rows (one token).
@@ -147,7 +153,7 @@ hipError_t launch_cache_plan(const CacheArgs& a, hipStream_t st);
 hipError_t launch_cache_init(const CacheArgs& a, int n_pinned, hipStream_t st);
 hipError_t launch_reduce(const ReduceArgs& a, hipStream_t st, hipEvent_t ev0 = nullptr,
                          hipEvent_t ev1 = nullptr);
-hipError_t launch_router(const RouterArgs& a, int B, hipStream_t st);
+hipError_t launch_route_z(const RouterArgs& a, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1);
 
 // Batched path (fp16 layers): up to BATCH_TILE tokens per pass share one read of the union of
 // their active neurons' rows.

@@ -7,6 +7,8 @@
 // the chosen experts' weight records (from the table passed by value in the kernel arguments)
 // into per-slot records in the workspace, and the expert kernels that follow take their weight
 // pointers from those records.
+#include <hip/hip_ext.h>
+
 #include "common.h"
 #include "launch.h"
 
@@ -18,12 +20,11 @@ constexpr int RT_EPW = (MOE_MAX_E + RT_NW - 1) / RT_NW;   // experts per wave
 constexpr int RT_CPL = 8;                                  // chunks per lane in flight
 
 template <int XK>
-__global__ __launch_bounds__(RT_THREADS) void k_router(RouterArgs a) {
+__device__ __forceinline__ void route_token(const RouterArgs& a, int b) {
   constexpr int EPC = Kind<XK>::EPC;
   __shared__ float s_logit[MOE_MAX_E];
   __shared__ int s_ids[MOE_MAX_K];
   __shared__ float s_w[MOE_MAX_K];
-  const int b = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & (WAVE - 1), wave = tid / WAVE;
   const int nch = a.d / EPC;
   const char* xb = static_cast<const char*>(a.x) + (size_t)b * nch * 16;
@@ -101,11 +102,49 @@ __global__ __launch_bounds__(RT_THREADS) void k_router(RouterArgs a) {
   }
 }
 
-hipError_t launch_router(const RouterArgs& a, int B, hipStream_t st) {
-  if (a.x_f16)
-    hipLaunchKernelGGL(k_router<WK_F16>, dim3(B), dim3(RT_THREADS), 0, st, a);
-  else
-    hipLaunchKernelGGL(k_router<WK_F32>, dim3(B), dim3(RT_THREADS), 0, st, a);
+// Router and predictor stage 1 of every expert in one launch.  Blocks [0, B) route token b
+// (above); each further block runs eight P1 rows, a wave per row (token b, expert e, row k of
+// the flattened (b, e, k) order): 16-byte chunks per lane, all loads issued before use, wave sum.
+// Computing stage 1 for the experts the router is about to drop costs P1 bytes of E instead of
+// top_k experts, but takes the routing decision off the path to the predictor's second stage.
+template <int XK, int CPL>
+__global__ __launch_bounds__(RT_THREADS) void k_route_z(RouterArgs a) {
+  if ((int)blockIdx.x < a.B) {
+    route_token<XK>(a, blockIdx.x);
+    return;
+  }
+  const int lane = threadIdx.x & (WAVE - 1), wave = threadIdx.x / WAVE;
+  const int q = ((int)blockIdx.x - a.B) * RT_NW + wave;
+  if (q >= a.B * a.E * a.rank) return;                // whole waves
+  const int k = q % a.rank, e = (q / a.rank) % a.E, b = q / (a.rank * a.E);
+  const int nch = a.d / Kind<XK>::EPC;
+  XRegs<XK, CPL> xr;
+  load_x<XK, CPL>(xr, static_cast<const char*>(a.x) + (size_t)b * nch * 16, nch, lane);
+  u32x4 w[CPL];
+  float sc[CPL];
+  load_row<XK, CPL>(w, sc, a.tab.e[e].p1, nullptr, k, nch, lane);
+  issue_fence();
+  const float acc = wave_sum(row_dot<XK, CPL>(w, sc, xr));
+  if (lane == 0) a.zall[q] = acc + (a.tab.e[e].c1 ? a.tab.e[e].c1[k] : 0.0f);
+}
+
+hipError_t launch_route_z(const RouterArgs& a, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
+  const dim3 grid(a.B + (a.B * a.E * a.rank + RT_NW - 1) / RT_NW);
+#define RZ(X, C)                                                                                \
+  do {                                                                                        \
+    if (ev0 && ev1)                                                                           \
+      hipExtLaunchKernelGGL((k_route_z<X, C>), grid, dim3(RT_THREADS), 0, st, ev0, ev1, 0, a); \
+    else                                                                                      \
+      hipLaunchKernelGGL((k_route_z<X, C>), grid, dim3(RT_THREADS), 0, st, a);                \
+  } while (0)
+#define RZ_CASE(C) \
+  case C: if (a.x_f16) RZ(WK_F16, C); else RZ(WK_F32, C); break;
+  switch (a.cpl) {
+    RZ_CASE(1) RZ_CASE(2) RZ_CASE(3) RZ_CASE(4) RZ_CASE(6) RZ_CASE(8) RZ_CASE(12) RZ_CASE(16)
+    default: return hipErrorInvalidValue;
+  }
+#undef RZ_CASE
+#undef RZ
   return hipGetLastError();
 }
 

@@ -439,7 +439,9 @@ def main():
             k = cfg.top_k if moe else 1
             pzm, psm = float(pz.mean()), float(ps.mean())
             if sname == "pred_z":
-                nb = pzm * k                                         # the slots run side by side
+                # the slots run side by side; a mixture's stage 1 runs in the router's launch
+                # (the algorithmic bytes: the router and the chosen experts' P1)
+                nb = pzm * k + router_b
             elif sname == "pred_s":
                 nb = psm * k
             elif sname == "gather":
