@@ -250,3 +250,30 @@ def test_calibrated_crossover(ffn):
         y_ref, _ = oracle.ffn(OL, xh[t], mask_from_idx(lt, cfg.ffn))
         assert normwise(yh[t], y_ref) <= TOL["f16"]
     m.close()
+
+
+def test_largest_batch_dense_and_auto(ffn):
+    """max_batch = 4096 tokens of a small fp16 layer: the dense GEMMs at their largest M (and
+    AUTO choosing them), sampled rows against the oracle on each token's own set."""
+    cfg = synth.small_config(d=256, ffn=1024, rank=32, act="reglu", w_dtype="f16", x_dtype="f16",
+                             p_dtype="f16", density=0.1, bias_gate=True, bias_down=True)
+    host = synth.make_layer(cfg, device="cuda")
+    L, OL = to_device(host), oracle_layer(host)
+    B = 4096
+    x = synth.make_tokens(cfg, B).cuda()
+    m = ffn.SparseFFN(L, max_batch=B)
+    ffn.ffn_plan_set_crossover(m.plan, B, 0.0)          # AUTO: always dense at this batch
+    for path in (ffn.FFN_PATH_DENSE, ffn.FFN_PATH_AUTO):
+        y = torch.full((B, cfg.d), float("nan"), device="cuda")
+        idx = torch.full((B, cfg.ffn), -1, dtype=torch.int32, device="cuda")
+        cnt = torch.full((B,), -1, dtype=torch.int32, device="cuda")
+        m.forward(x, y=y, idx=idx, cnt=cnt, path=path)
+        torch.cuda.synchronize()
+        yh, ih, ch = y.cpu().numpy(), idx.cpu().numpy(), cnt.cpu().numpy()
+        xh = x.cpu().numpy()
+        for t in (0, 31, 32, 2047, 4064, 4095):
+            pred = oracle.predictor(OL["p1"], OL["p2"], OL["c1"], OL["c2"], xh[t], OL["tau"])
+            check_index_list(ih[t, :ch[t]], pred, OL["tau"])
+            y_ref, _ = oracle.ffn(OL, xh[t], mask_from_idx(ih[t, :ch[t]], cfg.ffn))
+            assert normwise(yh[t], y_ref) <= TOL["f16"], (path, t)
+    m.close()

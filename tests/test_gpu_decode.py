@@ -331,3 +331,18 @@ def test_fused_variant_small_and_edge_sets(ffn):
                 y_ref, _ = oracle.ffn(OL, xh[t], mask_from_idx(lt, cfg.ffn))
                 assert normwise(y[0].cpu().numpy(), y_ref) <= TOL["f16"]
         m.close()
+
+
+@pytest.mark.parametrize("kw", [
+    dict(d=2048, ffn=1024, rank=2048, act="reglu", w_dtype="f16", x_dtype="f16", p_dtype="f16",
+         bias_gate=True),                                        # the largest fp16 rank
+    dict(d=1024, ffn=512, rank=1024, act="relu", w_dtype="f32", x_dtype="f32", p_dtype="f32",
+         bias_up=True),                                          # the largest fp32 rank
+    dict(d=8192, ffn=1024, rank=64, act="drelu", w_dtype="f16", x_dtype="f16", p_dtype="f16",
+         bias_gate=True, bias_up=True),                          # the widest fp16 rows
+    dict(d=4096, ffn=512, rank=64, act="relu", w_dtype="f32", x_dtype="f32", p_dtype="f32",
+         bias_up=True),                                          # the widest fp32 rows
+], ids=["f16_rank2048", "f32_rank1024", "f16_d8192", "f32_d4096"])
+def test_shape_limits(ffn, kw):
+    cfg = synth.small_config(density=0.1, **kw)
+    _check_predicted(ffn, cfg, n_tokens=3)
