@@ -90,8 +90,18 @@ __device__ __forceinline__ float group_sum_last(float v, int width) {
 // whole batch is in flight before the wave waits (instead of load / wait / use one by one).
 __device__ __forceinline__ void issue_fence() { __builtin_amdgcn_sched_barrier(0); }
 
+// 16-byte load from device (or mapped host) memory, issued as a global load.  Pointers fetched
+// from memory (expert slot records) are generic to the compiler, and generic loads both count
+// against the LDS counter and make it wait early, so every weight / token read goes through here.
 __device__ __forceinline__ u32x4 ld16(const void* p) {
-  return *reinterpret_cast<const u32x4*>(p);
+  return *(const __attribute__((address_space(1))) u32x4*)p;
+}
+
+// The 32-bit word holding fp16 element i (an int4 group scale) of an array of an even number of
+// elements, as a global load; pick_h takes the element out of it once the value is needed.
+// A 16-bit load would be merged into a register half as soon as it lands, which needs a wait.
+__device__ __forceinline__ uint32_t ldh_word(const void* p, size_t i) {
+  return ((const __attribute__((address_space(1))) uint32_t*)p)[i >> 1];
 }
 
 __device__ __forceinline__ h2 as_h2(uint32_t v) { return __builtin_bit_cast(h2, v); }
@@ -116,6 +126,7 @@ __device__ __forceinline__ float dot4_f32(u32x4 w, u32x4 x, float acc) {
 
 __device__ __forceinline__ float h_lo(uint32_t v) { return (float)as_h2(v).x; }
 __device__ __forceinline__ float h_hi(uint32_t v) { return (float)as_h2(v).y; }
+__device__ __forceinline__ float pick_h(uint32_t v, size_t i) { return i & 1 ? h_hi(v) : h_lo(v); }
 
 // int4 group: 16 bytes = 32 signed nibbles, element 2k in the low nibble of byte k.
 // Decoding: flipping the sign bit of each nibble gives n' = q + 8 in [0, 15]; the fp16 with bit
@@ -166,18 +177,29 @@ struct XRegs {
   u32x4 v[CPL][Kind<WK>::XW];
 };
 
+// Raw loads only (clamped, so never predicated): finish_x, called once every load of the caller
+// is issued, zeroes the chunks past the row end and puts int4 slices in nibble order.  Doing that
+// here would make the wave wait for the token before it issues its weight loads.
 template <int WK, int CPL>
 __device__ __forceinline__ void load_x(XRegs<WK, CPL>& xr, const void* x, int nch, int lane) {
 #pragma unroll
   for (int k = 0; k < CPL; ++k) {
-    const int c = lane + k * WAVE;
-    const int cc = min(c, nch - 1);           // clamped: loads are never predicated
+    const int cc = min(lane + k * WAVE, nch - 1);
 #pragma unroll
-    for (int q = 0; q < Kind<WK>::XW; ++q) {
+    for (int q = 0; q < Kind<WK>::XW; ++q)
       // fp32 / fp16 rows: 16 token bytes per chunk.  int4 rows: 32 fp16 token values per chunk.
-      const u32x4 v = ld16(static_cast<const char*>(x) + (size_t)cc * 16 * Kind<WK>::XW + q * 16);
-      xr.v[k][q] = c < nch ? v : u32x4{0u, 0u, 0u, 0u};
-    }
+      xr.v[k][q] = ld16(static_cast<const char*>(x) + (size_t)cc * 16 * Kind<WK>::XW + q * 16);
+  }
+}
+
+template <int WK, int CPL>
+__device__ __forceinline__ void finish_x(XRegs<WK, CPL>& xr, int nch, int lane) {
+#pragma unroll
+  for (int k = 0; k < CPL; ++k) {
+    const bool in = lane + k * WAVE < nch;
+#pragma unroll
+    for (int q = 0; q < Kind<WK>::XW; ++q)
+      xr.v[k][q] = in ? xr.v[k][q] : u32x4{0u, 0u, 0u, 0u};
     if constexpr (WK == WK_I4) i4_perm_x(xr.v[k]);
   }
 }

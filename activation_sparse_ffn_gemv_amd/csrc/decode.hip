@@ -54,6 +54,7 @@ __global__ __launch_bounds__(64) void k_pred_z(const void* __restrict__ p1,
   float sc[CPL];
   load_row<PK, CPL>(w, sc, p1, nullptr, row, nch, lane);
   issue_fence();
+  finish_x<PK, CPL>(xr, nch, lane);
   const float acc = wave_sum(row_dot<PK, CPL>(w, sc, xr));
   FFN_TS(0, 1);
   if (lane == 0) z[row] = acc + (c1 ? c1[row] : 0.0f);
@@ -105,6 +106,8 @@ __global__ __launch_bounds__(PS_THREADS) void k_pred_s(PredArgs a) {
       zr[k][q] = c < pch ? v : f32x4{0.f, 0.f, 0.f, 0.f};
     }
   }
+  // every pass's loads in one straight run (rows clamped into the word, so a pass past P just
+  // re-reads a row of it): a per-pass branch here would make each pass wait for its own loads
   u32x4 w[MAXP][CPR];
 #pragma unroll
   for (int p = 0; p < MAXP; ++p) {
@@ -112,7 +115,7 @@ __global__ __launch_bounds__(PS_THREADS) void k_pred_s(PredArgs a) {
 #pragma unroll
     for (int k = 0; k < CPR; ++k) {
       const int cc = min(gl + k * L, pch - 1);
-      if (p < P) w[p][k] = ld16(static_cast<const char*>(a.p2) + ((size_t)(i0 + r) * pch + cc) * 16);
+      w[p][k] = ld16(static_cast<const char*>(a.p2) + ((size_t)(i0 + r) * pch + cc) * 16);
     }
   }
   issue_fence();
@@ -321,7 +324,7 @@ __global__ __launch_bounds__(GA_THREADS) void k_gather(GatherArgs a) {
     FFN_TS(1, 2);
     for (int t0 = 0; t0 < nl; t0 += RQ) {
       u32x4 wu[RN][CPT], wg[RN][CPT], wd[RN][CPT];
-      float su[RN][CPT], sg[RN][CPT], sd[RN][CPT];
+      uint32_t su[RN][CPT], sg[RN][CPT], sd[RN][CPT];        // words holding int4 group scales
       // the biases of the round's neurons travel with the rows (thread q < RQ: neuron q)
       float bu = 0.0f, bgt = 0.0f;
       if (tid < RQ && t0 + tid < nl) {
@@ -353,15 +356,16 @@ __global__ __launch_bounds__(GA_THREADS) void k_gather(GatherArgs a) {
           const int cc = min(ct + k * TPR, nch - 1);
           const size_t off = (row * nch + cc) * 16;
           wu[r][k] = wg[r][k] = wd[r][k] = u32x4{0u, 0u, 0u, 0u};
-          su[r][k] = sg[r][k] = sd[r][k] = 0.0f;
+          su[r][k] = sg[r][k] = sd[r][k] = 0u;
           if (live_r) {
             wu[r][k] = ld16(pu + off);
             if (a.has_gate) wg[r][k] = ld16(pg + off);
             wd[r][k] = ld16(pd + off);
             if constexpr (WK == WK_I4) {
-              su[r][k] = (float)static_cast<const _Float16*>(a.s_up)[nr * nch + cc];
-              if (a.has_gate) sg[r][k] = (float)static_cast<const _Float16*>(a.s_gate)[nr * nch + cc];
-              sd[r][k] = (float)static_cast<const _Float16*>(a.s_dn)[nr * nch + cc];
+              // (ffn is a multiple of 32, so the word of the last scale is inside the array)
+              su[r][k] = ldh_word(a.s_up, nr * nch + cc);
+              if (a.has_gate) sg[r][k] = ldh_word(a.s_gate, nr * nch + cc);
+              sd[r][k] = ldh_word(a.s_dn, nr * nch + cc);
             }
           }
         }
@@ -380,8 +384,10 @@ __global__ __launch_bounds__(GA_THREADS) void k_gather(GatherArgs a) {
               pu = dot8_f16(wu[r][k], xr[k][0], pu);
               if (a.has_gate) pg = dot8_f16(wg[r][k], xr[k][0], pg);
             } else {
-              pu = dot32_i4(wu[r][k], xr[k], su[r][k], pu);
-              if (a.has_gate) pg = dot32_i4(wg[r][k], xr[k], sg[r][k], pg);
+              const size_t si = (size_t)s_list[min(t0 + r * SLOTS + slot, nl - 1)] * nch +
+                                min(ct + k * TPR, nch - 1);
+              pu = dot32_i4(wu[r][k], xr[k], pick_h(su[r][k], si), pu);
+              if (a.has_gate) pg = dot32_i4(wg[r][k], xr[k], pick_h(sg[r][k], si), pg);
             }
           }
           pu = wave_sum(pu);
@@ -449,7 +455,9 @@ __global__ __launch_bounds__(GA_THREADS) void k_gather(GatherArgs a) {
               acc[k][2 * q + 1] = __builtin_fmaf(h, h_hi(ww[q]), acc[k][2 * q + 1]);
             }
           } else {
-            const float hs = h * sd[r][k];
+            const size_t si = (size_t)s_list[min(t0 + r * SLOTS + slot, nl - 1)] * nch +
+                              min(ct + k * TPR, nch - 1);
+            const float hs = h * pick_h(sd[r][k], si);
             const uint32_t ww[4] = {wd[r][k].x, wd[r][k].y, wd[r][k].z, wd[r][k].w};
 #pragma unroll
             for (int q = 0; q < 4; ++q)
@@ -585,15 +593,18 @@ __global__ __launch_bounds__(FU_THREADS) void k_fused(FusedArgs f) {
       zr[k][q] = c < pch ? v : f32x4{0.f, 0.f, 0.f, 0.f};
     }
   }
+  // every pass's loads in one straight run (rows clamped into the workgroup's): a per-pass branch
+  // here would make each pass wait for its own loads
   u32x4 w[PS_MAXP][CPR];
+  if (nh < n) {                                         // uniform: not a whole-head workgroup
 #pragma unroll
-  for (int pp = 0; pp < PS_MAXP; ++pp) {
-    const int r = min(pp * R + g, n - 1);
+    for (int pp = 0; pp < PS_MAXP; ++pp) {
+      const int r = min(pp * R + g, n - 1);
 #pragma unroll
-    for (int k = 0; k < CPR; ++k) {
-      const int cc = min(gl + k * L, pch - 1);
-      if (pp < P && nh < n)
+      for (int k = 0; k < CPR; ++k) {
+        const int cc = min(gl + k * L, pch - 1);
         w[pp][k] = ld16(static_cast<const char*>(p.p2) + ((size_t)(i0 + r) * pch + cc) * 16);
+      }
     }
   }
   issue_fence();

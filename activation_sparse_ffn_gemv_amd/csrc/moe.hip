@@ -124,6 +124,7 @@ __global__ __launch_bounds__(RT_THREADS) void k_route_z(RouterArgs a) {
   float sc[CPL];
   load_row<XK, CPL>(w, sc, a.tab.e[e].p1, nullptr, k, nch, lane);
   issue_fence();
+  finish_x<XK, CPL>(xr, nch, lane);
   const float acc = wave_sum(row_dot<XK, CPL>(w, sc, xr));
   if (lane == 0) a.zall[q] = acc + (a.tab.e[e].c1 ? a.tab.e[e].c1[k] : 0.0f);
 }
