@@ -176,48 +176,54 @@ __global__ __launch_bounds__(BS_T) void k_bs(BatchArgs a) {
   const char* zb = reinterpret_cast<const char*>(a.zhl);
   const char* pb = static_cast<const char*>(a.p2);
 
+  // Raw loads (clamped addresses, never predicated); what lies past the rank or the layer is
+  // zeroed on the way into LDS, so that no load has to land before the loop turns.
   auto load = [&](int c, u32x4 (&z)[BS_ZL], u32x4 (&p)[BS_PL]) {
 #pragma unroll
     for (int i = 0; i < BS_ZL; ++i) {
       const int e = tid + BS_T * i;        // (hl, token row, piece)
       const int hl = e / (MB * BS_PC), zr = (e / BS_PC) % MB, zc = e % BS_PC;
       const int pc = c * BS_PC + zc;
-      const u32x4 v = ld16(zb + (((size_t)hl * MB + zr) * a.r) * 2 + (size_t)min(pc, rch - 1) * 16);
-      z[i] = pc < rch ? v : u32x4{0u, 0u, 0u, 0u};
+      z[i] = ld16(zb + (((size_t)hl * MB + zr) * a.r) * 2 + (size_t)min(pc, rch - 1) * 16);
     }
 #pragma unroll
     for (int i = 0; i < BS_PL; ++i) {
       const int e = tid + BS_T * i;        // (neuron, piece)
       const int n = nb + e / BS_PC, pc = c * BS_PC + e % BS_PC;
-      const u32x4 v = ld16(pb + ((size_t)min(n, a.ffn - 1) * rch + min(pc, rch - 1)) * 16);
-      p[i] = (n < a.ffn && pc < rch) ? v : u32x4{0u, 0u, 0u, 0u};
+      p[i] = ld16(pb + ((size_t)min(n, a.ffn - 1) * rch + min(pc, rch - 1)) * 16);
     }
   };
-  auto store = [&](int buf, const u32x4 (&z)[BS_ZL], const u32x4 (&p)[BS_PL]) {
+  auto store = [&](int buf, int c, const u32x4 (&z)[BS_ZL], const u32x4 (&p)[BS_PL]) {
 #pragma unroll
     for (int i = 0; i < BS_ZL; ++i) {
       const int e = tid + BS_T * i;
       const int hl = e / (MB * BS_PC), zr = (e / BS_PC) % MB, zc = e % BS_PC;
-      s_z[buf][hl][zr * BS_LD + zc] = z[i];
+      s_z[buf][hl][zr * BS_LD + zc] = c * BS_PC + zc < rch ? z[i] : u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int i = 0; i < BS_PL; ++i) {
       const int e = tid + BS_T * i;
-      s_p[buf][(e / BS_PC) * BS_LD + e % BS_PC] = p[i];
+      const bool ok = nb + e / BS_PC < a.ffn && c * BS_PC + e % BS_PC < rch;
+      s_p[buf][(e / BS_PC) * BS_LD + e % BS_PC] = ok ? p[i] : u32x4{0u, 0u, 0u, 0u};
     }
   };
 
-  // loads run two chunks ahead: (z1, p1) hold chunk c+1, (z2, p2) receive chunk c+2; LDS holds
-  // the current chunk and the next one
+  // Loads run two chunks ahead; LDS holds the current chunk and the next one.  The two register
+  // sets swap roles by name each turn (chunk c+1 held for LDS in zh/qh, chunk c+2 arriving in
+  // zr/qr), never by copy: copying a register that a load is still filling waits for the load.
+  // Loads and LDS stores are unconditional (the last two turns re-read the last chunk, from L2,
+  // and the last store writes zeros): a branch around either would merge a path with other
+  // loads in flight, and the waits would then cover this turn's loads too.
   f32x16 acc = {};
-  u32x4 z1[BS_ZL], z2[BS_ZL], q1[BS_PL], q2[BS_PL];
-  load(0, z1, q1);
-  store(0, z1, q1);
-  if (nchunk > 1) load(1, z1, q1);
+  u32x4 zA[BS_ZL], zB[BS_ZL], qA[BS_PL], qB[BS_PL];
+  load(0, zB, qB);
+  load(min(1, nchunk - 1), zA, qA);
+  store(0, 0, zB, qB);
   __syncthreads();
-  for (int c = 0; c < nchunk; ++c) {
+  auto step = [&](int c, const u32x4 (&zh)[BS_ZL], const u32x4 (&qh)[BS_PL], u32x4 (&zn)[BS_ZL],
+                  u32x4 (&qn)[BS_PL]) {
     const int buf = c & 1;
-    if (c + 2 < nchunk) load(c + 2, z2, q2);
+    load(min(c + 2, nchunk - 1), zn, qn);
     if (live) {
 #pragma unroll
       for (int s = 0; s < BS_SW; ++s) {
@@ -229,13 +235,17 @@ __global__ __launch_bounds__(BS_T) void k_bs(BatchArgs a) {
         acc = mma16(al, bv, acc);
       }
     }
-    if (c + 1 < nchunk) store(buf ^ 1, z1, q1);
-#pragma unroll
-    for (int i = 0; i < BS_ZL; ++i) z1[i] = z2[i];
-#pragma unroll
-    for (int i = 0; i < BS_PL; ++i) q1[i] = q2[i];
+    store(buf ^ 1, c + 1, zh, qh);         // past the last chunk: zeros nobody reads
     __syncthreads();
+  };
+  // pairs in the loop, an odd last chunk after it (an exit between the two steps would join the
+  // loop head with loads in other registers in flight, and the head would wait for them all)
+  int c0 = 0;
+  for (; c0 + 2 <= nchunk; c0 += 2) {
+    step(c0, zA, qA, zB, qB);
+    step(c0 + 1, zB, qB, zA, qA);
   }
+  if (c0 < nchunk) step(c0, zA, qA, zB, qB);
   // the second half's sums join the first's (the Z buffers are free now)
   float* red = reinterpret_cast<float*>(&s_p[0][0]);      // [4 words][16][64]
   static_assert(sizeof(s_p) >= 4 * 16 * WAVE * sizeof(float), "sums fit in the P2 buffers");
@@ -424,23 +434,26 @@ __global__ __launch_bounds__(BT) void k_bug(BatchArgs a) {
     lrow_off[i] = (size_t)max(s_nid[e / UG_KC], 0) * nchk * 16;
     lch[i] = e % UG_KC;
   }
+  // Loads are raw (clamped addresses, never predicated); chunks past the row end are zeroed where
+  // the values are next used (LDS store, MFMA operand), so that no load of a stage two ahead has
+  // to land before the loop turns.
   auto load_w = [&](int st, u32x4 (&r)[NMAT][LPT]) {
 #pragma unroll
     for (int mt = 0; mt < NMAT; ++mt)
 #pragma unroll
       for (int i = 0; i < LPT; ++i) {
         const int c = st * UG_KC + lch[i];
-        const u32x4 t = ld16(wsrc[mt] + lrow_off[i] + (size_t)min(c, nchk - 1) * 16);
-        r[mt][i] = c < nchk ? t : u32x4{0u, 0u, 0u, 0u};
+        r[mt][i] = ld16(wsrc[mt] + lrow_off[i] + (size_t)min(c, nchk - 1) * 16);
       }
   };
-  auto store_w = [&](int buf, const u32x4 (&r)[NMAT][LPT]) {
+  auto store_w = [&](int buf, int st, const u32x4 (&r)[NMAT][LPT]) {
 #pragma unroll
     for (int mt = 0; mt < NMAT; ++mt)
 #pragma unroll
       for (int i = 0; i < LPT; ++i) {
         const int e = tid + BT * i;
-        s_w[buf][mt][(e / UG_KC) * UG_LD + e % UG_KC] = r[mt][i];
+        s_w[buf][mt][(e / UG_KC) * UG_LD + e % UG_KC] =
+            st * UG_KC + lch[i] < nchk ? r[mt][i] : u32x4{0u, 0u, 0u, 0u};
       }
   };
   // token operand straight from global: wave w takes the stage's 16-k steps 4w .. 4w+3
@@ -451,49 +464,80 @@ __global__ __launch_bounds__(BT) void k_bug(BatchArgs a) {
 #pragma unroll
     for (int j = 0; j < SPW; ++j) {
       const int c = st * UG_KC + 2 * (wave * SPW + j) + g;
-      const u32x4 t = ld16(xr + (size_t)min(c, nchk - 1) * 16);
-      xv[j] = (xok && c < nchk) ? t : u32x4{0u, 0u, 0u, 0u};
+      xv[j] = ld16(xr + (size_t)min(c, nchk - 1) * 16);
     }
   };
 
-  // loads two stages ahead: (wr1, xn1) hold stage st+1, (wr2, xn2) receive stage st+2
+  // Loads run two stages ahead.  Register sets rotate by name, not by copy (a copy of a register
+  // that a load is still filling waits for that load): the token slices over three sets (stage
+  // st in xa, st+1 held, st+2 arriving in xc), the row chunks over two (stage st+1 in wb, bound
+  // for LDS this turn; st+2 arriving in wc), so the loop body is written out for six stages.
+  // Loads and LDS stores are unconditional (the last two turns re-read the last stage, from L2,
+  // and the last store writes zeros): a branch around either would merge a path with other
+  // loads in flight, and the waits would then cover this turn's loads too.
   f32x16 au[NTL], ag[NTL];
 #pragma unroll
   for (int t = 0; t < NTL; ++t) au[t] = ag[t] = f32x16{};
-  u32x4 wr1[NMAT][LPT], wr2[NMAT][LPT], xv[SPW], xn1[SPW], xn2[SPW];
-  load_w(0, wr1);
-  load_x(0, xv);
-  store_w(0, wr1);
-  if (nstage > 1) {
-    load_w(1, wr1);
-    load_x(1, xn1);
-  }
+  u32x4 wA[NMAT][LPT], wB[NMAT][LPT], xA[SPW], xB[SPW], xC[SPW];
+  load_w(0, wB);
+  load_x(0, xA);
+  load_w(min(1, nstage - 1), wA);
+  load_x(min(1, nstage - 1), xB);
+  store_w(0, 0, wB);
   __syncthreads();
-  for (int st = 0; st < nstage; ++st) {
+  auto step = [&](int st, const u32x4 (&xa)[SPW], u32x4 (&xc)[SPW], const u32x4 (&wb)[NMAT][LPT],
+                  u32x4 (&wc)[NMAT][LPT]) {
     const int buf = st & 1;
-    if (st + 2 < nstage) {
-      load_w(st + 2, wr2);
-      load_x(st + 2, xn2);
-    }
+    load_w(min(st + 2, nstage - 1), wc);
+    load_x(min(st + 2, nstage - 1), xc);
 #pragma unroll
-    for (int j = 0; j < SPW; ++j)
+    for (int j = 0; j < SPW; ++j) {
+      const bool ok = xok && st * UG_KC + 2 * (wave * SPW + j) + g < nchk;
+      const u32x4 xj = ok ? xa[j] : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
       for (int t = 0; t < NTL; ++t) {
         const int idx = (t * 32 + row) * UG_LD + 2 * (wave * SPW + j) + g;
-        au[t] = mma16(xv[j], s_w[buf][0][idx], au[t]);
-        if constexpr (GATE) ag[t] = mma16(xv[j], s_w[buf][NMAT - 1][idx], ag[t]);
+        au[t] = mma16(xj, s_w[buf][0][idx], au[t]);
+        if constexpr (GATE) ag[t] = mma16(xj, s_w[buf][NMAT - 1][idx], ag[t]);
       }
-    if (st + 1 < nstage) store_w(buf ^ 1, wr1);
-#pragma unroll
-    for (int mt = 0; mt < NMAT; ++mt)
-#pragma unroll
-      for (int i = 0; i < LPT; ++i) wr1[mt][i] = wr2[mt][i];
-#pragma unroll
-    for (int j = 0; j < SPW; ++j) {
-      xv[j] = xn1[j];
-      xn1[j] = xn2[j];
     }
+    store_w(buf ^ 1, st + 1, wb);                       // past the last stage: zeros, unread
     __syncthreads();
+  };
+  // whole rounds of six in the loop, the rest after it (an exit between the steps would join the
+  // loop head with loads in other registers in flight, and the head would wait for them all)
+  int st0 = 0;
+  for (; st0 + 6 <= nstage; st0 += 6) {
+    step(st0, xA, xC, wA, wB);
+    step(st0 + 1, xB, xA, wB, wA);
+    step(st0 + 2, xC, xB, wA, wB);
+    step(st0 + 3, xA, xC, wB, wA);
+    step(st0 + 4, xB, xA, wA, wB);
+    step(st0 + 5, xC, xB, wB, wA);
+  }
+  const int rest = nstage - st0;
+  if (rest > 0) {
+    step(st0, xA, xC, wA, wB);
+    if (rest > 1) {
+      step(st0 + 1, xB, xA, wB, wA);
+      if (rest > 2) {
+        step(st0 + 2, xC, xB, wA, wB);
+        if (rest > 3) {
+          step(st0 + 3, xA, xC, wB, wA);
+          if (rest > 4) step(st0 + 4, xB, xA, wA, wB);
+        }
+      }
+    }
+  }
+  // the tokens' own bitmap words for phase 3, all loads issued at once (clamped addresses, so
+  // unconditional), their latency hidden behind the cross-wave sums
+  uint32_t ob[NTL][16];
+#pragma unroll
+  for (int t = 0; t < NTL; ++t) {
+    const int nc = max(s_nid[t * 32 + row], 0);
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      ob[t][i] = ldg(a.bits, (size_t)min(acc_row(i, lane), a.B - 1) * W + (nc >> 5));
   }
 #pragma unroll
   for (int t = 0; t < NTL; ++t) {
@@ -519,8 +563,7 @@ __global__ __launch_bounds__(BT) void k_bug(BatchArgs a) {
           const float gg = fmaxf(ag[t][i] + bg, 0.0f);
           h = a.act == FFN_ACT_REGLU ? gg * u : gg * fmaxf(u, 0.0f);
         }
-        bool on = false;
-        if (nid >= 0 && m < a.B) on = (a.bits[(size_t)m * W + (nid >> 5)] >> (nid & 31)) & 1u;
+        const bool on = nid >= 0 && m < a.B && ((ob[t][i] >> (nid & 31)) & 1u);
         if (t0 + t * 32 + row < a.ffn) a.H[(size_t)m * a.ffn + t0 + t * 32 + row] = (_Float16)(on ? h : 0.0f);
       }
     }

@@ -97,6 +97,12 @@ __device__ __forceinline__ u32x4 ld16(const void* p) {
   return *(const __attribute__((address_space(1))) u32x4*)p;
 }
 
+// Element i of a device array, as a global load.
+template <class T>
+__device__ __forceinline__ T ldg(const T* p, size_t i) {
+  return ((const __attribute__((address_space(1))) T*)p)[i];
+}
+
 // The 32-bit word holding fp16 element i (an int4 group scale) of an array of an even number of
 // elements, as a global load; pick_h takes the element out of it once the value is needed.
 // A 16-bit load would be merged into a register half as soon as it lands, which needs a wait.
