@@ -224,6 +224,7 @@ __global__ __launch_bounds__(BS_T) void k_bs(BatchArgs a) {
                   u32x4 (&qn)[BS_PL]) {
     const int buf = c & 1;
     load(min(c + 2, nchunk - 1), zn, qn);
+    issue_fence();                         // the loads go out first
     if (live) {
 #pragma unroll
       for (int s = 0; s < BS_SW; ++s) {
@@ -490,6 +491,7 @@ __global__ __launch_bounds__(BT) void k_bug(BatchArgs a) {
     const int buf = st & 1;
     load_w(min(st + 2, nstage - 1), wc);
     load_x(min(st + 2, nstage - 1), xc);
+    issue_fence();                                      // the loads go out first
 #pragma unroll
     for (int j = 0; j < SPW; ++j) {
       const bool ok = xok && st * UG_KC + 2 * (wave * SPW + j) + g < nchk;

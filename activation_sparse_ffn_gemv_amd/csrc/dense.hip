@@ -105,30 +105,28 @@ __global__ __launch_bounds__(UP_T) void k_dup(DenseArgs a) {
     boff[i] = (size_t)n * nchk * 16;
     bch[i] = e % UP_KC;
   }
+  // Raw loads (clamped addresses, never predicated); rows past the tokens and chunks past the
+  // row end are zeroed on the way into LDS, so that no load has to land before the loop turns.
   auto load = [&](int st, u32x4 (&ra)[LA], u32x4 (&rb)[LB]) {
 #pragma unroll
-    for (int i = 0; i < LA; ++i) {
-      const int c = st * UP_KC + ach[i];
-      const u32x4 t = ld16(xsrc + aoff[i] + (size_t)min(c, nchk - 1) * 16);
-      ra[i] = (aok[i] && c < nchk) ? t : u32x4{0u, 0u, 0u, 0u};
-    }
+    for (int i = 0; i < LA; ++i)
+      ra[i] = ld16(xsrc + aoff[i] + (size_t)min(st * UP_KC + ach[i], nchk - 1) * 16);
 #pragma unroll
-    for (int i = 0; i < LB; ++i) {
-      const int c = st * UP_KC + bch[i];
-      const u32x4 t = ld16(bsrc[i] + boff[i] + (size_t)min(c, nchk - 1) * 16);
-      rb[i] = c < nchk ? t : u32x4{0u, 0u, 0u, 0u};
-    }
+    for (int i = 0; i < LB; ++i)
+      rb[i] = ld16(bsrc[i] + boff[i] + (size_t)min(st * UP_KC + bch[i], nchk - 1) * 16);
   };
-  auto store = [&](int buf, const u32x4 (&ra)[LA], const u32x4 (&rb)[LB]) {
+  auto store = [&](int buf, int st, const u32x4 (&ra)[LA], const u32x4 (&rb)[LB]) {
 #pragma unroll
     for (int i = 0; i < LA; ++i) {
       const int e = tid + UP_T * i;
-      sA[buf][(e / UP_KC) * UP_LD + e % UP_KC] = ra[i];
+      const bool ok = aok[i] && st * UP_KC + ach[i] < nchk;
+      sA[buf][(e / UP_KC) * UP_LD + e % UP_KC] = ok ? ra[i] : u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int i = 0; i < LB; ++i) {
       const int e = tid + UP_T * i;
-      sB[buf][(e / UP_KC) * UP_LD + e % UP_KC] = rb[i];
+      const bool ok = st * UP_KC + bch[i] < nchk;
+      sB[buf][(e / UP_KC) * UP_LD + e % UP_KC] = ok ? rb[i] : u32x4{0u, 0u, 0u, 0u};
     }
   };
 
@@ -140,16 +138,24 @@ __global__ __launch_bounds__(UP_T) void k_dup(DenseArgs a) {
 #pragma unroll
       for (int mt = 0; mt < NMAT; ++mt) acc[ms][ns][mt] = f32x16{};
 
-  // loads run two stages ahead (two register sets), LDS holds the current and the next stage
+  // Loads run two stages ahead, LDS holds the current and the next stage.  The two register sets
+  // swap roles by name each turn (stage s+1 held for LDS, stage s+2 arriving), never by copy: a
+  // copy of a register that a load is still filling waits for the load.  Loads and LDS stores are
+  // unconditional (the last two turns re-read the last stage, from L2, and the last store writes
+  // zeros nobody reads), and the loop holds whole pairs of stages: a branch around a load or an
+  // exit between the pair would join paths with other loads in flight, and the waits would then
+  // cover this turn's loads too.
   const int nstage = (nchk + UP_KC - 1) / UP_KC;
-  u32x4 ra1[LA], rb1[LB], ra2[LA], rb2[LB];             // stages s+1 and s+2 in flight
-  load(0, ra1, rb1);
-  store(0, ra1, rb1);
-  if (nstage > 1) load(1, ra1, rb1);
+  u32x4 raA[LA], rbA[LB], raB[LA], rbB[LB];
+  load(0, raB, rbB);
+  load(min(1, nstage - 1), raA, rbA);
+  store(0, 0, raB, rbB);
   __syncthreads();
-  for (int s = 0; s < nstage; ++s) {
+  auto step = [&](int s, const u32x4 (&rah)[LA], const u32x4 (&rbh)[LB], u32x4 (&ran)[LA],
+                  u32x4 (&rbn)[LB]) {
     const int buf = s & 1;
-    if (s + 2 < nstage) load(s + 2, ra2, rb2);
+    load(min(s + 2, nstage - 1), ran, rbn);
+    issue_fence();                                      // the loads go out first
 #pragma unroll
     for (int kk = 0; kk < UP_KC / 2; ++kk) {
       u32x4 af[2];
@@ -165,16 +171,36 @@ __global__ __launch_bounds__(UP_T) void k_dup(DenseArgs a) {
           for (int ms = 0; ms < 2; ++ms) acc[ms][ns][mt] = mma16(af[ms], bf, acc[ms][ns][mt]);
         }
     }
-    if (s + 1 < nstage) store(buf ^ 1, ra1, rb1);
+    store(buf ^ 1, s + 1, rah, rbh);
+    __syncthreads();
+  };
+  int s0 = 0;
+  for (; s0 + 2 <= nstage; s0 += 2) {
+    step(s0, raA, rbA, raB, rbB);
+    step(s0 + 1, raB, rbB, raA, rbA);
+  }
+  if (s0 < nstage) step(s0, raA, rbA, raB, rbB);
+
+  // the tile's words of the tokens' bitmaps, staged in LDS (the stage buffers are free now) by
+  // one round of loads, instead of one dependent load per output element
+  constexpr int TW = UP_N / 32;                         // bitmap words per token row
+  uint32_t* s_bits = reinterpret_cast<uint32_t*>(&sA[0][0]);
+  static_assert(sizeof(sA) >= UP_M * TW * sizeof(uint32_t), "bitmap words fit in the A stages");
+  const int W = a.ffn / 32;
+  if (a.bits) {
+    constexpr int BL = UP_M * TW / UP_T;
+    uint32_t bw[BL];
 #pragma unroll
-    for (int i = 0; i < LA; ++i) ra1[i] = ra2[i];
+    for (int i = 0; i < BL; ++i) {
+      const int e = tid + UP_T * i, row = e / TW, wc = e % TW;
+      bw[i] = ldg(a.bits, (size_t)min(m0 + row, a.M - 1) * W + min(n0 / 32 + wc, W - 1));
+    }
 #pragma unroll
-    for (int i = 0; i < LB; ++i) rb1[i] = rb2[i];
+    for (int i = 0; i < BL; ++i) s_bits[tid + UP_T * i] = bw[i];
     __syncthreads();
   }
 
   // epilogue: h per (token, neuron), masked by the token's set, to H (fp16)
-  const int W = a.ffn / 32;
 #pragma unroll
   for (int ns = 0; ns < NSUB; ++ns) {
     const int n = n0 + wn * (UP_N / 2) + ns * 32 + r32;
@@ -195,7 +221,7 @@ __global__ __launch_bounds__(UP_T) void k_dup(DenseArgs a) {
           h = a.act == FFN_ACT_REGLU ? gg * u : gg * fmaxf(u, 0.0f);
         }
         if (m < a.M && n < a.ffn) {
-          if (a.bits && !((a.bits[(size_t)m * W + (n >> 5)] >> (n & 31)) & 1u)) h = 0.0f;
+          if (a.bits && !((s_bits[(m - m0) * TW + (n - n0) / 32] >> (n & 31)) & 1u)) h = 0.0f;
           a.H[(size_t)m * a.ffn + n] = (_Float16)h;
         }
       }
