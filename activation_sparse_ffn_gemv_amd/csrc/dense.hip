@@ -228,7 +228,7 @@ __global__ __launch_bounds__(UP_T) void k_dup(DenseArgs a) {
   }
 }
 
-__global__ __launch_bounds__(DT) void k_ddown(DenseArgs a) {
+__global__ __launch_bounds__(DT, 2) void k_ddown(DenseArgs a) {
   __shared__ u32x4 s_b[2][DD_K * DD_LD];             // [buffer][k row * DD_LD + column chunk]
   if (a.run_if && *a.run_if != a.run_want) return;
   const int nb_m = (a.M + DD_M - 1) / DD_M, nb_n = (a.d + DD_N - 1) / DD_N;
@@ -268,12 +268,10 @@ __global__ __launch_bounds__(DT) void k_ddown(DenseArgs a) {
       s_b[buf][(e / (DD_N / 8)) * DD_LD + e % (DD_N / 8)] = v[i];
     }
   };
+  // raw loads of the token rows; rows past the tokens are zeroed where they feed the MFMAs
   auto load_a = [&](int k0, u32x4 (&v)[2]) {
 #pragma unroll
-    for (int ss = 0; ss < 2; ++ss) {
-      const u32x4 t = *reinterpret_cast<const u32x4*>(arow + (size_t)(k0 + 16 * ss + 8 * g) * 2);
-      v[ss] = aok ? t : u32x4{0u, 0u, 0u, 0u};
-    }
+    for (int ss = 0; ss < 2; ++ss) v[ss] = ld16(arow + (size_t)(k0 + 16 * ss + 8 * g) * 2);
   };
 
   f32x16 acc[8];
@@ -281,25 +279,31 @@ __global__ __launch_bounds__(DT) void k_ddown(DenseArgs a) {
   for (int b = 0; b < 8; ++b) acc[b] = f32x16{};
 
   if (st0 < st1) {
-    // loads two stages ahead: (wn1, an1) hold stage s+1, (wn2, an2) receive stage s+2; LDS holds
-    // the current and the next stage
-    u32x4 wn1[4], wn2[4], av[2], an1[2], an2[2];
-    load_w(st0 * DD_K, wn1);
-    load_a(st0 * DD_K, av);
-    store_w(0, wn1);
-    if (st0 + 1 < st1) {
-      load_w((st0 + 1) * DD_K, wn1);
-      load_a((st0 + 1) * DD_K, an1);
-    }
+    // Loads run two stages ahead, LDS holds the current and the next stage of weights.  Three
+    // register sets of each operand swap roles by name (stage t in use / held for LDS, stage
+    // t+2 arriving), never by copy: a copy of a register that a load is still filling waits for
+    // the load.  Loads and LDS stores are unconditional (the last two turns re-read the slice's
+    // last stage, from L2; the last store is never read), and the loop holds whole rounds of
+    // three: a branch around a load or an exit inside the round would join paths with other
+    // loads in flight, and the waits would then cover this turn's loads too.
+    const int nst = st1 - st0;
+    u32x4 w0[4], w1[4], w2[4], a0[2], a1[2], a2[2];
+    auto kof = [&](int t) { return (st0 + min(t, nst - 1)) * DD_K; };
+    load_w(kof(0), w0);
+    load_a(kof(0), a0);
+    load_w(kof(1), w1);
+    load_a(kof(1), a1);
+    store_w(0, w0);
     __syncthreads();
-    for (int s = st0; s < st1; ++s) {
-      const int buf = (s - st0) & 1;
-      if (s + 2 < st1) {
-        load_w((s + 2) * DD_K, wn2);
-        load_a((s + 2) * DD_K, an2);
-      }
+    auto step = [&](int t, const u32x4 (&acur)[2], u32x4 (&arecv)[2], const u32x4 (&whold)[4],
+                    u32x4 (&wrecv)[4]) {
+      const int buf = t & 1;
+      load_w(kof(t + 2), wrecv);
+      load_a(kof(t + 2), arecv);
+      issue_fence();                                    // the loads go out first
 #pragma unroll
       for (int ss = 0; ss < 2; ++ss) {
+        const u32x4 av = aok ? acur[ss] : u32x4{0u, 0u, 0u, 0u};
         // rows 16 ss + 8 g + j (j = 0..7), columns 8p .. 8p+7 of the tile
         uint32_t r[8][4];
 #pragma unroll
@@ -322,18 +326,22 @@ __global__ __launch_bounds__(DT) void k_ddown(DenseArgs a) {
           hi.y = __builtin_amdgcn_perm(r[3][q], r[2][q], 0x07060302u);
           hi.z = __builtin_amdgcn_perm(r[5][q], r[4][q], 0x07060302u);
           hi.w = __builtin_amdgcn_perm(r[7][q], r[6][q], 0x07060302u);
-          acc[2 * q] = mma16(av[ss], lo, acc[2 * q]);
-          acc[2 * q + 1] = mma16(av[ss], hi, acc[2 * q + 1]);
+          acc[2 * q] = mma16(av, lo, acc[2 * q]);
+          acc[2 * q + 1] = mma16(av, hi, acc[2 * q + 1]);
         }
       }
-      if (s + 1 < st1) store_w(buf ^ 1, wn1);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) wn1[i] = wn2[i];
-      av[0] = an1[0];
-      av[1] = an1[1];
-      an1[0] = an2[0];
-      an1[1] = an2[1];
+      store_w(buf ^ 1, whold);
       __syncthreads();
+    };
+    int t0 = 0;
+    for (; t0 + 3 <= nst; t0 += 3) {
+      step(t0, a0, a2, w1, w2);
+      step(t0 + 1, a1, a0, w2, w0);
+      step(t0 + 2, a2, a1, w0, w1);
+    }
+    if (t0 < nst) {
+      step(t0, a0, a2, w1, w2);
+      if (t0 + 1 < nst) step(t0 + 1, a1, a0, w2, w0);
     }
   }
 
