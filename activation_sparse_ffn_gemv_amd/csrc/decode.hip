@@ -803,16 +803,18 @@ __global__ __launch_bounds__(RD_THREADS) void k_reduce(ReduceArgs a) {
   const int j = tile * RD_TW + q * 4;
   FFN_TS(2, 0);
   const int nslot = MODE == 2 ? a.nslot : 1;
-  // b_down (of each expert slot, routing-weighted), fetched with the partials
+  // b_down (of each expert slot, routing-weighted).  One layer: the load goes out now and is
+  // first used after the loop, so it does not hold up the partials' loads.
   f32x4 bias = {0.f, 0.f, 0.f, 0.f};
-  if (threadIdx.x < RD_Q && j < a.d) {
-    for (int k = 0; k < nslot; ++k) {
-      const float* b_down = MODE == 2 ? a.slot[k].b_down : a.b_down;
-      if (b_down) {
-        const f32x4 b = *reinterpret_cast<const f32x4*>(b_down + j);
-        bias += MODE == 2 ? a.slot[k].wgt * b : b;
+  if (MODE == 2) {
+    if (threadIdx.x < RD_Q && j < a.d) {
+      for (int k = 0; k < nslot; ++k) {
+        const float* b_down = a.slot[k].b_down;
+        if (b_down) bias += a.slot[k].wgt * *reinterpret_cast<const f32x4*>(b_down + j);
       }
     }
+  } else if (threadIdx.x < RD_Q && j < a.d && a.b_down) {
+    bias = ldg(reinterpret_cast<const f32x4*>(a.b_down + j), 0);
   }
   const uint32_t np = MODE == 0 ? (uint32_t)GA_BLOCKS : (uint32_t)a.n_part;
   const uint32_t items = (uint32_t)nslot * np;
