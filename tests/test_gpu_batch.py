@@ -66,12 +66,21 @@ BATCH_SHAPES = [
 ]
 
 
-@pytest.mark.parametrize("B", [2, 7, 32, 33, 45])
+@pytest.mark.parametrize("B", [2, 7, 8, 31, 32, 33, 45])
 @pytest.mark.parametrize("kw", BATCH_SHAPES, ids=lambda k: "%s_d%d_f%d" % (k["act"], k["d"],
                                                                           k["ffn"]))
 def test_batched_predicted_path(ffn, kw, B):
     cfg = synth.small_config(w_dtype="f16", x_dtype="f16", p_dtype="f16", density=0.1, **kw)
     _check(ffn, cfg, B)
+
+
+@pytest.mark.parametrize("kw", BATCH_SHAPES[:3], ids=lambda k: "%s_d%d_f%d" % (k["act"], k["d"],
+                                                                              k["ffn"]))
+def test_batched_predicted_path_512_tokens(ffn, kw):
+    """512 tokens on the sparse path: sixteen passes of 32 tokens, each with its own union;
+    sampled tokens at the pass edges and the last one are checked against the oracle."""
+    cfg = synth.small_config(w_dtype="f16", x_dtype="f16", p_dtype="f16", density=0.1, **kw)
+    _check(ffn, cfg, 512, tokens=[0, 31, 32, 33, 255, 256, 480, 511])
 
 
 def test_batched_caller_masks(ffn):
