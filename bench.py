@@ -55,14 +55,16 @@ def pred_bytes(cfg, n_hot=0):
     return cfg.rank * cfg.d * pb, nf * cfg.rank * pb + 4 * nf
 
 
-def profiled_traffic(kernel: str, workload: str):
+def profiled_traffic(kernel: str, workload: str, with_trace: bool = False):
     """HBM bytes per launch of `kernel` on `workload` from a committed rocprofv3 summary under
     profiles/ (FETCH_SIZE + WRITE_SIZE, scaled against a copy of known size), or None when there
-    is none or the kernel source has changed since the counters were taken."""
+    is none or the kernel source has changed since the counters were taken.  with_trace: also
+    the summary's kernel-trace mean duration in microseconds (or None), as a pair."""
     import glob
     import hashlib
     for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
-        for line in open(path):
+        lines = open(path).read().splitlines()
+        for line in lines:
             f = line.split()
             if not f or f[0] != "traffic":
                 continue
@@ -70,12 +72,16 @@ def profiled_traffic(kernel: str, workload: str):
             if kv.get("kernel") != kernel or kv.get("workload") != workload:
                 continue
             src = os.path.join(ROOT, kv["source"])
-            if not os.path.exists(src):
-                return None
-            if hashlib.sha256(open(src, "rb").read()).hexdigest() != kv.get("sha256"):
-                return None
-            return int(kv["bytes_per_launch"])
-    return None
+            if (not os.path.exists(src) or
+                    hashlib.sha256(open(src, "rb").read()).hexdigest() != kv.get("sha256")):
+                return (None, None) if with_trace else None
+            trace_us = None
+            for ln in lines:
+                if ln.startswith("- mean duration (kernel trace):"):
+                    trace_us = float(ln.split(":", 1)[1].split()[0])
+            nb = int(kv["bytes_per_launch"])
+            return (nb, trace_us) if with_trace else nb
+    return (None, None) if with_trace else None
 
 
 def main():
@@ -466,20 +472,22 @@ def main():
               "reduce": "k_reduce", "batch_upgate": "k_bug", "batch_down": "k_bdown",
               "dense_up": "k_dup", "dense_down": "k_ddown"}
     if prefill:
+        prof = profiled_traffic(knames[dom], cfg.name + ":prefill%d" % Bt, with_trace=True)
         roof = {"bound": "mfma", "kernel": knames[dom], "achieved": stages[dom]["tflops"],
                 "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(stages[dom]["tflops"] / MFMA_F16_PEAK_TFLOPS, 4),
-                "traffic": profiled_traffic(knames[dom], cfg.name + ":prefill%d" % Bt),
+                "traffic": prof[0], "trace_avg_us": prof[1],
                 "avg_us": stages[dom]["avg_us"],
                 "flops_per_launch": stages[dom]["flops_per_launch"]}
     else:
         wl = ((cfg.name if Bt == 1 else cfg.name + ":batch%d" % Bt) + (":hot" if n_hot else "")
               + (":fit" if fitq is not None or cfg.spectrum_alpha else "")
               + (":offload" if args.offload else ""))
+        prof = profiled_traffic(knames[dom], wl, with_trace=True)
         roof = {"bound": "hbm", "kernel": knames[dom], "achieved": stages[dom]["gbps"],
                 "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(stages[dom]["gbps"] / HBM_PEAK_GBPS, 4),
-                "traffic": profiled_traffic(knames[dom], wl),
+                "traffic": prof[0], "trace_avg_us": prof[1],
                 "avg_us": stages[dom]["avg_us"],
                 "bytes_per_launch": stages[dom]["bytes_per_launch"]}
 
@@ -523,10 +531,21 @@ def main():
         what = ("dense FFN" if prefill else
                 "router + the chosen experts' predictor and sparse FFN" if moe else
                 "predictor + sparse FFN")
+        cpu_model = ""
+        try:
+            with open("/proc/cpuinfo") as f:
+                cpu_model = next((ln.split(":", 1)[1].strip() for ln in f
+                                  if ln.startswith("model name")), "")
+        except OSError:
+            pass
+        tok_bytes = touched.sum() / (K * Bt)              # touched bytes per token, all layers
         cpu = {"value": round(rate, 5), "unit": "tokens/s", "cores": 1, "kind": "oracle",
                "sample": "first %d token(s) x %d of %d layers, %s, single-threaded C with fp64 "
                          "accumulation (%.1f s of CPU), scaled to all layers" % (
-                             nt, L_cpu, L, what, t_cpu)}
+                             nt, L_cpu, L, what, t_cpu),
+               "s_per_token": round(1.0 / rate, 3),
+               "gbps_over_touched_bytes": round(rate * tok_bytes / 1e9, 4),
+               "host": {"cpu_model": cpu_model, "logical_cpus": os.cpu_count()}}
 
         # parity spot check against the oracle evaluated on the GPU's own sets: the sampled
         # tokens of layer 0, then seeded random (layer, token) pairs over the whole stack; every

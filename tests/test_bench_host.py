@@ -40,14 +40,17 @@ def test_profiled_traffic_follows_the_source_hash(tmp_path, monkeypatch):
     prof = tmp_path / "profiles"
     prof.mkdir()
     (prof / "k_x_w.md").write_text(
-        "# summary\n\n    traffic kernel=k_x workload=w bytes_per_launch=1234 source=k.hip "
+        "# summary\n\n- mean duration (kernel trace): 10.89 us\n\n"
+        "    traffic kernel=k_x workload=w bytes_per_launch=1234 source=k.hip "
         "sha256=%s\n" % h)
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
     assert bench.profiled_traffic("k_x", "w") == 1234
+    assert bench.profiled_traffic("k_x", "w", with_trace=True) == (1234, 10.89)
     assert bench.profiled_traffic("k_x", "other") is None
-    assert bench.profiled_traffic("k_y", "w") is None
+    assert bench.profiled_traffic("k_y", "w", with_trace=True) == (None, None)
     src.write_text("kernel source v2\n")                 # kernel changed since the counters
     assert bench.profiled_traffic("k_x", "w") is None
+    assert bench.profiled_traffic("k_x", "w", with_trace=True) == (None, None)
 
 
 def test_committed_profiles_name_existing_sources():
