@@ -84,7 +84,7 @@ def profiled_traffic(kernel: str, workload: str, with_trace: bool = False):
     return (None, None) if with_trace else None
 
 
-def main():
+def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None,
@@ -128,7 +128,9 @@ def main():
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="first run a plain device copy of this many MiB five times (a known "
                          "size against which a profiler's HBM byte counters are scaled)")
-    args = ap.parse_args()
+    ap.add_argument("--cpu-budget", type=float, default=CPU_BUDGET_S,
+                    help="seconds of CPU time after which the oracle baseline stops adding layers")
+    args = ap.parse_args(argv)
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (the operator "
               "would shard by neurons, see the design notes); run with --gpus 1",
@@ -525,7 +527,7 @@ def main():
                     oracle.sparse_token(OL, xh[t], n_hot=n_hot)
                 t_cpu += time.perf_counter() - c0
             L_cpu = l + 1
-            if t_cpu > CPU_BUDGET_S:
+            if t_cpu > args.cpu_budget:
                 break
         rate = nt * L_cpu / t_cpu / L          # tokens through all L layers per second
         what = ("dense FFN" if prefill else
