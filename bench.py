@@ -100,6 +100,8 @@ def main(argv=None):
     ap.add_argument("--parity-pairs", type=int, default=8,
                     help="seeded random (layer, token) pairs beyond layer 0 whose timed-run "
                          "outputs are checked against the oracle (prefill: at most 2)")
+    ap.add_argument("--parity-stack-tokens", type=int, default=0,
+                    help="also check the first N tokens at every layer of the stack")
     ap.add_argument("--cpu-tokens", type=int, default=3,
                     help="tokens the CPU oracle baseline runs per layer; 0 = skip")
     ap.add_argument("--decode-variant", type=int, default=None,
@@ -558,6 +560,8 @@ def main(argv=None):
         if L > 1 and n_pairs > 0:
             pairs += [(int(l), int(t)) for l, t in zip(rng.integers(1, L, size=n_pairs),
                                                        rng.integers(0, K * Bt, size=n_pairs))]
+        pairs += [(l, t) for l in range(L) for t in range(min(args.parity_stack_tokens, K * Bt))]
+        pairs = sorted(set(pairs))
         worst = 0.0
         torch.cuda.synchronize()
 
@@ -574,7 +578,7 @@ def main(argv=None):
 
         t_par = time.time()
         l_host, OLs = -1, None
-        for l, t in sorted(pairs):
+        for l, t in pairs:
             if l != l_host:                                  # one layer on the host at a time
                 OLs, l_host = None, l
                 OLs = [host(e) for e in layers[l]]

@@ -20,11 +20,13 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 # (case id, bench arguments, smallest number of (layer, token) pairs checked)
 CASES = [
     ("opt125m", ["--config", "opt125m_relu_f32", "--steps", "8", "--cpu-tokens", "4"], 4),
-    ("llama2", ["--config", "llama2_7b_reglu_f16", "--steps", "4", "--parity-pairs", "6"], 7),
+    # the 7B-shaped stacks: the first two tokens at every one of the 32 layers, plus random pairs
+    ("llama2", ["--config", "llama2_7b_reglu_f16", "--steps", "4", "--parity-pairs", "6",
+                "--parity-stack-tokens", "2"], 64),
     ("mistral", ["--config", "turbosparse_mistral_7b_drelu_f16", "--steps", "4",
-                 "--parity-pairs", "6"], 7),
+                 "--parity-pairs", "6", "--parity-stack-tokens", "2"], 64),
     ("mixtral_int4", ["--config", "turbosparse_mixtral_47b_moe_int4", "--steps", "4",
-                      "--parity-pairs", "6"], 7),
+                      "--parity-pairs", "6", "--parity-stack-tokens", "2"], 64),
     ("falcon_b1", ["--config", "falcon_40b_relu_f16", "--steps", "2", "--parity-pairs", "3"], 4),
     ("falcon_b8", ["--config", "falcon_40b_relu_f16", "--batch", "8", "--steps", "2",
                    "--parity-pairs", "3"], 4),
@@ -63,6 +65,8 @@ def test_full_size_parity_in_bench_configuration(bench_main, capsys, argv, min_p
     assert par["max_normwise_err"] <= par["tolerance"]
     if "opt125m" not in argv[1]:
         assert len(par["layers"]) > 1, par              # beyond layer 0
+    if "--parity-stack-tokens" in argv:
+        assert len(par["layers"]) == line["config"]["layers"], par     # every layer
     assert line["value"] > 0 and line["n_gpus"] == 1
     roof = line["roofline"]
     assert roof["achieved"] > 0 and 0 < roof["frac"] < 1, roof
