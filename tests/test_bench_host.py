@@ -65,3 +65,11 @@ def test_committed_profiles_name_existing_sources():
                 assert int(kv["bytes_per_launch"]) > 0
                 n += 1
     assert n >= 1
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """More than one GPU is refused with a message before anything touches a device."""
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
