@@ -228,6 +228,204 @@ __global__ __launch_bounds__(UP_T) void k_dup(DenseArgs a) {
   }
 }
 
+// k_dupq: the same tile and wave split as k_dup, with both operands copied from global memory
+// straight into LDS by gfx950's global_load_lds_dwordx4 (no register staging: the registers
+// the staging took hold a second set of MFMA fragments instead).  K stages of 32 (four 16-byte
+// chunks per row), a ring of four LDS slots, the copies for stage s + 3 issued once every wave
+// has finished stage s - 1.  A row's four chunks sit in its 64 LDS bytes in an order swizzled by
+// the row, (chunk ^ (row / 4) % 4), so that the fragment reads of 16 consecutive rows meet no bank
+// twice.  Rows past the tokens or neurons are clamped copies (their outputs are never stored);
+// d must be a multiple of 32 (no partial stage).
+constexpr int UQ_DK = 4;                   // chunks per row per stage (K = 32)
+constexpr int UQ_NS = 4;                   // LDS ring slots
+
+__device__ __forceinline__ constexpr int waitcnt_imm(int vm, int lgkm) {
+  return (vm & 0xf) | (0x7 << 4) | ((lgkm & 0xf) << 8) | (((vm >> 4) & 0x3) << 14);
+}
+// the target builtins sit in device helpers (a kernel template that names them directly gets
+// no host-side launch stub)
+__device__ __forceinline__ void lds_copy16(const void* src, u32x4* dst) {
+  __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+}
+template <int VM, int LGKM>
+__device__ __forceinline__ void wait_counts() {
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(VM, LGKM));
+}
+__device__ __forceinline__ void barrier_only() { __builtin_amdgcn_s_barrier(); }
+__device__ __forceinline__ int wave_uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+template <int MASK, int N>
+__device__ __forceinline__ void sched_group() { __builtin_amdgcn_sched_group_barrier(MASK, N, 0); }
+
+template <bool GATE>
+__global__ __launch_bounds__(UP_T) void k_dupq(DenseArgs a) {
+  constexpr int NMAT = GATE ? 2 : 1;
+  constexpr int UP_N = GATE ? 128 : 256;   // neurons per tile
+  constexpr int BROWS = UP_N * NMAT;       // weight rows per stage (up rows, then gate rows)
+  constexpr int NSUB = UP_N / 2 / 32;      // 32-neuron MFMA blocks per wave
+  constexpr int NW = UP_T / WAVE;          // 8 waves
+  constexpr int AI = UP_M / 16 / NW;       // A copy instructions per wave and stage (2)
+  constexpr int BI = BROWS / 16 / NW;      // B copy instructions per wave and stage (2)
+  constexpr int NB = NSUB * NMAT;
+  static_assert(AI * NW * 16 == UP_M && BI * NW * 16 == BROWS, "whole copy instructions");
+  // one array per ring slot (not one indexed array): the compiler then sees that a stage's reads
+  // and the copies in flight into the other slots touch different memory, and does not make the
+  // reads wait for those copies
+  __shared__ u32x4 sA0[UP_M * UQ_DK], sA1[UP_M * UQ_DK], sA2[UP_M * UQ_DK], sA3[UP_M * UQ_DK];
+  __shared__ u32x4 sB0[BROWS * UQ_DK], sB1[BROWS * UQ_DK], sB2[BROWS * UQ_DK], sB3[BROWS * UQ_DK];
+  static_assert(UQ_NS == 4, "four ring slots");
+  if (a.run_if && *a.run_if != a.run_want) return;
+  const int nb_m = (a.M + UP_M - 1) / UP_M, nb_n = (a.ffn + UP_N - 1) / UP_N;
+  const int tile = xcd_tile(nb_m * nb_n);
+  if (tile >= nb_m * nb_n) return;
+  const int m0 = (tile % nb_m) * UP_M, n0 = (tile / nb_m) * UP_N;
+  const int tid = threadIdx.x, lane = tid & (WAVE - 1);
+  const int wave = wave_uniform(tid / WAVE);             // scalar: the copies' LDS base
+  const int r32 = lane & 31, g = lane >> 5;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int nchk = a.d / 8, nst = nchk / UQ_DK;
+  const size_t rowb = (size_t)nchk * 16;
+
+  // copy sources: instruction i of this wave covers rows 16 (wave * AI + i) .. +15 of the tile,
+  // lane l row + l / 4 and LDS position l % 4, which holds chunk (l % 4) ^ (row / 4) % 4
+  const char* asrc[AI];
+  const char* bsrc[BI];
+  const int pos = lane & 3;
+#pragma unroll
+  for (int i = 0; i < AI; ++i) {
+    const int row = (wave * AI + i) * 16 + (lane >> 2);
+    asrc[i] = static_cast<const char*>(a.x) + (size_t)min(m0 + row, a.M - 1) * rowb +
+              (size_t)(pos ^ ((row >> 2) & 3)) * 16;
+  }
+#pragma unroll
+  for (int i = 0; i < BI; ++i) {
+    const int row = (wave * BI + i) * 16 + (lane >> 2);
+    const int mat = row / UP_N, n = min(n0 + row % UP_N, a.ffn - 1);
+    bsrc[i] = static_cast<const char*>(mat == 0 ? a.w_up : a.w_gate) + (size_t)n * rowb +
+              (size_t)(pos ^ ((row >> 2) & 3)) * 16;
+  }
+  auto copy = [&](int st, u32x4* dA, u32x4* dB) {   // stage st (clamped) into a ring slot
+    const size_t kb = (size_t)min(st, nst - 1) * UQ_DK * 16;
+#pragma unroll
+    for (int i = 0; i < AI; ++i)
+      lds_copy16(asrc[i] + kb, dA + (wave * AI + i) * 64);
+#pragma unroll
+    for (int i = 0; i < BI; ++i)
+      lds_copy16(bsrc[i] + kb, dB + (wave * BI + i) * 64);
+  };
+  constexpr int PER_STAGE = AI + BI;       // copy instructions per wave and stage
+
+  f32x16 acc[2][NSUB][NMAT];
+#pragma unroll
+  for (int ms = 0; ms < 2; ++ms)
+#pragma unroll
+    for (int ns = 0; ns < NSUB; ++ns)
+#pragma unroll
+      for (int mt = 0; mt < NMAT; ++mt) acc[ms][ns][mt] = f32x16{};
+
+  // fragment (row, chunk) of a slot, at the row's swizzled position
+  auto frag = [&](const u32x4* base, int row, int c) {
+    return base[row * UQ_DK + (c ^ ((row >> 2) & 3))];
+  };
+  copy(0, sA0, sB0);
+  copy(1, sA1, sB1);
+  copy(2, sA2, sB2);
+  // stage st lives in slot st % 4; the turn reads it and copies stage st + 3 into the slot of
+  // stage st - 1 (slots named statically, four turns per loop round)
+  auto step = [&](int st, const u32x4* pa, const u32x4* pb, u32x4* nA, u32x4* nB) {
+    // this wave's copies of stage st have landed (stages st + 1, st + 2 may still be in
+    // flight) and its reads of stage st - 1 are done; after the barrier every wave's are
+    wait_counts<2 * PER_STAGE, 0>();
+    barrier_only();
+    issue_fence();
+    copy(st + 3, nA, nB);
+    issue_fence();
+    u32x4 fa[2][2], fb[2][NB];
+#pragma unroll
+    for (int kk = 0; kk < UQ_DK / 2; ++kk) {
+#pragma unroll
+      for (int ms = 0; ms < 2; ++ms) fa[kk][ms] = frag(pa, wm * 64 + ms * 32 + r32, 2 * kk + g);
+#pragma unroll
+      for (int ns = 0; ns < NSUB; ++ns)
+#pragma unroll
+        for (int mt = 0; mt < NMAT; ++mt)
+          fb[kk][ns * NMAT + mt] = frag(pb, mt * UP_N + wn * (UP_N / 2) + ns * 32 + r32, 2 * kk + g);
+    }
+#pragma unroll
+    for (int kk = 0; kk < UQ_DK / 2; ++kk)
+#pragma unroll
+      for (int ns = 0; ns < NSUB; ++ns)
+#pragma unroll
+        for (int mt = 0; mt < NMAT; ++mt)
+#pragma unroll
+          for (int ms = 0; ms < 2; ++ms)
+            acc[ms][ns][mt] = mma16(fa[kk][ms], fb[kk][ns * NMAT + mt], acc[ms][ns][mt]);
+    // every fragment read of the stage first, then the MFMAs (the second step's reads land
+    // while the first step's MFMAs run)
+    sched_group<0x100, UQ_DK / 2 * (2 + NB)>();
+    sched_group<0x008, UQ_DK / 2 * 2 * NB>();
+  };
+  int st = 0;
+  for (; st + 4 <= nst; st += 4) {
+    step(st, sA0, sB0, sA3, sB3);
+    step(st + 1, sA1, sB1, sA0, sB0);
+    step(st + 2, sA2, sB2, sA1, sB1);
+    step(st + 3, sA3, sB3, sA2, sB2);
+  }
+  if (st < nst) {
+    step(st, sA0, sB0, sA3, sB3);
+    if (st + 1 < nst) {
+      step(st + 1, sA1, sB1, sA0, sB0);
+      if (st + 2 < nst) step(st + 2, sA2, sB2, sA1, sB1);
+    }
+  }
+  // every copy (the clamped ones past the last stage included) has landed before the slots
+  // are reused for the bitmap words
+  wait_counts<0, 0>();
+  __syncthreads();
+
+  constexpr int TW = UP_N / 32;                         // bitmap words per token row
+  uint32_t* s_bits = reinterpret_cast<uint32_t*>(&sA0[0]);
+  static_assert(sizeof(sA0) >= UP_M * TW * sizeof(uint32_t), "bitmap words fit in an A slot");
+  const int W = a.ffn / 32;
+  if (a.bits) {
+    constexpr int BL = UP_M * TW / UP_T;
+    uint32_t bw[BL];
+#pragma unroll
+    for (int i = 0; i < BL; ++i) {
+      const int e = tid + UP_T * i, row = e / TW, wc = e % TW;
+      bw[i] = ldg(a.bits, (size_t)min(m0 + row, a.M - 1) * W + min(n0 / 32 + wc, W - 1));
+    }
+#pragma unroll
+    for (int i = 0; i < BL; ++i) s_bits[tid + UP_T * i] = bw[i];
+    __syncthreads();
+  }
+#pragma unroll
+  for (int ns = 0; ns < NSUB; ++ns) {
+    const int n = n0 + wn * (UP_N / 2) + ns * 32 + r32;
+    const int nc = min(n, a.ffn - 1);
+    const float bu = a.b_up ? a.b_up[nc] : 0.0f;
+    const float bg = (GATE && a.b_gate) ? a.b_gate[nc] : 0.0f;
+#pragma unroll
+    for (int ms = 0; ms < 2; ++ms)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int m = m0 + wm * 64 + ms * 32 + acc_row(i, lane);
+        const float u = acc[ms][ns][0][i] + bu;
+        float h;
+        if constexpr (!GATE) {
+          h = fmaxf(u, 0.0f);
+        } else {
+          const float gg = fmaxf(acc[ms][ns][NMAT - 1][i] + bg, 0.0f);
+          h = a.act == FFN_ACT_REGLU ? gg * u : gg * fmaxf(u, 0.0f);
+        }
+        if (m < a.M && n < a.ffn) {
+          if (a.bits && !((s_bits[(m - m0) * TW + (n - n0) / 32] >> (n & 31)) & 1u)) h = 0.0f;
+          a.H[(size_t)m * a.ffn + n] = (_Float16)h;
+        }
+      }
+  }
+}
+
 __global__ __launch_bounds__(DT, 2) void k_ddown(DenseArgs a) {
   __shared__ u32x4 s_b[2][DD_K * DD_LD];             // [buffer][k row * DD_LD + column chunk]
   if (a.run_if && *a.run_if != a.run_want) return;
@@ -411,17 +609,23 @@ hipError_t launch_dense(const DenseArgs& a, hipStream_t st, hipEvent_t (*ev)[2])
   const int t_dn = ((a.M + DD_M - 1) / DD_M) * ((a.d + DD_N - 1) / DD_N) * a.ks;
   const dim3 g_up(8 * ((t_up + 7) / 8)), g_dn(8 * ((t_dn + 7) / 8));
   const dim3 g_red((unsigned)(((size_t)a.M * a.d / 4 + 255) / 256));
+  // rows in whole 32-wide K stages take the LDS-copy kernel
+  const bool q = a.d % (8 * UQ_DK) == 0;
+#define UP_LAUNCH(K)                                                                      \
+  do {                                                                                    \
+    if (ev && ev[0][0])                                                                   \
+      hipExtLaunchKernelGGL(K, g_up, dim3(UP_T), 0, st, ev[0][0], ev[0][1], 0, a);        \
+    else                                                                                  \
+      hipLaunchKernelGGL(K, g_up, dim3(UP_T), 0, st, a);                                  \
+  } while (0)
   if (a.has_gate) {
-    if (ev && ev[0][0])
-      hipExtLaunchKernelGGL(k_dup<true>, g_up, dim3(UP_T), 0, st, ev[0][0], ev[0][1], 0, a);
-    else
-      hipLaunchKernelGGL(k_dup<true>, g_up, dim3(UP_T), 0, st, a);
+    if (q) UP_LAUNCH(k_dupq<true>);
+    else UP_LAUNCH(k_dup<true>);
   } else {
-    if (ev && ev[0][0])
-      hipExtLaunchKernelGGL(k_dup<false>, g_up, dim3(UP_T), 0, st, ev[0][0], ev[0][1], 0, a);
-    else
-      hipLaunchKernelGGL(k_dup<false>, g_up, dim3(UP_T), 0, st, a);
+    if (q) UP_LAUNCH(k_dupq<false>);
+    else UP_LAUNCH(k_dup<false>);
   }
+#undef UP_LAUNCH
   if (ev && ev[1][0])
     hipExtLaunchKernelGGL(k_ddown, g_dn, dim3(DT), 0, st, ev[1][0], ev[1][1], 0, a);
   else

@@ -474,7 +474,8 @@ def main(argv=None):
     dom = max(stages, key=lambda k: stages[k]["avg_us"])
     knames = {"pred_z": "k_pred_z", "pred_s": "k_pred_s", "gather": "k_gather",
               "reduce": "k_reduce", "batch_upgate": "k_bug", "batch_down": "k_bdown",
-              "dense_up": "k_dup", "dense_down": "k_ddown"}
+              # rows in whole 32-wide K stages take the LDS-copy up projection
+              "dense_up": "k_dupq" if cfg.d % 32 == 0 else "k_dup", "dense_down": "k_ddown"}
     if prefill:
         prof = profiled_traffic(knames[dom], cfg.name + ":prefill%d" % Bt, with_trace=True)
         roof = {"bound": "mfma", "kernel": knames[dom], "achieved": stages[dom]["tflops"],
