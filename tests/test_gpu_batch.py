@@ -286,3 +286,22 @@ def test_largest_batch_dense_and_auto(ffn):
             y_ref, _ = oracle.ffn(OL, xh[t], mask_from_idx(ih[t, :ch[t]], cfg.ffn))
             assert normwise(yh[t], y_ref) <= TOL["f16"], (path, t)
     m.close()
+
+
+@pytest.mark.parametrize("act,B", [("drelu", 70), ("relu", 256)])
+def test_dense_path_is_deterministic(ffn, act, B):
+    """The dense GEMMs (every copy into LDS waited for before its stage is read) give
+    bit-identical outputs call after call."""
+    kw = dict(bias_gate=True, bias_up=True) if act == "drelu" else dict(bias_up=True)
+    cfg = synth.small_config(d=1024, ffn=4096, rank=64, act=act, w_dtype="f16", x_dtype="f16",
+                             p_dtype="f16", density=0.1, **kw)
+    L = to_device(synth.make_layer(cfg))
+    x = synth.make_tokens(cfg, B).cuda()
+    m = ffn.SparseFFN(L, max_batch=B)
+    y0 = m.dense(x).clone()
+    torch.cuda.synchronize()
+    for _ in range(12):
+        y = m.dense(x)
+        torch.cuda.synchronize()
+        assert torch.equal(y, y0)
+    m.close()
