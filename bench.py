@@ -20,6 +20,7 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import re
 import sys
 import time
 
@@ -82,6 +83,30 @@ def profiled_traffic(kernel: str, workload: str, with_trace: bool = False):
             nb = int(kv["bytes_per_launch"])
             return (nb, trace_us) if with_trace else nb
     return (None, None) if with_trace else None
+
+
+def profiled_mfma_busy(kernel: str, workload: str):
+    """MFMA utilisation (a fraction) of `kernel` on `workload` from the busy-cycle counter pass
+    in its committed rocprofv3 summary (SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE per XCD x
+    1024 SIMDs), or None when the summary has no such pass or its kernel source has changed."""
+    import glob
+    import hashlib
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
+        lines = open(path).read().splitlines()
+        tl = [ln.split() for ln in lines if ln.split()[:1] == ["traffic"]]
+        kv = next((dict(t.split("=", 1) for t in f[1:] if "=" in t) for f in tl), None)
+        if kv is None or kv.get("kernel") != kernel or kv.get("workload") != workload:
+            continue
+        src = os.path.join(ROOT, kv["source"])
+        if (not os.path.exists(src) or
+                hashlib.sha256(open(src, "rb").read()).hexdigest() != kv.get("sha256")):
+            return None
+        for ln in lines:
+            m = re.match(r"- MFMA utilisation .*\*\*([0-9.]+)%\*\*", ln)
+            if m:
+                return round(float(m.group(1)) / 100.0, 4)
+        return None
+    return None
 
 
 def main(argv=None):
@@ -482,6 +507,7 @@ def main(argv=None):
                 "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(stages[dom]["tflops"] / MFMA_F16_PEAK_TFLOPS, 4),
                 "traffic": prof[0], "trace_avg_us": prof[1],
+                "mfma_busy": profiled_mfma_busy(knames[dom], cfg.name + ":prefill%d" % Bt),
                 "avg_us": stages[dom]["avg_us"],
                 "flops_per_launch": stages[dom]["flops_per_launch"]}
     else:

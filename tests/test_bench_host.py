@@ -53,6 +53,32 @@ def test_profiled_traffic_follows_the_source_hash(tmp_path, monkeypatch):
     assert bench.profiled_traffic("k_x", "w", with_trace=True) == (None, None)
 
 
+def test_profiled_mfma_busy_follows_the_source_hash(tmp_path, monkeypatch):
+    src = tmp_path / "k.hip"
+    src.write_text("gemm v1\n")
+    h = hashlib.sha256(src.read_bytes()).hexdigest()
+    prof = tmp_path / "profiles"
+    prof.mkdir()
+    (prof / "k_g_w.md").write_text(
+        "# summary\n\n- MFMA utilisation (busy cycles / (GRBM_GUI_ACTIVE per XCD x 1024 SIMDs)): "
+        "**45.9%%**\n\n    traffic kernel=k_g workload=w bytes_per_launch=1 source=k.hip "
+        "sha256=%s\n" % h)
+    (prof / "k_n_w.md").write_text(
+        "    traffic kernel=k_n workload=w bytes_per_launch=1 source=k.hip sha256=%s\n" % h)
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    assert bench.profiled_mfma_busy("k_g", "w") == 0.459
+    assert bench.profiled_mfma_busy("k_n", "w") is None       # no counter pass in the summary
+    assert bench.profiled_mfma_busy("k_g", "other") is None
+    src.write_text("gemm v2\n")
+    assert bench.profiled_mfma_busy("k_g", "w") is None
+
+
+def test_committed_prefill_summaries_carry_mfma_busy():
+    for k in ("k_dupq", "k_ddown"):
+        u = bench.profiled_mfma_busy(k, "falcon_40b_relu_f16:prefill512")
+        assert u is not None and 0.0 < u < 1.0, (k, u)
+
+
 def test_committed_profiles_name_existing_sources():
     pdir = os.path.join(ROOT, "profiles")
     n = 0
