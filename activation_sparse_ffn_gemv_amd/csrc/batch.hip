@@ -382,13 +382,11 @@ __global__ __launch_bounds__(BT) void k_bug(BatchArgs a) {
     bw[k] = w < W ? a.ubits[w] : 0u;
     local += __popc(bw[k]);
   }
-  int v = local;
-#pragma unroll
-  for (int o = 1; o < WAVE; o <<= 1) {
-    const int u = __shfl_up(v, o, WAVE);
-    if (lane >= o) v += u;
-  }
-  if (lane == WAVE - 1) s_wsum[wave] = v;
+  // local <= 32 * WPT = 128: eight bit planes
+  static_assert(32 * WPT < (1 << 8), "a thread's count fits the prefix's eight bit planes");
+  int wtot;
+  const int before = wave_prefix_small<8>(local, wtot);
+  if (lane == 0) s_wsum[wave] = wtot;
   if (tid < NN) s_nid[tid] = -1;
   __syncthreads();
   int base = 0, total = 0;
@@ -400,7 +398,7 @@ __global__ __launch_bounds__(BT) void k_bug(BatchArgs a) {
   if (blockIdx.x == 0 && tid == 0) *a.ucnt = total;
   const int t0 = blockIdx.x * NN;
   if (t0 >= total) return;                              // uniform over the workgroup
-  const int run0 = base + v - local;
+  const int run0 = base + before;
   if (run0 < t0 + NN && run0 + local > t0) {
     int pos = run0;
 #pragma unroll

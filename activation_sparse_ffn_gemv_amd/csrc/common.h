@@ -242,6 +242,24 @@ __device__ __forceinline__ void load_row(u32x4 (&w)[CPL], float (&sc)[CPL], cons
 }
 
 
+// Exclusive prefix sum over the wave of v, for 0 <= v < 2^BITS, and the wave's total, without
+// lane exchanges: bit j of v is counted by a ballot of that bit and the lanes below this one in it
+// (mbcnt), weighted 2^j.  Every lane of the wave must be active.
+template <int BITS>
+__device__ __forceinline__ int wave_prefix_small(int v, int& total) {
+  int pre = 0, tot = 0;
+#pragma unroll
+  for (int j = 0; j < BITS; ++j) {
+    const unsigned long long m = __ballot((v >> j) & 1);
+    const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                     __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+    pre += (int)below << j;
+    tot += __popcll(m) << j;
+  }
+  total = tot;
+  return pre;
+}
+
 // Ascending list of the set bits of bitmap[0 .. words) (neuron w*32 + b for bit b of word w) and
 // its length, written by one workgroup of NT threads.  idx_out / cnt_out may each be nullptr.
 template <int NT>

@@ -216,6 +216,7 @@ __global__ __launch_bounds__(GA_THREADS) void k_gather(GatherArgs a) {
   constexpr int EPC = Kind<WK>::EPC;
   static_assert(RQ <= GA_LIST && GA_LIST % RQ == 0, "rounds tile the rank batch");
   static_assert(!CACHED || WK == WK_F16, "the neuron cache holds fp16 rows");
+  static_assert(32 * GA_MAXW < (1 << 7), "a thread's count fits the prefix's seven bit planes");
   __shared__ int s_wsum[GA_NW];
   __shared__ int s_list[GA_LIST];
   __shared__ int s_src[CACHED ? GA_LIST : 1];
@@ -270,13 +271,10 @@ __global__ __launch_bounds__(GA_THREADS) void k_gather(GatherArgs a) {
     b[k] = w < words ? a.bitmap[w] : 0u;
     local += __popc(b[k]);
   }
-  int v = local;
-#pragma unroll
-  for (int o = 1; o < WAVE; o <<= 1) {
-    const int u = __shfl_up(v, o, WAVE);
-    if (lane >= o) v += u;
-  }
-  if (lane == WAVE - 1) s_wsum[wave] = v;
+  // local <= 32 * GA_MAXW = 64: seven bit planes
+  int wtot;
+  const int before = wave_prefix_small<7>(local, wtot);
+  if (lane == 0) s_wsum[wave] = wtot;
   __syncthreads();
   int base = 0;
 #pragma unroll
@@ -284,7 +282,7 @@ __global__ __launch_bounds__(GA_THREADS) void k_gather(GatherArgs a) {
     base += k < wave ? s_wsum[k] : 0;
     total += s_wsum[k];
   }
-  run0 = base + v - local;                       // rank of this thread's first active neuron
+  run0 = base + before;                          // rank of this thread's first active neuron
   }
   // 32-bit exact: |A| <= 32768 and at most 256 workgroups
   const int r0 = (int)(((uint32_t)total * blockIdx.x) / gridDim.x);
