@@ -260,6 +260,7 @@ __global__ __launch_bounds__(GA_THREADS) void k_gather(GatherArgs a) {
 
   // 1. word prefix of the bitmap: thread t owns words 2t, 2t+1 (consecutive)
   const int words = a.ffn / 32;
+  const uint32_t nblk = gridDim.x;
   uint32_t b[GA_MAXW];
   int local = 0, total = 0, run0 = 0;
   if constexpr (CACHED) {
@@ -271,6 +272,9 @@ __global__ __launch_bounds__(GA_THREADS) void k_gather(GatherArgs a) {
     b[k] = w < words ? a.bitmap[w] : 0u;
     local += __popc(b[k]);
   }
+  // the grid size (a hidden kernel argument, on its own scalar-cache line) is waited for here,
+  // while the token and bitmap loads are in flight, rather than after the barrier below
+  asm volatile("" ::"s"(nblk));
   // local <= 32 * GA_MAXW = 64: seven bit planes
   int wtot;
   const int before = wave_prefix_small<7>(local, wtot);
@@ -285,8 +289,8 @@ __global__ __launch_bounds__(GA_THREADS) void k_gather(GatherArgs a) {
   run0 = base + before;                          // rank of this thread's first active neuron
   }
   // 32-bit exact: |A| <= 32768 and at most 256 workgroups
-  const int r0 = (int)(((uint32_t)total * blockIdx.x) / gridDim.x);
-  const int r1 = (int)(((uint32_t)total * (blockIdx.x + 1)) / gridDim.x);
+  const int r0 = (int)(((uint32_t)total * blockIdx.x) / nblk);
+  const int r1 = (int)(((uint32_t)total * (blockIdx.x + 1)) / nblk);
   FFN_TS(1, 1);
 
   float acc[CPT][EPC];
@@ -509,7 +513,7 @@ __global__ __launch_bounds__(GA_THREADS) void k_gather(GatherArgs a) {
 #pragma unroll
           for (int e = 0; e < EPC; e += 4) {
             const int col = c * EPC + e;
-            float* dst = a.part + ((size_t)(col / RD_TW) * gridDim.x + blockIdx.x) * RD_TW +
+            float* dst = a.part + ((size_t)(col / RD_TW) * nblk + blockIdx.x) * RD_TW +
                          col % RD_TW;
             // streaming store: the partial is read once, by the next kernel
             __builtin_nontemporal_store(f32x4{acc[k][e], acc[k][e + 1], acc[k][e + 2], acc[k][e + 3]},
