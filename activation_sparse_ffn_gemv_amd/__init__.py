@@ -38,7 +38,8 @@ EXPORTS = [
     "ffn_workspace_size", "ffn_sparse_plan", "ffn_sparse_forward", "ffn_dense_forward",
     "ffn_plan_crossover", "ffn_plan_set_crossover", "ffn_plan_set_decode_variant",
     "ffn_plan_set_hot_head", "ffn_offload_workspace_size", "ffn_offload_plan",
-    "ffn_offload_tables", "ffn_plan_destroy", "ffn_plan_set_timing_events", "ffn_last_error",
+    "ffn_offload_tables", "ffn_plan_destroy", "ffn_plan_set_timing_events", "ffn_status_string",
+    "ffn_last_error",
     "ffn_moe_workspace_size",
     "ffn_moe_plan", "ffn_moe_forward", "ffn_moe_destroy",
 ]
@@ -78,6 +79,8 @@ def lib():
         st = ctypes.c_int
         L.ffn_last_error.restype = ctypes.c_char_p
         L.ffn_last_error.argtypes = []
+        L.ffn_status_string.restype = ctypes.c_char_p
+        L.ffn_status_string.argtypes = [ctypes.c_int]
         L.ffn_workspace_size.restype = st
         L.ffn_workspace_size.argtypes = [ctypes.POINTER(ffn_layer_desc), ctypes.POINTER(S)]
         L.ffn_sparse_plan.restype = st
@@ -123,7 +126,11 @@ def lib():
 
 def _check(status: int):
     if status != FFN_OK:
-        raise FFNError(status, lib().ffn_last_error().decode())
+        raise FFNError(status, "%s: %s" % (ffn_status_string(status), ffn_last_error()))
+
+
+def ffn_status_string(status: int) -> str:
+    return lib().ffn_status_string(status).decode()
 
 
 def ffn_last_error() -> str:

@@ -532,6 +532,18 @@ extern "C" {
 
 const char* ffn_last_error(void) { return g_err; }
 
+const char* ffn_status_string(ffn_status s) {
+  switch (s) {
+    case FFN_OK: return "FFN_OK";
+    case FFN_ERR_INVALID_ARGUMENT: return "FFN_ERR_INVALID_ARGUMENT";
+    case FFN_ERR_UNSUPPORTED: return "FFN_ERR_UNSUPPORTED";
+    case FFN_ERR_WORKSPACE_TOO_SMALL: return "FFN_ERR_WORKSPACE_TOO_SMALL";
+    case FFN_ERR_HIP: return "FFN_ERR_HIP";
+    case FFN_ERR_INTERNAL: return "FFN_ERR_INTERNAL";
+  }
+  return "FFN_STATUS_UNKNOWN";
+}
+
 ffn_status ffn_workspace_size(const ffn_layer_desc* desc, size_t* bytes) {
   ffn_status st = check_desc(desc);
   if (st != FFN_OK) return st;

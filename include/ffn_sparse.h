@@ -246,6 +246,10 @@ typedef enum {
 
 ffn_status ffn_plan_set_timing_events(ffn_plan *plan, int32_t stage, void *start, void *stop);
 
+/* Fixed name of a status code ("FFN_OK", "FFN_ERR_INVALID_ARGUMENT", ...; "FFN_STATUS_UNKNOWN"
+ * for a value outside the enum).  A static string: never NULL, never freed, safe from any thread. */
+const char *ffn_status_string(ffn_status status);
+
 /* Message of the last error on the calling thread ("" if none).  Never NULL. */
 const char *ffn_last_error(void);
 

@@ -34,6 +34,30 @@ def test_library_exports_every_declared_symbol():
         assert name in syms, name
 
 
+def test_status_strings_cover_every_status():
+    names = ["FFN_OK", "FFN_ERR_INVALID_ARGUMENT", "FFN_ERR_UNSUPPORTED",
+             "FFN_ERR_WORKSPACE_TOO_SMALL", "FFN_ERR_HIP", "FFN_ERR_INTERNAL"]
+    # the enum in the header and the binding's constants agree with the names
+    src = open(HEADER).read()
+    for v, n in enumerate(names):
+        assert getattr(ffn, n) == v
+        assert re.search(r"\b%s\s*=\s*%d\b" % (n, v), src), n
+        assert ffn.ffn_status_string(v) == n
+    for v in (-1, 6, 1 << 30):
+        assert ffn.ffn_status_string(v) == "FFN_STATUS_UNKNOWN"
+    # the same static string on every call (no allocation)
+    L = ffn.lib()
+    L.ffn_status_string.restype = ctypes.c_void_p
+    try:
+        assert L.ffn_status_string(3) == L.ffn_status_string(3)
+    finally:
+        L.ffn_status_string.restype = ctypes.c_char_p
+    # an error raised by the binding names its status
+    with pytest.raises(ffn.FFNError) as e:
+        ffn.ffn_workspace_size(_desc(d=0))
+    assert "FFN_ERR_INVALID_ARGUMENT" in str(e.value)
+
+
 def test_header_compiles_as_c():
     r = subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-fsyntax-only", "-x", "c", "-"],
                        input='#include "%s"\nint main(void){return 0;}\n' % HEADER,
