@@ -36,7 +36,8 @@ DTYPE = {"f32": FFN_F32, "f16": FFN_F16, "i4g32": FFN_I4G32}
 # Every symbol the header declares (checked by the tests).
 EXPORTS = [
     "ffn_workspace_size", "ffn_sparse_plan", "ffn_sparse_forward", "ffn_dense_forward",
-    "ffn_plan_crossover", "ffn_plan_set_crossover", "ffn_plan_set_decode_variant",
+    "ffn_plan_crossover", "ffn_plan_set_crossover", "ffn_plan_path_flag",
+    "ffn_plan_set_decode_variant",
     "ffn_plan_set_hot_head", "ffn_offload_workspace_size", "ffn_offload_plan",
     "ffn_offload_tables", "ffn_plan_destroy", "ffn_plan_set_timing_events", "ffn_status_string",
     "ffn_last_error",
@@ -95,6 +96,8 @@ def lib():
         L.ffn_plan_crossover.argtypes = [P, I, ctypes.POINTER(ctypes.c_float)]
         L.ffn_plan_set_crossover.restype = st
         L.ffn_plan_set_crossover.argtypes = [P, I, ctypes.c_float]
+        L.ffn_plan_path_flag.restype = st
+        L.ffn_plan_path_flag.argtypes = [P, ctypes.POINTER(P)]
         L.ffn_plan_set_decode_variant.restype = st
         L.ffn_plan_set_decode_variant.argtypes = [P, I]
         L.ffn_plan_set_hot_head.restype = st
@@ -170,6 +173,13 @@ def ffn_plan_crossover(plan: int, B: int) -> float:
 
 def ffn_plan_set_crossover(plan: int, B: int, density: float):
     _check(lib().ffn_plan_set_crossover(plan, B, density))
+
+
+def ffn_plan_path_flag(plan: int) -> int:
+    """Device address of the int32 recording the path of the last AUTO call of >= 64 tokens."""
+    v = ctypes.c_void_p(0)
+    _check(lib().ffn_plan_path_flag(plan, ctypes.byref(v)))
+    return v.value
 
 
 def ffn_plan_set_decode_variant(plan: int, variant: int):
@@ -305,6 +315,13 @@ class SparseFFN:
 
     def crossover(self, B: int) -> float:
         return ffn_plan_crossover(self.plan, B)
+
+    def last_auto_path(self) -> str:
+        """The path the device chose on the last AUTO call of 64 tokens or more (a copy of the
+        plan's flag: 'dense' or 'sparse')."""
+        base = self.workspace.data_ptr()
+        off = ffn_plan_path_flag(self.plan) - base
+        return "dense" if int(self.workspace[off:off + 4].view(torch.int32)[0]) == 1 else "sparse"
 
     def close(self):
         if self.plan:

@@ -601,9 +601,16 @@ ffn_status ffn_sparse_plan(const ffn_layer_desc* desc, const ffn_layer_weights* 
   p->dense_ypart_rows = L.dense_rows;
   const double tau = desc->threshold;
   p->thr = tau >= 1.0 ? INFINITY : (float)log(tau / (1.0 - tau));
-  // built-in table: the batched kernels read the union of the tokens' rows, which never costs
-  // more than every row, so the union is kept (crossover 1) until calibration says otherwise
-  for (int k = 0; k < 13; ++k) p->crossover_density[k] = 1.0f;
+  // built-in table, by row bytes: below DENSE_MIN_M tokens a pass reads the union of its
+  // tokens' rows once, never more than every row (crossover 1); from DENSE_MIN_M tokens on the
+  // sparse passes (BATCH_TILE tokens each) read the union ceil(B / BATCH_TILE) times against the
+  // dense GEMMs' one read of every row, so dense wins above a union density of
+  // 1 / ceil(B / BATCH_TILE) (B = the bucket's smallest batch)
+  for (int k = 0; k < 13; ++k) {
+    const int B = 1 << k;
+    p->crossover_density[k] =
+        B < DENSE_MIN_M ? 1.0f : 1.0f / (float)((B + BATCH_TILE - 1) / BATCH_TILE);
+  }
   p->dense_min_batch = 2;
   p->decode_variant = 0;
   p->head_words = 0;
@@ -904,6 +911,15 @@ ffn_status ffn_plan_set_crossover(ffn_plan* p, int32_t B, float density) {
   int k = 0;
   while (k < 12 && (1 << (k + 1)) <= B) ++k;
   p->crossover_density[k] = density;
+  return FFN_OK;
+}
+
+ffn_status ffn_plan_path_flag(const ffn_plan* p, const int32_t** flag) {
+  if (!p || !flag) return fail(FFN_ERR_INVALID_ARGUMENT, "plan / flag is NULL");
+  if (!p->off_dense)
+    return fail(FFN_ERR_UNSUPPORTED, "the plan has no dense GEMMs (fp16 rows, max_batch >= %d)",
+                DENSE_MIN_M);
+  *flag = dense_bufs(p->ws, p).flag;
   return FFN_OK;
 }
 

@@ -2,12 +2,15 @@
 """Benchmark of the activation-sparse FFN on one MI355X.
 
 Default: decode of the Llama-2-7B-shaped ReGLU layer stack (d=4096, ffn=11008, predictor rank
-256, fp16 weights, 32 layers, 512 tokens, batch 1).  A step is one decode token through every
+256, fp16 weights, 32 layers, 512 tokens, batch 1), followed by short runs of every other workload
+(each in a child process), summarised under "all_configs" in the one JSON line.  A step is one decode token through every
 layer: per layer the predictor picks the token's active neurons and only their rows are read
 (PowerInfer, unite.ai, "自适应稀疏预测器" / "神经元感知运算符").  Layers run one after another on one
 stream, as in a real decode.  Other workloads: --config (the OPT-125m, Mistral-7B dReLU,
 Mixtral-47B int4 mixture and Falcon-40B shaped ones), --batch N (decode steps of N tokens whose
-active sets are united), --prefill N (N tokens per layer through the dense MFMA path).
+active sets are united), --prefill N (N tokens per layer with the path chosen on the device:
+the predictor's sets, their union density against the plan's crossover, and the dense MFMA GEMMs
+above it).
 
 Inputs are seeded synthetic tensors already resident in HBM; the timed region replays HIP graphs
 of the library's launches.  Printed (one JSON line on stdout): tokens/s, the effective HBM
@@ -109,16 +112,82 @@ def profiled_mfma_busy(kernel: str, workload: str):
     return None
 
 
+HEADLINE = "llama2_7b_reglu_f16"
+
+# The other workloads of the default run: (workload, extra arguments).  Short step counts keep
+# the whole default run within a few minutes; each checks its timed outputs against the oracle
+# on a few (layer, token) pairs.
+OTHERS = [
+    ("opt125m_relu_f32", ["--steps", "256", "--parity-pairs", "0"]),
+    ("turbosparse_mistral_7b_drelu_f16", ["--steps", "64"]),
+    ("turbosparse_mixtral_47b_moe_int4", ["--steps", "64"]),
+    ("falcon_40b_relu_f16", ["--steps", "32"]),
+    ("falcon_40b_relu_f16", ["--batch", "8", "--steps", "8"]),
+    ("falcon_40b_relu_f16", ["--batch", "32", "--steps", "4"]),
+    ("falcon_40b_relu_f16", ["--prefill", "512", "--steps", "2"]),
+]
+
+
+def summarise(r: dict) -> dict:
+    """The fields of one workload's JSON line kept in the default run's summary."""
+    roof, par, c = r.get("roofline") or {}, r.get("parity_sample") or {}, r["config"]
+    out = {"workload": c["workload"], "mode": c["mode"], "tokens_per_call": c["tokens_per_call"],
+           "path": c.get("path"), "layers": c["layers"], "tokens_per_s": r["value"],
+           "ms_per_step": r["ms_per_step"], "effective_gbps": r.get("effective_gbps"),
+           "measured_density": c.get("measured_density"),
+           "dominant_kernel": roof.get("kernel"), "bound": roof.get("bound"),
+           "achieved": roof.get("achieved"), "unit": roof.get("unit"), "frac": roof.get("frac"),
+           "traffic": roof.get("traffic"), "mfma_busy": roof.get("mfma_busy"),
+           "parity": {k: par.get(k) for k in ("pairs", "max_normwise_err", "tolerance",
+                                              "within_tolerance")} if par else None}
+    if r.get("prefill_path"):
+        out["prefill_path"] = r["prefill_path"]
+    return out
+
+
+def run_others() -> list:
+    """Short runs of the other workloads, one child process each (so that each starts with the
+    GPU memory of its own inputs only); a failed run is recorded with its error."""
+    import subprocess
+    out = []
+    for name, extra in OTHERS:
+        cmd = [sys.executable, os.path.abspath(__file__), "--config", name, "--warmup", "2",
+               "--kernel-sample", "8", "--cpu-tokens", "1", "--cpu-budget", "2",
+               "--parity-pairs", "2"] + extra
+        log("other workload: %s %s" % (name, " ".join(extra)))
+        t0 = time.time()
+        try:
+            r = subprocess.run(cmd, capture_output=True, text=True, timeout=400)
+            lines = [ln for ln in r.stdout.splitlines() if ln.startswith("{")]
+            if r.returncode != 0 or not lines:
+                raise RuntimeError("exit %d: %s" % (r.returncode, r.stderr.strip()[-400:]))
+            rec = summarise(json.loads(lines[-1]))
+        except Exception as e:  # recorded, the default line is still printed
+            rec = {"workload": name, "args": extra, "error": str(e)[-500:]}
+        rec["wall_s"] = round(time.time() - t0, 1)
+        log("  -> %s" % json.dumps(rec)[:300])
+        out.append(rec)
+    return out
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None,
                     help="timed steps (default: the workload's token count / batch)")
     ap.add_argument("--warmup", type=int, default=16, help="untimed steps replayed first")
-    ap.add_argument("--config", default="llama2_7b_reglu_f16")
+    ap.add_argument("--config", default=None,
+                    help="one workload (default: the Llama-2-shaped stack, then short runs of "
+                         "the others)")
+    ap.add_argument("--no-others", action="store_true",
+                    help="default workload only: skip the short runs of the other workloads")
     ap.add_argument("--batch", type=int, default=1, help="tokens per decode step (union path)")
     ap.add_argument("--prefill", type=int, default=0,
-                    help="tokens per layer through the dense MFMA path instead of decode")
+                    help="tokens per layer in one call (prefill) instead of decode")
+    ap.add_argument("--prefill-path", choices=("auto", "dense"), default="auto",
+                    help="prefill calls: 'auto' = ffn_sparse_forward with FFN_PATH_AUTO (the "
+                         "predictor's sets, the device's choice by union density, per-token "
+                         "masks); 'dense' = ffn_dense_forward (the dense FFN, no predictor)")
     ap.add_argument("--layers", type=int, default=0, help="override the layer count (0: all)")
     ap.add_argument("--kernel-sample", type=int, default=32,
                     help="steps whose kernel launches are timed with dispatch events")
@@ -170,7 +239,8 @@ def main(argv=None):
     import activation_sparse_ffn_gemv_amd as ffn
     import synth
 
-    cfg = synth.CONFIGS[args.config]
+    others = args.config is None and not args.no_others
+    cfg = synth.CONFIGS[args.config or HEADLINE]
     if args.spectrum_alpha > 0:
         cfg = synth.with_(cfg, spectrum_alpha=args.spectrum_alpha)
     L = args.layers or cfg.layers
@@ -274,9 +344,14 @@ def main(argv=None):
     xp = [[x[l].data_ptr() + t * Bt * xb for t in range(K)] for l in range(L)]
     yp = [[y[l].data_ptr() + t * Bt * cfg.d * 4 for t in range(K)] for l in range(L)]
 
+    auto_prefill = prefill and args.prefill_path == "auto"
+
     def call(l, t, **kw):
-        if prefill:
+        if prefill and not auto_prefill:
             ffn.ffn_dense_forward(mods[l][0].plan, xp[l][t], Bt, yp[l][t], stream=sp)
+        elif prefill:
+            ffn.ffn_sparse_forward(mods[l][0].plan, xp[l][t], Bt, yp[l][t],
+                                   path=ffn.FFN_PATH_AUTO, stream=sp, **kw)
         elif moe:
             ffn.ffn_moe_forward(moes[l], xp[l][t], 1, yp[l][t], stream=sp, **kw)
         else:
@@ -292,9 +367,26 @@ def main(argv=None):
     pz, ps = pz * ranks / cfg.rank, ps * ranks / cfg.rank       # [L][1]: each layer's own rank
     rowb = n_rows(cfg) * row_bytes(cfg) + 4 * n_bias(cfg)
     router_b = cfg.n_experts * cfg.d * 2 if moe else 0
+    path_chosen = None
     if prefill:
-        touched = np.full((L, K), float(cfg.ffn * rowb))      # every row once per call
+        # every row once per call (plus, on the AUTO path, the predictor once per call)
+        touched = np.full((L, K), float(cfg.ffn * rowb)) + ((pz + ps) if auto_prefill else 0.0)
         density = 1.0
+        if auto_prefill:
+            # the device's choice at every layer (each layer's call, then its plan's flag)
+            ch = []
+            with torch.cuda.stream(stream):
+                for l in range(L):
+                    call(l, 0)
+                    stream.synchronize()
+                    ch.append(mods[l][0].last_auto_path())
+            n_dense = ch.count("dense")
+            path_chosen = {"dense_layers": n_dense, "layers": L,
+                           "crossover_density": round(mods[0][0].crossover(Bt), 4),
+                           "path": "dense" if n_dense == L else "sparse" if n_dense == 0
+                           else "mixed"}
+            log("AUTO prefill: the device chose the dense GEMMs at %d of %d layers (crossover "
+                "density %.4f for %d tokens)" % (n_dense, L, path_chosen["crossover_density"], Bt))
     elif moe:
         ids = torch.zeros(L, K, cfg.top_k, dtype=torch.int32, device=dev)
         with torch.cuda.stream(stream):
@@ -496,7 +588,10 @@ def main(argv=None):
             sname, dur.mean() * 1e3, len(dur),
             ("%.1f TFLOP/s" % rec["tflops"]) if "tflops" in rec else
             ("%.1f GB/s algorithmic" % rec["gbps"])))
-    dom = max(stages, key=lambda k: stages[k]["avg_us"])
+    # the dominant kernel: the longest of those that move the method's bytes (or flops); a
+    # reduction of partial sums moves none, so it is never the roofline's kernel
+    movers = [k for k in stages if stages[k].get("bytes_per_launch", 1) > 0]
+    dom = max(movers or list(stages), key=lambda k: stages[k]["avg_us"])
     knames = {"pred_z": "k_pred_z", "pred_s": "k_pred_s", "gather": "k_gather",
               "reduce": "k_reduce", "batch_upgate": "k_bug", "batch_down": "k_bdown",
               # rows in whole 32-wide K stages take the LDS-copy up projection
@@ -548,7 +643,7 @@ def main(argv=None):
                 OL = host(layers[l][0])
             for t in range(nt):
                 c0 = time.perf_counter()
-                if prefill:
+                if prefill and not auto_prefill:
                     oracle.ffn(OL, xh[t], None)
                 elif moe:
                     oracle.moe_token(OLs, Rh, xh[t], cfg.top_k)
@@ -559,7 +654,7 @@ def main(argv=None):
             if t_cpu > args.cpu_budget:
                 break
         rate = nt * L_cpu / t_cpu / L          # tokens through all L layers per second
-        what = ("dense FFN" if prefill else
+        what = ("dense FFN" if prefill and not auto_prefill else
                 "router + the chosen experts' predictor and sparse FFN" if moe else
                 "predictor + sparse FFN")
         cpu_model = ""
@@ -612,7 +707,7 @@ def main(argv=None):
             t_ptr = x[l].data_ptr() + t * xb
             xh_t = x[l, t].cpu().numpy()
             yg = y[l, t].cpu().numpy().astype(np.float64)          # from the timed run
-            if prefill:
+            if prefill and not auto_prefill:
                 yref, _ = oracle.ffn(OLs[0], xh_t, None)
             elif moe:
                 idsc = torch.zeros(1, cfg.top_k, dtype=torch.int32, device=dev)
@@ -635,7 +730,9 @@ def main(argv=None):
                 cn = torch.zeros(Bt, dtype=torch.int32, device=dev)
                 yb = torch.zeros(Bt, cfg.d, dtype=torch.float32, device=dev)
                 ffn.ffn_sparse_forward(mods[l][0].plan, xp[l][st], Bt, yb.data_ptr(),
-                                       idx=idx.data_ptr(), cnt=cn.data_ptr(), stream=sp)
+                                       idx=idx.data_ptr(), cnt=cn.data_ptr(),
+                                       path=ffn.FFN_PATH_AUTO if auto_prefill
+                                       else ffn.FFN_PATH_SPARSE, stream=sp)
                 torch.cuda.synchronize()
                 mk = np.zeros(cfg.ffn, np.uint8)
                 mk[idx[j, :int(cn[j])].cpu().numpy()] = 1
@@ -662,7 +759,9 @@ def main(argv=None):
     dtype = {"f32": "f32", "f16": "f16xf16->f32", "i4g32": "i4g32xf16->f32"}[cfg.w_dtype]
     result = {
         "metric": ("sparse-FFN decode tokens/s at 1 GPU; effective HBM GB/s of touched weights"
-                   if not prefill else "dense-FFN prefill tokens/s at 1 GPU (MFMA fallback)"),
+                   if not prefill else
+                   "prefill tokens/s at 1 GPU (path chosen on the device by union density)"
+                   if auto_prefill else "dense-FFN prefill tokens/s at 1 GPU (MFMA fallback)"),
         "value": round(tok_s, 2),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -675,12 +774,14 @@ def main(argv=None):
         "dtype": dtype,
         "data": "synthetic (seeded; power-law hot set)",
         "config": {"workload": cfg.name, "mode": mode, "tokens_per_call": Bt, "d": cfg.d,
+                   "path": ("auto" if auto_prefill else "dense") if prefill else "sparse",
                    "decode_variant": args.decode_variant, "hot_head": n_hot or None,
                    "spectrum_alpha": cfg.spectrum_alpha or None,
                    "ffn": cfg.ffn, "rank": cfg.rank, "act": cfg.act, "layers": L,
                    "experts": cfg.n_experts, "top_k": cfg.top_k if moe else None,
                    "target_density": cfg.density, "measured_density": round(density, 5)},
         "predictor": quality,
+        "prefill_path": path_chosen,
         "offload": offload,
         "effective_gbps": round(eff_gbps, 1),
         "touched_bytes_per_step": int(touched.sum() / K),
@@ -691,6 +792,11 @@ def main(argv=None):
     }
     if crossover is not None:
         result["crossover_density"] = crossover
+    if others:
+        del layers, mods, graphs, x, y
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        result["all_configs"] = run_others()
     print(json.dumps(result), flush=True)
 
 

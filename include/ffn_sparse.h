@@ -102,7 +102,10 @@ ffn_status ffn_workspace_size(const ffn_layer_desc *desc, size_t *bytes);
  * its sparse path over a density sweep for B = 2, 4, ..., max_batch on `stream` and stores the
  * crossover density per batch bucket used by FFN_PATH_AUTO; it is the only call that
  * synchronises, and it allocates (and frees) its own scratch inputs.  calibrate = 0 keeps the
- * built-in crossover table (1: never dense).
+ * built-in crossover table: 1 (never dense) below 64 tokens, where the batched kernels read the
+ * union of a pass's sets once; from 64 tokens on 1 / ceil(B / 32) for the bucket's smallest B,
+ * the union density at which the sparse passes (one per 32 tokens, each re-reading the union's
+ * rows) read as many row bytes as the dense GEMMs' single read of every row.
  */
 ffn_status ffn_sparse_plan(const ffn_layer_desc *desc, const ffn_layer_weights *weights,
                            void *workspace, size_t workspace_bytes, void *stream,
@@ -142,10 +145,17 @@ ffn_status ffn_dense_forward(ffn_plan *plan, const void *x, int32_t B, float *y,
                              const uint8_t *mask, void *stream);
 
 /* Crossover density for batch B: the union density above which AUTO takes the dense path
- * (batch buckets 1, 2-3, 4-7, ..., 4096).  The built-in value is 1 (never dense); calibration
- * measures it, and a caller may set it. */
+ * (batch buckets 1, 2-3, 4-7, ..., 4096).  The built-in table is described at ffn_sparse_plan;
+ * calibration measures it, and a caller may set it. */
 ffn_status ffn_plan_crossover(const ffn_plan *plan, int32_t B, float *density);
 ffn_status ffn_plan_set_crossover(ffn_plan *plan, int32_t B, float density);
+
+/* Device address (inside the plan's workspace, read-only for the caller) of the int32 in which
+ * the device records the path it chose on the plan's last AUTO call of 64 tokens or more: 1 =
+ * the dense GEMMs ran, 0 = the sparse passes ran.  Calls with another path, or fewer tokens,
+ * leave it as it was; it is unspecified before the first such call.  FFN_ERR_UNSUPPORTED for a
+ * plan without the dense GEMMs (fp16 layers with max_batch >= 64 have them). */
+ffn_status ffn_plan_path_flag(const ffn_plan *plan, const int32_t **flag);
 
 /*
  * Batch-1 decode variant (a tuning knob; results agree within rounding).  0: the predictor's

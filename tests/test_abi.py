@@ -135,6 +135,9 @@ def test_plan_validation_before_any_gpu_call():
             ffn.ffn_dense_forward(plan, 0x1000, 1, 0x2000, mask=0x3001)
         assert e.value.status == ffn.FFN_ERR_INVALID_ARGUMENT
         assert ffn.ffn_plan_crossover(plan, 1) <= 1.0
+        with pytest.raises(ffn.FFNError) as e:              # max_batch 1: no dense GEMMs
+            ffn.ffn_plan_path_flag(plan)
+        assert e.value.status == ffn.FFN_ERR_UNSUPPORTED
         ffn.ffn_plan_set_crossover(plan, 8, 0.25)           # bucket 8..15
         assert ffn.ffn_plan_crossover(plan, 8) == 0.25
         assert ffn.ffn_plan_crossover(plan, 15) == 0.25
@@ -148,6 +151,23 @@ def test_plan_validation_before_any_gpu_call():
             assert e.value.status == ffn.FFN_ERR_INVALID_ARGUMENT
         ffn.ffn_plan_set_hot_head(plan, d.ffn)
         ffn.ffn_plan_set_hot_head(plan, 0)
+    finally:
+        ffn.ffn_plan_destroy(plan)
+
+
+def test_builtin_crossover_table():
+    """Uncalibrated plans: never dense below 64 tokens; from 64 on, dense above the union density
+    at which ceil(B / 32) sparse passes read as many row bytes as one dense read."""
+    plan = _fake_plan(max_batch=4096)
+    try:
+        for B in (1, 2, 5, 32, 63):
+            assert ffn.ffn_plan_crossover(plan, B) == 1.0
+        for B, rho in ((64, 0.5), (100, 0.5), (128, 0.25), (256, 0.125), (512, 1 / 16),
+                       (4096, 1 / 128)):
+            assert abs(ffn.ffn_plan_crossover(plan, B) - rho) < 1e-7, B
+        flag = ffn.ffn_plan_path_flag(plan)                 # inside the workspace
+        assert 0x10000 <= flag < 0x10000 + ffn.ffn_workspace_size(_desc(max_batch=4096))
+        assert flag % 4 == 0
     finally:
         ffn.ffn_plan_destroy(plan)
 

@@ -72,3 +72,9 @@ def test_full_size_parity_in_bench_configuration(bench_main, capsys, argv, min_p
     assert roof["achieved"] > 0 and 0 < roof["frac"] < 1, roof
     cpu = line["cpu_baseline"]
     assert cpu["kind"] == "oracle" and cpu["value"] > 0 and cpu["cores"] == 1
+    if "--prefill" in argv:
+        # the bench's prefill goes through AUTO on an uncalibrated plan: the device took the
+        # dense GEMMs at every layer (the 512-token union is far above the built-in crossover)
+        pp = line["prefill_path"]
+        assert line["config"]["path"] == "auto" and pp["path"] == "dense", pp
+        assert pp["dense_layers"] == line["config"]["layers"], pp
