@@ -35,7 +35,8 @@ DTYPE = {"f32": FFN_F32, "f16": FFN_F16, "i4g32": FFN_I4G32}
 
 # Every symbol the header declares (checked by the tests).
 EXPORTS = [
-    "ffn_workspace_size", "ffn_sparse_plan", "ffn_sparse_forward", "ffn_dense_forward",
+    "ffn_workspace_size", "ffn_sparse_plan", "ffn_sparse_forward", "ffn_sparse_forward_static",
+    "ffn_dense_forward",
     "ffn_plan_crossover", "ffn_plan_set_crossover", "ffn_plan_path_flag",
     "ffn_plan_set_decode_variant",
     "ffn_plan_set_hot_head", "ffn_offload_workspace_size", "ffn_offload_plan",
@@ -90,6 +91,10 @@ def lib():
                                       ctypes.POINTER(P)]
         L.ffn_sparse_forward.restype = st
         L.ffn_sparse_forward.argtypes = [P, P, I, P, P, P, P, P, I, P]
+        L.ffn_sparse_forward_static.restype = st
+        L.ffn_sparse_forward_static.argtypes = [ctypes.POINTER(ffn_layer_desc),
+                                                ctypes.POINTER(ffn_layer_weights), P, I, P, P,
+                                                P, P, P]
         L.ffn_dense_forward.restype = st
         L.ffn_dense_forward.argtypes = [P, P, I, P, P, P]
         L.ffn_plan_crossover.restype = st
@@ -159,6 +164,13 @@ def ffn_sparse_forward(plan: int, x: int, B: int, y: int, mask: int = 0, idx: in
                        stream: int = 0):
     _check(lib().ffn_sparse_forward(plan, x, B, y, mask or None, idx or None, cnt or None,
                                     scores or None, path, stream or None))
+
+
+def ffn_sparse_forward_static(desc, weights, x: int, B: int, y: int, mask: int = 0,
+                              idx: int = 0, cnt: int = 0, stream: int = 0):
+    _check(lib().ffn_sparse_forward_static(ctypes.byref(desc), ctypes.byref(weights), x, B, y,
+                                           mask or None, idx or None, cnt or None,
+                                           stream or None))
 
 
 def ffn_dense_forward(plan: int, x: int, B: int, y: int, mask: int = 0, stream: int = 0):

@@ -9,6 +9,7 @@
 
 #include <algorithm>
 #include <functional>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -526,6 +527,39 @@ ffn_status calibrate_crossover(ffn_plan* p, hipStream_t st) {
 
 namespace {
 
+ffn_status check_weights(const ffn_layer_desc* desc, const ffn_layer_weights* w);
+void init_plan(ffn_plan* p, const ffn_layer_desc* desc, const ffn_layer_weights* w,
+               void* workspace, size_t workspace_bytes);
+
+// Scratch of the plan-less entry point (ffn_sparse_forward_static): one token's decode scratch
+// (z, bitmap, |A|, the gather's partial sums of y) in a file-scope device array instead of a
+// caller workspace.  Every GPU the library runs on holds its own copy until the process ends;
+// its device address is looked up once per device (host code never uses the array's name as an
+// address) and kept here.
+constexpr size_t STATIC_SCRATCH_BYTES = (size_t)(4u << 20) + (64u << 10);
+__device__ __align__(256) char scratch[STATIC_SCRATCH_BYTES];
+constexpr int STATIC_MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+char* g_scratch_ptr[STATIC_MAX_DEVICES];
+
+ffn_status scratch_of_current_device(char** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= STATIC_MAX_DEVICES)
+    return fail(FFN_ERR_UNSUPPORTED, "device %d: the static scratch covers devices 0..%d", dev,
+                STATIC_MAX_DEVICES - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    g_scratch_ptr[dev] = static_cast<char*>(ptr);
+  }
+  *out = g_scratch_ptr[dev];
+  return FFN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -562,6 +596,35 @@ ffn_status ffn_sparse_plan(const ffn_layer_desc* desc, const ffn_layer_weights* 
   if (st != FFN_OK) return st;
   if (!w || !out) return fail(FFN_ERR_INVALID_ARGUMENT, "weights / out is NULL");
   *out = nullptr;
+  if ((st = check_weights(desc, w)) != FFN_OK) return st;
+  if (!aligned16(workspace)) return fail(FFN_ERR_INVALID_ARGUMENT, "pointer not 16-byte aligned");
+  size_t need = 0;
+  if ((st = ffn_workspace_size(desc, &need)) != FFN_OK) return st;
+  if (!workspace) return fail(FFN_ERR_INVALID_ARGUMENT, "workspace is NULL");
+  if (workspace_bytes < need)
+    return fail(FFN_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", workspace_bytes, need);
+
+  ffn_plan* p = new (std::nothrow) ffn_plan();
+  if (!p) return fail(FFN_ERR_INTERNAL, "out of host memory");
+  init_plan(p, desc, w, workspace, workspace_bytes);
+  if (calibrate && batched(desc) && desc->max_batch >= 2) {
+    st = calibrate_crossover(p, static_cast<hipStream_t>(stream));
+    if (st != FFN_OK) {
+      delete p;
+      return st;
+    }
+  }
+  *out = p;
+  g_err[0] = 0;
+  return FFN_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+// Every weight pointer the descriptor needs is present and every pointer 16-byte aligned.
+ffn_status check_weights(const ffn_layer_desc* desc, const ffn_layer_weights* w) {
   const bool i4 = desc->w_dtype == FFN_I4G32;
   const bool gate = desc->act != FFN_ACT_RELU;
   if (!w->w_up || !w->w_down_t || (gate && !w->w_gate))
@@ -573,17 +636,16 @@ ffn_status ffn_sparse_plan(const ffn_layer_desc* desc, const ffn_layer_weights* 
   const void* ptrs[] = {w->w_up, gate ? w->w_gate : nullptr, w->w_down_t,
                         i4 ? w->s_up : nullptr, (i4 && gate) ? w->s_gate : nullptr,
                         i4 ? w->s_down_t : nullptr, w->b_up, gate ? w->b_gate : nullptr,
-                        w->b_down, w->p1, w->p2, w->c1, w->c2, workspace};
+                        w->b_down, w->p1, w->p2, w->c1, w->c2};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return fail(FFN_ERR_INVALID_ARGUMENT, "pointer not 16-byte aligned");
-  size_t need = 0;
-  if ((st = ffn_workspace_size(desc, &need)) != FFN_OK) return st;
-  if (!workspace) return fail(FFN_ERR_INVALID_ARGUMENT, "workspace is NULL");
-  if (workspace_bytes < need)
-    return fail(FFN_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", workspace_bytes, need);
+  return FFN_OK;
+}
 
-  ffn_plan* p = new (std::nothrow) ffn_plan();
-  if (!p) return fail(FFN_ERR_INTERNAL, "out of host memory");
+// A plan's fields for a checked descriptor and weights over `workspace` (no allocation).
+void init_plan(ffn_plan* p, const ffn_layer_desc* desc, const ffn_layer_weights* w,
+               void* workspace, size_t workspace_bytes) {
+  const bool gate = desc->act != FFN_ACT_RELU;
   p->desc = *desc;
   p->w = *w;
   if (!gate) { p->w.w_gate = nullptr; p->w.s_gate = nullptr; p->w.b_gate = nullptr; }
@@ -616,17 +678,11 @@ ffn_status ffn_sparse_plan(const ffn_layer_desc* desc, const ffn_layer_weights* 
   p->head_words = 0;
   p->cache_cap = 0;
   p->off_cache = 0;
-  if (calibrate && batched(desc) && desc->max_batch >= 2) {
-    st = calibrate_crossover(p, static_cast<hipStream_t>(stream));
-    if (st != FFN_OK) {
-      delete p;
-      return st;
-    }
-  }
-  *out = p;
-  g_err[0] = 0;
-  return FFN_OK;
 }
+
+}  // namespace
+
+extern "C" {
 
 ffn_status ffn_offload_workspace_size(const ffn_layer_desc* desc, int32_t capacity,
                                       size_t* bytes) {
@@ -851,6 +907,47 @@ ffn_status ffn_sparse_forward(ffn_plan* p, const void* x, int32_t B, float* y,
                                  idx ? idx + (size_t)b * D.ffn : nullptr, cnt ? cnt + b : nullptr,
                                  scores ? scores + (size_t)b * D.ffn : nullptr, nullptr, 1, 0, st);
     if (s != FFN_OK) return s;
+  }
+  g_err[0] = 0;
+  return FFN_OK;
+}
+
+ffn_status ffn_sparse_forward_static(const ffn_layer_desc* desc, const ffn_layer_weights* w,
+                                     const void* x, int32_t B, float* y, const uint8_t* mask,
+                                     int32_t* idx, int32_t* cnt, void* stream) {
+  ffn_status st = check_desc(desc);
+  if (st != FFN_OK) return st;
+  if (!w) return fail(FFN_ERR_INVALID_ARGUMENT, "weights is NULL");
+  if ((st = check_weights(desc, w)) != FFN_OK) return st;
+  if (!x || !y) return fail(FFN_ERR_INVALID_ARGUMENT, "x / y is NULL");
+  if (B < 1 || B > desc->max_batch)
+    return fail(FFN_ERR_INVALID_ARGUMENT, "B = %d outside [1, %d]", B, desc->max_batch);
+  if (!mask && desc->rank == 0)
+    return fail(FFN_ERR_INVALID_ARGUMENT, "no predictor (rank 0) and no mask");
+  if (!aligned16(x) || !aligned16(y) || !aligned16(mask))
+    return fail(FFN_ERR_INVALID_ARGUMENT, "x / y / mask not 16-byte aligned");
+  // one token's scratch: z | bitmap | |A| | partials of the balanced gather's workgroups
+  const Layout L = layout_for(desc);
+  const size_t need =
+      L.off_part + (size_t)gather_blocks() * reduce_tiles(desc->d) * 16 * 4;
+  if (need > STATIC_SCRATCH_BYTES)
+    return fail(FFN_ERR_WORKSPACE_TOO_SMALL,
+                "d = %d, ffn = %d, rank = %d needs %zu bytes of scratch; the static scratch "
+                "holds %zu (d <= 4096)", desc->d, desc->ffn, desc->rank, need,
+                STATIC_SCRATCH_BYTES);
+  char* ws = nullptr;
+  if ((st = scratch_of_current_device(&ws)) != FFN_OK) return st;
+  ffn_plan p{};                                   // on the stack: nothing is allocated
+  init_plan(&p, desc, w, ws, STATIC_SCRATCH_BYTES);
+  hipStream_t sm = static_cast<hipStream_t>(stream);
+  const size_t xbytes = (size_t)desc->d * (desc->x_dtype == FFN_F32 ? 4 : 2);
+  const TokenBufs wb = token_bufs(ws, &p);
+  for (int b = 0; b < B; ++b) {
+    st = enqueue_token(&p, wb, static_cast<const char*>(x) + b * xbytes,
+                       mask ? mask + (size_t)b * desc->ffn : nullptr, y + (size_t)b * desc->d,
+                       idx ? idx + (size_t)b * desc->ffn : nullptr, cnt ? cnt + b : nullptr,
+                       nullptr, nullptr, 1, 0, sm);
+    if (st != FFN_OK) return st;
   }
   g_err[0] = 0;
   return FFN_OK;

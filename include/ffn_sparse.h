@@ -137,6 +137,27 @@ ffn_status ffn_sparse_forward(ffn_plan *plan, const void *x, int32_t B, float *y
                               int32_t path, void *stream);
 
 /*
+ * The batch-1 decode path of ffn_sparse_forward without a plan and without a workspace, for
+ * callers that cannot allocate: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  It calls no hipMalloc / hipFree and no allocating routine, and creates
+ * no plan: the descriptor and weights are checked on every call (as ffn_sparse_plan checks
+ * them, max_batch bounding B), and the per-token scratch (predictor stage 1, the active
+ * bitmap, |A| and the gather's partial sums of y) lives in a fixed device array inside the
+ * library, 4 MiB + 64 KiB per GPU, held from the first call on that GPU until the process ends.
+ * That covers every layer with d <= 4096 (the scratch grows with d); larger layers give
+ * FFN_ERR_WORKSPACE_TOO_SMALL before anything is enqueued.
+ *   x, y, mask, idx, cnt: as ffn_sparse_forward (device pointers; y fully overwritten).  The B
+ *   tokens run one after another through the batch-1 kernels (decode variant 0, no hot head),
+ *   so each token's y and set equal those of ffn_sparse_forward on that token alone.
+ * Every call on one GPU shares that GPU's scratch: calls on different streams that overlap in
+ * time race and give unspecified results; calls ordered on one stream (or synchronised) are
+ * safe.  The scratch's earlier contents never matter: every word a call reads, it wrote first.
+ */
+ffn_status ffn_sparse_forward_static(const ffn_layer_desc *desc, const ffn_layer_weights *weights,
+                                     const void *x, int32_t B, float *y, const uint8_t *mask,
+                                     int32_t *idx, int32_t *cnt, void *stream);
+
+/*
  * Dense FFN (every neuron), y[B][d] fp32, through the MFMA GEMM kernels (the prefill path).
  * mask [B][ffn] uint8 or NULL: non-NULL zeroes h for inactive (token, neuron) pairs in the
  * epilogue, which equals the sparse result.

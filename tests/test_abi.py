@@ -172,6 +172,35 @@ def test_builtin_crossover_table():
         ffn.ffn_plan_destroy(plan)
 
 
+def test_static_entry_point_validation_before_any_gpu_call():
+    """The allocation-free entry point checks its descriptor, weights and sizes on every call
+    and returns before anything touches the GPU."""
+    w = ffn.ffn_layer_weights(w_up=0x1000, w_gate=0x2000, w_down_t=0x3000, p1=0x4000,
+                              p2=0x5000)
+    with pytest.raises(ffn.FFNError) as e:                     # bad descriptor
+        ffn.ffn_sparse_forward_static(_desc(d=0), w, 0x6000, 1, 0x7000)
+    assert e.value.status == ffn.FFN_ERR_INVALID_ARGUMENT
+    with pytest.raises(ffn.FFNError) as e:                     # missing gate rows
+        ffn.ffn_sparse_forward_static(_desc(), ffn.ffn_layer_weights(w_up=0x1000, w_down_t=0x3000,
+                                                                     p1=0x4000, p2=0x5000),
+                                      0x6000, 1, 0x7000)
+    assert e.value.status == ffn.FFN_ERR_INVALID_ARGUMENT
+    with pytest.raises(ffn.FFNError) as e:                     # B beyond max_batch
+        ffn.ffn_sparse_forward_static(_desc(max_batch=2), w, 0x6000, 3, 0x7000)
+    assert e.value.status == ffn.FFN_ERR_INVALID_ARGUMENT
+    with pytest.raises(ffn.FFNError) as e:                     # misaligned y
+        ffn.ffn_sparse_forward_static(_desc(), w, 0x6000, 1, 0x7004)
+    assert e.value.status == ffn.FFN_ERR_INVALID_ARGUMENT
+    with pytest.raises(ffn.FFNError) as e:                     # no predictor and no mask
+        ffn.ffn_sparse_forward_static(_desc(rank=0), w, 0x6000, 1, 0x7000)
+    assert e.value.status == ffn.FFN_ERR_INVALID_ARGUMENT
+    with pytest.raises(ffn.FFNError) as e:                     # beyond the static scratch
+        ffn.ffn_sparse_forward_static(_desc(d=8192, ffn=32768, rank=1024, act=ffn.FFN_ACT_RELU),
+                                      w, 0x6000, 1, 0x7000)
+    assert e.value.status == ffn.FFN_ERR_WORKSPACE_TOO_SMALL
+    assert "static scratch" in ffn.ffn_last_error()
+
+
 def test_no_predictor_requires_mask():
     d = _desc(rank=0)
     w = ffn.ffn_layer_weights(w_up=0x1000, w_gate=0x2000, w_down_t=0x3000)
