@@ -66,6 +66,37 @@ size_t dense_rows_for(const ffn_layer_desc* d) {
 // The batched kernels (MFMA) cover fp16 layers; other storage types run B > 1 token by token.
 bool batched(const ffn_layer_desc* d) { return d->w_dtype == FFN_F16; }
 
+// The dense region, from byte `base` of the workspace: per-token bitmaps [max_batch][ffn/32] |
+// the path flag | H [passes * 32][ffn] fp16 (the dense GEMMs' H, and the batched kernels' H of
+// a call whose passes share one launch: only one of the two runs per call) | the dense GEMMs'
+// partials [rows][d] | for `passes` = ceil(max_batch / 32) passes: predictor stage-1 partials,
+// z (hi, lo), union words, |U|, union ranks and the down projection's segment partials.
+struct DenseRegion {
+  size_t bits, flag, H, ypart, zpart, zhl, ubits, ucnt, uidx, mpart, end;
+  int passes, S;
+};
+
+DenseRegion dense_region(const ffn_layer_desc* d, size_t base) {
+  DenseRegion R{};
+  const BatchShape s = batch_shape(d->d, d->ffn, d->rank);
+  R.passes = (d->max_batch + BATCH_TILE - 1) / BATCH_TILE;
+  R.S = batch_segments_mp(d->d, R.passes);
+  const size_t P = (size_t)R.passes, W = (size_t)d->ffn / 32;
+  size_t off = base;
+  R.bits = off;   off = round_up(off + (size_t)d->max_batch * W * 4, 256);
+  R.flag = off;   off = round_up(off + 4, 256);
+  R.H = off;      off = round_up(off + P * BATCH_TILE * d->ffn * 2, 256);
+  R.ypart = off;  off = round_up(off + dense_rows_for(d) * d->d * 4, 256);
+  R.zpart = off;  off = round_up(off + P * s.zpart_bytes, 256);
+  R.zhl = off;    off = round_up(off + P * s.zhl_bytes, 256);
+  R.ubits = off;  off = round_up(off + P * W * 4, 256);
+  R.ucnt = off;   off = round_up(off + P * 4, 256);
+  R.uidx = off;   off = round_up(off + P * d->ffn * 4, 256);
+  R.mpart = off;  off = round_up(off + P * R.S * BATCH_TILE * d->d * 4, 256);
+  R.end = off;
+  return R;
+}
+
 ffn_status check_desc(const ffn_layer_desc* d) {
   if (!d) return fail(FFN_ERR_INVALID_ARGUMENT, "desc is NULL");
   if (d->d <= 0 || d->ffn <= 0 || d->rank < 0 || d->max_batch <= 0)
@@ -131,10 +162,7 @@ Layout layout_for(const ffn_layer_desc* d) {
   if (batched(d) && d->max_batch >= DENSE_MIN_M) {
     L.off_dense = off;
     L.dense_rows = dense_rows_for(d);
-    off = round_up(off + (size_t)d->max_batch * (d->ffn / 32) * 4, 256);
-    off = round_up(off + 4, 256);
-    off = round_up(off + (size_t)d->max_batch * d->ffn * 2, 256);
-    off = round_up(off + L.dense_rows * d->d * 4, 256);
+    off = dense_region(d, off).end;
   }
   L.total = off;
   return L;
@@ -145,19 +173,31 @@ struct DenseBufs {
   int* flag;
   _Float16* H;
   float* ypart;
+  // the batched kernels' buffers for all passes of one call (grid.z = pass)
+  float* zpart;
+  _Float16* zhl;
+  uint32_t* ubits;
+  int* ucnt;
+  int* uidx;
+  float* mpart;
+  int passes, S;
 };
 
 DenseBufs dense_bufs(char* ws, const ffn_plan* p) {
-  const ffn_layer_desc& D = p->desc;
-  size_t off = p->off_dense;
+  const DenseRegion R = dense_region(&p->desc, p->off_dense);
   DenseBufs b{};
-  b.bits = reinterpret_cast<uint32_t*>(ws + off);
-  off = round_up(off + (size_t)D.max_batch * (D.ffn / 32) * 4, 256);
-  b.flag = reinterpret_cast<int*>(ws + off);
-  off = round_up(off + 4, 256);
-  b.H = reinterpret_cast<_Float16*>(ws + off);
-  off = round_up(off + (size_t)D.max_batch * D.ffn * 2, 256);
-  b.ypart = reinterpret_cast<float*>(ws + off);
+  b.bits = reinterpret_cast<uint32_t*>(ws + R.bits);
+  b.flag = reinterpret_cast<int*>(ws + R.flag);
+  b.H = reinterpret_cast<_Float16*>(ws + R.H);
+  b.ypart = reinterpret_cast<float*>(ws + R.ypart);
+  b.zpart = reinterpret_cast<float*>(ws + R.zpart);
+  b.zhl = reinterpret_cast<_Float16*>(ws + R.zhl);
+  b.ubits = reinterpret_cast<uint32_t*>(ws + R.ubits);
+  b.ucnt = reinterpret_cast<int*>(ws + R.ucnt);
+  b.uidx = reinterpret_cast<int*>(ws + R.uidx);
+  b.mpart = reinterpret_cast<float*>(ws + R.mpart);
+  b.passes = R.passes;
+  b.S = R.S;
   return b;
 }
 
@@ -789,28 +829,44 @@ ffn_status run_large(ffn_plan* p, const void* x, int32_t B, float* y, const uint
                      bool dense_only) {
   const ffn_layer_desc& D = p->desc;
   const int W = D.ffn / 32;
-  const size_t xbytes = (size_t)D.d * 2;
   const DenseBufs db = dense_bufs(p->ws, p);
   const bool sets = !dense_only || mask;         // dense FFN without a mask needs no sets
   hipError_t e;
-  if (sets) {
-    for (int b0 = 0; b0 < B; b0 += BATCH_TILE) {
-      BatchArgs a = batch_bufs(p->ws, p);
-      a.B = std::min(BATCH_TILE, B - b0);
-      a.x = static_cast<const char*>(x) + b0 * xbytes;
-      a.mask = mask ? mask + (size_t)b0 * D.ffn : nullptr;
-      a.bits = db.bits + (size_t)b0 * W;
-      a.scores = scores ? scores + (size_t)b0 * D.ffn : nullptr;
-      if ((e = launch_batch_sets(a, mask == nullptr, st)) != hipSuccess)
-        return hip_fail(e, "active-set launch");
-    }
-  }
+  // every pass of BATCH_TILE tokens in one launch per kernel (grid.z = pass), each pass with its
+  // own buffers in the dense region
+  const int P = (B + BATCH_TILE - 1) / BATCH_TILE;
+  const BatchShape bs = batch_shape(D.d, D.ffn, D.rank);
+  BatchArgs a = batch_bufs(p->ws, p);            // shapes, weights, threshold
+  a.Btot = B;
+  a.B = std::min(BATCH_TILE, B);
+  a.x = x;
+  a.mask = mask;
+  a.bits = db.bits;
+  a.scores = scores;
+  a.y = y;
+  a.idx_out = idx;
+  a.cnt_out = cnt;
+  a.zpart = db.zpart;
+  a.zhl = db.zhl;
+  a.ubits = db.ubits;
+  a.ucnt = db.ucnt;
+  a.uidx = db.uidx;
+  a.H = db.H;
+  a.ypart = db.mpart;
+  a.S = db.S;
+  a.zpart_ps = bs.zpart_bytes / 4;
+  a.zhl_ps = bs.zhl_bytes / 2;
+  a.ubits_ps = (size_t)W;
+  a.uidx_ps = (size_t)D.ffn;
+  a.ypart_ps = (size_t)db.S * BATCH_TILE * D.d;
+  if (sets && (e = launch_batch_sets(a, mask == nullptr, st, P)) != hipSuccess)
+    return hip_fail(e, "active-set launch");
   const int* flag = nullptr;
   if (path == FFN_PATH_AUTO) {
     float rho = 1.0f;
     ffn_plan_crossover(p, B, &rho);
     const int dense_above = rho >= 1.0f ? D.ffn : (int)(rho * D.ffn);
-    if ((e = launch_dense_choice(db.bits, B, D.ffn, dense_above, db.flag, st)) != hipSuccess)
+    if ((e = launch_dense_choice(db.ubits, P, D.ffn, dense_above, db.flag, st)) != hipSuccess)
       return hip_fail(e, "path choice launch");
     flag = db.flag;
   }
@@ -825,20 +881,10 @@ ffn_status run_large(ffn_plan* p, const void* x, int32_t B, float* y, const uint
       return hip_fail(e, "dense launch");
   }
   if (path != FFN_PATH_DENSE) {
-    for (int b0 = 0; b0 < B; b0 += BATCH_TILE) {
-      BatchArgs a = batch_bufs(p->ws, p);
-      a.B = std::min(BATCH_TILE, B - b0);
-      a.x = static_cast<const char*>(x) + b0 * xbytes;
-      a.bits = db.bits + (size_t)b0 * W;
-      a.y = y + (size_t)b0 * D.d;
-      a.idx_out = idx ? idx + (size_t)b0 * D.ffn : nullptr;
-      a.cnt_out = cnt ? cnt + b0 : nullptr;
-      a.run_if = flag;
-      a.run_want = 0;
-      if ((e = launch_batch_union(a, st)) != hipSuccess ||
-          (e = launch_batch_rows(a, 0, st, p->ev + FFN_STAGE_BATCH_UPGATE)) != hipSuccess)
-        return hip_fail(e, "batched launch");
-    }
+    a.run_if = flag;
+    a.run_want = 0;
+    if ((e = launch_batch_rows(a, 0, st, p->ev + FFN_STAGE_BATCH_UPGATE, P)) != hipSuccess)
+      return hip_fail(e, "batched launch");
   }
   g_err[0] = 0;
   return FFN_OK;
@@ -871,7 +917,7 @@ ffn_status ffn_sparse_forward(ffn_plan* p, const void* x, int32_t B, float* y,
   //  - otherwise SPARSE runs the batch-1 kernels for one token and the batched kernels for
   //    more; DENSE and AUTO run the batched kernels, widening the pass's union to every neuron
   //    (DENSE: always; AUTO: when it exceeds the crossover density).
-  if (batched(&D) && p->off_dense && B >= DENSE_MIN_M && path != FFN_PATH_SPARSE)
+  if (batched(&D) && p->off_dense && B >= DENSE_MIN_M)
     return run_large(p, x, B, y, mask, idx, cnt, scores, path, st, false);
   if (batched(&D) && (B > 1 || path == FFN_PATH_DENSE)) {
     int choose = 0, dense_above = 0;

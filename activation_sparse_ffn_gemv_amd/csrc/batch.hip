@@ -70,6 +70,46 @@ __device__ __forceinline__ f32x16 wg_sum4(f32x16 acc, float* red /* [3][16][64] 
   return acc;
 }
 
+// Pass p of a multi-pass launch (by default blockIdx.z): the pass's tokens, buffers and count.
+__device__ __forceinline__ void at_pass(BatchArgs& a, int p = blockIdx.z) {
+  if (a.Btot > 0) a.B = min(MB, a.Btot - p * MB);      // (Btot 0: a one-pass launch)
+  if (p == 0) return;
+  const size_t tok = (size_t)p * MB;
+  a.x = static_cast<const char*>(a.x) + tok * a.d * 2;
+  if (a.mask) a.mask += tok * a.ffn;
+  a.bits += tok * (a.ffn / 32);
+  if (a.scores) a.scores += tok * a.ffn;
+  a.y += tok * a.d;
+  if (a.idx_out) a.idx_out += tok * a.ffn;
+  if (a.cnt_out) a.cnt_out += tok;
+  a.zpart += (size_t)p * a.zpart_ps;
+  a.zhl += (size_t)p * a.zhl_ps;
+  a.ubits += (size_t)p * a.ubits_ps;
+  a.ucnt += p;
+  a.uidx += (size_t)p * a.uidx_ps;
+  a.H += tok * a.ffn;
+  a.ypart += (size_t)p * a.ypart_ps;
+}
+
+// Workgroup id -> (weight block, pass) for a multi-pass launch over nb weight blocks.  Workgroup
+// id runs on XCD id % 8 (consecutive workgroups go to the eight XCDs in turn); the passes of one
+// block go to consecutive workgroups of one XCD, so that they run side by side and read the
+// block's weights from that XCD's L2 instead of once per pass from HBM.  nb not a multiple of
+// 8: plain block-major order.
+__device__ __forceinline__ void xcd_block_pass(int id, int nb, int passes, int& bx, int& p) {
+  if (passes == 1) {
+    bx = id;
+    p = 0;
+  } else if (nb % 8) {
+    bx = id % nb;
+    p = id / nb;
+  } else {
+    const int k = id / 8;
+    p = k % passes;
+    bx = (k / passes) * 8 + id % 8;
+  }
+}
+
 // Union ranks [r0, r1) of segment s: segments are cut at multiples of 8 ranks (one x8 step).
 // 32-bit exact: total <= 32768 (so units <= 4096) and s + 1 <= S <= 64.
 __device__ __forceinline__ void seg_range(int total, int s, int S, int& r0, int& r1) {
@@ -81,12 +121,18 @@ __device__ __forceinline__ void seg_range(int total, int s, int S, int& r0, int&
 // ---------------------------------------------------------------------------------------------
 // Predictor stage 1: workgroup (tile of 32 P1 rows, K slice); wave w of slice k takes 16-k
 // steps [(4k + w) * spw, ... + spw).
+// Grid: one dimension of (P1 tile, K slice) blocks times passes (xcd_block_pass).
 __global__ __launch_bounds__(BT) void k_bz(BatchArgs a) {
+  const int tiles = (a.r + 31) / 32;
+  int bx, pass;
+  xcd_block_pass(blockIdx.x, tiles * a.ks, gridDim.x / (tiles * a.ks), bx, pass);
+  at_pass(a, pass);
+  const int tile = bx % tiles, slice = bx / tiles;
   __shared__ float red[3 * 16 * WAVE];
   const int lane = threadIdx.x & (WAVE - 1), wave = threadIdx.x / WAVE;
-  const int n0 = blockIdx.x * 32, row = lane & 31, g = lane >> 5;
+  const int n0 = tile * 32, row = lane & 31, g = lane >> 5;
   const int nchk = a.d / 8, nsteps = (nchk + 1) / 2;
-  const int s0 = (blockIdx.y * 4 + wave) * a.spw, s1 = min(nsteps, s0 + a.spw);
+  const int s0 = (slice * 4 + wave) * a.spw, s1 = min(nsteps, s0 + a.spw);
   const bool pok = n0 + row < a.r, xok = row < a.B;
   const char* pr = static_cast<const char*>(a.p1) + (size_t)min(n0 + row, a.r - 1) * a.d * 2;
   const char* xr = static_cast<const char*>(a.x) + (size_t)min(row, a.B - 1) * a.d * 2;
@@ -114,12 +160,13 @@ __global__ __launch_bounds__(BT) void k_bz(BatchArgs a) {
   if (wave == 0 && n0 + row < a.r) {
 #pragma unroll
     for (int i = 0; i < 16; ++i)
-      a.zpart[((size_t)blockIdx.y * MB + acc_row(i, lane)) * a.r + n0 + row] = acc[i];
+      a.zpart[((size_t)slice * MB + acc_row(i, lane)) * a.r + n0 + row] = acc[i];
   }
 }
 
 // z = sum over the K slices (in order) + c1, stored as fp16 hi and lo planes.
 __global__ __launch_bounds__(256) void k_bzr(BatchArgs a) {
+  at_pass(a);
   const int e = blockIdx.x * 256 + threadIdx.x;       // m * r + k
   if (e >= MB * a.r) return;
   const int k = e % a.r;
@@ -156,20 +203,25 @@ constexpr int BS_LD = BS_PC + 1;           // padded LDS row
 constexpr int BS_ZL = 2 * MB * BS_PC / BS_T;   // Z pieces per thread and chunk (2)
 constexpr int BS_PL = BS_N * BS_PC / BS_T;     // P2 pieces per thread and chunk (4)
 
+// Grid: one dimension of 128-neuron blocks times passes (xcd_block_pass).
 __global__ __launch_bounds__(BS_T) void k_bs(BatchArgs a) {
+  const int W = a.ffn / 32;
+  const int nblk = (W + 3) / 4;
+  int bx, pass;
+  xcd_block_pass(blockIdx.x, nblk, gridDim.x / nblk, bx, pass);
+  at_pass(a, pass);
   __shared__ u32x4 s_z[2][2][MB * BS_LD];  // [buffer][hi, lo][token row][piece]
   __shared__ u32x4 s_p[2][BS_N * BS_LD];   // [buffer][neuron][piece]
   const int tid = threadIdx.x, lane = tid & (WAVE - 1), wave = tid / WAVE;
-  const int W = a.ffn / 32;
   const int tw = wave & 3, kh = wave >> 2; // word of the workgroup, half of each chunk
-  const int word = blockIdx.x * 4 + tw;
+  const int word = bx * 4 + tw;
   const bool head = word < a.head_words;   // hot head: every token's word set, no score
   const bool live = word < W && !head;     // uniform per wave
   if (kh == 0 && word < W && head) {
     if (lane < min(a.B, MB)) a.bits[(size_t)lane * W + word] = ~0u;
     if (lane == 0) a.ubits[word] = ~0u;
   }
-  const int nb = blockIdx.x * BS_N;        // first neuron of the workgroup
+  const int nb = bx * BS_N;                // first neuron of the workgroup
   const int row = lane & 31, g = lane >> 5;
   const int rch = a.r / 8;
   const int nchunk = (rch + BS_PC - 1) / BS_PC;
@@ -280,6 +332,7 @@ __global__ __launch_bounds__(BS_T) void k_bs(BatchArgs a) {
 
 // Caller masks -> per-token bitmap words and the union words (one thread per word).
 __global__ __launch_bounds__(256) void k_bmask(BatchArgs a) {
+  at_pass(a);
   const int w = blockIdx.x * 256 + threadIdx.x;
   const int W = a.ffn / 32;
   if (w >= W) return;
@@ -311,6 +364,7 @@ __global__ __launch_bounds__(256) void k_bmask(BatchArgs a) {
 // reads every neuron's rows; each token's h is still zeroed outside its own set, so the result
 // is the same either way.
 __global__ __launch_bounds__(1024) void k_bpath(BatchArgs a) {
+  at_pass(a);
   __shared__ int s_total;
   if (a.run_if && *a.run_if != a.run_want) return;
   const int W = a.ffn / 32;
@@ -324,6 +378,7 @@ __global__ __launch_bounds__(1024) void k_bpath(BatchArgs a) {
 
 // Union words of the pass's tokens from their bitmap words (bits written by an earlier step).
 __global__ __launch_bounds__(256) void k_bunion(BatchArgs a) {
+  at_pass(a);
   if (a.run_if && *a.run_if != a.run_want) return;
   const int w = blockIdx.x * 256 + threadIdx.x, W = a.ffn / 32;
   if (w >= W) return;
@@ -332,16 +387,23 @@ __global__ __launch_bounds__(256) void k_bunion(BatchArgs a) {
   a.ubits[w] = uw;
 }
 
-// Dense-or-sparse for a whole call: union of B tokens' sets against dense_above.
-__global__ __launch_bounds__(1024) void k_dchoice(const uint32_t* __restrict__ bits, int B,
-                                                  int W, int dense_above, int* __restrict__ flag) {
+// Dense-or-sparse for a whole call: the union of its passes' union words against dense_above.
+__global__ __launch_bounds__(1024) void k_dchoice(const uint32_t* __restrict__ ubits,
+                                                  int passes, int W, int dense_above,
+                                                  int* __restrict__ flag) {
   __shared__ int s_total;
   const int w = threadIdx.x;                            // W <= 1024
   if (w == 0) s_total = 0;
   __syncthreads();
   if (w < W) {
     uint32_t uw = 0u;
-    for (int m = 0; m < B; ++m) uw |= bits[(size_t)m * W + w];
+    for (int p0 = 0; p0 < passes; p0 += 8) {            // eight loads in flight at a time
+      uint32_t v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = ubits[(size_t)min(p0 + u, passes - 1) * W + w];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) uw |= v[u];           // a repeated last word changes nothing
+    }
     atomicAdd(&s_total, __popc(uw));                    // LDS atomic
   }
   __syncthreads();
@@ -359,6 +421,7 @@ constexpr int UG_WIDE_B = 16;             // ReLU batches above this take 64 neu
 // NN = 32 or 64 neurons per workgroup (64: each token slice read from L2 serves twice the rows).
 template <bool GATE, int NN>
 __global__ __launch_bounds__(BT) void k_bug(BatchArgs a) {
+  at_pass(a);
   constexpr int NMAT = GATE ? 2 : 1;
   constexpr int NTL = NN / 32;            // 32-neuron MFMA tiles
   constexpr int LPT = NN * UG_KC / BT;    // chunk loads per thread and matrix per stage
@@ -575,6 +638,7 @@ __global__ __launch_bounds__(BT) void k_bug(BatchArgs a) {
 // c0 + 8p .. c0 + 8p + 7 of four rows; element b of those chunks feeds MFMA block b, whose
 // output column p is y column c0 + 8p + b.
 __global__ __launch_bounds__(BT) void k_bdown(BatchArgs a) {
+  at_pass(a);
   __shared__ int s_nid[DN_CH];
   __shared__ float s_y[MB * DN_COLS];
   const int tid = threadIdx.x, lane = tid & (WAVE - 1), wave = tid / WAVE;
@@ -655,8 +719,10 @@ __global__ __launch_bounds__(BT) void k_bdown(BatchArgs a) {
 // y = b_down + sum of the non-empty segments' partials (in segment order); workgroup (0, m)
 // also writes token m's ascending index list and count.
 __global__ __launch_bounds__(256) void k_bred(BatchArgs a) {
+  at_pass(a);
   if (a.run_if && *a.run_if != a.run_want) return;
   const int m = blockIdx.y;
+  if (m >= a.B) return;                                 // the last pass of a call may be short
   const int col = (blockIdx.x * 256 + threadIdx.x) * 4;
   const int total = *a.ucnt;
   if (col < a.d) {
@@ -706,14 +772,15 @@ BatchShape batch_shape(int d, int ffn, int r) {
   return s;
 }
 
-hipError_t launch_batch_sets(const BatchArgs& a, int use_predictor, hipStream_t st) {
+hipError_t launch_batch_sets(const BatchArgs& a, int use_predictor, hipStream_t st,
+                             int passes) {
   const int W = a.ffn / 32;
   if (use_predictor) {
-    hipLaunchKernelGGL(k_bz, dim3((a.r + 31) / 32, a.ks), dim3(BT), 0, st, a);
-    hipLaunchKernelGGL(k_bzr, dim3((MB * a.r + 255) / 256), dim3(256), 0, st, a);
-    hipLaunchKernelGGL(k_bs, dim3((W + 3) / 4), dim3(BS_T), 0, st, a);
+    hipLaunchKernelGGL(k_bz, dim3((a.r + 31) / 32 * a.ks * passes), dim3(BT), 0, st, a);
+    hipLaunchKernelGGL(k_bzr, dim3((MB * a.r + 255) / 256, 1, passes), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(k_bs, dim3((W + 3) / 4 * passes), dim3(BS_T), 0, st, a);
   } else {
-    hipLaunchKernelGGL(k_bmask, dim3((W + 255) / 256), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(k_bmask, dim3((W + 255) / 256, 1, passes), dim3(256), 0, st, a);
   }
   return hipGetLastError();
 }
@@ -724,7 +791,7 @@ hipError_t launch_batch_union(const BatchArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_batch_rows(const BatchArgs& a, int choose_path, hipStream_t st,
-                             hipEvent_t (*ev)[2]) {
+                             hipEvent_t (*ev)[2], int passes) {
   const int W = a.ffn / 32;
   if (choose_path) hipLaunchKernelGGL(k_bpath, dim3(1), dim3(1024), 0, st, a);
   // ReLU layers at larger batches take 64 union neurons per workgroup: each token slice then
@@ -732,28 +799,37 @@ hipError_t launch_batch_rows(const BatchArgs& a, int choose_path, hipStream_t st
   // and the gate's second tile would not fit the LDS of several resident workgroups)
   if (a.has_gate) {
     if (ev && ev[0][0])
-      hipExtLaunchKernelGGL((k_bug<true, 32>), dim3(W), dim3(BT), 0, st, ev[0][0], ev[0][1], 0, a);
+      hipExtLaunchKernelGGL((k_bug<true, 32>), dim3(W, 1, passes), dim3(BT), 0, st, ev[0][0],
+                            ev[0][1], 0, a);
     else
-      hipLaunchKernelGGL((k_bug<true, 32>), dim3(W), dim3(BT), 0, st, a);
+      hipLaunchKernelGGL((k_bug<true, 32>), dim3(W, 1, passes), dim3(BT), 0, st, a);
   } else if (a.B > UG_WIDE_B) {
-    const dim3 g2((W + 1) / 2);
+    const dim3 g2((W + 1) / 2, 1, passes);
     if (ev && ev[0][0])
       hipExtLaunchKernelGGL((k_bug<false, 64>), g2, dim3(BT), 0, st, ev[0][0], ev[0][1], 0, a);
     else
       hipLaunchKernelGGL((k_bug<false, 64>), g2, dim3(BT), 0, st, a);
   } else {
     if (ev && ev[0][0])
-      hipExtLaunchKernelGGL((k_bug<false, 32>), dim3(W), dim3(BT), 0, st, ev[0][0], ev[0][1], 0, a);
+      hipExtLaunchKernelGGL((k_bug<false, 32>), dim3(W, 1, passes), dim3(BT), 0, st, ev[0][0],
+                            ev[0][1], 0, a);
     else
-      hipLaunchKernelGGL((k_bug<false, 32>), dim3(W), dim3(BT), 0, st, a);
+      hipLaunchKernelGGL((k_bug<false, 32>), dim3(W, 1, passes), dim3(BT), 0, st, a);
   }
-  const dim3 gd((a.d + DN_COLS - 1) / DN_COLS, a.S);
+  const dim3 gd((a.d + DN_COLS - 1) / DN_COLS, a.S, passes);
   if (ev && ev[1][0])
     hipExtLaunchKernelGGL(k_bdown, gd, dim3(BT), 0, st, ev[1][0], ev[1][1], 0, a);
   else
     hipLaunchKernelGGL(k_bdown, gd, dim3(BT), 0, st, a);
-  hipLaunchKernelGGL(k_bred, dim3((a.d + 1023) / 1024, a.B), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(k_bred, dim3((a.d + 1023) / 1024, passes > 1 ? MB : a.B, passes), dim3(256),
+                     0, st, a);
   return hipGetLastError();
+}
+
+int batch_segments_mp(int d, int passes) {
+  const int ctiles = (d + DN_COLS - 1) / DN_COLS;
+  const int S = std::max(1, std::min(64, 256 / ctiles));
+  return std::max(1, std::min(S, 2048 / (ctiles * std::max(passes, 1))));
 }
 
 hipError_t launch_batch(const BatchArgs& a, int use_predictor, int choose_path, hipStream_t st,
@@ -763,9 +839,10 @@ hipError_t launch_batch(const BatchArgs& a, int use_predictor, int choose_path, 
   return launch_batch_rows(a, choose_path, st, ev);
 }
 
-hipError_t launch_dense_choice(const uint32_t* bits, int B, int ffn, int dense_above, int* flag,
-                               hipStream_t st) {
-  hipLaunchKernelGGL(k_dchoice, dim3(1), dim3(1024), 0, st, bits, B, ffn / 32, dense_above, flag);
+hipError_t launch_dense_choice(const uint32_t* ubits, int passes, int ffn, int dense_above,
+                               int* flag, hipStream_t st) {
+  hipLaunchKernelGGL(k_dchoice, dim3(1), dim3(1024), 0, st, ubits, passes, ffn / 32, dense_above,
+                     flag);
   return hipGetLastError();
 }
 

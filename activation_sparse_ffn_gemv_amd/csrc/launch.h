@@ -185,6 +185,11 @@ struct BatchArgs {
   const int* run_if;          // device flag: the row kernels run only if *run_if == run_want
   int run_want;               //   (nullptr: always)
   int head_words;             // hot head (as PredArgs)
+  // Several passes in one launch (grid.z = pass p, tokens [32p, 32p + 32) of the call): every
+  // per-token pointer above advances by 32 tokens per pass, the per-pass buffers by the strides
+  // below (elements), and B = min(32, Btot - 32p).  One pass: Btot = 0 and the strides unused.
+  int Btot;
+  size_t zpart_ps, zhl_ps, ubits_ps, uidx_ps, ypart_ps;
 };
 
 struct BatchShape {
@@ -198,16 +203,19 @@ BatchShape batch_shape(int d, int ffn, int r);
 hipError_t launch_batch(const BatchArgs& a, int use_predictor, int choose_path, hipStream_t st,
                         hipEvent_t (*ev)[2] = nullptr);
 // The pieces: the pass's active sets (bits, scores, union) ...
-hipError_t launch_batch_sets(const BatchArgs& a, int use_predictor, hipStream_t st);
+hipError_t launch_batch_sets(const BatchArgs& a, int use_predictor, hipStream_t st,
+                             int passes = 1);
 // ... the union recomputed from bits (when bits were written by an earlier step) ...
 hipError_t launch_batch_union(const BatchArgs& a, hipStream_t st);
 // ... and the rows (optional k_bpath, k_bug, k_bdown, k_bred).
 hipError_t launch_batch_rows(const BatchArgs& a, int choose_path, hipStream_t st,
-                             hipEvent_t (*ev)[2] = nullptr);
-// Device-side choice for a call of B tokens whose sets are in bits[B][ffn/32]: flag = 1 when the
-// union of all their sets holds more than dense_above neurons.
-hipError_t launch_dense_choice(const uint32_t* bits, int B, int ffn, int dense_above, int* flag,
-                               hipStream_t st);
+                             hipEvent_t (*ev)[2] = nullptr, int passes = 1);
+// Device-side choice for a call whose passes' union words are in ubits[passes][ffn/32]: flag =
+// 1 when the union of all of them holds more than dense_above neurons.
+hipError_t launch_dense_choice(const uint32_t* ubits, int passes, int ffn, int dense_above,
+                               int* flag, hipStream_t st);
+// Segments of the down projection per pass when `passes` passes share one launch.
+int batch_segments_mp(int d, int passes);
 
 // Dense path (fp16 layers, many tokens): two MFMA GEMMs and a fixed-order reduce.
 constexpr int DENSE_MIN_M = 64;   // token count from which the dense GEMMs replace the batched kernels
