@@ -607,7 +607,11 @@ extern "C" {
 const char* ffn_last_error(void) { return g_err; }
 
 const char* ffn_status_string(ffn_status s) {
-  switch (s) {
+  // A C caller may pass any int; reading a value outside the enumerators through the enum type
+  // is undefined in C++, so the value is taken from the argument's bytes.
+  int v;
+  memcpy(&v, &s, sizeof v);
+  switch (v) {
     case FFN_OK: return "FFN_OK";
     case FFN_ERR_INVALID_ARGUMENT: return "FFN_ERR_INVALID_ARGUMENT";
     case FFN_ERR_UNSUPPORTED: return "FFN_ERR_UNSUPPORTED";
