@@ -24,6 +24,7 @@
 #include <algorithm>
 
 #include "common.h"
+#include "index.h"
 #include "launch.h"
 
 namespace ffn {
@@ -74,48 +75,22 @@ __device__ __forceinline__ f32x16 wg_sum4(f32x16 acc, float* red /* [3][16][64] 
 __device__ __forceinline__ void at_pass(BatchArgs& a, int p = blockIdx.z) {
   if (a.Btot > 0) a.B = min(MB, a.Btot - p * MB);      // (Btot 0: a one-pass launch)
   if (p == 0) return;
-  const size_t tok = (size_t)p * MB;
-  a.x = static_cast<const char*>(a.x) + tok * a.d * 2;
-  if (a.mask) a.mask += tok * a.ffn;
-  a.bits += tok * (a.ffn / 32);
-  if (a.scores) a.scores += tok * a.ffn;
-  a.y += tok * a.d;
-  if (a.idx_out) a.idx_out += tok * a.ffn;
-  if (a.cnt_out) a.cnt_out += tok;
-  a.zpart += (size_t)p * a.zpart_ps;
-  a.zhl += (size_t)p * a.zhl_ps;
-  a.ubits += (size_t)p * a.ubits_ps;
-  a.ucnt += p;
-  a.uidx += (size_t)p * a.uidx_ps;
-  a.H += tok * a.ffn;
-  a.ypart += (size_t)p * a.ypart_ps;
-}
-
-// Workgroup id -> (weight block, pass) for a multi-pass launch over nb weight blocks.  Workgroup
-// id runs on XCD id % 8 (consecutive workgroups go to the eight XCDs in turn); the passes of one
-// block go to consecutive workgroups of one XCD, so that they run side by side and read the
-// block's weights from that XCD's L2 instead of once per pass from HBM.  nb not a multiple of
-// 8: plain block-major order.
-__device__ __forceinline__ void xcd_block_pass(int id, int nb, int passes, int& bx, int& p) {
-  if (passes == 1) {
-    bx = id;
-    p = 0;
-  } else if (nb % 8) {
-    bx = id % nb;
-    p = id / nb;
-  } else {
-    const int k = id / 8;
-    p = k % passes;
-    bx = (k / passes) * 8 + id % 8;
-  }
-}
-
-// Union ranks [r0, r1) of segment s: segments are cut at multiples of 8 ranks (one x8 step).
-// 32-bit exact: total <= 32768 (so units <= 4096) and s + 1 <= S <= 64.
-__device__ __forceinline__ void seg_range(int total, int s, int S, int& r0, int& r1) {
-  const uint32_t units = ((uint32_t)total + 7u) / 8u;
-  r0 = (int)(8u * (units * (uint32_t)s / (uint32_t)S));
-  r1 = (int)(8u * (units * (uint32_t)(s + 1) / (uint32_t)S));
+  const PassOffsets o = pass_offsets(p, MB, a.zpart_ps, a.zhl_ps, a.ubits_ps, a.uidx_ps,
+                                     a.ypart_ps);
+  a.x = static_cast<const char*>(a.x) + o.tok * a.d * 2;
+  if (a.mask) a.mask += o.tok * a.ffn;
+  a.bits += o.tok * (a.ffn / 32);
+  if (a.scores) a.scores += o.tok * a.ffn;
+  a.y += o.tok * a.d;
+  if (a.idx_out) a.idx_out += o.tok * a.ffn;
+  if (a.cnt_out) a.cnt_out += o.tok;
+  a.zpart += o.zpart;
+  a.zhl += o.zhl;
+  a.ubits += o.ubits;
+  a.ucnt += o.ucnt;
+  a.uidx += o.uidx;
+  a.H += o.tok * a.ffn;
+  a.ypart += o.ypart;
 }
 
 // ---------------------------------------------------------------------------------------------

@@ -19,6 +19,7 @@
 #include <hip/hip_ext.h>
 
 #include "common.h"
+#include "index.h"
 #include "launch.h"
 
 namespace ffn {
@@ -193,7 +194,6 @@ __global__ __launch_bounds__(256) void k_mask_bits(const unsigned char* __restri
 constexpr int GA_THREADS = 512;
 constexpr int GA_NW = GA_THREADS / WAVE;
 constexpr int GA_BLOCKS = 256;
-constexpr int RD_TW = 16;             // columns per reduce tile (64 bytes of every partial)
 constexpr int GA_MAXW = 2;            // bitmap words per thread: ffn <= 32768
 constexpr int GA_LIST = 64;           // ranks resolved per batch
 
@@ -288,9 +288,8 @@ __global__ __launch_bounds__(GA_THREADS) void k_gather(GatherArgs a) {
   }
   run0 = base + before;                          // rank of this thread's first active neuron
   }
-  // 32-bit exact: |A| <= 32768 and at most 256 workgroups
-  const int r0 = (int)(((uint32_t)total * blockIdx.x) / nblk);
-  const int r1 = (int)(((uint32_t)total * (blockIdx.x + 1)) / nblk);
+  int r0, r1;
+  gather_rank_range((uint32_t)total, blockIdx.x, nblk, r0, r1);
   FFN_TS(1, 1);
 
   float acc[CPT][EPC];
@@ -512,9 +511,7 @@ __global__ __launch_bounds__(GA_THREADS) void k_gather(GatherArgs a) {
         if (c < nch) {
 #pragma unroll
           for (int e = 0; e < EPC; e += 4) {
-            const int col = c * EPC + e;
-            float* dst = a.part + ((size_t)(col / RD_TW) * nblk + blockIdx.x) * RD_TW +
-                         col % RD_TW;
+            float* dst = a.part + part_offset(c * EPC + e, blockIdx.x, nblk);
             // streaming store: the partial is read once, by the next kernel
             __builtin_nontemporal_store(f32x4{acc[k][e], acc[k][e + 1], acc[k][e + 2], acc[k][e + 3]},
                                         reinterpret_cast<f32x4*>(dst));
@@ -768,8 +765,7 @@ __global__ __launch_bounds__(FU_THREADS) void k_fused(FusedArgs f) {
       if (c < nch) {
 #pragma unroll
         for (int e = 0; e < EPC; e += 4) {
-          const int col = c * EPC + e;
-          float* dst = a.part + ((size_t)(col / RD_TW) * nparts + blockIdx.x) * RD_TW + col % RD_TW;
+          float* dst = a.part + part_offset(c * EPC + e, blockIdx.x, nparts);
           __builtin_nontemporal_store(f32x4{acc[k][e], acc[k][e + 1], acc[k][e + 2], acc[k][e + 3]},
                                       reinterpret_cast<f32x4*>(dst));
         }
@@ -834,15 +830,14 @@ __global__ __launch_bounds__(RD_THREADS) void k_reduce(ReduceArgs a) {
       if (MODE == 1) {
         on = (a.bitmap[2 * c] | (2 * c + 1 < (uint32_t)a.ffn / 32 ? a.bitmap[2 * c + 1] : 0u)) != 0u;
       } else {
-        // partial c exists iff gather workgroup c owned at least one rank (32-bit exact:
-        // |A| <= 32768 and c < 512)
+        // partial c exists iff gather workgroup c owned at least one rank
         const uint32_t total = MODE == 0 ? total0 : (uint32_t)a.cnt[(size_t)k * a.cstride];
-        on = (total * (c + 1)) / np > (total * c) / np;
+        on = gather_wrote_partial(total, c, np);
       }
       on = on && i0 + g + u * RD_G < items;
       wt[u] = on ? (MODE == 2 ? a.slot[k].wgt : 1.0f) : 0.0f;
       v[u] = *reinterpret_cast<const f32x4*>(a.part + (size_t)k * a.pstride +
-                                             ((size_t)tile * np + c) * RD_TW + q * 4);
+                                             part_offset(tile * RD_TW + q * 4, c, np));
     }
     issue_fence();
 #pragma unroll

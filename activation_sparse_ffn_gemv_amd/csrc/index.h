@@ -1,0 +1,84 @@
+// Index arithmetic of the kernels that split work between workgroups and exchange partial
+// results through the workspace, as host-and-device functions: the kernels call them, and a CPU
+// build of the same functions (tests/index_check.cpp) walks every workgroup and thread of the
+// launch shapes the library uses and checks that each index stays inside its buffer, that
+// writers and readers agree, and that the 32-bit products never wrap.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ffn {
+
+// Columns of y per tile of the batch-1 partial sums: the gather stores its partial tile-major,
+// part[col / RD_TW][workgroup][col % RD_TW], so the reduce reads one contiguous block per tile.
+constexpr int RD_TW = 16;
+
+// Ranks [r0, r1) of the active set owned by gather workgroup b of nblk (an even split).
+// 32-bit exact for total <= 32768 and nblk <= 512: total * nblk < 2^24.
+__host__ __device__ inline void gather_rank_range(uint32_t total, uint32_t b, uint32_t nblk,
+                                                  int& r0, int& r1) {
+  r0 = (int)((total * b) / nblk);
+  r1 = (int)((total * (b + 1)) / nblk);
+}
+
+// Whether gather workgroup b of nblk owned a rank (so wrote a partial).
+__host__ __device__ inline bool gather_wrote_partial(uint32_t total, uint32_t b, uint32_t nblk) {
+  return (total * (b + 1)) / nblk > (total * b) / nblk;
+}
+
+// Element offset of column col of workgroup blk's partial (nblk partials), tile-major.
+__host__ __device__ inline size_t part_offset(int col, int blk, int nblk) {
+  return ((size_t)(col / RD_TW) * nblk + blk) * RD_TW + col % RD_TW;
+}
+
+// Union ranks [r0, r1) of segment s of S of the batched down projection: segments are cut at
+// multiples of 8 ranks (one 8-deep MFMA step).  32-bit exact: total <= 32768 (so at most 4096
+// units) and s + 1 <= S <= 64.
+__host__ __device__ inline void seg_range(int total, int s, int S, int& r0, int& r1) {
+  const uint32_t units = ((uint32_t)total + 7u) / 8u;
+  r0 = (int)(8u * (units * (uint32_t)s / (uint32_t)S));
+  r1 = (int)(8u * (units * (uint32_t)(s + 1) / (uint32_t)S));
+}
+
+// Workgroup id -> (weight block, pass) for a launch over nb weight blocks and `passes` passes.
+// Workgroup id runs on XCD id % 8 (consecutive workgroups go to the eight XCDs in turn); the
+// passes of one block go to consecutive workgroups of one XCD, so that they run side by side and
+// read the block's weights from that XCD's L2 instead of once per pass from HBM.  nb not a
+// multiple of 8: plain block-major order.
+__host__ __device__ inline void xcd_block_pass(int id, int nb, int passes, int& bx, int& p) {
+  if (passes == 1) {
+    bx = id;
+    p = 0;
+  } else if (nb % 8) {
+    bx = id % nb;
+    p = id / nb;
+  } else {
+    const int k = id / 8;
+    p = k % passes;
+    bx = (k / passes) * 8 + id % 8;
+  }
+}
+
+// Element offsets of pass p's share of the batched path's buffers when the passes of one call
+// run in one launch (tokens [32 p, 32 p + 32)); strides per pass in elements.
+struct PassOffsets {
+  size_t tok;                 // tokens before the pass
+  size_t zpart, zhl, ubits, ucnt, uidx, ypart;
+};
+__host__ __device__ inline PassOffsets pass_offsets(int p, int tile, size_t zpart_ps,
+                                                    size_t zhl_ps, size_t ubits_ps,
+                                                    size_t uidx_ps, size_t ypart_ps) {
+  PassOffsets o;
+  o.tok = (size_t)p * tile;
+  o.zpart = (size_t)p * zpart_ps;
+  o.zhl = (size_t)p * zhl_ps;
+  o.ubits = (size_t)p * ubits_ps;
+  o.ucnt = (size_t)p;
+  o.uidx = (size_t)p * uidx_ps;
+  o.ypart = (size_t)p * ypart_ps;
+  return o;
+}
+
+}  // namespace ffn

@@ -1,0 +1,175 @@
+// CPU build of the kernels' index arithmetic (activation_sparse_ffn_gemv_amd/csrc/index.h, the
+// functions the kernels call) under AddressSanitizer / UndefinedBehaviorSanitizer, walked over
+// every workgroup and thread of the launch shapes the library uses: every index must stay inside
+// its buffer, the gather's partial writes and the reduce's reads must address the same elements,
+// the work splits must partition their ranges exactly, and no 32-bit product may wrap.  The
+// shapes come from the built library's own host functions (workgroup counts, tiles, the batched
+// path's buffer shapes).  Exit status 0 and "index check: OK" when every check holds.
+#include <stdio.h>
+#include <stdlib.h>
+
+#include <algorithm>
+#include <vector>
+
+#include "../activation_sparse_ffn_gemv_amd/csrc/index.h"
+#include "../activation_sparse_ffn_gemv_amd/csrc/launch.h"
+
+using namespace ffn;
+
+static long checks = 0, failures = 0;
+
+#define CHECK(cond, ...)                                                  \
+  do {                                                                    \
+    ++checks;                                                             \
+    if (!(cond)) {                                                        \
+      if (failures < 20) {                                                \
+        printf("FAIL %s:%d: %s: ", __FILE__, __LINE__, #cond);            \
+        printf(__VA_ARGS__);                                              \
+        printf("\n");                                                     \
+      }                                                                   \
+      ++failures;                                                         \
+    }                                                                     \
+  } while (0)
+
+// Batch-1 gather -> reduce: nblk workgroups split `total` ranks; each writes the partial of all
+// d columns (16-byte pieces of 4 floats); the reduce reads tile by tile.
+static void check_partials(int d, int ffn, int nblk) {
+  const int tiles = reduce_tiles(d);
+  const size_t region = (size_t)nblk * tiles * RD_TW;           // the layout's partial block
+  std::vector<unsigned char> written(region, 0);
+  for (int blk = 0; blk < nblk; ++blk)
+    for (int col = 0; col < d; col += 4) {                       // the gather's f32x4 stores
+      const size_t o = part_offset(col, blk, nblk);
+      CHECK(o + 3 < region, "d %d nblk %d blk %d col %d offset %zu region %zu", d, nblk, blk,
+            col, o, region);
+      if (o + 3 < region)
+        for (int e = 0; e < 4; ++e) {
+          CHECK(!written[o + e], "element written twice: d %d blk %d col %d", d, blk, col);
+          written[o + e] = 1;
+        }
+    }
+  for (int tile = 0; tile < tiles; ++tile)                       // the reduce's f32x4 reads
+    for (int c = 0; c < nblk; ++c)
+      for (int q = 0; q < RD_TW / 4; ++q) {
+        const int col = tile * RD_TW + q * 4;
+        const size_t o = part_offset(col, c, nblk);
+        CHECK(o + 3 < region, "reduce read out of the region: d %d tile %d c %d", d, tile, c);
+        if (col < d && o + 3 < region)                           // columns the reduce stores
+          CHECK(written[o] && written[o + 3], "reduce reads an unwritten column %d", col);
+      }
+  // rank split: consecutive, covering [0, total) exactly, balanced; the existence test agrees
+  const int totals[] = {0, 1, 7, nblk - 1, nblk, nblk + 1, 1093, ffn / 2, ffn - 1, ffn};
+  for (int total : totals) {
+    if (total < 0 || total > ffn) continue;
+    int prev = 0;
+    for (int b = 0; b < nblk; ++b) {
+      int r0, r1;
+      gather_rank_range((uint32_t)total, (uint32_t)b, (uint32_t)nblk, r0, r1);
+      const long long e0 = (long long)total * b / nblk, e1 = (long long)total * (b + 1) / nblk;
+      CHECK(r0 == e0 && r1 == e1, "32-bit rank split wraps: total %d b %d nblk %d", total, b,
+            nblk);
+      CHECK(r0 == prev && r1 >= r0, "ranks not consecutive: total %d b %d", total, b);
+      CHECK(r1 - r0 <= (total + nblk - 1) / nblk, "unbalanced split: total %d b %d", total, b);
+      CHECK(gather_wrote_partial((uint32_t)total, (uint32_t)b, (uint32_t)nblk) == (r1 > r0),
+            "existence test disagrees: total %d b %d", total, b);
+      prev = r1;
+    }
+    CHECK(prev == total, "split does not cover [0, %d)", total);
+  }
+}
+
+// Batched down projection: S segments of the union ranks, cut at multiples of 8.
+static void check_segments() {
+  for (int S = 1; S <= 64; ++S)
+    for (int total = 0; total <= 32768; total += (total < 300 ? 1 : 97)) {
+      int prev = 0;
+      const long long units = (total + 7) / 8;
+      for (int s = 0; s < S; ++s) {
+        int r0, r1;
+        seg_range(total, s, S, r0, r1);
+        CHECK(r0 == 8 * (units * s / S) && r1 == 8 * (units * (s + 1) / S),
+              "32-bit segment split wraps: total %d S %d s %d", total, S, s);
+        CHECK(r0 == prev && r1 >= r0 && r0 % 8 == 0, "segments not consecutive: %d %d", S, s);
+        prev = r1;
+      }
+      CHECK(prev == 8 * units, "segments do not cover the union: total %d S %d", total, S);
+    }
+}
+
+// (block, pass) order of a multi-pass launch: a bijection onto [0, nb) x [0, passes).
+static void check_xcd_order() {
+  const int passes_list[] = {1, 2, 3, 16, 128};
+  for (int nb = 1; nb <= 520; ++nb)
+    for (int passes : passes_list) {
+      std::vector<unsigned char> seen((size_t)nb * passes, 0);
+      for (int id = 0; id < nb * passes; ++id) {
+        int bx, p;
+        xcd_block_pass(id, nb, passes, bx, p);
+        CHECK(bx >= 0 && bx < nb && p >= 0 && p < passes, "nb %d passes %d id %d -> %d %d", nb,
+              passes, id, bx, p);
+        if (bx >= 0 && bx < nb && p >= 0 && p < passes) {
+          CHECK(!seen[(size_t)p * nb + bx], "pair given twice: nb %d passes %d", nb, passes);
+          seen[(size_t)p * nb + bx] = 1;
+        }
+      }
+    }
+}
+
+// The passes of one call in one launch: each pass's share of every buffer lies inside the
+// region laid out for ceil(max_batch / 32) passes, and the kernels' largest index inside a pass
+// stays below the pass's stride.
+static void check_passes(int d, int ffn, int r, int max_batch) {
+  const BatchShape s = batch_shape(d, ffn, r);
+  const int P = (max_batch + BATCH_TILE - 1) / BATCH_TILE;
+  const int S = batch_segments_mp(d, P);
+  const size_t zpart_ps = s.zpart_bytes / 4, zhl_ps = s.zhl_bytes / 2, ubits_ps = ffn / 32,
+               uidx_ps = ffn, ypart_ps = (size_t)S * BATCH_TILE * d;
+  // largest element index each kernel touches inside one pass
+  CHECK((size_t)(s.ks - 1) * BATCH_TILE * r + (size_t)(BATCH_TILE - 1) * r + (r - 1) < zpart_ps,
+        "predictor stage-1 partials overflow a pass: d %d r %d", d, r);
+  CHECK((size_t)BATCH_TILE * r + (size_t)BATCH_TILE * r - 1 < zhl_ps + 0, "z hi/lo overflow");
+  CHECK(((size_t)(S - 1) * BATCH_TILE + BATCH_TILE - 1) * d + (d - 1) < ypart_ps,
+        "segment partials overflow a pass: d %d S %d", d, S);
+  CHECK(S >= 1 && S <= 64, "segments per pass %d", S);
+  for (int B = 64; B <= max_batch; B += (B < 200 ? 1 : 61)) {
+    const int Pc = (B + BATCH_TILE - 1) / BATCH_TILE;
+    CHECK(Pc <= P, "a call of %d tokens needs %d passes, the region holds %d", B, Pc, P);
+    for (int p = 0; p < Pc; ++p) {
+      const PassOffsets o = pass_offsets(p, BATCH_TILE, zpart_ps, zhl_ps, ubits_ps, uidx_ps,
+                                         ypart_ps);
+      const int Bp = std::min(BATCH_TILE, B - p * BATCH_TILE);
+      CHECK(Bp >= 1 && o.tok + Bp <= (size_t)B, "pass %d of %d tokens: tokens out of range", p, B);
+      CHECK(o.zpart + zpart_ps <= (size_t)P * zpart_ps, "zpart");
+      CHECK(o.zhl + zhl_ps <= (size_t)P * zhl_ps, "zhl");
+      CHECK(o.ubits + ubits_ps <= (size_t)P * ubits_ps, "ubits");
+      CHECK(o.ucnt + 1 <= (size_t)P, "ucnt");
+      CHECK(o.uidx + uidx_ps <= (size_t)P * uidx_ps, "uidx");
+      CHECK(o.ypart + ypart_ps <= (size_t)P * ypart_ps, "ypart");
+      // H rows of the pass (every one of its 32 rows is written, the last pass's too)
+      CHECK(o.tok + BATCH_TILE <= (size_t)P * BATCH_TILE, "H rows");
+    }
+  }
+}
+
+int main() {
+  const int ds[] = {64, 256, 512, 768, 776, 1024, 4096, 4104, 8192};
+  const int ffns[] = {256, 1024, 3072, 11008, 14336, 32768};
+  for (int d : ds)
+    for (int ffn : ffns) {
+      const int nblks[] = {gather_blocks(1), gather_blocks(2), gather_blocks(3), gather_blocks(4),
+                           fused_blocks(ffn)};
+      for (int nblk : nblks) check_partials(d, ffn, nblk);
+    }
+  check_segments();
+  check_xcd_order();
+  const int shapes[][4] = {{4096, 11008, 256, 64}, {4096, 14336, 512, 100},
+                           {8192, 32768, 1024, 512}, {256, 1024, 32, 4096}, {512, 2048, 64, 70},
+                           {1024, 4096, 64, 256}};
+  for (const auto& sh : shapes) check_passes(sh[0], sh[1], sh[2], sh[3]);
+  if (failures) {
+    printf("index check: %ld of %ld checks failed\n", failures, checks);
+    return 1;
+  }
+  printf("index check: OK (%ld checks)\n", checks);
+  return 0;
+}

@@ -83,3 +83,31 @@ def test_host_code_clean_under_asan_and_ubsan(tmp_path):
     bad = subprocess.run([exe, "planted"], capture_output=True, text=True, env=env, timeout=300)
     assert bad.returncode != 0 and "heap-buffer-overflow" in bad.stderr, bad.stdout + bad.stderr
     assert "check_desc" in bad.stderr or "ffn_workspace_size" in bad.stderr, bad.stderr[-3000:]
+
+
+@pytest.mark.skipif(not (os.path.exists(HIPCC) and _runtime_dir()),
+                    reason="needs hipcc and clang's sanitizer runtimes")
+def test_kernel_index_arithmetic_in_a_cpu_build(tmp_path):
+    """The kernels' index functions (csrc/index.h) compiled for the CPU with ASan and UBSan and
+    walked over every workgroup and thread of the library's launch shapes (tests/index_check.cpp:
+    partial-sum writes and reads, rank and segment splits, the XCD-ordered (block, pass) map and
+    the per-pass buffer offsets of calls that run all their passes in one launch)."""
+    lib_dir = os.path.join(ROOT, "activation_sparse_ffn_gemv_amd")
+    if not os.path.exists(os.path.join(lib_dir, "libffn_sparse.so")):
+        pytest.skip("library not built")
+    exe = str(tmp_path / "index_check")
+    r = subprocess.run([HIPCC, "-x", "hip", "--cuda-host-only", "-std=c++17", "-O1", "-g",
+                        "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                        "-Xarch_host", "-fno-sanitize-recover=all", "-shared-libsan",
+                        os.path.join(ROOT, "tests", "index_check.cpp"),
+                        "-L" + lib_dir, "-l:libffn_sparse.so", "-Wl,-rpath," + lib_dir,
+                        "-Wl,-rpath," + _runtime_dir(), "-o", exe],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-2000:]
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0", UBSAN_OPTIONS="print_stacktrace=1",
+               LD_LIBRARY_PATH=":".join([_runtime_dir(), os.environ.get("LD_LIBRARY_PATH", "")]))
+    env.pop("LD_PRELOAD", None)
+    run = subprocess.run([exe], capture_output=True, text=True, env=env, timeout=600)
+    assert run.returncode == 0, run.stdout[-3000:] + run.stderr[-3000:]
+    assert "index check: OK" in run.stdout, run.stdout[-2000:]
+    assert "runtime error" not in run.stderr, run.stderr[-3000:]
