@@ -125,7 +125,7 @@ def lib():
         L.ffn_moe_plan.restype = st
         L.ffn_moe_plan.argtypes = [I, I, P, ctypes.POINTER(P), P, S, ctypes.POINTER(P)]
         L.ffn_moe_forward.restype = st
-        L.ffn_moe_forward.argtypes = [P, P, I, P, P, P, P]
+        L.ffn_moe_forward.argtypes = [P, P, I, P, P, P, P, P]
         L.ffn_moe_destroy.restype = st
         L.ffn_moe_destroy.argtypes = [P]
         _lib = L
@@ -248,9 +248,9 @@ def ffn_moe_plan(n_experts: int, top_k: int, w_router: int, experts, workspace: 
 
 
 def ffn_moe_forward(moe: int, x: int, B: int, y: int, expert_idx: int = 0, expert_w: int = 0,
-                    stream: int = 0):
+                    expert_cnt: int = 0, stream: int = 0):
     _check(lib().ffn_moe_forward(moe, x, B, y, expert_idx or None, expert_w or None,
-                                 stream or None))
+                                 expert_cnt or None, stream or None))
 
 
 def ffn_moe_destroy(moe: int):
@@ -409,12 +409,12 @@ class MoEFFN:
         self.moe = ffn_moe_plan(len(plans), top_k, router.data_ptr(), plans,
                                 self.workspace.data_ptr(), n)
 
-    def forward(self, x, y=None, expert_idx=None, expert_w=None):
+    def forward(self, x, y=None, expert_idx=None, expert_w=None, expert_cnt=None):
         B = x.shape[0]
         if y is None:
             y = torch.empty(B, self.d, dtype=torch.float32, device=x.device)
         ffn_moe_forward(self.moe, x.data_ptr(), B, y.data_ptr(), _ptr(expert_idx), _ptr(expert_w),
-                        _stream())
+                        _ptr(expert_cnt), _stream())
         return y
 
     def close(self):

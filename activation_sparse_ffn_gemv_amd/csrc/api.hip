@@ -1183,7 +1183,7 @@ ffn_status ffn_moe_plan(int32_t n_experts, int32_t top_k, const void* w_router,
 }
 
 ffn_status ffn_moe_forward(ffn_moe* m, const void* x, int32_t B, float* y, int32_t* expert_idx,
-                           float* expert_w, void* stream) {
+                           float* expert_w, int32_t* expert_cnt, void* stream) {
   if (!m) return fail(FFN_ERR_INVALID_ARGUMENT, "moe is NULL");
   if (!x || !y) return fail(FFN_ERR_INVALID_ARGUMENT, "x / y is NULL");
   const ffn_plan* p = m->e0;
@@ -1218,7 +1218,8 @@ ffn_status ffn_moe_forward(ffn_moe* m, const void* x, int32_t B, float* y, int32
   for (int b = 0; b < B; ++b) {
     // the token's top_k experts run side by side, one launch per stage
     ffn_status s = enqueue_token(p, wb, static_cast<const char*>(x) + b * xbytes, nullptr,
-                                 y + (size_t)b * D.d, nullptr, nullptr, nullptr,
+                                 y + (size_t)b * D.d, nullptr,
+                                 expert_cnt ? expert_cnt + (size_t)b * m->top_k : nullptr, nullptr,
                                  slots + (size_t)b * m->top_k, m->top_k, m->L.slot_stride, st,
                                  false, zall + (size_t)b * m->n_experts * D.rank);
     if (s != FFN_OK) return s;

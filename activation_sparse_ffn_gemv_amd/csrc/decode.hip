@@ -863,8 +863,13 @@ __global__ __launch_bounds__(RD_THREADS) void k_reduce(ReduceArgs a) {
     for (int w = 1; w < RD_THREADS / WAVE; ++w) t += s[w][q];
     *reinterpret_cast<f32x4*>(a.y + j) = t + bias;
   }
-  if (blockIdx.x == 0 && (a.idx_out || a.cnt_out))
+  if (MODE == 2) {
+    // expert slots: each slot's |A| (written by the gather) in slot order
+    if (blockIdx.x == 0 && a.cnt_out && (int)threadIdx.x < nslot)
+      a.cnt_out[threadIdx.x] = a.cnt[(size_t)threadIdx.x * a.cstride];
+  } else if (blockIdx.x == 0 && (a.idx_out || a.cnt_out)) {
     write_index_list<RD_THREADS>(a.bitmap, a.ffn / 32, a.idx_out, a.cnt_out);
+  }
   FFN_TS(2, 5);
 }
 

@@ -111,8 +111,8 @@ struct ReduceArgs {
   const uint32_t* bitmap;     // [ffn/32], for the index-list output
   const float* b_down;
   float* y;                   // [d]
-  int* idx_out;               // [ffn] ascending active list, or nullptr
-  int* cnt_out;               // [1], or nullptr
+  int* idx_out;               // [ffn] ascending active list, or nullptr (one token)
+  int* cnt_out;               // [1] |A|, or nullptr; expert slots: [nslot], each slot's |A|
   int d, ffn, n_part;
   int fused;                  // partials from the fused kernel: partial c exists iff bitmap words
                               //   2c, 2c+1 are not both zero (else: from |A| and the rank split)

@@ -388,21 +388,13 @@ def main(argv=None):
             log("AUTO prefill: the device chose the dense GEMMs at %d of %d layers (crossover "
                 "density %.4f for %d tokens)" % (n_dense, L, path_chosen["crossover_density"], Bt))
     elif moe:
+        # the mixture's own calls report each chosen expert's |A| (the launches the bench times)
         ids = torch.zeros(L, K, cfg.top_k, dtype=torch.int32, device=dev)
-        with torch.cuda.stream(stream):
-            for t in range(K):
-                for l in range(L):
-                    call(l, t, expert_idx=ids[l, t].data_ptr())
-        torch.cuda.synchronize()
-        ids_h = ids.cpu().numpy()
         cnt = torch.zeros(L, K, cfg.top_k, dtype=torch.int32, device=dev)
         with torch.cuda.stream(stream):
             for t in range(K):
                 for l in range(L):
-                    for j in range(cfg.top_k):
-                        ffn.ffn_sparse_forward(mods[l][ids_h[l, t, j]].plan, xp[l][t], 1,
-                                               yp[l][t], cnt=cnt[l, t].data_ptr() + 4 * j,
-                                               stream=sp)
+                    call(l, t, expert_idx=ids[l, t].data_ptr(), expert_cnt=cnt[l, t].data_ptr())
         torch.cuda.synchronize()
         cnt_h = cnt.cpu().numpy().astype(np.float64)
         touched = router_b + cfg.top_k * (pz + ps) + cnt_h.sum(axis=2) * rowb

@@ -311,9 +311,11 @@ ffn_status ffn_moe_plan(int32_t n_experts, int32_t top_k, const void *w_router,
                         ffn_moe **out);
 
 /* B tokens x[B][d]; y[B][d] fp32 overwritten.  expert_idx [B][top_k] int32 and expert_w
- * [B][top_k] fp32 (device, each may be NULL) receive the routing decision, best expert first. */
+ * [B][top_k] fp32 (device, each may be NULL) receive the routing decision, best expert first;
+ * expert_cnt [B][top_k] int32 (device or NULL) the size of each chosen expert's active set. */
 ffn_status ffn_moe_forward(ffn_moe *moe, const void *x, int32_t B, float *y,
-                           int32_t *expert_idx, float *expert_w, void *stream);
+                           int32_t *expert_idx, float *expert_w, int32_t *expert_cnt,
+                           void *stream);
 ffn_status ffn_moe_destroy(ffn_moe *moe);
 
 #ifdef __cplusplus

@@ -182,7 +182,7 @@ int main(int argc, char **argv)
     ffn_moe *moe = NULL;
     EXPECT(ffn_moe_plan(3, 2, DEV(10), experts, ws, mb - 256, &moe), FFN_ERR_WORKSPACE_TOO_SMALL);
     EXPECT(ffn_moe_plan(3, 2, DEV(10), experts, ws, mb, &moe), FFN_OK);
-    EXPECT(ffn_moe_forward(moe, DEV(9), 2, y, NULL, NULL, NULL), FFN_ERR_INVALID_ARGUMENT);
+    EXPECT(ffn_moe_forward(moe, DEV(9), 2, y, NULL, NULL, NULL, NULL), FFN_ERR_INVALID_ARGUMENT);
     EXPECT(ffn_moe_destroy(moe), FFN_OK);
     ffn_plan *odd = NULL;
     ffn_layer_desc *dodd = new_desc(4096, 14336, 128, FFN_ACT_DRELU, FFN_I4G32, 1);

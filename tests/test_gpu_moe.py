@@ -55,9 +55,11 @@ def _check_moe(ffn, cfg, n_experts, top_k, n_tokens, experts=None, R=None):
     y = torch.full((n_tokens, cfg.d), float("nan"), device="cuda")
     ids = torch.full((n_tokens, top_k), -1, dtype=torch.int32, device="cuda")
     w = torch.zeros(n_tokens, top_k, dtype=torch.float32, device="cuda")
-    moe.forward(x, y=y, expert_idx=ids, expert_w=w)
+    cnt = torch.full((n_tokens, top_k), -1, dtype=torch.int32, device="cuda")
+    moe.forward(x, y=y, expert_idx=ids, expert_w=w, expert_cnt=cnt)
     torch.cuda.synchronize()
     y_h, ids_h, w_h = y.cpu().numpy(), ids.cpu().numpy(), w.cpu().numpy()
+    cnt_h = cnt.cpu().numpy()
     moe.close()
 
     OLs = [oracle_layer(e) for e in experts]
@@ -74,10 +76,11 @@ def _check_moe(ffn, cfg, n_experts, top_k, n_tokens, experts=None, R=None):
         assert abs(w_h[t].sum() - 1.0) < 1e-6
         assert len(set(ids_h[t].tolist())) == top_k
         masks = []
-        for e in ids_h[t]:
+        for j, e in enumerate(ids_h[t]):
             if e not in sets:
                 sets[e] = _expert_sets(ffn, experts[e], x)
             masks.append(mask_from_idx(sets[e][t], cfg.ffn))
+            assert cnt_h[t, j] == len(sets[e][t]), (t, j, cnt_h[t, j], len(sets[e][t]))
         # oracle on the GPU's routing decision and the GPU's active sets
         y_ref = np.zeros(cfg.d)
         for j, e in enumerate(ids_h[t]):
