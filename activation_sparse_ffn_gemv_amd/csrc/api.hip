@@ -72,7 +72,7 @@ bool batched(const ffn_layer_desc* d) { return d->w_dtype == FFN_F16; }
 // partials [rows][d] | for `passes` = ceil(max_batch / 32) passes: predictor stage-1 partials,
 // z (hi, lo), union words, |U|, union ranks and the down projection's segment partials.
 struct DenseRegion {
-  size_t bits, flag, H, ypart, zpart, zhl, ubits, ucnt, uidx, mpart, end;
+  size_t bits, flag, H, ypart, zpart, zhl, ubits, ucnt, uidx, mpart, zcat, end;
   int passes, S;
 };
 
@@ -93,6 +93,7 @@ DenseRegion dense_region(const ffn_layer_desc* d, size_t base) {
   R.ucnt = off;   off = round_up(off + P * 4, 256);
   R.uidx = off;   off = round_up(off + P * d->ffn * 4, 256);
   R.mpart = off;  off = round_up(off + P * R.S * BATCH_TILE * d->d * 4, 256);
+  R.zcat = off;   off = round_up(off + P * BATCH_TILE * std::max(d->rank, 1) * 2 * 2, 256);
   R.end = off;
   return R;
 }
@@ -180,6 +181,7 @@ struct DenseBufs {
   int* ucnt;
   int* uidx;
   float* mpart;
+  _Float16* zcat;
   int passes, S;
 };
 
@@ -196,6 +198,7 @@ DenseBufs dense_bufs(char* ws, const ffn_plan* p) {
   b.ucnt = reinterpret_cast<int*>(ws + R.ucnt);
   b.uidx = reinterpret_cast<int*>(ws + R.uidx);
   b.mpart = reinterpret_cast<float*>(ws + R.mpart);
+  b.zcat = reinterpret_cast<_Float16*>(ws + R.zcat);
   b.passes = R.passes;
   b.S = R.S;
   return b;
@@ -828,6 +831,10 @@ namespace {
 // bitmaps first (predictor or caller masks, 32 tokens per pass), then the rows run as dense
 // GEMMs (DENSE), as sparse passes (SPARSE), or as whichever the device picks from the union
 // density of the whole call (AUTO: both are enqueued, each gated on the device flag).
+// Calls of at least this many tokens run predictor stage 2 as one GEMM (launch_dense_scores)
+// instead of the batched kernels' per-pass products.
+constexpr int SCORE_GEMM_MIN = 128;
+
 ffn_status run_large(ffn_plan* p, const void* x, int32_t B, float* y, const uint8_t* mask,
                      int32_t* idx, int32_t* cnt, float* scores, int32_t path, hipStream_t st,
                      bool dense_only) {
@@ -863,8 +870,29 @@ ffn_status run_large(ffn_plan* p, const void* x, int32_t B, float* y, const uint
   a.ubits_ps = (size_t)W;
   a.uidx_ps = (size_t)D.ffn;
   a.ypart_ps = (size_t)db.S * BATCH_TILE * D.d;
-  if (sets && (e = launch_batch_sets(a, mask == nullptr, st, P)) != hipSuccess)
+  if (sets && !mask && B >= SCORE_GEMM_MIN && D.rank % 32 == 0) {
+    // many tokens: predictor stage 2 as one GEMM on the matrix cores (z as [B][2 rank], hi then
+    // lo, against P2 twice), its epilogue writing the bitmap and union words
+    a.zcat = db.zcat;
+    if ((e = launch_batch_stage1(a, st, P)) != hipSuccess) return hip_fail(e, "stage-1 launch");
+    DenseArgs sa{};
+    sa.x = db.zcat;
+    sa.w_up = p->w.p2;
+    sa.M = B;
+    sa.d = 2 * D.rank;
+    sa.ffn = D.ffn;
+    sa.c2 = p->w.c2;
+    sa.thr = p->thr;
+    sa.bits_out = db.bits;
+    sa.ubits_out = db.ubits;
+    sa.scores = scores;
+    sa.head_words = p->head_words;
+    sa.b_rowb = (size_t)D.rank * 2;
+    sa.bwrap = D.rank / 32;
+    if ((e = launch_dense_scores(sa, st)) != hipSuccess) return hip_fail(e, "score launch");
+  } else if (sets && (e = launch_batch_sets(a, mask == nullptr, st, P)) != hipSuccess) {
     return hip_fail(e, "active-set launch");
+  }
   const int* flag = nullptr;
   if (path == FFN_PATH_AUTO) {
     float rho = 1.0f;

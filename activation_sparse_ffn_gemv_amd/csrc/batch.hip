@@ -161,6 +161,13 @@ __global__ __launch_bounds__(256) void k_bzr(BatchArgs a) {
   const _Float16 lo = (_Float16)(z - (float)hi);
   a.zhl[e] = hi;
   a.zhl[(size_t)MB * a.r + e] = lo;
+  const int m = e / a.r;                                 // token of the pass
+  if (a.zcat && m < a.B) {
+    // the call's token (pass offset applied to x above): row of [hi | lo]
+    const size_t row = (size_t)blockIdx.z * MB + m;
+    a.zcat[row * 2 * a.r + k] = hi;
+    a.zcat[row * 2 * a.r + a.r + k] = lo;
+  }
 }
 
 // Predictor stage 2 for 128 neurons (four bitmap words per token) per workgroup:
@@ -757,6 +764,12 @@ hipError_t launch_batch_sets(const BatchArgs& a, int use_predictor, hipStream_t 
   } else {
     hipLaunchKernelGGL(k_bmask, dim3((W + 255) / 256, 1, passes), dim3(256), 0, st, a);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_batch_stage1(const BatchArgs& a, hipStream_t st, int passes) {
+  hipLaunchKernelGGL(k_bz, dim3((a.r + 31) / 32 * a.ks * passes), dim3(BT), 0, st, a);
+  hipLaunchKernelGGL(k_bzr, dim3((MB * a.r + 255) / 256, 1, passes), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

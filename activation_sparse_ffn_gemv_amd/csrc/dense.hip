@@ -256,8 +256,13 @@ __device__ __forceinline__ int wave_uniform(int v) { return __builtin_amdgcn_rea
 template <int MASK, int N>
 __device__ __forceinline__ void sched_group() { __builtin_amdgcn_sched_group_barrier(MASK, N, 0); }
 
-template <bool GATE>
+// EPI 0: the FFN's up projection (h = act, masked, to H).  EPI 1: predictor stage 2 of a
+// large call (scores against the threshold into bitmap and union words; GATE false).
+constexpr int EPI_FFN = 0, EPI_SCORE = 1;
+
+template <bool GATE, int EPI = EPI_FFN>
 __global__ __launch_bounds__(UP_T) void k_dupq(DenseArgs a) {
+  static_assert(EPI == EPI_FFN || !GATE, "scores have no gate rows");
   constexpr int NMAT = GATE ? 2 : 1;
   constexpr int UP_N = GATE ? 128 : 256;   // neurons per tile
   constexpr int BROWS = UP_N * NMAT;       // weight rows per stage (up rows, then gate rows)
@@ -300,17 +305,21 @@ __global__ __launch_bounds__(UP_T) void k_dupq(DenseArgs a) {
   for (int i = 0; i < BI; ++i) {
     const int row = (wave * BI + i) * 16 + (lane >> 2);
     const int mat = row / UP_N, n = min(n0 + row % UP_N, a.ffn - 1);
-    bsrc[i] = static_cast<const char*>(mat == 0 ? a.w_up : a.w_gate) + (size_t)n * rowb +
+    bsrc[i] = static_cast<const char*>(mat == 0 ? a.w_up : a.w_gate) +
+              (size_t)n * (EPI == EPI_SCORE ? a.b_rowb : rowb) +
               (size_t)(pos ^ ((row >> 2) & 3)) * 16;
   }
   auto copy = [&](int st, u32x4* dA, u32x4* dB) {   // stage st (clamped) into a ring slot
-    const size_t kb = (size_t)min(st, nst - 1) * UQ_DK * 16;
+    const int sc = min(st, nst - 1);
+    const size_t kb = (size_t)sc * UQ_DK * 16;
+    // the score GEMM's B operand repeats its K (the hi, then the lo half of z meet P2 again)
+    const size_t kbb = EPI == EPI_SCORE ? (size_t)(sc % a.bwrap) * UQ_DK * 16 : kb;
 #pragma unroll
     for (int i = 0; i < AI; ++i)
       lds_copy16(asrc[i] + kb, dA + (wave * AI + i) * 64);
 #pragma unroll
     for (int i = 0; i < BI; ++i)
-      lds_copy16(bsrc[i] + kb, dB + (wave * BI + i) * 64);
+      lds_copy16(bsrc[i] + kbb, dB + (wave * BI + i) * 64);
   };
   constexpr int PER_STAGE = AI + BI;       // copy instructions per wave and stage
 
@@ -382,6 +391,44 @@ __global__ __launch_bounds__(UP_T) void k_dupq(DenseArgs a) {
   // are reused for the bitmap words
   wait_counts<0, 0>();
   __syncthreads();
+
+  if constexpr (EPI == EPI_SCORE) {
+    // s = acc + c2; a neuron is on iff s > logit(tau) (hot-head words: always, unscored).
+    // Accumulator element i of a lane holds token row 8 (i / 4) + 4 (lane / 32) + i % 4 of the
+    // wave's 32-row block and neuron (lane % 32) of its 32-neuron block, so a ballot over the
+    // wave gives the bitmap word of two token rows; the OR over the block's 16 elements is the
+    // union word of the block's 32 tokens (one pass).
+    const int W = a.ffn / 32;
+#pragma unroll
+    for (int ns = 0; ns < NSUB; ++ns) {
+      const int nb32 = n0 + wn * (UP_N / 2) + ns * 32;    // the block's first neuron
+      if (nb32 >= a.ffn) continue;                        // uniform: ffn % 32 == 0
+      const int word = nb32 / 32, n = nb32 + r32;
+      const bool head = word < a.head_words;
+      const float c2v = a.c2 ? a.c2[n] : 0.0f;
+#pragma unroll
+      for (int ms = 0; ms < 2; ++ms) {
+        const int mb = m0 + wm * 64 + ms * 32;            // the block's first token (a pass)
+        if (mb >= a.M) continue;                          // uniform
+        uint32_t uw = 0u;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int m = mb + acc_row(i, lane);
+          const float s = acc[ms][ns][0][i] + c2v;
+          const bool on = m < a.M && (head || s > a.thr);
+          if (a.scores && !head && m < a.M) a.scores[(size_t)m * a.ffn + n] = s;
+          const unsigned long long bal = __ballot(on);
+          const int mr = mb + 8 * (i >> 2) + (i & 3);     // lanes 0..31: row mr; 32..63: mr + 4
+          if (lane == 0 && mr < a.M) a.bits_out[(size_t)mr * W + word] = (uint32_t)bal;
+          if (lane == 32 && mr + 4 < a.M)
+            a.bits_out[(size_t)(mr + 4) * W + word] = (uint32_t)(bal >> 32);
+          uw |= (uint32_t)bal | (uint32_t)(bal >> 32);
+        }
+        if (lane == 0) a.ubits_out[(size_t)(mb / 32) * W + word] = uw;
+      }
+    }
+    return;
+  }
 
   constexpr int TW = UP_N / 32;                         // bitmap words per token row
   uint32_t* s_bits = reinterpret_cast<uint32_t*>(&sA0[0]);
@@ -601,6 +648,13 @@ int dense_ks(int M, int d, int ffn) {
   // two workgroups per CU (the kernel's occupancy): split ffn until the grid reaches 512
   const int ks = std::max(1, std::min({8, (512 + tiles - 1) / tiles, ffn / DD_K}));
   return ks;
+}
+
+hipError_t launch_dense_scores(const DenseArgs& a, hipStream_t st) {
+  if (a.d % (8 * UQ_DK) || a.bwrap < 1 || a.has_gate) return hipErrorInvalidValue;
+  const int t = ((a.M + UP_M - 1) / UP_M) * ((a.ffn + 255) / 256);
+  hipLaunchKernelGGL((k_dupq<false, EPI_SCORE>), dim3(8 * ((t + 7) / 8)), dim3(UP_T), 0, st, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_dense(const DenseArgs& a, hipStream_t st, hipEvent_t (*ev)[2]) {

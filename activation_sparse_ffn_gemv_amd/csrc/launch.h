@@ -185,6 +185,8 @@ struct BatchArgs {
   const int* run_if;          // device flag: the row kernels run only if *run_if == run_want
   int run_want;               //   (nullptr: always)
   int head_words;             // hot head (as PredArgs)
+  _Float16* zcat;             // k_bzr: also z as [tokens][2 r] (hi then lo) for the stage-2 GEMM,
+                              //   or nullptr
   // Several passes in one launch (grid.z = pass p, tokens [32p, 32p + 32) of the call): every
   // per-token pointer above advances by 32 tokens per pass, the per-pass buffers by the strides
   // below (elements), and B = min(32, Btot - 32p).  One pass: Btot = 0 and the strides unused.
@@ -205,6 +207,8 @@ hipError_t launch_batch(const BatchArgs& a, int use_predictor, int choose_path, 
 // The pieces: the pass's active sets (bits, scores, union) ...
 hipError_t launch_batch_sets(const BatchArgs& a, int use_predictor, hipStream_t st,
                              int passes = 1);
+// ... or only predictor stage 1 (z, and z as [tokens][2 r] when a.zcat is set) ...
+hipError_t launch_batch_stage1(const BatchArgs& a, hipStream_t st, int passes);
 // ... the union recomputed from bits (when bits were written by an earlier step) ...
 hipError_t launch_batch_union(const BatchArgs& a, hipStream_t st);
 // ... and the rows (optional k_bpath, k_bug, k_bdown, k_bred).
@@ -233,8 +237,22 @@ struct DenseArgs {
   int M, d, ffn, act, has_gate, ks;
   const int* run_if;          // device flag: run only if *run_if == run_want (nullptr: always)
   int run_want;
+  // predictor stage 2 of a large call on the same GEMM kernel (launch_dense_scores):
+  // S = [z_hi | z_lo] [P2 | P2]^T + c2 with x = [M][2 rank] fp16 (d = 2 rank), w_up = P2 (rows of
+  // b_rowb bytes, its K repeating after bwrap stages), ffn = neurons; each token's bitmap words,
+  // each pass's (32 tokens') union words and, optionally, the scores are written
+  const float* c2;
+  float thr;
+  uint32_t* bits_out;         // [M][ffn/32]
+  uint32_t* ubits_out;        // [passes][ffn/32]
+  float* scores;              // [M][ffn] or nullptr
+  int head_words;             // words [0, head_words): every neuron on, no score
+  size_t b_rowb;
+  int bwrap;
 };
 int dense_ks(int M, int d, int ffn);
+// Predictor stage 2 of a call of many tokens as one GEMM (fields above); rank % 32 == 0.
+hipError_t launch_dense_scores(const DenseArgs& a, hipStream_t st);
 // ev: three (start, stop) pairs for k_dup, k_ddown, k_dred (entries may be null), or nullptr
 hipError_t launch_dense(const DenseArgs& a, hipStream_t st, hipEvent_t (*ev)[2]);
 
