@@ -56,6 +56,19 @@ def _check(ffn, cfg, B, tokens=None, layer_dev="cuda"):
     return y, lists, len(union)
 
 
+@pytest.mark.parametrize("kw,B", [
+    (dict(d=1024, ffn=4128, rank=128, act="reglu", bias_gate=True), 128),
+    (dict(d=512, ffn=2048, rank=64, act="relu", bias_up=True, bias_down=True), 300),
+    (dict(d=1024, ffn=1120, rank=96, act="drelu", bias_gate=True, bias_up=True), 161),
+], ids=["reglu_f4128_B128", "relu_B300", "drelu_f1120_B161"])
+def test_large_call_scores_on_the_matrix_cores(ffn, kw, B):
+    """Calls of 128+ tokens compute predictor stage 2 as one GEMM whose epilogue writes the
+    bitmap and union words: sets, scores and y against the oracle, with a last 256-neuron tile
+    cut short (ffn 4128, 1120) and a short last pass of 32 tokens (300, 161)."""
+    cfg = synth.small_config(w_dtype="f16", x_dtype="f16", p_dtype="f16", density=0.1, **kw)
+    _check(ffn, cfg, B, tokens=[0, 1, 31, 32, 100, B - 2, B - 1])
+
+
 BATCH_SHAPES = [
     dict(d=512, ffn=2048, rank=64, act="relu", bias_up=True, bias_down=True),
     dict(d=1024, ffn=4128, rank=128, act="reglu", bias_gate=True),

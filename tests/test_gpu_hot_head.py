@@ -104,6 +104,9 @@ def test_hot_head_dense_and_auto(ffn):
                              x_dtype="f16", p_dtype="f16", density=0.1, bias_up=True)
     _check(ffn, cfg, 128, n_tokens=70, path=ffn.FFN_PATH_DENSE, tokens=[0, 33, 69])
     _check(ffn, cfg, 128, n_tokens=70, path=ffn.FFN_PATH_AUTO, tokens=[0, 33, 69])
+    # 128+ tokens: the head's words come from the score GEMM's epilogue
+    _check(ffn, cfg, 128, n_tokens=130, path=ffn.FFN_PATH_AUTO, tokens=[0, 64, 129])
+    _check(ffn, cfg, 128, n_tokens=130, tokens=[0, 64, 129])      # sparse: head scores untouched
 
 
 def test_caller_mask_ignores_the_head(ffn):
