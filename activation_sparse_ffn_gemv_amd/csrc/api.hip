@@ -87,7 +87,10 @@ DenseRegion dense_region(const ffn_layer_desc* d, size_t base) {
   R.flag = off;   off = round_up(off + 4, 256);
   R.H = off;      off = round_up(off + P * BATCH_TILE * d->ffn * 2, 256);
   R.ypart = off;  off = round_up(off + dense_rows_for(d) * d->d * 4, 256);
-  R.zpart = off;  off = round_up(off + P * s.zpart_bytes, 256);
+  // (stage-1 partials of either the batched kernels or the stage-1 GEMM's K slices)
+  R.zpart = off;
+  off = round_up(off + P * std::max(s.zpart_bytes, (size_t)ZPART_MAX_KS * BATCH_TILE *
+                                                       std::max(d->rank, 1) * 4), 256);
   R.zhl = off;    off = round_up(off + P * s.zhl_bytes, 256);
   R.ubits = off;  off = round_up(off + P * W * 4, 256);
   R.ucnt = off;   off = round_up(off + P * 4, 256);
@@ -874,7 +877,25 @@ ffn_status run_large(ffn_plan* p, const void* x, int32_t B, float* y, const uint
     // many tokens: predictor stage 2 as one GEMM on the matrix cores (z as [B][2 rank], hi then
     // lo, against P2 twice), its epilogue writing the bitmap and union words
     a.zcat = db.zcat;
-    if ((e = launch_batch_stage1(a, st, P)) != hipSuccess) return hip_fail(e, "stage-1 launch");
+    if (D.d % 32 == 0) {
+      // stage 1 as a GEMM too, split over d; the batched path's fixed-order sum adds the slices
+      DenseArgs za{};
+      za.x = x;
+      za.w_up = p->w.p1;
+      za.M = B;
+      za.d = D.d;
+      za.ffn = D.rank;
+      za.kslices = zpart_kslices(B, D.d, D.rank);
+      za.zpart_out = db.zpart;
+      za.zpart_ps = (size_t)za.kslices * BATCH_TILE * D.rank;
+      a.ks = za.kslices;
+      a.zpart_ps = za.zpart_ps;
+      if ((e = launch_dense_zpart(za, st)) != hipSuccess ||
+          (e = launch_batch_zsum(a, st, P)) != hipSuccess)
+        return hip_fail(e, "stage-1 launch");
+    } else if ((e = launch_batch_stage1(a, st, P)) != hipSuccess) {
+      return hip_fail(e, "stage-1 launch");
+    }
     DenseArgs sa{};
     sa.x = db.zcat;
     sa.w_up = p->w.p2;

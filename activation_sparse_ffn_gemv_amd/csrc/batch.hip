@@ -773,6 +773,11 @@ hipError_t launch_batch_stage1(const BatchArgs& a, hipStream_t st, int passes) {
   return hipGetLastError();
 }
 
+hipError_t launch_batch_zsum(const BatchArgs& a, hipStream_t st, int passes) {
+  hipLaunchKernelGGL(k_bzr, dim3((MB * a.r + 255) / 256, 1, passes), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_batch_union(const BatchArgs& a, hipStream_t st) {
   hipLaunchKernelGGL(k_bunion, dim3((a.ffn / 32 + 255) / 256), dim3(256), 0, st, a);
   return hipGetLastError();

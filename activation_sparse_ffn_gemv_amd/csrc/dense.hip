@@ -257,12 +257,15 @@ template <int MASK, int N>
 __device__ __forceinline__ void sched_group() { __builtin_amdgcn_sched_group_barrier(MASK, N, 0); }
 
 // EPI 0: the FFN's up projection (h = act, masked, to H).  EPI 1: predictor stage 2 of a
-// large call (scores against the threshold into bitmap and union words; GATE false).
-constexpr int EPI_FFN = 0, EPI_SCORE = 1;
+// large call (scores against the threshold into bitmap and union words; GATE false).  EPI 2:
+// predictor stage 1 of a large call, split over K (a.kslices slices of d): each slice's fp32
+// partial of Z = X P1^T, in the per-pass layout [pass][slice][32 tokens][rank] that the batched
+// path's fixed-order sum (k_bzr) reads.
+constexpr int EPI_FFN = 0, EPI_SCORE = 1, EPI_ZPART = 2;
 
 template <bool GATE, int EPI = EPI_FFN>
 __global__ __launch_bounds__(UP_T) void k_dupq(DenseArgs a) {
-  static_assert(EPI == EPI_FFN || !GATE, "scores have no gate rows");
+  static_assert(EPI == EPI_FFN || !GATE, "the predictor GEMMs have no gate rows");
   constexpr int NMAT = GATE ? 2 : 1;
   constexpr int UP_N = GATE ? 128 : 256;   // neurons per tile
   constexpr int BROWS = UP_N * NMAT;       // weight rows per stage (up rows, then gate rows)
@@ -280,14 +283,19 @@ __global__ __launch_bounds__(UP_T) void k_dupq(DenseArgs a) {
   static_assert(UQ_NS == 4, "four ring slots");
   if (a.run_if && *a.run_if != a.run_want) return;
   const int nb_m = (a.M + UP_M - 1) / UP_M, nb_n = (a.ffn + UP_N - 1) / UP_N;
-  const int tile = xcd_tile(nb_m * nb_n);
-  if (tile >= nb_m * nb_n) return;
-  const int m0 = (tile % nb_m) * UP_M, n0 = (tile / nb_m) * UP_N;
+  const int nks = EPI == EPI_ZPART ? a.kslices : 1;
+  const int tile = xcd_tile(nb_m * nb_n * nks);
+  if (tile >= nb_m * nb_n * nks) return;
+  const int m0 = (tile % nb_m) * UP_M, n0 = (tile / nb_m % nb_n) * UP_N;
+  const int kslice = tile / (nb_m * nb_n);
   const int tid = threadIdx.x, lane = tid & (WAVE - 1);
   const int wave = wave_uniform(tid / WAVE);             // scalar: the copies' LDS base
   const int r32 = lane & 31, g = lane >> 5;
   const int wm = wave >> 1, wn = wave & 1;
-  const int nchk = a.d / 8, nst = nchk / UQ_DK;
+  const int nchk = a.d / 8, nst_all = nchk / UQ_DK;
+  // this workgroup's K stages: all of them, or its slice's [sbase, sbase + nst)
+  const int sbase = (int)((long long)nst_all * kslice / nks);
+  const int nst = (int)((long long)nst_all * (kslice + 1) / nks) - sbase;
   const size_t rowb = (size_t)nchk * 16;
 
   // copy sources: instruction i of this wave covers rows 16 (wave * AI + i) .. +15 of the tile,
@@ -310,7 +318,7 @@ __global__ __launch_bounds__(UP_T) void k_dupq(DenseArgs a) {
               (size_t)(pos ^ ((row >> 2) & 3)) * 16;
   }
   auto copy = [&](int st, u32x4* dA, u32x4* dB) {   // stage st (clamped) into a ring slot
-    const int sc = min(st, nst - 1);
+    const int sc = sbase + min(st, nst - 1);
     const size_t kb = (size_t)sc * UQ_DK * 16;
     // the score GEMM's B operand repeats its K (the hi, then the lo half of z meet P2 again)
     const size_t kbb = EPI == EPI_SCORE ? (size_t)(sc % a.bwrap) * UQ_DK * 16 : kb;
@@ -391,6 +399,24 @@ __global__ __launch_bounds__(UP_T) void k_dupq(DenseArgs a) {
   // are reused for the bitmap words
   wait_counts<0, 0>();
   __syncthreads();
+
+  if constexpr (EPI == EPI_ZPART) {
+    const int N = a.ffn;                                  // the rank
+#pragma unroll
+    for (int ns = 0; ns < NSUB; ++ns) {
+      const int n = n0 + wn * (UP_N / 2) + ns * 32 + r32;
+#pragma unroll
+      for (int ms = 0; ms < 2; ++ms)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int m = m0 + wm * 64 + ms * 32 + acc_row(i, lane);
+          if (m < a.M && n < N)
+            a.zpart_out[(size_t)(m / 32) * a.zpart_ps + ((size_t)kslice * 32 + m % 32) * N + n] =
+                acc[ms][ns][0][i];
+        }
+    }
+    return;
+  }
 
   if constexpr (EPI == EPI_SCORE) {
     // s = acc + c2; a neuron is on iff s > logit(tau) (hot-head words: always, unscored).
@@ -648,6 +674,19 @@ int dense_ks(int M, int d, int ffn) {
   // two workgroups per CU (the kernel's occupancy): split ffn until the grid reaches 512
   const int ks = std::max(1, std::min({8, (512 + tiles - 1) / tiles, ffn / DD_K}));
   return ks;
+}
+
+hipError_t launch_dense_zpart(const DenseArgs& a, hipStream_t st) {
+  if (a.d % (8 * UQ_DK) || a.kslices < 1 || a.kslices > a.d / (8 * UQ_DK) || a.has_gate)
+    return hipErrorInvalidValue;
+  const int t = ((a.M + UP_M - 1) / UP_M) * ((a.ffn + 255) / 256) * a.kslices;
+  hipLaunchKernelGGL((k_dupq<false, EPI_ZPART>), dim3(8 * ((t + 7) / 8)), dim3(UP_T), 0, st, a);
+  return hipGetLastError();
+}
+
+int zpart_kslices(int M, int d, int rank) {
+  const int tiles = ((M + UP_M - 1) / UP_M) * ((rank + 255) / 256);
+  return std::max(1, std::min({ZPART_MAX_KS, (256 + tiles - 1) / tiles, d / (8 * UQ_DK)}));
 }
 
 hipError_t launch_dense_scores(const DenseArgs& a, hipStream_t st) {

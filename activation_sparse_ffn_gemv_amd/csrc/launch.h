@@ -209,6 +209,8 @@ hipError_t launch_batch_sets(const BatchArgs& a, int use_predictor, hipStream_t 
                              int passes = 1);
 // ... or only predictor stage 1 (z, and z as [tokens][2 r] when a.zcat is set) ...
 hipError_t launch_batch_stage1(const BatchArgs& a, hipStream_t st, int passes);
+// ... or only the fixed-order sum of stage 1's a.ks K-slice partials (k_bzr) ...
+hipError_t launch_batch_zsum(const BatchArgs& a, hipStream_t st, int passes);
 // ... the union recomputed from bits (when bits were written by an earlier step) ...
 hipError_t launch_batch_union(const BatchArgs& a, hipStream_t st);
 // ... and the rows (optional k_bpath, k_bug, k_bdown, k_bred).
@@ -249,8 +251,18 @@ struct DenseArgs {
   int head_words;             // words [0, head_words): every neuron on, no score
   size_t b_rowb;
   int bwrap;
+  // predictor stage 1 of a large call on the same GEMM kernel (launch_dense_zpart): Z = X P1^T
+  // with x = X, w_up = P1, ffn = rank, split over d into kslices slices; the fp32 partials go to
+  // zpart_out in the batched path's per-pass layout ([pass][slice][32][rank], zpart_ps per pass)
+  float* zpart_out;
+  size_t zpart_ps;
+  int kslices;
 };
 int dense_ks(int M, int d, int ffn);
+// K slices of the stage-1 GEMM for a call of M tokens (at most ZPART_MAX_KS).
+constexpr int ZPART_MAX_KS = 32;
+int zpart_kslices(int M, int d, int rank);
+hipError_t launch_dense_zpart(const DenseArgs& a, hipStream_t st);
 // Predictor stage 2 of a call of many tokens as one GEMM (fields above); rank % 32 == 0.
 hipError_t launch_dense_scores(const DenseArgs& a, hipStream_t st);
 // ev: three (start, stop) pairs for k_dup, k_ddown, k_dred (entries may be null), or nullptr
