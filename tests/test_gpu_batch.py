@@ -153,9 +153,8 @@ def test_falcon_40b_shape_batched(ffn, B):
                                       ("i4g32", "drelu", 256)])
 def test_dense_forward_is_the_dense_ffn(ffn, wd, act, d, B):
     """fp16 with 64 tokens or more runs the two MFMA GEMMs (ragged token, K and column tiles
-    here), fewer tokens the batched kernels over every neuron."""
-    if wd != "f16" and B > 40:
-        pytest.skip("fp32 / int4 dense runs token by token: covered by the smaller batches")
+    here), fewer tokens the batched kernels over every neuron; fp32 and int4 layers run every
+    token through the batch-1 kernels over every neuron."""
     xd = "f32" if wd == "f32" else "f16"
     cfg = synth.small_config(d=d, ffn=1056, rank=32, act=act, w_dtype=wd, x_dtype=xd,
                              p_dtype=xd, density=0.1, bias_up=True, bias_gate=True,
