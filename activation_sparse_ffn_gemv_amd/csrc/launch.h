@@ -34,8 +34,9 @@ struct RouterArgs {
   ExpertW* slots;             // [B][K] out
   int d, E, K, x_f16;
   ExpertTable tab;
-  // predictor stage 1 of every expert, computed in the router's launch (the chosen experts are
-  // not known yet): zall[(b * E + e) * rank + k] = c1_e[k] + P1_e[k] . x_b
+  // predictor stage 1 of the chosen experts, computed in the router's launch (each stage-1
+  // workgroup reaches its token's routing decision itself): zall[(b * E + e) * rank + k] =
+  // c1_e[k] + P1_e[k] . x_b for the K experts e chosen for token b (the other rows untouched)
   float* zall;
   int rank, cpl, B;
 };

@@ -19,20 +19,19 @@ constexpr int RT_NW = RT_THREADS / WAVE;
 constexpr int RT_EPW = (MOE_MAX_E + RT_NW - 1) / RT_NW;   // experts per wave
 constexpr int RT_CPL = 8;                                  // chunks per lane in flight
 
+// Logits of token b over every expert (into s_logit) and its top-K (repeated arg-max over the
+// experts not yet taken, strict >: ties keep the lower index) into ids[0, K) of every thread.
+// Wave w takes experts w, w + RT_NW, ...; lanes split the rows in 16-byte chunks, and a lane's
+// chunks of the token and of its rows are requested together (one round trip at d = 4096 fp16).  Every workgroup that needs the decision
+// runs this same code on the same data, so all of them reach the same experts.
 template <int XK>
-__device__ __forceinline__ void route_token(const RouterArgs& a, int b) {
+__device__ __forceinline__ void route_decide(const RouterArgs& a, int b, float* s_logit,
+                                             int (&ids)[MOE_MAX_K]) {
   constexpr int EPC = Kind<XK>::EPC;
-  __shared__ float s_logit[MOE_MAX_E];
-  __shared__ int s_ids[MOE_MAX_K];
-  __shared__ float s_w[MOE_MAX_K];
   const int tid = threadIdx.x, lane = tid & (WAVE - 1), wave = tid / WAVE;
   const int nch = a.d / EPC;
   const char* xb = static_cast<const char*>(a.x) + (size_t)b * nch * 16;
   const char* R = static_cast<const char*>(a.R);
-
-  // logits: wave w takes experts w and w + RT_NW; lanes split the rows in 16-byte chunks, and a
-  // lane's chunks of the token and of both rows are requested together (one round trip at
-  // d = 4096 fp16)
   float acc[RT_EPW] = {};
   for (int c0 = 0; c0 < nch; c0 += RT_CPL * WAVE) {
     u32x4 xv[RT_CPL], w[RT_EPW][RT_CPL];
@@ -42,8 +41,8 @@ __device__ __forceinline__ void route_token(const RouterArgs& a, int b) {
       xv[k] = ld16(xb + (size_t)c * 16);
 #pragma unroll
       for (int j = 0; j < RT_EPW; ++j) {
-        const int e = min(wave + j * RT_NW, a.E - 1);
-        w[j][k] = ld16(R + ((size_t)e * nch + c) * 16);
+        const int e = wave + j * RT_NW;
+        w[j][k] = e < a.E ? ld16(R + ((size_t)e * nch + c) * 16) : u32x4{0u, 0u, 0u, 0u};
       }
     }
     issue_fence();
@@ -64,25 +63,52 @@ __device__ __forceinline__ void route_token(const RouterArgs& a, int b) {
     if (lane == 0 && wave + j * RT_NW < a.E) s_logit[wave + j * RT_NW] = l;
   }
   __syncthreads();
-
-  if (tid == 0) {
-    // top-K by repeated arg-max over the experts not yet taken (strict >: ties keep the lower
-    // index), then the softmax over the chosen logits (the first is the largest)
-    unsigned taken = 0u;
-    for (int t = 0; t < a.K; ++t) {
-      int best = -1;
-      for (int e = 0; e < a.E; ++e)
-        if (!(taken >> e & 1u) && (best < 0 || s_logit[e] > s_logit[best])) best = e;
-      taken |= 1u << best;
-      s_ids[t] = best;
+  // every thread takes the top-K from the E logits itself (the same comparisons everywhere): no
+  // serial step on one thread and no second barrier
+  float lg[MOE_MAX_E];
+#pragma unroll
+  for (int e = 0; e < MOE_MAX_E; ++e) lg[e] = e < a.E ? s_logit[e] : 0.0f;
+  unsigned taken = 0u;
+#pragma unroll
+  for (int t = 0; t < MOE_MAX_K; ++t) {
+    float bv = 0.0f;
+    int bi = -1;
+#pragma unroll
+    for (int e = 0; e < MOE_MAX_E; ++e)
+      if (e < a.E && !(taken >> e & 1u) && (bi < 0 || lg[e] > bv)) {
+        bv = lg[e];
+        bi = e;
+      }
+    if (t < a.K) {
+      taken |= 1u << bi;
+      ids[t] = bi;
     }
-    const float mx = s_logit[s_ids[0]];
+  }
+}
+
+template <int XK>
+__device__ __forceinline__ void route_token(const RouterArgs& a, int b) {
+  __shared__ float s_logit[MOE_MAX_E];
+  __shared__ int s_ids[MOE_MAX_K];
+  __shared__ float s_w[MOE_MAX_K];
+  const int tid = threadIdx.x;
+  int ids[MOE_MAX_K];
+  route_decide<XK>(a, b, s_logit, ids);
+  if (tid == 0) {
+    // the softmax over the chosen logits (the first is the largest)
+    const float mx = s_logit[ids[0]];
     float den = 0.0f;
-    for (int t = 0; t < a.K; ++t) den += expf(s_logit[s_ids[t]] - mx);
-    for (int t = 0; t < a.K; ++t) {
-      s_w[t] = expf(s_logit[s_ids[t]] - mx) / den;
-      if (a.ids_out) a.ids_out[b * a.K + t] = s_ids[t];
-      if (a.w_out) a.w_out[b * a.K + t] = s_w[t];
+#pragma unroll
+    for (int t = 0; t < MOE_MAX_K; ++t)
+      if (t < a.K) den += expf(s_logit[ids[t]] - mx);
+#pragma unroll
+    for (int t = 0; t < MOE_MAX_K; ++t) {
+      if (t < a.K) {
+        s_ids[t] = ids[t];
+        s_w[t] = expf(s_logit[ids[t]] - mx) / den;
+        if (a.ids_out) a.ids_out[b * a.K + t] = ids[t];
+        if (a.w_out) a.w_out[b * a.K + t] = s_w[t];
+      }
     }
   }
   __syncthreads();
@@ -102,35 +128,47 @@ __device__ __forceinline__ void route_token(const RouterArgs& a, int b) {
   }
 }
 
-// Router and predictor stage 1 of every expert in one launch.  Blocks [0, B) route token b
-// (above); each further block runs eight P1 rows, a wave per row (token b, expert e, row k of
-// the flattened (b, e, k) order): 16-byte chunks per lane, all loads issued before use, wave sum.
-// Computing stage 1 for the experts the router is about to drop costs P1 bytes of E instead of
-// top_k experts, but takes the routing decision off the path to the predictor's second stage.
+// Router and predictor stage 1 of the chosen experts in one launch.  Blocks [0, B) route token b
+// (above) and write its slot records; each further block runs eight P1 rows of one token's chosen
+// experts, a wave per row (rows in (token b, slot t, row k) order; rank is a multiple of eight, so
+// a block's rows share the token and the slot).  Such a block first reaches the token's routing
+// decision itself (the same code as the routing block, so the same experts), then reads the P1
+// rows of the experts chosen and no others: 16-byte chunks per lane, all loads issued before use,
+// wave sum.  The rows land at zall[(b * E + e) * rank + k], where the stage-2 kernels look for
+// the slot's expert e.
 template <int XK, int CPL>
 __global__ __launch_bounds__(RT_THREADS) void k_route_z(RouterArgs a) {
   if ((int)blockIdx.x < a.B) {
     route_token<XK>(a, blockIdx.x);
     return;
   }
+  __shared__ float s_logit[MOE_MAX_E];
   const int lane = threadIdx.x & (WAVE - 1), wave = threadIdx.x / WAVE;
   const int q = ((int)blockIdx.x - a.B) * RT_NW + wave;
-  if (q >= a.B * a.E * a.rank) return;                // whole waves
-  const int k = q % a.rank, e = (q / a.rank) % a.E, b = q / (a.rank * a.E);
+  const int b = (((int)blockIdx.x - a.B) * RT_NW) / (a.K * a.rank);
   const int nch = a.d / Kind<XK>::EPC;
   XRegs<XK, CPL> xr;
   load_x<XK, CPL>(xr, static_cast<const char*>(a.x) + (size_t)b * nch * 16, nch, lane);
+  int ids[MOE_MAX_K];
+  route_decide<XK>(a, b, s_logit, ids);
+  const int k = q % a.rank, t = (q / a.rank) % a.K;
+  int e = ids[0];
+#pragma unroll
+  for (int j = 1; j < MOE_MAX_K; ++j) e = t == j ? ids[j] : e;
+  e = __builtin_amdgcn_readfirstlane(e);
   u32x4 w[CPL];
   float sc[CPL];
   load_row<XK, CPL>(w, sc, a.tab.e[e].p1, nullptr, k, nch, lane);
   issue_fence();
   finish_x<XK, CPL>(xr, nch, lane);
   const float acc = wave_sum(row_dot<XK, CPL>(w, sc, xr));
-  if (lane == 0) a.zall[q] = acc + (a.tab.e[e].c1 ? a.tab.e[e].c1[k] : 0.0f);
+  if (lane == 0)
+    a.zall[((size_t)b * a.E + e) * a.rank + k] = acc + (a.tab.e[e].c1 ? a.tab.e[e].c1[k] : 0.0f);
 }
 
 hipError_t launch_route_z(const RouterArgs& a, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
-  const dim3 grid(a.B + (a.B * a.E * a.rank + RT_NW - 1) / RT_NW);
+  if (a.rank % RT_NW) return hipErrorInvalidValue;   // a block's rows share one token
+  const dim3 grid(a.B + a.B * a.K * a.rank / RT_NW);
 #define RZ(X, C)                                                                                \
   do {                                                                                        \
     if (ev0 && ev1)                                                                           \
