@@ -100,3 +100,60 @@ def test_static_entry_point_rejects_larger_layers_before_any_launch(ffn):
         ffn.ffn_sparse_forward_static(desc, w, 0x5000, 1, 0x6000)
     assert e.value.status == ffn.FFN_ERR_WORKSPACE_TOO_SMALL
     assert "static scratch" in ffn.ffn_last_error()
+
+
+def test_static_entry_point_in_a_graph(ffn):
+    """Callers under graph capture are the ones this entry point is for: the call is captured
+    once and replayed three times, with eager work and a static call on another layer (which
+    leaves that layer's bytes in the shared scratch) between the replays; every replay equals
+    the eager call bit for bit."""
+    cfg = synth.small_config(d=512, ffn=2048, rank=64, act="reglu", w_dtype="f16",
+                             x_dtype="f16", p_dtype="f16", density=0.1, bias_gate=True,
+                             bias_down=True)
+    other = synth.small_config(d=256, ffn=1024, rank=32, act="relu", w_dtype="f16",
+                               x_dtype="f16", p_dtype="f16", density=0.2, bias_up=True)
+    print("no-alloc graph case: d=%d ffn=%d B=2, other layer d=%d ffn=%d" % (
+        cfg.d, cfg.ffn, other.d, other.ffn), flush=True)
+    m = ffn.SparseFFN(to_device(synth.make_layer(cfg, device="cuda")), max_batch=2)
+    mo = ffn.SparseFFN(to_device(synth.make_layer(other, device="cuda")), max_batch=1)
+    x = synth.make_tokens(cfg, 2, device="cuda")
+    xo = synth.make_tokens(other, 1, device="cuda")
+    y = torch.zeros(2, cfg.d, device="cuda")
+    yo = torch.zeros(1, other.d, device="cuda")
+    idx = torch.zeros(2, cfg.ffn, dtype=torch.int32, device="cuda")
+    cnt = torch.zeros(2, dtype=torch.int32, device="cuda")
+
+    def run():
+        ffn.ffn_sparse_forward_static(m.desc, m.weights, x.data_ptr(), 2, y.data_ptr(), 0,
+                                      idx.data_ptr(), cnt.data_ptr(),
+                                      torch.cuda.current_stream().cuda_stream)
+
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        run()
+    torch.cuda.synchronize()
+    ref = (y.clone(), idx.clone(), cnt.clone())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            run()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        y.fill_(float("nan"))
+        idx.fill_(-1)
+        cnt.fill_(-1)
+        junk = torch.randn(1 << 20, device="cuda").sum()
+        ffn.ffn_sparse_forward_static(mo.desc, mo.weights, xo.data_ptr(), 1, yo.data_ptr(),
+                                      stream=torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, ref[0]), "replay %d: y differs" % rep
+        assert torch.equal(cnt, ref[2]), "replay %d: counts differ" % rep
+        for t in range(2):
+            n = int(ref[2][t])
+            assert torch.equal(idx[t, :n], ref[1][t, :n]), "replay %d: index list differs" % rep
+        del junk
+    del g
+    m.close()
+    mo.close()
