@@ -6,13 +6,14 @@
 // with fp32 accumulation on v_mfma_f32_32x32x16_f16:
 //   k_dup    H = act(X W_up^T + b_up [, X W_gate^T + b_gate]), zeroed where a token's set
 //            (if given) excludes the neuron; H stored fp16, [M][ffn]
-//   k_ddown  Y_k = H[:, K slice k] W_down_t[K slice k, :]     (split over ffn when the tiles
-//            alone do not fill the GPU)
+//   k_ddq / k_ddown  Y_k = H[:, K slice k] W_down_t[K slice k, :]   (split over ffn when the
+//            tiles alone do not fill the GPU; k_ddq with 256-token tiles, k_ddown with 128-token
+//            ones where those pad the tokens less)
 //   k_dred   y = b_down + sum_k Y_k (in slice order)
-// Both GEMMs stage the weight tile in LDS (double-buffered) and read the token-side operand
-// straight into registers; each wave owns 32 tokens.  Tiles are mapped to the eight XCDs so that
-// the M tiles sharing a weight tile run on the same XCD one after another (its L2 serves the
-// repeats).
+// k_dupq and k_ddq copy both operands straight into LDS (global_load_lds_dwordx4, a four-slot
+// ring); k_dup and k_ddown stage the weight tile in LDS from registers and read the token-side
+// operand straight into registers.  Tiles are mapped to the eight XCDs so that the M tiles
+// sharing a weight tile run on the same XCD one after another (its L2 serves the repeats).
 //
 // W_down_t is stored [ffn][d] (d contiguous): for the second GEMM the MFMA needs 8 consecutive
 // ffn values per lane and column, so a lane reads 16-byte pieces of 8 rows (8 columns each) and
@@ -639,6 +640,150 @@ __global__ __launch_bounds__(DT, 2) void k_ddown(DenseArgs a) {
   }
 }
 
+// k_ddq: the down projection with k_dupq's structure: 8 waves, a tile of 256 tokens x 256
+// columns (wave w: tokens 64 (w / 2) .. +63, columns 128 (w % 2) .. +127), K stages of 32 ffn rows
+// copied straight into a four-slot LDS ring by global_load_lds_dwordx4 (H rows swizzled as in
+// k_dupq; W_down_t rows as they are, 512 bytes per row and stage).  The B fragment of a column
+// needs 8 consecutive ffn rows: a lane reads 8 bytes (4 columns) from each of 8 rows and
+// regroups them in registers, so MFMA block b (b = 0..3) holds columns 4p + b of the wave's
+// 128 (p = lane % 32), and each B fragment serves both of the wave's 32-token blocks (12 LDS
+// bytes per lane and MFMA against k_ddown's 16).  Only LDS copies are in flight inside the loop,
+// so the count-based wait covers exactly the copies of the stages it names.
+constexpr int DQ_M = 256, DQ_N = 256;
+
+__global__ __launch_bounds__(UP_T) void k_ddq(DenseArgs a) {
+  constexpr int NW = UP_T / WAVE;                        // 8 waves
+  constexpr int AI = DQ_M / 16 / NW;                     // A copies per wave and stage (2)
+  constexpr int BI = 32 / 2 / NW;                        // B copies (two K rows each) (2)
+  constexpr int PER_STAGE = AI + BI;
+  __shared__ u32x4 sA0[DQ_M * UQ_DK], sA1[DQ_M * UQ_DK], sA2[DQ_M * UQ_DK], sA3[DQ_M * UQ_DK];
+  __shared__ u32x4 sB0[32 * 32], sB1[32 * 32], sB2[32 * 32], sB3[32 * 32];
+  if (a.run_if && *a.run_if != a.run_want) return;
+  const int nb_m = (a.M + DQ_M - 1) / DQ_M, nb_n = (a.d + DQ_N - 1) / DQ_N;
+  const int total = nb_m * nb_n * a.ks;
+  const int tile = xcd_tile(total);
+  if (tile >= total) return;
+  const int m0 = (tile % nb_m) * DQ_M, c0 = (tile / nb_m % nb_n) * DQ_N;
+  const int kslice = tile / (nb_m * nb_n);
+  const int nst_all = a.ffn / 32;
+  const int sbase = (int)((long long)nst_all * kslice / a.ks);
+  const int nst = (int)((long long)nst_all * (kslice + 1) / a.ks) - sbase;
+  const int tid = threadIdx.x, lane = tid & (WAVE - 1);
+  const int wave = wave_uniform(tid / WAVE);
+  const int r32 = lane & 31, g = lane >> 5;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int dch = a.d / 8;
+  const size_t hrow = (size_t)a.ffn * 2;
+
+  const char* asrc[AI];
+  const char* bsrc[BI];
+  const int pos = lane & 3;
+#pragma unroll
+  for (int i = 0; i < AI; ++i) {
+    const int row = (wave * AI + i) * 16 + (lane >> 2);
+    asrc[i] = reinterpret_cast<const char*>(a.H) + (size_t)min(m0 + row, a.M - 1) * hrow +
+              (size_t)(pos ^ ((row >> 2) & 3)) * 16;
+  }
+#pragma unroll
+  for (int i = 0; i < BI; ++i) {
+    const int krow = (wave * BI + i) * 2 + (lane >> 5);
+    bsrc[i] = static_cast<const char*>(a.w_dn) +
+              ((size_t)krow * dch + min(c0 / 8 + (lane & 31), dch - 1)) * 16;
+  }
+  auto copy = [&](int st, u32x4* dA, u32x4* dB) {
+    const int sc = sbase + min(st, nst - 1);
+#pragma unroll
+    for (int i = 0; i < AI; ++i)
+      lds_copy16(asrc[i] + (size_t)sc * 64, dA + (wave * AI + i) * 64);
+#pragma unroll
+    for (int i = 0; i < BI; ++i)
+      lds_copy16(bsrc[i] + (size_t)sc * 32 * dch * 16, dB + (wave * BI + i) * 64);
+  };
+
+  f32x16 acc[2][4];
+#pragma unroll
+  for (int ms = 0; ms < 2; ++ms)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[ms][b] = f32x16{};
+
+  auto frag = [&](const u32x4* base, int row, int c) {
+    return base[row * UQ_DK + (c ^ ((row >> 2) & 3))];
+  };
+  if (nst > 0) {
+    copy(0, sA0, sB0);
+    copy(1, sA1, sB1);
+    copy(2, sA2, sB2);
+    auto step = [&](int st, const u32x4* pa, const u32x4* pb, u32x4* nA, u32x4* nB) {
+      wait_counts<2 * PER_STAGE, 0>();
+      barrier_only();
+      issue_fence();
+      copy(st + 3, nA, nB);
+      issue_fence();
+      const uint2* pb2 = reinterpret_cast<const uint2*>(pb);
+      u32x4 fa[2][2];
+      uint2 r[2][8];
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+        for (int ms = 0; ms < 2; ++ms) fa[kk][ms] = frag(pa, wm * 64 + ms * 32 + r32, 2 * kk + g);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) r[kk][j] = pb2[(16 * kk + 8 * g + j) * 64 + wn * 32 + r32];
+      }
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          u32x4 lo, hi;
+          uint32_t w[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) w[j] = q ? r[kk][j].y : r[kk][j].x;
+          lo.x = __builtin_amdgcn_perm(w[1], w[0], 0x05040100u);
+          lo.y = __builtin_amdgcn_perm(w[3], w[2], 0x05040100u);
+          lo.z = __builtin_amdgcn_perm(w[5], w[4], 0x05040100u);
+          lo.w = __builtin_amdgcn_perm(w[7], w[6], 0x05040100u);
+          hi.x = __builtin_amdgcn_perm(w[1], w[0], 0x07060302u);
+          hi.y = __builtin_amdgcn_perm(w[3], w[2], 0x07060302u);
+          hi.z = __builtin_amdgcn_perm(w[5], w[4], 0x07060302u);
+          hi.w = __builtin_amdgcn_perm(w[7], w[6], 0x07060302u);
+#pragma unroll
+          for (int ms = 0; ms < 2; ++ms) {
+            acc[ms][2 * q] = mma16(fa[kk][ms], lo, acc[ms][2 * q]);
+            acc[ms][2 * q + 1] = mma16(fa[kk][ms], hi, acc[ms][2 * q + 1]);
+          }
+        }
+      }
+    };
+    int st = 0;
+    for (; st + 4 <= nst; st += 4) {
+      step(st, sA0, sB0, sA3, sB3);
+      step(st + 1, sA1, sB1, sA0, sB0);
+      step(st + 2, sA2, sB2, sA1, sB1);
+      step(st + 3, sA3, sB3, sA2, sB2);
+    }
+    if (st < nst) {
+      step(st, sA0, sB0, sA3, sB3);
+      if (st + 1 < nst) {
+        step(st + 1, sA1, sB1, sA0, sB0);
+        if (st + 2 < nst) step(st + 2, sA2, sB2, sA1, sB1);
+      }
+    }
+    wait_counts<0, 0>();
+  }
+  // the slice's partial: element i of block b is token row acc_row(i) of the 32-token block and
+  // column 4p + b, so a lane's four blocks give 16 contiguous bytes of a row
+  const int col = c0 + wn * 128 + 4 * r32;
+#pragma unroll
+  for (int ms = 0; ms < 2; ++ms)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int m = m0 + wm * 64 + ms * 32 + acc_row(i, lane);
+      if (m < a.M && col < a.d) {
+        const f32x4 v = {acc[ms][0][i], acc[ms][1][i], acc[ms][2][i], acc[ms][3][i]};
+        *reinterpret_cast<f32x4*>(a.ypart + ((size_t)kslice * a.M + m) * a.d + col) = v;
+      }
+    }
+}
+
 __global__ __launch_bounds__(256) void k_dred(DenseArgs a) {
   if (a.run_if && *a.run_if != a.run_want) return;
   const size_t e = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4;     // m * d + col
@@ -669,7 +814,15 @@ __global__ __launch_bounds__(256) void k_dlists(DenseArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------------
+// k_ddq's 256-token tiles where they cover the tokens with no more padding than k_ddown's
+bool dense_down_wide(int M) { return (M + DQ_M - 1) / DQ_M * DQ_M == (M + DD_M - 1) / DD_M * DD_M; }
+
 int dense_ks(int M, int d, int ffn) {
+  if (dense_down_wide(M)) {
+    // one workgroup per CU: split ffn until the grid reaches 256
+    const int t = ((M + DQ_M - 1) / DQ_M) * ((d + DQ_N - 1) / DQ_N);
+    return std::max(1, std::min({8, (256 + t - 1) / t, ffn / 32}));
+  }
   const int tiles = ((M + DD_M - 1) / DD_M) * ((d + DD_N - 1) / DD_N);
   // two workgroups per CU (the kernel's occupancy): split ffn until the grid reaches 512
   const int ks = std::max(1, std::min({8, (512 + tiles - 1) / tiles, ffn / DD_K}));
@@ -699,7 +852,9 @@ hipError_t launch_dense_scores(const DenseArgs& a, hipStream_t st) {
 hipError_t launch_dense(const DenseArgs& a, hipStream_t st, hipEvent_t (*ev)[2]) {
   const int up_n = a.has_gate ? 128 : 256;
   const int t_up = ((a.M + UP_M - 1) / UP_M) * ((a.ffn + up_n - 1) / up_n);
-  const int t_dn = ((a.M + DD_M - 1) / DD_M) * ((a.d + DD_N - 1) / DD_N) * a.ks;
+  const bool wide = dense_down_wide(a.M);
+  const int t_dn = wide ? ((a.M + DQ_M - 1) / DQ_M) * ((a.d + DQ_N - 1) / DQ_N) * a.ks
+                        : ((a.M + DD_M - 1) / DD_M) * ((a.d + DD_N - 1) / DD_N) * a.ks;
   const dim3 g_up(8 * ((t_up + 7) / 8)), g_dn(8 * ((t_dn + 7) / 8));
   const dim3 g_red((unsigned)(((size_t)a.M * a.d / 4 + 255) / 256));
   // rows in whole 32-wide K stages take the LDS-copy kernel
@@ -719,10 +874,16 @@ hipError_t launch_dense(const DenseArgs& a, hipStream_t st, hipEvent_t (*ev)[2])
     else UP_LAUNCH(k_dup<false>);
   }
 #undef UP_LAUNCH
-  if (ev && ev[1][0])
+  if (wide) {
+    if (ev && ev[1][0])
+      hipExtLaunchKernelGGL(k_ddq, g_dn, dim3(UP_T), 0, st, ev[1][0], ev[1][1], 0, a);
+    else
+      hipLaunchKernelGGL(k_ddq, g_dn, dim3(UP_T), 0, st, a);
+  } else if (ev && ev[1][0]) {
     hipExtLaunchKernelGGL(k_ddown, g_dn, dim3(DT), 0, st, ev[1][0], ev[1][1], 0, a);
-  else
+  } else {
     hipLaunchKernelGGL(k_ddown, g_dn, dim3(DT), 0, st, a);
+  }
   if (ev && ev[2][0])
     hipExtLaunchKernelGGL(k_dred, g_red, dim3(256), 0, st, ev[2][0], ev[2][1], 0, a);
   else

@@ -587,7 +587,10 @@ def main(argv=None):
     knames = {"pred_z": "k_pred_z", "pred_s": "k_pred_s", "gather": "k_gather",
               "reduce": "k_reduce", "batch_upgate": "k_bug", "batch_down": "k_bdown",
               # rows in whole 32-wide K stages take the LDS-copy up projection
-              "dense_up": "k_dupq" if cfg.d % 32 == 0 else "k_dup", "dense_down": "k_ddown"}
+              "dense_up": "k_dupq" if cfg.d % 32 == 0 else "k_dup",
+              # 256-token tiles where they pad the tokens no more than 128-token ones
+              "dense_down": ("k_ddq" if (Bt + 255) // 256 * 256 == (Bt + 127) // 128 * 128
+                             else "k_ddown")}
     if prefill:
         prof = profiled_traffic(knames[dom], cfg.name + ":prefill%d" % Bt, with_trace=True)
         roof = {"bound": "mfma", "kernel": knames[dom], "achieved": stages[dom]["tflops"],

@@ -74,7 +74,7 @@ def test_profiled_mfma_busy_follows_the_source_hash(tmp_path, monkeypatch):
 
 
 def test_committed_prefill_summaries_carry_mfma_busy():
-    for k in ("k_dupq", "k_ddown"):
+    for k in ("k_dupq", "k_ddq"):
         u = bench.profiled_mfma_busy(k, "falcon_40b_relu_f16:prefill512")
         assert u is not None and 0.0 < u < 1.0, (k, u)
 
