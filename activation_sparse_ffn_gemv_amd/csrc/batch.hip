@@ -49,9 +49,6 @@ __device__ __forceinline__ f32x16 mma8(u32x2 a, u32x2 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x8f16(__builtin_bit_cast(h4v, a),
                                               __builtin_bit_cast(h4v, b), c, 0, 0, 0);
 }
-__device__ __forceinline__ int acc_row(int i, int lane) {
-  return 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-}
 
 // Sum of the four waves' 32x32 accumulators in wave order; the result is valid in wave 0.
 __device__ __forceinline__ f32x16 wg_sum4(f32x16 acc, float* red /* [3][16][64] */) {

@@ -24,6 +24,7 @@
 #include <algorithm>
 
 #include "common.h"
+#include "index.h"
 #include "launch.h"
 
 namespace ffn {
@@ -37,22 +38,13 @@ __device__ __forceinline__ f32x16 mma16(u32x4 a, u32x4 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(h8v, a),
                                                 __builtin_bit_cast(h8v, b), c, 0, 0, 0);
 }
-__device__ __forceinline__ int acc_row(int i, int lane) {
-  return 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-}
-
 constexpr int DT = 256;            // threads per workgroup: 4 waves
-constexpr int DD_M = 128;          // k_ddown: tokens per tile
-constexpr int DD_N = 256;          // k_ddown: columns per tile (8 MFMA blocks of 32 x 8)
+// k_ddown: DD_M tokens x DD_N columns per tile (8 MFMA blocks of 32 x 8; index.h)
 constexpr int DD_K = 32;           // k_ddown: ffn rows per stage
 constexpr int DD_LD = DD_N / 8 + 1;
 
-// blockIdx -> linear tile id such that consecutive ids run on one XCD (workgroups are dealt to
-// the eight XCDs round-robin); ids >= total are idle.
-__device__ __forceinline__ int xcd_tile(int total) {
-  const int per = (total + 7) / 8;
-  return (blockIdx.x % 8) * per + blockIdx.x / 8;
-}
+// this workgroup's tile (consecutive tile ids run on one XCD; ids >= total are idle)
+__device__ __forceinline__ int xcd_tile(int total) { return xcd_tile_of(blockIdx.x, total); }
 
 }  // namespace
 
@@ -287,16 +279,17 @@ __global__ __launch_bounds__(UP_T) void k_dupq(DenseArgs a) {
   const int nks = EPI == EPI_ZPART ? a.kslices : 1;
   const int tile = xcd_tile(nb_m * nb_n * nks);
   if (tile >= nb_m * nb_n * nks) return;
-  const int m0 = (tile % nb_m) * UP_M, n0 = (tile / nb_m % nb_n) * UP_N;
-  const int kslice = tile / (nb_m * nb_n);
+  int mt, nt, kslice;
+  gemm_tile(tile, nb_m, nb_n, mt, nt, kslice);
+  const int m0 = mt * UP_M, n0 = nt * UP_N;
   const int tid = threadIdx.x, lane = tid & (WAVE - 1);
   const int wave = wave_uniform(tid / WAVE);             // scalar: the copies' LDS base
   const int r32 = lane & 31, g = lane >> 5;
   const int wm = wave >> 1, wn = wave & 1;
   const int nchk = a.d / 8, nst_all = nchk / UQ_DK;
   // this workgroup's K stages: all of them, or its slice's [sbase, sbase + nst)
-  const int sbase = (int)((long long)nst_all * kslice / nks);
-  const int nst = (int)((long long)nst_all * (kslice + 1) / nks) - sbase;
+  int sbase, nst;
+  slice_stages(nst_all, kslice, nks, sbase, nst);
   const size_t rowb = (size_t)nchk * 16;
 
   // copy sources: instruction i of this wave covers rows 16 (wave * AI + i) .. +15 of the tile,
@@ -507,13 +500,14 @@ __global__ __launch_bounds__(DT, 2) void k_ddown(DenseArgs a) {
   const int total = nb_m * nb_n * a.ks;
   const int tile = xcd_tile(total);
   if (tile >= total) return;
-  const int mt = tile % nb_m, rest = tile / nb_m;
-  const int nt = rest % nb_n, kslice = rest / nb_n;
+  int mt, nt, kslice;
+  gemm_tile(tile, nb_m, nb_n, mt, nt, kslice);
   const int m0 = mt * DD_M, c0 = nt * DD_N;
   // this slice's ffn rows, in whole stages
   const int nst_all = a.ffn / DD_K;
-  const int st0 = (int)((long long)nst_all * kslice / a.ks);
-  const int st1 = (int)((long long)nst_all * (kslice + 1) / a.ks);
+  int st0, nsl;
+  slice_stages(nst_all, kslice, a.ks, st0, nsl);
+  const int st1 = st0 + nsl;
   const int tid = threadIdx.x, lane = tid & (WAVE - 1), wave = tid / WAVE;
   const int p = lane & 31, g = lane >> 5;
   const int dch = a.d / 8;
@@ -631,7 +625,8 @@ __global__ __launch_bounds__(DT, 2) void k_ddown(DenseArgs a) {
     __syncthreads();
     for (int e = tid; e < 32 * DD_N / 4; e += DT) {
       const int row = e / (DD_N / 4), c4 = e % (DD_N / 4);
-      const int m = m0 + w * 32 + row, col = c0 + 4 * c4;
+      int m, col;
+      ddown_store_pos(m0, c0, w, e, m, col);
       if (m < a.M && col < a.d)
         *reinterpret_cast<f32x4*>(a.ypart + ((size_t)kslice * a.M + m) * a.d + col) =
             *reinterpret_cast<const f32x4*>(&sy[row * DD_N + 4 * c4]);
@@ -649,7 +644,6 @@ __global__ __launch_bounds__(DT, 2) void k_ddown(DenseArgs a) {
 // 128 (p = lane % 32), and each B fragment serves both of the wave's 32-token blocks (12 LDS
 // bytes per lane and MFMA against k_ddown's 16).  Only LDS copies are in flight inside the loop,
 // so the count-based wait covers exactly the copies of the stages it names.
-constexpr int DQ_M = 256, DQ_N = 256;
 
 __global__ __launch_bounds__(UP_T) void k_ddq(DenseArgs a) {
   constexpr int NW = UP_T / WAVE;                        // 8 waves
@@ -663,11 +657,12 @@ __global__ __launch_bounds__(UP_T) void k_ddq(DenseArgs a) {
   const int total = nb_m * nb_n * a.ks;
   const int tile = xcd_tile(total);
   if (tile >= total) return;
-  const int m0 = (tile % nb_m) * DQ_M, c0 = (tile / nb_m % nb_n) * DQ_N;
-  const int kslice = tile / (nb_m * nb_n);
+  int mt, nt, kslice;
+  gemm_tile(tile, nb_m, nb_n, mt, nt, kslice);
+  const int m0 = mt * DQ_M, c0 = nt * DQ_N;
   const int nst_all = a.ffn / 32;
-  const int sbase = (int)((long long)nst_all * kslice / a.ks);
-  const int nst = (int)((long long)nst_all * (kslice + 1) / a.ks) - sbase;
+  int sbase, nst;
+  slice_stages(nst_all, kslice, a.ks, sbase, nst);
   const int tid = threadIdx.x, lane = tid & (WAVE - 1);
   const int wave = wave_uniform(tid / WAVE);
   const int r32 = lane & 31, g = lane >> 5;
@@ -771,12 +766,12 @@ __global__ __launch_bounds__(UP_T) void k_ddq(DenseArgs a) {
   }
   // the slice's partial: element i of block b is token row acc_row(i) of the 32-token block and
   // column 4p + b, so a lane's four blocks give 16 contiguous bytes of a row
-  const int col = c0 + wn * 128 + 4 * r32;
 #pragma unroll
   for (int ms = 0; ms < 2; ++ms)
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const int m = m0 + wm * 64 + ms * 32 + acc_row(i, lane);
+      int m, col;
+      ddq_store_pos(m0, c0, wave, ms, i, lane, m, col);
       if (m < a.M && col < a.d) {
         const f32x4 v = {acc[ms][0][i], acc[ms][1][i], acc[ms][2][i], acc[ms][3][i]};
         *reinterpret_cast<f32x4*>(a.ypart + ((size_t)kslice * a.M + m) * a.d + col) = v;
@@ -814,8 +809,6 @@ __global__ __launch_bounds__(256) void k_dlists(DenseArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// k_ddq's 256-token tiles where they cover the tokens with no more padding than k_ddown's
-bool dense_down_wide(int M) { return (M + DQ_M - 1) / DQ_M * DQ_M == (M + DD_M - 1) / DD_M * DD_M; }
 
 int dense_ks(int M, int d, int ffn) {
   if (dense_down_wide(M)) {

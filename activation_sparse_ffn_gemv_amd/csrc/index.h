@@ -1,5 +1,5 @@
 // Index arithmetic of the kernels that split work between workgroups and exchange partial
-// results through the workspace, as host-and-device functions: the kernels call them, and a CPU
+// results through the workspace (and the GEMMs' tile and K-slice maps), as host-and-device functions: the kernels call them, and a CPU
 // build of the same functions (tests/index_check.cpp) walks every workgroup and thread of the
 // launch shapes the library uses and checks that each index stays inside its buffer, that
 // writers and readers agree, and that the 32-bit products never wrap.
@@ -79,6 +79,59 @@ __host__ __device__ inline PassOffsets pass_offsets(int p, int tile, size_t zpar
   o.uidx = (size_t)p * uidx_ps;
   o.ypart = (size_t)p * ypart_ps;
   return o;
+}
+
+// Row (within its 32-row block) of accumulator element i of lane `lane` of a 32 x 32 MFMA
+// output block: lanes 0-31 hold rows 8 (i / 4) + i % 4, lanes 32-63 the rows four further on.
+__host__ __device__ inline int acc_row(int i, int lane) {
+  return 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+}
+
+// Workgroup b of a GEMM grid of 8 ceil(total / 8) workgroups -> its tile id, such that
+// consecutive ids run on one XCD (workgroup b runs on XCD b % 8); ids >= total are idle.
+__host__ __device__ inline int xcd_tile_of(int b, int total) {
+  const int per = (total + 7) / 8;
+  return (b % 8) * per + b / 8;
+}
+
+// K stages [s0, s0 + n) of slice k of ks over nst_all stages (an even split; n >= 1 when
+// ks <= nst_all).
+__host__ __device__ inline void slice_stages(int nst_all, int k, int ks, int& s0, int& n) {
+  s0 = (int)((long long)nst_all * k / ks);
+  n = (int)((long long)nst_all * (k + 1) / ks) - s0;
+}
+
+// Tile id -> (token tile mt, column tile nt, K slice k) of the dense GEMMs, token tiles fastest:
+// the token tiles that share a weight tile have consecutive ids, so they run on one XCD.
+__host__ __device__ inline void gemm_tile(int tile, int nb_m, int nb_n, int& mt, int& nt,
+                                          int& k) {
+  mt = tile % nb_m;
+  nt = tile / nb_m % nb_n;
+  k = tile / (nb_m * nb_n);
+}
+
+// Down-projection tiles: k_ddown 128 tokens x 256 columns, k_ddq 256 x 256.  k_ddq takes the
+// token counts whose 256-token tiles pad no more than 128-token ones.
+constexpr int DD_M = 128, DD_N = 256;
+constexpr int DQ_M = 256, DQ_N = 256;
+__host__ __device__ inline bool dense_down_wide(int M) {
+  return (M + DQ_M - 1) / DQ_M * DQ_M == (M + DD_M - 1) / DD_M * DD_M;
+}
+
+// k_ddq's partial-sum store of lane `lane` of wave `wave`, 32-token block ms, accumulator
+// element i: token m and the first of the lane's four consecutive columns col (MFMA block b
+// holds column 4 (lane % 32) + b of the wave's 128).
+__host__ __device__ inline void ddq_store_pos(int m0, int c0, int wave, int ms, int i, int lane,
+                                              int& m, int& col) {
+  m = m0 + (wave >> 1) * 64 + ms * 32 + acc_row(i, lane);
+  col = c0 + (wave & 1) * 128 + 4 * (lane & 31);
+}
+
+// k_ddown's partial-sum store: wave w's 32 x 256 tile staged through LDS, element e of the
+// workgroup's pass over it (four columns each): token m and first column col.
+__host__ __device__ inline void ddown_store_pos(int m0, int c0, int w, int e, int& m, int& col) {
+  m = m0 + w * 32 + e / (DD_N / 4);
+  col = c0 + 4 * (e % (DD_N / 4));
 }
 
 }  // namespace ffn

@@ -259,6 +259,7 @@ struct DenseArgs {
   size_t zpart_ps;
   int kslices;
 };
+// K slices of the down projection for M tokens (k_ddq's or k_ddown's tiles: dense_down_wide).
 int dense_ks(int M, int d, int ffn);
 // K slices of the stage-1 GEMM for a call of M tokens (at most ZPART_MAX_KS).
 constexpr int ZPART_MAX_KS = 32;

@@ -4,7 +4,7 @@
 // its buffer, the gather's partial writes and the reduce's reads must address the same elements,
 // the work splits must partition their ranges exactly, and no 32-bit product may wrap.  The
 // shapes come from the built library's own host functions (workgroup counts, tiles, the batched
-// path's buffer shapes).  Exit status 0 and "index check: OK" when every check holds.
+// path's buffer shapes, the dense down projection's K slices).  Exit status 0 and "index check: OK" when every check holds.
 #include <stdio.h>
 #include <stdlib.h>
 
@@ -151,6 +151,78 @@ static void check_passes(int d, int ffn, int r, int max_batch) {
   }
 }
 
+
+// Dense down projection (k_ddq or k_ddown by the token count): the grid's tiles are each
+// (token tile, column tile, K slice) once, the K slices split the ffn stages with none empty,
+// and every (slice, token, column) element of the partial-sum buffer [ks][M][d] is stored exactly
+// once by the epilogue's index arithmetic, inside the buffer.
+static void check_dense_down(int M, int d, int ffn) {
+  const bool wide = dense_down_wide(M);
+  const int TM = wide ? DQ_M : DD_M, TN = wide ? DQ_N : DD_N;
+  const int ks = dense_ks(M, d, ffn), nst_all = ffn / 32;
+  CHECK(ks >= 1 && ks <= nst_all, "M %d d %d ffn %d: %d K slices over %d stages", M, d, ffn, ks,
+        nst_all);
+  if (ks < 1 || ks > nst_all) return;
+  const int nb_m = (M + TM - 1) / TM, nb_n = (d + TN - 1) / TN, total = nb_m * nb_n * ks;
+  const int grid = 8 * ((total + 7) / 8);
+  const size_t nel = (size_t)ks * M * d;
+  std::vector<unsigned char> seen(total, 0), el(nel / 4, 0);
+  for (int b = 0; b < grid; ++b) {
+    const int tile = xcd_tile_of(b, total);
+    CHECK(tile >= 0 && tile < grid, "tile id %d of grid %d", tile, grid);
+    if (tile < 0 || tile >= total) continue;
+    CHECK(!seen[tile], "tile %d given twice (M %d d %d)", tile, M, d);
+    seen[tile] = 1;
+    int mt, nt, k;
+    gemm_tile(tile, nb_m, nb_n, mt, nt, k);
+    CHECK(mt < nb_m && nt < nb_n && k < ks, "tile %d decodes outside the grid", tile);
+    int s0, n;
+    slice_stages(nst_all, k, ks, s0, n);
+    CHECK(n >= 1 && s0 >= 0 && s0 + n <= nst_all, "slice %d of %d: stages [%d, %d)", k, ks, s0,
+          s0 + n);
+    const int m0 = mt * TM, c0 = nt * TN;
+    auto store = [&](int m, int col) {
+      if (m >= M || col >= d) return;                     // the kernels' own guard
+      CHECK(m >= 0 && col >= 0 && col % 4 == 0 && col + 3 < d, "store at m %d col %d", m, col);
+      const size_t off = ((size_t)k * M + m) * d + col;
+      CHECK(off + 3 < nel, "store past the partials: M %d d %d off %zu", M, d, off);
+      if (off + 3 < nel && col % 4 == 0) {
+        CHECK(!el[off / 4], "element stored twice: M %d d %d k %d m %d col %d", M, d, k, m, col);
+        el[off / 4] = 1;
+      }
+    };
+    if (wide) {
+      for (int wave = 0; wave < 8; ++wave)
+        for (int ms = 0; ms < 2; ++ms)
+          for (int i = 0; i < 16; ++i)
+            for (int lane = 0; lane < 64; ++lane) {
+              int m, col;
+              ddq_store_pos(m0, c0, wave, ms, i, lane, m, col);
+              store(m, col);
+            }
+    } else {
+      for (int w = 0; w < 4; ++w)
+        for (int e = 0; e < 32 * DD_N / 4; ++e) {
+          int m, col;
+          ddown_store_pos(m0, c0, w, e, m, col);
+          store(m, col);
+        }
+    }
+  }
+  for (int t = 0; t < total; ++t) CHECK(seen[t], "tile %d never given (M %d d %d)", t, M, d);
+  size_t missing = 0;
+  for (unsigned char v : el) missing += !v;
+  CHECK(missing == 0, "M %d d %d ffn %d: %zu partial elements never stored", M, d, ffn, missing);
+  int prev = 0;
+  for (int k = 0; k < ks; ++k) {
+    int s0, n;
+    slice_stages(nst_all, k, ks, s0, n);
+    CHECK(s0 == prev, "slices not consecutive: M %d k %d", M, k);
+    prev = s0 + n;
+  }
+  CHECK(prev == nst_all, "slices do not cover the ffn stages: M %d", M);
+}
+
 int main() {
   const int ds[] = {64, 256, 512, 768, 776, 1024, 4096, 4104, 8192};
   const int ffns[] = {256, 1024, 3072, 11008, 14336, 32768};
@@ -166,6 +238,11 @@ int main() {
                            {8192, 32768, 1024, 512}, {256, 1024, 32, 4096}, {512, 2048, 64, 70},
                            {1024, 4096, 64, 256}};
   for (const auto& sh : shapes) check_passes(sh[0], sh[1], sh[2], sh[3]);
+  const int dshapes[][3] = {{64, 256, 1024},   {70, 264, 1056},   {129, 264, 2048},
+                            {130, 512, 2048},  {256, 256, 1024},  {300, 768, 3072},
+                            {385, 4096, 11008}, {512, 8192, 32768}, {1000, 1024, 4096},
+                            {4096, 512, 2048}};
+  for (const auto& sh : dshapes) check_dense_down(sh[0], sh[1], sh[2]);
   if (failures) {
     printf("index check: %ld of %ld checks failed\n", failures, checks);
     return 1;
