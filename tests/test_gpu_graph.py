@@ -84,3 +84,57 @@ def test_dense_forward_in_a_graph(ffn):
     y = torch.zeros(96, cfg.d, device="cuda")
     _replays_match(lambda: m.dense(x, y=y), y)
     m.close()
+
+
+def test_auto_choice_in_a_graph_follows_the_data(ffn):
+    """One captured AUTO call of 130 tokens (two passes in one launch per kernel) replayed with
+    different caller sets in the same mask buffer: a dense set (union above the crossover) makes
+    the device run the dense GEMMs, a sparse one the sparse passes, replay after replay, and each
+    replay equals the eager call on the same sets bit for bit."""
+    cfg = synth.small_config(d=256, ffn=1024, rank=32, act="relu", w_dtype="f16", x_dtype="f16",
+                             p_dtype="f16", density=0.1, bias_up=True, bias_down=True)
+    L = to_device(synth.make_layer(cfg))
+    B = 130
+    x = synth.make_tokens(cfg, B).cuda()
+    m = ffn.SparseFFN(L, max_batch=B)
+    ffn.ffn_plan_set_crossover(m.plan, B, 0.5)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(11)
+    masks = {
+        # every token's set: 90% of the neurons (union 100%: dense) or a shared 5% (sparse)
+        "dense": (torch.rand(B, cfg.ffn, generator=g, device="cuda") < 0.9).to(torch.uint8),
+        "sparse": (torch.rand(1, cfg.ffn, generator=g, device="cuda") < 0.05)
+        .to(torch.uint8).expand(B, cfg.ffn).contiguous(),
+    }
+    mask = torch.zeros(B, cfg.ffn, dtype=torch.uint8, device="cuda")
+    y = torch.zeros(B, cfg.d, device="cuda")
+
+    def run():
+        m.forward(x, y=y, mask=mask, path=ffn.FFN_PATH_AUTO)
+
+    s = torch.cuda.Stream()
+    ref = {}
+    for kind, mk in masks.items():
+        mask.copy_(mk)
+        with torch.cuda.stream(s):
+            run()
+        torch.cuda.synchronize()
+        assert m.last_auto_path() == kind, (kind, m.last_auto_path())
+        ref[kind] = y.clone()
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(gr, stream=s):
+            run()
+    torch.cuda.synchronize()
+    for kind in ("dense", "sparse", "sparse", "dense", "dense", "sparse"):
+        mask.copy_(masks[kind])
+        y.fill_(float("nan"))
+        junk = torch.randn(1 << 20, device="cuda").sum()
+        torch.cuda.synchronize()
+        gr.replay()
+        torch.cuda.synchronize()
+        assert m.last_auto_path() == kind
+        assert torch.equal(y, ref[kind]), "replay with the %s sets differs" % kind
+        del junk
+    del gr
+    m.close()
