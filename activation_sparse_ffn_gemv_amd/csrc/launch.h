@@ -262,7 +262,7 @@ struct DenseArgs {
 // K slices of the down projection for M tokens (k_ddq's or k_ddown's tiles: dense_down_wide).
 int dense_ks(int M, int d, int ffn);
 // K slices of the stage-1 GEMM for a call of M tokens (at most ZPART_MAX_KS).
-constexpr int ZPART_MAX_KS = 32;
+constexpr int ZPART_MAX_KS = 16;
 int zpart_kslices(int M, int d, int rank);
 hipError_t launch_dense_zpart(const DenseArgs& a, hipStream_t st);
 // Predictor stage 2 of a call of many tokens as one GEMM (fields above); rank % 32 == 0.
