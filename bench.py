@@ -125,6 +125,7 @@ OTHERS = [
     ("falcon_40b_relu_f16", ["--batch", "8", "--steps", "8"]),
     ("falcon_40b_relu_f16", ["--batch", "32", "--steps", "4"]),
     ("falcon_40b_relu_f16", ["--prefill", "512", "--steps", "2"]),
+    ("falcon_40b_relu_f16", ["--prefill", "512", "--steps", "2", "--prefill-path", "dense"]),
 ]
 
 
