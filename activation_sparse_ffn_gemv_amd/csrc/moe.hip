@@ -3,10 +3,10 @@
 // top-K experts by the logits l_e = R[e] . x, ties going to the lower expert index, and weighs
 // them by the softmax over the chosen logits.
 //
-// One workgroup of eight waves per token.  The routing decision never leaves the device: the workgroup copies
-// the chosen experts' weight records (from the table passed by value in the kernel arguments)
-// into per-slot records in the workspace, and the expert kernels that follow take their weight
-// pointers from those records.
+// One workgroup of four waves per token.  The routing decision never leaves the device: the
+// workgroup copies the chosen experts' weight records (from the table passed by value in the
+// kernel arguments) into per-slot records in the workspace, and the expert kernels that follow
+// take their weight pointers from those records.
 #include <hip/hip_ext.h>
 
 #include "common.h"
@@ -14,7 +14,7 @@
 
 namespace ffn {
 
-constexpr int RT_THREADS = 512;
+constexpr int RT_THREADS = 256;
 constexpr int RT_NW = RT_THREADS / WAVE;
 constexpr int RT_EPW = (MOE_MAX_E + RT_NW - 1) / RT_NW;   // experts per wave
 constexpr int RT_CPL = 8;                                  // chunks per lane in flight
@@ -129,9 +129,10 @@ __device__ __forceinline__ void route_token(const RouterArgs& a, int b) {
 }
 
 // Router and predictor stage 1 of the chosen experts in one launch.  Blocks [0, B) route token b
-// (above) and write its slot records; each further block runs eight P1 rows of one token's chosen
+// (above) and write its slot records; each further block runs four P1 rows of one token's chosen
 // experts, a wave per row (rows in (token b, slot t, row k) order; rank is a multiple of eight, so
-// a block's rows share the token and the slot).  Such a block first reaches the token's routing
+// a block's rows share the token and the slot).  Four waves per block rather than eight: the
+// chosen experts' P1 rows spread over twice as many CUs.  Such a block first reaches the token's routing
 // decision itself (the same code as the routing block, so the same experts), then reads the P1
 // rows of the experts chosen and no others: 16-byte chunks per lane, all loads issued before use,
 // wave sum.  The rows land at zall[(b * E + e) * rank + k], where the stage-2 kernels look for
