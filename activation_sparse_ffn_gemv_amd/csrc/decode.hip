@@ -801,15 +801,21 @@ __global__ __launch_bounds__(RD_THREADS) void k_reduce(ReduceArgs a) {
   const int j = tile * RD_TW + q * 4;
   FFN_TS(2, 0);
   const int nslot = MODE == 2 ? a.nslot : 1;
-  // b_down (of each expert slot, routing-weighted).  One layer: the load goes out now and is
-  // first used after the loop, so it does not hold up the partials' loads.
+  // b_down.  One layer: the load goes out now and is first used after the loop, so it does not
+  // hold up the partials' loads.  Expert slots: each slot's routing weight, |A| and b_down come
+  // from its record, all requested at once ahead of the partials (the weighted biases are added
+  // after the loop: their loads depend on the records).
   f32x4 bias = {0.f, 0.f, 0.f, 0.f};
-  if (MODE == 2) {
-    if (threadIdx.x < RD_Q && j < a.d) {
-      for (int k = 0; k < nslot; ++k) {
-        const float* b_down = a.slot[k].b_down;
-        if (b_down) bias += a.slot[k].wgt * *reinterpret_cast<const f32x4*>(b_down + j);
-      }
+  float sw[MOE_MAX_K];
+  uint32_t stot[MOE_MAX_K];
+  const float* sbd[MOE_MAX_K];
+  if constexpr (MODE == 2) {
+#pragma unroll
+    for (int k = 0; k < MOE_MAX_K; ++k) {
+      const int kk = min(k, nslot - 1);
+      sw[k] = a.slot[kk].wgt;
+      sbd[k] = a.slot[kk].b_down;
+      stot[k] = (uint32_t)a.cnt[(size_t)kk * a.cstride];
     }
   } else if (threadIdx.x < RD_Q && j < a.d && a.b_down) {
     bias = ldg(reinterpret_cast<const f32x4*>(a.b_down + j), 0);
@@ -818,32 +824,60 @@ __global__ __launch_bounds__(RD_THREADS) void k_reduce(ReduceArgs a) {
   const uint32_t items = (uint32_t)nslot * np;
   const uint32_t total0 = MODE == 0 ? (uint32_t)a.cnt[0] : 0u;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (uint32_t i0 = 0; i0 < items; i0 += RD_G * RD_UNROLL) {
+  // expert slots: nslot * n_part <= RD_G * RD_UNROLL (the gather's workgroups are shared between
+  // the slots), so one pass, which lets the slots' constants arrive while the partials load
+  const uint32_t passes = MODE == 2 ? 1u : (items + RD_G * RD_UNROLL - 1) / (RD_G * RD_UNROLL);
+  for (uint32_t ip = 0; ip < passes; ++ip) {
+    const uint32_t i0 = ip * RD_G * RD_UNROLL;
     f32x4 v[RD_UNROLL];
     float wt[RD_UNROLL];
+    uint32_t ks[RD_UNROLL], cs[RD_UNROLL];
+    // the partials' loads first (their addresses need no loaded value), then the weights
 #pragma unroll
     for (int u = 0; u < RD_UNROLL; ++u) {
       const uint32_t it = min(i0 + g + u * RD_G, items - 1);
-      const uint32_t k = MODE == 2 ? it / np : 0u;
-      const uint32_t c = it - k * np;
+      ks[u] = MODE == 2 ? it / np : 0u;
+      cs[u] = it - ks[u] * np;
+      v[u] = *reinterpret_cast<const f32x4*>(a.part + (size_t)ks[u] * a.pstride +
+                                             part_offset(tile * RD_TW + q * 4, cs[u], np));
+    }
+#pragma unroll
+    for (int u = 0; u < RD_UNROLL; ++u) {
+      const uint32_t k = ks[u], c = cs[u];
+      // the slot's weight and |A| (a select over the slots, not a per-lane load)
+      float wk = 1.0f;
+      uint32_t total = total0;
+      if constexpr (MODE == 2) {
+        wk = sw[0];
+        total = stot[0];
+#pragma unroll
+        for (int s2 = 1; s2 < MOE_MAX_K; ++s2) {
+          wk = k == (uint32_t)s2 ? sw[s2] : wk;
+          total = k == (uint32_t)s2 ? stot[s2] : total;
+        }
+      }
       bool on;
       if (MODE == 1) {
         on = (a.bitmap[2 * c] | (2 * c + 1 < (uint32_t)a.ffn / 32 ? a.bitmap[2 * c + 1] : 0u)) != 0u;
       } else {
         // partial c exists iff gather workgroup c owned at least one rank
-        const uint32_t total = MODE == 0 ? total0 : (uint32_t)a.cnt[(size_t)k * a.cstride];
         on = gather_wrote_partial(total, c, np);
       }
       on = on && i0 + g + u * RD_G < items;
-      wt[u] = on ? (MODE == 2 ? a.slot[k].wgt : 1.0f) : 0.0f;
-      v[u] = *reinterpret_cast<const f32x4*>(a.part + (size_t)k * a.pstride +
-                                             part_offset(tile * RD_TW + q * 4, c, np));
+      wt[u] = on ? wk : 0.0f;
     }
     issue_fence();
 #pragma unroll
     for (int u = 0; u < RD_UNROLL; ++u) {
       // partials that were not written hold stale bytes: skipped, never multiplied by 0
       if (wt[u] != 0.0f) acc += MODE == 2 ? wt[u] * v[u] : v[u];
+    }
+  }
+  if constexpr (MODE == 2) {
+    if (threadIdx.x < RD_Q && j < a.d) {
+#pragma unroll
+      for (int k = 0; k < MOE_MAX_K; ++k)
+        if (k < nslot && sbd[k]) bias += sw[k] * *reinterpret_cast<const f32x4*>(sbd[k] + j);
     }
   }
   // fixed-order tree over the groups: within each wave by lane exchange (lane = 4 g' + q), then
@@ -1068,6 +1102,10 @@ hipError_t launch_reduce(const ReduceArgs& a, hipStream_t st, hipEvent_t ev0, hi
   const dim3 grid(reduce_tiles(a.d)), block(RD_THREADS);
   auto kern = a.slot ? k_reduce<2> : a.fused ? k_reduce<1> : k_reduce<0>;
   if (!a.slot && !a.fused && a.n_part != GA_BLOCKS) return hipErrorInvalidValue;
+  // expert slots: every (slot, partial) item in the reduce's one pass
+  if (a.slot && (a.nslot < 1 || a.nslot > MOE_MAX_K ||
+                 (long long)a.nslot * a.n_part > RD_G * RD_UNROLL))
+    return hipErrorInvalidValue;
   if (ev0 && ev1)
     hipExtLaunchKernelGGL(kern, grid, block, 0, st, ev0, ev1, 0, a);
   else
