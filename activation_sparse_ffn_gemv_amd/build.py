@@ -23,6 +23,9 @@ FLAGS = [
     # packed fp32 instructions stay off: the compiler must not emit them
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function", "-Wno-unknown-pragmas",
+    # up to 16 SGPRs of a kernel's leading scalar arguments preloaded by the command processor
+    # instead of fetched by the wave (kernels that take one argument struct are unaffected)
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
 ]
 
 
