@@ -165,3 +165,36 @@ def test_moe_batch_equals_single_tokens(ffn):
         torch.cuda.synchronize()
         assert torch.equal(y1[0], yb[t])
     moe.close()
+
+
+def test_chosen_expert_with_an_empty_set(ffn):
+    """The router's first choice is an expert whose predictor fires for no neuron (c2 far below
+    the threshold): its slot reports |A| = 0, reads no row, and y is the other expert's weighted
+    FFN plus the empty expert's weighted b_down (the oracle on the same sets)."""
+    cfg = synth.small_config(d=256, ffn=1024, rank=32, act="relu", w_dtype="f16", x_dtype="f16",
+                             p_dtype="f16", density=0.1, bias_up=True, bias_down=True)
+    experts = [to_device(synth.make_layer(cfg, expert=e, device="cuda")) for e in range(4)]
+    experts[2]["c2"] = torch.full_like(experts[2]["c2"], -1.0e4)   # expert 2 never fires
+    x = synth.make_tokens(cfg, 1).cuda()
+    R = torch.zeros(4, cfg.d, dtype=torch.float16, device="cuda")
+    k = int(torch.argmax(x[0].abs()))
+    s = 1.0 if float(x[0, k]) > 0 else -1.0
+    R[2, k], R[0, k], R[1, k], R[3, k] = 3.0 * s, 2.0 * s, -1.0 * s, 0.5 * s   # winners 2, then 0
+    moe = ffn.MoEFFN(experts, R, top_k=2, max_batch=1)
+    y = torch.full((1, cfg.d), float("nan"), device="cuda")
+    ids = torch.zeros(1, 2, dtype=torch.int32, device="cuda")
+    w = torch.zeros(1, 2, device="cuda")
+    cnt = torch.full((1, 2), -1, dtype=torch.int32, device="cuda")
+    moe.forward(x, y=y, expert_idx=ids, expert_w=w, expert_cnt=cnt)
+    torch.cuda.synchronize()
+    assert ids.cpu().tolist() == [[2, 0]]
+    cnt_h, w_h = cnt.cpu().numpy()[0], w.cpu().numpy()[0]
+    assert cnt_h[0] == 0
+    set0 = _expert_sets(ffn, experts[0], x)[0]
+    assert cnt_h[1] == len(set0)
+    xh = x.cpu().numpy()[0]
+    y2, _ = oracle.ffn(oracle_layer(experts[2]), xh, np.zeros(cfg.ffn, np.uint8))
+    y0, _ = oracle.ffn(oracle_layer(experts[0]), xh, mask_from_idx(set0, cfg.ffn))
+    y_ref = float(w_h[0]) * y2 + float(w_h[1]) * y0
+    assert normwise(y.cpu().numpy()[0], y_ref) <= TOL["f16"]
+    moe.close()
