@@ -16,49 +16,52 @@ namespace ffn {
 
 constexpr int RT_THREADS = 256;
 constexpr int RT_NW = RT_THREADS / WAVE;
-constexpr int RT_EPW = (MOE_MAX_E + RT_NW - 1) / RT_NW;   // experts per wave
-constexpr int RT_CPL = 8;                                  // chunks per lane in flight
+
+// Experts per wave of the logits (a template parameter: 1, 2 or 4 for up to 4, 8 or 16
+// experts), so that every row load is unconditional: a load under a branch makes the compiler
+// wait for the loads before it where the paths join, and the token's round trip would become
+// one per expert.
+constexpr int rt_epw(int E) { return E <= RT_NW ? 1 : E <= 2 * RT_NW ? 2 : 4; }
+static_assert(MOE_MAX_E <= 4 * RT_NW, "four experts per wave at most");
 
 // Logits of token b over every expert (into s_logit) and its top-K (repeated arg-max over the
 // experts not yet taken, strict >: ties keep the lower index) into ids[0, K) of every thread.
-// Wave w takes experts w, w + RT_NW, ...; lanes split the rows in 16-byte chunks, and a lane's
-// chunks of the token and of its rows are requested together (one round trip at d = 4096 fp16).  Every workgroup that needs the decision
-// runs this same code on the same data, so all of them reach the same experts.
-template <int XK>
-__device__ __forceinline__ void route_decide(const RouterArgs& a, int b, float* s_logit,
-                                             int (&ids)[MOE_MAX_K]) {
+// xr holds the token's chunks as load_x requested them (lane l: chunks l, l + 64, ...; they may
+// still be in flight).  Wave w takes experts w, w + RT_NW, ... (EPW of them; a slot past the last
+// expert reads the last expert's row again and is not used); a lane requests its chunks of all its
+// rows at once, so the token and the rows take one round trip.  Every workgroup that needs the
+// decision runs this same code on the same data, so all of them reach the same experts.
+template <int XK, int CPL, int EPW>
+__device__ __forceinline__ void route_decide(const RouterArgs& a, const XRegs<XK, CPL>& xr,
+                                             float* s_logit, int (&ids)[MOE_MAX_K]) {
   constexpr int EPC = Kind<XK>::EPC;
   const int tid = threadIdx.x, lane = tid & (WAVE - 1), wave = tid / WAVE;
   const int nch = a.d / EPC;
-  const char* xb = static_cast<const char*>(a.x) + (size_t)b * nch * 16;
   const char* R = static_cast<const char*>(a.R);
-  float acc[RT_EPW] = {};
-  for (int c0 = 0; c0 < nch; c0 += RT_CPL * WAVE) {
-    u32x4 xv[RT_CPL], w[RT_EPW][RT_CPL];
+  u32x4 w[EPW][CPL];
 #pragma unroll
-    for (int k = 0; k < RT_CPL; ++k) {
-      const int c = min(c0 + lane + k * WAVE, nch - 1);
-      xv[k] = ld16(xb + (size_t)c * 16);
+  for (int k = 0; k < CPL; ++k) {
+    const int c = min(lane + k * WAVE, nch - 1);
 #pragma unroll
-      for (int j = 0; j < RT_EPW; ++j) {
-        const int e = wave + j * RT_NW;
-        w[j][k] = e < a.E ? ld16(R + ((size_t)e * nch + c) * 16) : u32x4{0u, 0u, 0u, 0u};
-      }
+    for (int j = 0; j < EPW; ++j) {
+      const int e = min(wave + j * RT_NW, a.E - 1);
+      w[j][k] = ld16(R + ((size_t)e * nch + c) * 16);
     }
-    issue_fence();
+  }
+  issue_fence();
+  float acc[EPW] = {};
 #pragma unroll
-    for (int k = 0; k < RT_CPL; ++k) {
-      if (c0 + lane + k * WAVE < nch) {
+  for (int k = 0; k < CPL; ++k) {
+    if (lane + k * WAVE < nch) {
 #pragma unroll
-        for (int j = 0; j < RT_EPW; ++j) {
-          if constexpr (XK == WK_F16) acc[j] = dot8_f16(w[j][k], xv[k], acc[j]);
-          else acc[j] = dot4_f32(w[j][k], xv[k], acc[j]);
-        }
+      for (int j = 0; j < EPW; ++j) {
+        if constexpr (XK == WK_F16) acc[j] = dot8_f16(w[j][k], xr.v[k][0], acc[j]);
+        else acc[j] = dot4_f32(w[j][k], xr.v[k][0], acc[j]);
       }
     }
   }
 #pragma unroll
-  for (int j = 0; j < RT_EPW; ++j) {
+  for (int j = 0; j < EPW; ++j) {
     const float l = wave_sum(acc[j]);
     if (lane == 0 && wave + j * RT_NW < a.E) s_logit[wave + j * RT_NW] = l;
   }
@@ -86,14 +89,17 @@ __device__ __forceinline__ void route_decide(const RouterArgs& a, int b, float* 
   }
 }
 
-template <int XK>
+template <int XK, int CPL, int EPW>
 __device__ __forceinline__ void route_token(const RouterArgs& a, int b) {
   __shared__ float s_logit[MOE_MAX_E];
   __shared__ int s_ids[MOE_MAX_K];
   __shared__ float s_w[MOE_MAX_K];
   const int tid = threadIdx.x;
+  const int nch = a.d / Kind<XK>::EPC;
+  XRegs<XK, CPL> xr;
+  load_x<XK, CPL>(xr, static_cast<const char*>(a.x) + (size_t)b * nch * 16, nch, tid & (WAVE - 1));
   int ids[MOE_MAX_K];
-  route_decide<XK>(a, b, s_logit, ids);
+  route_decide<XK, CPL, EPW>(a, xr, s_logit, ids);
   if (tid == 0) {
     // the softmax over the chosen logits (the first is the largest)
     const float mx = s_logit[ids[0]];
@@ -137,10 +143,10 @@ __device__ __forceinline__ void route_token(const RouterArgs& a, int b) {
 // rows of the experts chosen and no others: 16-byte chunks per lane, all loads issued before use,
 // wave sum.  The rows land at zall[(b * E + e) * rank + k], where the stage-2 kernels look for
 // the slot's expert e.
-template <int XK, int CPL>
+template <int XK, int CPL, int EPW>
 __global__ __launch_bounds__(RT_THREADS) void k_route_z(RouterArgs a) {
   if ((int)blockIdx.x < a.B) {
-    route_token<XK>(a, blockIdx.x);
+    route_token<XK, CPL, EPW>(a, blockIdx.x);
     return;
   }
   __shared__ float s_logit[MOE_MAX_E];
@@ -151,7 +157,7 @@ __global__ __launch_bounds__(RT_THREADS) void k_route_z(RouterArgs a) {
   XRegs<XK, CPL> xr;
   load_x<XK, CPL>(xr, static_cast<const char*>(a.x) + (size_t)b * nch * 16, nch, lane);
   int ids[MOE_MAX_K];
-  route_decide<XK>(a, b, s_logit, ids);
+  route_decide<XK, CPL, EPW>(a, xr, s_logit, ids);
   const int k = q % a.rank, t = (q / a.rank) % a.K;
   int e = ids[0];
 #pragma unroll
@@ -167,24 +173,32 @@ __global__ __launch_bounds__(RT_THREADS) void k_route_z(RouterArgs a) {
     a.zall[((size_t)b * a.E + e) * a.rank + k] = acc + (a.tab.e[e].c1 ? a.tab.e[e].c1[k] : 0.0f);
 }
 
+template <int XK, int CPL>
+static void launch_route_z_t(const RouterArgs& a, dim3 grid, hipStream_t st, hipEvent_t ev0,
+                             hipEvent_t ev1) {
+  const int epw = rt_epw(a.E);
+  auto kern = epw == 1 ? k_route_z<XK, CPL, 1> : epw == 2 ? k_route_z<XK, CPL, 2>
+                                                          : k_route_z<XK, CPL, 4>;
+  if (ev0 && ev1)
+    hipExtLaunchKernelGGL(kern, grid, dim3(RT_THREADS), 0, st, ev0, ev1, 0, a);
+  else
+    hipLaunchKernelGGL(kern, grid, dim3(RT_THREADS), 0, st, a);
+}
+
 hipError_t launch_route_z(const RouterArgs& a, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
   if (a.rank % RT_NW) return hipErrorInvalidValue;   // a block's rows share one token
+  if (a.E < 1 || a.E > MOE_MAX_E) return hipErrorInvalidValue;
   const dim3 grid(a.B + a.B * a.K * a.rank / RT_NW);
-#define RZ(X, C)                                                                                \
-  do {                                                                                        \
-    if (ev0 && ev1)                                                                           \
-      hipExtLaunchKernelGGL((k_route_z<X, C>), grid, dim3(RT_THREADS), 0, st, ev0, ev1, 0, a); \
-    else                                                                                      \
-      hipLaunchKernelGGL((k_route_z<X, C>), grid, dim3(RT_THREADS), 0, st, a);                \
-  } while (0)
-#define RZ_CASE(C) \
-  case C: if (a.x_f16) RZ(WK_F16, C); else RZ(WK_F32, C); break;
+#define RZ_CASE(C)                                                              \
+  case C:                                                                       \
+    if (a.x_f16) launch_route_z_t<WK_F16, C>(a, grid, st, ev0, ev1);            \
+    else launch_route_z_t<WK_F32, C>(a, grid, st, ev0, ev1);                    \
+    break;
   switch (a.cpl) {
     RZ_CASE(1) RZ_CASE(2) RZ_CASE(3) RZ_CASE(4) RZ_CASE(6) RZ_CASE(8) RZ_CASE(12) RZ_CASE(16)
     default: return hipErrorInvalidValue;
   }
 #undef RZ_CASE
-#undef RZ
   return hipGetLastError();
 }
 
