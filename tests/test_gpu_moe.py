@@ -99,7 +99,13 @@ def _check_moe(ffn, cfg, n_experts, top_k, n_tokens, experts=None, R=None):
           bias_gate=True, bias_down=True), 8, 2),
     (dict(d=256, ffn=1056, rank=24, act="drelu", w_dtype="f16", x_dtype="f16", p_dtype="f16",
           bias_gate=True, bias_up=True), 16, 4),
-], ids=["i4_e4k2", "f32_e3k1", "f16_e8k2", "f16_e16k4"])
+    # expert counts that leave some waves' logit slots past the last expert (they re-read the
+    # last expert's row and must not be used): 6 experts at two per wave, 13 at four per wave
+    (dict(d=256, ffn=512, rank=16, act="reglu", w_dtype="f16", x_dtype="f16", p_dtype="f16",
+          bias_gate=True), 6, 2),
+    (dict(d=384, ffn=768, rank=16, act="relu", w_dtype="f32", x_dtype="f32", p_dtype="f32",
+          bias_up=True), 13, 3),
+], ids=["i4_e4k2", "f32_e3k1", "f16_e8k2", "f16_e16k4", "f16_e6k2", "f32_e13k3"])
 def test_moe_small(ffn, kw, E, K):
     cfg = synth.small_config(density=0.1, **kw)
     _check_moe(ffn, cfg, E, K, n_tokens=5)
