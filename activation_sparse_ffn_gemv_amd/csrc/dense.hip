@@ -253,35 +253,39 @@ __device__ __forceinline__ void sched_group() { __builtin_amdgcn_sched_group_bar
 // large call (scores against the threshold into bitmap and union words; GATE false).  EPI 2:
 // predictor stage 1 of a large call, split over K (a.kslices slices of d): each slice's fp32
 // partial of Z = X P1^T, in the per-pass layout [pass][slice][32 tokens][rank] that the batched
-// path's fixed-order sum (k_bzr) reads.
+// path's fixed-order sum (k_bzr) reads.  TM x TN: the tile (tokens x neurons); the stage-1 GEMM
+// takes ZP_M x ZP_N (its rank columns give few 256 x 256 tiles, which the K split would have to
+// make up for with more partials).
 constexpr int EPI_FFN = 0, EPI_SCORE = 1, EPI_ZPART = 2;
 
-template <bool GATE, int EPI = EPI_FFN>
+template <bool GATE, int EPI = EPI_FFN, int TM = UP_M, int TN = 256>
 __global__ __launch_bounds__(UP_T) void k_dupq(DenseArgs a) {
   static_assert(EPI == EPI_FFN || !GATE, "the predictor GEMMs have no gate rows");
+  static_assert((TM == UP_M && TN == 256) || EPI == EPI_ZPART, "smaller tiles: stage-1 GEMM only");
   constexpr int NMAT = GATE ? 2 : 1;
-  constexpr int UP_N = GATE ? 128 : 256;   // neurons per tile
+  constexpr int UP_N = GATE ? 128 : TN;    // neurons per tile
+  constexpr int MS = TM / 4 / 32;          // 32-token MFMA blocks per wave (wave rows: TM / 4)
   constexpr int BROWS = UP_N * NMAT;       // weight rows per stage (up rows, then gate rows)
   constexpr int NSUB = UP_N / 2 / 32;      // 32-neuron MFMA blocks per wave
   constexpr int NW = UP_T / WAVE;          // 8 waves
-  constexpr int AI = UP_M / 16 / NW;       // A copy instructions per wave and stage (2)
+  constexpr int AI = TM / 16 / NW;         // A copy instructions per wave and stage (2)
   constexpr int BI = BROWS / 16 / NW;      // B copy instructions per wave and stage (2)
   constexpr int NB = NSUB * NMAT;
-  static_assert(AI * NW * 16 == UP_M && BI * NW * 16 == BROWS, "whole copy instructions");
+  static_assert(AI * NW * 16 == TM && BI * NW * 16 == BROWS, "whole copy instructions");
   // one array per ring slot (not one indexed array): the compiler then sees that a stage's reads
   // and the copies in flight into the other slots touch different memory, and does not make the
   // reads wait for those copies
-  __shared__ u32x4 sA0[UP_M * UQ_DK], sA1[UP_M * UQ_DK], sA2[UP_M * UQ_DK], sA3[UP_M * UQ_DK];
+  __shared__ u32x4 sA0[TM * UQ_DK], sA1[TM * UQ_DK], sA2[TM * UQ_DK], sA3[TM * UQ_DK];
   __shared__ u32x4 sB0[BROWS * UQ_DK], sB1[BROWS * UQ_DK], sB2[BROWS * UQ_DK], sB3[BROWS * UQ_DK];
   static_assert(UQ_NS == 4, "four ring slots");
   if (a.run_if && *a.run_if != a.run_want) return;
-  const int nb_m = (a.M + UP_M - 1) / UP_M, nb_n = (a.ffn + UP_N - 1) / UP_N;
+  const int nb_m = (a.M + TM - 1) / TM, nb_n = (a.ffn + UP_N - 1) / UP_N;
   const int nks = EPI == EPI_ZPART ? a.kslices : 1;
   const int tile = xcd_tile(nb_m * nb_n * nks);
   if (tile >= nb_m * nb_n * nks) return;
   int mt, nt, kslice;
   gemm_tile(tile, nb_m, nb_n, mt, nt, kslice);
-  const int m0 = mt * UP_M, n0 = nt * UP_N;
+  const int m0 = mt * TM, n0 = nt * UP_N;
   const int tid = threadIdx.x, lane = tid & (WAVE - 1);
   const int wave = wave_uniform(tid / WAVE);             // scalar: the copies' LDS base
   const int r32 = lane & 31, g = lane >> 5;
@@ -325,9 +329,9 @@ __global__ __launch_bounds__(UP_T) void k_dupq(DenseArgs a) {
   };
   constexpr int PER_STAGE = AI + BI;       // copy instructions per wave and stage
 
-  f32x16 acc[2][NSUB][NMAT];
+  f32x16 acc[MS][NSUB][NMAT];
 #pragma unroll
-  for (int ms = 0; ms < 2; ++ms)
+  for (int ms = 0; ms < MS; ++ms)
 #pragma unroll
     for (int ns = 0; ns < NSUB; ++ns)
 #pragma unroll
@@ -350,11 +354,11 @@ __global__ __launch_bounds__(UP_T) void k_dupq(DenseArgs a) {
     issue_fence();
     copy(st + 3, nA, nB);
     issue_fence();
-    u32x4 fa[2][2], fb[2][NB];
+    u32x4 fa[2][MS], fb[2][NB];
 #pragma unroll
     for (int kk = 0; kk < UQ_DK / 2; ++kk) {
 #pragma unroll
-      for (int ms = 0; ms < 2; ++ms) fa[kk][ms] = frag(pa, wm * 64 + ms * 32 + r32, 2 * kk + g);
+      for (int ms = 0; ms < MS; ++ms) fa[kk][ms] = frag(pa, wm * (TM / 4) + ms * 32 + r32, 2 * kk + g);
 #pragma unroll
       for (int ns = 0; ns < NSUB; ++ns)
 #pragma unroll
@@ -368,12 +372,12 @@ __global__ __launch_bounds__(UP_T) void k_dupq(DenseArgs a) {
 #pragma unroll
         for (int mt = 0; mt < NMAT; ++mt)
 #pragma unroll
-          for (int ms = 0; ms < 2; ++ms)
+          for (int ms = 0; ms < MS; ++ms)
             acc[ms][ns][mt] = mma16(fa[kk][ms], fb[kk][ns * NMAT + mt], acc[ms][ns][mt]);
     // every fragment read of the stage first, then the MFMAs (the second step's reads land
     // while the first step's MFMAs run)
-    sched_group<0x100, UQ_DK / 2 * (2 + NB)>();
-    sched_group<0x008, UQ_DK / 2 * 2 * NB>();
+    sched_group<0x100, UQ_DK / 2 * (MS + NB)>();
+    sched_group<0x008, UQ_DK / 2 * MS * NB>();
   };
   int st = 0;
   for (; st + 4 <= nst; st += 4) {
@@ -397,18 +401,15 @@ __global__ __launch_bounds__(UP_T) void k_dupq(DenseArgs a) {
   if constexpr (EPI == EPI_ZPART) {
     const int N = a.ffn;                                  // the rank
 #pragma unroll
-    for (int ns = 0; ns < NSUB; ++ns) {
-      const int n = n0 + wn * (UP_N / 2) + ns * 32 + r32;
+    for (int ns = 0; ns < NSUB; ++ns)
 #pragma unroll
-      for (int ms = 0; ms < 2; ++ms)
+      for (int ms = 0; ms < MS; ++ms)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int m = m0 + wm * 64 + ms * 32 + acc_row(i, lane);
-          if (m < a.M && n < N)
-            a.zpart_out[(size_t)(m / 32) * a.zpart_ps + ((size_t)kslice * 32 + m % 32) * N + n] =
-                acc[ms][ns][0][i];
+          int m, n;
+          zpart_store_pos(m0, n0, TM, UP_N, wave, ms, ns, i, lane, m, n);
+          if (m < a.M && n < N) a.zpart_out[zpart_offset(m, kslice, n, N, a.zpart_ps)] = acc[ms][ns][0][i];
         }
-    }
     return;
   }
 
@@ -825,13 +826,14 @@ int dense_ks(int M, int d, int ffn) {
 hipError_t launch_dense_zpart(const DenseArgs& a, hipStream_t st) {
   if (a.d % (8 * UQ_DK) || a.kslices < 1 || a.kslices > a.d / (8 * UQ_DK) || a.has_gate)
     return hipErrorInvalidValue;
-  const int t = ((a.M + UP_M - 1) / UP_M) * ((a.ffn + 255) / 256) * a.kslices;
-  hipLaunchKernelGGL((k_dupq<false, EPI_ZPART>), dim3(8 * ((t + 7) / 8)), dim3(UP_T), 0, st, a);
+  const int t = ((a.M + ZP_M - 1) / ZP_M) * ((a.ffn + ZP_N - 1) / ZP_N) * a.kslices;
+  hipLaunchKernelGGL((k_dupq<false, EPI_ZPART, ZP_M, ZP_N>), dim3(8 * ((t + 7) / 8)), dim3(UP_T), 0,
+                     st, a);
   return hipGetLastError();
 }
 
 int zpart_kslices(int M, int d, int rank) {
-  const int tiles = ((M + UP_M - 1) / UP_M) * ((rank + 255) / 256);
+  const int tiles = ((M + ZP_M - 1) / ZP_M) * ((rank + ZP_N - 1) / ZP_N);
   return std::max(1, std::min({ZPART_MAX_KS, (256 + tiles - 1) / tiles, d / (8 * UQ_DK)}));
 }
 

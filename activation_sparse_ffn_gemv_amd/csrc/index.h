@@ -118,6 +118,23 @@ __host__ __device__ inline bool dense_down_wide(int M) {
   return (M + DQ_M - 1) / DQ_M * DQ_M == (M + DD_M - 1) / DD_M * DD_M;
 }
 
+// Predictor stage 1 of a large call (Z = X P1^T, rank columns): 128 tokens x 128 columns per
+// tile, so that the GPU fills with fewer K slices (fewer fp32 partials to write and sum).
+constexpr int ZP_M = 128, ZP_N = 128;
+
+// Stage-1 GEMM epilogue: accumulator element i of lane's block (ms, ns) of wave `wave` (8 waves,
+// 2 per row of the tile) in the tm x tn tile at (m0, n0) -> token m, rank column n.
+__host__ __device__ inline void zpart_store_pos(int m0, int n0, int tm, int tn, int wave, int ms,
+                                                int ns, int i, int lane, int& m, int& n) {
+  m = m0 + (wave >> 1) * (tm / 4) + ms * 32 + acc_row(i, lane);
+  n = n0 + (wave & 1) * (tn / 2) + ns * 32 + (lane & 31);
+}
+// Offset of (token m, K slice k, column n) of the stage-1 partials, per-pass layout
+// [pass = m / 32][slice][m % 32][N] with zpart_ps elements per pass.
+__host__ __device__ inline size_t zpart_offset(int m, int k, int n, int N, size_t zpart_ps) {
+  return (size_t)(m / 32) * zpart_ps + ((size_t)k * 32 + m % 32) * N + n;
+}
+
 // k_ddq's partial-sum store of lane `lane` of wave `wave`, 32-token block ms, accumulator
 // element i: token m and the first of the lane's four consecutive columns col (MFMA block b
 // holds column 4 (lane % 32) + b of the wave's 128).

@@ -252,9 +252,10 @@ struct DenseArgs {
   int head_words;             // words [0, head_words): every neuron on, no score
   size_t b_rowb;
   int bwrap;
-  // predictor stage 1 of a large call on the same GEMM kernel (launch_dense_zpart): Z = X P1^T
-  // with x = X, w_up = P1, ffn = rank, split over d into kslices slices; the fp32 partials go to
-  // zpart_out in the batched path's per-pass layout ([pass][slice][32][rank], zpart_ps per pass)
+  // predictor stage 1 of a large call on the same GEMM kernel (launch_dense_zpart; tiles of
+  // ZP_M x ZP_N): Z = X P1^T with x = X, w_up = P1, ffn = rank, split over d into kslices slices;
+  // the fp32 partials go to zpart_out in the batched path's per-pass layout
+  // ([pass][slice][32][rank], zpart_ps per pass)
   float* zpart_out;
   size_t zpart_ps;
   int kslices;

@@ -4,7 +4,7 @@
 // its buffer, the gather's partial writes and the reduce's reads must address the same elements,
 // the work splits must partition their ranges exactly, and no 32-bit product may wrap.  The
 // shapes come from the built library's own host functions (workgroup counts, tiles, the batched
-// path's buffer shapes, the dense down projection's K slices).  Exit status 0 and "index check: OK" when every check holds.
+// path's buffer shapes, the dense down projection's and the stage-1 GEMM's K slices).  Exit status 0 and "index check: OK" when every check holds.
 #include <stdio.h>
 #include <stdlib.h>
 
@@ -223,6 +223,56 @@ static void check_dense_down(int M, int d, int ffn) {
   CHECK(prev == nst_all, "slices do not cover the ffn stages: M %d", M);
 }
 
+// Predictor stage 1 of a large call (the GEMM's ZP_M x ZP_N tiles, split over d): the grid's
+// tiles are each (token tile, rank tile, K slice) once, the slices split d's 32-wide stages with
+// none empty, and every (token, slice, rank column) element of the per-pass partials
+// [pass][slice][32][rank] is stored exactly once, inside the passes' buffer.
+static void check_zpart(int M, int d, int rank) {
+  const int ks = zpart_kslices(M, d, rank), nst_all = d / 32;
+  CHECK(ks >= 1 && ks <= ZPART_MAX_KS && ks <= nst_all, "M %d d %d rank %d: %d K slices", M, d,
+        rank, ks);
+  if (ks < 1 || ks > nst_all) return;
+  const int nb_m = (M + ZP_M - 1) / ZP_M, nb_n = (rank + ZP_N - 1) / ZP_N;
+  const int total = nb_m * nb_n * ks, grid = 8 * ((total + 7) / 8);
+  const size_t zpart_ps = (size_t)ks * 32 * rank, passes = (M + 31) / 32;
+  const size_t nel = passes * zpart_ps;
+  std::vector<unsigned char> seen(total, 0), el(nel, 0);
+  for (int b = 0; b < grid; ++b) {
+    const int tile = xcd_tile_of(b, total);
+    if (tile < 0 || tile >= total) continue;
+    CHECK(!seen[tile], "tile %d given twice (M %d rank %d)", tile, M, rank);
+    seen[tile] = 1;
+    int mt, nt, k;
+    gemm_tile(tile, nb_m, nb_n, mt, nt, k);
+    int s0, n;
+    slice_stages(nst_all, k, ks, s0, n);
+    CHECK(n >= 1 && s0 >= 0 && s0 + n <= nst_all, "slice %d of %d: stages [%d, %d)", k, ks, s0,
+          s0 + n);
+    for (int wave = 0; wave < 8; ++wave)
+      for (int ms = 0; ms < ZP_M / 4 / 32; ++ms)
+        for (int ns = 0; ns < ZP_N / 2 / 32; ++ns)
+          for (int i = 0; i < 16; ++i)
+            for (int lane = 0; lane < 64; ++lane) {
+              int m, c;
+              zpart_store_pos(mt * ZP_M, nt * ZP_N, ZP_M, ZP_N, wave, ms, ns, i, lane, m, c);
+              if (m >= M || c >= rank) continue;             // the kernel's own guard
+              const size_t off = zpart_offset(m, k, c, rank, zpart_ps);
+              CHECK(off < nel, "store past the partials: M %d rank %d off %zu", M, rank, off);
+              if (off < nel) {
+                CHECK(!el[off], "element stored twice: M %d k %d m %d c %d", M, k, m, c);
+                el[off] = 1;
+              }
+            }
+  }
+  for (int t = 0; t < total; ++t) CHECK(seen[t], "tile %d never given (M %d rank %d)", t, M, rank);
+  size_t missing = 0;
+  for (size_t e = 0; e < nel; ++e) {
+    const size_t p = e / zpart_ps, m = p * 32 + e % zpart_ps / rank % 32;
+    if (m < (size_t)M) missing += !el[e];                    // rows past the last token: unused
+  }
+  CHECK(missing == 0, "M %d d %d rank %d: %zu partial elements never stored", M, d, rank, missing);
+}
+
 int main() {
   const int ds[] = {64, 256, 512, 768, 776, 1024, 4096, 4104, 8192};
   const int ffns[] = {256, 1024, 3072, 11008, 14336, 32768};
@@ -243,6 +293,9 @@ int main() {
                             {385, 4096, 11008}, {512, 8192, 32768}, {1000, 1024, 4096},
                             {4096, 512, 2048}};
   for (const auto& sh : dshapes) check_dense_down(sh[0], sh[1], sh[2]);
+  const int zshapes[][3] = {{128, 4096, 256}, {130, 4096, 512}, {512, 8192, 1024},
+                            {300, 768, 64}, {4096, 2048, 2048}, {1000, 512, 96}};
+  for (const auto& sh : zshapes) check_zpart(sh[0], sh[1], sh[2]);
   if (failures) {
     printf("index check: %ld of %ld checks failed\n", failures, checks);
     return 1;

@@ -92,7 +92,7 @@ def test_kernel_index_arithmetic_in_a_cpu_build(tmp_path):
     walked over every workgroup and thread of the library's launch shapes (tests/index_check.cpp:
     partial-sum writes and reads, rank and segment splits, the XCD-ordered (block, pass) map, the
     per-pass buffer offsets of calls that run all their passes in one launch, and the dense down
-    projection's tile map, K slices and partial-sum stores)."""
+    projection's and the stage-1 GEMM's tile maps, K slices and partial-sum stores)."""
     lib_dir = os.path.join(ROOT, "activation_sparse_ffn_gemv_amd")
     if not os.path.exists(os.path.join(lib_dir, "libffn_sparse.so")):
         pytest.skip("library not built")
