@@ -1129,7 +1129,7 @@ ffn_status ffn_plan_set_decode_variant(ffn_plan* p, int32_t variant) {
     return fail(FFN_ERR_UNSUPPORTED, "the fused decode variant does not read a neuron cache");
   if (variant == 1 && (!fused_supported(wk, D.d) || D.rank == 0))
     return fail(FFN_ERR_UNSUPPORTED, "the fused decode variant needs fp32 / fp16 rows of "
-                "%d..%d chunks and a predictor", 256, 1024);
+                "%d..%d chunks and a predictor", 64, 1024);
   p->decode_variant = variant;
   return FFN_OK;
 }

@@ -1061,11 +1061,12 @@ int reduce_tiles(int d) { return (d + RD_TW - 1) / RD_TW; }
 
 int fused_blocks(int ffn) { return (ffn + FU_ROWS - 1) / FU_ROWS; }
 
-// fp32 / fp16 rows of at least 512 chunks per 512 threads (one or two chunks per thread)
+// fp32 / fp16 rows of 64 to 1024 16-byte chunks (one or two chunks per thread; threads past a
+// narrower row load a clamped chunk, multiply it by a zero token slice and store nothing)
 bool fused_supported(int wk, int d) {
   if (wk == WK_I4) return false;
   const int nch = d / (wk == WK_F32 ? 4 : 8);
-  return nch >= FU_THREADS / 2 && nch <= 2 * FU_THREADS;
+  return nch >= WAVE && nch <= 2 * FU_THREADS;
 }
 
 template <int WK, int CPT, int CPR>

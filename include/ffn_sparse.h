@@ -182,7 +182,7 @@ ffn_status ffn_plan_path_flag(const ffn_plan *plan, const int32_t **flag);
  * Batch-1 decode variant (a tuning knob; results agree within rounding).  0: the predictor's
  * second stage and a rank-balanced gather are separate launches (the default); 1: one fused
  * launch in which every workgroup scores 64 neurons and gathers its own active ones (one launch
- * and one scan fewer, no balancing).  1 needs fp32 / fp16 rows of 256..1024 16-byte chunks and
+ * and one scan fewer, no balancing).  1 needs fp32 / fp16 rows of 64..1024 16-byte chunks and
  * a predictor (FFN_ERR_UNSUPPORTED otherwise); calls with a caller mask use variant 0.
  */
 ffn_status ffn_plan_set_decode_variant(ffn_plan *plan, int32_t variant);

@@ -268,7 +268,8 @@ def test_index_and_count_outputs_are_independent(ffn):
 
 @pytest.mark.parametrize("cfgname,tokens", [("llama2_7b_reglu_f16", 3),
                                             ("turbosparse_mistral_7b_drelu_f16", 2),
-                                            ("falcon_40b_relu_f16", 1)])
+                                            ("falcon_40b_relu_f16", 1),
+                                            ("opt125m_relu_f32", 8)])
 def test_fused_decode_variant(ffn, cfgname, tokens):
     """The fused predictor + gather variant against the oracle (and the balanced variant)."""
     cfg = synth.CONFIGS[cfgname]
