@@ -15,6 +15,9 @@ only compiles it with gcc, marshals numpy arrays and composes per-token calls:
   citnews, "Dynamic neuron cache": inactive neurons do not change the output).
 * ``router``/``moe`` -- top-k softmax router and the weighted sum of the chosen experts
   (TurboSparse-Mixtral, nubint.ai review and citnews).
+* ``attn_kv``/``attn``/``attn_token`` -- the self-attention block of one token over a key/value
+  cache with a head-level active set (unite.ai, "Adaptive sparse predictor": a second predictor
+  per layer for the self-attention block; the unit it predicts is read as a head).
 * ``NeuronCache`` -- the LRU neuron cache of host-resident FFN rows (citnews, "Dynamic neuron
   cache": an LRU pool of neurons, segmented by weight type).
 
@@ -67,6 +70,10 @@ def lib():
         L.oracle_ffn.argtypes = [L_, L_, I, I, P, P, P, P, P, P, P, P, P, I, P, P, P, P]
         L.oracle_router.restype = None
         L.oracle_router.argtypes = [L_, L_, L_, I, P, I, P, P, P, P]
+        L.oracle_attn_kv.restype = None
+        L.oracle_attn_kv.argtypes = [L_, L_, L_, I, P, P, I, P, P, P]
+        L.oracle_attn.restype = None
+        L.oracle_attn.argtypes = [L_, L_, L_, L_, L_, L_, I, P, P, I, P, P, I, P, P, P, P]
         _lib = L
     return _lib
 
@@ -222,6 +229,59 @@ def moe_token(experts, R, x, k: int = 2, masks=None):
         preds.append(pred)
         y += w[t] * ye
     return y, ids, w, preds
+
+
+def attn_kv(w_k, w_v, x, e: int):
+    """Key and value of one token for every key/value head: (k, v) float64 [G*e] each."""
+    L = lib()
+    rows, d = w_k.shape
+    assert w_v.shape == (rows, d) and w_v.dtype == w_k.dtype and x.shape == (d,) and rows % e == 0
+    k = np.empty(rows, np.float64)
+    v = np.empty(rows, np.float64)
+    L.oracle_attn_kv(d, rows // e, e, _dtype_code(w_k), _ptr(w_k), _ptr(w_v), _dtype_code(x),
+                     _ptr(x), _ptr(k), _ptr(v))
+    return k, v
+
+
+def attn(w_q, w_o_t, Kc, Vc, x, t: int, mask=None):
+    """Output of the attention block for the token at position t over the cache Kc, Vc
+    ([G][S][e], positions 0..t filled, t being the token's own).  mask uint8 [H] or None (every
+    head).  Returns (y float64[d], o float64[H][e])."""
+    L = lib()
+    G, S, e = Kc.shape
+    He, d = w_q.shape
+    H = He // e
+    assert He == H * e and w_o_t.shape == (He, d) and Vc.shape == Kc.shape and Vc.dtype == Kc.dtype
+    assert H % G == 0 and 0 <= t < S and x.shape == (d,) and e <= 512
+    if mask is not None:
+        mask = np.ascontiguousarray(mask, dtype=np.uint8)
+        assert mask.shape == (H,)
+    o = np.empty(He, np.float64)
+    y = np.empty(d, np.float64)
+    L.oracle_attn(d, H, G, e, S, t, _dtype_code(w_q), _ptr(w_q), _ptr(w_o_t), _dtype_code(Kc),
+                  _ptr(Kc), _ptr(Vc), _dtype_code(x), _ptr(x), _ptr(mask), _ptr(o), _ptr(y))
+    return y, o.reshape(H, e)
+
+
+def attn_token(layer: dict, Kc, Vc, x, t: int, mask=None):
+    """One token through the attention block at position t: the head predictor (unless a mask is
+    given), this token's key and value for every key/value head, stored at position t of copies
+    of the caches in the caches' dtype (numpy's round-to-nearest-even conversion), then ``attn``
+    over the active heads.  ``layer`` holds numpy w_q, w_k, w_v, w_o_t, p1, p2, c1, c2, tau and
+    head_dim.  Returns (y, pred dict|None, Kc', Vc')."""
+    e = int(layer["head_dim"])
+    pred = None
+    if mask is None:
+        pred = predictor(layer["p1"], layer["p2"], layer.get("c1"), layer.get("c2"), x,
+                         layer["tau"])
+        mask = pred["active"]
+    k, v = attn_kv(layer["w_k"], layer["w_v"], x, e)
+    G = Kc.shape[0]
+    Kn, Vn = Kc.copy(), Vc.copy()
+    Kn[:, t, :] = k.reshape(G, e).astype(Kc.dtype)
+    Vn[:, t, :] = v.reshape(G, e).astype(Vc.dtype)
+    y, _ = attn(layer["w_q"], layer["w_o_t"], Kn, Vn, x, t, mask)
+    return y, pred, Kn, Vn
 
 
 PINNED = 0xFFFFFFFF

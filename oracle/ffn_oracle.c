@@ -27,7 +27,10 @@
  *  - int4: signed two's-complement nibble, element 2k in the low nibble of byte k, one fp16 scale
  *    per 32 consecutive elements of a row, w = scale * q;
  *  - MoE router: logits l = R x, top-k with ties to the lower expert index, weights = softmax over
- *    the k selected logits.
+ *    the k selected logits;
+ *  - attention block: the predicted unit is a head (W_q rows, scores, values, W_o columns); keys
+ *    and values are computed for every head; scores scaled by 1/sqrt(head width), plain softmax,
+ *    no positional rotation and no biases (the pages name none).
  */
 #include <math.h>
 #include <stdint.h>
@@ -211,4 +214,102 @@ void oracle_router(long d, long n_exp, long k, int r_dtype, const void *R, int x
         den += exp(logits[ids[t]] - mx);
     for (t = 0; t < k; ++t)
         w[t] = exp(logits[ids[t]] - mx) / den;
+}
+
+/*
+ * Self-attention block of one token with a head-level active set.  [UA] "Adaptive sparse
+ * predictor" gives every transformer layer a second predictor, for its self-attention block,
+ * and [UA] "Online stage" restricts computation to what is predicted active.  The pages do not
+ * say what the attention block's unit is; the reading here is one head: its W_q rows, its share
+ * of the scores and values, and its W_o columns (the only unit whose contribution enters the
+ * block's output as one additive term, as a neuron's row does in the FFN).
+ *
+ * Shapes: H query heads and G key/value heads of width e (H a multiple of G; query head h reads
+ * key/value head h / (H / G)).  W_q and W_o_t are [H*e][d], W_k and W_v [G*e][d], row-major in
+ * w_dtype; row h*e + c of W_q is channel c of head h, and row h*e + c of W_o_t holds the weights
+ * from channel c of head h to the d outputs (the output projection stored transposed, so that a
+ * head contributes whole rows).
+ *
+ * oracle_attn_kv: key and value of the token for every key/value head, active or not: a head
+ * predicted inactive now may be active for a later token, whose scores then need this token's
+ * key and value, so the cache stays exactly that of the dense model.
+ *   k[g*e + c] = W_k[g*e + c] . x ;   v[g*e + c] = W_v[g*e + c] . x
+ */
+void oracle_attn_kv(long d, long G, long e, int w_dtype, const void *w_k, const void *w_v,
+                    int x_dtype, const void *x, double *k, double *v)
+{
+    long r, j;
+    for (r = 0; r < G * e; ++r) {
+        double ak = 0.0, av = 0.0;
+        for (j = 0; j < d; ++j) {
+            ak += oracle_elem(w_dtype, w_k, NULL, r, j, d) * vec_elem(x_dtype, x, j);
+            av += oracle_elem(w_dtype, w_v, NULL, r, j, d) * vec_elem(x_dtype, x, j);
+        }
+        k[r] = ak;
+        v[r] = av;
+    }
+}
+
+/*
+ * oracle_attn: the block's output for the token at position t, over a cache Kc, Vc
+ * ([G][S][e] in kv_dtype, S >= t + 1) whose positions 0..t hold the keys and values of the
+ * token's context and of the token itself (position t); positions past t are never read.
+ *   for h with mask_h = 1 (mask == NULL: every head), g = h / (H / G):
+ *     q_h = W_q[h] x                                   (e values)
+ *     a_j = (q_h . Kc[g][j]) / sqrt(e),   j = 0..t
+ *     p_j = exp(a_j - max a) / sum_i exp(a_i - max a)
+ *     o_h = sum_j p_j Vc[g][j]
+ *   for h with mask_h = 0: o_h = 0
+ *   y = sum_{h: mask_h = 1} sum_c o_h[c] W_o_t[h*e + c]
+ * Outputs o[H*e] and y[d] in double.
+ */
+void oracle_attn(long d, long H, long G, long e, long S, long t, int w_dtype, const void *w_q,
+                 const void *w_o_t, int kv_dtype, const void *Kc, const void *Vc, int x_dtype,
+                 const void *x, const uint8_t *mask, double *o, double *y)
+{
+    long h, c, j;
+    double scale = 1.0 / sqrt((double)e);
+    for (j = 0; j < d; ++j)
+        y[j] = 0.0;
+    for (h = 0; h < H; ++h) {
+        long g = h / (H / G);
+        double mx = -INFINITY, den = 0.0;
+        double q[512];                      /* e <= 512 */
+        for (c = 0; c < e; ++c)
+            o[h * e + c] = 0.0;
+        if (mask && !mask[h])
+            continue;
+        for (c = 0; c < e; ++c) {
+            double acc = 0.0;
+            for (j = 0; j < d; ++j)
+                acc += oracle_elem(w_dtype, w_q, NULL, h * e + c, j, d) * vec_elem(x_dtype, x, j);
+            q[c] = acc;
+        }
+        /* scores, their maximum, and the softmax denominator */
+        for (j = 0; j <= t; ++j) {
+            double a = 0.0;
+            for (c = 0; c < e; ++c)
+                a += q[c] * oracle_elem(kv_dtype, Kc, NULL, g * S + j, c, e);
+            a *= scale;
+            if (a > mx)
+                mx = a;
+        }
+        for (j = 0; j <= t; ++j) {
+            double a = 0.0;
+            for (c = 0; c < e; ++c)
+                a += q[c] * oracle_elem(kv_dtype, Kc, NULL, g * S + j, c, e);
+            den += exp(a * scale - mx);
+        }
+        for (j = 0; j <= t; ++j) {
+            double a = 0.0, p;
+            for (c = 0; c < e; ++c)
+                a += q[c] * oracle_elem(kv_dtype, Kc, NULL, g * S + j, c, e);
+            p = exp(a * scale - mx) / den;
+            for (c = 0; c < e; ++c)
+                o[h * e + c] += p * oracle_elem(kv_dtype, Vc, NULL, g * S + j, c, e);
+        }
+        for (c = 0; c < e; ++c)
+            for (j = 0; j < d; ++j)
+                y[j] += o[h * e + c] * oracle_elem(w_dtype, w_o_t, NULL, h * e + c, j, d);
+    }
 }

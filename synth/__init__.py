@@ -24,7 +24,12 @@ are scattered through the matrix):
   P2[i, k] = W_src[i, S_k] (W_src = up for ReLU, gate otherwise), c2_i = |P2[i]| * Phi^-1(p_i),
   c1 absent, threshold tau = 0.5 -- the predicted set has density ~ p_i and tracks the true set;
 * router of a mixture of experts: R[e] ~ N(0, 0.02^2), fp16;
-* tokens x ~ N(0, 1) drawn independently per (token, layer), stored in the activation dtype.
+* tokens x ~ N(0, 1) drawn independently per (token, layer), stored in the activation dtype;
+* attention block (``AttnConfig``): W_q, W_k, W_v, W_o_t ~ N(0, 0.02^2) in fp16; a head
+  predictor of the same selector form (P1 picks r input coordinates, P2 [heads][r] ~ N(0, 1),
+  c2_h = |P2[h]| * Phi^-1(density), so each head is predicted active with probability
+  ``density`` for x ~ N(0, I)); the key/value cache of the context ~ N(0, (0.02 sqrt d)^2) in
+  fp16, the spread of W_k x for such tokens.
 
 All random draws use torch generators seeded from (base seed, layer, expert, tensor id), on the
 device the tensors are made on.
@@ -91,6 +96,81 @@ CONFIGS = {
         batches=(1, 8, 32), seed=1005),
 }
 CONFIG_ORDER = list(CONFIGS)
+
+
+@dataclass(frozen=True)
+class AttnConfig:
+    """A self-attention block: H query heads, G key/value heads of width e, a head predictor of
+    rank r, and a token at position ``context`` (positions 0..context-1 already in the cache)."""
+    name: str
+    d: int
+    heads: int
+    kv_heads: int
+    head_dim: int
+    rank: int
+    density: float            # probability that a head is predicted active
+    context: int
+    max_seq: int = 0          # cache positions per head (0: context + 1)
+    p_dtype: str = F16
+    layers: int = 1
+    tau: float = 0.5
+    seed: int = 2000
+
+    @property
+    def seq(self) -> int:
+        return self.max_seq if self.max_seq else self.context + 1
+
+
+# Attention blocks of the pages' dense-attention models (Llama-2-7B: 32 heads of 128; Mistral-7B:
+# 32 query heads sharing 8 key/value heads), at a 512-token context.  The pages print no
+# head-level activity figure; half the heads active is the stand-in.
+ATTN_CONFIGS = {
+    "llama2_7b_attn_f16": AttnConfig("llama2_7b_attn_f16", d=4096, heads=32, kv_heads=32,
+                                     head_dim=128, rank=128, density=0.5, context=511,
+                                     layers=32, seed=2001),
+    "mistral_7b_attn_f16": AttnConfig("mistral_7b_attn_f16", d=4096, heads=32, kv_heads=8,
+                                      head_dim=128, rank=128, density=0.5, context=511,
+                                      layers=32, seed=2002),
+}
+
+
+def make_attn_layer(cfg: AttnConfig, layer: int = 0, device="cpu") -> dict:
+    """All tensors of one attention block of ``cfg`` (weights, head predictor) on ``device``."""
+    d, H, G, e, r = cfg.d, cfg.heads, cfg.kv_heads, cfg.head_dim, cfg.rank
+
+    def w(rows, tid):
+        t = torch.randn(rows, d, generator=_gen(device, _seed(cfg, layer, 0, tid)),
+                        device=device, dtype=torch.float32) * 0.02
+        return t.to(torch.float16).contiguous()
+
+    out = {"cfg": cfg, "tau": cfg.tau, "head_dim": e, "layer": layer,
+           "w_q": w(H * e, 11), "w_k": w(G * e, 12), "w_v": w(G * e, 13), "w_o_t": w(H * e, 14)}
+    sel = np.random.Generator(np.random.PCG64(_seed(cfg, layer, 0, 15))).choice(
+        d, size=r, replace=False)
+    pt = _tdtype(cfg.p_dtype)
+    p1 = torch.zeros(r, d, dtype=pt, device=device)
+    p1[torch.arange(r, device=device), torch.from_numpy(sel.astype(np.int64)).to(device)] = 1
+    p2 = torch.randn(H, r, generator=_gen(device, _seed(cfg, layer, 0, 16)), device=device,
+                     dtype=torch.float32).to(pt).contiguous()
+    c2 = (p2.double().norm(dim=1) * float(_ndtri(np.array([cfg.density]))[0])).float()
+    out.update(p1=p1.contiguous(), p2=p2, c1=None, c2=c2.contiguous(), selector=sel)
+    return out
+
+
+def make_kv_cache(cfg: AttnConfig, layer: int = 0, device="cpu"):
+    """Key and value caches [G][seq][e] fp16 of one block; every position holds a seeded value
+    (positions from ``context`` on are overwritten by the tokens that run)."""
+    shape = (cfg.kv_heads, cfg.seq, cfg.head_dim)
+    sd = 0.02 * np.sqrt(cfg.d)
+    K = torch.randn(*shape, generator=_gen(device, _seed(cfg, layer, 0, 17)), device=device) * sd
+    V = torch.randn(*shape, generator=_gen(device, _seed(cfg, layer, 0, 18)), device=device) * sd
+    return K.to(torch.float16).contiguous(), V.to(torch.float16).contiguous()
+
+
+def make_attn_tokens(cfg: AttnConfig, n: int, layer: int = 0, device="cpu") -> torch.Tensor:
+    """n tokens x ~ N(0, 1) [n][d] fp16 for one attention block."""
+    g = _gen(device, _seed(cfg, layer, 0, 1019))
+    return torch.randn(n, cfg.d, generator=g, device=device).to(torch.float16).contiguous()
 
 
 def small_config(**kw) -> LayerConfig:

@@ -25,6 +25,11 @@ void oracle_ffn(long d, long ffn, int act, int w_dtype,
                 int x_dtype, const void *x, const uint8_t *mask, double *h, double *y);
 void oracle_router(long d, long n_exp, long k, int r_dtype, const void *R, int x_dtype,
                    const void *x, double *logits, int32_t *ids, double *w);
+void oracle_attn_kv(long d, long G, long e, int w_dtype, const void *w_k, const void *w_v,
+                    int x_dtype, const void *x, double *k, double *v);
+void oracle_attn(long d, long H, long G, long e, long S, long t, int w_dtype, const void *w_q,
+                 const void *w_o_t, int kv_dtype, const void *Kc, const void *Vc, int x_dtype,
+                 const void *x, const uint8_t *mask, double *o, double *y);
 
 static uint64_t state = 0x9e3779b97f4a7c15ull;
 static uint32_t next_u32(void)
@@ -155,6 +160,42 @@ static int run_router(long d, long n_exp, long k)
     return ok;
 }
 
+/* Attention block: caches sized for exactly t + 1 positions (so a read past t is reported), the
+ * output additive over a split of the heads, and every-head == no mask. */
+static int run_attn(long d, long H, long G, long e, long t)
+{
+    long i, S = t + 1;
+    uint16_t *wq = malloc(sizeof(uint16_t) * H * e * d), *wo = malloc(sizeof(uint16_t) * H * e * d);
+    uint16_t *wk = malloc(sizeof(uint16_t) * G * e * d), *wv = malloc(sizeof(uint16_t) * G * e * d);
+    uint16_t *K = malloc(sizeof(uint16_t) * G * S * e), *V = malloc(sizeof(uint16_t) * G * S * e);
+    uint16_t *x = malloc(sizeof(uint16_t) * d);
+    uint8_t *m1 = malloc(H), *m2 = malloc(H), *all = malloc(H);
+    double *k = malloc(sizeof(double) * G * e), *v = malloc(sizeof(double) * G * e);
+    double *o = malloc(sizeof(double) * H * e);
+    double *y = malloc(sizeof(double) * d), *y1 = malloc(sizeof(double) * d);
+    double *y2 = malloc(sizeof(double) * d), *ya = malloc(sizeof(double) * d);
+    int ok = 1;
+    for (i = 0; i < H * e * d; ++i) { wq[i] = rand_half(); wo[i] = rand_half(); }
+    for (i = 0; i < G * e * d; ++i) { wk[i] = rand_half(); wv[i] = rand_half(); }
+    for (i = 0; i < G * S * e; ++i) { K[i] = rand_half(); V[i] = rand_half(); }
+    for (i = 0; i < d; ++i) x[i] = rand_half();
+    for (i = 0; i < H; ++i) { m1[i] = (uint8_t)(next_u32() & 1); m2[i] = (uint8_t)!m1[i]; all[i] = 1; }
+    oracle_attn_kv(d, G, e, 1, wk, wv, 1, x, k, v);
+    oracle_attn(d, H, G, e, S, t, 1, wq, wo, 1, K, V, 1, x, NULL, o, y);
+    oracle_attn(d, H, G, e, S, t, 1, wq, wo, 1, K, V, 1, x, all, o, ya);
+    oracle_attn(d, H, G, e, S, t, 1, wq, wo, 1, K, V, 1, x, m1, o, y1);
+    oracle_attn(d, H, G, e, S, t, 1, wq, wo, 1, K, V, 1, x, m2, o, y2);
+    for (i = 0; i < d; ++i) {
+        ok &= y[i] == ya[i];
+        ok &= fabs(y1[i] + y2[i] - y[i]) <= 1e-9 * (1.0 + fabs(y[i]));
+    }
+    for (i = 0; i < G * e; ++i) ok &= isfinite(k[i]) && isfinite(v[i]);
+    free(wq); free(wo); free(wk); free(wv); free(K); free(V); free(x); free(m1); free(m2);
+    free(all); free(k); free(v); free(o); free(y); free(y1); free(y2); free(ya);
+    if (!ok) fprintf(stderr, "attn d=%ld H=%ld G=%ld e=%ld t=%ld: identity failed\n", d, H, G, e, t);
+    return ok;
+}
+
 int main(void)
 {
     int ok = 1, act, wd;
@@ -168,6 +209,8 @@ int main(void)
         }
     ok &= run_router(64, 8, 2);
     ok &= run_router(32, 4, 4);
+    ok &= run_attn(32, 4, 2, 8, 0);
+    ok &= run_attn(48, 6, 3, 16, 9);
     printf(ok ? "oracle sanitizer run: OK\n" : "oracle sanitizer run: FAILED\n");
     return ok ? 0 : 1;
 }
