@@ -26,9 +26,12 @@ FFN_PATH_AUTO, FFN_PATH_SPARSE, FFN_PATH_DENSE = 0, 1, 2
 FFN_STAGE_PRED_Z, FFN_STAGE_PRED_S, FFN_STAGE_GATHER, FFN_STAGE_REDUCE = 0, 1, 2, 3
 FFN_STAGE_BATCH_UPGATE, FFN_STAGE_BATCH_DOWN = 4, 5
 FFN_STAGE_DENSE_UP, FFN_STAGE_DENSE_DOWN, FFN_STAGE_DENSE_REDUCE = 6, 7, 8
+FFN_STAGE_ATTN_PROJ, FFN_STAGE_ATTN_SCORES = 9, 10
+FFN_STAGE_ATTN_OUT, FFN_STAGE_ATTN_REDUCE = 11, 12
 STAGES = ("pred_z", "pred_s", "gather", "reduce")          # the batch-1 decode kernels
 BATCH_STAGES = ("batch_upgate", "batch_down")
 DENSE_STAGES = ("dense_up", "dense_down", "dense_reduce")
+ATTN_STAGES = ("pred_z", "attn_proj", "attn_scores", "attn_out", "attn_reduce")
 
 ACT = {"relu": FFN_ACT_RELU, "reglu": FFN_ACT_REGLU, "drelu": FFN_ACT_DRELU}
 DTYPE = {"f32": FFN_F32, "f16": FFN_F16, "i4g32": FFN_I4G32}
@@ -44,6 +47,8 @@ EXPORTS = [
     "ffn_last_error",
     "ffn_moe_workspace_size",
     "ffn_moe_plan", "ffn_moe_forward", "ffn_moe_destroy",
+    "ffn_attn_workspace_size", "ffn_attn_plan", "ffn_attn_forward", "ffn_attn_set_timing_events",
+    "ffn_attn_destroy",
 ]
 
 
@@ -64,6 +69,17 @@ class ffn_layer_weights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in
                 ["w_up", "w_gate", "w_down_t", "s_up", "s_gate", "s_down_t", "b_up", "b_gate",
                  "b_down", "p1", "p2", "c1", "c2"]]
+
+
+class ffn_attn_desc(ctypes.Structure):
+    _fields_ = [("d", ctypes.c_int32), ("heads", ctypes.c_int32), ("kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("rank", ctypes.c_int32),
+                ("max_seq", ctypes.c_int32), ("threshold", ctypes.c_float)]
+
+
+class ffn_attn_weights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ["w_q", "w_k", "w_v", "w_o_t", "p1", "p2", "c1", "c2"]]
 
 
 _lib = None
@@ -128,6 +144,17 @@ def lib():
         L.ffn_moe_forward.argtypes = [P, P, I, P, P, P, P, P]
         L.ffn_moe_destroy.restype = st
         L.ffn_moe_destroy.argtypes = [P]
+        L.ffn_attn_workspace_size.restype = st
+        L.ffn_attn_workspace_size.argtypes = [ctypes.POINTER(ffn_attn_desc), ctypes.POINTER(S)]
+        L.ffn_attn_plan.restype = st
+        L.ffn_attn_plan.argtypes = [ctypes.POINTER(ffn_attn_desc),
+                                    ctypes.POINTER(ffn_attn_weights), P, S, ctypes.POINTER(P)]
+        L.ffn_attn_forward.restype = st
+        L.ffn_attn_forward.argtypes = [P, P, I, P, P, P, P, P, P, P, P]
+        L.ffn_attn_set_timing_events.restype = st
+        L.ffn_attn_set_timing_events.argtypes = [P, I, P, P]
+        L.ffn_attn_destroy.restype = st
+        L.ffn_attn_destroy.argtypes = [P]
         _lib = L
     return _lib
 
@@ -255,6 +282,34 @@ def ffn_moe_forward(moe: int, x: int, B: int, y: int, expert_idx: int = 0, exper
 
 def ffn_moe_destroy(moe: int):
     _check(lib().ffn_moe_destroy(moe))
+
+
+def ffn_attn_workspace_size(desc: ffn_attn_desc) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().ffn_attn_workspace_size(ctypes.byref(desc), ctypes.byref(n)))
+    return n.value
+
+
+def ffn_attn_plan(desc, weights, workspace: int, workspace_bytes: int) -> int:
+    out = ctypes.c_void_p(0)
+    _check(lib().ffn_attn_plan(ctypes.byref(desc), ctypes.byref(weights), workspace,
+                               workspace_bytes, ctypes.byref(out)))
+    return out.value
+
+
+def ffn_attn_forward(plan: int, x: int, pos: int, k_cache: int, v_cache: int, y: int,
+                     mask: int = 0, idx: int = 0, cnt: int = 0, scores: int = 0,
+                     stream: int = 0):
+    _check(lib().ffn_attn_forward(plan, x, pos, k_cache, v_cache, y, mask or None, idx or None,
+                                  cnt or None, scores or None, stream or None))
+
+
+def ffn_attn_set_timing_events(plan: int, stage: int, start: int = 0, stop: int = 0):
+    _check(lib().ffn_attn_set_timing_events(plan, stage, start or None, stop or None))
+
+
+def ffn_attn_destroy(plan: int):
+    _check(lib().ffn_attn_destroy(plan))
 
 
 # ---------------------------------------------------------------------------------------------
@@ -423,6 +478,50 @@ class MoEFFN:
             self.moe = 0
         for e in self.experts:
             e.close()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class SparseAttention:
+    """Holds one attention block's device tensors, its workspace and its plan.
+
+    ``layer`` maps the names of ``ffn_attn_weights`` to device fp16 tensors (c1 / c2 fp32, any
+    may be None where the header allows NULL) and carries ``head_dim``, ``tau`` and the head
+    counts through the tensors' shapes: w_q [H e][d], w_k [G e][d].  The caches are the
+    caller's [G][max_seq][e] fp16 tensors, passed per call."""
+
+    def __init__(self, layer: dict, max_seq: int, threshold: float = 0.5):
+        w_q, w_k = layer["w_q"], layer["w_k"]
+        e = int(layer["head_dim"])
+        p1 = layer.get("p1")
+        self.desc = ffn_attn_desc(d=w_q.shape[1], heads=w_q.shape[0] // e,
+                                  kv_heads=w_k.shape[0] // e, head_dim=e,
+                                  rank=0 if p1 is None else p1.shape[0], max_seq=max_seq,
+                                  threshold=float(layer.get("tau", threshold)))
+        self.tensors = {k: layer.get(k) for k, _ in ffn_attn_weights._fields_}
+        self.weights = ffn_attn_weights(**{k: (_ptr(v) or None) for k, v in self.tensors.items()})
+        self.ws_bytes = ffn_attn_workspace_size(self.desc)
+        self.workspace = torch.empty(self.ws_bytes, dtype=torch.uint8, device=w_q.device)
+        self.d, self.heads = self.desc.d, self.desc.heads
+        self.plan = ffn_attn_plan(self.desc, self.weights, self.workspace.data_ptr(),
+                                  self.ws_bytes)
+
+    def forward(self, x, pos: int, k_cache, v_cache, y=None, mask=None, idx=None, cnt=None,
+                scores=None):
+        if y is None:
+            y = torch.empty(self.d, dtype=torch.float32, device=x.device)
+        ffn_attn_forward(self.plan, x.data_ptr(), pos, k_cache.data_ptr(), v_cache.data_ptr(),
+                         y.data_ptr(), _ptr(mask), _ptr(idx), _ptr(cnt), _ptr(scores), _stream())
+        return y
+
+    def close(self):
+        if self.plan:
+            ffn_attn_destroy(self.plan)
+            self.plan = 0
 
     def __del__(self):
         try:

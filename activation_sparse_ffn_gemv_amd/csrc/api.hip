@@ -1,6 +1,6 @@
 // C ABI of libffn_sparse: validation, workspace layout, path choice and launch sequencing.
 // Kernels live in decode.hip (batch-1 decode), batch.hip (several tokens), dense.hip (MFMA
-// GEMMs) and moe.hip (router).  Nothing here allocates device memory or synchronises, except
+// GEMMs), moe.hip (router) and attn.hip (attention block).  Nothing here allocates device memory or synchronises, except
 // ffn_sparse_plan with calibrate = 1.
 #include <math.h>
 #include <stdarg.h>
@@ -1279,6 +1279,204 @@ ffn_status ffn_moe_forward(ffn_moe* m, const void* x, int32_t B, float* y, int32
 
 ffn_status ffn_moe_destroy(ffn_moe* m) {
   delete m;
+  return FFN_OK;
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------------------------
+// Attention block with a head-level active set (kernels in attn.hip).
+struct ffn_attn {
+  ffn_attn_desc desc;
+  ffn_attn_weights w;
+  char* ws;
+  size_t off_z, off_hdr, off_alist, off_q, off_rec, off_part;
+  int cpl_w;
+  hipEvent_t ev[FFN_STAGE_ATTN_REDUCE + 1][2];
+};
+
+namespace {
+
+// Chunks of positions per head that k_attn_part splits a context of n positions into: about
+// 1024 / H per head (so that half the heads active give ~512 workgroups), each a whole number
+// of the kernel's steps, at most ATTN_MAX_CHUNKS.
+void attn_chunks(int H, int e, int n, int* lc, int* nchunk) {
+  const int step = attn_step_positions(e);
+  const int target = std::min(ATTN_MAX_CHUNKS, std::max(1, (1024 + H - 1) / H));
+  int per = (n + target - 1) / target;
+  per = (per + step - 1) / step * step;
+  *lc = per;
+  *nchunk = (n + per - 1) / per;
+}
+
+ffn_status check_attn_desc(const ffn_attn_desc* d) {
+  if (!d) return fail(FFN_ERR_INVALID_ARGUMENT, "desc is NULL");
+  if (d->d <= 0 || d->d % 8 || d->d > 8192)
+    return fail(FFN_ERR_UNSUPPORTED, "d = %d: need d %% 8 == 0 and d <= 8192", d->d);
+  if (d->heads < 1 || d->heads > ATTN_MAX_HEADS)
+    return fail(FFN_ERR_UNSUPPORTED, "heads = %d: need 1..%d", d->heads, ATTN_MAX_HEADS);
+  if (d->kv_heads < 1 || d->heads % d->kv_heads)
+    return fail(FFN_ERR_UNSUPPORTED, "kv_heads = %d must divide heads = %d", d->kv_heads,
+                d->heads);
+  if (d->head_dim != 64 && d->head_dim != 128)
+    return fail(FFN_ERR_UNSUPPORTED, "head_dim = %d: need 64 or 128", d->head_dim);
+  if (d->heads * d->head_dim > ATTN_OUT_BLOCKS * ATTN_OUT_MAXR)
+    return fail(FFN_ERR_UNSUPPORTED, "heads * head_dim = %d exceeds %d",
+                d->heads * d->head_dim, ATTN_OUT_BLOCKS * ATTN_OUT_MAXR);
+  if (d->rank < 0 || d->rank % 8 || d->rank > ATTN_MAX_RANK)
+    return fail(FFN_ERR_UNSUPPORTED, "rank = %d: need rank %% 8 == 0 and rank <= %d", d->rank,
+                ATTN_MAX_RANK);
+  if (d->max_seq < 1) return fail(FFN_ERR_INVALID_ARGUMENT, "max_seq = %d", d->max_seq);
+  if (!(d->threshold > 0.0f && d->threshold <= 1.0f))
+    return fail(FFN_ERR_INVALID_ARGUMENT, "threshold %g not in (0, 1]", (double)d->threshold);
+  if (cpl_for(d->d / 8) < 0) return fail(FFN_ERR_UNSUPPORTED, "d too large");
+  return FFN_OK;
+}
+
+size_t attn_layout(const ffn_attn_desc* d, ffn_attn* p) {
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = round_up(off + bytes, 256);
+    return o;
+  };
+  const size_t z = take(sizeof(float) * std::max(d->rank, 8));
+  const size_t hdr = take(64);
+  const size_t alist = take(sizeof(int) * ATTN_MAX_HEADS);
+  const size_t q = take(sizeof(float) * (size_t)d->heads * d->head_dim);
+  const size_t rec = take(sizeof(float) * (size_t)d->heads * ATTN_MAX_CHUNKS * (d->head_dim + 4));
+  const size_t part = take(sizeof(float) * (size_t)ATTN_OUT_BLOCKS * d->d);
+  if (p) {
+    p->off_z = z;
+    p->off_hdr = hdr;
+    p->off_alist = alist;
+    p->off_q = q;
+    p->off_rec = rec;
+    p->off_part = part;
+  }
+  return off;
+}
+
+}  // namespace
+
+extern "C" {
+
+ffn_status ffn_attn_workspace_size(const ffn_attn_desc* desc, size_t* bytes) {
+  ffn_status st = check_attn_desc(desc);
+  if (st != FFN_OK) return st;
+  if (!bytes) return fail(FFN_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  *bytes = attn_layout(desc, nullptr);
+  return FFN_OK;
+}
+
+ffn_status ffn_attn_plan(const ffn_attn_desc* desc, const ffn_attn_weights* w, void* workspace,
+                         size_t workspace_bytes, ffn_attn** out) {
+  ffn_status st = check_attn_desc(desc);
+  if (st != FFN_OK) return st;
+  if (!w || !out) return fail(FFN_ERR_INVALID_ARGUMENT, "weights or out is NULL");
+  if (!w->w_q || !w->w_k || !w->w_v || !w->w_o_t)
+    return fail(FFN_ERR_INVALID_ARGUMENT, "w_q, w_k, w_v and w_o_t are required");
+  if (desc->rank > 0 && (!w->p1 || !w->p2))
+    return fail(FFN_ERR_INVALID_ARGUMENT, "rank > 0 needs p1 and p2");
+  const void* ptrs[] = {w->w_q, w->w_k, w->w_v, w->w_o_t, w->p1, w->p2, w->c1, w->c2, workspace};
+  for (const void* q : ptrs)
+    if (q && !aligned16(q)) return fail(FFN_ERR_INVALID_ARGUMENT, "pointer not 16-byte aligned");
+  if (!workspace) return fail(FFN_ERR_INVALID_ARGUMENT, "workspace is NULL");
+  const size_t need = attn_layout(desc, nullptr);
+  if (workspace_bytes < need)
+    return fail(FFN_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes, need %zu", workspace_bytes,
+                need);
+  ffn_attn* p = new (std::nothrow) ffn_attn();
+  if (!p) return fail(FFN_ERR_INTERNAL, "out of host memory");
+  p->desc = *desc;
+  p->w = *w;
+  p->ws = static_cast<char*>(workspace);
+  attn_layout(desc, p);
+  p->cpl_w = cpl_for(desc->d / 8);
+  *out = p;
+  return FFN_OK;
+}
+
+ffn_status ffn_attn_forward(ffn_attn* p, const void* x, int32_t pos, void* k_cache,
+                            void* v_cache, float* y, const uint8_t* mask, int32_t* idx,
+                            int32_t* cnt, float* scores, void* stream) {
+  if (!p) return fail(FFN_ERR_INVALID_ARGUMENT, "plan is NULL");
+  const ffn_attn_desc& D = p->desc;
+  if (!x || !y || !k_cache || !v_cache)
+    return fail(FFN_ERR_INVALID_ARGUMENT, "x, y, k_cache and v_cache are required");
+  if (!aligned16(x) || !aligned16(y) || !aligned16(k_cache) || !aligned16(v_cache))
+    return fail(FFN_ERR_INVALID_ARGUMENT, "x, y and the caches must be 16-byte aligned");
+  if (pos < 0 || pos >= D.max_seq)
+    return fail(FFN_ERR_INVALID_ARGUMENT, "pos = %d not in [0, %d)", pos, D.max_seq);
+  if (!mask && D.rank == 0)
+    return fail(FFN_ERR_INVALID_ARGUMENT, "no predictor (rank 0): a mask is required");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char* ws = p->ws;
+  AttnArgs a{};
+  a.wq = p->w.w_q;
+  a.wk = p->w.w_k;
+  a.wv = p->w.w_v;
+  a.wo = p->w.w_o_t;
+  a.p2 = p->w.p2;
+  a.c2 = p->w.c2;
+  a.z = reinterpret_cast<const float*>(ws + p->off_z);
+  a.mask = mask;
+  a.x = x;
+  a.kc = k_cache;
+  a.vc = v_cache;
+  a.q = reinterpret_cast<float*>(ws + p->off_q);
+  a.bits = reinterpret_cast<uint32_t*>(ws + p->off_hdr);
+  a.cnt = reinterpret_cast<int*>(ws + p->off_hdr + 16);
+  a.alist = reinterpret_cast<int*>(ws + p->off_alist);
+  a.rec = reinterpret_cast<float*>(ws + p->off_rec);
+  a.part = reinterpret_cast<float*>(ws + p->off_part);
+  a.y = y;
+  a.scores_out = mask ? nullptr : scores;
+  a.idx_out = idx;
+  a.cnt_out = cnt;
+  a.d = D.d;
+  a.H = D.heads;
+  a.G = D.kv_heads;
+  a.e = D.head_dim;
+  a.S = D.max_seq;
+  a.pos = pos;
+  a.rank = D.rank;
+  attn_chunks(D.heads, D.head_dim, pos + 1, &a.lc, &a.nchunk);
+  const double tau = D.threshold;
+  a.thr = tau >= 1.0 ? INFINITY : (float)log(tau / (1.0 - tau));
+  a.scale = 1.0f / sqrtf((float)D.head_dim);
+  hipError_t e = hipSuccess;
+  if (!mask) {
+    e = launch_pred_z(1, p->cpl_w, p->w.p1, p->w.c1, x, reinterpret_cast<float*>(ws + p->off_z),
+                      D.d, D.rank, nullptr, 1, 0, st, p->ev[FFN_STAGE_PRED_Z][0],
+                      p->ev[FFN_STAGE_PRED_Z][1]);
+    if (e != hipSuccess) return hip_fail(e, "attention predictor stage 1");
+  }
+  e = launch_attn_proj(p->cpl_w, a, st, p->ev[FFN_STAGE_ATTN_PROJ][0],
+                       p->ev[FFN_STAGE_ATTN_PROJ][1]);
+  if (e != hipSuccess) return hip_fail(e, "attention projections");
+  e = launch_attn_part(a, st, p->ev[FFN_STAGE_ATTN_SCORES][0], p->ev[FFN_STAGE_ATTN_SCORES][1]);
+  if (e != hipSuccess) return hip_fail(e, "attention scores");
+  e = launch_attn_out(a, st, p->ev[FFN_STAGE_ATTN_OUT][0], p->ev[FFN_STAGE_ATTN_OUT][1]);
+  if (e != hipSuccess) return hip_fail(e, "attention output projection");
+  e = launch_attn_reduce(a, st, p->ev[FFN_STAGE_ATTN_REDUCE][0], p->ev[FFN_STAGE_ATTN_REDUCE][1]);
+  if (e != hipSuccess) return hip_fail(e, "attention reduce");
+  return FFN_OK;
+}
+
+ffn_status ffn_attn_set_timing_events(ffn_attn* p, int32_t stage, void* start, void* stop) {
+  if (!p) return fail(FFN_ERR_INVALID_ARGUMENT, "plan is NULL");
+  if (stage != FFN_STAGE_PRED_Z && (stage < FFN_STAGE_ATTN_PROJ || stage > FFN_STAGE_ATTN_REDUCE))
+    return fail(FFN_ERR_INVALID_ARGUMENT, "stage %d is not an attention stage", stage);
+  if ((start == nullptr) != (stop == nullptr))
+    return fail(FFN_ERR_INVALID_ARGUMENT, "start and stop must both be set or both be NULL");
+  p->ev[stage][0] = static_cast<hipEvent_t>(start);
+  p->ev[stage][1] = static_cast<hipEvent_t>(stop);
+  return FFN_OK;
+}
+
+ffn_status ffn_attn_destroy(ffn_attn* p) {
+  delete p;
   return FFN_OK;
 }
 

@@ -271,4 +271,44 @@ hipError_t launch_dense_scores(const DenseArgs& a, hipStream_t st);
 // ev: three (start, stop) pairs for k_dup, k_ddown, k_dred (entries may be null), or nullptr
 hipError_t launch_dense(const DenseArgs& a, hipStream_t st, hipEvent_t (*ev)[2]);
 
+// Self-attention block of one token with a head-level active set (fp16 weights, token and
+// cache).  Heads H <= ATTN_MAX_HEADS of width e in {64, 128}, G key/value heads (H % G == 0).
+constexpr int ATTN_MAX_HEADS = 128;
+constexpr int ATTN_MAX_RANK = 1024;
+constexpr int ATTN_MAX_CHUNKS = 256;      // chunk records per head (positions per chunk: lc)
+constexpr int ATTN_OUT_BLOCKS = 256;      // workgroups (and partials of y) of the output projection
+constexpr int ATTN_OUT_MAXR = 64;         // rows per output workgroup: H e <= 256 * 64
+struct AttnArgs {
+  const void *wq, *wk, *wv, *wo;  // [H e][d], [G e][d], [G e][d], [H e][d] fp16 (wo transposed)
+  const void* p2;                 // head predictor stage 2 [H][rank] fp16
+  const float* c2;                // [H] or nullptr
+  const float* z;                 // [rank] predictor stage 1
+  const uint8_t* mask;            // [H] caller's head set, or nullptr (the predictor's)
+  const void* x;                  // [d] fp16
+  void *kc, *vc;                  // caches [G][S][e] fp16; position pos is written
+  float* q;                       // [H][e] queries of the active heads, by rank
+  uint32_t* bits;                 // [4] active-head bitmap
+  int* cnt;                       // [1] |A|
+  int* alist;                     // [H] active heads by rank
+  float* rec;                     // [H][ATTN_MAX_CHUNKS][e + 4] chunk records: o, max, sum
+  float* part;                    // [ATTN_OUT_BLOCKS][d] partials of y
+  float* y;                       // [d]
+  float* scores_out;              // [H] or nullptr (predictor scores)
+  int* idx_out;                   // [H] or nullptr (ascending active heads)
+  int* cnt_out;                   // [1] or nullptr
+  int d, H, G, e, S, pos, rank;
+  int lc, nchunk;                 // positions per chunk, chunks = ceil((pos + 1) / lc)
+  float thr, scale;               // logit(tau), 1 / sqrt(e)
+};
+int attn_heads_per_wave(int H);
+int attn_step_positions(int e);   // positions one k_attn_part step covers (lc is a multiple)
+hipError_t launch_attn_proj(int cpl, const AttnArgs& a, hipStream_t st, hipEvent_t e0 = nullptr,
+                            hipEvent_t e1 = nullptr);
+hipError_t launch_attn_part(const AttnArgs& a, hipStream_t st, hipEvent_t e0 = nullptr,
+                            hipEvent_t e1 = nullptr);
+hipError_t launch_attn_out(const AttnArgs& a, hipStream_t st, hipEvent_t e0 = nullptr,
+                           hipEvent_t e1 = nullptr);
+hipError_t launch_attn_reduce(const AttnArgs& a, hipStream_t st, hipEvent_t e0 = nullptr,
+                              hipEvent_t e1 = nullptr);
+
 }  // namespace ffn

@@ -272,7 +272,12 @@ typedef enum {
     FFN_STAGE_BATCH_DOWN = 5,
     FFN_STAGE_DENSE_UP = 6,
     FFN_STAGE_DENSE_DOWN = 7,
-    FFN_STAGE_DENSE_REDUCE = 8
+    FFN_STAGE_DENSE_REDUCE = 8,
+    /* attention block (ffn_attn_set_timing_events; predictor stage 1 is FFN_STAGE_PRED_Z) */
+    FFN_STAGE_ATTN_PROJ = 9,     /* head scores and set, query / key / value rows            */
+    FFN_STAGE_ATTN_SCORES = 10,  /* scores, softmax and values per (active head, chunk)      */
+    FFN_STAGE_ATTN_OUT = 11,     /* active heads' output-projection rows into partials of y  */
+    FFN_STAGE_ATTN_REDUCE = 12   /* sum of the partials                                      */
 } ffn_stage;
 
 ffn_status ffn_plan_set_timing_events(ffn_plan *plan, int32_t stage, void *start, void *stop);
@@ -317,6 +322,75 @@ ffn_status ffn_moe_forward(ffn_moe *moe, const void *x, int32_t B, float *y,
                            int32_t *expert_idx, float *expert_w, int32_t *expert_cnt,
                            void *stream);
 ffn_status ffn_moe_destroy(ffn_moe *moe);
+
+/* ---------------------------------------------------------------------------------------------
+ * Self-attention block with a head-level active set (unite.ai PowerInfer, section "Adaptive
+ * sparse predictor": each layer has a second predictor, for its self-attention block; section
+ * "Online stage": what is predicted inactive is not computed).  The pages do not name the
+ * attention block's unit; here it is one head: its query rows, its scores over the cache and its
+ * rows of the transposed output projection.  For one token x (d values, fp16) at position t:
+ *   predictor  z = P1 x + c1 ;  s = P2 z + c2  (one score per head)
+ *              A = { h : sigmoid(s_h) > threshold }, ascending
+ *   cache      K[g][t] = fp16(W_k[g] x),  V[g][t] = fp16(W_v[g] x)  for EVERY key/value head g (a
+ *              head skipped now may be active later, and its scores then need this position)
+ *   heads      for h in A, g = h / (H / G):  q_h = W_q[h] x ;  a_j = q_h . K[g][j] / sqrt(e),
+ *              j = 0..t ;  o_h = sum_j softmax(a)_j V[g][j]
+ *   output     y = sum_{h in A} sum_{c < e} o_h[c] W_o_t[h e + c]
+ * Row h e + c of W_q (and of W_o_t) is channel c of head h; W_o_t is the output projection stored
+ * transposed, so an active head contributes e contiguous rows.  No positional rotation and no
+ * biases are applied (the pages name neither).  Limits: d % 8 == 0, d <= 8192; 1 <= H <= 128;
+ * G divides H; e in {64, 128}; rank % 8 == 0, rank <= 1024 (0: no predictor, forward calls then
+ * need a mask); max_seq >= 1.  Everything is fp16 except the fp32 c1, c2, y and scores.
+ * Conventions as above: every device pointer 16-byte aligned, nothing allocated or synchronised
+ * by a forward call, one plan used by one stream at a time.
+ */
+typedef struct {
+    int32_t d;          /* model width                                                       */
+    int32_t heads;      /* H query heads                                                      */
+    int32_t kv_heads;   /* G key / value heads                                                */
+    int32_t head_dim;   /* e                                                                  */
+    int32_t rank;       /* head-predictor rank                                                */
+    int32_t max_seq;    /* S: positions of the caller's caches                                */
+    float threshold;    /* tau in (0, 1]: head active iff sigmoid(s) > tau, strictly          */
+} ffn_attn_desc;
+
+typedef struct {                          /* device pointers, caller-owned                     */
+    const void *w_q, *w_k, *w_v, *w_o_t;  /* fp16 [H e][d], [G e][d], [G e][d], [H e][d]        */
+    const void *p1, *p2;                  /* fp16 [rank][d], [H][rank] (NULL when rank == 0)    */
+    const float *c1, *c2;                 /* [rank], [H] fp32; may be NULL (= 0)                */
+} ffn_attn_weights;
+
+typedef struct ffn_attn ffn_attn;         /* opaque host object                                */
+
+/* Bytes of device workspace a plan for `desc` needs. */
+ffn_status ffn_attn_workspace_size(const ffn_attn_desc *desc, size_t *bytes);
+
+/* Validate and return a plan over the caller's weights and workspace (device, >=
+ * ffn_attn_workspace_size bytes, caller-owned, outliving the plan).  Enqueues nothing. */
+ffn_status ffn_attn_plan(const ffn_attn_desc *desc, const ffn_attn_weights *weights,
+                         void *workspace, size_t workspace_bytes, ffn_attn **out);
+
+/*
+ * One token x [d] (fp16, device) at position pos in [0, max_seq): writes position pos of the
+ * caches k_cache, v_cache ([G][max_seq][e] fp16, device; positions 0..pos-1 must hold the
+ * context's keys and values, positions past pos are neither read nor written) and y [d] (fp32,
+ * fully overwritten).
+ *   mask    [H] uint8 0/1 or NULL (NULL: the predictor picks the heads; needs rank > 0).
+ *   idx     [H] int32 or NULL: the active heads, ascending, in idx[0 .. cnt).
+ *   cnt     [1] int32 or NULL: |A|.
+ *   scores  [H] fp32 or NULL: the predictor's scores s (written only when mask == NULL).
+ * An empty set gives y = 0 (the caches are still written).
+ * Errors: FFN_ERR_INVALID_ARGUMENT for NULL x / y / caches, misaligned pointers, pos out of
+ * range, mask == NULL with rank == 0.
+ */
+ffn_status ffn_attn_forward(ffn_attn *plan, const void *x, int32_t pos, void *k_cache,
+                            void *v_cache, float *y, const uint8_t *mask, int32_t *idx,
+                            int32_t *cnt, float *scores, void *stream);
+
+/* As ffn_plan_set_timing_events, for the stages FFN_STAGE_PRED_Z and FFN_STAGE_ATTN_*. */
+ffn_status ffn_attn_set_timing_events(ffn_attn *plan, int32_t stage, void *start, void *stop);
+
+ffn_status ffn_attn_destroy(ffn_attn *plan);
 
 #ifdef __cplusplus
 }

@@ -280,3 +280,66 @@ def test_offload_validation_before_any_gpu_call():
     with pytest.raises(ffn.FFNError) as e:                     # not a pool plan
         ffn.ffn_offload_tables(0)
     assert e.value.status == ffn.FFN_ERR_INVALID_ARGUMENT
+
+
+def _adesc(**kw):
+    base = dict(d=4096, heads=32, kv_heads=8, head_dim=128, rank=128, max_seq=512,
+                threshold=0.5)
+    base.update(kw)
+    return ffn.ffn_attn_desc(**base)
+
+
+def test_attn_validation_before_any_gpu_call():
+    n = ffn.ffn_attn_workspace_size(_adesc())
+    assert n > 256 * 4096 * 4 and n % 256 == 0
+    for kw, status in [(dict(d=4100), ffn.FFN_ERR_UNSUPPORTED),
+                       (dict(d=16384), ffn.FFN_ERR_UNSUPPORTED),
+                       (dict(heads=0), ffn.FFN_ERR_UNSUPPORTED),
+                       (dict(heads=129), ffn.FFN_ERR_UNSUPPORTED),
+                       (dict(kv_heads=5), ffn.FFN_ERR_UNSUPPORTED),      # does not divide H
+                       (dict(head_dim=96), ffn.FFN_ERR_UNSUPPORTED),
+                       (dict(rank=12), ffn.FFN_ERR_UNSUPPORTED),
+                       (dict(rank=2048), ffn.FFN_ERR_UNSUPPORTED),
+                       (dict(max_seq=0), ffn.FFN_ERR_INVALID_ARGUMENT),
+                       (dict(threshold=0.0), ffn.FFN_ERR_INVALID_ARGUMENT),
+                       (dict(threshold=1.5), ffn.FFN_ERR_INVALID_ARGUMENT)]:
+        with pytest.raises(ffn.FFNError) as e:
+            ffn.ffn_attn_workspace_size(_adesc(**kw))
+        assert e.value.status == status, kw
+    w = ffn.ffn_attn_weights(w_q=0x1000, w_k=0x2000, w_v=0x3000, w_o_t=0x4000, p1=0x5000,
+                             p2=0x6000)
+    with pytest.raises(ffn.FFNError) as e:
+        ffn.ffn_attn_plan(_adesc(), w, 0x10000, n - 1)
+    assert e.value.status == ffn.FFN_ERR_WORKSPACE_TOO_SMALL
+    with pytest.raises(ffn.FFNError) as e:                     # predictor without P2
+        ffn.ffn_attn_plan(_adesc(), ffn.ffn_attn_weights(w_q=0x1000, w_k=0x2000, w_v=0x3000,
+                                                         w_o_t=0x4000, p1=0x5000), 0x10000, n)
+    assert e.value.status == ffn.FFN_ERR_INVALID_ARGUMENT
+    with pytest.raises(ffn.FFNError) as e:                     # misaligned weight
+        ffn.ffn_attn_plan(_adesc(), ffn.ffn_attn_weights(w_q=0x1008, w_k=0x2000, w_v=0x3000,
+                                                         w_o_t=0x4000, p1=0x5000, p2=0x6000),
+                          0x10000, n)
+    assert e.value.status == ffn.FFN_ERR_INVALID_ARGUMENT
+    p = ffn.ffn_attn_plan(_adesc(), w, 0x10000, n)
+    try:
+        for pos in (-1, 512):                                  # outside [0, max_seq)
+            with pytest.raises(ffn.FFNError) as e:
+                ffn.ffn_attn_forward(p, 0x1000, pos, 0x2000, 0x3000, 0x4000)
+            assert e.value.status == ffn.FFN_ERR_INVALID_ARGUMENT
+        with pytest.raises(ffn.FFNError) as e:                 # NULL cache
+            ffn.ffn_attn_forward(p, 0x1000, 0, 0, 0x3000, 0x4000)
+        assert e.value.status == ffn.FFN_ERR_INVALID_ARGUMENT
+        with pytest.raises(ffn.FFNError) as e:                 # not an attention stage
+            ffn.ffn_attn_set_timing_events(p, ffn.FFN_STAGE_GATHER)
+        assert e.value.status == ffn.FFN_ERR_INVALID_ARGUMENT
+    finally:
+        ffn.ffn_attn_destroy(p)
+    p0 = ffn.ffn_attn_plan(_adesc(rank=0), ffn.ffn_attn_weights(w_q=0x1000, w_k=0x2000,
+                                                                w_v=0x3000, w_o_t=0x4000),
+                           0x10000, n)
+    try:
+        with pytest.raises(ffn.FFNError) as e:                 # no predictor, no mask
+            ffn.ffn_attn_forward(p0, 0x1000, 0, 0x2000, 0x3000, 0x4000)
+        assert e.value.status == ffn.FFN_ERR_INVALID_ARGUMENT
+    finally:
+        ffn.ffn_attn_destroy(p0)
