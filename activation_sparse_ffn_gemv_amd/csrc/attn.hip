@@ -238,10 +238,12 @@ __global__ __launch_bounds__(AT_THREADS) void k_attn_part(AttnArgs a) {
   constexpr int PB = PPW * (AT_THREADS / WAVE);     // positions per workgroup and step
   __shared__ float s_rec[AT_THREADS / WAVE][LPR][10];
   const int k = blockIdx.y;
-  if (k >= *a.cnt) return;
+  // |A| and the head of rank k requested together (an entry past |A| is stale and unused)
+  const int n = *a.cnt;
+  const int h = a.alist[k];
+  if (k >= n) return;
   const int tid = threadIdx.x, lane = tid & (WAVE - 1), wave = tid / WAVE;
   const int pg = lane / LPR, ci = lane % LPR;
-  const int h = a.alist[k];
   const int g = h / (a.H / a.G);
   const int j0 = (int)blockIdx.x * a.lc;
   const int j1 = min(j0 + a.lc, a.pos + 1);
@@ -322,31 +324,118 @@ __global__ __launch_bounds__(AT_THREADS) void k_attn_part(AttnArgs a) {
 
 // ---------------------------------------------------------------------------------------------
 // Output projection: workgroup b takes ranked rows [n e b / 256, n e (b+1) / 256) of the active
-// heads' W_o_t rows (n = |A|); thread t owns 16-byte column chunks t, t + 256, ... of every row.
+// heads' W_o_t rows (n = |A|; at most 64 rows, so at most two heads); thread t owns 16-byte
+// column chunks t, t + 256, ... of every row.  The first rows' loads are issued before the
+// channels' outputs are merged from the chunk records, so the merge hides under them: per head
+// the chunks' maxima and sums are reduced by the whole workgroup, then each row's weighted sum
+// over the chunks is split over 256 / rows threads and added up in a fixed order.
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 1; o < WAVE; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, WAVE));
+  return v;
+}
+
 template <int CPT>
 __global__ __launch_bounds__(AO_THREADS) void k_attn_out(AttnArgs a) {
+  constexpr int RB = 8;                             // rows whose loads are in flight at once
+  constexpr int NW = AO_THREADS / WAVE;
   __shared__ float s_a[ATTN_OUT_MAXR];
-  __shared__ int s_row[ATTN_OUT_MAXR];
-  const int tid = threadIdx.x;
-  const int e = a.e, nch = a.d / 8;
-  const int rows = *a.cnt * e;
+  __shared__ int s_alist[ATTN_MAX_HEADS];
+  __shared__ float s_f[2][ATTN_MAX_CHUNKS];
+  __shared__ float s_red[2][NW][2];
+  __shared__ float s_part[AO_THREADS];
+  const int tid = threadIdx.x, lane = tid & (WAVE - 1), wave = tid / WAVE;
+  const int e = a.e, nch = a.d / 8, nc = a.nchunk;
+  const int n = *a.cnt;
+  if (tid < a.H) s_alist[tid] = a.alist[tid];       // entries past |A| are stale and unused
+  const int rows = n * e;
   const int r0 = (int)((long long)rows * blockIdx.x / ATTN_OUT_BLOCKS);
   const int r1 = (int)((long long)rows * (blockIdx.x + 1) / ATTN_OUT_BLOCKS);
-  if (tid < r1 - r0) {
-    // the channel's output: merge the head's chunk records (fixed order)
-    const int row = r0 + tid, k = row / e, c = row % e;
-    const float* rec = a.rec + (size_t)k * ATTN_MAX_CHUNKS * (e + 4);
-    float M = -INFINITY;
-    for (int ch = 0; ch < a.nchunk; ++ch) M = fmaxf(M, rec[(size_t)ch * (e + 4) + e]);
-    float L = 0.0f, O = 0.0f;
-    for (int ch = 0; ch < a.nchunk; ++ch) {
-      const float* rc = rec + (size_t)ch * (e + 4);
-      const float f = __expf(rc[e] - M);
-      L = __builtin_fmaf(rc[e + 1], f, L);
-      O = __builtin_fmaf(rc[c], f, O);
+  const int nr = r1 - r0;
+  float* part = a.part + (size_t)blockIdx.x * a.d;
+  if (nr == 0) {                                    // no rows: a zero partial (uniform branch)
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int cc = tid + i * AO_THREADS;
+      if (cc < nch) {
+        f32x4* p = reinterpret_cast<f32x4*>(part + (size_t)cc * 8);
+        __builtin_nontemporal_store(f32x4{0.0f, 0.0f, 0.0f, 0.0f}, p);
+        __builtin_nontemporal_store(f32x4{0.0f, 0.0f, 0.0f, 0.0f}, p + 1);
+      }
     }
-    s_a[tid] = O / L;
-    s_row[tid] = a.alist[k] * e + c;
+    return;
+  }
+  const int k0 = r0 / e, k1 = (r1 - 1) / e;         // k1 <= k0 + 1
+  // Requests before the first rows' loads (the load counter retires in order, so a value
+  // requested after them could only be used once they have all landed): the heads' chunk maxima
+  // and sums, and this thread's share of its row's channel values (row i, chunks j, j + tpr, ..)
+  float m[2], l[2];
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+    const float* rc = a.rec + ((size_t)min(k0 + hh, k1) * ATTN_MAX_CHUNKS + min(tid, nc - 1)) *
+                                  (e + 4);
+    m[hh] = rc[e];
+    l[hh] = rc[e + 1];
+  }
+  const int tpr = AO_THREADS / nr;
+  const int ri = tid % nr, rj = tid / nr;
+  const int rrow = r0 + ri, rhh = rrow / e - k0;
+  const float* rco = a.rec + (size_t)(rrow / e) * ATTN_MAX_CHUNKS * (e + 4) + rrow % e;
+  constexpr int NPRE = 2;
+  float ov[NPRE];
+#pragma unroll
+  for (int u = 0; u < NPRE; ++u) ov[u] = rco[(size_t)min(rj + u * tpr, nc - 1) * (e + 4)];
+  __syncthreads();                                  // s_alist
+  u32x4 w[RB][CPT];
+  auto issue = [&](int rb) {
+#pragma unroll
+    for (int u = 0; u < RB; ++u) {
+      const int row = r0 + min(rb + u, nr - 1);
+      const char* rp = static_cast<const char*>(a.wo) +
+                       (size_t)(s_alist[row / e] * e + row % e) * nch * 16;
+#pragma unroll
+      for (int i = 0; i < CPT; ++i)
+        w[u][i] = ld16(rp + (size_t)min(tid + i * AO_THREADS, nch - 1) * 16);
+    }
+  };
+  issue(0);
+  // per head: M = max over the chunks, f_ch = exp(m_ch - M), L = sum l_ch f_ch
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+    const float v = wave_max(tid < nc ? m[hh] : -INFINITY);
+    if (lane == 0) s_red[hh][wave][0] = v;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+    float M = s_red[hh][0][0];
+#pragma unroll
+    for (int q = 1; q < NW; ++q) M = fmaxf(M, s_red[hh][q][0]);
+    const float f = tid < nc ? __expf(m[hh] - M) : 0.0f;
+    if (tid < nc) s_f[hh][tid] = f;
+    const float sl = wave_sum(l[hh] * f);
+    if (lane == 0) s_red[hh][wave][1] = sl;
+  }
+  __syncthreads();
+  // each row's weighted sum over the chunks, tpr threads per row, then in a fixed order
+  if (tid < nr * tpr) {
+    float acc = 0.0f;
+#pragma unroll
+    for (int u = 0; u < NPRE; ++u)
+      if (rj + u * tpr < nc) acc = __builtin_fmaf(ov[u], s_f[rhh][rj + u * tpr], acc);
+    for (int ch = rj + NPRE * tpr; ch < nc; ch += tpr)
+      acc = __builtin_fmaf(rco[(size_t)ch * (e + 4)], s_f[rhh][ch], acc);
+    s_part[tid] = acc;
+  }
+  __syncthreads();
+  if (tid < nr) {
+    const int hh = (r0 + tid) / e - k0;
+    float acc = s_part[tid];
+    for (int j = 1; j < tpr; ++j) acc += s_part[j * nr + tid];
+    float L = s_red[hh][0][1];
+#pragma unroll
+    for (int q = 1; q < NW; ++q) L += s_red[hh][q][1];
+    s_a[tid] = acc / L;
   }
   __syncthreads();
   float acc[CPT][8];
@@ -354,31 +443,21 @@ __global__ __launch_bounds__(AO_THREADS) void k_attn_out(AttnArgs a) {
   for (int i = 0; i < CPT; ++i)
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[i][j] = 0.0f;
-  constexpr int RB = 8;                             // rows whose loads are in flight at once
-  for (int rb = 0; rb < r1 - r0; rb += RB) {
-    u32x4 w[RB][CPT];
-    float coef[RB];
-#pragma unroll
-    for (int u = 0; u < RB; ++u) {
-      const int ri = min(rb + u, r1 - r0 - 1);
-      coef[u] = rb + u < r1 - r0 ? s_a[ri] : 0.0f;
-      const char* rp = static_cast<const char*>(a.wo) + (size_t)s_row[ri] * nch * 16;
-#pragma unroll
-      for (int i = 0; i < CPT; ++i)
-        w[u][i] = ld16(rp + (size_t)min(tid + i * AO_THREADS, nch - 1) * 16);
-    }
+  for (int rb = 0; rb < nr; rb += RB) {
+    if (rb) issue(rb);
     issue_fence();
 #pragma unroll
-    for (int u = 0; u < RB; ++u)
+    for (int u = 0; u < RB; ++u) {
+      const float coef = rb + u < nr ? s_a[rb + u] : 0.0f;
 #pragma unroll
       for (int i = 0; i < CPT; ++i) {
         float f[8];
         unpack8(w[u][i], f);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[i][j] = __builtin_fmaf(coef[u], f[j], acc[i][j]);
+        for (int j = 0; j < 8; ++j) acc[i][j] = __builtin_fmaf(coef, f[j], acc[i][j]);
       }
+    }
   }
-  float* part = a.part + (size_t)blockIdx.x * a.d;
 #pragma unroll
   for (int i = 0; i < CPT; ++i) {
     const int cc = tid + i * AO_THREADS;

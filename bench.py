@@ -128,6 +128,9 @@ OTHERS = [
     ("falcon_40b_relu_f16", ["--batch", "32", "--steps", "4"]),
     ("falcon_40b_relu_f16", ["--prefill", "512", "--steps", "2"]),
     ("falcon_40b_relu_f16", ["--prefill", "512", "--steps", "2", "--prefill-path", "dense"]),
+    # attention blocks with a head-level active set (a token at position 511 of a 512 context)
+    ("llama2_7b_attn_f16", ["--steps", "64"]),
+    ("mistral_7b_attn_f16", ["--steps", "64"]),
 ]
 
 
@@ -173,6 +176,217 @@ def run_others() -> list:
     return out
 
 
+def run_attn(args):
+    """Decode of a stack of attention blocks with a head-level active set: a step is one token
+    at the context's last position through every block (predictor, key / value rows of every
+    head into the cache, the active heads' query rows, scores over the cache and output rows).
+    Prints the same JSON line as the FFN workloads."""
+    import numpy as np
+    import torch
+
+    import activation_sparse_ffn_gemv_amd as ffn
+    import synth
+
+    cfg = synth.ATTN_CONFIGS[args.config]
+    L = args.layers or cfg.layers
+    K = args.steps if args.steps else 64
+    W = min(args.warmup, K)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    d, H, G, e, r, pos = cfg.d, cfg.heads, cfg.kv_heads, cfg.head_dim, cfg.rank, cfg.context
+    log("attention %s: d=%d heads=%d kv_heads=%d head_dim=%d rank=%d position=%d layers=%d "
+        "steps=%d" % (cfg.name, d, H, G, e, r, pos, L, K))
+    t0 = time.time()
+    layers = [synth.make_attn_layer(cfg, layer=l, device=dev) for l in range(L)]
+    caches = [synth.make_kv_cache(cfg, layer=l, device=dev) for l in range(L)]
+    x = torch.stack([synth.make_attn_tokens(cfg, K, layer=l, device=dev) for l in range(L)])
+    y = torch.empty(L, K, d, dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    log("inputs generated on the GPU in %.1f s" % (time.time() - t0))
+    stream = torch.cuda.Stream(device=dev)
+    sp = stream.cuda_stream
+    mods = [ffn.SparseAttention(layers[l], max_seq=cfg.seq) for l in range(L)]
+    xb = 2 * d
+
+    def call(l, t, **kw):
+        ffn.ffn_attn_forward(mods[l].plan, x[l].data_ptr() + t * xb, pos, caches[l][0].data_ptr(),
+                             caches[l][1].data_ptr(), y[l, t].data_ptr(), stream=sp, **kw)
+
+    # bytes the method touches per (layer, step), from each call's |A| (untimed counting pass)
+    cnt = torch.zeros(L, K, dtype=torch.int32, device=dev)
+    with torch.cuda.stream(stream):
+        for t in range(K):
+            for l in range(L):
+                call(l, t, cnt=cnt[l].data_ptr() + 4 * t)
+    torch.cuda.synchronize()
+    n_act = cnt.cpu().numpy().astype(np.float64)
+    b_pz = r * d * 2 + d * 2
+    b_proj_fixed = H * r * 2 + H * 4 + 2 * G * e * d * 2 + 2 * G * e * 2  # P2, c2, K/V rows+writes
+    b_q = e * d * 2                                                     # per active head
+    b_cache = (pos + 1) * e * 2 * 2                                     # per active head
+    b_o = e * d * 2                                                     # per active head
+    touched = b_pz + b_proj_fixed + n_act * (b_q + b_cache + b_o)
+    density = float(n_act.mean() / H)
+    log("measured head density %.4f (mean |A| = %.2f of %d)" % (density, n_act.mean(), H))
+
+    gsteps = max(1, min(K, 256 // L))
+    graphs = []
+    with torch.cuda.stream(stream):
+        for g0 in range(0, K, gsteps):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                for t in range(g0, min(K, g0 + gsteps)):
+                    for l in range(L):
+                        call(l, t)
+            graphs.append(g)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        for g in graphs[:max(1, (W + gsteps - 1) // gsteps)]:
+            g.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        for g in graphs:
+            g.replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    tok_s = K / (ms / 1e3)
+    eff_gbps = touched.sum() / (ms / 1e3) / 1e9
+    log("timed %d step(s): %.3f ms/step, %.1f tokens/s, %.1f GB/s effective over touched bytes"
+        % (K, ms / K, tok_s, eff_gbps))
+
+    # per-kernel durations: plain launches of the sampled steps with HIP events on one stage's
+    # dispatches (on the stream they run on)
+    S = min(args.kernel_sample, K)
+    per_call = touched[:, :S].sum() / (L * S)
+    na = float(n_act[:, :S].mean())
+    kinds = [("pred_z", ffn.FFN_STAGE_PRED_Z, b_pz),
+             ("attn_proj", ffn.FFN_STAGE_ATTN_PROJ, b_proj_fixed + na * b_q),
+             ("attn_scores", ffn.FFN_STAGE_ATTN_SCORES, na * b_cache),
+             ("attn_out", ffn.FFN_STAGE_ATTN_OUT, na * b_o),
+             ("attn_reduce", ffn.FFN_STAGE_ATTN_REDUCE, 0.0)]
+    assert abs(sum(k[2] for k in kinds) - per_call) < 1e-6 * per_call
+    stages = {}
+    for sname, sid, nb in kinds:
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(S * L)]
+        with torch.cuda.stream(stream):
+            for a, b in evs:
+                a.record(stream)
+                b.record(stream)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            for i, (a, b) in enumerate(evs):
+                l, t = i % L, i // L
+                ffn.ffn_attn_set_timing_events(mods[l].plan, sid, a.cuda_event, b.cuda_event)
+                call(l, t)
+        torch.cuda.synchronize()
+        for m in mods:
+            ffn.ffn_attn_set_timing_events(m.plan, sid, 0, 0)
+        dur = np.array([a.elapsed_time(b) for a, b in evs])
+        stages[sname] = {"avg_us": round(float(dur.mean()) * 1e3, 3), "bytes_per_launch": int(nb),
+                         "gbps": round(nb / (dur.mean() / 1e3) / 1e9, 1)}
+        log("kernel %-13s %9.2f us avg over %d launches  %.1f GB/s algorithmic" % (
+            sname, dur.mean() * 1e3, len(dur), stages[sname]["gbps"]))
+    knames = {"pred_z": "k_pred_z", "attn_proj": "k_attn_proj", "attn_scores": "k_attn_part",
+              "attn_out": "k_attn_out", "attn_reduce": "k_attn_reduce"}
+    movers = [k for k in stages if stages[k]["bytes_per_launch"] > 0]
+    dom = max(movers, key=lambda k: stages[k]["avg_us"])
+    prof = profiled_traffic(knames[dom], cfg.name, with_trace=True)
+    roof = {"bound": "hbm", "kernel": knames[dom], "achieved": stages[dom]["gbps"],
+            "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": round(stages[dom]["gbps"] / HBM_PEAK_GBPS, 4), "traffic": prof[0],
+            "trace_avg_us": prof[1], "avg_us": stages[dom]["avg_us"],
+            "bytes_per_launch": stages[dom]["bytes_per_launch"]}
+
+    # CPU oracle on a bounded sample, and parity of the timed outputs on (layer, token) pairs:
+    # the oracle's cache is the generator's with position `pos` holding the token's own key and
+    # value, which is the state every timed step saw
+    cpu, parity = None, None
+    nt = min(args.cpu_tokens, K)
+    if nt > 0:
+        import oracle
+        oracle.build()
+        keys = ["w_q", "w_k", "w_v", "w_o_t", "p1", "p2", "c1", "c2"]
+
+        def host(l):
+            OL = {k: (None if layers[l].get(k) is None else
+                      np.ascontiguousarray(layers[l][k].cpu().numpy())) for k in keys}
+            OL.update(tau=cfg.tau, head_dim=e)
+            # the device caches: positions below pos are the generator's, untouched by the run
+            Kh, Vh = (np.ascontiguousarray(c.cpu().numpy()) for c in caches[l])
+            return OL, Kh, Vh
+
+        t_cpu, L_cpu = 0.0, 0
+        for l in range(L):
+            OL, Kh, Vh = host(l)
+            xh = x[l, :nt].cpu().numpy()
+            for t in range(nt):
+                c0 = time.perf_counter()
+                oracle.attn_token(OL, Kh, Vh, xh[t], pos)
+                t_cpu += time.perf_counter() - c0
+            L_cpu = l + 1
+            if t_cpu > args.cpu_budget:
+                break
+        rate = nt * L_cpu / t_cpu / L
+        cpu_model = ""
+        try:
+            with open("/proc/cpuinfo") as f:
+                cpu_model = next((ln.split(":", 1)[1].strip() for ln in f
+                                  if ln.startswith("model name")), "")
+        except OSError:
+            pass
+        cpu = {"value": round(rate, 5), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+               "sample": "first %d token(s) x %d of %d blocks, head predictor + attention block, "
+                         "single-threaded C with fp64 accumulation (%.1f s of CPU), scaled to all "
+                         "blocks" % (nt, L_cpu, L, t_cpu),
+               "s_per_token": round(1.0 / rate, 3),
+               "host": {"cpu_model": cpu_model, "logical_cpus": os.cpu_count()}}
+        rng = np.random.default_rng(cfg.seed)
+        pairs = sorted({(0, t) for t in range(nt)} |
+                       {(int(l), int(t)) for l, t in zip(rng.integers(0, L, args.parity_pairs),
+                                                         rng.integers(0, K, args.parity_pairs))})
+        worst = 0.0
+        ie = torch.zeros(H, dtype=torch.int32, device=dev)
+        ce = torch.zeros(1, dtype=torch.int32, device=dev)
+        yy = torch.zeros(d, dtype=torch.float32, device=dev)
+        for l, t in pairs:
+            OL, Kh, Vh = host(l)
+            yg = y[l, t].cpu().numpy().astype(np.float64)          # from the timed run
+            ffn.ffn_attn_forward(mods[l].plan, x[l].data_ptr() + t * xb, pos,
+                                 caches[l][0].data_ptr(), caches[l][1].data_ptr(),
+                                 yy.data_ptr(), idx=ie.data_ptr(), cnt=ce.data_ptr(), stream=sp)
+            torch.cuda.synchronize()
+            mk = np.zeros(H, np.uint8)
+            mk[ie[:int(ce[0])].cpu().numpy()] = 1
+            yref, _, _, _ = oracle.attn_token(OL, Kh, Vh, x[l, t].cpu().numpy(), pos, mk)
+            worst = max(worst, float(np.max(np.abs(yg - yref)) / np.max(np.abs(yref))))
+        parity = {"pairs": len(pairs), "layers": sorted({l for l, _ in pairs}),
+                  "max_normwise_err": worst, "tolerance": 2e-3, "within_tolerance": worst <= 2e-3}
+        log("oracle: %.2f s for %d token(s) x %d block(s); GPU parity over %d pairs: max "
+            "normwise error %.2e" % (t_cpu, nt, L_cpu, len(pairs), worst))
+
+    result = {
+        "metric": "sparse-attention decode tokens/s at 1 GPU (head-level active set); effective "
+                  "HBM GB/s of touched bytes",
+        "value": round(tok_s, 2), "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": round(ms / K, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f16xf16->f32",
+        "data": "synthetic (seeded; cache of the context drawn at the projections' spread)",
+        "config": {"workload": cfg.name, "mode": "decode", "tokens_per_call": 1, "d": d,
+                   "path": "sparse", "heads": H, "kv_heads": G, "head_dim": e, "rank": r,
+                   "position": pos, "layers": L, "target_density": cfg.density,
+                   "measured_density": round(density, 5)},
+        "effective_gbps": round(eff_gbps, 1),
+        "touched_bytes_per_step": int(touched.sum() / K),
+        "roofline": roof, "kernels": stages, "cpu_baseline": cpu, "parity_sample": parity,
+    }
+    print(json.dumps(result), flush=True)
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -181,7 +395,7 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=16, help="untimed steps replayed first")
     ap.add_argument("--config", default=None,
                     help="one workload (default: the Llama-2-shaped stack, then short runs of "
-                         "the others)")
+                         "the others); the *_attn_* names run attention blocks")
     ap.add_argument("--no-others", action="store_true",
                     help="default workload only: skip the short runs of the other workloads")
     ap.add_argument("--batch", type=int, default=1, help="tokens per decode step (union path)")
@@ -242,6 +456,8 @@ def main(argv=None):
     import activation_sparse_ffn_gemv_amd as ffn
     import synth
 
+    if args.config in synth.ATTN_CONFIGS:
+        return run_attn(args)
     others = args.config is None and not args.no_others
     cfg = synth.CONFIGS[args.config or HEADLINE]
     if args.spectrum_alpha > 0:
