@@ -176,6 +176,20 @@ def run_others() -> list:
     return out
 
 
+def copy_calibration(mib: int, dev):
+    """Five device-to-device copies of `mib` MiB: the known-size kernel that the HBM byte
+    counters of a profiled run are scaled against."""
+    import torch
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log("copy calibration: 5 x %d MiB device-to-device" % mib)
+    del src, dst
+
+
 def run_attn(args):
     """Decode of a stack of attention blocks with a head-level active set: a step is one token
     at the context's last position through every block (predictor, key / value rows of every
@@ -196,6 +210,8 @@ def run_attn(args):
     d, H, G, e, r, pos = cfg.d, cfg.heads, cfg.kv_heads, cfg.head_dim, cfg.rank, cfg.context
     log("attention %s: d=%d heads=%d kv_heads=%d head_dim=%d rank=%d position=%d layers=%d "
         "steps=%d" % (cfg.name, d, H, G, e, r, pos, L, K))
+    if args.copy_mib:
+        copy_calibration(args.copy_mib, dev)
     t0 = time.time()
     layers = [synth.make_attn_layer(cfg, layer=l, device=dev) for l in range(L)]
     caches = [synth.make_kv_cache(cfg, layer=l, device=dev) for l in range(L)]
@@ -483,14 +499,7 @@ def main(argv=None):
         "steps=%d" % (cfg.name, mode, Bt, cfg.d, cfg.ffn, cfg.rank, cfg.act, cfg.w_dtype, L, K))
 
     if args.copy_mib:
-        n = args.copy_mib << 20
-        src = torch.ones(n, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(5):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        log("copy calibration: 5 x %d MiB device-to-device" % args.copy_mib)
-        del src, dst
+        copy_calibration(args.copy_mib, dev)
 
     # ---- inputs, resident in HBM
     t0 = time.time()
