@@ -14,6 +14,7 @@
 #include <vector>
 
 #include "common.h"
+#include "index.h"
 #include "launch.h"
 
 using namespace ffn;
@@ -1297,18 +1298,6 @@ struct ffn_attn {
 
 namespace {
 
-// Chunks of positions per head that k_attn_part splits a context of n positions into: about
-// 1024 / H per head (so that half the heads active give ~512 workgroups), each a whole number
-// of the kernel's steps, at most ATTN_MAX_CHUNKS.
-void attn_chunks(int H, int e, int n, int* lc, int* nchunk) {
-  const int step = attn_step_positions(e);
-  const int target = std::min(ATTN_MAX_CHUNKS, std::max(1, (1024 + H - 1) / H));
-  int per = (n + target - 1) / target;
-  per = (per + step - 1) / step * step;
-  *lc = per;
-  *nchunk = (n + per - 1) / per;
-}
-
 ffn_status check_attn_desc(const ffn_attn_desc* d) {
   if (!d) return fail(FFN_ERR_INVALID_ARGUMENT, "desc is NULL");
   if (d->d <= 0 || d->d % 8 || d->d > 8192)
@@ -1441,7 +1430,8 @@ ffn_status ffn_attn_forward(ffn_attn* p, const void* x, int32_t pos, void* k_cac
   a.S = D.max_seq;
   a.pos = pos;
   a.rank = D.rank;
-  attn_chunks(D.heads, D.head_dim, pos + 1, &a.lc, &a.nchunk);
+  attn_chunk_split(D.heads, attn_step_positions(D.head_dim), pos + 1, ATTN_MAX_CHUNKS, a.lc,
+                   a.nchunk);
   const double tau = D.threshold;
   a.thr = tau >= 1.0 ? INFINITY : (float)log(tau / (1.0 - tau));
   a.scale = 1.0f / sqrtf((float)D.head_dim);

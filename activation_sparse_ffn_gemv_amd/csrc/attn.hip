@@ -24,6 +24,7 @@
 #include <math.h>
 
 #include "common.h"
+#include "index.h"
 #include "launch.h"
 
 namespace ffn {
@@ -311,7 +312,7 @@ __global__ __launch_bounds__(AT_THREADS) void k_attn_part(AttnArgs a) {
       for (int i = 0; i < 8; ++i) o2[i] = s_rec[w][ci][i];
       merge_run(m, l, o, s_rec[w][ci][8], s_rec[w][ci][9], o2);
     }
-    float* rec = a.rec + ((size_t)k * ATTN_MAX_CHUNKS + blockIdx.x) * (E + 4);
+    float* rec = a.rec + attn_rec_offset(k, blockIdx.x, E, ATTN_MAX_CHUNKS);
     f32x4* ro = reinterpret_cast<f32x4*>(rec + ci * 8);
     ro[0] = f32x4{o[0], o[1], o[2], o[3]};
     ro[1] = f32x4{o[4], o[5], o[6], o[7]};
@@ -348,9 +349,8 @@ __global__ __launch_bounds__(AO_THREADS) void k_attn_out(AttnArgs a) {
   const int e = a.e, nch = a.d / 8, nc = a.nchunk;
   const int n = *a.cnt;
   if (tid < a.H) s_alist[tid] = a.alist[tid];       // entries past |A| are stale and unused
-  const int rows = n * e;
-  const int r0 = (int)((long long)rows * blockIdx.x / ATTN_OUT_BLOCKS);
-  const int r1 = (int)((long long)rows * (blockIdx.x + 1) / ATTN_OUT_BLOCKS);
+  int r0, r1;
+  attn_out_rows(n * e, blockIdx.x, ATTN_OUT_BLOCKS, r0, r1);
   const int nr = r1 - r0;
   float* part = a.part + (size_t)blockIdx.x * a.d;
   if (nr == 0) {                                    // no rows: a zero partial (uniform branch)
@@ -372,15 +372,15 @@ __global__ __launch_bounds__(AO_THREADS) void k_attn_out(AttnArgs a) {
   float m[2], l[2];
 #pragma unroll
   for (int hh = 0; hh < 2; ++hh) {
-    const float* rc = a.rec + ((size_t)min(k0 + hh, k1) * ATTN_MAX_CHUNKS + min(tid, nc - 1)) *
-                                  (e + 4);
+    const float* rc = a.rec + attn_rec_offset(min(k0 + hh, k1), min(tid, nc - 1), e,
+                                              ATTN_MAX_CHUNKS);
     m[hh] = rc[e];
     l[hh] = rc[e + 1];
   }
   const int tpr = AO_THREADS / nr;
   const int ri = tid % nr, rj = tid / nr;
   const int rrow = r0 + ri, rhh = rrow / e - k0;
-  const float* rco = a.rec + (size_t)(rrow / e) * ATTN_MAX_CHUNKS * (e + 4) + rrow % e;
+  const float* rco = a.rec + attn_rec_offset(rrow / e, 0, e, ATTN_MAX_CHUNKS) + rrow % e;
   constexpr int NPRE = 2;
   float ov[NPRE];
 #pragma unroll

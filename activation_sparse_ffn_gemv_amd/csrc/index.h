@@ -151,4 +151,29 @@ __host__ __device__ inline void ddown_store_pos(int m0, int c0, int w, int e, in
   col = c0 + 4 * (e % (DD_N / 4));
 }
 
+// Attention block.  Chunks of a context of n positions for the score kernel: about 1024 / H
+// chunks per head (so that half the heads active give ~512 workgroups), each a whole number of
+// the kernel's steps of `step` positions, at most max_chunks; every chunk holds >= 1 position.
+__host__ __device__ inline void attn_chunk_split(int H, int step, int n, int max_chunks, int& lc,
+                                                 int& nchunk) {
+  int target = (1024 + H - 1) / H;
+  target = target < 1 ? 1 : target > max_chunks ? max_chunks : target;
+  int per = (n + target - 1) / target;
+  per = (per + step - 1) / step * step;
+  lc = per;
+  nchunk = (n + per - 1) / per;
+}
+
+// Output-projection rows [r0, r1) of workgroup b of nblk (an even split of `rows` ranked rows).
+// 32-bit exact for rows <= 16384 and nblk <= 256 (rows * nblk < 2^23).
+__host__ __device__ inline void attn_out_rows(int rows, int b, int nblk, int& r0, int& r1) {
+  r0 = (int)((uint32_t)rows * (uint32_t)b / (uint32_t)nblk);
+  r1 = (int)((uint32_t)rows * (uint32_t)(b + 1) / (uint32_t)nblk);
+}
+
+// Element offset of chunk ch's record (e values of o, then max and sum) of the head of rank k.
+__host__ __device__ inline size_t attn_rec_offset(int k, int ch, int e, int max_chunks) {
+  return ((size_t)k * max_chunks + ch) * (size_t)(e + 4);
+}
+
 }  // namespace ffn

@@ -211,6 +211,47 @@ int main(int argc, char **argv)
     EXPECT(ffn_sparse_forward_static(dbig, w, DEV(9), 1, y, NULL, NULL, NULL, NULL),
            FFN_ERR_WORKSPACE_TOO_SMALL);
 
+    /* the attention block: descriptor checks, workspace size, plan and the forward's checks */
+    ffn_attn_desc *ad = (ffn_attn_desc *)malloc(sizeof(ffn_attn_desc));
+    ad->d = 4096;
+    ad->heads = 32;
+    ad->kv_heads = 8;
+    ad->head_dim = 128;
+    ad->rank = 128;
+    ad->max_seq = 512;
+    ad->threshold = 0.5f;
+    ffn_attn_weights *aw = (ffn_attn_weights *)calloc(1, sizeof(ffn_attn_weights));
+    aw->w_q = DEV(1);
+    aw->w_k = DEV(2);
+    aw->w_v = DEV(3);
+    aw->w_o_t = DEV(4);
+    aw->p1 = DEV(5);
+    aw->p2 = DEV(6);
+    size_t ab = 0;
+    EXPECT(ffn_attn_workspace_size(ad, &ab), FFN_OK);
+    EXPECT(ffn_attn_workspace_size(ad, NULL), FFN_ERR_INVALID_ARGUMENT);
+    ad->kv_heads = 5;
+    EXPECT(ffn_attn_workspace_size(ad, &ab), FFN_ERR_UNSUPPORTED);
+    ad->kv_heads = 8;
+    ad->head_dim = 96;
+    EXPECT(ffn_attn_workspace_size(ad, &ab), FFN_ERR_UNSUPPORTED);
+    ad->head_dim = 128;
+    ffn_attn *ap = NULL;
+    EXPECT(ffn_attn_plan(ad, aw, ws, ab - 1, &ap), FFN_ERR_WORKSPACE_TOO_SMALL);
+    EXPECT(ffn_attn_plan(ad, aw, ws, ab, &ap), FFN_OK);
+    EXPECT(ffn_attn_forward(ap, DEV(9), 512, DEV(10), DEV(11), y, NULL, NULL, NULL, NULL, NULL),
+           FFN_ERR_INVALID_ARGUMENT);
+    EXPECT(ffn_attn_forward(ap, DEV(9), 0, NULL, DEV(11), y, NULL, NULL, NULL, NULL, NULL),
+           FFN_ERR_INVALID_ARGUMENT);
+    EXPECT(ffn_attn_forward(NULL, DEV(9), 0, DEV(10), DEV(11), y, NULL, NULL, NULL, NULL, NULL),
+           FFN_ERR_INVALID_ARGUMENT);
+    EXPECT(ffn_attn_set_timing_events(ap, FFN_STAGE_GATHER, NULL, NULL),
+           FFN_ERR_INVALID_ARGUMENT);
+    EXPECT(ffn_attn_destroy(ap), FFN_OK);
+    EXPECT(ffn_attn_destroy(NULL), FFN_OK);
+    free(ad);
+    free(aw);
+
     EXPECT(ffn_plan_destroy(plan), FFN_OK);
     EXPECT(ffn_plan_destroy(NULL), FFN_OK);
     free(d);

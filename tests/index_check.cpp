@@ -4,7 +4,8 @@
 // its buffer, the gather's partial writes and the reduce's reads must address the same elements,
 // the work splits must partition their ranges exactly, and no 32-bit product may wrap.  The
 // shapes come from the built library's own host functions (workgroup counts, tiles, the batched
-// path's buffer shapes, the dense down projection's and the stage-1 GEMM's K slices).  Exit status 0 and "index check: OK" when every check holds.
+// path's buffer shapes, the dense down projection's and the stage-1 GEMM's K slices, the
+// attention kernels' steps).  Exit status 0 and "index check: OK" when every check holds.
 #include <stdio.h>
 #include <stdlib.h>
 
@@ -273,6 +274,49 @@ static void check_zpart(int M, int d, int rank) {
   CHECK(missing == 0, "M %d d %d rank %d: %zu partial elements never stored", M, d, rank, missing);
 }
 
+// Attention block, for H heads of width e (G key/value heads), d columns and contexts of n
+// positions: the projection workgroups' rows stay inside their matrices; the score kernel's
+// chunks cover [0, n) exactly, each non-empty and a whole number of steps, at most the record
+// slots; the output projection's row split partitions the active heads' rows, at most
+// ATTN_OUT_MAXR rows and two heads per workgroup, with every record and partial index in range.
+static void check_attn(int H, int G, int e, int d, int S) {
+  const int step = attn_step_positions(e);
+  const size_t rec_size = (size_t)H * ATTN_MAX_CHUNKS * (e + 4);
+  for (int b = 0; b < H * e / 8; ++b) {               // query workgroups: rank, channels
+    const int k = b * 8 / e, c0 = b * 8 % e;
+    CHECK(k < H && c0 + 8 <= e && (k * e + c0) / e == k, "q block %d", b);
+  }
+  for (int b = 0; b < 2 * G * e / 8; ++b) {           // key then value workgroups
+    const int r = b * 8, row0 = r < G * e ? r : r - G * e;
+    CHECK(row0 + 8 <= G * e && row0 / e == (row0 + 7) / e, "kv block %d", b);
+  }
+  for (int n = 1; n <= S; n += (n < 300 ? 1 : 97)) {
+    int lc, nc;
+    attn_chunk_split(H, step, n, ATTN_MAX_CHUNKS, lc, nc);
+    CHECK(lc > 0 && lc % step == 0 && nc >= 1 && nc <= ATTN_MAX_CHUNKS, "H %d n %d", H, n);
+    CHECK((long)(nc - 1) * lc < n && (long)nc * lc >= n, "H %d n %d lc %d nc %d", H, n, lc, nc);
+    for (int k = 0; k < H; k += H - 1 > 0 ? H - 1 : 1)
+      CHECK(attn_rec_offset(k, nc - 1, e, ATTN_MAX_CHUNKS) + e + 2 <= rec_size, "rec H %d", H);
+  }
+  for (int act = 0; act <= H; ++act) {
+    const int rows = act * e;
+    int prev = 0;
+    for (int b = 0; b < ATTN_OUT_BLOCKS; ++b) {
+      int r0, r1;
+      attn_out_rows(rows, b, ATTN_OUT_BLOCKS, r0, r1);
+      CHECK(r0 == prev && r1 >= r0, "rows %d b %d", rows, b);
+      CHECK(r1 - r0 <= ATTN_OUT_MAXR, "rows %d b %d: %d rows", rows, b, r1 - r0);
+      if (r1 > r0) {
+        CHECK((r1 - 1) / e - r0 / e <= 1, "rows %d b %d spans >2 heads", rows, b);
+        CHECK((size_t)b * d + (size_t)d <= (size_t)ATTN_OUT_BLOCKS * d, "part b %d", b);
+        CHECK((r1 - 1) / e < act, "rows %d b %d past |A|", rows, b);
+      }
+      prev = r1;
+    }
+    CHECK(prev == rows, "rows %d not covered (%d)", rows, prev);
+  }
+}
+
 int main() {
   const int ds[] = {64, 256, 512, 768, 776, 1024, 4096, 4104, 8192};
   const int ffns[] = {256, 1024, 3072, 11008, 14336, 32768};
@@ -296,6 +340,11 @@ int main() {
   const int zshapes[][3] = {{128, 4096, 256}, {130, 4096, 512}, {512, 8192, 1024},
                             {300, 768, 64}, {4096, 2048, 2048}, {1000, 512, 96}};
   for (const auto& sh : zshapes) check_zpart(sh[0], sh[1], sh[2]);
+  const int ashapes[][5] = {{32, 32, 128, 4096, 4096}, {32, 8, 128, 4096, 32768},
+                            {12, 12, 64, 768, 2048}, {128, 8, 64, 1024, 8192},
+                            {128, 1, 128, 8192, 4096}, {1, 1, 64, 64, 300},
+                            {6, 3, 64, 328, 33}, {16, 1, 128, 1024, 300}};
+  for (const auto& sh : ashapes) check_attn(sh[0], sh[1], sh[2], sh[3], sh[4]);
   if (failures) {
     printf("index check: %ld of %ld checks failed\n", failures, checks);
     return 1;

@@ -1,6 +1,6 @@
 """Parity at the workloads' full sizes, in the launch configuration the benchmark times.
 
-Each case runs bench.py's main() in this process on one of the five workloads (all layers,
+Each case runs bench.py's main() in this process on one of the workloads (all layers,
 HIP-graph replay of whole steps), then checks the JSON line it prints: the outputs the timed run
 wrote, at layer 0 and at seeded random (layer, token) pairs over the whole stack, must match the
 oracle evaluated on the GPU's own active sets within the tolerance (1e-5 for fp32 weights, 2e-3
@@ -34,6 +34,10 @@ CASES = [
                     "--parity-pairs", "3"], 4),
     ("falcon_prefill512", ["--config", "falcon_40b_relu_f16", "--prefill", "512", "--steps", "1",
                            "--parity-pairs", "2"], 3),
+    # attention blocks (32 blocks, a token at position 511 of each block's cache)
+    ("llama2_attn", ["--config", "llama2_7b_attn_f16", "--steps", "4", "--parity-pairs", "8"], 6),
+    ("mistral_attn", ["--config", "mistral_7b_attn_f16", "--steps", "4", "--parity-pairs", "8"],
+     6),
 ]
 
 
