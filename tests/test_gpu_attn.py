@@ -101,6 +101,8 @@ SMALL = [
     ("ragged_d", 328, 6, 3, 64, 8, 33),
     ("h128_e64", 1024, 128, 8, 64, 64, 20),
     ("mqa_e128", 1024, 16, 1, 128, 128, 300),
+    # a long context: 256 chunk records per head (the most the workspace holds)
+    ("long_ctx", 256, 4, 2, 64, 16, 8192),
 ]
 
 

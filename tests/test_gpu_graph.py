@@ -138,3 +138,32 @@ def test_auto_choice_in_a_graph_follows_the_data(ffn):
         del junk
     del gr
     m.close()
+
+
+@pytest.mark.parametrize("predicted", [True, False])
+def test_attention_in_a_graph(ffn, predicted):
+    """The attention block's forward (predicted heads, or a caller mask) captured and replayed:
+    y, the head list and the cache position it writes equal the eager call's on every replay."""
+    cfg = synth.AttnConfig("graph", d=512, heads=8, kv_heads=2, head_dim=64, rank=32,
+                           density=0.5, context=40)
+    L = {k: (v.cuda() if isinstance(v, torch.Tensor) else v)
+         for k, v in synth.make_attn_layer(cfg).items()}
+    K, V = (t.cuda() for t in synth.make_kv_cache(cfg))
+    x = synth.make_attn_tokens(cfg, 1)[0].cuda()
+    m = ffn.SparseAttention(L, max_seq=cfg.seq)
+    mask = None if predicted else (torch.arange(8, device="cuda") % 3 == 0).to(torch.uint8)
+    y = torch.zeros(cfg.d, device="cuda")
+    idx = torch.zeros(8, dtype=torch.int32, device="cuda")
+    cnt = torch.zeros(1, dtype=torch.int32, device="cuda")
+
+    def run():
+        m.forward(x, cfg.context, K, V, y=y, mask=mask, idx=idx, cnt=cnt)
+
+    _replays_match(run, y)
+    # the list and the cache position of the last replay equal a fresh eager call's
+    idx0, cnt0, k0 = idx.clone(), cnt.clone(), K[:, cfg.context].clone()
+    run()
+    torch.cuda.synchronize()
+    assert torch.equal(cnt, cnt0) and torch.equal(idx[:int(cnt0)], idx0[:int(cnt0)])
+    assert torch.equal(K[:, cfg.context], k0)
+    m.close()
