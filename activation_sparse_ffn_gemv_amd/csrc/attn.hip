@@ -232,11 +232,12 @@ __device__ __forceinline__ void merge_run(float& m, float& l, float (&o)[8], flo
   m = M;
 }
 
-template <int E>
+template <int E, bool PIPE>
 __global__ __launch_bounds__(AT_THREADS) void k_attn_part(AttnArgs a) {
   constexpr int LPR = E / 8;                        // lanes per position
   constexpr int PPW = WAVE / LPR;                   // positions per wave and step
   constexpr int PB = PPW * (AT_THREADS / WAVE);     // positions per workgroup and step
+  constexpr int U = AT_UNROLL;
   __shared__ float s_rec[AT_THREADS / WAVE][LPR][10];
   const int k = blockIdx.y;
   // |A| and the head of rank k requested together (an entry past |A| is stale and unused)
@@ -253,20 +254,20 @@ __global__ __launch_bounds__(AT_THREADS) void k_attn_part(AttnArgs a) {
   const f32x4 qa = ldg(reinterpret_cast<const f32x4*>(a.q + (size_t)k * E + ci * 8), 0);
   const f32x4 qb = ldg(reinterpret_cast<const f32x4*>(a.q + (size_t)k * E + ci * 8), 1);
   float m = -INFINITY, l = 0.0f, o[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  for (int s0 = j0; s0 < j1; s0 += AT_UNROLL * PB) {
-    u32x4 kr[AT_UNROLL], vr[AT_UNROLL];
-    bool val[AT_UNROLL];
+  // keys and values of U steps from position s0 (clamped to the chunk, so never predicated)
+  auto load_batch = [&](u32x4 (&kr)[U], u32x4 (&vr)[U], int s0) {
 #pragma unroll
-    for (int u = 0; u < AT_UNROLL; ++u) {
-      const int j = s0 + u * PB + wave * PPW + pg;
-      val[u] = j < j1;
-      const size_t jj = (size_t)min(j, j1 - 1);
+    for (int u = 0; u < U; ++u) {
+      const size_t jj = (size_t)min(s0 + u * PB + wave * PPW + pg, j1 - 1);
       kr[u] = ld16(kb + jj * E * 2);
       vr[u] = ld16(vb + jj * E * 2);
     }
-    issue_fence();
+  };
+  // the running softmax over those steps (positions past the chunk weigh nothing)
+  auto run_batch = [&](const u32x4 (&kr)[U], const u32x4 (&vr)[U], int s0) {
 #pragma unroll
-    for (int u = 0; u < AT_UNROLL; ++u) {
+    for (int u = 0; u < U; ++u) {
+      const bool val = s0 + u * PB + wave * PPW + pg < j1;
       float kf[8], vf[8];
       unpack8(kr[u], kf);
       float dp = qa.x * kf[0];
@@ -278,15 +279,35 @@ __global__ __launch_bounds__(AT_THREADS) void k_attn_part(AttnArgs a) {
       dp = __builtin_fmaf(qb.z, kf[6], dp);
       dp = __builtin_fmaf(qb.w, kf[7], dp);
       const float sc = lanes_sum<LPR>(dp) * a.scale;  // LPR <= 16: every lane of the row
-      const float sv = val[u] ? sc : -INFINITY;
+      const float sv = val ? sc : -INFINITY;
       const float mn = fmaxf(m, sv);
       const float corr = mn == m ? 1.0f : __expf(m - mn);
-      const float p = val[u] ? __expf(sv - mn) : 0.0f;
+      const float p = val ? __expf(sv - mn) : 0.0f;
       unpack8(vr[u], vf);
       l = __builtin_fmaf(l, corr, p);
 #pragma unroll
       for (int i = 0; i < 8; ++i) o[i] = __builtin_fmaf(o[i], corr, p * vf[i]);
       m = mn;
+    }
+  };
+  if constexpr (!PIPE) {
+    for (int s0 = j0; s0 < j1; s0 += U * PB) {
+      u32x4 kr[U], vr[U];
+      load_batch(kr, vr, s0);
+      issue_fence();
+      run_batch(kr, vr, s0);
+    }
+  } else {
+    // chunks of two batches or more: the next batch's loads are in flight while one is used
+    u32x4 k0[U], v0[U], k1[U], v1[U];
+    load_batch(k0, v0, j0);
+    for (int s0 = j0; s0 < j1; s0 += 2 * U * PB) {
+      load_batch(k1, v1, s0 + U * PB);
+      issue_fence();
+      run_batch(k0, v0, s0);
+      load_batch(k0, v0, s0 + 2 * U * PB);
+      issue_fence();
+      run_batch(k1, v1, s0 + U * PB);
     }
   }
   // merge the wave's position rows (lanes with the same ci), fixed order
@@ -548,15 +569,19 @@ int attn_step_positions(int e) { return (WAVE / (e / 8)) * (AT_THREADS / WAVE); 
 
 hipError_t launch_attn_part(const AttnArgs& a, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
   const dim3 grid(a.nchunk, a.H);
-#define ATT_L(E)                                                                               \
+  // two batches of loads in flight once a chunk holds two batches or more
+  const bool pipe = a.lc >= 2 * AT_UNROLL * attn_step_positions(a.e);
+#define ATT_L(E, P)                                                                            \
   do {                                                                                         \
     if (e0 && e1)                                                                              \
-      hipExtLaunchKernelGGL((k_attn_part<E>), grid, dim3(AT_THREADS), 0, st, e0, e1, 0, a);    \
+      hipExtLaunchKernelGGL((k_attn_part<E, P>), grid, dim3(AT_THREADS), 0, st, e0, e1, 0, a); \
     else                                                                                       \
-      hipLaunchKernelGGL((k_attn_part<E>), grid, dim3(AT_THREADS), 0, st, a);                  \
+      hipLaunchKernelGGL((k_attn_part<E, P>), grid, dim3(AT_THREADS), 0, st, a);               \
   } while (0)
-  if (a.e == 64) ATT_L(64);
-  else if (a.e == 128) ATT_L(128);
+  if (a.e == 64 && pipe) ATT_L(64, true);
+  else if (a.e == 64) ATT_L(64, false);
+  else if (a.e == 128 && pipe) ATT_L(128, true);
+  else if (a.e == 128) ATT_L(128, false);
   else return hipErrorInvalidValue;
 #undef ATT_L
   return hipGetLastError();

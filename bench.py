@@ -202,6 +202,10 @@ def run_attn(args):
     import synth
 
     cfg = synth.ATTN_CONFIGS[args.config]
+    if args.context:
+        import dataclasses
+        cfg = dataclasses.replace(cfg, context=args.context, max_seq=0)
+    wl = cfg.name if not args.context else "%s:ctx%d" % (cfg.name, cfg.context)
     L = args.layers or cfg.layers
     K = args.steps if args.steps else 64
     W = min(args.warmup, K)
@@ -311,7 +315,7 @@ def run_attn(args):
               "attn_out": "k_attn_out", "attn_reduce": "k_attn_reduce"}
     movers = [k for k in stages if stages[k]["bytes_per_launch"] > 0]
     dom = max(movers, key=lambda k: stages[k]["avg_us"])
-    prof = profiled_traffic(knames[dom], cfg.name, with_trace=True)
+    prof = profiled_traffic(knames[dom], wl, with_trace=True)
     roof = {"bound": "hbm", "kernel": knames[dom], "achieved": stages[dom]["gbps"],
             "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": round(stages[dom]["gbps"] / HBM_PEAK_GBPS, 4), "traffic": prof[0],
@@ -392,7 +396,7 @@ def run_attn(args):
         "ms_per_step": round(ms / K, 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f16xf16->f32",
         "data": "synthetic (seeded; cache of the context drawn at the projections' spread)",
-        "config": {"workload": cfg.name, "mode": "decode", "tokens_per_call": 1, "d": d,
+        "config": {"workload": wl, "mode": "decode", "tokens_per_call": 1, "d": d,
                    "path": "sparse", "heads": H, "kv_heads": G, "head_dim": e, "rank": r,
                    "position": pos, "layers": L, "target_density": cfg.density,
                    "measured_density": round(density, 5)},
@@ -422,6 +426,8 @@ def main(argv=None):
                          "predictor's sets, the device's choice by union density, per-token "
                          "masks); 'dense' = ffn_dense_forward (the dense FFN, no predictor)")
     ap.add_argument("--layers", type=int, default=0, help="override the layer count (0: all)")
+    ap.add_argument("--context", type=int, default=0,
+                    help="attention blocks: the token's position (its context length; 0: 511)")
     ap.add_argument("--kernel-sample", type=int, default=32,
                     help="steps whose kernel launches are timed with dispatch events")
     ap.add_argument("--parity-pairs", type=int, default=8,
