@@ -103,6 +103,9 @@ SMALL = [
     ("mqa_e128", 1024, 16, 1, 128, 128, 300),
     # a long context: 256 chunk records per head (the most the workspace holds)
     ("long_ctx", 256, 4, 2, 64, 16, 8192),
+    # chunks of two load batches or more (the score kernel's double-buffered form), ragged ends
+    ("pipe_e128", 512, 32, 8, 128, 32, 4096),
+    ("pipe_e64", 256, 32, 4, 64, 16, 8192),
 ]
 
 
