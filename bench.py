@@ -131,6 +131,7 @@ OTHERS = [
     # attention blocks with a head-level active set (a token at position 511 of a 512 context)
     ("llama2_7b_attn_f16", ["--steps", "64"]),
     ("mistral_7b_attn_f16", ["--steps", "64"]),
+    ("llama2_7b_attn_f16", ["--steps", "32", "--context", "8191"]),
 ]
 
 
