@@ -71,3 +71,41 @@ def test_int4_quantizer_error_bound():
     # (up to the fp16 rounding of s itself)
     assert (err <= s * 0.5 * (1 + 2e-3) + 1e-12).all()
     assert (q >= -8).all() and (q <= 7).all()
+
+
+def test_attention_inputs_deterministic_and_shaped():
+    cfg = synth.AttnConfig("t", d=128, heads=8, kv_heads=2, head_dim=64, rank=16, density=0.5,
+                           context=30, max_seq=40)
+    a = synth.make_attn_layer(cfg, layer=1)
+    b = synth.make_attn_layer(cfg, layer=1)
+    c = synth.make_attn_layer(cfg, layer=2)
+    for k in ["w_q", "w_k", "w_v", "w_o_t", "p1", "p2", "c2"]:
+        assert torch.equal(a[k], b[k]), k
+    assert not torch.equal(a["w_q"], c["w_q"])
+    assert a["w_q"].shape == (8 * 64, 128) and a["w_k"].shape == (2 * 64, 128)
+    assert a["w_o_t"].shape == (8 * 64, 128) and a["w_q"].dtype == torch.float16
+    assert a["p1"].shape == (16, 128) and a["p2"].shape == (8, 16) and a["c2"].shape == (8,)
+    # P1 is a selector of 16 distinct input coordinates
+    assert torch.equal(a["p1"].float().sum(dim=1), torch.ones(16))
+    assert int((a["p1"].float().sum(dim=0) > 0).sum()) == 16
+    K, V = synth.make_kv_cache(cfg, layer=1)
+    assert K.shape == (2, 40, 64) and K.dtype == torch.float16
+    K2, _ = synth.make_kv_cache(cfg, layer=1)
+    assert torch.equal(K, K2) and not torch.equal(K, V)
+    # the cache's spread is that of W_k x for x ~ N(0, I): 0.02 sqrt(d)
+    assert abs(float(K.float().std()) - 0.02 * np.sqrt(128)) < 0.03
+    x = synth.make_attn_tokens(cfg, 3, layer=1)
+    assert x.shape == (3, 128) and torch.equal(x, synth.make_attn_tokens(cfg, 3, layer=1))
+
+
+def test_attention_head_density_calibration():
+    """s_h = P2[h] . x_S + c2_h is N(c2_h, |P2[h]|^2) for x ~ N(0, I), so with
+    c2_h = |P2[h]| Phi^-1(density) a head is active (s > 0) with probability `density`."""
+    for dens in (0.25, 0.5, 0.8):
+        cfg = synth.AttnConfig("t", d=256, heads=64, kv_heads=8, head_dim=64, rank=32,
+                               density=dens, context=4, seed=7)
+        L = synth.make_attn_layer(cfg)
+        x = torch.randn(4000, 256, generator=torch.Generator().manual_seed(3))
+        z = x @ L["p1"].float().T
+        s = z @ L["p2"].float().T + L["c2"]
+        assert abs(float((s > 0).float().mean()) - dens) < 0.03, dens
