@@ -168,3 +168,22 @@ def test_attn_full_shape(ffn, name):
     cfg = synth.ATTN_CONFIGS[name]
     counts = _run_case(ffn, cfg, [cfg.context, 0], layer=3)
     assert all(0 < c < cfg.heads for c in counts)
+
+
+def test_attn_plan_without_predictor(ffn):
+    """rank 0: no predictor weights at all (P1, P2 NULL); the caller's mask picks the heads."""
+    cfg = synth.AttnConfig("nopred", d=256, heads=4, kv_heads=4, head_dim=64, rank=8,
+                           density=0.5, context=12, max_seq=16)
+    dev, OL = _layers(cfg)
+    for k in ("p1", "p2", "c1", "c2"):
+        dev[k] = None
+    Kd, Vd = (t.cuda() for t in synth.make_kv_cache(cfg))
+    Kh, Vh = (t.numpy() for t in synth.make_kv_cache(cfg))
+    m = ffn.SparseAttention(dev, max_seq=cfg.seq)
+    assert m.desc.rank == 0
+    x = synth.make_attn_tokens(cfg, 1)[0].cuda()
+    with pytest.raises(ffn.FFNError):                  # no predictor and no mask
+        m.forward(x, 12, Kd, Vd)
+    mk = np.array([0, 1, 1, 0], np.uint8)
+    _check_token(ffn, m, cfg, OL, x, 12, Kd, Vd, Kh, Vh, mk)
+    m.close()
