@@ -91,7 +91,7 @@ __device__ void head_set(const AttnArgs& a, unsigned long long& lo, unsigned lon
     const int hh = min(h, a.H - 1);
     const char* prow = static_cast<const char*>(a.p2) + (size_t)hh * a.rank * 2;
     // the first P2 chunks are requested before z is staged (independent round trips)
-    constexpr int NPRE = 4;
+    constexpr int NPRE = 8;
     u32x4 pre[NPRE];
 #pragma unroll
     for (int i = 0; i < NPRE; ++i) pre[i] = ld16(prow + (size_t)min(sub + i * TPH, pch - 1) * 16);

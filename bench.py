@@ -132,6 +132,7 @@ OTHERS = [
     ("llama2_7b_attn_f16", ["--steps", "64"]),
     ("mistral_7b_attn_f16", ["--steps", "64"]),
     ("llama2_7b_attn_f16", ["--steps", "32", "--context", "8191"]),
+    ("falcon_40b_attn_f16", ["--steps", "16"]),
 ]
 
 

@@ -121,9 +121,10 @@ class AttnConfig:
         return self.max_seq if self.max_seq else self.context + 1
 
 
-# Attention blocks of the pages' dense-attention models (Llama-2-7B: 32 heads of 128; Mistral-7B:
-# 32 query heads sharing 8 key/value heads), at a 512-token context.  The pages print no
-# head-level activity figure; half the heads active is the stand-in.
+# Attention blocks of the pages' models (Llama-2-7B: 32 heads of 128; Mistral-7B: 32 query heads
+# sharing 8 key/value heads; Falcon-40B: 128 query heads of 64 sharing 8 key/value heads), at a
+# 512-token context.  The pages print no head-level activity figure; half the heads active is
+# the stand-in.
 ATTN_CONFIGS = {
     "llama2_7b_attn_f16": AttnConfig("llama2_7b_attn_f16", d=4096, heads=32, kv_heads=32,
                                      head_dim=128, rank=128, density=0.5, context=511,
@@ -131,6 +132,9 @@ ATTN_CONFIGS = {
     "mistral_7b_attn_f16": AttnConfig("mistral_7b_attn_f16", d=4096, heads=32, kv_heads=8,
                                       head_dim=128, rank=128, density=0.5, context=511,
                                       layers=32, seed=2002),
+    "falcon_40b_attn_f16": AttnConfig("falcon_40b_attn_f16", d=8192, heads=128, kv_heads=8,
+                                      head_dim=64, rank=128, density=0.5, context=511,
+                                      layers=60, seed=2003),
 }
 
 

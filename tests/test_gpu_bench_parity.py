@@ -38,6 +38,8 @@ CASES = [
     ("llama2_attn", ["--config", "llama2_7b_attn_f16", "--steps", "4", "--parity-pairs", "8"], 6),
     ("mistral_attn", ["--config", "mistral_7b_attn_f16", "--steps", "4", "--parity-pairs", "8"],
      6),
+    ("falcon_attn", ["--config", "falcon_40b_attn_f16", "--steps", "2", "--parity-pairs", "3"],
+     3),
 ]
 
 
