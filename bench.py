@@ -204,6 +204,9 @@ def run_attn(args):
     import synth
 
     cfg = synth.ATTN_CONFIGS[args.config]
+    if args.batch != 1 or args.prefill or args.offload or args.hot_head or args.fit_recall:
+        raise SystemExit("attention blocks are measured at batch-1 decode (no batch, prefill, "
+                         "offload, hot head or predictor fit)")
     if args.context:
         import dataclasses
         cfg = dataclasses.replace(cfg, context=args.context, max_seq=0)
