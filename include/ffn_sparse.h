@@ -1,5 +1,7 @@
 /*
- * ffn_sparse.h -- C ABI of the MI355X (gfx950) activation-sparse FFN library, libffn_sparse.so.
+ * ffn_sparse.h -- C ABI of the MI355X (gfx950) activation-sparse FFN library, libffn_sparse.so
+ * (the sparse FFN, its mixture-of-experts form, and, at the end of this file, the attention block
+ * with a head-level active set).
  *
  * The operator is the neuron-aware sparse FFN of PowerInfer / PowerInfer-2:
  *  - "PowerInfer: Fast LLM Serving with a Consumer-grade GPU" (unite.ai): section "Adaptive sparse
